@@ -1,0 +1,376 @@
+"""Pins for the float64 oracle: closed forms, invariants, brute force.
+
+Each test ties an oracle function to something fixed outside the oracle's own
+code (the mathematics, a worked example on the page, an exhaustive search),
+chosen so that a dropped term, a wrong sign or a transposed operand fails.
+Source of the method: "Fast KV Compaction via Attention Matching", technical
+summary section 2 (main objective; algorithmic pipeline)."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.optimize import nnls as scipy_nnls
+
+import oracle as orc
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(seed, *shape, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+# --------------------------------------------------------------------- P1
+def test_lse_and_output_match_elementwise_fsum():
+    """lse, O and the RMS importance against scalar loops with math.fsum."""
+    Q, K, V = _rand(1, 5, 3, scale=0.7), _rand(2, 11, 3), _rand(3, 11, 2)
+    lse = orc.row_lse(Q, K, block=4)
+    O, imp = orc.attention_stats(Q, K, V, lse, block=3)
+    for i in range(5):
+        s = [math.fsum(Q[i, c] * K[j, c] for c in range(3)) for j in range(11)]
+        z = math.fsum(math.exp(x) for x in s)
+        assert abs(lse[i] - math.log(z)) < 1e-13
+        for c in range(2):
+            o = math.fsum(math.exp(s[j]) * V[j, c] for j in range(11)) / z
+            assert abs(O[i, c] - o) < 1e-13
+    for j in range(11):
+        p2 = [math.exp(2 * (math.fsum(Q[i, c] * K[j, c] for c in range(3))))
+              / math.exp(2 * lse[i]) for i in range(5)]
+        assert abs(imp[j] - math.sqrt(math.fsum(p2) / 5)) < 1e-13
+    _, imp_mean = orc.attention_stats(Q, K, V, lse, agg="mean")
+    p = np.exp(Q @ K.T - lse[:, None])
+    assert np.allclose(imp_mean, p.mean(axis=0), rtol=1e-13, atol=0)
+
+
+def test_lse_blocking_invariance_and_large_logits():
+    """Any block size gives the same lse (concatenation identity), and logits
+    of size 700 neither overflow nor lose precision."""
+    Q, K = _rand(4, 7, 16, scale=0.3), _rand(5, 1000, 16)
+    ref = orc.row_lse(Q, K, block=1000)
+    for b in (1, 7, 64, 333):
+        assert np.allclose(orc.row_lse(Q, K, block=b), ref, rtol=0, atol=1e-12)
+    K2 = np.zeros((3, 1))
+    K2[:, 0] = [700.0, 699.0, -5.0]
+    got = orc.row_lse(np.ones((1, 1)), K2)[0]
+    assert abs(got - (700.0 + math.log(1 + math.exp(-1) + math.exp(-705)))) < 1e-12
+
+
+def test_zero_query_uniform_attention():
+    """q = 0 -> every p_ij = 1/T, lse = log T, O = column mean of V,
+    importance 1/T for both aggregators."""
+    T = 37
+    Q, K, V = np.zeros((4, 5)), _rand(6, T, 5), _rand(7, T, 3)
+    lse = orc.row_lse(Q, K)
+    assert np.allclose(lse, math.log(T), atol=1e-14)
+    O, imp = orc.attention_stats(Q, K, V, lse)
+    assert np.allclose(O, V.mean(axis=0)[None, :], atol=1e-14)
+    assert np.allclose(imp, 1.0 / T, rtol=1e-13)
+
+
+# --------------------------------------------------------------------- P7
+def test_block_decomposition_identity():
+    """Attention over [A; B] = mass-weighted mix of the two blocks' outputs."""
+    Q = _rand(8, 6, 4, scale=0.5)
+    KA, VA, KB, VB = _rand(9, 13, 4), _rand(10, 13, 3), _rand(11, 9, 4), _rand(12, 9, 3)
+    full = orc.attend(Q, np.vstack([KA, KB]), np.vstack([VA, VB]))
+    la, lb = orc.row_lse(Q, KA), orc.row_lse(Q, KB)
+    oa, ob = orc.attend(Q, KA, VA), orc.attend(Q, KB, VB)
+    za, zb = np.exp(la)[:, None], np.exp(lb)[:, None]
+    assert np.allclose(full, (za * oa + zb * ob) / (za + zb), atol=1e-13)
+
+
+def test_bias_acts_as_key_multiplicity():
+    """A logit bias of log m on one key equals m copies of that key, for the
+    attention output and the mass (the role of beta on the page)."""
+    Q, K, V = _rand(13, 5, 4, scale=0.5), _rand(14, 6, 4), _rand(15, 6, 2)
+    bias = np.zeros(6)
+    bias[2] = math.log(3.0)
+    Kr, Vr = np.vstack([K, K[2], K[2]]), np.vstack([V, V[2], V[2]])
+    assert np.allclose(orc.attend(Q, K, V, bias), orc.attend(Q, Kr, Vr), atol=1e-13)
+
+
+# --------------------------------------------------------------------- P9
+@pytest.mark.parametrize("seed", range(6))
+def test_selection_matches_exhaustive_subset_search(seed):
+    """top-t with the lower-index tie rule = the lexicographically smallest
+    subset that maximises the summed importance (exhaustive over C(T, t))."""
+    rng = np.random.default_rng(100 + seed)
+    T, t = 12 + seed % 3, 2 + seed % 5
+    imp = rng.integers(0, 5, size=T).astype(float)      # many exact ties
+    best, best_set = -1.0, None
+    for S in itertools.combinations(range(T), t):          # lexicographic order
+        v = imp[list(S)].sum()
+        if v > best:
+            best, best_set = v, S
+    assert list(orc.select_topt(imp, t)) == list(best_set)
+
+
+def test_selection_ties_from_duplicate_keys_go_low():
+    """Bitwise-identical keys tie exactly; the lower index is kept."""
+    K = _rand(16, 10, 4)
+    K[7] = K[2]
+    Q = _rand(17, 8, 4, scale=0.4)
+    lse = orc.row_lse(Q, K)
+    _, imp = orc.attention_stats(Q, K, np.zeros((10, 1)), lse)
+    assert imp[7] == imp[2]
+    order = np.argsort(-imp, kind="stable")
+    r = list(order).index(2)
+    idx = orc.select_topt(imp, r + 1)
+    assert 2 in idx and 7 not in idx
+
+
+# -------------------------------------------------------------------- P10
+def _kkt(H, c, w, tol):
+    g = H @ w - c
+    assert (w >= 0).all()
+    assert np.all(np.abs(g[w > 0]) <= tol)
+    assert np.all(g[w == 0] >= -tol)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_nnls_brute_force_over_passive_sets(seed):
+    """For t <= 10 exactly one passive set satisfies the KKT conditions; its
+    solution is the oracle's."""
+    rng = np.random.default_rng(200 + seed)
+    n, t = 14, 6 + seed % 5
+    A = np.abs(rng.standard_normal((n, t))) * rng.uniform(0.1, 1, t)
+    A[:, 1] = A[:, 0] * 0.9 + 0.1 * A[:, 2]                 # near-collinear pair
+    b = rng.uniform(0.5, 1.5, n)
+    H, c = A.T @ A + 1e-3 * np.eye(t), A.T @ b + 1e-3 * rng.standard_normal(t)
+    found = []
+    for mask in itertools.product([False, True], repeat=t):
+        F = np.array(mask)
+        x = np.zeros(t)
+        if F.any():
+            x[F] = np.linalg.solve(H[np.ix_(F, F)], c[F])
+        g = H @ x - c
+        if (x[F] > 0).all() and (g[~F] >= 0).all():
+            found.append(x)
+    assert len(found) == 1
+    w, _, _ = orc.nnls_normal(H, c, w0=np.ones(t))
+    assert np.allclose(w, found[0], atol=1e-11)
+    w0, _, _ = orc.nnls_normal(H, c)                      # start at zero
+    assert np.allclose(w0, found[0], atol=1e-11)
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_bias_fit_kkt_and_independent_nnls(cfg):
+    """On real compaction problems: KKT holds, and scipy's independent
+    Lawson-Hanson code on the augmented system agrees."""
+    w = synth.CONFIGS[cfg]
+    if cfg == 2:
+        w = synth.custom(3, 1, 2048, 256, 128, 205, "bf16", "channel_lognormal")
+    a = synth.head(w, 0)
+    Q, K, V = (synth.to_f64(a[k]) for k in ("Q", "K", "V"))
+    r = orc.compact(Q, K, V, w.t)
+    PS, lam, t = r["PS"], r["lam_w"], w.t
+    H = PS.T @ PS + lam * np.eye(t)
+    c = PS.sum(axis=0) + lam
+    _kkt(H, c, r["w"], 1e-9 * np.abs(c).max())
+    A = np.vstack([PS, math.sqrt(lam) * np.eye(t)])
+    rhs = np.concatenate([np.ones(PS.shape[0]), math.sqrt(lam) * np.ones(t)])
+    ws = scipy_nnls(A, rhs, maxiter=50 * t)[0]
+    assert orc.rel_l2(r["w"], ws) < 1e-7
+    assert r["n_zero"] > 0      # the constraint is active on these problems
+
+
+# --------------------------------------------------------------------- P2
+@pytest.mark.parametrize("n,ridge", [(40, 1e-6), (8, 1e-6), (40, 1e-3)])
+def test_keep_everything_is_exact(n, ridge):
+    """t = T: all indices kept, w = 1 (beta = 0), C_v = V, output unchanged,
+    for any number of reference queries (the ridge prior makes the zero-loss
+    point unique)."""
+    T, d = 24, 8
+    Q, K, V = _rand(20, n, d, scale=0.4), _rand(21, T, d), _rand(22, T, 5)
+    r = orc.compact(Q, K, V, T, ridge_rel=ridge)
+    assert list(r["idx"]) == list(range(T))
+    assert np.allclose(r["w"], 1.0, atol=1e-10)
+    assert np.allclose(r["beta"], 0.0, atol=1e-10)
+    assert np.allclose(r["Cv"], V, atol=1e-9)
+    Qn = _rand(23, 9, d, scale=0.4)
+    assert np.allclose(orc.attend(Qn, r["Ck"], r["Cv"], r["beta"]), orc.attend(Qn, K, V),
+                       atol=1e-9)
+
+
+# --------------------------------------------------------------------- P4
+def test_zero_queries_golden_bias():
+    """Page example (q = 0: full mass T versus t kept keys), stored under
+    tests/golden with its citation: beta -> log(T/t)."""
+    with open(os.path.join(GOLDEN, "q0_mass_example.json")) as f:
+        gold = json.load(f)
+    for case in gold["cases"]:
+        T, t, n, d = case["T"], case["t"], case["n"], case["d"]
+        Q, K, V = np.zeros((n, d)), _rand(T, T, d), _rand(T + 1, T, 3)
+        r = orc.compact(Q, K, V, t, ridge_rel=1e-12)
+        assert list(r["idx"]) == list(range(t))          # all tie -> lowest indices
+        assert np.allclose(r["beta"], case["beta"], atol=1e-9)
+
+
+@pytest.mark.parametrize("rho", [1e-6, 1e-2, 0.5])
+def test_zero_queries_closed_form_with_ridge(rho):
+    """q = 0 at finite ridge: w = (T + rho)/(t + rho) and
+    C_v,j = V_j + (mean(V) - mean(V_S)) / (1 + rho/t)."""
+    T, t, n = 30, 7, 5
+    V = _rand(31, T, 4)
+    r = orc.compact(np.zeros((n, 6)), _rand(30, T, 6), V, t, ridge_rel=rho)
+    assert np.allclose(r["w"], (T + rho) / (t + rho), rtol=1e-9)
+    VS = V[:t]
+    expect = VS + (V.mean(axis=0) - VS.mean(axis=0)) / (1 + rho / t)
+    assert np.allclose(r["Cv"], expect, atol=1e-7)
+
+
+# --------------------------------------------------------------------- P5
+@pytest.mark.parametrize("rho", [1e-6, 1e-3, 0.3])
+def test_single_query_closed_form(rho):
+    """n = 1: w = 1 + p (1 - sum p) / (|p|^2 + lam_w) (inactive constraint),
+    C_v = V_S + x (o - x V_S) / (|x|^2 + lam_v)   (Sherman-Morrison)."""
+    T, t, d = 40, 9, 6
+    q, K, V = _rand(40, 1, d, scale=0.6), _rand(41, T, d), _rand(42, T, 3)
+    r = orc.compact(q, K, V, t, ridge_rel=rho)
+    s = (q @ K.T)[0]
+    p_all = np.exp(s - s.max())
+    p_all /= p_all.sum()
+    S = np.sort(np.argsort(-p_all, kind="stable")[:t])
+    assert list(r["idx"]) == list(S)
+    p = p_all[S]
+    lam_w = rho * (p @ p) / t
+    w = 1 + p * (1 - p.sum()) / (p @ p + lam_w)
+    assert np.allclose(r["w"], w, rtol=1e-9)
+    x = p * w / (p @ w)
+    o = p_all @ V
+    lam_v = rho * (x @ x) / t
+    Cv = V[S] + np.outer(x, o - x @ V[S]) / (x @ x + lam_v)
+    assert np.allclose(r["Cv"], Cv, atol=1e-8)
+
+
+# --------------------------------------------------------------------- P6
+def test_duplicated_keys_recovered_exactly_for_all_queries():
+    """t distinct keys, key j repeated m_j times, fit on the first copies:
+    w_j = m_j, C_v,j = mean of V over the copies, exact for fresh queries."""
+    rng = np.random.default_rng(50)
+    t, d = 5, 6
+    base = rng.standard_normal((t, d))
+    mult = np.array([1, 3, 2, 4, 1])
+    rows = np.repeat(np.arange(t), mult)
+    perm = rng.permutation(rows.size)
+    K = base[rows[perm]]
+    V = rng.standard_normal((rows.size, 3))
+    first = np.array([np.flatnonzero(rows[perm] == j)[0] for j in range(t)])
+    order = np.argsort(first)
+    idx = first[order]
+    Q = rng.standard_normal((12, d)) * 0.5
+    w, beta, Cv, _ = orc.fit(Q, K, V, idx, ridge_rel=1e-12)
+    assert np.allclose(w, mult[order], rtol=1e-8)
+    means = np.array([V[rows[perm] == j].mean(axis=0) for j in range(t)])[order]
+    assert np.allclose(Cv, means, atol=1e-7)
+    Qn = rng.standard_normal((20, d)) * 0.5
+    assert np.allclose(orc.attend(Qn, K[idx], Cv, beta), orc.attend(Qn, K, V), atol=1e-7)
+
+
+# --------------------------------------------------------------------- P3
+@pytest.mark.parametrize("ridge", [1e-6, 1e-2])
+def test_value_fit_gradient_vanishes_and_normal_equations_agree(ridge):
+    w = synth.custom(7, 1, 700, 96, 32, 70, "f32", "normal")
+    a = synth.head(w, 0)
+    Q, K, V = (synth.to_f64(a[k]) for k in ("Q", "K", "V"))
+    r = orc.compact(Q, K, V, w.t, ridge_rel=ridge)
+    X, O, VS, C = r["X"], r["O"], V[r["idx"]], r["Cv"]
+    lam = r["lam_v"]
+    grad = X.T @ (X @ C - O) + lam * (C - VS)
+    scale = np.linalg.norm(X.T @ O) + lam * np.linalg.norm(VS)
+    assert np.linalg.norm(grad) <= 1e-10 * scale
+    Cne = np.linalg.solve(X.T @ X + lam * np.eye(w.t), X.T @ O + lam * VS)
+    assert orc.rel_l2(C, Cne) < 1e-6
+    # the compacted weights are a softmax over the kept keys with the bias
+    s = Q @ K[r["idx"]].T + r["beta"][None, :]
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    assert np.allclose(X, e / e.sum(axis=1, keepdims=True), atol=1e-14)
+
+
+def test_bias_mass_equation_and_relative_weighting():
+    """The fitted multipliers minimise the relative mass residual: perturbing
+    any positive w_j along +-eps does not lower the objective."""
+    w = synth.custom(8, 1, 600, 80, 32, 40, "f32", "normal")
+    a = synth.head(w, 0)
+    Q, K, V = (synth.to_f64(a[k]) for k in ("Q", "K", "V"))
+    r = orc.compact(Q, K, V, w.t)
+    PS, lam, wv = r["PS"], r["lam_w"], r["w"]
+
+    def obj(x):
+        return np.sum((PS @ x - 1) ** 2) + lam * np.sum((x - 1) ** 2)
+
+    f0 = obj(wv)
+    rng = np.random.default_rng(0)
+    for _ in range(20):
+        dx = rng.standard_normal(wv.size) * 1e-4
+        x = np.maximum(wv + dx, 0)
+        assert obj(x) >= f0 - 1e-15
+    # relative mass: with the full mass on the left, p sums to one per query
+    full = np.exp(Q @ K.T - r["lse"][:, None]).sum(axis=1)
+    assert np.allclose(full, 1.0, atol=1e-13)
+
+
+# --------------------------------------------------------------------- P8
+@pytest.mark.parametrize("cfg_seed", range(3))
+def test_eviction_error_bound(cfg_seed):
+    """Eviction only (beta = 0, values kept): |o - o'| <= 2 Vmax delta per
+    query, delta the dropped attention mass (error-bound page, section 2B)."""
+    w = synth.custom(20 + cfg_seed, 1, 300, 40, 16, 30, "f32", "normal")
+    a = synth.head(w, 0)
+    Q, K, V = (synth.to_f64(a[k]) for k in ("Q", "K", "V"))
+    r = orc.compact(Q, K, V, w.t)
+    idx = r["idx"]
+    o = orc.attend(Q, K, V)
+    o2 = orc.attend(Q, K[idx], V[idx])
+    delta = 1 - r["PS"].sum(axis=1)
+    vmax = np.linalg.norm(V, axis=1).max()
+    assert np.all(np.linalg.norm(o - o2, axis=1) <= 2 * vmax * delta + 1e-12)
+
+
+def test_am_fit_beats_eviction_on_reference_queries():
+    """Eviction (w = 1, C_v = V_S) is a feasible point of both fits, so the
+    fitted cache cannot be worse on the reference queries' objective."""
+    w = synth.custom(30, 1, 1024, 128, 32, 64, "bf16", "clusters")
+    a = synth.head(w, 0)
+    Q, K, V = (synth.to_f64(a[k]) for k in ("Q", "K", "V"))
+    r = orc.compact(Q, K, V, w.t)
+    am = orc.attend(Q, r["Ck"], r["Cv"], r["beta"])
+    ev = orc.attend(Q, r["Ck"], V[r["idx"]])
+    assert orc.rel_l2(am, r["O"]) < orc.rel_l2(ev, r["O"])
+
+
+def test_argument_checks():
+    with pytest.raises(ValueError):
+        orc.compact(np.zeros((2, 3)), np.zeros((4, 3)), np.zeros((4, 3)), 5)
+    with pytest.raises(ValueError):
+        orc.compact(np.zeros((2, 3)), np.zeros((4, 3)), np.zeros((4, 3)), 0)
+
+
+# ----------------------------------------------------------------- synth
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -2.5, 3.3e38,
+                  1e-40], dtype=np.float64)
+    b = synth.round_bf16_bits(x)
+    back = synth.bf16_bits_to_f64(b)
+    assert back[0] == 1.0
+    assert back[1] == 1.0                    # tie -> even mantissa
+    assert back[2] == 1.0 + 4 * 2 ** -8      # tie -> even (up)
+    assert back[3] == 1.0
+    assert back[4] == -2.5
+    for v, r in zip(x[:5], back[:5]):
+        assert abs(v - r) <= abs(v) * 2 ** -8
+
+
+def test_workload_shapes_and_determinism():
+    w = synth.CONFIGS[3]
+    small = synth.Workload(3, "c3_small", 2, 512, 32, 128, 10, "bf16", "clusters", 8)
+    a, b = synth.batch(small), synth.batch(small)
+    for k in a:
+        assert np.array_equal(a[k], b[k])
+    assert a["K"].shape == (2, 512, 128) and a["K"].dtype == np.uint16
+    assert w.T // w.t == 50
+    assert synth.CONFIGS[4].B == 256 and synth.CONFIGS[5].T == 131072

@@ -1,0 +1,141 @@
+/* kvc.h -- attention-matching KV-cache compaction on AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Fast KV Compaction via Attention Matching" (Zweiger, Fu, Guo, Kim),
+ * technical summary, section 2.  Per (layer, KV head) the library builds a
+ * compact cache (C_k, beta, C_v) of t << T entries from the full cache (K, V)
+ * and a set of reference queries Q_ref so that, on those queries, attention
+ * over the compact cache reproduces both the attention output and the
+ * attention mass of the full cache (the output- and mass-matching equations of
+ * the "main objective" paragraph):
+ *
+ *   1. s = Q_ref K^T (no extra scale: Q_ref carries 1/sqrt(d)), lse per query,
+ *      p = exp(s - lse), full-cache output O = P V;
+ *   2. importance of key j = RMS over the reference queries of p_ij (or the
+ *      mean, KVC_AGG_MEAN); keep the t most important ORIGINAL keys
+ *      ("highest-attention keys" in the algorithmic pipeline); equal
+ *      importances go to the lower index; kept indices ascend;
+ *   3. bias: w = argmin_{w >= 0} ||P_S w - 1||^2 + lam_w ||w - 1||^2 (each
+ *      query's kept mass, re-weighted, equals its full mass; the pipeline's
+ *      NNLS bias fit), beta = log(max(w, 1e-30));
+ *   4. values: C_v = argmin ||X C - O||^2 + lam_v ||C - V_S||^2 with X the
+ *      softmax over the kept keys with the fitted bias (the pipeline's
+ *      least-squares value fit given keys and bias).
+ *   lam_w = ridge_rel * trace(P_S^T P_S) / t and lam_v = ridge_rel *
+ *   trace(X^T X) / t: a vanishing ridge toward the prior (w = 1, C_v = V_S).
+ *
+ * Conventions for every entry point below:
+ *   - every array pointer is a DEVICE pointer to row-major, contiguous data,
+ *     aligned to 16 bytes; the caller owns every buffer; the library keeps no
+ *     state between calls and allocates no device memory in these calls;
+ *   - work is enqueued on `stream` and is asynchronous: outputs are valid once
+ *     the stream has completed;
+ *   - argument errors (KVC_EINVAL, KVC_EWORKSPACE, KVC_EUNSUPPORTED) are
+ *     detected before anything is enqueued;
+ *   - calls are reentrant across distinct workspaces; two calls that share a
+ *     workspace must be ordered on one stream.
+ */
+#ifndef KVC_H_
+#define KVC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_OK            0
+#define KVC_EINVAL       -1   /* null pointer, misalignment, bad size or enum     */
+#define KVC_EWORKSPACE   -2   /* workspace smaller than kvc_workspace_bytes()     */
+#define KVC_EHIP         -3   /* a HIP launch or query failed                     */
+#define KVC_EUNSUPPORTED -4   /* head dim other than 64/128, or sizes past limits */
+
+/* Per-head numerical status written to out_status[b] (0 = ok). */
+#define KVC_STATUS_OK            0
+#define KVC_STATUS_NOT_SPD       1  /* a Cholesky pivot was <= 0                */
+#define KVC_STATUS_NNLS_CAP      2  /* NNLS stopped at max_nnls_iters           */
+#define KVC_STATUS_NONFINITE     4  /* a non-finite value reached the fits      */
+
+typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype_t;
+typedef enum { KVC_AGG_RMS = 0, KVC_AGG_MEAN = 1 } kvc_agg_t;
+
+typedef struct {
+  int64_t B;              /* independent (layer, KV head) problems, >= 1          */
+  int64_t T;              /* cache length per head, >= 1                          */
+  int64_t n;              /* reference queries per head, >= 1                     */
+  int64_t d;              /* head dim: 64 or 128                                  */
+  int64_t t;              /* kept keys per head, 1 <= t <= T, t <= 8192           */
+  int32_t in_dtype;       /* kvc_dtype_t of Q_ref, K, V (out_K has the same)      */
+  int32_t agg;            /* kvc_agg_t, default KVC_AGG_RMS                       */
+  double  ridge_rel;      /* ridge weight relative to the Gram's mean diagonal,
+                             default 1e-6; must be > 0                            */
+  int32_t max_nnls_iters; /* cap on NNLS pivoting rounds, default 32              */
+  int32_t reserved;       /* must be 0                                            */
+} kvc_params_t;
+
+/* Fill *p with the defaults above (sizes zeroed). */
+void kvc_params_default(kvc_params_t* p);
+
+/* Bytes of device workspace kvc_compact / kvc_fit need for these parameters,
+ * or 0 if the parameters are invalid.  Depends on B, T, n, d, t only. */
+size_t kvc_workspace_bytes(const kvc_params_t* p);
+
+/* Compact B independent heads.
+ *   Q_ref   [B, n, d]  in_dtype   reference queries (scaled by the caller)
+ *   K, V    [B, T, d]  in_dtype   full cache (keys as stored, e.g. post-RoPE)
+ *   out_K   [B, t, d]  in_dtype   kept keys: exact copies of K rows
+ *   out_bias[B, t]     float32    beta, an additive logit bias per kept key
+ *   out_V   [B, t, d]  float32    fitted values
+ *   out_idx [B, t]     int32      kept indices, ascending; may be NULL
+ *   out_status [B]     int32      per-head KVC_STATUS_* bits; may be NULL
+ *   workspace          >= kvc_workspace_bytes(p) bytes of device memory
+ * Returns KVC_OK once everything is enqueued, or a negative KVC_E* code. */
+int kvc_compact(const kvc_params_t* p, const void* Q_ref, const void* K, const void* V,
+                void* out_K, float* out_bias, float* out_V, int32_t* out_idx,
+                int32_t* out_status, void* workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/* Bias and value fit for a caller-given kept set (steps 3-4 only).
+ *   idx [B, t] int32, strictly ascending, in [0, T).  Other arguments as in
+ *   kvc_compact.  Used to check the fits in isolation and to re-fit a cache
+ *   whose keys were chosen elsewhere. */
+int kvc_fit(const kvc_params_t* p, const void* Q_ref, const void* K, const void* V,
+            const int32_t* idx, float* out_bias, float* out_V, int32_t* out_status,
+            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Where the intermediates of the last call live inside its workspace (byte
+ * offsets), for inspection after the stream completes:
+ *   lse [B, n] f32; O [B, n, d] f32 (full-cache output); imp [B, T] f32 holding
+ *   sum_i p_ij^2 (RMS) or sum_i p_ij (mean) -- the ranking key before the
+ *   monotone sqrt(./n) or ./n; w [B, t] f64 the NNLS multipliers. */
+typedef struct {
+  size_t lse, O, imp, w;
+} kvc_ws_layout_t;
+int kvc_workspace_layout(const kvc_params_t* p, kvc_ws_layout_t* out);
+
+/* Instrumentation for benchmarks (not thread-safe; leave off in production).
+ * While the stage mask is non-zero, every kvc_compact / kvc_fit call records a
+ * HIP event pair on its stream around each selected stage; events are created
+ * on first use and reused.  kvc_profile_enable() resets the counters;
+ * kvc_profile_read() waits for the recorded events of one stage and returns
+ * the summed elapsed time and the number of recorded launches. */
+#define KVC_STAGE_SCORE_LSE 0  /* scores + online log-sum-exp kernel          */
+#define KVC_STAGE_EXPWEIGHT 1  /* p = exp(s - lse), P V, importance kernel     */
+#define KVC_STAGE_SELECT    2  /* importance reduction, top-t select, gather  */
+#define KVC_STAGE_PS        3  /* kept-key softmax weights P_S (fp64)          */
+#define KVC_STAGE_GRAM      4  /* mass Gram P_S^T P_S (fp64 MFMA)              */
+#define KVC_STAGE_NNLS      5  /* pivoting rounds incl. their Cholesky solves  */
+#define KVC_STAGE_VALUE     6  /* value fit: Gram, right-hand side, solve      */
+#define KVC_STAGE_TOTAL     7  /* the whole call                               */
+#define KVC_NUM_STAGES      8
+int kvc_profile_enable(uint32_t stage_mask);
+int kvc_profile_read(int stage, double* total_ms, int64_t* launches);
+
+/* Static text for a KVC_* return code. */
+const char* kvc_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVC_H_ */

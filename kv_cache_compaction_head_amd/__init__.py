@@ -1,0 +1,136 @@
+"""Attention-matching KV-cache compaction on AMD MI355X (gfx950).
+
+Python front of the C ABI in include/kvc.h.  Torch tensors supply device
+memory and the stream; every step of the computation runs in the HIP library
+(libkvc.so), which must be built first (`python -m
+kv_cache_compaction_head_amd.build`).  There is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+
+from . import _lib
+from ._lib import (KVC_AGG_MEAN, KVC_AGG_RMS, KVC_BF16, KVC_F32, STATUS_NNLS_CAP,
+                   STATUS_NONFINITE, STATUS_NOT_SPD, Params, load, make_params, strerror,
+                   workspace_bytes, workspace_layout)
+
+__all__ = ["compact", "fit", "Compacted", "intermediates", "load", "make_params",
+           "workspace_bytes", "workspace_layout", "strerror", "Params"]
+
+
+@dataclasses.dataclass
+class Compacted:
+    """Outputs of one call (device tensors; valid once the stream completes)."""
+    keys: "object"       # [B, t, d] input dtype, exact copies of kept K rows
+    bias: "object"       # [B, t] float32, additive logit bias per kept key
+    values: "object"     # [B, t, d] float32, fitted values
+    idx: "object"        # [B, t] int32, kept indices (ascending)
+    status: "object"     # [B] int32, KVC_STATUS_* bits per head
+    workspace: "object"  # uint8 device buffer holding the intermediates
+    params: Params
+
+
+def _vp(x):
+    return ctypes.c_void_p(x.data_ptr())
+
+
+def _prep(Q, K, V):
+    import torch
+    squeeze = Q.dim() == 2
+    if squeeze:
+        Q, K, V = Q.unsqueeze(0), K.unsqueeze(0), V.unsqueeze(0)
+    if Q.dim() != 3 or K.dim() != 3 or V.dim() != 3:
+        raise ValueError("expected Q_ref [B,n,d], K [B,T,d], V [B,T,d] (or unbatched)")
+    if not (Q.is_cuda and K.is_cuda and V.is_cuda):
+        raise ValueError("tensors must be on a HIP device")
+    if not (Q.dtype == K.dtype == V.dtype) or Q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("Q_ref, K, V must share one dtype: bfloat16 or float32")
+    if K.shape != V.shape or Q.shape[0] != K.shape[0] or Q.shape[2] != K.shape[2]:
+        raise ValueError("shape mismatch between Q_ref, K and V")
+    return Q.contiguous(), K.contiguous(), V.contiguous(), squeeze
+
+
+def _stream(stream, device):
+    import torch
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(p, device, workspace):
+    import torch
+    need = workspace_bytes(p)
+    if need == 0:
+        raise ValueError("invalid compaction parameters")
+    if workspace is None:
+        return torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    return workspace
+
+
+def compact(Q, K, V, t: int, *, agg: str = "rms", ridge_rel: float = 1e-6,
+            max_nnls_iters: int = 32, workspace=None, stream=None) -> Compacted:
+    """Compact each head's cache to t kept keys with fitted bias and values."""
+    import torch
+    Q, K, V, _ = _prep(Q, K, V)
+    B, n, d = Q.shape
+    T = K.shape[1]
+    dt = "bf16" if Q.dtype == torch.bfloat16 else "f32"
+    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters)
+    dev = Q.device
+    ws = _workspace(p, dev, workspace)
+    keys = torch.empty((B, t, d), dtype=Q.dtype, device=dev)
+    bias = torch.empty((B, t), dtype=torch.float32, device=dev)
+    values = torch.empty((B, t, d), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, t), dtype=torch.int32, device=dev)
+    status = torch.empty((B,), dtype=torch.int32, device=dev)
+    rc = load().kvc_compact(ctypes.byref(p), _vp(Q), _vp(K), _vp(V), _vp(keys), _vp(bias),
+                            _vp(values), _vp(idx), _vp(status), _vp(ws),
+                            ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(stream, dev))
+    _lib.check(rc)
+    return Compacted(keys, bias, values, idx, status, ws, p)
+
+
+def fit(Q, K, V, idx, *, ridge_rel: float = 1e-6, max_nnls_iters: int = 32,
+        workspace=None, stream=None) -> Compacted:
+    """Bias and value fit for a given kept set idx [B, t] (int32, ascending)."""
+    import torch
+    Q, K, V, _ = _prep(Q, K, V)
+    if idx.dim() == 1:
+        idx = idx.unsqueeze(0)
+    idx = idx.to(torch.int32).contiguous()
+    B, n, d = Q.shape
+    T, t = K.shape[1], idx.shape[1]
+    dt = "bf16" if Q.dtype == torch.bfloat16 else "f32"
+    p = make_params(B, T, n, d, t, dt, "rms", ridge_rel, max_nnls_iters)
+    dev = Q.device
+    ws = _workspace(p, dev, workspace)
+    bias = torch.empty((B, t), dtype=torch.float32, device=dev)
+    values = torch.empty((B, t, d), dtype=torch.float32, device=dev)
+    status = torch.empty((B,), dtype=torch.int32, device=dev)
+    rc = load().kvc_fit(ctypes.byref(p), _vp(Q), _vp(K), _vp(V), _vp(idx), _vp(bias),
+                        _vp(values), _vp(status), _vp(ws),
+                        ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(stream, dev))
+    _lib.check(rc)
+    keys = None
+    return Compacted(keys, bias, values, idx, status, ws, p)
+
+
+def intermediates(res: Compacted) -> dict:
+    """Views into the workspace: lse [B,n], O [B,n,d], imp [B,T] (sum of p^2 or
+    p per key), w [B,t] (float64 NNLS multipliers).  Synchronise first."""
+    import torch
+    p = res.params
+    L = workspace_layout(p)
+    ws = res.workspace
+    B, T, n, d, t = p.B, p.T, p.n, p.d, p.t
+
+    def view(off, count, dtype, shape):
+        nbytes = count * torch.tensor([], dtype=dtype).element_size()
+        return ws[off:off + nbytes].view(dtype).view(*shape)
+
+    return {"lse": view(L.lse, B * n, torch.float32, (B, n)),
+            "O": view(L.O, B * n * d, torch.float32, (B, n, d)),
+            "imp": view(L.imp, B * T, torch.float32, (B, T)),
+            "w": view(L.w, B * t, torch.float64, (B, t))}

@@ -1,0 +1,328 @@
+// Host side of the C ABI declared in include/kvc.h: argument checks,
+// workspace layout and the launch sequence on the caller's stream.
+//
+// Pipeline ("Fast KV Compaction via Attention Matching", section 2): scores
+// and log-sum-exp over the full cache, full-cache output and per-key
+// importance, top-t selection of original keys, NNLS bias fit on the relative
+// attention mass, least-squares value fit.  Nothing here allocates device
+// memory or synchronises with the device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "../../include/kvc.h"
+
+#include "launch.h"
+
+namespace {
+
+struct ProfState {
+  uint32_t mask = 0;
+  std::vector<hipEvent_t> ev[KVC_NUM_STAGES];  // start, stop, start, stop, ...
+  size_t used[KVC_NUM_STAGES] = {};
+};
+ProfState g_prof;
+
+}  // namespace
+
+namespace kvc {
+void prof_mark(int stage, bool end, hipStream_t st) {
+  if (!(g_prof.mask & (1u << stage))) return;
+  auto& v = g_prof.ev[stage];
+  size_t& u = g_prof.used[stage];
+  if (!end && (u & 1)) return;  // unmatched start: ignore
+  if (end && !(u & 1)) return;
+  if (u == v.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return;
+    v.push_back(e);
+  }
+  if (hipEventRecord(v[u], st) == hipSuccess) ++u;
+}
+}  // namespace kvc
+
+namespace {
+
+constexpr int64_t kMaxT = 1 << 30;
+constexpr int64_t kMaxT_keep = 8192;
+constexpr int64_t kMaxB = 65535;
+constexpr int kBM = 128;  // reference queries per score workgroup
+
+struct Plan {
+  int nqb, nsplit1, kps1, nsplit2, kps2;
+};
+
+// Split the key range so the score grid has ~1024 workgroups; splits are a
+// multiple of 64 keys (a whole number of K1 tiles).
+void split_keys(int64_t T, int64_t work_per_split, int& nsplit, int& kps) {
+  int64_t want = (1024 + work_per_split - 1) / work_per_split;
+  int64_t maxs = T / 512 > 0 ? T / 512 : 1;
+  if (want > maxs) want = maxs;
+  if (want < 1) want = 1;
+  int64_t per = (T + want - 1) / want;
+  per = (per + 63) / 64 * 64;
+  kps = static_cast<int>(per);
+  nsplit = static_cast<int>((T + per - 1) / per);
+}
+
+Plan make_plan(const kvc_params_t* p) {
+  Plan pl;
+  pl.nqb = static_cast<int>((p->n + kBM - 1) / kBM);
+  split_keys(p->T, static_cast<int64_t>(pl.nqb) * p->B, pl.nsplit1, pl.kps1);
+  split_keys(p->T, static_cast<int64_t>(pl.nqb) * p->B, pl.nsplit2, pl.kps2);
+  return pl;
+}
+
+struct Layout {
+  size_t ml, lse, Opart, O, imp_part, imp, idx, status, PS, H, W, cvec, xs, R, wv, lam, mask,
+      Fidx, inv, msz, state, total;
+};
+
+size_t align_up(size_t x) { return (x + 255) / 256 * 256; }
+
+Layout make_layout(const kvc_params_t* p) {
+  const Plan pl = make_plan(p);
+  const size_t B = p->B, T = p->T, n = p->n, d = p->d, t = p->t;
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.ml = take(B * pl.nsplit1 * n * 8);
+  L.lse = take(B * n * 4);
+  L.Opart = take(B * pl.nsplit2 * d * n * 4);
+  L.O = take(B * n * d * 4);
+  L.imp_part = take(B * pl.nqb * T * 4);
+  L.imp = take(B * T * 4);
+  L.idx = take(B * t * 4);
+  L.status = take(B * 4);
+  L.PS = take(B * n * t * 8);
+  L.H = take(B * t * t * 8);
+  L.W = take(B * t * t * 8);
+  L.cvec = take(B * t * 8);
+  L.xs = take(B * t * 8);
+  L.R = take(B * t * d * 8);
+  L.wv = take(B * t * 8);
+  L.lam = take(B * 2 * 8);
+  L.mask = take(B * t * 4);
+  L.Fidx = take(B * t * 4);
+  L.inv = take(B * t * 4);
+  L.msz = take(B * 4);
+  L.state = take(B * 4 * 4);
+  L.total = off;
+  return L;
+}
+
+bool params_ok(const kvc_params_t* p) {
+  if (!p) return false;
+  if (p->B < 1 || p->B > kMaxB) return false;
+  if (p->T < 1 || p->T > kMaxT) return false;
+  if (p->n < 1 || p->n > kMaxT) return false;
+  if (p->d != 64 && p->d != 128) return false;
+  if (p->t < 1 || p->t > p->T || p->t > kMaxT_keep) return false;
+  if (p->in_dtype != KVC_F32 && p->in_dtype != KVC_BF16) return false;
+  if (p->agg != KVC_AGG_RMS && p->agg != KVC_AGG_MEAN) return false;
+  if (!(p->ridge_rel > 0.0) || !std::isfinite(p->ridge_rel)) return false;
+  if (p->max_nnls_iters < 1 || p->max_nnls_iters > 1000) return false;
+  if (p->reserved != 0) return false;
+  return true;
+}
+
+bool aligned(const void* ptr) { return ptr && (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+kvc::FitBufs fit_bufs(void* ws, const Layout& L) {
+  kvc::FitBufs fb;
+  fb.PS = at<double>(ws, L.PS);
+  fb.H = at<double>(ws, L.H);
+  fb.W = at<double>(ws, L.W);
+  fb.cvec = at<double>(ws, L.cvec);
+  fb.xs = at<double>(ws, L.xs);
+  fb.R = at<double>(ws, L.R);
+  fb.wv = at<double>(ws, L.wv);
+  fb.lam = at<double>(ws, L.lam);
+  fb.mask = at<int32_t>(ws, L.mask);
+  fb.Fidx = at<int32_t>(ws, L.Fidx);
+  fb.inv = at<int32_t>(ws, L.inv);
+  fb.msz = at<int32_t>(ws, L.msz);
+  fb.state = at<int32_t>(ws, L.state);
+  return fb;
+}
+
+template <class In, int D>
+hipError_t run_score(const kvc_params_t* p, const void* Q, const void* K, const void* V,
+                     void* ws, const Layout& L, hipStream_t st) {
+  const Plan pl = make_plan(p);
+  return kvc::launch_score<In, D>(Q, K, V, at<float2>(ws, L.ml), at<float>(ws, L.lse),
+                                  at<float>(ws, L.Opart), at<float>(ws, L.O),
+                                  at<float>(ws, L.imp_part), at<float>(ws, L.imp),
+                                  static_cast<int>(p->B), static_cast<int>(p->n),
+                                  static_cast<int>(p->T), pl.nsplit1, pl.kps1, pl.nsplit2,
+                                  pl.kps2, p->agg == KVC_AGG_RMS, st);
+}
+
+template <class In, int D>
+hipError_t run_fit(const kvc_params_t* p, const void* Q, const void* K, const void* V,
+                   const int32_t* idx, float* out_bias, float* out_V, int32_t* status, void* ws,
+                   const Layout& L, hipStream_t st) {
+  return kvc::launch_fit<In, D>(Q, K, V, at<float>(ws, L.lse), at<float>(ws, L.O), idx,
+                                fit_bufs(ws, L), out_bias, out_V, status,
+                                static_cast<int>(p->B), static_cast<int>(p->n),
+                                static_cast<int>(p->T), static_cast<int>(p->t), p->ridge_rel,
+                                p->max_nnls_iters, st);
+}
+
+// Dispatch on (dtype, head dim).
+template <template <class, int> class F, class... A>
+hipError_t dispatch(const kvc_params_t* p, A... args) {
+  if (p->in_dtype == KVC_BF16) {
+    if (p->d == 128) return F<kvc::bf16_t, 128>::run(p, args...);
+    return F<kvc::bf16_t, 64>::run(p, args...);
+  }
+  if (p->d == 128) return F<float, 128>::run(p, args...);
+  return F<float, 64>::run(p, args...);
+}
+
+template <class In, int D>
+struct ScoreOp {
+  static hipError_t run(const kvc_params_t* p, const void* Q, const void* K, const void* V,
+                        void* ws, const Layout* L, hipStream_t st) {
+    return run_score<In, D>(p, Q, K, V, ws, *L, st);
+  }
+};
+template <class In, int D>
+struct FitOp {
+  static hipError_t run(const kvc_params_t* p, const void* Q, const void* K, const void* V,
+                        const int32_t* idx, float* ob, float* ov, int32_t* status, void* ws,
+                        const Layout* L, hipStream_t st) {
+    return run_fit<In, D>(p, Q, K, V, idx, ob, ov, status, ws, *L, st);
+  }
+};
+
+int common_checks(const kvc_params_t* p, const void* Q, const void* K, const void* V,
+                  const void* out_bias, const void* out_V, void* ws, size_t ws_bytes) {
+  if (!params_ok(p)) return KVC_EINVAL;
+  if (!aligned(Q) || !aligned(K) || !aligned(V) || !aligned(out_bias) || !aligned(out_V) ||
+      !aligned(ws))
+    return KVC_EINVAL;
+  if (ws_bytes < make_layout(p).total) return KVC_EWORKSPACE;
+  return KVC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void kvc_params_default(kvc_params_t* p) {
+  if (!p) return;
+  std::memset(p, 0, sizeof(*p));
+  p->in_dtype = KVC_BF16;
+  p->agg = KVC_AGG_RMS;
+  p->ridge_rel = 1e-6;
+  p->max_nnls_iters = 32;
+  p->reserved = 0;
+}
+
+size_t kvc_workspace_bytes(const kvc_params_t* p) {
+  if (!params_ok(p)) return 0;
+  return make_layout(p).total;
+}
+
+int kvc_workspace_layout(const kvc_params_t* p, kvc_ws_layout_t* out) {
+  if (!params_ok(p) || !out) return KVC_EINVAL;
+  const Layout L = make_layout(p);
+  out->lse = L.lse;
+  out->O = L.O;
+  out->imp = L.imp;
+  out->w = L.wv;
+  return KVC_OK;
+}
+
+int kvc_compact(const kvc_params_t* p, const void* Q_ref, const void* K, const void* V,
+                void* out_K, float* out_bias, float* out_V, int32_t* out_idx,
+                int32_t* out_status, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  int rc = common_checks(p, Q_ref, K, V, out_bias, out_V, workspace, workspace_bytes);
+  if (rc) return rc;
+  if (!aligned(out_K) || (out_idx && !aligned(out_idx)) || (out_status && !aligned(out_status)))
+    return KVC_EINVAL;
+  const Layout L = make_layout(p);
+  int32_t* idx = out_idx ? out_idx : at<int32_t>(workspace, L.idx);
+  int32_t* status = out_status ? out_status : at<int32_t>(workspace, L.status);
+  const int B = static_cast<int>(p->B), T = static_cast<int>(p->T), t = static_cast<int>(p->t);
+  const int es = p->in_dtype == KVC_BF16 ? 2 : 4;
+  kvc::prof_mark(KVC_STAGE_TOTAL, false, stream);
+  hipError_t e = kvc::launch_fill_i32(status, 0, p->B, stream);
+  if (e == hipSuccess) e = dispatch<ScoreOp>(p, Q_ref, K, V, workspace, &L, stream);
+  kvc::prof_mark(KVC_STAGE_SELECT, false, stream);
+  if (e == hipSuccess) e = kvc::launch_select(at<float>(workspace, L.imp), idx, status, B, T, t, stream);
+  if (e == hipSuccess)
+    e = kvc::launch_gather(K, idx, out_K, B, T, t, static_cast<int>(p->d) * es, stream);
+  kvc::prof_mark(KVC_STAGE_SELECT, true, stream);
+  if (e == hipSuccess)
+    e = dispatch<FitOp>(p, Q_ref, K, V, static_cast<const int32_t*>(idx), out_bias, out_V,
+                        status, workspace, &L, stream);
+  kvc::prof_mark(KVC_STAGE_TOTAL, true, stream);
+  return e == hipSuccess ? KVC_OK : KVC_EHIP;
+}
+
+int kvc_fit(const kvc_params_t* p, const void* Q_ref, const void* K, const void* V,
+            const int32_t* idx, float* out_bias, float* out_V, int32_t* out_status,
+            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc = common_checks(p, Q_ref, K, V, out_bias, out_V, workspace, workspace_bytes);
+  if (rc) return rc;
+  if (!aligned(idx) || (out_status && !aligned(out_status))) return KVC_EINVAL;
+  const Layout L = make_layout(p);
+  int32_t* status = out_status ? out_status : at<int32_t>(workspace, L.status);
+  kvc::prof_mark(KVC_STAGE_TOTAL, false, stream);
+  hipError_t e = kvc::launch_fill_i32(status, 0, p->B, stream);
+  if (e == hipSuccess) e = dispatch<ScoreOp>(p, Q_ref, K, V, workspace, &L, stream);
+  if (e == hipSuccess)
+    e = dispatch<FitOp>(p, Q_ref, K, V, idx, out_bias, out_V, status, workspace, &L, stream);
+  kvc::prof_mark(KVC_STAGE_TOTAL, true, stream);
+  return e == hipSuccess ? KVC_OK : KVC_EHIP;
+}
+
+int kvc_profile_enable(uint32_t stage_mask) {
+  g_prof.mask = stage_mask & ((1u << KVC_NUM_STAGES) - 1);
+  for (int s = 0; s < KVC_NUM_STAGES; ++s) g_prof.used[s] = 0;
+  return KVC_OK;
+}
+
+int kvc_profile_read(int stage, double* total_ms, int64_t* launches) {
+  if (stage < 0 || stage >= KVC_NUM_STAGES || !total_ms || !launches) return KVC_EINVAL;
+  const auto& v = g_prof.ev[stage];
+  const size_t pairs = g_prof.used[stage] / 2;
+  double sum = 0.0;
+  for (size_t i = 0; i < pairs; ++i) {
+    if (hipEventSynchronize(v[2 * i + 1]) != hipSuccess) return KVC_EHIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, v[2 * i], v[2 * i + 1]) != hipSuccess) return KVC_EHIP;
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = static_cast<int64_t>(pairs);
+  return KVC_OK;
+}
+
+const char* kvc_strerror(int code) {
+  switch (code) {
+    case KVC_OK: return "ok";
+    case KVC_EINVAL: return "invalid argument (null/misaligned pointer, bad size or enum)";
+    case KVC_EWORKSPACE: return "workspace smaller than kvc_workspace_bytes()";
+    case KVC_EHIP: return "HIP launch failed";
+    case KVC_EUNSUPPORTED: return "unsupported configuration";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,32 @@
+// Host-callable launchers of the kernels (each enqueues on the given stream
+// and returns hipGetLastError()).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvc {
+using bf16_t = uint16_t;
+
+template <class In, int D>
+hipError_t launch_score(const void* Q, const void* K, const void* V, float2* ml, float* lse,
+                        float* Opart, float* O, float* imp_part, float* imp, int B, int n, int T,
+                        int nsplit1, int kps1, int nsplit2, int kps2, bool rms, hipStream_t st);
+hipError_t launch_select(const float* imp, int32_t* idx, int32_t* status, int B, int T, int t,
+                         hipStream_t st);
+hipError_t launch_gather(const void* K, const int32_t* idx, void* outK, int B, int T, int t,
+                         int row_bytes, hipStream_t st);
+hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t count, hipStream_t st);
+
+// Float64 work buffers of the fits (device pointers into the workspace).
+struct FitBufs {
+  double *PS, *H, *W, *cvec, *xs, *R, *wv, *lam;
+  int32_t *mask, *Fidx, *inv, *msz, *state;
+};
+template <class In, int D>
+hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const float* lse,
+                      const float* O, const int32_t* idx, FitBufs fb, float* out_bias,
+                      float* out_V, int32_t* status, int B, int n, int T, int t, double ridge,
+                      int max_iters, hipStream_t st);
+// Event-pair instrumentation (defined with the C ABI): no-op unless enabled.
+void prof_mark(int stage, bool end, hipStream_t st);
+}  // namespace kvc

@@ -1,0 +1,167 @@
+// Key selection and gather.
+//
+// "Fast KV Compaction via Attention Matching", section 2, algorithmic
+// pipeline: keep the original keys with the highest aggregated attention.
+// The ranking key is the per-key sum over reference queries of p^2 (RMS
+// aggregation) or p (mean); the page's sqrt(./n) and ./n are monotone and do
+// not change the order.  Equal values go to the lower index, and the kept
+// indices are emitted in ascending order so the compacted cache keeps the
+// positional order of the original (a contiguous re-indexing of the survivors).
+//
+//   k_select   one workgroup per head: MSB-first radix select over the
+//              uint32 bit patterns of the (non-negative) importances finds the
+//              t-th largest value tau exactly; an order-preserving block scan
+//              then keeps every value > tau and the lowest-index values == tau.
+//   k_gather   C_k = K[idx] (exact copies, input dtype).
+#include "common.h"
+#include "launch.h"
+
+namespace kvc {
+
+constexpr int kSelThreads = 1024;
+
+// Exclusive prefix sum over the block (kSelThreads threads), returns the
+// total in *total.  Deterministic (integer).
+__device__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kSelThreads / 64 ? scratch[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(w, off);
+      if (lane >= off) w += y;
+    }
+    if (lane < kSelThreads / 64) scratch[32 + lane] = w;  // inclusive wave totals
+  }
+  __syncthreads();
+  const int before = (wave ? scratch[32 + wave - 1] : 0) + x - v;
+  *total = scratch[32 + kSelThreads / 64 - 1];
+  __syncthreads();
+  return before;
+}
+
+// grid (B), block kSelThreads.  imp [B][T] (non-negative floats), idx [B][t].
+// status[b] |= 4 if an importance is not finite (NaN/Inf input upstream).
+__global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict__ imp,
+                                                        int32_t* __restrict__ idx,
+                                                        int32_t* __restrict__ status, int T,
+                                                        int t) {
+  __shared__ unsigned int hist[256];
+  __shared__ int scratch[64];
+  __shared__ unsigned int s_prefix, s_mask;
+  __shared__ int s_need, s_bad;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const unsigned int* u = reinterpret_cast<const unsigned int*>(imp) + static_cast<size_t>(b) * T;
+
+  if (tid == 0) {
+    s_prefix = 0;
+    s_mask = 0;
+    s_need = t;
+    s_bad = 0;
+  }
+  __syncthreads();
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+    __syncthreads();
+    const unsigned int prefix = s_prefix, mask = s_mask;
+    for (int j = tid; j < T; j += kSelThreads) {
+      const unsigned int v = u[j];
+      if (shift == 24 && v >= 0x7f800000u) s_bad = 1;  // inf / nan (non-negative inputs)
+      if ((v & mask) == prefix) atomicAdd(&hist[(v >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int need = s_need;
+      unsigned int cum = 0;
+      int digit = 0;
+      for (int bin = 255; bin >= 0; --bin) {
+        const unsigned int h = hist[bin];
+        if (cum + h >= static_cast<unsigned int>(need)) {
+          digit = bin;
+          break;
+        }
+        cum += h;
+      }
+      s_need = need - static_cast<int>(cum);
+      s_prefix = prefix | (static_cast<unsigned int>(digit) << shift);
+      s_mask = mask | (255u << shift);
+    }
+    __syncthreads();
+  }
+  const unsigned int tau = s_prefix;
+  const int need_eq = s_need;  // how many values equal to tau are kept
+
+  // order-preserving compaction over contiguous chunks
+  const int chunk = (T + kSelThreads - 1) / kSelThreads;
+  const int c0 = min(T, tid * chunk), c1 = min(T, c0 + chunk);
+  int n_gt = 0, n_eq = 0;
+  for (int j = c0; j < c1; ++j) {
+    const unsigned int v = u[j];
+    n_gt += v > tau;
+    n_eq += v == tau;
+  }
+  int tot;
+  const int eq_before = block_exclusive_scan(n_eq, scratch, &tot);
+  const int take_eq = max(0, min(n_eq, need_eq - eq_before));
+  const int pos0 = block_exclusive_scan(n_gt + take_eq, scratch, &tot);
+  int32_t* out = idx + static_cast<size_t>(b) * t;
+  int pos = pos0, eq_taken = 0;
+  for (int j = c0; j < c1; ++j) {
+    const unsigned int v = u[j];
+    bool keep = v > tau;
+    if (v == tau && eq_taken < take_eq) {
+      keep = true;
+      ++eq_taken;
+    }
+    if (keep) out[pos++] = j;
+  }
+  if (tid == 0 && status && s_bad) status[b] |= 4;
+}
+
+// out_K[b][a][:] = K[b][idx[b][a]][:].  grid (ceil(t*D*es/16/256), B).
+__global__ void k_gather_rows(const uint4* __restrict__ K, const int32_t* __restrict__ idx,
+                              uint4* __restrict__ out, int T, int t, int row_vecs) {
+  const int b = blockIdx.y;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= t * row_vecs) return;
+  const int a = i / row_vecs, c = i % row_vecs;
+  const int j = idx[static_cast<size_t>(b) * t + a];
+  out[(static_cast<size_t>(b) * t + a) * row_vecs + c] =
+      K[(static_cast<size_t>(b) * T + j) * row_vecs + c];
+}
+
+__global__ void k_fill_i32(int32_t* __restrict__ p, int32_t v, size_t count) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < count) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t count, hipStream_t st) {
+  hipLaunchKernelGGL(k_fill_i32, dim3((count + 255) / 256), dim3(256), 0, st, p, v, count);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const float* imp, int32_t* idx, int32_t* status, int B, int T, int t,
+                         hipStream_t st) {
+  hipLaunchKernelGGL(k_select, dim3(B), dim3(kSelThreads), 0, st, imp, idx, status, T, t);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const void* K, const int32_t* idx, void* outK, int B, int T, int t,
+                         int row_bytes, hipStream_t st) {
+  const int row_vecs = row_bytes / 16;
+  const int tot = t * row_vecs;
+  hipLaunchKernelGGL(k_gather_rows, dim3((tot + 255) / 256, B), dim3(256), 0, st,
+                     static_cast<const uint4*>(K), idx, static_cast<uint4*>(outK), T, t,
+                     row_vecs);
+  return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -1,0 +1,100 @@
+"""The C ABI loads, exports what include/kvc.h declares, and rejects bad
+arguments before enqueuing anything (host logic only: runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kv_cache_compaction_head_amd as kvc
+from kv_cache_compaction_head_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libkvc.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = kvc.load()
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_params_struct_layout_and_defaults():
+    assert ctypes.sizeof(_lib.Params) == 64
+    p = _lib.Params()
+    kvc.load().kvc_params_default(ctypes.byref(p))
+    assert p.in_dtype == _lib.KVC_BF16 and p.agg == _lib.KVC_AGG_RMS
+    assert p.ridge_rel == 1e-6 and p.max_nnls_iters == 32 and p.reserved == 0
+    assert p.B == p.T == p.n == p.d == p.t == 0
+
+
+@pytest.mark.parametrize("field,value", [("B", 0), ("T", 0), ("n", 0), ("d", 96), ("t", 0),
+                                         ("t", 1025), ("in_dtype", 7), ("agg", 3),
+                                         ("ridge_rel", 0.0), ("ridge_rel", float("nan")),
+                                         ("max_nnls_iters", 0), ("reserved", 1)])
+def test_invalid_params_have_no_workspace(field, value):
+    p = kvc.make_params(2, 1024, 64, 128, 16, "bf16")
+    assert kvc.workspace_bytes(p) > 0
+    setattr(p, field, value)
+    assert kvc.workspace_bytes(p) == 0
+    with pytest.raises(ValueError):
+        kvc.workspace_layout(p)
+
+
+def test_workspace_grows_with_problem_and_layout_is_aligned():
+    small = kvc.make_params(1, 512, 64, 64, 64, "f32")
+    big = kvc.make_params(8, 32768, 2048, 128, 655, "bf16")
+    assert 0 < kvc.workspace_bytes(small) < kvc.workspace_bytes(big)
+    L = kvc.workspace_layout(big)
+    for off in (L.lse, L.O, L.imp, L.w):
+        assert off % 256 == 0 and off < kvc.workspace_bytes(big)
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_argument_errors_return_before_enqueue():
+    """Null, misaligned and undersized arguments are rejected on the host; the
+    fake device addresses below are never dereferenced."""
+    lib = kvc.load()
+    p = kvc.make_params(2, 1024, 64, 128, 16, "bf16")
+    need = kvc.workspace_bytes(p)
+    A = [_fake(0x10000 * (i + 1)) for i in range(9)]
+
+    def call(params, ptrs, ws_bytes):
+        return lib.kvc_compact(ctypes.byref(params), *ptrs, ctypes.c_size_t(ws_bytes), None)
+
+    assert call(p, [None] + A[1:], need) == _lib.KVC_EINVAL
+    bad = list(A)
+    bad[3] = _fake(0x10008)  # misaligned out_K
+    assert call(p, bad, need) == _lib.KVC_EINVAL
+    assert call(p, A, need - 1) == _lib.KVC_EWORKSPACE
+    q = kvc.make_params(2, 1024, 64, 128, 2000, "bf16")  # t > T
+    assert call(q, A, need) == _lib.KVC_EINVAL
+    rc = lib.kvc_fit(ctypes.byref(p), A[0], A[1], A[2], None, A[4], A[5], None, A[8],
+                     ctypes.c_size_t(need), None)
+    assert rc == _lib.KVC_EINVAL
+    with pytest.raises(ValueError):
+        _lib.check(_lib.KVC_EWORKSPACE)
+    with pytest.raises(RuntimeError):
+        _lib.check(_lib.KVC_EHIP)
+    assert "workspace" in kvc.strerror(_lib.KVC_EWORKSPACE)
+
+
+def test_header_documents_each_entry_point():
+    src = open(HEADER).read()
+    assert "Fast KV Compaction via Attention Matching" in src
+    for name in _declared():
+        assert src.count(name) >= 1

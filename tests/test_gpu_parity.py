@@ -1,0 +1,126 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on
+the same seeded inputs.  Bars: kept indices identical up to near-ties below
+1e-6 relative importance gap; multipliers w, fitted values and the compacted
+attention output within 2e-3 relative L2 for bf16 inputs, 1e-4 for float32."""
+import numpy as np
+import pytest
+
+import oracle as orc
+import synth
+from parity import TOL_BF16, TOL_F32, compare_head, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _tol(w):
+    return TOL_F32 if w.dtype == "f32" else TOL_BF16
+
+
+SMALL = [
+    synth.CONFIGS[1],
+    synth.custom(1, 3, 1000, 200, 128, 77, "bf16", "clusters"),          # ragged T, n, t
+    synth.custom(2, 2, 4096, 256, 64, 100, "bf16", "channel_lognormal"),  # d = 64
+    synth.custom(3, 2, 777, 130, 128, 64, "f32", "sinks"),               # fp32, d = 128
+    synth.custom(4, 1, 2500, 384, 128, 250, "bf16", "student_t3"),
+    synth.custom(5, 4, 640, 64, 128, 1, "bf16", "normal"),               # t = 1
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_small_cases_match_oracle(w):
+    data = synth.batch(w)
+    gpu = run_gpu(w, data)
+    for h in range(w.B):
+        err = compare_head(gpu, h, data, w.t, _tol(w))
+        print(w.name, h, {k: (round(v, 9) if isinstance(v, float) else v) for k, v in err.items()},
+              flush=True)
+
+
+def test_mean_aggregator():
+    w = synth.custom(6, 2, 1500, 128, 128, 120, "bf16", "clusters")
+    data = synth.batch(w)
+    gpu = run_gpu(w, data, agg="mean")
+    for h in range(w.B):
+        compare_head(gpu, h, data, w.t, TOL_BF16, agg="mean")
+
+
+@pytest.mark.parametrize("n", [40, 130])
+def test_keep_everything_is_exact(n):
+    """t = T: every index kept, w = 1, C_v = V (the ridge prior makes this the
+    unique zero-loss point for any n).  The GPU's P_S rows carry the float32
+    log-sum-exp's rounding (~1e-7 relative); with n > T that perturbs the
+    least-squares point by about cond(P) * 1e-7, hence the 1e-4 bound."""
+    w = synth.custom(7, 2, 96, n, 128, 96, "bf16", "normal")
+    data = synth.batch(w)
+    gpu = run_gpu(w, data)
+    for h in range(w.B):
+        assert list(gpu["idx"][h]) == list(range(96))
+        assert np.allclose(gpu["w"][h], 1.0, atol=1e-4)
+        V = synth.to_f64(data["V"][h])
+        assert orc.rel_l2(gpu["values"][h], V) < 1e-4
+
+
+def test_zero_queries_tie_rule_and_closed_form():
+    """q = 0: all importances tie -> indices 0..t-1; w = (T + rho)/(t + rho)."""
+    w = synth.custom(8, 2, 700, 64, 128, 50, "bf16", "normal")
+    data = synth.batch(w)
+    data["Q"][:] = 0
+    gpu = run_gpu(w, data, ridge_rel=1e-2)
+    for h in range(w.B):
+        assert list(gpu["idx"][h]) == list(range(50))
+        assert np.allclose(gpu["w"][h], (700 + 1e-2) / (50 + 1e-2), rtol=1e-6)
+
+
+def test_duplicated_keys_fit_recovers_multiplicities():
+    """kvc_fit on the first copies of t distinct keys repeated m_j times:
+    w_j = m_j and C_v,j = mean of V over the copies (ridge -> 0)."""
+    import torch
+    import kv_cache_compaction_head_amd as kvc
+    rng = np.random.default_rng(9)
+    t, d = 6, 128
+    mult = np.array([1, 3, 2, 5, 1, 4])
+    rows = rng.permutation(np.repeat(np.arange(t), mult))
+    base = rng.standard_normal((t, d)) * 0.7
+    K = synth.round_bf16_bits(base[rows])
+    V = synth.round_bf16_bits(rng.standard_normal((rows.size, d)))
+    Q = synth.round_bf16_bits(rng.standard_normal((64, d)) / np.sqrt(d))
+    first = np.sort([np.flatnonzero(rows == j)[0] for j in range(t)])
+    res = kvc.fit(to_device(Q[None]), to_device(K[None]), to_device(V[None]),
+                  torch.from_numpy(first.astype(np.int32)[None]).cuda(), ridge_rel=1e-12)
+    torch.cuda.synchronize()
+    wgpu = kvc.intermediates(res)["w"].cpu().numpy()[0]
+    assert np.allclose(wgpu, mult[rows[first]], rtol=1e-6)
+    Vf = synth.to_f64(V)
+    means = np.array([Vf[rows == rows[j]].mean(axis=0) for j in first])
+    assert orc.rel_l2(res.values.cpu().numpy()[0], means) < 1e-5
+
+
+def test_bitwise_deterministic():
+    w = synth.custom(10, 2, 3000, 300, 128, 90, "bf16", "clusters")
+    data = synth.batch(w)
+    a, b = run_gpu(w, data), run_gpu(w, data)
+    for k in ("idx", "bias", "values", "lse", "O", "imp", "w"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_nonfinite_input_is_flagged():
+    w = synth.custom(11, 2, 512, 64, 128, 16, "bf16", "normal")
+    data = synth.batch(w)
+    data["K"][1, 3, 5] = 0x7FC0  # NaN in head 1
+    gpu = run_gpu(w, data)
+    assert gpu["status"][0] == 0
+    assert gpu["status"][1] & 4
+
+
+@pytest.mark.parametrize("cfg,heads", [(2, [0, 7]), (3, [0, 5]), (4, [0, 131, 255])])
+def test_full_configs_sampled_heads(cfg, heads):
+    """The full-size workloads, launched exactly as the benchmark times them;
+    the oracle checks a sample of heads."""
+    w = synth.CONFIGS[cfg]
+    data = synth.batch(w)
+    gpu = run_gpu(w, data)
+    assert (gpu["status"] == 0).all(), gpu["status"]
+    for h in heads:
+        err = compare_head(gpu, h, data, w.t, _tol(w), tight=False)
+        print(f"C{cfg} head {h}:", {k: (float(f"{v:.3g}") if isinstance(v, float) else v)
+                                    for k, v in err.items()}, flush=True)

@@ -56,6 +56,8 @@ extern "C" {
 #define KVC_STATUS_NOT_SPD       1  /* a Cholesky pivot was <= 0                */
 #define KVC_STATUS_NNLS_CAP      2  /* NNLS stopped at max_nnls_iters           */
 #define KVC_STATUS_NONFINITE     4  /* a non-finite value reached the fits      */
+#define KVC_STATUS_SYNC_TIMEOUT  8  /* a fit team's barrier wait ran out (the
+                                       head's fit is incomplete)               */
 
 typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype_t;
 typedef enum { KVC_AGG_RMS = 0, KVC_AGG_MEAN = 1 } kvc_agg_t;
@@ -65,7 +67,7 @@ typedef struct {
   int64_t T;              /* cache length per head, >= 1                          */
   int64_t n;              /* reference queries per head, >= 1                     */
   int64_t d;              /* head dim: 64 or 128                                  */
-  int64_t t;              /* kept keys per head, 1 <= t <= T, t <= 8192           */
+  int64_t t;              /* kept keys per head, 1 <= t <= T, t <= 4096           */
   int32_t in_dtype;       /* kvc_dtype_t of Q_ref, K, V (out_K has the same)      */
   int32_t agg;            /* kvc_agg_t, default KVC_AGG_RMS                       */
   double  ridge_rel;      /* ridge weight relative to the Gram's mean diagonal,
@@ -106,7 +108,7 @@ int kvc_fit(const kvc_params_t* p, const void* Q_ref, const void* K, const void*
 
 /* Where the intermediates of the last call live inside its workspace (byte
  * offsets), for inspection after the stream completes:
- *   lse [B, n] f32; O [B, n, d] f32 (full-cache output); imp [B, T] f32 holding
+ *   lse [B, n] f64; O [B, n, d] f32 (full-cache output); imp [B, T] f32 holding
  *   sum_i p_ij^2 (RMS) or sum_i p_ij (mean) -- the ranking key before the
  *   monotone sqrt(./n) or ./n; w [B, t] f64 the NNLS multipliers. */
 typedef struct {

@@ -118,7 +118,7 @@ def fit(Q, K, V, idx, *, ridge_rel: float = 1e-6, max_nnls_iters: int = 32,
 
 
 def intermediates(res: Compacted) -> dict:
-    """Views into the workspace: lse [B,n], O [B,n,d], imp [B,T] (sum of p^2 or
+    """Views into the workspace: lse [B,n] (float64), O [B,n,d], imp [B,T] (sum of p^2 or
     p per key), w [B,t] (float64 NNLS multipliers).  Synchronise first."""
     import torch
     p = res.params
@@ -130,7 +130,7 @@ def intermediates(res: Compacted) -> dict:
         nbytes = count * torch.tensor([], dtype=dtype).element_size()
         return ws[off:off + nbytes].view(dtype).view(*shape)
 
-    return {"lse": view(L.lse, B * n, torch.float32, (B, n)),
+    return {"lse": view(L.lse, B * n, torch.float64, (B, n)),
             "O": view(L.O, B * n * d, torch.float32, (B, n, d)),
             "imp": view(L.imp, B * T, torch.float32, (B, T)),
             "w": view(L.w, B * t, torch.float64, (B, t))}

@@ -83,7 +83,7 @@ __device__ __forceinline__ void tri_decode(int bid, int& ty, int& tx) {
 template <class In, int D>
 __global__ __launch_bounds__(256) void k_ps(const In* __restrict__ Q, const In* __restrict__ K,
                                             const int32_t* __restrict__ idx,
-                                            const float* __restrict__ lse,
+                                            const double* __restrict__ lse,
                                             double* __restrict__ PS, int n, int T, int t,
                                             int tiles_a) {
   __shared__ double sA[kKC * kTile], sB[kKC * kTile];
@@ -114,14 +114,17 @@ __global__ __launch_bounds__(256) void k_ps(const In* __restrict__ Q, const In* 
         const int r = i0 + tile_row(wave, lane, ra, i), a = a0 + tile_col(wave, lane, rb);
         if (r < n && a < t)
           PS[(static_cast<size_t>(b) * n + r) * t + a] =
-              exp(acc[ra][rb][i] - static_cast<double>(lse[static_cast<size_t>(b) * n + r]));
+              exp(acc[ra][rb][i] - lse[static_cast<size_t>(b) * n + r]);
       }
 }
 
 // ---------------------------------------------------------------------------
-// C[b][a][c] = sum_i A[b][i][ca(a)] * Bm[b][i][cb(c)]  for a < mA_b, c < mB_b.
-// ca/cb: optional per-head column index maps.  SYM: B = A, lower tiles only,
-// mirrored.  grid (tiles, B).
+// C[b][a][c] = sum_i A[b][i][ca(a)] * Bm[b][i][c]  for a < mA_b, c < mB_b.
+// ca: optional per-head column map of A.  SYM: B = A, lower tiles only,
+// mirrored.  grid (tiles, ksplit, B): with ksplit > 1 each workgroup sums a
+// slice of the rows into part[b][split][tile][64*64] and k_atb_reduce adds
+// the slices in order.  The next 16-row chunk is fetched into registers while
+// the MFMAs consume the current one.
 // ---------------------------------------------------------------------------
 template <class TB, bool SYM>
 __global__ __launch_bounds__(256) void k_atb(const double* __restrict__ A, size_t sA, int lda,
@@ -129,9 +132,10 @@ __global__ __launch_bounds__(256) void k_atb(const double* __restrict__ A, size_
                                              const TB* __restrict__ Bm, size_t sB, int ldb,
                                              double* __restrict__ C, size_t sC, int ldc,
                                              int nrows, const int32_t* __restrict__ msz,
-                                             int mA_const, int mB_const, int tiles_x) {
+                                             int mA_const, int mB_const, int tiles_x,
+                                             double* __restrict__ part, int ntiles) {
   __shared__ double sAt[kKC * kTile], sBt[kKC * kTile];
-  const int b = blockIdx.y;
+  const int b = blockIdx.z, split = blockIdx.y, ksplit = gridDim.y;
   const int mA = msz ? msz[b] : mA_const;
   const int mB = SYM ? mA : mB_const;
   int ty, tx;
@@ -146,50 +150,128 @@ __global__ __launch_bounds__(256) void k_atb(const double* __restrict__ A, size_
   const double* Ab = A + b * sA;
   const TB* Bb = Bm + b * sB;
   const int32_t* ca = colA ? colA + b * sColA : nullptr;
+  // this slice's rows, whole 16-row chunks
+  const int nchunk = (nrows + kKC - 1) / kKC;
+  const int per = (nchunk + ksplit - 1) / ksplit;
+  const int k0 = split * per * kKC, k1 = min(nrows, (split + 1) * per * kKC);
+  constexpr int NE = kKC * kTile / 256;
+  int colA_r[NE], colB_r[NE];
+#pragma unroll
+  for (int q = 0; q < NE; ++q) {
+    const int r = (threadIdx.x + q * 256) % kTile;
+    const int a = a0 + r, c = c0 + r;
+    colA_r[q] = a < mA ? (ca ? ca[a] : a) : -1;
+    colB_r[q] = c < mB ? (SYM ? (ca ? ca[c] : c) : c) : -1;
+  }
+  double va[NE], vb[NE];
+  auto fetch = [&](int kbase) {
+#pragma unroll
+    for (int q = 0; q < NE; ++q) {
+      const int e = threadIdx.x + q * 256, i = kbase + e / kTile;
+      va[q] = (i < k1 && colA_r[q] >= 0) ? Ab[static_cast<size_t>(i) * lda + colA_r[q]] : 0.0;
+      if (SYM)
+        vb[q] = (i < k1 && colB_r[q] >= 0) ? Ab[static_cast<size_t>(i) * lda + colB_r[q]] : 0.0;
+      else
+        vb[q] = (i < k1 && colB_r[q] >= 0)
+                    ? static_cast<double>(Bb[static_cast<size_t>(i) * ldb + colB_r[q]])
+                    : 0.0;
+    }
+  };
   f64x4 acc[2][2] = {};
-  for (int k0 = 0; k0 < nrows; k0 += kKC) {
+  if (k0 < k1) fetch(k0);
+  for (int k = k0; k < k1; k += kKC) {
     __syncthreads();
-    for (int e = threadIdx.x; e < kKC * kTile; e += 256) {
-      const int k = e / kTile, r = e % kTile;
-      const int i = k0 + k;
-      const int a = a0 + r, c = c0 + r;
-      double va = 0.0, vb = 0.0;
-      if (i < nrows) {
-        if (a < mA) va = Ab[static_cast<size_t>(i) * lda + (ca ? ca[a] : a)];
-        if (SYM) {
-          if (c < mB) vb = Ab[static_cast<size_t>(i) * lda + (ca ? ca[c] : c)];
-        } else if (c < mB) {
-          vb = static_cast<double>(Bb[static_cast<size_t>(i) * ldb + c]);
-        }
-      }
-      sAt[k * kTile + r] = va;
-      sBt[k * kTile + r] = vb;
+#pragma unroll
+    for (int q = 0; q < NE; ++q) {
+      const int e = threadIdx.x + q * 256;
+      sAt[e] = va[q];
+      sBt[e] = vb[q];
     }
     __syncthreads();
+    if (k + kKC < k1) fetch(k + kKC);
     tile_mma(sAt, sBt, acc, wave, lane);
   }
-  double* Cb = C + b * sC;
+  if (ksplit == 1) {
+    double* Cb = C + b * sC;
 #pragma unroll
-  for (int ra = 0; ra < 2; ++ra)
+    for (int ra = 0; ra < 2; ++ra)
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = a0 + tile_row(wave, lane, ra, i), c = c0 + tile_col(wave, lane, rb);
-        if (r < mA && c < mB) {
-          Cb[static_cast<size_t>(r) * ldc + c] = acc[ra][rb][i];
-          if (SYM && tx != ty) Cb[static_cast<size_t>(c) * ldc + r] = acc[ra][rb][i];
+        for (int i = 0; i < 4; ++i) {
+          const int r = a0 + tile_row(wave, lane, ra, i), c = c0 + tile_col(wave, lane, rb);
+          if (r < mA && c < mB) {
+            Cb[static_cast<size_t>(r) * ldc + c] = acc[ra][rb][i];
+            if (SYM && tx != ty) Cb[static_cast<size_t>(c) * ldc + r] = acc[ra][rb][i];
+          }
         }
-      }
+  } else {
+    double* P = part + ((static_cast<size_t>(b) * ksplit + split) * ntiles + blockIdx.x) * (kTile * kTile);
+#pragma unroll
+    for (int ra = 0; ra < 2; ++ra)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          P[tile_row(wave, lane, ra, i) * kTile + tile_col(wave, lane, rb)] = acc[ra][rb][i];
+  }
 }
 
-// Column sums of P_S: colsum[b][a] = sum_i P_S[b][i][a].  grid (ceil(t/256), B).
-__global__ void k_colsum(const double* __restrict__ PS, double* __restrict__ out, int n, int t) {
+// Sum the ksplit row slices of each tile in order and store (mirrored for
+// symmetric products).  grid (tiles, B), block 256.
+template <bool SYM>
+__global__ __launch_bounds__(256) void k_atb_reduce(const double* __restrict__ part,
+                                                    double* __restrict__ C, size_t sC, int ldc,
+                                                    const int32_t* __restrict__ msz, int mA_const,
+                                                    int mB_const, int tiles_x, int ntiles,
+                                                    int ksplit) {
+  const int b = blockIdx.y;
+  const int mA = msz ? msz[b] : mA_const;
+  const int mB = SYM ? mA : mB_const;
+  int ty, tx;
+  if (SYM) tri_decode(blockIdx.x, ty, tx);
+  else {
+    ty = blockIdx.x / tiles_x;
+    tx = blockIdx.x % tiles_x;
+  }
+  const int a0 = ty * kTile, c0 = tx * kTile;
+  if (a0 >= mA || c0 >= mB) return;
+  double* Cb = C + b * sC;
+  const double* P = part + (static_cast<size_t>(b) * ksplit * ntiles + blockIdx.x) * (kTile * kTile);
+  for (int e = threadIdx.x; e < kTile * kTile; e += 256) {
+    const int r = a0 + e / kTile, c = c0 + e % kTile;
+    double v = 0.0;
+    for (int sp = 0; sp < ksplit; ++sp) v += P[static_cast<size_t>(sp) * ntiles * kTile * kTile + e];
+    if (r < mA && c < mB) {
+      Cb[static_cast<size_t>(r) * ldc + c] = v;
+      if (SYM && tx != ty) Cb[static_cast<size_t>(c) * ldc + r] = v;
+    }
+  }
+}
+
+// Column sums of P_S in two fixed-order stages: partial sums over 256-row
+// slabs, then over slabs.  grid (ceil(t/64), ceil(n/256), B), block (64, 4).
+__global__ void k_colsum_part(const double* __restrict__ PS, double* __restrict__ part, int n,
+                              int t) {
+  __shared__ double sh[4][64];
+  const int b = blockIdx.z, a = blockIdx.x * 64 + threadIdx.x;
+  const int i0 = blockIdx.y * 256, i1 = min(n, i0 + 256);
+  double s = 0.0;
+  if (a < t)
+    for (int i = i0 + threadIdx.y; i < i1; i += 4) s += PS[(static_cast<size_t>(b) * n + i) * t + a];
+  sh[threadIdx.y][threadIdx.x] = s;
+  __syncthreads();
+  if (threadIdx.y == 0 && a < t)
+    part[(static_cast<size_t>(b) * gridDim.y + blockIdx.y) * t + a] =
+        ((sh[0][threadIdx.x] + sh[1][threadIdx.x]) + sh[2][threadIdx.x]) + sh[3][threadIdx.x];
+}
+
+__global__ void k_colsum_final(const double* __restrict__ part, double* __restrict__ out, int nslab,
+                               int t) {
   const int b = blockIdx.y, a = blockIdx.x * blockDim.x + threadIdx.x;
   if (a >= t) return;
-  const double* p = PS + static_cast<size_t>(b) * n * t + a;
   double s = 0.0;
-  for (int i = 0; i < n; ++i) s += p[static_cast<size_t>(i) * t];
+  for (int k = 0; k < nslab; ++k) s += part[(static_cast<size_t>(b) * nslab + k) * t + a];
   out[static_cast<size_t>(b) * t + a] = s;
 }
 
@@ -266,179 +348,323 @@ __global__ __launch_bounds__(1024) void k_bias_prep(double* __restrict__ H,
   }
 }
 
-// Passive index list and its size; rhs = c[F].  grid (B), block 1024.
-__global__ __launch_bounds__(1024) void k_bpp_index(const int32_t* __restrict__ mask,
-                                                    const double* __restrict__ cvec,
-                                                    const int32_t* __restrict__ state,
-                                                    int32_t* __restrict__ Fidx,
-                                                    int32_t* __restrict__ inv,
-                                                    int32_t* __restrict__ msz,
-                                                    double* __restrict__ rhs, int t) {
-  __shared__ int scr[64];
-  const int b = blockIdx.x;
-  if (state && state[4 * b]) {
-    if (threadIdx.x == 0) msz[b] = 0;  // nothing to factor this round
+// ---------------------------------------------------------------------------
+// Teams.  The iterative parts of the fits (the pivoting rounds of the NNLS and
+// the value system's factorization and solve) run in one cooperative launch:
+// each head gets a team of g co-resident workgroups synchronised by
+// team_sync, a barrier through a counter in global memory.
+//
+// Placement and coherence: workgroups are dispatched round-robin over the
+// XCDs, so with nteams a multiple of 8, team = blockIdx mod nteams keeps a
+// team on one XCD, sharing one L2.  At start every member records its
+// hardware XCC id.  If a team's members all match, its barrier only has every
+// wave wait for its stores (which write through the CU's L1 into the shared
+// L2) and, after the wait, invalidates the CU's L1 so later loads see the
+// other members' data.  Otherwise the team falls back to agent-scope fences
+// (L2 write-back and invalidate), which are correct for any placement.  The
+// few control words (sizes, tolerances, pivoting state) are always read and
+// written with agent-scope atomics.
+//
+// Every wait is bounded by the constant-rate wall clock; a wait that runs out
+// raises a flag that turns every later wait into a no-op and flags the heads,
+// so no workgroup can spin forever.
+// ---------------------------------------------------------------------------
+constexpr uint64_t kSpinTicks = 2000000000ull;  // 20 s at the 100 MHz wall clock
+constexpr int kXcds = 8;                        // round-robin dispatch period
+
+// bulk data: ordinary accesses (made coherent by team_sync)
+__device__ __forceinline__ double ldc(const double* p) { return *p; }
+__device__ __forceinline__ int ldc(const int32_t* p) { return *p; }
+__device__ __forceinline__ void stc(double* p, double v) { *p = v; }
+__device__ __forceinline__ void stc(int32_t* p, int v) { *p = v; }
+// control words: agent-scope atomics
+__device__ __forceinline__ double lda(const double* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int lda(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void sta(double* p, double v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void sta(int32_t* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct Team {
+  int rank, size;
+  unsigned* ctr;
+  unsigned gen;
+  int* err;
+  bool fast;
+};
+
+__device__ __forceinline__ int hw_xcc_id() {
+  return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xf;  // HW_REG_XCC_ID[3:0]
+}
+
+__device__ void team_sync(Team& tm) {
+  if (tm.size == 1) {
+    __syncthreads();
     return;
   }
-  const int32_t* mk = mask + static_cast<size_t>(b) * t;
-  const int chunk = (t + blockDim.x - 1) / blockDim.x;
-  const int c0 = min(t, static_cast<int>(threadIdx.x) * chunk), c1 = min(t, c0 + chunk);
-  int cnt = 0;
-  for (int j = c0; j < c1; ++j) cnt += mk[j] != 0;
-  // exclusive scan over the block
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int x = cnt;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) scr[wave] = x;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are done
   __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += scr[w];
-  int pos = base + x - cnt;
-  for (int j = c0; j < c1; ++j) {
-    if (mk[j]) {
-      Fidx[static_cast<size_t>(b) * t + pos] = j;
-      inv[static_cast<size_t>(b) * t + j] = pos;
-      if (rhs) rhs[static_cast<size_t>(b) * t + pos] = cvec[static_cast<size_t>(b) * t + j];
-      ++pos;
-    } else {
-      inv[static_cast<size_t>(b) * t + j] = -1;
-    }
-  }
-  if (threadIdx.x == blockDim.x - 1) {
-    int tot = 0;
-    for (int w = 0; w < nw; ++w) tot += scr[w];
-    msz[b] = tot;
-  }
-}
-
-// W[a][a'] = H[F[a]][F[a']] for a' <= a < m.  grid (ceil(t*t/256), B).
-__global__ void k_gather_sub(const double* __restrict__ H, const int32_t* __restrict__ Fidx,
-                             const int32_t* __restrict__ msz, double* __restrict__ W, int t) {
-  const int b = blockIdx.y, m = msz[b];
-  const size_t e = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int a = static_cast<int>(e / t), a2 = static_cast<int>(e % t);
-  if (a >= m || a2 > a) return;
-  const int32_t* F = Fidx + static_cast<size_t>(b) * t;
-  W[(static_cast<size_t>(b) * t + a) * t + a2] =
-      H[(static_cast<size_t>(b) * t + F[a]) * t + F[a2]];
-}
-
-// ---------------------------------------------------------------------------
-// Blocked right-looking Cholesky, panel width 64, lower triangle in place.
-// Per panel k: k_trsm_panel solves the rows below the (already factored)
-// diagonal block, then k_syrk_update subtracts the panel's outer product from
-// the trailing lower tiles; the workgroup that owns trailing tile (0,0) -- the
-// next diagonal block -- also factors it, so every diagonal block is factored
-// by exactly one workgroup after its last update.  A non-positive pivot sets
-// status bit 1 and is replaced by 1 (the head is flagged, never NaN).
-// ---------------------------------------------------------------------------
-typedef double DiagBlock[kNB][kNB + 1];
-
-// Factor sD[0:kb][0:kb] (lower) in place; thread r owns row r.  All threads of
-// the block must call it.
-__device__ void factor_diag(DiagBlock& sD, int kb, int32_t* status, int b) {
-  const int r = threadIdx.x;
-  for (int c = 0; c < kb; ++c) {
-    if (r == c) {
-      double dv = sD[c][c];
-      if (!(dv > 0.0)) {
-        if (status) status[b] |= 1;
-        dv = 1.0;
+  if (threadIdx.x == 0) {
+    if (!tm.fast) __threadfence();
+    atomicAdd(tm.ctr, 1u);
+    const unsigned target = (tm.gen + 1) * static_cast<unsigned>(tm.size);
+    const uint64_t t0 = wall_clock64();
+    while (__hip_atomic_load(tm.ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (__hip_atomic_load(tm.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+      if (wall_clock64() - t0 > kSpinTicks) {
+        atomicOr(tm.err, 1);
+        break;
       }
-      sD[c][c] = sqrt(dv);
+      __builtin_amdgcn_s_sleep(1);
     }
-    __syncthreads();
-    if (r > c && r < kb) sD[r][c] /= sD[c][c];
-    __syncthreads();
-    if (r > c && r < kb) {
-      const double lrc = sD[r][c];
-      for (int j = c + 1; j <= r; ++j) sD[r][j] -= lrc * sD[j][c];
-    }
-    __syncthreads();
+    if (tm.fast) asm volatile("buffer_inv sc1" ::: "memory");
+    else __threadfence();
   }
+  tm.gen++;
+  __syncthreads();
 }
 
-// Factor the first diagonal block of each head.  grid (B), block 256.
-__global__ __launch_bounds__(256) void k_potrf_first(double* __restrict__ W, int ld,
-                                                     const int32_t* __restrict__ msz,
-                                                     int32_t* __restrict__ status) {
-  __shared__ DiagBlock sD;
-  const int b = blockIdx.x, m = msz[b];
-  if (m <= 0) return;
-  const int kb = min(kNB, m);
-  double* Wb = W + static_cast<size_t>(b) * ld * ld;
-  for (int e = threadIdx.x; e < kNB * kNB; e += blockDim.x) {
-    const int r = e / kNB, c = e % kNB;
-    sD[r][c] = (r < kb && c <= r) ? Wb[static_cast<size_t>(r) * ld + c] : 0.0;
+// Team of this workgroup from the XCD-aligned mapping, then one agent-fenced
+// barrier to compare the members' XCC ids (fast barrier if they all match).
+__device__ void team_setup(Team& tm, int& team, int& nteams, unsigned* bar, int* err, int* xcc,
+                           int tx) {
+  nteams = kXcds * tx;
+  team = static_cast<int>(blockIdx.x % nteams);
+  tm.rank = static_cast<int>(blockIdx.x / nteams);
+  tm.size = static_cast<int>(gridDim.x / nteams);
+  tm.ctr = bar + team;
+  tm.gen = 0;
+  tm.err = err;
+  tm.fast = false;
+  if (tm.size == 1) return;
+  __shared__ int s_ok;
+  if (threadIdx.x == 0) sta(&xcc[blockIdx.x], hw_xcc_id());
+  team_sync(tm);
+  if (threadIdx.x == 0) {
+    const int mine = lda(&xcc[blockIdx.x]);
+    int ok = 1;
+    for (int r = 0; r < tm.size; ++r) ok &= lda(&xcc[team + r * nteams]) == mine;
+    s_ok = ok;
   }
   __syncthreads();
-  factor_diag(sD, kb, status, b);
-  for (int e = threadIdx.x; e < kb * kb; e += blockDim.x) {
-    const int r = e / kb, c = e % kb;
-    if (c <= r) Wb[static_cast<size_t>(r) * ld + c] = sD[r][c];
+  tm.fast = s_ok != 0;
+}
+
+constexpr int kMaxTeamT = 4096;  // largest t the team kernels stage in LDS
+// Team kernels run 256 threads per workgroup; staging loops are unrolled on
+// that so every thread issues its loads back to back.
+constexpr int kTeamThreads = 256;
+
+struct __align__(16) TeamSmem {
+  double sx[kMaxTeamT];
+  int sF[kMaxTeamT];
+  double sD[kNB][kNB + 1];
+  double sA[kKC * kTile];
+  double sB[kKC * kTile];
+  double col[2][kNB];
+  double vec[4][kNB];
+  double dpiv[kNB];
+  double rdiag[kNB];
+  double red[16];
+  int ired[16];
+  int scan[64];
+};
+// The team kernels' LDS, at file scope so that the (non-inlined) helpers
+// address it as LDS rather than through generic pointers.
+__shared__ TeamSmem g_team_smem;
+
+
+// Factor sD[0:kb][0:kb] (lower) in place, 256 threads, in four 16-column
+// micro-panels.  Micro-panel p (columns 16p..16p+15, rows 16p..kb-1) is
+// factored by wave 0 alone: lane = row holds its 16 values in registers and
+// the pivot row's values are broadcast with readlane, so the 16 column steps
+// need no workgroup barrier.  The rank-16 update of the rows and columns
+// below then runs on all threads through LDS.  sm.rdiag receives 1/L[c][c].
+// A pivot <= 0 is replaced by 1 and flags status bit 1.
+__device__ __forceinline__ double bcast(double v, int lane) {
+  const long long u = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(u & 0xffffffff), lane);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(u >> 32), lane);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) |
+                              static_cast<unsigned int>(lo));
+}
+
+__device__ __noinline__ void factor_diag(int kb, int32_t* status, int b) {
+  TeamSmem& sm = g_team_smem;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int MP = 16;
+#pragma unroll 1
+  for (int p0 = 0; p0 < kb; p0 += MP) {
+    const int pw = min(MP, kb - p0);
+    if (wave == 0) {
+      double a[MP];
+      const int r = lane;  // row of the block
+      const bool live = r >= p0 && r < kb;
+#pragma unroll
+      for (int j = 0; j < MP; ++j) a[j] = (live && j < pw && p0 + j <= r) ? sm.sD[r][p0 + j] : 0.0;
+#pragma unroll
+      for (int c = 0; c < MP; ++c) {
+        if (c < pw) {
+          double piv = bcast(a[c], p0 + c);
+          const bool good = piv > 0.0;
+          if (!good) {
+            if (lane == 0 && status) atomicOr(&status[b], 1);
+            piv = 1.0;
+          }
+          const double d = sqrt(piv), id = 1.0 / d;
+          if (r == p0 + c) a[c] = d;
+          else if (live && r > p0 + c) a[c] *= id;
+          if (lane == 0) sm.rdiag[p0 + c] = id;
+#pragma unroll
+          for (int j = c + 1; j < MP; ++j) {
+            const double ljc = bcast(a[c], min(p0 + j, 63));
+            if (j < pw && live && r >= p0 + j) a[j] -= a[c] * ljc;
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < MP; ++j)
+        if (live && j < pw && p0 + j <= r) sm.sD[r][p0 + j] = a[j];
+    }
+    __syncthreads();
+    // rank-pw update of the trailing block rows/cols [p0+pw, kb)
+    const int s0 = p0 + pw, ns = kb - s0;
+    for (int e = tid; e < ns * ns; e += kTeamThreads) {
+      const int r = s0 + e / ns, j = s0 + e % ns;
+      if (j <= r) {
+        double v = sm.sD[r][j];
+#pragma unroll
+        for (int c = 0; c < MP; ++c)
+          if (c < pw) v -= sm.sD[r][p0 + c] * sm.sD[j][p0 + c];
+        sm.sD[r][j] = v;
+      }
+    }
+    __syncthreads();
   }
 }
 
-// L[i, k:k+64] = A[i, k:k+64] L_kk^{-T} for rows i >= k+64.  grid (nchunks, B).
-__global__ __launch_bounds__(256) void k_trsm_panel(double* __restrict__ W, int ld,
-                                                    const int32_t* __restrict__ msz, int k) {
-  __shared__ DiagBlock sD;
-  const int b = blockIdx.y, m = msz[b];
-  if (k + kNB >= m) return;
-  double* Wb = W + static_cast<size_t>(b) * ld * ld;
-  for (int e = threadIdx.x; e < kNB * kNB; e += blockDim.x) {
-    const int r = e / kNB, c = e % kNB;
-    sD[r][c] = c <= r ? Wb[static_cast<size_t>(k + r) * ld + k + c] : 0.0;
+
+__device__ void load_diag(const double* W, int ld, int k, int kb) {
+  TeamSmem& sm = g_team_smem;
+  double v[kNB * kNB / kTeamThreads];
+#pragma unroll
+  for (int i = 0; i < kNB * kNB / kTeamThreads; ++i) {
+    const int e = threadIdx.x + i * kTeamThreads, r = e >> 6, c = e & 63;
+    v[i] = (r < kb && c <= r) ? ldc(&W[static_cast<size_t>(k + r) * ld + k + c]) : 0.0;
+  }
+#pragma unroll
+  for (int i = 0; i < kNB * kNB / kTeamThreads; ++i) {
+    const int e = threadIdx.x + i * kTeamThreads;
+    sm.sD[e >> 6][e & 63] = v[i];
   }
   __syncthreads();
-  const int i = k + kNB + blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= m) return;
-  double* row = Wb + static_cast<size_t>(i) * ld + k;
-  double x[kNB];
-#pragma unroll
-  for (int c = 0; c < kNB; ++c) {
-    double v = row[c];
-    for (int e = 0; e < c; ++e) v -= x[e] * sD[c][e];
-    x[c] = v / sD[c][c];
-  }
-#pragma unroll
-  for (int c = 0; c < kNB; ++c) row[c] = x[c];
+  if (threadIdx.x < kNB) sm.rdiag[threadIdx.x] = threadIdx.x < kb ? 1.0 / sm.sD[threadIdx.x][threadIdx.x] : 0.0;
+  __syncthreads();
 }
 
-// Trailing update A[i][j] -= sum_c L[i][k+c] L[j][k+c] over the lower tiles
-// of the trailing block; tile (0,0) then factors the next diagonal block.
-// grid (tiles, B), block 256.
-__global__ __launch_bounds__(256) void k_syrk_update(double* __restrict__ W, int ld,
-                                                     const int32_t* __restrict__ msz, int k,
-                                                     int32_t* __restrict__ status) {
-  __shared__ double sAt[kKC * kTile], sBt[kKC * kTile];
-  __shared__ DiagBlock sD;
-  const int b = blockIdx.y, m = msz[b];
-  const int s0 = k + kNB;  // first trailing row
-  if (s0 >= m) return;
+__device__ void store_diag(double* W, int ld, int k, int kb) {
+  const TeamSmem& sm = g_team_smem;
+  for (int e = threadIdx.x; e < kNB * kNB; e += blockDim.x) {
+    const int r = e >> 6, c = e & 63;
+    if (r < kb && c <= r) stc(&W[static_cast<size_t>(k + r) * ld + k + c], sm.sD[r][c]);
+  }
+  __syncthreads();
+}
+
+// Rows [r0, r1) of the panel at column k: L[i, k:k+64] = A[i, k:k+64] L_kk^{-T}
+// with L_kk in sm.sD.  One thread per row; each half row (32 values) is loaded
+// in one batch before the substitution uses it.
+__device__ __noinline__ void trsm_rows(double* W, int ld, int k, int r0, int r1) {
+  const TeamSmem& sm = g_team_smem;
+  const int i = r0 + threadIdx.x;
+  if (i >= r1) return;
+  double* row = W + static_cast<size_t>(i) * ld + k;
+  constexpr int H = kNB / 2;
+  double x[H], y[H];
+#pragma unroll
+  for (int c = 0; c < H; ++c) x[c] = ldc(&row[c]);
+#pragma unroll
+  for (int c = 0; c < H; ++c) y[c] = ldc(&row[H + c]);
+// independent partial sums shorten the dependent chains 4x
+#pragma unroll
+  for (int c = 0; c < H; ++c) {
+    double v0 = x[c], v1 = 0.0, v2 = 0.0, v3 = 0.0;
+#pragma unroll
+    for (int e = 0; e + 3 < c; e += 4) {
+      v0 -= x[e] * sm.sD[c][e];
+      v1 -= x[e + 1] * sm.sD[c][e + 1];
+      v2 -= x[e + 2] * sm.sD[c][e + 2];
+      v3 -= x[e + 3] * sm.sD[c][e + 3];
+    }
+#pragma unroll
+    for (int e = c & ~3; e < c; ++e) v0 -= x[e] * sm.sD[c][e];
+    x[c] = ((v0 + v1) + (v2 + v3)) * sm.rdiag[c];
+  }
+#pragma unroll
+  for (int c = 0; c < H; ++c) {
+    double v0 = y[c], v1 = 0.0, v2 = 0.0, v3 = 0.0;
+#pragma unroll
+    for (int e = 0; e < H; e += 4) {
+      v0 -= x[e] * sm.sD[H + c][e];
+      v1 -= x[e + 1] * sm.sD[H + c][e + 1];
+      v2 -= x[e + 2] * sm.sD[H + c][e + 2];
+      v3 -= x[e + 3] * sm.sD[H + c][e + 3];
+    }
+#pragma unroll
+    for (int e = 0; e + 3 < c; e += 4) {
+      v0 -= y[e] * sm.sD[H + c][H + e];
+      v1 -= y[e + 1] * sm.sD[H + c][H + e + 1];
+      v2 -= y[e + 2] * sm.sD[H + c][H + e + 2];
+      v3 -= y[e + 3] * sm.sD[H + c][H + e + 3];
+    }
+#pragma unroll
+    for (int e = c & ~3; e < c; ++e) v0 -= y[e] * sm.sD[H + c][H + e];
+    y[c] = ((v0 + v1) + (v2 + v3)) * sm.rdiag[H + c];
+  }
+#pragma unroll
+  for (int c = 0; c < H; ++c) stc(&row[c], x[c]);
+#pragma unroll
+  for (int c = 0; c < H; ++c) stc(&row[H + c], y[c]);
+}
+
+// One lower tile of the trailing update after panel k; tile 0 (the next
+// diagonal block) is then factored in place.
+__device__ __noinline__ void syrk_tile(double* W, int ld, int m, int k, int tau, int32_t* status,
+                                       int b) {
+  TeamSmem& sm = g_team_smem;
+  const int s0 = k + kNB;
   int ty, tx;
-  tri_decode(blockIdx.x, ty, tx);
+  tri_decode(tau, ty, tx);
   const int r0 = s0 + ty * kTile, c0 = s0 + tx * kTile;
-  if (r0 >= m) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  double* Wb = W + static_cast<size_t>(b) * ld * ld;
   f64x4 acc[2][2] = {};
+  constexpr int NE = kKC * kTile / kTeamThreads;
   for (int kk = 0; kk < kNB; kk += kKC) {
-    __syncthreads();
-    for (int e = threadIdx.x; e < kKC * kTile; e += 256) {
-      const int r = e / kKC, c = e % kKC;
+    double va[NE], vb[NE];
+#pragma unroll
+    for (int q = 0; q < NE; ++q) {
+      const int e = threadIdx.x + q * kTeamThreads, r = e / kKC, c = e % kKC;
       const int i = r0 + r, j = c0 + r;
-      sAt[c * kTile + r] = i < m ? Wb[static_cast<size_t>(i) * ld + k + kk + c] : 0.0;
-      sBt[c * kTile + r] = j < m ? Wb[static_cast<size_t>(j) * ld + k + kk + c] : 0.0;
+      va[q] = i < m ? ldc(&W[static_cast<size_t>(i) * ld + k + kk + c]) : 0.0;
+      vb[q] = j < m ? ldc(&W[static_cast<size_t>(j) * ld + k + kk + c]) : 0.0;
     }
     __syncthreads();
-    tile_mma(sAt, sBt, acc, wave, lane);
+#pragma unroll
+    for (int q = 0; q < NE; ++q) {
+      const int e = threadIdx.x + q * kTeamThreads, r = e / kKC, c = e % kKC;
+      sm.sA[c * kTile + r] = va[q];
+      sm.sB[c * kTile + r] = vb[q];
+    }
+    __syncthreads();
+    tile_mma(sm.sA, sm.sB, acc, wave, lane);
   }
-  const bool diag = ty == 0 && tx == 0;
+  const bool diag = tau == 0;
 #pragma unroll
   for (int ra = 0; ra < 2; ++ra)
 #pragma unroll
@@ -448,187 +674,358 @@ __global__ __launch_bounds__(256) void k_syrk_update(double* __restrict__ W, int
         const int rr = tile_row(wave, lane, ra, i), cc = tile_col(wave, lane, rb);
         const int r = r0 + rr, c = c0 + cc;
         if (r < m && c <= r) {
-          const double v = Wb[static_cast<size_t>(r) * ld + c] - acc[ra][rb][i];
-          if (diag) sD[rr][cc] = v;
-          else Wb[static_cast<size_t>(r) * ld + c] = v;
+          double* p = &W[static_cast<size_t>(r) * ld + c];
+          const double v = ldc(p) - acc[ra][rb][i];
+          if (diag) sm.sD[rr][cc] = v;
+          else stc(p, v);
         } else if (diag) {
-          sD[rr][cc] = 0.0;
+          sm.sD[rr][cc] = 0.0;
         }
       }
+  __syncthreads();
   if (!diag) return;
-  __syncthreads();
   const int kb = min(kNB, m - s0);
-  factor_diag(sD, kb, status, b);
-  for (int e = threadIdx.x; e < kb * kb; e += blockDim.x) {
-    const int r = e / kb, c = e % kb;
-    if (c <= r) Wb[static_cast<size_t>(s0 + r) * ld + s0 + c] = sD[r][c];
+  factor_diag(kb, status, b);
+  store_diag(W, ld, s0, kb);
+}
+
+// Blocked right-looking Cholesky of the m x m lower triangle of W by a team:
+// panel rows split over members by 256-row chunks, trailing tiles round-robin.
+__device__ __noinline__ void chol_team(double* W, int ld, int m, Team& tm, int32_t* status,
+                                       int b) {
+  if (m > 0 && tm.rank == 0) {
+    const int kb = min(kNB, m);
+    load_diag(W, ld, 0, kb);
+    factor_diag(kb, status, b);
+    store_diag(W, ld, 0, kb);
+  }
+  team_sync(tm);
+  for (int k = 0; k + kNB < m; k += kNB) {
+    const int below = m - k - kNB;
+    const int nchunk = (below + 255) / 256;
+    if (tm.rank < nchunk) {
+      load_diag(W, ld, k, kNB);
+      for (int ch = tm.rank; ch < nchunk; ch += tm.size)
+        trsm_rows(W, ld, k, k + kNB + ch * 256, m);
+    }
+    team_sync(tm);
+    const int nt = (below + kTile - 1) / kTile;
+    const int ntiles = nt * (nt + 1) / 2;
+    for (int tau = tm.rank; tau < ntiles; tau += tm.size) syrk_tile(W, ld, m, k, tau, status, b);
+    team_sync(tm);
   }
 }
 
-// Solve L L^T x = y in place for nrhs columns of Y [ld_y rows][nrhs] (row a of
-// the system at Y[a*nrhs + col]).  One wave per column; grid (ceil(nrhs/4), B),
-// block 64*min(4,nrhs).
-__global__ __launch_bounds__(256) void k_chol_solve(const double* __restrict__ W, int ld,
-                                                    const int32_t* __restrict__ msz,
-                                                    double* __restrict__ Y, int nrhs) {
-  const int b = blockIdx.y, m = msz[b];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int col = blockIdx.x * (blockDim.x >> 6) + wave;
-  if (col >= nrhs || m == 0) return;
-  const double* L = W + static_cast<size_t>(b) * ld * ld;
-  double* y = Y + static_cast<size_t>(b) * ld * nrhs + col;
-  // forward: L z = y
-  for (int kb = 0; kb < m; kb += 64) {
-    const int r = kb + lane;
-    double v = r < m ? y[static_cast<size_t>(r) * nrhs] : 0.0;
-    const int nb = min(64, m - kb);
-    for (int e = 0; e < nb; ++e) {
-      if (lane == e) v /= L[static_cast<size_t>(r) * ld + r];
-      const double ze = __shfl(v, e);
-      if (lane > e && r < m) v -= L[static_cast<size_t>(r) * ld + kb + e] * ze;
-    }
-    if (r < m) y[static_cast<size_t>(r) * nrhs] = v;
-    for (int r2 = kb + 64 + lane; r2 - lane < m; r2 += 64) {
-      double acc = 0.0;
-      for (int e = 0; e < nb; ++e) {
-        const double ze = __shfl(v, e);
-        if (r2 < m) acc += L[static_cast<size_t>(r2) * ld + kb + e] * ze;
-      }
-      if (r2 < m) y[static_cast<size_t>(r2) * nrhs] -= acc;
-    }
-  }
-  // backward: L^T x = z
-  const int nblk = (m + 63) / 64;
-  for (int bi = nblk - 1; bi >= 0; --bi) {
-    const int kb = bi * 64, r = kb + lane, nb = min(64, m - kb);
-    double v = r < m ? y[static_cast<size_t>(r) * nrhs] : 0.0;
-    for (int e = nb - 1; e >= 0; --e) {
-      if (lane == e) v /= L[static_cast<size_t>(r) * ld + r];
-      const double xe = __shfl(v, e);
-      if (lane < e) v -= L[static_cast<size_t>(kb + e) * ld + r] * xe;
-    }
-    if (r < m) y[static_cast<size_t>(r) * nrhs] = v;
-    for (int r2 = lane; r2 < kb; r2 += 64) {
-      double acc = 0.0;
-      for (int e = 0; e < nb; ++e) {
-        const double xe = __shfl(v, e);
-        acc += L[static_cast<size_t>(kb + e) * ld + r2] * xe;
-      }
-      y[static_cast<size_t>(r2) * nrhs] -= acc;
-    }
-  }
-}
-
-// One pivoting round's bookkeeping.  x (passive solution) in xs[b][0..m);
-// full-length w; gradient y_j = (H w - c)_j for j off F; exchange rule.
-// grid (B), block 1024.
-__global__ __launch_bounds__(1024) void k_bpp_update(const double* __restrict__ H,
-                                                     const double* __restrict__ cvec,
-                                                     const double* __restrict__ xs,
-                                                     const int32_t* __restrict__ Fidx,
-                                                     const int32_t* __restrict__ msz,
-                                                     int32_t* __restrict__ mask,
-                                                     int32_t* __restrict__ state,
-                                                     double* __restrict__ wv,
-                                                     int32_t* __restrict__ status, int t,
-                                                     int max_iters) {
-  __shared__ double shd[16];
-  __shared__ int shi[16];
-  __shared__ int s_vmax;
-  const int b = blockIdx.x;
-  int32_t* st = state + 4 * b;
-  if (st[0]) return;
-  const int m = msz[b];
-  const double* Hb = H + static_cast<size_t>(b) * t * t;
-  const double* cb = cvec + static_cast<size_t>(b) * t;
-  const int32_t* F = Fidx + static_cast<size_t>(b) * t;
-  int32_t* mk = mask + static_cast<size_t>(b) * t;
-  double* w = wv + static_cast<size_t>(b) * t;
-  const double* x = xs + static_cast<size_t>(b) * t;
-  for (int j = threadIdx.x; j < t; j += blockDim.x) w[j] = 0.0;
-  __syncthreads();
-  for (int a = threadIdx.x; a < m; a += blockDim.x) w[F[a]] = x[a];
-  __syncthreads();
-  double cmax = 0.0, hmax = 0.0, xmax = 0.0;
-  for (int j = threadIdx.x; j < t; j += blockDim.x) {
-    cmax = fmax(cmax, fabs(cb[j]));
-    hmax = fmax(hmax, Hb[static_cast<size_t>(j) * t + j]);
-    xmax = fmax(xmax, fabs(w[j]));
-  }
-  cmax = block_max(cmax, shd);
-  hmax = block_max(hmax, shd);
-  xmax = block_max(xmax, shd);
-  const double tol = 1e-13 * fmax(cmax, hmax) * fmax(1.0, xmax);
-  if (threadIdx.x == 0) s_vmax = -1;
-  __syncthreads();
-  int nv = 0, vmax = -1;
-  for (int j = threadIdx.x; j < t; j += blockDim.x) {
-    bool infeasible;
-    if (mk[j]) {
-      infeasible = w[j] < 0.0;
-    } else {
-      const double* hr = Hb + static_cast<size_t>(j) * t;
-      double y = -cb[j];
-      for (int a = 0; a < m; ++a) y += hr[F[a]] * x[a];
-      infeasible = y < -tol;
-    }
-    if (infeasible) {
-      ++nv;
-      vmax = max(vmax, j);
-    }
-  }
-  nv = block_count(nv, shi);
-  atomicMax(&s_vmax, vmax);
-  __syncthreads();
-  vmax = s_vmax;
-  const int it = st[3] + 1;
-  int mode;  // 0 done, 1 exchange all, 2 exchange the largest index only
-  if (nv == 0) {
-    mode = 0;
-  } else if (nv < st[1]) {
-    mode = 1;
-  } else if (st[2] >= 1) {
-    mode = 1;
-  } else {
-    mode = 2;
-  }
-  __syncthreads();
-  if (mode == 1) {
-    // recompute the infeasible set and flip it (reads mask before writes: the
-    // decision for j depends only on j's own entry and on x, H, c)
-    for (int j = threadIdx.x; j < t; j += blockDim.x) {
-      bool infeasible;
-      if (mk[j]) {
-        infeasible = w[j] < 0.0;
-      } else {
-        const double* hr = Hb + static_cast<size_t>(j) * t;
-        double y = -cb[j];
-        for (int a = 0; a < m; ++a) y += hr[F[a]] * x[a];
-        infeasible = y < -tol;
-      }
-      if (infeasible) mk[j] = !mk[j];
-    }
-  } else if (mode == 2 && threadIdx.x == 0) {
-    mk[vmax] = !mk[vmax];
-  }
-  if (threadIdx.x == 0) {
-    if (mode == 0) st[0] = 1;
-    else if (nv < st[1]) {
-      st[1] = nv;
-      st[2] = 3;
-    } else if (st[2] >= 1) {
-      st[2] -= 1;
-    }
-    st[3] = it;
-    if (mode != 0 && it >= max_iters) {
-      st[0] = 2;
-      if (status) status[b] |= 2;
-    }
-  }
-  if (mode != 0 && it >= max_iters) {
+// Solve L L^T Y = Y in place for columns [c0, c0+4) of Y [m][ncol] (row stride
+// ncol), one wave per column (ncol = 1 for a vector).  The waves walk the
+// diagonal blocks together: block staged in LDS, triangle with lane = row,
+// then the off-diagonal rows.  All accesses coherent (ldc/stc).
+__device__ __noinline__ void chol_solve_cols(const double* L, int ld, int m, double* Y, int ncol,
+                                             int c0) {
+  TeamSmem& sm = g_team_smem;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = c0 + wave;
+  const bool on = col < ncol;
+  for (int kb = 0; kb < m; kb += kNB) {
+    const int nb = min(kNB, m - kb);
     __syncthreads();
-    for (int j = threadIdx.x; j < t; j += blockDim.x) w[j] = fmax(w[j], 0.0);
+    load_diag(L, ld, kb, nb);
+    if (on) {
+      double v = lane < nb ? ldc(&Y[static_cast<size_t>(kb + lane) * ncol + col]) : 0.0;
+      for (int e = 0; e < nb; ++e) {
+        if (lane == e) v *= sm.rdiag[e];
+        const double ve = __shfl(v, e);
+        if (lane > e && lane < nb) v -= sm.sD[lane][e] * ve;
+      }
+      if (lane < nb) stc(&Y[static_cast<size_t>(kb + lane) * ncol + col], v);
+      sm.vec[wave][lane] = lane < nb ? v : 0.0;
+      for (int r2 = kb + nb + lane; r2 < m; r2 += 64) {
+        const double* row = L + static_cast<size_t>(r2) * ld + kb;
+        double* py = &Y[static_cast<size_t>(r2) * ncol + col];
+        const double yv = ldc(py);
+        double acc = 0.0;
+#pragma unroll 1
+        for (int e0 = 0; e0 < kNB; e0 += 16) {
+          double lv[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) lv[e] = e0 + e < nb ? ldc(&row[e0 + e]) : 0.0;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc += lv[e] * sm.vec[wave][e0 + e];
+        }
+        stc(py, yv - acc);
+      }
+    }
   }
+  const int nblk = (m + kNB - 1) / kNB;
+  for (int bi = nblk - 1; bi >= 0; --bi) {
+    const int kb = bi * kNB, nb = min(kNB, m - kb);
+    __syncthreads();
+    load_diag(L, ld, kb, nb);
+    if (on) {
+      double v = lane < nb ? ldc(&Y[static_cast<size_t>(kb + lane) * ncol + col]) : 0.0;
+      for (int e = nb - 1; e >= 0; --e) {
+        if (lane == e) v *= sm.rdiag[e];
+        const double ve = __shfl(v, e);
+        if (lane < e) v -= sm.sD[e][lane] * ve;
+      }
+      if (lane < nb) stc(&Y[static_cast<size_t>(kb + lane) * ncol + col], v);
+      sm.vec[wave][lane] = lane < nb ? v : 0.0;
+      for (int r2 = lane; r2 < kb; r2 += 64) {
+        double* py = &Y[static_cast<size_t>(r2) * ncol + col];
+        const double yv = ldc(py);
+        double acc = 0.0;
+#pragma unroll 1
+        for (int e0 = 0; e0 < kNB; e0 += 16) {
+          double lv[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            lv[e] = e0 + e < nb ? ldc(&L[static_cast<size_t>(kb + e0 + e) * ld + r2]) : 0.0;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc += lv[e] * sm.vec[wave][e0 + e];
+        }
+        stc(py, yv - acc);
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Passive index list F (ascending), inverse map, |F|, rhs = c[F]; one workgroup.
+__device__ __noinline__ void build_index(const int32_t* mk, const double* cb, int32_t* F,
+                                         int32_t* inv, int32_t* msz, double* rhs, int t) {
+  TeamSmem& sm = g_team_smem;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int chunk = (t + blockDim.x - 1) / blockDim.x;
+  const int c0 = min(t, tid * chunk), c1 = min(t, c0 + chunk);
+  int cnt = 0;
+  for (int j = c0; j < c1; ++j) cnt += ldc(&mk[j]) != 0;
+  int x = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) sm.scan[wave] = x;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += sm.scan[w];
+  int pos = base + x - cnt;
+  for (int j = c0; j < c1; ++j) {
+    if (ldc(&mk[j])) {
+      stc(&F[pos], j);
+      stc(&inv[j], pos);
+      if (rhs) stc(&rhs[pos], cb[j]);
+      ++pos;
+    } else {
+      stc(&inv[j], -1);
+    }
+  }
+  if (tid == 0) {
+    int tot = 0;
+    for (int w = 0; w < nw; ++w) tot += sm.scan[w];
+    sta(msz, tot);
+  }
+  __syncthreads();
+}
+
+__device__ double wg_max(double v) {
+  TeamSmem& sm = g_team_smem;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off));
+  __syncthreads();
+  if (lane == 0) sm.red[wave] = v;
+  __syncthreads();
+  double s = -INFINITY;
+  for (int w = 0; w < nw; ++w) s = fmax(s, sm.red[w]);
+  __syncthreads();
+  return s;
+}
+
+__device__ int wg_isum(int v) {
+  TeamSmem& sm = g_team_smem;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  __syncthreads();
+  if (lane == 0) sm.ired[wave] = v;
+  __syncthreads();
+  int s = 0;
+  for (int w = 0; w < nw; ++w) s += sm.ired[w];
+  __syncthreads();
+  return s;
+}
+
+__device__ int wg_imax(int v) {
+  TeamSmem& sm = g_team_smem;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off));
+  __syncthreads();
+  if (lane == 0) sm.ired[wave] = v;
+  __syncthreads();
+  int s = -1;
+  for (int w = 0; w < nw; ++w) s = max(s, sm.ired[w]);
+  __syncthreads();
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// NNLS by block principal pivoting, one team per head (cooperative launch).
+// Round: passive list -> gather H_FF -> Cholesky -> solve -> infeasibility of
+// every variable -> exchange rule.  The loop stops as soon as the head's
+// point is feasible and optimal (KKT), or at max_iters (status bit 2).
+// State per head: [0] done (1 ok, 2 capped), [1] best infeasible count,
+// [2] backup budget, [3] rounds; tolv[b] the round's gradient tolerance.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_nnls_team(
+    const double* __restrict__ H, const double* __restrict__ cvec, double* __restrict__ W,
+    double* __restrict__ xs, int32_t* __restrict__ mask, int32_t* __restrict__ Fidx,
+    int32_t* __restrict__ inv, int32_t* __restrict__ msz, int32_t* __restrict__ state,
+    double* __restrict__ tolv, double* __restrict__ wv, int32_t* __restrict__ viol,
+    int32_t* __restrict__ status, unsigned* __restrict__ bar, int* __restrict__ err,
+    int* __restrict__ xcc, int B, int t, int max_iters, int tx) {
+  TeamSmem& sm = g_team_smem;
+  Team tm;
+  int team, nteams;
+  team_setup(tm, team, nteams, bar, err, xcc, tx);
+  const int g = tm.size;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int b = team; b < B; b += nteams) {
+    const size_t tt = static_cast<size_t>(t) * t;
+    const double* Hb = H + b * tt;
+    const double* cb = cvec + static_cast<size_t>(b) * t;
+    double* Wb = W + b * tt;
+    double* xb = xs + static_cast<size_t>(b) * t;
+    int32_t* mk = mask + static_cast<size_t>(b) * t;
+    int32_t* Fb = Fidx + static_cast<size_t>(b) * t;
+    int32_t* ib = inv + static_cast<size_t>(b) * t;
+    int32_t* vb = viol + static_cast<size_t>(b) * t;
+    int32_t* st = state + 4 * b;
+    double* w = wv + static_cast<size_t>(b) * t;
+    for (int it = 0; it < max_iters; ++it) {
+      if (tm.rank == 0) build_index(mk, cb, Fb, ib, &msz[b], xb, t);
+      team_sync(tm);
+      const int m = lda(&msz[b]);
+      for (int a = tid; a < m; a += kTeamThreads) sm.sF[a] = ldc(&Fb[a]);
+      __syncthreads();
+      for (int a = tm.rank; a < m; a += g) {
+        const double* hr = Hb + static_cast<size_t>(sm.sF[a]) * t;
+        for (int a2 = tid; a2 <= a; a2 += kTeamThreads)
+          stc(&Wb[static_cast<size_t>(a) * t + a2], hr[sm.sF[a2]]);
+      }
+      team_sync(tm);
+      chol_team(Wb, t, m, tm, status, b);
+      if (tm.rank == 0) {
+        chol_solve_cols(Wb, t, m, xb, 1, 0);
+        double cmax = 0.0, hmax = 0.0, xmax = 0.0;
+        for (int j = tid; j < t; j += blockDim.x) {
+          cmax = fmax(cmax, fabs(cb[j]));
+          hmax = fmax(hmax, Hb[static_cast<size_t>(j) * t + j]);
+        }
+        for (int a = tid; a < m; a += blockDim.x) xmax = fmax(xmax, fabs(ldc(&xb[a])));
+        cmax = wg_max(cmax);
+        hmax = wg_max(hmax);
+        xmax = wg_max(xmax);
+        if (tid == 0) sta(&tolv[b], 1e-13 * fmax(cmax, hmax) * fmax(1.0, xmax));
+      }
+      team_sync(tm);
+      const double tol = lda(&tolv[b]);
+      // full-length solution (zero off F) in LDS, then infeasibility: a wave
+      // per variable, gradient y_j = H[j,:] x - c_j over the whole row
+      for (int j = tid; j < t; j += kTeamThreads) sm.sx[j] = 0.0;
+      __syncthreads();
+      for (int a = tid; a < m; a += kTeamThreads) sm.sx[sm.sF[a]] = ldc(&xb[a]);
+      __syncthreads();
+      for (int j = tm.rank * 4 + wave; j < t; j += g * 4) {
+        int v = 0;
+        if (ldc(&mk[j])) {
+          v = sm.sx[j] < 0.0;
+        } else {
+          const double* hr = Hb + static_cast<size_t>(j) * t;
+          double acc = 0.0;
+          for (int k2 = lane; k2 < t; k2 += 64) acc += hr[k2] * sm.sx[k2];
+#pragma unroll
+          for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+          v = acc - cb[j] < -tol;
+        }
+        if (lane == 0) stc(&vb[j], v);
+      }
+      team_sync(tm);
+      if (tm.rank == 0) {
+        int nv = 0, vmax = -1;
+        for (int j = tid; j < t; j += blockDim.x) {
+          w[j] = sm.sx[j];
+          if (ldc(&vb[j])) {
+            ++nv;
+            vmax = max(vmax, j);
+          }
+        }
+        nv = wg_isum(nv);
+        vmax = wg_imax(vmax);
+        const int N = lda(&st[1]), pbud = lda(&st[2]);
+        const int mode = nv == 0 ? 0 : (nv < N || pbud >= 1) ? 1 : 2;
+        if (mode == 1) {
+          for (int j = tid; j < t; j += blockDim.x)
+            if (ldc(&vb[j])) stc(&mk[j], !ldc(&mk[j]));
+        } else if (mode == 2 && tid == 0) {
+          stc(&mk[vmax], !ldc(&mk[vmax]));
+        }
+        const bool capped = mode != 0 && it + 1 >= max_iters;
+        if (capped)
+          for (int j = tid; j < t; j += blockDim.x) w[j] = fmax(w[j], 0.0);
+        __syncthreads();
+        if (tid == 0) {
+          if (mode == 0) sta(&st[0], 1);
+          else if (nv < N) {
+            sta(&st[1], nv);
+            sta(&st[2], 3);
+          } else if (pbud >= 1) {
+            sta(&st[2], pbud - 1);
+          }
+          sta(&st[3], it + 1);
+          if (capped) {
+            sta(&st[0], 2);
+            if (status) atomicOr(&status[b], 2);
+          }
+        }
+      }
+      team_sync(tm);
+      if (lda(&st[0]) != 0) break;
+    }
+    // final passive list for the value fit (the support of w)
+    if (tm.rank == 0) build_index(mk, cb, Fb, ib, &msz[b], nullptr, t);
+    team_sync(tm);
+  }
+  if (tm.rank == 0 && tid == 0 && __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+    for (int b = team; b < B; b += nteams) atomicOr(&status[b], 8);
+}
+
+// Value system: Cholesky of G_FF + lam_v I (in W) and solve for the D
+// right-hand sides in R, one team per head; members split the columns.
+__global__ __launch_bounds__(256) void k_value_team(double* __restrict__ W, double* __restrict__ R,
+                                                    const int32_t* __restrict__ msz,
+                                                    int32_t* __restrict__ status,
+                                                    unsigned* __restrict__ bar,
+                                                    int* __restrict__ err, int* __restrict__ xcc,
+                                                    int B, int t, int D, int tx) {
+  TeamSmem& sm = g_team_smem;
+  Team tm;
+  int team, nteams;
+  team_setup(tm, team, nteams, bar, err, xcc, tx);
+  const int g = tm.size;
+  for (int b = team; b < B; b += nteams) {
+    const size_t tt = static_cast<size_t>(t) * t;
+    double* Wb = W + b * tt;
+    double* Rb = R + static_cast<size_t>(b) * t * D;
+    const int m = msz[b];
+    chol_team(Wb, t, m, tm, status, b);
+    for (int c0 = tm.rank * 4; c0 < D; c0 += g * 4) chol_solve_cols(Wb, t, m, Rb, D, c0);
+    team_sync(tm);
+  }
+  if (tm.rank == 0 && threadIdx.x == 0 &&
+      __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+    for (int b = team; b < B; b += nteams) atomicOr(&status[b], 8);
 }
 
 // r_i = sum_a P_S[i][a] w'_a, X = P_S diag(w') / r (in place), w' = max(w, 1e-30).
@@ -705,22 +1102,62 @@ __global__ void k_write_out(const double* __restrict__ R, const In* __restrict__
 // Host launchers.
 // ---------------------------------------------------------------------------
 
-static hipError_t launch_cholesky(double* W, int ld, const int32_t* msz, int B, int tmax,
-                                  int32_t* status, hipStream_t st) {
-  hipLaunchKernelGGL(k_potrf_first, dim3(B), dim3(256), 0, st, W, ld, msz, status);
-  for (int k = 0; k + kNB < tmax; k += kNB) {
-    const int below = tmax - k - kNB;
-    hipLaunchKernelGGL(k_trsm_panel, dim3((below + 255) / 256, B), dim3(256), 0, st, W, ld, msz,
-                       k);
-    const int nt = (below + kTile - 1) / kTile;
-    hipLaunchKernelGGL(k_syrk_update, dim3(nt * (nt + 1) / 2, B), dim3(256), 0, st, W, ld, msz,
-                       k, status);
+// Co-resident workgroups of a team kernel on the current device (cached).
+static int coop_capacity(const void* func) {
+  static int cache[2][64] = {};
+  const int which = func == reinterpret_cast<const void*>(&k_nnls_team) ? 0 : 1;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[which][dev] == 0) {
+    int nb = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, func, 256, 0) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cache[which][dev] = nb * cus < kMaxTeamGrid ? nb * cus : kMaxTeamGrid;
   }
-  return hipGetLastError();
+  return cache[which][dev];
+}
+
+// Team shape: nteams = 8*tx teams (a multiple of the XCD count, so each team
+// stays on one XCD), g members each: enough for the first trailing update (up
+// to 64), no more than the device holds.  Returns the grid size.
+static int team_shape(int B, int t, int cap, int& tx) {
+  const int nt = (t + kNB - 1) / kNB;
+  int tiles = nt * (nt - 1) / 2;
+  tiles = tiles < 1 ? 1 : (tiles > 64 ? 64 : tiles);
+  tx = (B + kXcds - 1) / kXcds;
+  if (kXcds * tx > cap) tx = cap / kXcds > 0 ? cap / kXcds : 1;
+  const int nteams = kXcds * tx;
+  int g = cap / nteams < tiles ? cap / nteams : tiles;
+  if (g < 1) g = 1;
+  return g * nteams;
+}
+
+// A^T B over heads with split-K chosen so the grid has ~2048 workgroups.
+template <class TB, bool SYM>
+static void launch_atb(const double* A, size_t sA, int lda, const int32_t* colA, size_t sColA,
+                       const TB* Bm, size_t sB, int ldb, double* C, size_t sC, int ldc, int nrows,
+                       const int32_t* msz, int mA, int mB, double* part, size_t part_cap, int B,
+                       hipStream_t st) {
+  const int ta = (mA + kTile - 1) / kTile, tb = (mB + kTile - 1) / kTile;
+  const int ntiles = SYM ? ta * (ta + 1) / 2 : ta * tb;
+  const int nchunk = (nrows + kKC - 1) / kKC;
+  int ksplit = 2048 / (ntiles * B);
+  if (ksplit > 16) ksplit = 16;
+  if (ksplit > nchunk / 4) ksplit = nchunk / 4;
+  while (ksplit > 1 &&
+         static_cast<size_t>(B) * ksplit * ntiles * kTile * kTile > part_cap)
+    --ksplit;
+  if (ksplit < 1) ksplit = 1;
+  hipLaunchKernelGGL((k_atb<TB, SYM>), dim3(ntiles, ksplit, B), dim3(256), 0, st, A, sA, lda,
+                     colA, sColA, Bm, sB, ldb, C, sC, ldc, nrows, msz, mA, mB, tb, part, ntiles);
+  if (ksplit > 1)
+    hipLaunchKernelGGL((k_atb_reduce<SYM>), dim3(ntiles, B), dim3(256), 0, st, part, C, sC, ldc,
+                       msz, mA, mB, tb, ntiles, ksplit);
 }
 
 template <class In, int D>
-hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const float* lse,
+hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const double* lse,
                       const float* O, const int32_t* idx, FitBufs fb, float* out_bias,
                       float* out_V, int32_t* status, int B, int n, int T, int t, double ridge,
                       int max_iters, hipStream_t st) {
@@ -728,54 +1165,72 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const floa
   const In* K = static_cast<const In*>(Kv);
   const In* V = static_cast<const In*>(Vv);
   const int tt = (t + kTile - 1) / kTile, tn = (n + kTile - 1) / kTile;
-  // P_S, M = P_S^T P_S (into H), colsum (into cvec)
+  const size_t tsq = static_cast<size_t>(t) * t;
+  // P_S, M = P_S^T P_S (into H), column sums (into cvec)
   prof_mark(3, false, st);
   hipLaunchKernelGGL((k_ps<In, D>), dim3(tn * tt, B), dim3(256), 0, st, Q, K, idx, lse, fb.PS, n,
                      T, t, tt);
   prof_mark(3, true, st);
   prof_mark(4, false, st);
-  hipLaunchKernelGGL((k_atb<double, true>), dim3(tt * (tt + 1) / 2, B), dim3(256), 0, st, fb.PS,
-                     static_cast<size_t>(n) * t, t, nullptr, size_t(0), fb.PS,
-                     static_cast<size_t>(n) * t, t, fb.H, static_cast<size_t>(t) * t, t, n,
-                     nullptr, t, t, tt);
+  launch_atb<double, true>(fb.PS, static_cast<size_t>(n) * t, t, nullptr, 0, fb.PS,
+                           static_cast<size_t>(n) * t, t, fb.H, tsq, t, n, nullptr, t, t, fb.part,
+                           fb.part_cap, B, st);
   prof_mark(4, true, st);
-  hipLaunchKernelGGL(k_colsum, dim3((t + 255) / 256, B), dim3(256), 0, st, fb.PS, fb.cvec, n, t);
+  const int nslab = (n + 255) / 256;
+  hipLaunchKernelGGL(k_colsum_part, dim3(tt, nslab, B), dim3(64, 4), 0, st, fb.PS, fb.colpart, n,
+                     t);
+  hipLaunchKernelGGL(k_colsum_final, dim3((t + 255) / 256, B), dim3(256), 0, st, fb.colpart,
+                     fb.cvec, nslab, t);
   hipLaunchKernelGGL(k_bias_prep, dim3(B), dim3(1024), 0, st, fb.H, fb.cvec, fb.lam, fb.mask,
                      fb.state, fb.wv, t, ridge);
-  // block principal pivoting rounds
-  const size_t tsq = static_cast<size_t>(t) * t;
+  // pivoting rounds: one cooperative launch, a team per head
   prof_mark(5, false, st);
-  for (int it = 0; it < max_iters; ++it) {
-    hipLaunchKernelGGL(k_bpp_index, dim3(B), dim3(1024), 0, st, fb.mask, fb.cvec, fb.state,
-                       fb.Fidx, fb.inv, fb.msz, fb.xs, t);
-    hipLaunchKernelGGL(k_gather_sub, dim3((tsq + 255) / 256, B), dim3(256), 0, st, fb.H, fb.Fidx,
-                       fb.msz, fb.W, t);
-    (void)launch_cholesky(fb.W, t, fb.msz, B, t, status, st);
-    hipLaunchKernelGGL(k_chol_solve, dim3(1, B), dim3(64), 0, st, fb.W, t, fb.msz, fb.xs, 1);
-    hipLaunchKernelGGL(k_bpp_update, dim3(B), dim3(1024), 0, st, fb.H, fb.cvec, fb.xs, fb.Fidx,
-                       fb.msz, fb.mask, fb.state, fb.wv, status, t, max_iters);
+  int cap = coop_capacity(reinterpret_cast<const void*>(&k_nnls_team));
+  if (cap <= 0) return hipErrorLaunchFailure;
+  int tx;
+  int grid = team_shape(B, t, cap, tx);
+  hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(fb.bar), 0, kBarWords, st);
+  if (e != hipSuccess) return e;
+  {
+    const double* H = fb.H;
+    const double* cv = fb.cvec;
+    int* err = reinterpret_cast<int*>(fb.bar + kBarWords - 1);
+    int* xcc = fb.xcc;
+    void* args[] = {&H,        &cv,        &fb.W,    &fb.xs,   &fb.mask, &fb.Fidx, &fb.inv,
+                    &fb.msz,   &fb.state,  &fb.tolv, &fb.wv,   &fb.viol, &status,  &fb.bar,
+                    &err,      &xcc,       &B,       &t,       &max_iters, &tx};
+    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_nnls_team), dim3(grid),
+                                   dim3(256), args, 0, st);
+    if (e != hipSuccess) return e;
   }
   prof_mark(5, true, st);
-  // final passive set (done heads keep their mask) -> index lists
-  prof_mark(6, false, st);
-  hipLaunchKernelGGL(k_bpp_index, dim3(B), dim3(1024), 0, st, fb.mask, fb.cvec,
-                     static_cast<const int32_t*>(nullptr), fb.Fidx, fb.inv, fb.msz,
-                     static_cast<double*>(nullptr), t);
   // value fit on the passive set
+  prof_mark(6, false, st);
   hipLaunchKernelGGL(k_value_prep, dim3(n, B), dim3(256), 0, st, fb.PS, fb.wv, n, t);
-  hipLaunchKernelGGL((k_atb<double, true>), dim3(tt * (tt + 1) / 2, B), dim3(256), 0, st, fb.PS,
-                     static_cast<size_t>(n) * t, t, fb.Fidx, static_cast<size_t>(t), fb.PS,
-                     static_cast<size_t>(n) * t, t, fb.W, tsq, t, n, fb.msz, t, t, tt);
+  launch_atb<double, true>(fb.PS, static_cast<size_t>(n) * t, t, fb.Fidx, t, fb.PS,
+                           static_cast<size_t>(n) * t, t, fb.W, tsq, t, n, fb.msz, t, t, fb.part,
+                           fb.part_cap, B, st);
   hipLaunchKernelGGL(k_ridge_v, dim3(B), dim3(256), 0, st, fb.W, fb.msz, fb.lam, t, ridge);
-  const int td = D / kTile;
-  hipLaunchKernelGGL((k_atb<float, false>), dim3(tt * td, B), dim3(256), 0, st, fb.PS,
-                     static_cast<size_t>(n) * t, t, fb.Fidx, static_cast<size_t>(t), O,
-                     static_cast<size_t>(n) * D, D, fb.R, static_cast<size_t>(t) * D, D, n,
-                     fb.msz, t, D, td);
+  launch_atb<float, false>(fb.PS, static_cast<size_t>(n) * t, t, fb.Fidx, t, O,
+                           static_cast<size_t>(n) * D, D, fb.R, static_cast<size_t>(t) * D, D, n,
+                           fb.msz, t, D, fb.part, fb.part_cap, B, st);
   hipLaunchKernelGGL((k_rhs_ridge<In>), dim3((t * D + 255) / 256, B), dim3(256), 0, st, fb.R, V,
                      idx, fb.Fidx, fb.msz, fb.lam, T, t, D);
-  (void)launch_cholesky(fb.W, t, fb.msz, B, t, status, st);
-  hipLaunchKernelGGL(k_chol_solve, dim3(D / 4, B), dim3(256), 0, st, fb.W, t, fb.msz, fb.R, D);
+  cap = coop_capacity(reinterpret_cast<const void*>(&k_value_team));
+  if (cap <= 0) return hipErrorLaunchFailure;
+  grid = team_shape(B, t, cap, tx);
+  e = launch_fill_i32(reinterpret_cast<int32_t*>(fb.bar), 0, kBarWords, st);
+  if (e != hipSuccess) return e;
+  {
+    int* err = reinterpret_cast<int*>(fb.bar + kBarWords - 1);
+    const int32_t* ms = fb.msz;
+    int Dv = D;
+    int* xcc = fb.xcc;
+    void* args[] = {&fb.W, &fb.R, &ms, &status, &fb.bar, &err, &xcc, &B, &t, &Dv, &tx};
+    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_value_team), dim3(grid),
+                                   dim3(256), args, 0, st);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((k_write_out<In>), dim3((t * D + 255) / 256, B), dim3(256), 0, st, fb.R, V,
                      idx, fb.inv, fb.wv, out_V, out_bias, T, t, D);
   prof_mark(6, true, st);
@@ -783,7 +1238,7 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const floa
 }
 
 #define KVC_INST_FIT(In, D)                                                                   \
-  template hipError_t launch_fit<In, D>(const void*, const void*, const void*, const float*,  \
+  template hipError_t launch_fit<In, D>(const void*, const void*, const void*, const double*, \
                                         const float*, const int32_t*, FitBufs, float*, float*, \
                                         int32_t*, int, int, int, int, double, int, hipStream_t);
 KVC_INST_FIT(bf16_t, 128)

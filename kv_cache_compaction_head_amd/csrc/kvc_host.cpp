@@ -47,7 +47,7 @@ void prof_mark(int stage, bool end, hipStream_t st) {
 namespace {
 
 constexpr int64_t kMaxT = 1 << 30;
-constexpr int64_t kMaxT_keep = 8192;
+constexpr int64_t kMaxT_keep = 4096;  // the fit kernels stage t values in LDS
 constexpr int64_t kMaxB = 65535;
 constexpr int kBM = 128;  // reference queries per score workgroup
 
@@ -77,8 +77,9 @@ Plan make_plan(const kvc_params_t* p) {
 }
 
 struct Layout {
-  size_t ml, lse, Opart, O, imp_part, imp, idx, status, PS, H, W, cvec, xs, R, wv, lam, mask,
-      Fidx, inv, msz, state, total;
+  size_t ml, lse, Opart, O, imp_part, imp, idx, status, PS, H, W, cvec, xs, R, wv, lam, tolv,
+      colpart, mask, Fidx, inv, msz, state, viol, bar, xcc, part, total;
+  size_t part_cap;
 };
 
 size_t align_up(size_t x) { return (x + 255) / 256 * 256; }
@@ -93,8 +94,8 @@ Layout make_layout(const kvc_params_t* p) {
     off = align_up(off + bytes);
     return o;
   };
-  L.ml = take(B * pl.nsplit1 * n * 8);
-  L.lse = take(B * n * 4);
+  L.ml = take(B * pl.nsplit1 * n * 16);
+  L.lse = take(B * n * 8);
   L.Opart = take(B * pl.nsplit2 * d * n * 4);
   L.O = take(B * n * d * 4);
   L.imp_part = take(B * pl.nqb * T * 4);
@@ -109,11 +110,24 @@ Layout make_layout(const kvc_params_t* p) {
   L.R = take(B * t * d * 8);
   L.wv = take(B * t * 8);
   L.lam = take(B * 2 * 8);
+  L.tolv = take(B * 8);
+  L.colpart = take(B * ((n + 255) / 256) * t * 8);
   L.mask = take(B * t * 4);
   L.Fidx = take(B * t * 4);
   L.inv = take(B * t * 4);
   L.msz = take(B * 4);
   L.state = take(B * 4 * 4);
+  L.viol = take(B * t * 4);
+  L.bar = take(static_cast<size_t>(kvc::kBarWords) * 4);
+  L.xcc = take(static_cast<size_t>(kvc::kMaxTeamGrid) * 4);
+  // split-K partials: up to 2048 * 4 tile slices of 64 x 64 doubles, never
+  // more than the (already needed) t x t matrix per head times 4
+  {
+    size_t cap = static_cast<size_t>(8192) * 64 * 64;
+    const size_t lim = 4 * B * t * t + 64 * 64;
+    L.part_cap = cap < lim ? cap : lim;
+    L.part = take(L.part_cap * 8);
+  }
   L.total = off;
   return L;
 }
@@ -150,6 +164,13 @@ kvc::FitBufs fit_bufs(void* ws, const Layout& L) {
   fb.R = at<double>(ws, L.R);
   fb.wv = at<double>(ws, L.wv);
   fb.lam = at<double>(ws, L.lam);
+  fb.tolv = at<double>(ws, L.tolv);
+  fb.colpart = at<double>(ws, L.colpart);
+  fb.viol = at<int32_t>(ws, L.viol);
+  fb.bar = at<unsigned>(ws, L.bar);
+  fb.xcc = at<int32_t>(ws, L.xcc);
+  fb.part = at<double>(ws, L.part);
+  fb.part_cap = L.part_cap;
   fb.mask = at<int32_t>(ws, L.mask);
   fb.Fidx = at<int32_t>(ws, L.Fidx);
   fb.inv = at<int32_t>(ws, L.inv);
@@ -162,7 +183,7 @@ template <class In, int D>
 hipError_t run_score(const kvc_params_t* p, const void* Q, const void* K, const void* V,
                      void* ws, const Layout& L, hipStream_t st) {
   const Plan pl = make_plan(p);
-  return kvc::launch_score<In, D>(Q, K, V, at<float2>(ws, L.ml), at<float>(ws, L.lse),
+  return kvc::launch_score<In, D>(Q, K, V, at<double2>(ws, L.ml), at<double>(ws, L.lse),
                                   at<float>(ws, L.Opart), at<float>(ws, L.O),
                                   at<float>(ws, L.imp_part), at<float>(ws, L.imp),
                                   static_cast<int>(p->B), static_cast<int>(p->n),
@@ -174,7 +195,7 @@ template <class In, int D>
 hipError_t run_fit(const kvc_params_t* p, const void* Q, const void* K, const void* V,
                    const int32_t* idx, float* out_bias, float* out_V, int32_t* status, void* ws,
                    const Layout& L, hipStream_t st) {
-  return kvc::launch_fit<In, D>(Q, K, V, at<float>(ws, L.lse), at<float>(ws, L.O), idx,
+  return kvc::launch_fit<In, D>(Q, K, V, at<double>(ws, L.lse), at<float>(ws, L.O), idx,
                                 fit_bufs(ws, L), out_bias, out_V, status,
                                 static_cast<int>(p->B), static_cast<int>(p->n),
                                 static_cast<int>(p->T), static_cast<int>(p->t), p->ridge_rel,

@@ -8,7 +8,7 @@ namespace kvc {
 using bf16_t = uint16_t;
 
 template <class In, int D>
-hipError_t launch_score(const void* Q, const void* K, const void* V, float2* ml, float* lse,
+hipError_t launch_score(const void* Q, const void* K, const void* V, double2* ml, double* lse,
                         float* Opart, float* O, float* imp_part, float* imp, int B, int n, int T,
                         int nsplit1, int kps1, int nsplit2, int kps2, bool rms, hipStream_t st);
 hipError_t launch_select(const float* imp, int32_t* idx, int32_t* status, int B, int T, int t,
@@ -19,11 +19,17 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t count, hipStream_t st);
 
 // Float64 work buffers of the fits (device pointers into the workspace).
 struct FitBufs {
-  double *PS, *H, *W, *cvec, *xs, *R, *wv, *lam;
-  int32_t *mask, *Fidx, *inv, *msz, *state;
+  double *PS, *H, *W, *cvec, *xs, *R, *wv, *lam, *tolv, *colpart;
+  int32_t *mask, *Fidx, *inv, *msz, *state, *viol;
+  unsigned* bar;  // kBarWords words: team barrier counters, the last one the timeout flag
+  int32_t* xcc;   // kMaxTeamGrid words: each team workgroup's XCC id
+  double* part;     // split-K partial tiles of the fit GEMMs
+  size_t part_cap;  // its capacity in doubles
 };
+constexpr int kMaxTeamGrid = 8192;
+constexpr int kBarWords = kMaxTeamGrid + 1;
 template <class In, int D>
-hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const float* lse,
+hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const double* lse,
                       const float* O, const int32_t* idx, FitBufs fb, float* out_bias,
                       float* out_V, int32_t* status, int B, int n, int T, int t, double ridge,
                       int max_iters, hipStream_t st);

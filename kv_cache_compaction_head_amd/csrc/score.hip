@@ -83,7 +83,7 @@ __device__ __forceinline__ void load_q_frags(typename Frag<In>::T* bq, const In*
 template <class In, int D>
 __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
                                                    const In* __restrict__ K,
-                                                   float2* __restrict__ ml, int n, int T,
+                                                   double2* __restrict__ ml, int n, int T,
                                                    int keys_per_split) {
   constexpr int KS = Frag<In>::KS, NK = D / KS, BN = 64, LD = D + 16 / sizeof(In);
   __shared__ __align__(16) In sK[BN * LD];
@@ -98,7 +98,11 @@ __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
 
   const int j0 = split * keys_per_split;
   const int j1 = min(T, j0 + keys_per_split);
-  float m = -INFINITY, l = 0.f;
+  // running max m (a score, exact in fp32) and sum l = sum exp(s - m) in fp64:
+  // each 16-term tile sum is formed in fp32, then accumulated in double, and
+  // the rare rescale on a new maximum uses a double exp.
+  float m = -INFINITY;
+  double l = 0.0;
   for (int jt = j0; jt < j1; jt += BN) {
     __syncthreads();
     load_tile<In, D, LD>(sK, Kb + static_cast<size_t>(jt) * D, BN, j1 - jt);
@@ -119,46 +123,50 @@ __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
         acc[r] = s;
         tmax = fmaxf(tmax, s);
       }
-      const float mn = fmaxf(m, tmax);
-      if (mn != -INFINITY) {
-        const float mn2 = mn * KVC_LOG2E;
+      if (tmax > m) {
+        if (m != -INFINITY) l *= exp(static_cast<double>(m) - static_cast<double>(tmax));
+        m = tmax;
+      }
+      if (m != -INFINITY) {
+        const float m2 = m * KVC_LOG2E;
+        const float m2lo = fmaf(m, KVC_LOG2E, -m2);  // m*log2e = m2 + m2lo exactly
         float sum = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -mn2));
-        l = l * __builtin_amdgcn_exp2f((m - mn) * KVC_LOG2E) + sum;
-        m = mn;
+        for (int r = 0; r < 16; ++r)
+          sum += __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -m2) - m2lo);
+        l += static_cast<double>(sum);
       }
     }
   }
   // lanes l and l+32 hold the same query over different keys: merge them
-  const float m2 = __shfl_xor(m, 32), l2 = __shfl_xor(l, 32);
-  const float mm = fmaxf(m, m2);
-  float ll = 0.f;
-  if (mm != -INFINITY) {
-    const float a = g == 0 ? l : l2, am = g == 0 ? m : m2;  // same order in both lanes
-    const float c = g == 0 ? l2 : l, cm = g == 0 ? m2 : m;
-    ll = a * __builtin_amdgcn_exp2f((am - mm) * KVC_LOG2E) +
-         c * __builtin_amdgcn_exp2f((cm - mm) * KVC_LOG2E);
+  const float mo = __shfl_xor(m, 32);
+  const double lo = __shfl_xor(l, 32);
+  if (g == 0 && q < n) {
+    const float mm = fmaxf(m, mo);
+    double ll = 0.0;
+    if (mm != -INFINITY) {
+      if (m != -INFINITY) ll += l * exp(static_cast<double>(m) - mm);
+      if (mo != -INFINITY) ll += lo * exp(static_cast<double>(mo) - mm);
+    }
+    ml[(static_cast<size_t>(b) * gridDim.y + split) * n + q] = make_double2(mm, ll);
   }
-  if (g == 0 && q < n)
-    ml[(static_cast<size_t>(b) * gridDim.y + split) * n + q] = make_float2(mm, ll);
 }
 
-// lse[b][q] from the split partials, merged in split order.
-__global__ void k_lse_merge(const float2* __restrict__ ml, float* __restrict__ lse, int n,
+// lse[b][q] (float64) from the split partials, merged in split order.
+__global__ void k_lse_merge(const double2* __restrict__ ml, double* __restrict__ lse, int n,
                             int nsplit, int B) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= B * n) return;
   const int b = i / n, q = i % n;
-  const float2* p = ml + static_cast<size_t>(b) * nsplit * n + q;
-  float m = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, p[static_cast<size_t>(s) * n].x);
-  float l = 0.f;
+  const double2* p = ml + static_cast<size_t>(b) * nsplit * n + q;
+  double m = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) m = fmax(m, p[static_cast<size_t>(s) * n].x);
+  double l = 0.0;
   for (int s = 0; s < nsplit; ++s) {
-    const float2 v = p[static_cast<size_t>(s) * n];
-    if (v.x != -INFINITY) l += v.y * expf(v.x - m);
+    const double2 v = p[static_cast<size_t>(s) * n];
+    if (v.x != -INFINITY) l += v.y * exp(v.x - m);
   }
-  lse[i] = m + logf(l);
+  lse[i] = m + log(l);
 }
 
 // Position of key kk (0..31 inside a tile) in the transposed V tile: the
@@ -180,7 +188,7 @@ template <class In, int D, bool RMS>
 __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
                                                    const In* __restrict__ K,
                                                    const In* __restrict__ V,
-                                                   const float* __restrict__ lse,
+                                                   const double* __restrict__ lse,
                                                    float* __restrict__ Opart,
                                                    float* __restrict__ imp_part, int n, int T,
                                                    int keys_per_split) {
@@ -201,7 +209,11 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
 
   typename Frag<In>::T bq[NK];
   load_q_frags<In, D>(bq, Qb, q, n, g);
-  const float ml2 = q < n ? lse[static_cast<size_t>(b) * n + q] * KVC_LOG2E : 0.f;
+  // lse*log2e as an unevaluated fp32 pair, so exp2(s*log2e - hi - lo) keeps
+  // the float64 log-sum-exp's accuracy
+  const double l2 = q < n ? lse[static_cast<size_t>(b) * n + q] * 1.4426950408889634 : 0.0;
+  const float ml2 = static_cast<float>(l2);
+  const float ml2lo = static_cast<float>(l2 - static_cast<double>(ml2));
 
   f32x16 accO[ND];
 #pragma unroll
@@ -242,7 +254,8 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
     for (int r = 0; r < 16; ++r) {
       const int kk = mfma32_row(r, lane);
       float p = 0.f;
-      if (kk < valid && q < n) p = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2));
+      if (kk < valid && q < n)
+        p = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2) - ml2lo);
       acc[r] = p;
       sImp[(wave * 16 + r) * 64 + lane] = RMS ? p * p : p;
     }
@@ -339,7 +352,7 @@ __global__ void k_imp_reduce(const float* __restrict__ part, float* __restrict__
 // Host-side launchers (same library).
 // ---------------------------------------------------------------------------
 template <class In, int D>
-hipError_t launch_score(const void* Q, const void* K, const void* V, float2* ml, float* lse,
+hipError_t launch_score(const void* Q, const void* K, const void* V, double2* ml, double* lse,
                         float* Opart, float* O, float* imp_part, float* imp, int B, int n, int T,
                         int nsplit1, int kps1, int nsplit2, int kps2, bool rms,
                         hipStream_t st) {
@@ -369,17 +382,17 @@ hipError_t launch_score(const void* Q, const void* K, const void* V, float2* ml,
   return hipGetLastError();
 }
 
-template hipError_t launch_score<bf16_t, 128>(const void*, const void*, const void*, float2*,
-                                              float*, float*, float*, float*, float*, int, int,
+template hipError_t launch_score<bf16_t, 128>(const void*, const void*, const void*, double2*,
+                                              double*, float*, float*, float*, float*, int, int,
                                               int, int, int, int, int, bool, hipStream_t);
-template hipError_t launch_score<bf16_t, 64>(const void*, const void*, const void*, float2*,
-                                             float*, float*, float*, float*, float*, int, int,
+template hipError_t launch_score<bf16_t, 64>(const void*, const void*, const void*, double2*,
+                                             double*, float*, float*, float*, float*, int, int,
                                              int, int, int, int, int, bool, hipStream_t);
-template hipError_t launch_score<float, 128>(const void*, const void*, const void*, float2*,
-                                             float*, float*, float*, float*, float*, int, int,
+template hipError_t launch_score<float, 128>(const void*, const void*, const void*, double2*,
+                                             double*, float*, float*, float*, float*, int, int,
                                              int, int, int, int, int, bool, hipStream_t);
-template hipError_t launch_score<float, 64>(const void*, const void*, const void*, float2*,
-                                            float*, float*, float*, float*, float*, int, int,
+template hipError_t launch_score<float, 64>(const void*, const void*, const void*, double2*,
+                                            double*, float*, float*, float*, float*, int, int,
                                             int, int, int, int, int, bool, hipStream_t);
 
 }  // namespace kvc

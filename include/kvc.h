@@ -110,9 +110,11 @@ int kvc_fit(const kvc_params_t* p, const void* Q_ref, const void* K, const void*
  * offsets), for inspection after the stream completes:
  *   lse [B, n] f64; O [B, n, d] f32 (full-cache output); imp [B, T] f32 holding
  *   sum_i p_ij^2 (RMS) or sum_i p_ij (mean) -- the ranking key before the
- *   monotone sqrt(./n) or ./n; w [B, t] f64 the NNLS multipliers. */
+ *   monotone sqrt(./n) or ./n; w [B, t] f64 the NNLS multipliers;
+ *   fit_flops [B, 2] f64 the floating-point operations the NNLS rounds
+ *   (factorizations and solves) and the value solve performed for each head. */
 typedef struct {
-  size_t lse, O, imp, w;
+  size_t lse, O, imp, w, fit_flops;
 } kvc_ws_layout_t;
 int kvc_workspace_layout(const kvc_params_t* p, kvc_ws_layout_t* out);
 

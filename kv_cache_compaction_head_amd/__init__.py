@@ -119,7 +119,8 @@ def fit(Q, K, V, idx, *, ridge_rel: float = 1e-6, max_nnls_iters: int = 32,
 
 def intermediates(res: Compacted) -> dict:
     """Views into the workspace: lse [B,n] (float64), O [B,n,d], imp [B,T] (sum of p^2 or
-    p per key), w [B,t] (float64 NNLS multipliers).  Synchronise first."""
+    p per key), w [B,t] (float64 NNLS multipliers), fit_flops [B,2] (fp64
+    operations of the NNLS rounds and the value solve).  Synchronise first."""
     import torch
     p = res.params
     L = workspace_layout(p)
@@ -133,4 +134,5 @@ def intermediates(res: Compacted) -> dict:
     return {"lse": view(L.lse, B * n, torch.float64, (B, n)),
             "O": view(L.O, B * n * d, torch.float32, (B, n, d)),
             "imp": view(L.imp, B * T, torch.float32, (B, T)),
-            "w": view(L.w, B * t, torch.float64, (B, t))}
+            "w": view(L.w, B * t, torch.float64, (B, t)),
+            "fit_flops": view(L.fit_flops, B * 2, torch.float64, (B, 2))}

@@ -29,7 +29,7 @@ class Params(ctypes.Structure):
 
 class WsLayout(ctypes.Structure):
     _fields_ = [("lse", ctypes.c_size_t), ("O", ctypes.c_size_t), ("imp", ctypes.c_size_t),
-                ("w", ctypes.c_size_t)]
+                ("w", ctypes.c_size_t), ("fit_flops", ctypes.c_size_t)]
 
 
 _lib = None

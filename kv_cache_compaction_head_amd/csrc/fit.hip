@@ -480,13 +480,14 @@ struct __align__(16) TeamSmem {
 __shared__ TeamSmem g_team_smem;
 
 
-// Factor sD[0:kb][0:kb] (lower) in place, 256 threads, in four 16-column
-// micro-panels.  Micro-panel p (columns 16p..16p+15, rows 16p..kb-1) is
-// factored by wave 0 alone: lane = row holds its 16 values in registers and
-// the pivot row's values are broadcast with readlane, so the 16 column steps
-// need no workgroup barrier.  The rank-16 update of the rows and columns
-// below then runs on all threads through LDS.  sm.rdiag receives 1/L[c][c].
-// A pivot <= 0 is replaced by 1 and flags status bit 1.
+// Factor sD[0:kb][0:kb] (lower) in place, 256 threads.  The block is padded
+// to 64 x 64 with the identity, so everything below is fixed-size and
+// branch-free: four 16-column micro-panels, each factored by wave 0 alone
+// (lane = row, the micro-panel's 16 values in registers, pivot and column
+// values broadcast with readlane, so the 16 column steps need no workgroup
+// barrier), followed by the rank-16 update of the trailing block on fp64
+// MFMA.  Upper-triangle entries are computed but never stored.  sm.rdiag
+// receives 1/L[c][c].  A pivot <= 0 is replaced by 1 and flags status bit 1.
 __device__ __forceinline__ double bcast(double v, int lane) {
   const long long u = __double_as_longlong(v);
   const int lo = __builtin_amdgcn_readlane(static_cast<int>(u & 0xffffffff), lane);
@@ -495,60 +496,70 @@ __device__ __forceinline__ double bcast(double v, int lane) {
                               static_cast<unsigned int>(lo));
 }
 
+// 1/sqrt(x) for x > 0 to full double precision: hardware estimate, two
+// Newton steps y <- y (3 - x y^2) / 2.
+__device__ __forceinline__ double rsqrt_f64(double x) {
+  double y = __builtin_amdgcn_rsq(x);
+  y = y * fma(-0.5 * x * y, y, 1.5);
+  y = y * fma(-0.5 * x * y, y, 1.5);
+  return y;
+}
+
 __device__ __noinline__ void factor_diag(int kb, int32_t* status, int b) {
   TeamSmem& sm = g_team_smem;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  constexpr int MP = 16;
-#pragma unroll 1
-  for (int p0 = 0; p0 < kb; p0 += MP) {
-    const int pw = min(MP, kb - p0);
-    if (wave == 0) {
-      double a[MP];
-      const int r = lane;  // row of the block
-      const bool live = r >= p0 && r < kb;
-#pragma unroll
-      for (int j = 0; j < MP; ++j) a[j] = (live && j < pw && p0 + j <= r) ? sm.sD[r][p0 + j] : 0.0;
-#pragma unroll
-      for (int c = 0; c < MP; ++c) {
-        if (c < pw) {
-          double piv = bcast(a[c], p0 + c);
-          const bool good = piv > 0.0;
-          if (!good) {
-            if (lane == 0 && status) atomicOr(&status[b], 1);
-            piv = 1.0;
-          }
-          const double d = sqrt(piv), id = 1.0 / d;
-          if (r == p0 + c) a[c] = d;
-          else if (live && r > p0 + c) a[c] *= id;
-          if (lane == 0) sm.rdiag[p0 + c] = id;
-#pragma unroll
-          for (int j = c + 1; j < MP; ++j) {
-            const double ljc = bcast(a[c], min(p0 + j, 63));
-            if (j < pw && live && r >= p0 + j) a[j] -= a[c] * ljc;
-          }
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < MP; ++j)
-        if (live && j < pw && p0 + j <= r) sm.sD[r][p0 + j] = a[j];
-    }
-    __syncthreads();
-    // rank-pw update of the trailing block rows/cols [p0+pw, kb)
-    const int s0 = p0 + pw, ns = kb - s0;
-    for (int e = tid; e < ns * ns; e += kTeamThreads) {
-      const int r = s0 + e / ns, j = s0 + e % ns;
-      if (j <= r) {
-        double v = sm.sD[r][j];
-#pragma unroll
-        for (int c = 0; c < MP; ++c)
-          if (c < pw) v -= sm.sD[r][p0 + c] * sm.sD[j][p0 + c];
-        sm.sD[r][j] = v;
-      }
+  if (kb < kNB) {
+    for (int e = tid; e < kNB * kNB; e += kTeamThreads) {
+      const int r = e >> 6, c = e & 63;
+      if (r >= kb || c >= kb) sm.sD[r][c] = r == c ? 1.0 : 0.0;
     }
     __syncthreads();
   }
+  constexpr int MP = 16;
+#pragma unroll
+  for (int p = 0; p < kNB / MP; ++p) {
+    const int p0 = p * MP;
+    if (wave == 0) {
+      double a[MP];
+#pragma unroll
+      for (int j = 0; j < MP; ++j) a[j] = sm.sD[lane][p0 + j];
+      bool bad = false;
+#pragma unroll
+      for (int c = 0; c < MP; ++c) {
+        double piv = bcast(a[c], p0 + c);
+        bad |= !(piv > 0.0);
+        piv = piv > 0.0 ? piv : 1.0;
+        const double y = rsqrt_f64(piv);
+        a[c] = lane > p0 + c ? a[c] * y : (lane == p0 + c ? piv * y : a[c]);
+        if (lane == 0) sm.rdiag[p0 + c] = y;
+#pragma unroll
+        for (int j = c + 1; j < MP; ++j) a[j] = fma(-a[c], bcast(a[c], p0 + j), a[j]);
+      }
+      if (bad && lane == 0 && status) atomicOr(&status[b], 1);
+#pragma unroll
+      for (int j = 0; j < MP; ++j)
+        if (p0 + j <= lane) sm.sD[lane][p0 + j] = a[j];
+    }
+    __syncthreads();
+    if (p + 1 < kNB / MP) {
+      // trailing rows/cols [p0+16, 64): C -= P P^T, P = columns p0..p0+15
+      const int t0 = p0 + MP, nt = (kNB - t0) / 16;
+      for (int tau = wave; tau < nt * nt; tau += 4) {
+        const int R = t0 + 16 * (tau / nt), Cc = t0 + 16 * (tau % nt);
+        f64x4 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < MP / 4; ++ks) {
+          const int k = p0 + 4 * ks + (lane >> 4);
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(sm.sD[R + (lane & 15)][k],
+                                                     sm.sD[Cc + (lane & 15)][k], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.sD[R + (lane >> 4) + 4 * i][Cc + (lane & 15)] -= acc[i];
+      }
+      __syncthreads();
+    }
+  }
 }
-
 
 __device__ void load_diag(const double* W, int ld, int k, int kb) {
   TeamSmem& sm = g_team_smem;
@@ -645,21 +656,25 @@ __device__ __noinline__ void syrk_tile(double* W, int ld, int m, int k, int tau,
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   f64x4 acc[2][2] = {};
   constexpr int NE = kKC * kTile / kTeamThreads;
-  for (int kk = 0; kk < kNB; kk += kKC) {
-    double va[NE], vb[NE];
+  constexpr int NCH = kNB / kKC;
+  double va[NCH][NE], vb[NCH][NE];
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
     for (int q = 0; q < NE; ++q) {
       const int e = threadIdx.x + q * kTeamThreads, r = e / kKC, c = e % kKC;
       const int i = r0 + r, j = c0 + r;
-      va[q] = i < m ? ldc(&W[static_cast<size_t>(i) * ld + k + kk + c]) : 0.0;
-      vb[q] = j < m ? ldc(&W[static_cast<size_t>(j) * ld + k + kk + c]) : 0.0;
+      va[ch][q] = i < m ? ldc(&W[static_cast<size_t>(i) * ld + k + ch * kKC + c]) : 0.0;
+      vb[ch][q] = j < m ? ldc(&W[static_cast<size_t>(j) * ld + k + ch * kKC + c]) : 0.0;
     }
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < NE; ++q) {
       const int e = threadIdx.x + q * kTeamThreads, r = e / kKC, c = e % kKC;
-      sm.sA[c * kTile + r] = va[q];
-      sm.sB[c * kTile + r] = vb[q];
+      sm.sA[c * kTile + r] = va[ch][q];
+      sm.sB[c * kTile + r] = vb[ch][q];
     }
     __syncthreads();
     tile_mma(sm.sA, sm.sB, acc, wave, lane);
@@ -734,7 +749,7 @@ __device__ __noinline__ void chol_solve_cols(const double* L, int ld, int m, dou
       double v = lane < nb ? ldc(&Y[static_cast<size_t>(kb + lane) * ncol + col]) : 0.0;
       for (int e = 0; e < nb; ++e) {
         if (lane == e) v *= sm.rdiag[e];
-        const double ve = __shfl(v, e);
+        const double ve = bcast(v, e);
         if (lane > e && lane < nb) v -= sm.sD[lane][e] * ve;
       }
       if (lane < nb) stc(&Y[static_cast<size_t>(kb + lane) * ncol + col], v);
@@ -765,7 +780,7 @@ __device__ __noinline__ void chol_solve_cols(const double* L, int ld, int m, dou
       double v = lane < nb ? ldc(&Y[static_cast<size_t>(kb + lane) * ncol + col]) : 0.0;
       for (int e = nb - 1; e >= 0; --e) {
         if (lane == e) v *= sm.rdiag[e];
-        const double ve = __shfl(v, e);
+        const double ve = bcast(v, e);
         if (lane < e) v -= sm.sD[e][lane] * ve;
       }
       if (lane < nb) stc(&Y[static_cast<size_t>(kb + lane) * ncol + col], v);
@@ -785,6 +800,77 @@ __device__ __noinline__ void chol_solve_cols(const double* L, int ld, int m, dou
         }
         stc(py, yv - acc);
       }
+    }
+  }
+  __syncthreads();
+}
+
+// Solve L L^T y = y for one vector with a whole workgroup: diagonal blocks
+// staged in LDS and solved by wave 0 (lane = row), the off-diagonal updates
+// spread over all 256 threads, four threads per row each loading 16 values in
+// one batch and combining with shuffles.
+__device__ __noinline__ void chol_solve_vec(const double* L, int ld, int m, double* y) {
+  TeamSmem& sm = g_team_smem;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int quad = tid & 3, rsub = tid >> 2;  // 64 rows per pass, 4 threads each
+  for (int kb = 0; kb < m; kb += kNB) {
+    const int nb = min(kNB, m - kb);
+    __syncthreads();
+    load_diag(L, ld, kb, nb);
+    if (wave == 0) {
+      double v = lane < nb ? y[kb + lane] : 0.0;
+      for (int e = 0; e < nb; ++e) {
+        if (lane == e) v *= sm.rdiag[e];
+        const double ve = bcast(v, e);
+        if (lane > e && lane < nb) v -= sm.sD[lane][e] * ve;
+      }
+      if (lane < nb) y[kb + lane] = v;
+      sm.vec[0][lane] = lane < nb ? v : 0.0;
+    }
+    __syncthreads();
+    for (int r0 = kb + nb; r0 < m; r0 += 64) {
+      const int r2 = r0 + rsub;
+      const double* row = L + static_cast<size_t>(r2 < m ? r2 : kb) * ld + kb + quad * 16;
+      double lv[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) lv[e] = (r2 < m && quad * 16 + e < nb) ? row[e] : 0.0;
+      double acc = 0.0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc += lv[e] * sm.vec[0][quad * 16 + e];
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      if (quad == 0 && r2 < m) y[r2] -= acc;
+    }
+  }
+  const int nblk = (m + kNB - 1) / kNB;
+  for (int bi = nblk - 1; bi >= 0; --bi) {
+    const int kb = bi * kNB, nb = min(kNB, m - kb);
+    __syncthreads();
+    load_diag(L, ld, kb, nb);
+    if (wave == 0) {
+      double v = lane < nb ? y[kb + lane] : 0.0;
+      for (int e = nb - 1; e >= 0; --e) {
+        if (lane == e) v *= sm.rdiag[e];
+        const double ve = bcast(v, e);
+        if (lane < e) v -= sm.sD[e][lane] * ve;
+      }
+      if (lane < nb) y[kb + lane] = v;
+      sm.vec[0][lane] = lane < nb ? v : 0.0;
+    }
+    __syncthreads();
+    // y[r2] -= sum_e L[kb+e][r2] x_e for r2 < kb: thread per r2, 16-value batches
+    for (int r2 = tid; r2 < kb; r2 += kTeamThreads) {
+      double acc = 0.0;
+#pragma unroll 1
+      for (int e0 = 0; e0 < kNB; e0 += 16) {
+        double lv[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          lv[e] = e0 + e < nb ? L[static_cast<size_t>(kb + e0 + e) * ld + r2] : 0.0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc += lv[e] * sm.vec[0][e0 + e];
+      }
+      y[r2] -= acc;
     }
   }
   __syncthreads();
@@ -884,7 +970,7 @@ __global__ __launch_bounds__(256) void k_nnls_team(
     int32_t* __restrict__ inv, int32_t* __restrict__ msz, int32_t* __restrict__ state,
     double* __restrict__ tolv, double* __restrict__ wv, int32_t* __restrict__ viol,
     int32_t* __restrict__ status, unsigned* __restrict__ bar, int* __restrict__ err,
-    int* __restrict__ xcc, int B, int t, int max_iters, int tx) {
+    int* __restrict__ xcc, double* __restrict__ flops, int B, int t, int max_iters, int tx) {
   TeamSmem& sm = g_team_smem;
   Team tm;
   int team, nteams;
@@ -893,6 +979,7 @@ __global__ __launch_bounds__(256) void k_nnls_team(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   for (int b = team; b < B; b += nteams) {
     const size_t tt = static_cast<size_t>(t) * t;
+    if (tm.rank == 0 && tid == 0) flops[2 * b] = 0.0;
     const double* Hb = H + b * tt;
     const double* cb = cvec + static_cast<size_t>(b) * t;
     double* Wb = W + b * tt;
@@ -917,7 +1004,7 @@ __global__ __launch_bounds__(256) void k_nnls_team(
       team_sync(tm);
       chol_team(Wb, t, m, tm, status, b);
       if (tm.rank == 0) {
-        chol_solve_cols(Wb, t, m, xb, 1, 0);
+        chol_solve_vec(Wb, t, m, xb);
         double cmax = 0.0, hmax = 0.0, xmax = 0.0;
         for (int j = tid; j < t; j += blockDim.x) {
           cmax = fmax(cmax, fabs(cb[j]));
@@ -927,7 +1014,12 @@ __global__ __launch_bounds__(256) void k_nnls_team(
         cmax = wg_max(cmax);
         hmax = wg_max(hmax);
         xmax = wg_max(xmax);
-        if (tid == 0) sta(&tolv[b], 1e-13 * fmax(cmax, hmax) * fmax(1.0, xmax));
+        if (tid == 0) {
+          sta(&tolv[b], 1e-13 * fmax(cmax, hmax) * fmax(1.0, xmax));
+          // fp64 work of this round: factorization and the two triangular solves
+          const double md = m;
+          flops[2 * b] += md * md * md / 3.0 + 2.0 * md * md;
+        }
       }
       team_sync(tm);
       const double tol = lda(&tolv[b]);
@@ -1008,7 +1100,8 @@ __global__ __launch_bounds__(256) void k_value_team(double* __restrict__ W, doub
                                                     int32_t* __restrict__ status,
                                                     unsigned* __restrict__ bar,
                                                     int* __restrict__ err, int* __restrict__ xcc,
-                                                    int B, int t, int D, int tx) {
+                                                    double* __restrict__ flops, int B, int t,
+                                                    int D, int tx) {
   TeamSmem& sm = g_team_smem;
   Team tm;
   int team, nteams;
@@ -1019,6 +1112,10 @@ __global__ __launch_bounds__(256) void k_value_team(double* __restrict__ W, doub
     double* Wb = W + b * tt;
     double* Rb = R + static_cast<size_t>(b) * t * D;
     const int m = msz[b];
+    if (tm.rank == 0 && threadIdx.x == 0) {
+      const double md = m;
+      flops[2 * b + 1] = md * md * md / 3.0 + 2.0 * md * md * D;
+    }
     chol_team(Wb, t, m, tm, status, b);
     for (int c0 = tm.rank * 4; c0 < D; c0 += g * 4) chol_solve_cols(Wb, t, m, Rb, D, c0);
     team_sync(tm);
@@ -1198,7 +1295,7 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
     int* xcc = fb.xcc;
     void* args[] = {&H,        &cv,        &fb.W,    &fb.xs,   &fb.mask, &fb.Fidx, &fb.inv,
                     &fb.msz,   &fb.state,  &fb.tolv, &fb.wv,   &fb.viol, &status,  &fb.bar,
-                    &err,      &xcc,       &B,       &t,       &max_iters, &tx};
+                    &err,      &xcc,       &fb.flops, &B,      &t,       &max_iters, &tx};
     e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_nnls_team), dim3(grid),
                                    dim3(256), args, 0, st);
     if (e != hipSuccess) return e;
@@ -1226,7 +1323,7 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
     const int32_t* ms = fb.msz;
     int Dv = D;
     int* xcc = fb.xcc;
-    void* args[] = {&fb.W, &fb.R, &ms, &status, &fb.bar, &err, &xcc, &B, &t, &Dv, &tx};
+    void* args[] = {&fb.W, &fb.R, &ms, &status, &fb.bar, &err, &xcc, &fb.flops, &B, &t, &Dv, &tx};
     e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_value_team), dim3(grid),
                                    dim3(256), args, 0, st);
     if (e != hipSuccess) return e;

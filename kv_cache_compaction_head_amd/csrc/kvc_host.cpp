@@ -78,7 +78,7 @@ Plan make_plan(const kvc_params_t* p) {
 
 struct Layout {
   size_t ml, lse, Opart, O, imp_part, imp, idx, status, PS, H, W, cvec, xs, R, wv, lam, tolv,
-      colpart, mask, Fidx, inv, msz, state, viol, bar, xcc, part, total;
+      colpart, mask, Fidx, inv, msz, state, viol, bar, xcc, flops, part, total;
   size_t part_cap;
 };
 
@@ -120,6 +120,7 @@ Layout make_layout(const kvc_params_t* p) {
   L.viol = take(B * t * 4);
   L.bar = take(static_cast<size_t>(kvc::kBarWords) * 4);
   L.xcc = take(static_cast<size_t>(kvc::kMaxTeamGrid) * 4);
+  L.flops = take(B * 2 * 8);
   // split-K partials: up to 2048 * 4 tile slices of 64 x 64 doubles, never
   // more than the (already needed) t x t matrix per head times 4
   {
@@ -169,6 +170,7 @@ kvc::FitBufs fit_bufs(void* ws, const Layout& L) {
   fb.viol = at<int32_t>(ws, L.viol);
   fb.bar = at<unsigned>(ws, L.bar);
   fb.xcc = at<int32_t>(ws, L.xcc);
+  fb.flops = at<double>(ws, L.flops);
   fb.part = at<double>(ws, L.part);
   fb.part_cap = L.part_cap;
   fb.mask = at<int32_t>(ws, L.mask);
@@ -265,6 +267,7 @@ int kvc_workspace_layout(const kvc_params_t* p, kvc_ws_layout_t* out) {
   out->O = L.O;
   out->imp = L.imp;
   out->w = L.wv;
+  out->fit_flops = L.flops;
   return KVC_OK;
 }
 

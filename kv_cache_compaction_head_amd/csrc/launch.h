@@ -23,6 +23,7 @@ struct FitBufs {
   int32_t *mask, *Fidx, *inv, *msz, *state, *viol;
   unsigned* bar;  // kBarWords words: team barrier counters, the last one the timeout flag
   int32_t* xcc;   // kMaxTeamGrid words: each team workgroup's XCC id
+  double* flops;    // [B][2] fp64 work of the NNLS rounds and of the value solve
   double* part;     // split-K partial tiles of the fit GEMMs
   size_t part_cap;  // its capacity in doubles
 };

@@ -9,20 +9,15 @@
 //   values: min_C ||X C - O||^2 + lam_v ||C - V_S||^2,  X = P_S diag(w) / r
 // lam = ridge_rel * trace(Gram) / t pulls toward the prior (w = 1, C = V_S).
 //
-// Kernels (one per step, all batched over heads, per-head sizes read on the
-// device so nothing syncs with the host):
-//   k_ps          P_S = exp(Q C_k^T - lse) on fp64 MFMA (16x16x4)
-//   k_atb         C = A^T B tiles on fp64 MFMA (Grams, X^T O)
-//   k_bias_prep   lam_w, H = M + lam_w I, c = P_S^T 1 + lam_w, pivoting state
-//   k_bpp_index / k_gather_sub / k_bpp_update   block principal pivoting
-//                 (Judice & Pires 1994; Kim & Park 2011): solve on the passive
-//                 set, exchange every infeasible variable, fall back to single
-//                 exchanges (largest index) when the infeasible count stops
-//                 shrinking.  The passive-set system is solved by
-//   k_potrf_first / k_trsm_panel / k_syrk_update   right-looking blocked
-//                 Cholesky, 64 wide
-//   k_chol_solve  forward + back substitution, one wave per right-hand side
-//   k_value_prep, k_ridge_v, k_rhs_ridge, k_write_out   value fit plumbing.
+// Kernels (batched over heads; per-head sizes stay on the device, so nothing
+// syncs with the host):
+//   k_ps           P_S = exp(Q C_k^T - lse) on fp64 MFMA (16x16x4)
+//   k_atb          C = A^T B tiles on fp64 MFMA (Grams, X^T O), split-K
+//   k_bias_prep    lam_w, H = M + lam_w I, c = P_S^T 1 + lam_w
+//   k_nnls_sweep   block principal pivoting on the swept bias system
+//   k_value_prep, k_ridge_v, k_rhs_ridge   the value system
+//   k_value_sweep  its solve by the same block sweeps
+//   k_write_out    C_v and beta to the outputs.
 // Keys whose multiplier is pinned at zero carry a factor 1e-30 in X; their
 // coupling to the rest is ~1e-30 relative, so the value system is solved on
 // the passive set only and those keys keep C_v = V (the ridge prior).
@@ -33,7 +28,7 @@ namespace kvc {
 
 constexpr int kTile = 64;   // fp64 output tile (4 waves x 32x32)
 constexpr int kKC = 16;     // contraction rows staged per step
-constexpr int kNB = 64;     // Cholesky panel width
+constexpr int kSB = 64;     // sweep step: pivots per step, band height
 
 // ---------------------------------------------------------------------------
 // 64x64 fp64 tile product on MFMA.  sA, sB: [kKC][kTile] in LDS, k-major.
@@ -315,42 +310,34 @@ __device__ int block_count(int v, int* sh) {
   return s;
 }
 
-// Pivoting state per head: [0] done, [1] best infeasible count N, [2] backup
-// budget p, [3] rounds run.
-// H = M + lam_w I (M in H, full), c = colsum + lam_w, lam_w = ridge*tr(M)/t.
-// grid (B), block 1024.
-__global__ __launch_bounds__(1024) void k_bias_prep(double* __restrict__ H,
-                                                    double* __restrict__ cvec,
-                                                    double* __restrict__ lam,
-                                                    int32_t* __restrict__ mask,
-                                                    int32_t* __restrict__ state,
-                                                    double* __restrict__ wv, int t,
+// Bias system of head b in its sweep matrix (right-hand side in row 0,
+// variables from row 64; see the sweep engine below): the Gram M = P_S^T P_S
+// is already in the variable block; add lam_w = ridge * tr(M) / t to its
+// diagonal, store c = P_S^T 1 + lam_w in column 0 of the variable rows and
+// clear columns 1..63 (unused right-hand-side slots).  grid (B), block 1024.
+__global__ __launch_bounds__(1024) void k_bias_prep(double* __restrict__ S, size_t sS, int ld,
+                                                    const double* __restrict__ colsum,
+                                                    double* __restrict__ lam, int t,
                                                     double ridge) {
   __shared__ double sh[16];
   const int b = blockIdx.x;
-  double* Hb = H + static_cast<size_t>(b) * t * t;
+  double* Sb = S + b * sS;
   double tr = 0.0;
-  for (int a = threadIdx.x; a < t; a += blockDim.x) tr += Hb[static_cast<size_t>(a) * t + a];
+  for (int a = threadIdx.x; a < t; a += blockDim.x)
+    tr += Sb[static_cast<size_t>(kSB + a) * ld + kSB + a];
   tr = block_sum(tr, sh);
   const double lw = ridge * tr / t;
   for (int a = threadIdx.x; a < t; a += blockDim.x) {
-    Hb[static_cast<size_t>(a) * t + a] += lw;
-    cvec[static_cast<size_t>(b) * t + a] += lw;
-    mask[static_cast<size_t>(b) * t + a] = 1;
-    wv[static_cast<size_t>(b) * t + a] = 0.0;
+    double* row = Sb + static_cast<size_t>(kSB + a) * ld;
+    row[kSB + a] += lw;
+    row[0] = colsum[static_cast<size_t>(b) * t + a] + lw;
+    for (int c = 1; c < kSB; ++c) row[c] = 0.0;
   }
-  if (threadIdx.x == 0) {
-    lam[2 * b] = lw;
-    state[4 * b + 0] = 0;
-    state[4 * b + 1] = t + 1;
-    state[4 * b + 2] = 3;
-    state[4 * b + 3] = 0;
-  }
+  if (threadIdx.x == 0) lam[2 * b] = lw;
 }
 
-// ---------------------------------------------------------------------------
-// Teams.  The iterative parts of the fits (the pivoting rounds of the NNLS and
-// the value system's factorization and solve) run in one cooperative launch:
+// Teams.  The iterative parts of the fits (the NNLS pivoting rounds and the
+// value system's sweeps) run in cooperative launches:
 // each head gets a team of g co-resident workgroups synchronised by
 // team_sync, a barrier through a counter in global memory.
 //
@@ -456,672 +443,528 @@ __device__ void team_setup(Team& tm, int& team, int& nteams, unsigned* bar, int*
   tm.fast = s_ok != 0;
 }
 
-constexpr int kMaxTeamT = 4096;  // largest t the team kernels stage in LDS
-// Team kernels run 256 threads per workgroup; staging loops are unrolled on
-// that so every thread issues its loads back to back.
+constexpr int kMaxTeamT = 4096;            // largest t (variables of a sweep matrix)
+constexpr int kMaxRows = kMaxTeamT + 128;  // rows of a sweep matrix (right-hand sides first)
+// Team kernels run 256 threads per workgroup (4 waves, one 32 x 32 quadrant
+// of a 64 x 64 tile each).
 constexpr int kTeamThreads = 256;
 
-struct __align__(16) TeamSmem {
-  double sx[kMaxTeamT];
-  int sF[kMaxTeamT];
-  double sD[kNB][kNB + 1];
-  double sA[kKC * kTile];
-  double sB[kKC * kTile];
-  double col[2][kNB];
-  double vec[4][kNB];
-  double dpiv[kNB];
-  double rdiag[kNB];
+// ---------------------------------------------------------------------------
+// Block sweep engine.
+//
+// Both fits solve symmetric systems with the sweep operator (Goodnight 1979),
+// applied to up to 64 variables at a time.  For a symmetric A and an index
+// set F, sweeping F gives
+//     [ -A_FF^-1           A_FF^-1 A_FG              ]
+//     [  A_GF A_FF^-1      A_GG - A_GF A_FF^-1 A_FG  ].
+// Sweeping a set P whose members are partly in F (swept back out, sign
+// s = -1) and partly outside it (s = +1) is one rank-|P| update: with
+// B = A_PP^-1, U = A[:, P] and V = U B,
+//     A_ij -= V_i . U_j  (i, j not in P),   A_iP = V_iP s,   A_PP = -s B s.
+// The generic part is applied in factored form: with A_PP = L D L^T (L unit
+// lower, D the pivots, signs s), U B U^T = W D^-1 W^T for W = U L^-T, whose
+// terms are bounded by the diagonal as in a Cholesky update; U B U^T formed
+// through an explicit B loses everything when the pivot block is
+// ill-conditioned.  The pivot rows and columns are written from V and B
+// directly (folded into the update they would come out as differences of
+// terms of order 1 and of order |B|).
+//
+// A head's matrix is the lower triangle of S (leading dimension ld): rows
+// [0, r_al) are the right-hand sides (n_rhs of them), rows [r_al, r_al +
+// n_var) the variables.  Right-hand sides are never swept, so once F is swept
+// their columns hold A_FF^-1 b_F on F and b_G - A_GF A_FF^-1 b_F on G: the
+// passive-set solution and minus the gradient elsewhere (all the NNLS
+// pivoting rule reads), or the value fit's G^-1 R.
+//
+// One step (pivot set P, k <= 64) by a team:
+//   A. every member gathers A_PP and inverts it in LDS by k single sweeps
+//      (the pivot blocks are quasi-definite, so each pivot is nonzero with
+//      the sign s_q); the pivot rows of those sweeps also give L^-1 and D.
+//      The members split the 64-row bands, gather U for theirs, form
+//      W = U L^-T and V = U B on fp64 MFMA and stage both in global memory;
+//   -- team barrier --
+//   B. the members split the 64 x 64 tiles of the lower triangle and update
+//      them in place, A -= W D^-1 W^T on fp64 MFMA off the pivots (phase A
+//      copied every pivot column, so no tile is read by another member here);
+//   -- team barrier --
+// ---------------------------------------------------------------------------
+
+struct __align__(16) SweepSmem {
+  double pp[kSB][kSB + 1];         // pivot block, then its inverse B
+  double li[kSB * (kSB - 1) / 2];  // strictly lower part of L^-1, rows packed
+  double rD[kSB];                  // 1 / D (0 past k)
+  double bc[2][kSB];               // pivot-row broadcast of the small sweeps
+  double sgn[kSB];                 // s_q
+  int piv[kSB];                    // matrix row of pivot q
+  int16_t list[kMaxTeamT];         // NNLS: variables exchanged this round
+  int16_t pos[kMaxRows];           // matrix row -> pivot slot, -1 if not a pivot
+  uint8_t inF[kMaxTeamT];   // NNLS: passive set
   double red[16];
   int ired[16];
-  int scan[64];
+  int scan[16];
 };
 // The team kernels' LDS, at file scope so that the (non-inlined) helpers
 // address it as LDS rather than through generic pointers.
-__shared__ TeamSmem g_team_smem;
+__shared__ SweepSmem g_sw;
 
+struct SweepMat {
+  double* S;  // lower triangle, ld x ld
+  double* U;  // [rows][64] W = A[:, P] L^-T of the step
+  double* V;  // [rows][64] A[:, P] B
+  int ld, r_al, n_rhs, n_var;
+};
 
-// Factor sD[0:kb][0:kb] (lower) in place, 256 threads.  The block is padded
-// to 64 x 64 with the identity, so everything below is fixed-size and
-// branch-free: four 16-column micro-panels, each factored by wave 0 alone
-// (lane = row, the micro-panel's 16 values in registers, pivot and column
-// values broadcast with readlane, so the 16 column steps need no workgroup
-// barrier), followed by the rank-16 update of the trailing block on fp64
-// MFMA.  Upper-triangle entries are computed but never stored.  sm.rdiag
-// receives 1/L[c][c].  A pivot <= 0 is replaced by 1 and flags status bit 1.
-__device__ __forceinline__ double bcast(double v, int lane) {
-  const long long u = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_readlane(static_cast<int>(u & 0xffffffff), lane);
-  const int hi = __builtin_amdgcn_readlane(static_cast<int>(u >> 32), lane);
-  return __longlong_as_double((static_cast<long long>(hi) << 32) |
-                              static_cast<unsigned int>(lo));
+__device__ __forceinline__ double s_at(const SweepMat& M, int i, int j) {
+  return i >= j ? M.S[static_cast<size_t>(i) * M.ld + j] : M.S[static_cast<size_t>(j) * M.ld + i];
 }
-
-// 1/sqrt(x) for x > 0 to full double precision: hardware estimate, two
-// Newton steps y <- y (3 - x y^2) / 2.
-__device__ __forceinline__ double rsqrt_f64(double x) {
-  double y = __builtin_amdgcn_rsq(x);
-  y = y * fma(-0.5 * x * y, y, 1.5);
-  y = y * fma(-0.5 * x * y, y, 1.5);
-  return y;
+__device__ __forceinline__ bool s_active(const SweepMat& M, int s) {
+  return s < M.n_rhs || (s >= M.r_al && s < M.r_al + M.n_var);
 }
-
-__device__ __noinline__ void factor_diag(int kb, int32_t* status, int b) {
-  TeamSmem& sm = g_team_smem;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (kb < kNB) {
-    for (int e = tid; e < kNB * kNB; e += kTeamThreads) {
-      const int r = e >> 6, c = e & 63;
-      if (r >= kb || c >= kb) sm.sD[r][c] = r == c ? 1.0 : 0.0;
-    }
-    __syncthreads();
-  }
-  constexpr int MP = 16;
-#pragma unroll
-  for (int p = 0; p < kNB / MP; ++p) {
-    const int p0 = p * MP;
-    if (wave == 0) {
-      double a[MP];
-#pragma unroll
-      for (int j = 0; j < MP; ++j) a[j] = sm.sD[lane][p0 + j];
-      bool bad = false;
-#pragma unroll
-      for (int c = 0; c < MP; ++c) {
-        double piv = bcast(a[c], p0 + c);
-        bad |= !(piv > 0.0);
-        piv = piv > 0.0 ? piv : 1.0;
-        const double y = rsqrt_f64(piv);
-        a[c] = lane > p0 + c ? a[c] * y : (lane == p0 + c ? piv * y : a[c]);
-        if (lane == 0) sm.rdiag[p0 + c] = y;
-#pragma unroll
-        for (int j = c + 1; j < MP; ++j) a[j] = fma(-a[c], bcast(a[c], p0 + j), a[j]);
-      }
-      if (bad && lane == 0 && status) atomicOr(&status[b], 1);
-#pragma unroll
-      for (int j = 0; j < MP; ++j)
-        if (p0 + j <= lane) sm.sD[lane][p0 + j] = a[j];
-    }
-    __syncthreads();
-    if (p + 1 < kNB / MP) {
-      // trailing rows/cols [p0+16, 64): C -= P P^T, P = columns p0..p0+15
-      const int t0 = p0 + MP, nt = (kNB - t0) / 16;
-      for (int tau = wave; tau < nt * nt; tau += 4) {
-        const int R = t0 + 16 * (tau / nt), Cc = t0 + 16 * (tau % nt);
-        f64x4 acc = {};
-#pragma unroll
-        for (int ks = 0; ks < MP / 4; ++ks) {
-          const int k = p0 + 4 * ks + (lane >> 4);
-          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(sm.sD[R + (lane & 15)][k],
-                                                     sm.sD[Cc + (lane & 15)][k], acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm.sD[R + (lane >> 4) + 4 * i][Cc + (lane & 15)] -= acc[i];
-      }
-      __syncthreads();
-    }
-  }
-}
-
-__device__ void load_diag(const double* W, int ld, int k, int kb) {
-  TeamSmem& sm = g_team_smem;
-  double v[kNB * kNB / kTeamThreads];
-#pragma unroll
-  for (int i = 0; i < kNB * kNB / kTeamThreads; ++i) {
-    const int e = threadIdx.x + i * kTeamThreads, r = e >> 6, c = e & 63;
-    v[i] = (r < kb && c <= r) ? ldc(&W[static_cast<size_t>(k + r) * ld + k + c]) : 0.0;
-  }
-#pragma unroll
-  for (int i = 0; i < kNB * kNB / kTeamThreads; ++i) {
-    const int e = threadIdx.x + i * kTeamThreads;
-    sm.sD[e >> 6][e & 63] = v[i];
-  }
-  __syncthreads();
-  if (threadIdx.x < kNB) sm.rdiag[threadIdx.x] = threadIdx.x < kb ? 1.0 / sm.sD[threadIdx.x][threadIdx.x] : 0.0;
-  __syncthreads();
-}
-
-__device__ void store_diag(double* W, int ld, int k, int kb) {
-  const TeamSmem& sm = g_team_smem;
-  for (int e = threadIdx.x; e < kNB * kNB; e += blockDim.x) {
-    const int r = e >> 6, c = e & 63;
-    if (r < kb && c <= r) stc(&W[static_cast<size_t>(k + r) * ld + k + c], sm.sD[r][c]);
-  }
-  __syncthreads();
-}
-
-// Rows [r0, r1) of the panel at column k: L[i, k:k+64] = A[i, k:k+64] L_kk^{-T}
-// with L_kk in sm.sD.  One thread per row; each half row (32 values) is loaded
-// in one batch before the substitution uses it.
-__device__ __noinline__ void trsm_rows(double* W, int ld, int k, int r0, int r1) {
-  const TeamSmem& sm = g_team_smem;
-  const int i = r0 + threadIdx.x;
-  if (i >= r1) return;
-  double* row = W + static_cast<size_t>(i) * ld + k;
-  constexpr int H = kNB / 2;
-  double x[H], y[H];
-#pragma unroll
-  for (int c = 0; c < H; ++c) x[c] = ldc(&row[c]);
-#pragma unroll
-  for (int c = 0; c < H; ++c) y[c] = ldc(&row[H + c]);
-// independent partial sums shorten the dependent chains 4x
-#pragma unroll
-  for (int c = 0; c < H; ++c) {
-    double v0 = x[c], v1 = 0.0, v2 = 0.0, v3 = 0.0;
-#pragma unroll
-    for (int e = 0; e + 3 < c; e += 4) {
-      v0 -= x[e] * sm.sD[c][e];
-      v1 -= x[e + 1] * sm.sD[c][e + 1];
-      v2 -= x[e + 2] * sm.sD[c][e + 2];
-      v3 -= x[e + 3] * sm.sD[c][e + 3];
-    }
-#pragma unroll
-    for (int e = c & ~3; e < c; ++e) v0 -= x[e] * sm.sD[c][e];
-    x[c] = ((v0 + v1) + (v2 + v3)) * sm.rdiag[c];
-  }
-#pragma unroll
-  for (int c = 0; c < H; ++c) {
-    double v0 = y[c], v1 = 0.0, v2 = 0.0, v3 = 0.0;
-#pragma unroll
-    for (int e = 0; e < H; e += 4) {
-      v0 -= x[e] * sm.sD[H + c][e];
-      v1 -= x[e + 1] * sm.sD[H + c][e + 1];
-      v2 -= x[e + 2] * sm.sD[H + c][e + 2];
-      v3 -= x[e + 3] * sm.sD[H + c][e + 3];
-    }
-#pragma unroll
-    for (int e = 0; e + 3 < c; e += 4) {
-      v0 -= y[e] * sm.sD[H + c][H + e];
-      v1 -= y[e + 1] * sm.sD[H + c][H + e + 1];
-      v2 -= y[e + 2] * sm.sD[H + c][H + e + 2];
-      v3 -= y[e + 3] * sm.sD[H + c][H + e + 3];
-    }
-#pragma unroll
-    for (int e = c & ~3; e < c; ++e) v0 -= y[e] * sm.sD[H + c][H + e];
-    y[c] = ((v0 + v1) + (v2 + v3)) * sm.rdiag[H + c];
-  }
-#pragma unroll
-  for (int c = 0; c < H; ++c) stc(&row[c], x[c]);
-#pragma unroll
-  for (int c = 0; c < H; ++c) stc(&row[H + c], y[c]);
-}
-
-// One lower tile of the trailing update after panel k; tile 0 (the next
-// diagonal block) is then factored in place.
-__device__ __noinline__ void syrk_tile(double* W, int ld, int m, int k, int tau, int32_t* status,
-                                       int b) {
-  TeamSmem& sm = g_team_smem;
-  const int s0 = k + kNB;
-  int ty, tx;
-  tri_decode(tau, ty, tx);
-  const int r0 = s0 + ty * kTile, c0 = s0 + tx * kTile;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  f64x4 acc[2][2] = {};
-  constexpr int NE = kKC * kTile / kTeamThreads;
-  constexpr int NCH = kNB / kKC;
-  double va[NCH][NE], vb[NCH][NE];
-#pragma unroll
-  for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-    for (int q = 0; q < NE; ++q) {
-      const int e = threadIdx.x + q * kTeamThreads, r = e / kKC, c = e % kKC;
-      const int i = r0 + r, j = c0 + r;
-      va[ch][q] = i < m ? ldc(&W[static_cast<size_t>(i) * ld + k + ch * kKC + c]) : 0.0;
-      vb[ch][q] = j < m ? ldc(&W[static_cast<size_t>(j) * ld + k + ch * kKC + c]) : 0.0;
-    }
-#pragma unroll
-  for (int ch = 0; ch < NCH; ++ch) {
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < NE; ++q) {
-      const int e = threadIdx.x + q * kTeamThreads, r = e / kKC, c = e % kKC;
-      sm.sA[c * kTile + r] = va[ch][q];
-      sm.sB[c * kTile + r] = vb[ch][q];
-    }
-    __syncthreads();
-    tile_mma(sm.sA, sm.sB, acc, wave, lane);
-  }
-  const bool diag = tau == 0;
-#pragma unroll
-  for (int ra = 0; ra < 2; ++ra)
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = tile_row(wave, lane, ra, i), cc = tile_col(wave, lane, rb);
-        const int r = r0 + rr, c = c0 + cc;
-        if (r < m && c <= r) {
-          double* p = &W[static_cast<size_t>(r) * ld + c];
-          const double v = ldc(p) - acc[ra][rb][i];
-          if (diag) sm.sD[rr][cc] = v;
-          else stc(p, v);
-        } else if (diag) {
-          sm.sD[rr][cc] = 0.0;
-        }
-      }
-  __syncthreads();
-  if (!diag) return;
-  const int kb = min(kNB, m - s0);
-  factor_diag(kb, status, b);
-  store_diag(W, ld, s0, kb);
-}
-
-// Blocked right-looking Cholesky of the m x m lower triangle of W by a team:
-// panel rows split over members by 256-row chunks, trailing tiles round-robin.
-__device__ __noinline__ void chol_team(double* W, int ld, int m, Team& tm, int32_t* status,
-                                       int b) {
-  if (m > 0 && tm.rank == 0) {
-    const int kb = min(kNB, m);
-    load_diag(W, ld, 0, kb);
-    factor_diag(kb, status, b);
-    store_diag(W, ld, 0, kb);
-  }
-  team_sync(tm);
-  for (int k = 0; k + kNB < m; k += kNB) {
-    const int below = m - k - kNB;
-    const int nchunk = (below + 255) / 256;
-    if (tm.rank < nchunk) {
-      load_diag(W, ld, k, kNB);
-      for (int ch = tm.rank; ch < nchunk; ch += tm.size)
-        trsm_rows(W, ld, k, k + kNB + ch * 256, m);
-    }
-    team_sync(tm);
-    const int nt = (below + kTile - 1) / kTile;
-    const int ntiles = nt * (nt + 1) / 2;
-    for (int tau = tm.rank; tau < ntiles; tau += tm.size) syrk_tile(W, ld, m, k, tau, status, b);
-    team_sync(tm);
-  }
-}
-
-// Solve L L^T Y = Y in place for columns [c0, c0+4) of Y [m][ncol] (row stride
-// ncol), one wave per column (ncol = 1 for a vector).  The waves walk the
-// diagonal blocks together: block staged in LDS, triangle with lane = row,
-// then the off-diagonal rows.  All accesses coherent (ldc/stc).
-__device__ __noinline__ void chol_solve_cols(const double* L, int ld, int m, double* Y, int ncol,
-                                             int c0) {
-  TeamSmem& sm = g_team_smem;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int col = c0 + wave;
-  const bool on = col < ncol;
-  for (int kb = 0; kb < m; kb += kNB) {
-    const int nb = min(kNB, m - kb);
-    __syncthreads();
-    load_diag(L, ld, kb, nb);
-    if (on) {
-      double v = lane < nb ? ldc(&Y[static_cast<size_t>(kb + lane) * ncol + col]) : 0.0;
-      for (int e = 0; e < nb; ++e) {
-        if (lane == e) v *= sm.rdiag[e];
-        const double ve = bcast(v, e);
-        if (lane > e && lane < nb) v -= sm.sD[lane][e] * ve;
-      }
-      if (lane < nb) stc(&Y[static_cast<size_t>(kb + lane) * ncol + col], v);
-      sm.vec[wave][lane] = lane < nb ? v : 0.0;
-      for (int r2 = kb + nb + lane; r2 < m; r2 += 64) {
-        const double* row = L + static_cast<size_t>(r2) * ld + kb;
-        double* py = &Y[static_cast<size_t>(r2) * ncol + col];
-        const double yv = ldc(py);
-        double acc = 0.0;
-#pragma unroll 1
-        for (int e0 = 0; e0 < kNB; e0 += 16) {
-          double lv[16];
-#pragma unroll
-          for (int e = 0; e < 16; ++e) lv[e] = e0 + e < nb ? ldc(&row[e0 + e]) : 0.0;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc += lv[e] * sm.vec[wave][e0 + e];
-        }
-        stc(py, yv - acc);
-      }
-    }
-  }
-  const int nblk = (m + kNB - 1) / kNB;
-  for (int bi = nblk - 1; bi >= 0; --bi) {
-    const int kb = bi * kNB, nb = min(kNB, m - kb);
-    __syncthreads();
-    load_diag(L, ld, kb, nb);
-    if (on) {
-      double v = lane < nb ? ldc(&Y[static_cast<size_t>(kb + lane) * ncol + col]) : 0.0;
-      for (int e = nb - 1; e >= 0; --e) {
-        if (lane == e) v *= sm.rdiag[e];
-        const double ve = bcast(v, e);
-        if (lane < e) v -= sm.sD[e][lane] * ve;
-      }
-      if (lane < nb) stc(&Y[static_cast<size_t>(kb + lane) * ncol + col], v);
-      sm.vec[wave][lane] = lane < nb ? v : 0.0;
-      for (int r2 = lane; r2 < kb; r2 += 64) {
-        double* py = &Y[static_cast<size_t>(r2) * ncol + col];
-        const double yv = ldc(py);
-        double acc = 0.0;
-#pragma unroll 1
-        for (int e0 = 0; e0 < kNB; e0 += 16) {
-          double lv[16];
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            lv[e] = e0 + e < nb ? ldc(&L[static_cast<size_t>(kb + e0 + e) * ld + r2]) : 0.0;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc += lv[e] * sm.vec[wave][e0 + e];
-        }
-        stc(py, yv - acc);
-      }
-    }
-  }
-  __syncthreads();
-}
-
-// Solve L L^T y = y for one vector with a whole workgroup: diagonal blocks
-// staged in LDS and solved by wave 0 (lane = row), the off-diagonal updates
-// spread over all 256 threads, four threads per row each loading 16 values in
-// one batch and combining with shuffles.
-__device__ __noinline__ void chol_solve_vec(const double* L, int ld, int m, double* y) {
-  TeamSmem& sm = g_team_smem;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int quad = tid & 3, rsub = tid >> 2;  // 64 rows per pass, 4 threads each
-  for (int kb = 0; kb < m; kb += kNB) {
-    const int nb = min(kNB, m - kb);
-    __syncthreads();
-    load_diag(L, ld, kb, nb);
-    if (wave == 0) {
-      double v = lane < nb ? y[kb + lane] : 0.0;
-      for (int e = 0; e < nb; ++e) {
-        if (lane == e) v *= sm.rdiag[e];
-        const double ve = bcast(v, e);
-        if (lane > e && lane < nb) v -= sm.sD[lane][e] * ve;
-      }
-      if (lane < nb) y[kb + lane] = v;
-      sm.vec[0][lane] = lane < nb ? v : 0.0;
-    }
-    __syncthreads();
-    for (int r0 = kb + nb; r0 < m; r0 += 64) {
-      const int r2 = r0 + rsub;
-      const double* row = L + static_cast<size_t>(r2 < m ? r2 : kb) * ld + kb + quad * 16;
-      double lv[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) lv[e] = (r2 < m && quad * 16 + e < nb) ? row[e] : 0.0;
-      double acc = 0.0;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc += lv[e] * sm.vec[0][quad * 16 + e];
-      acc += __shfl_xor(acc, 1);
-      acc += __shfl_xor(acc, 2);
-      if (quad == 0 && r2 < m) y[r2] -= acc;
-    }
-  }
-  const int nblk = (m + kNB - 1) / kNB;
-  for (int bi = nblk - 1; bi >= 0; --bi) {
-    const int kb = bi * kNB, nb = min(kNB, m - kb);
-    __syncthreads();
-    load_diag(L, ld, kb, nb);
-    if (wave == 0) {
-      double v = lane < nb ? y[kb + lane] : 0.0;
-      for (int e = nb - 1; e >= 0; --e) {
-        if (lane == e) v *= sm.rdiag[e];
-        const double ve = bcast(v, e);
-        if (lane < e) v -= sm.sD[e][lane] * ve;
-      }
-      if (lane < nb) y[kb + lane] = v;
-      sm.vec[0][lane] = lane < nb ? v : 0.0;
-    }
-    __syncthreads();
-    // y[r2] -= sum_e L[kb+e][r2] x_e for r2 < kb: thread per r2, 16-value batches
-    for (int r2 = tid; r2 < kb; r2 += kTeamThreads) {
-      double acc = 0.0;
-#pragma unroll 1
-      for (int e0 = 0; e0 < kNB; e0 += 16) {
-        double lv[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          lv[e] = e0 + e < nb ? L[static_cast<size_t>(kb + e0 + e) * ld + r2] : 0.0;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc += lv[e] * sm.vec[0][e0 + e];
-      }
-      y[r2] -= acc;
-    }
-  }
-  __syncthreads();
-}
-
-// Passive index list F (ascending), inverse map, |F|, rhs = c[F]; one workgroup.
-__device__ __noinline__ void build_index(const int32_t* mk, const double* cb, int32_t* F,
-                                         int32_t* inv, int32_t* msz, double* rhs, int t) {
-  TeamSmem& sm = g_team_smem;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
-  const int chunk = (t + blockDim.x - 1) / blockDim.x;
-  const int c0 = min(t, tid * chunk), c1 = min(t, c0 + chunk);
-  int cnt = 0;
-  for (int j = c0; j < c1; ++j) cnt += ldc(&mk[j]) != 0;
-  int x = cnt;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) sm.scan[wave] = x;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += sm.scan[w];
-  int pos = base + x - cnt;
-  for (int j = c0; j < c1; ++j) {
-    if (ldc(&mk[j])) {
-      stc(&F[pos], j);
-      stc(&inv[j], pos);
-      if (rhs) stc(&rhs[pos], cb[j]);
-      ++pos;
-    } else {
-      stc(&inv[j], -1);
-    }
-  }
-  if (tid == 0) {
-    int tot = 0;
-    for (int w = 0; w < nw; ++w) tot += sm.scan[w];
-    sta(msz, tot);
-  }
-  __syncthreads();
+// L^-1[c][q] for c, q < 64 (identity past k)
+__device__ __forceinline__ double li_at(int c, int q, int k) {
+  if (c >= k || q >= k) return c == q ? 1.0 : 0.0;
+  return c > q ? g_sw.li[c * (c - 1) / 2 + q] : (c == q ? 1.0 : 0.0);
 }
 
 __device__ double wg_max(double v) {
-  TeamSmem& sm = g_team_smem;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  SweepSmem& sm = g_sw;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off));
   __syncthreads();
   if (lane == 0) sm.red[wave] = v;
   __syncthreads();
   double s = -INFINITY;
-  for (int w = 0; w < nw; ++w) s = fmax(s, sm.red[w]);
-  __syncthreads();
-  return s;
-}
-
-__device__ int wg_isum(int v) {
-  TeamSmem& sm = g_team_smem;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  __syncthreads();
-  if (lane == 0) sm.ired[wave] = v;
-  __syncthreads();
-  int s = 0;
-  for (int w = 0; w < nw; ++w) s += sm.ired[w];
-  __syncthreads();
+  for (int w = 0; w < kTeamThreads / 64; ++w) s = fmax(s, sm.red[w]);
   return s;
 }
 
 __device__ int wg_imax(int v) {
-  TeamSmem& sm = g_team_smem;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  SweepSmem& sm = g_sw;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off));
   __syncthreads();
   if (lane == 0) sm.ired[wave] = v;
   __syncthreads();
   int s = -1;
-  for (int w = 0; w < nw; ++w) s = max(s, sm.ired[w]);
-  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kTeamThreads / 64; ++w) s = max(s, sm.ired[w]);
   return s;
 }
 
+// Order-preserving append: every thread with f set gets slot base + (number
+// of set flags in lower threads); returns base + total.  *slot = its slot.
+__device__ int wg_append(bool f, int base, int* slot) {
+  SweepSmem& sm = g_sw;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const unsigned long long m = __ballot(f);
+  const int below = __popcll(m & ((1ull << lane) - 1ull));
+  __syncthreads();
+  if (lane == 0) sm.scan[wave] = __popcll(m);
+  __syncthreads();
+  int off = base, tot = base;
+#pragma unroll
+  for (int w = 0; w < kTeamThreads / 64; ++w) {
+    const int c = sm.scan[w];
+    off += w < wave ? c : 0;
+    tot += c;
+  }
+  *slot = off + below;
+  return tot;
+}
+
+// sm.pp[0:k][0:k] <- its inverse (the rest 0), by k single sweeps on 256
+// threads (thread: row tid/4, 16 columns).  The block is symmetric, so the
+// pivot row doubles as the pivot column.  Before sweep p, row p holds
+// -L^-1[p][j] at the swept columns j < p and the pivot D[p] on the diagonal
+// (A_PP = L D L^T); both are recorded (sm.li, sm.rD).  A pivot without the
+// sign s_p is replaced by s_p (the system is not numerically definite);
+// returns whether that happened.
+__device__ __noinline__ bool small_inverse(int k) {
+  SweepSmem& sm = g_sw;
+  const int tid = threadIdx.x, r = tid >> 2, c0 = (tid & 3) * 16;
+  double a[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) a[j] = sm.pp[r][c0 + j];
+  bool bad = false;
+  for (int p = 0; p < k; ++p) {
+    double* bc = sm.bc[p & 1];
+    if (r == p) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        bc[c0 + j] = a[j];
+        if (c0 + j < p) sm.li[p * (p - 1) / 2 + c0 + j] = -a[j];
+      }
+    }
+    __syncthreads();
+    double d = bc[p];
+    const double sg = sm.sgn[p];
+    if (!(d * sg > 0.0)) {
+      bad = true;
+      d = sg;
+    }
+    const double rd = 1.0 / d;
+    if (tid == 0) sm.rD[p] = rd;
+    const double f = bc[r] * rd;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int c = c0 + j;
+      const double rc = bc[c];
+      const double upd = fma(-f, rc, a[j]);
+      a[j] = r == p ? (c == p ? -rd : rc * rd) : (c == p ? f : upd);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int c = c0 + j;
+    sm.pp[r][c] = (r < k && c < k) ? -a[j] : 0.0;
+  }
+  if (tid >= k && tid < kSB) sm.rD[tid] = 0.0;
+  __syncthreads();
+  return bad;
+}
+
+// Phase A for one 64-row band (matrix rows band*64 ..): U = A[rows, P]
+// gathered from the lower triangle, W = U L^-T and V = U B on MFMA, stored
+// to M.U / M.V.
+// The contraction index is permuted so that each lane's 16 values of a row
+// are contiguous: in MFMA step kk, lane l supplies q = 16*(l/16) + kk.
+__device__ __noinline__ void v_band(const SweepMat& M, int band, int k) {
+  SweepSmem& sm = g_sw;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wr = wave >> 1, wc = wave & 1, g16 = lane >> 4, l16 = lane & 15;
+  double u[2][16];
+#pragma unroll
+  for (int ra = 0; ra < 2; ++ra) {
+    const int s = band * kSB + wr * 32 + ra * 16 + l16;
+    const bool act = s_active(M, s);
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const int q = g16 * 16 + kk;
+      u[ra][kk] = (act && q < k) ? s_at(M, s, sm.piv[q]) : 0.0;
+    }
+  }
+  f64x4 acc[2][2] = {}, accw[2][2] = {};
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk) {
+    const int q = g16 * 16 + kk;
+    double bb[2], bl[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int c = wc * 32 + rb * 16 + l16;
+      bb[rb] = sm.pp[q][c];
+      bl[rb] = li_at(c, q, k);
+    }
+#pragma unroll
+    for (int ra = 0; ra < 2; ++ra)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        acc[ra][rb] = __builtin_amdgcn_mfma_f64_16x16x4f64(u[ra][kk], bb[rb], acc[ra][rb], 0, 0, 0);
+        accw[ra][rb] = __builtin_amdgcn_mfma_f64_16x16x4f64(u[ra][kk], bl[rb], accw[ra][rb], 0, 0, 0);
+      }
+  }
+#pragma unroll
+  for (int ra = 0; ra < 2; ++ra)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t s = static_cast<size_t>(band * kSB + wr * 32 + ra * 16 + g16 + 4 * i);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int c = wc * 32 + rb * 16 + l16;
+        M.V[s * kSB + c] = acc[ra][rb][i];
+        M.U[s * kSB + c] = accw[ra][rb][i];
+      }
+    }
+}
+
+// Phase B for tile (I, J) of the lower triangle (bands I >= J): entries off
+// the pivots get T -= W_I D^-1 W_J^T; pivot columns V_iq s_q, pivot rows
+// V_jq s_q and the pivot block -s_q s_q' B[q][q'] are written directly.
+__device__ __noinline__ void sweep_tile(const SweepMat& M, int I, int J) {
+  SweepSmem& sm = g_sw;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wr = wave >> 1, wc = wave & 1, g16 = lane >> 4, l16 = lane & 15;
+  const bool diag = I == J;
+  if (diag && wr < wc) return;  // strictly upper quadrant of a diagonal tile
+  double va[2][16], ub[2][16], tv[2][2][4];
+#pragma unroll
+  for (int ra = 0; ra < 2; ++ra) {
+    const double* p = M.U + static_cast<size_t>(I * kSB + wr * 32 + ra * 16 + l16) * kSB + g16 * 16;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) va[ra][kk] = p[kk] * sm.rD[g16 * 16 + kk];
+  }
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const double* p = M.U + static_cast<size_t>(J * kSB + wc * 32 + rb * 16 + l16) * kSB + g16 * 16;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) ub[rb][kk] = p[kk];
+  }
+  int pc[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int c = J * kSB + wc * 32 + rb * 16 + l16;
+    pc[rb] = s_active(M, c) ? sm.pos[c] : -1;
+  }
+#pragma unroll
+  for (int ra = 0; ra < 2; ++ra)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = I * kSB + wr * 32 + ra * 16 + g16 + 4 * i;
+      const int pr = s_active(M, r) ? sm.pos[r] : -1;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int c = J * kSB + wc * 32 + rb * 16 + l16;
+        double v = 0.0;
+        if (pr >= 0 && pc[rb] >= 0) v = -sm.sgn[pr] * sm.sgn[pc[rb]] * sm.pp[pr][pc[rb]];
+        else if (pc[rb] >= 0) v = sm.sgn[pc[rb]] * M.V[static_cast<size_t>(r) * kSB + pc[rb]];
+        else if (pr >= 0) v = sm.sgn[pr] * M.V[static_cast<size_t>(c) * kSB + pr];
+        else if (!diag || r >= c) v = M.S[static_cast<size_t>(r) * M.ld + c];
+        tv[ra][rb][i] = v;
+      }
+    }
+  f64x4 acc[2][2] = {};
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk)
+#pragma unroll
+    for (int ra = 0; ra < 2; ++ra)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+        acc[ra][rb] = __builtin_amdgcn_mfma_f64_16x16x4f64(va[ra][kk], ub[rb][kk], acc[ra][rb], 0, 0, 0);
+#pragma unroll
+  for (int ra = 0; ra < 2; ++ra)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = I * kSB + wr * 32 + ra * 16 + g16 + 4 * i;
+      const bool prow = s_active(M, r) && sm.pos[r] >= 0;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int c = J * kSB + wc * 32 + rb * 16 + l16;
+        if (diag && r < c) continue;
+        const double v = (prow || pc[rb] >= 0) ? tv[ra][rb][i] : tv[ra][rb][i] - acc[ra][rb][i];
+        M.S[static_cast<size_t>(r) * M.ld + c] = v;
+      }
+    }
+}
+
+// One sweep step over the k pivots in sm.piv / sm.sgn / sm.pos, by the team.
+// Tiles whose row band is a variable band below skip_below (and whose column
+// is a variable band) are left alone: the value fit never reads them again.
+// Returns whether a pivot had the wrong sign.
+__device__ __noinline__ bool sweep_step(const SweepMat& M, Team& tm, int k, int skip_below) {
+  SweepSmem& sm = g_sw;
+  for (int e = threadIdx.x; e < kSB * kSB; e += kTeamThreads) {
+    const int a = e >> 6, c = e & 63;
+    sm.pp[a][c] = (a < k && c < k) ? s_at(M, sm.piv[a], sm.piv[c]) : (a == c ? 1.0 : 0.0);
+  }
+  __syncthreads();
+  const bool bad = small_inverse(k);
+  const int nrb = (M.n_rhs + kSB - 1) / kSB, nvb = (M.n_var + kSB - 1) / kSB;
+  const int vb0 = M.r_al / kSB;
+  for (int bi = tm.rank; bi < nrb + nvb; bi += tm.size) v_band(M, bi < nrb ? bi : vb0 + bi - nrb, k);
+  team_sync(tm);
+  // tiles: variable band I (0..nvb-1) owns nrb right-hand-side tiles, then
+  // variable tiles J = 0..I
+  const int ntiles = nvb * nrb + nvb * (nvb + 1) / 2;
+  int I = 0, first = 0;
+  for (int tau = tm.rank; tau < ntiles; tau += tm.size) {
+    while (tau - first >= nrb + I + 1) {
+      first += nrb + I + 1;
+      ++I;
+    }
+    const int j = tau - first;
+    if (j >= nrb && I < skip_below) continue;
+    sweep_tile(M, vb0 + I, j < nrb ? j : vb0 + j - nrb);
+  }
+  team_sync(tm);
+  return bad;
+}
+
+__device__ __forceinline__ double sweep_flops(int k, int n) {
+  const double kd = k, nd = n;
+  return kd * nd * nd + 2.0 * nd * kd * kd + kd * kd * kd;
+}
+
 // ---------------------------------------------------------------------------
-// NNLS by block principal pivoting, one team per head (cooperative launch).
-// Round: passive list -> gather H_FF -> Cholesky -> solve -> infeasibility of
-// every variable -> exchange rule.  The loop stops as soon as the head's
-// point is feasible and optimal (KKT), or at max_iters (status bit 2).
-// State per head: [0] done (1 ok, 2 capped), [1] best infeasible count,
-// [2] backup budget, [3] rounds; tolv[b] the round's gradient tolerance.
+// NNLS by block principal pivoting (Judice & Pires 1994; Kim & Park 2011) on
+// the swept system [H c; c^T .] of each head, one team per head.  Start from
+// the empty passive set (x = 0, gradient -c); each round reads x_F and the
+// gradient from the right-hand-side column, exchanges every infeasible
+// variable while the infeasible count keeps falling (three more tries after
+// it stops), else only the one with the largest index, and sweeps the
+// exchanged variables in or out.  Stops at the KKT point or after max_iters
+// exchanges (status bit 2, w = max(x, 0)).  Every member runs the rule on the
+// same data, so the rule needs no barrier.  Output: w, and the passive list
+// (support of w) for the value fit.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_nnls_team(
-    const double* __restrict__ H, const double* __restrict__ cvec, double* __restrict__ W,
-    double* __restrict__ xs, int32_t* __restrict__ mask, int32_t* __restrict__ Fidx,
-    int32_t* __restrict__ inv, int32_t* __restrict__ msz, int32_t* __restrict__ state,
-    double* __restrict__ tolv, double* __restrict__ wv, int32_t* __restrict__ viol,
-    int32_t* __restrict__ status, unsigned* __restrict__ bar, int* __restrict__ err,
-    int* __restrict__ xcc, double* __restrict__ flops, int B, int t, int max_iters, int tx) {
-  TeamSmem& sm = g_team_smem;
+__global__ __launch_bounds__(256) void k_nnls_sweep(
+    double* __restrict__ S, size_t sS, int ld, double* __restrict__ Ub, double* __restrict__ Vb,
+    size_t sUV, double* __restrict__ wv, int32_t* __restrict__ Fidx, int32_t* __restrict__ inv,
+    int32_t* __restrict__ msz, int32_t* __restrict__ status, unsigned* __restrict__ bar,
+    int* __restrict__ err, int* __restrict__ xcc, double* __restrict__ flops, int B, int t,
+    int max_iters, int tx) {
+  SweepSmem& sm = g_sw;
   Team tm;
   int team, nteams;
   team_setup(tm, team, nteams, bar, err, xcc, tx);
-  const int g = tm.size;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x;
+  for (int s = tid; s < kMaxRows; s += kTeamThreads) sm.pos[s] = -1;
+  constexpr int NV = kMaxTeamT / kTeamThreads;
   for (int b = team; b < B; b += nteams) {
-    const size_t tt = static_cast<size_t>(t) * t;
-    if (tm.rank == 0 && tid == 0) flops[2 * b] = 0.0;
-    const double* Hb = H + b * tt;
-    const double* cb = cvec + static_cast<size_t>(b) * t;
-    double* Wb = W + b * tt;
-    double* xb = xs + static_cast<size_t>(b) * t;
-    int32_t* mk = mask + static_cast<size_t>(b) * t;
-    int32_t* Fb = Fidx + static_cast<size_t>(b) * t;
-    int32_t* ib = inv + static_cast<size_t>(b) * t;
-    int32_t* vb = viol + static_cast<size_t>(b) * t;
-    int32_t* st = state + 4 * b;
-    double* w = wv + static_cast<size_t>(b) * t;
-    for (int it = 0; it < max_iters; ++it) {
-      if (tm.rank == 0) build_index(mk, cb, Fb, ib, &msz[b], xb, t);
-      team_sync(tm);
-      const int m = lda(&msz[b]);
-      for (int a = tid; a < m; a += kTeamThreads) sm.sF[a] = ldc(&Fb[a]);
-      __syncthreads();
-      for (int a = tm.rank; a < m; a += g) {
-        const double* hr = Hb + static_cast<size_t>(sm.sF[a]) * t;
-        for (int a2 = tid; a2 <= a; a2 += kTeamThreads)
-          stc(&Wb[static_cast<size_t>(a) * t + a2], hr[sm.sF[a2]]);
-      }
-      team_sync(tm);
-      chol_team(Wb, t, m, tm, status, b);
-      if (tm.rank == 0) {
-        chol_solve_vec(Wb, t, m, xb);
-        double cmax = 0.0, hmax = 0.0, xmax = 0.0;
-        for (int j = tid; j < t; j += blockDim.x) {
-          cmax = fmax(cmax, fabs(cb[j]));
-          hmax = fmax(hmax, Hb[static_cast<size_t>(j) * t + j]);
-        }
-        for (int a = tid; a < m; a += blockDim.x) xmax = fmax(xmax, fabs(ldc(&xb[a])));
-        cmax = wg_max(cmax);
-        hmax = wg_max(hmax);
-        xmax = wg_max(xmax);
-        if (tid == 0) {
-          sta(&tolv[b], 1e-13 * fmax(cmax, hmax) * fmax(1.0, xmax));
-          // fp64 work of this round: factorization and the two triangular solves
-          const double md = m;
-          flops[2 * b] += md * md * md / 3.0 + 2.0 * md * md;
-        }
-      }
-      team_sync(tm);
-      const double tol = lda(&tolv[b]);
-      // full-length solution (zero off F) in LDS, then infeasibility: a wave
-      // per variable, gradient y_j = H[j,:] x - c_j over the whole row
-      for (int j = tid; j < t; j += kTeamThreads) sm.sx[j] = 0.0;
-      __syncthreads();
-      for (int a = tid; a < m; a += kTeamThreads) sm.sx[sm.sF[a]] = ldc(&xb[a]);
-      __syncthreads();
-      for (int j = tm.rank * 4 + wave; j < t; j += g * 4) {
-        int v = 0;
-        if (ldc(&mk[j])) {
-          v = sm.sx[j] < 0.0;
-        } else {
-          const double* hr = Hb + static_cast<size_t>(j) * t;
-          double acc = 0.0;
-          for (int k2 = lane; k2 < t; k2 += 64) acc += hr[k2] * sm.sx[k2];
-#pragma unroll
-          for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-          v = acc - cb[j] < -tol;
-        }
-        if (lane == 0) stc(&vb[j], v);
-      }
-      team_sync(tm);
-      if (tm.rank == 0) {
-        int nv = 0, vmax = -1;
-        for (int j = tid; j < t; j += blockDim.x) {
-          w[j] = sm.sx[j];
-          if (ldc(&vb[j])) {
-            ++nv;
-            vmax = max(vmax, j);
-          }
-        }
-        nv = wg_isum(nv);
-        vmax = wg_imax(vmax);
-        const int N = lda(&st[1]), pbud = lda(&st[2]);
-        const int mode = nv == 0 ? 0 : (nv < N || pbud >= 1) ? 1 : 2;
-        if (mode == 1) {
-          for (int j = tid; j < t; j += blockDim.x)
-            if (ldc(&vb[j])) stc(&mk[j], !ldc(&mk[j]));
-        } else if (mode == 2 && tid == 0) {
-          stc(&mk[vmax], !ldc(&mk[vmax]));
-        }
-        const bool capped = mode != 0 && it + 1 >= max_iters;
-        if (capped)
-          for (int j = tid; j < t; j += blockDim.x) w[j] = fmax(w[j], 0.0);
-        __syncthreads();
-        if (tid == 0) {
-          if (mode == 0) sta(&st[0], 1);
-          else if (nv < N) {
-            sta(&st[1], nv);
-            sta(&st[2], 3);
-          } else if (pbud >= 1) {
-            sta(&st[2], pbud - 1);
-          }
-          sta(&st[3], it + 1);
-          if (capped) {
-            sta(&st[0], 2);
-            if (status) atomicOr(&status[b], 2);
-          }
-        }
-      }
-      team_sync(tm);
-      if (lda(&st[0]) != 0) break;
+    const SweepMat M{S + b * sS, Ub + b * sUV, Vb + b * sUV, ld, kSB, 1, t};
+    for (int j = tid; j < t; j += kTeamThreads) sm.inF[j] = 0;
+    double cm = 0.0, hm = 0.0;
+    for (int j = tid; j < t; j += kTeamThreads) {
+      const double* row = M.S + static_cast<size_t>(kSB + j) * ld;
+      cm = fmax(cm, fabs(row[0]));
+      hm = fmax(hm, row[kSB + j]);
     }
-    // final passive list for the value fit (the support of w)
-    if (tm.rank == 0) build_index(mk, cb, Fb, ib, &msz[b], nullptr, t);
+    const double scale = fmax(wg_max(cm), wg_max(hm));
+    int N = t + 1, bud = 3, done = 0;
+    bool bad = false;
+    double fl = 0.0;
+    double val[NV];
+    for (int it = 0;; ++it) {
+      double xm = 0.0;
+#pragma unroll
+      for (int q = 0; q < NV; ++q) {
+        const int j = tid + q * kTeamThreads;
+        val[q] = j < t ? M.S[static_cast<size_t>(kSB + j) * ld] : 0.0;
+        if (j < t && sm.inF[j]) xm = fmax(xm, fabs(val[q]));
+      }
+      const double tol = 1e-13 * scale * fmax(1.0, wg_max(xm));
+      int nv = 0, vmax = -1, slot;
+#pragma unroll
+      for (int q = 0; q < NV; ++q) {
+        const int j = tid + q * kTeamThreads;
+        bool f = false;
+        if (j < t) f = sm.inF[j] ? val[q] < 0.0 : val[q] > tol;
+        if (q * kTeamThreads < t) {
+          nv = wg_append(f, nv, &slot);
+          if (f) {
+            sm.list[slot] = static_cast<int16_t>(j);
+            vmax = j;
+          }
+        }
+      }
+      if (nv == 0) {
+        done = 1;
+        break;
+      }
+      if (it >= max_iters) {
+        done = 2;
+        break;
+      }
+      int nflip = nv;
+      if (nv < N) {
+        N = nv;
+        bud = 3;
+      } else if (bud >= 1) {
+        --bud;
+      } else {
+        vmax = wg_imax(vmax);
+        __syncthreads();
+        if (tid == 0) sm.list[0] = static_cast<int16_t>(vmax);
+        nflip = 1;
+      }
+      __syncthreads();
+      for (int s0 = 0; s0 < nflip; s0 += kSB) {
+        const int k = min(kSB, nflip - s0);
+        if (tid < k) {
+          const int j = sm.list[s0 + tid];
+          sm.piv[tid] = kSB + j;
+          sm.sgn[tid] = sm.inF[j] ? -1.0 : 1.0;
+          sm.pos[kSB + j] = static_cast<int16_t>(tid);
+        }
+        __syncthreads();
+        bad |= sweep_step(M, tm, k, 0);
+        if (tid < k) {
+          const int j = sm.list[s0 + tid];
+          sm.inF[j] ^= 1;
+          sm.pos[kSB + j] = -1;
+        }
+        __syncthreads();
+        fl += sweep_flops(k, t + 1);
+      }
+    }
+    if (tm.rank == 0) {
+      double* w = wv + static_cast<size_t>(b) * t;
+      int32_t* Fb = Fidx + static_cast<size_t>(b) * t;
+      int32_t* ib = inv + static_cast<size_t>(b) * t;
+      int m = 0, slot;
+#pragma unroll
+      for (int q = 0; q < NV; ++q) {
+        const int j = tid + q * kTeamThreads;
+        double x = 0.0;
+        if (j < t) {
+          x = sm.inF[j] ? val[q] : 0.0;
+          if (done == 2) x = fmax(x, 0.0);
+          w[j] = x;
+        }
+        if (q * kTeamThreads < t) {
+          const bool f = j < t && x > 0.0;
+          m = wg_append(f, m, &slot);
+          if (j < t) {
+            ib[j] = f ? slot : -1;
+            if (f) Fb[slot] = j;
+          }
+        }
+      }
+      if (tid == 0) {
+        msz[b] = m;
+        flops[2 * b] = fl;
+        if (status) {
+          if (done == 2) atomicOr(&status[b], 2);
+          if (bad) atomicOr(&status[b], 1);
+        }
+      }
+    }
     team_sync(tm);
   }
   if (tm.rank == 0 && tid == 0 && __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
     for (int b = team; b < B; b += nteams) atomicOr(&status[b], 8);
 }
 
-// Value system: Cholesky of G_FF + lam_v I (in W) and solve for the D
-// right-hand sides in R, one team per head; members split the columns.
-__global__ __launch_bounds__(256) void k_value_team(double* __restrict__ W, double* __restrict__ R,
-                                                    const int32_t* __restrict__ msz,
-                                                    int32_t* __restrict__ status,
-                                                    unsigned* __restrict__ bar,
-                                                    int* __restrict__ err, int* __restrict__ xcc,
-                                                    double* __restrict__ flops, int B, int t,
-                                                    int D, int tx) {
-  TeamSmem& sm = g_team_smem;
+// Value system [G R; R^T .] (G = X_F^T X_F + lam_v I of order m = msz[b], R =
+// X_F^T O + lam_v V_F with D columns, right-hand sides in rows [0, r_al)):
+// sweep the m variables in bands of 64; afterwards rows r_al + a hold C_v[a].
+__global__ __launch_bounds__(256) void k_value_sweep(
+    double* __restrict__ S, size_t sS, int ld, int r_al, double* __restrict__ Ub,
+    double* __restrict__ Vb, size_t sUV, const int32_t* __restrict__ msz,
+    int32_t* __restrict__ status, unsigned* __restrict__ bar, int* __restrict__ err,
+    int* __restrict__ xcc, double* __restrict__ flops, int B, int D, int tx) {
+  SweepSmem& sm = g_sw;
   Team tm;
   int team, nteams;
   team_setup(tm, team, nteams, bar, err, xcc, tx);
-  const int g = tm.size;
+  const int tid = threadIdx.x;
+  for (int s = tid; s < kMaxRows; s += kTeamThreads) sm.pos[s] = -1;
   for (int b = team; b < B; b += nteams) {
-    const size_t tt = static_cast<size_t>(t) * t;
-    double* Wb = W + b * tt;
-    double* Rb = R + static_cast<size_t>(b) * t * D;
     const int m = msz[b];
-    if (tm.rank == 0 && threadIdx.x == 0) {
-      const double md = m;
-      flops[2 * b + 1] = md * md * md / 3.0 + 2.0 * md * md * D;
+    const SweepMat M{S + b * sS, Ub + b * sUV, Vb + b * sUV, ld, r_al, D, m};
+    bool bad = false;
+    for (int s0 = 0; s0 < m; s0 += kSB) {
+      const int k = min(kSB, m - s0);
+      if (tid < k) {
+        sm.piv[tid] = r_al + s0 + tid;
+        sm.sgn[tid] = 1.0;
+        sm.pos[r_al + s0 + tid] = static_cast<int16_t>(tid);
+      }
+      __syncthreads();
+      bad |= sweep_step(M, tm, k, s0 / kSB);
+      if (tid < k) sm.pos[r_al + s0 + tid] = -1;
+      __syncthreads();
     }
-    chol_team(Wb, t, m, tm, status, b);
-    for (int c0 = tm.rank * 4; c0 < D; c0 += g * 4) chol_solve_cols(Wb, t, m, Rb, D, c0);
-    team_sync(tm);
+    if (tm.rank == 0 && tid == 0) {
+      double fl = 0.0;
+      for (int s0 = 0; s0 < m; s0 += kSB) fl += sweep_flops(min(kSB, m - s0), m + D);
+      flops[2 * b + 1] = fl;
+      if (bad && status) atomicOr(&status[b], 1);
+    }
   }
-  if (tm.rank == 0 && threadIdx.x == 0 &&
-      __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+  if (tm.rank == 0 && tid == 0 && __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
     for (int b = team; b < B; b += nteams) atomicOr(&status[b], 8);
 }
 
@@ -1141,23 +984,25 @@ __global__ __launch_bounds__(256) void k_value_prep(double* __restrict__ PS,
   for (int a = threadIdx.x; a < t; a += blockDim.x) row[a] = row[a] * fmax(w[a], 1e-30) * inv;
 }
 
-// lam_v = ridge * trace(G) / t; G += lam_v I (G = W, size msz).  grid (B), block 256.
-__global__ void k_ridge_v(double* __restrict__ W, const int32_t* __restrict__ msz,
-                          double* __restrict__ lam, int t, double ridge) {
+// lam_v = ridge * trace(G) / t; G += lam_v I (G at Gb, order msz, stride ld).
+// grid (B), block 256.
+__global__ void k_ridge_v(double* __restrict__ Gb, size_t sS, int ld,
+                          const int32_t* __restrict__ msz, double* __restrict__ lam, int t,
+                          double ridge) {
   __shared__ double sh[16];
   const int b = blockIdx.x, m = msz[b];
-  double* Wb = W + static_cast<size_t>(b) * t * t;
+  double* G = Gb + b * sS;
   double tr = 0.0;
-  for (int a = threadIdx.x; a < m; a += blockDim.x) tr += Wb[static_cast<size_t>(a) * t + a];
+  for (int a = threadIdx.x; a < m; a += blockDim.x) tr += G[static_cast<size_t>(a) * ld + a];
   tr = block_sum(tr, sh);
   const double lv = ridge * tr / t;
-  for (int a = threadIdx.x; a < m; a += blockDim.x) Wb[static_cast<size_t>(a) * t + a] += lv;
+  for (int a = threadIdx.x; a < m; a += blockDim.x) G[static_cast<size_t>(a) * ld + a] += lv;
   if (threadIdx.x == 0) lam[2 * b + 1] = lv;
 }
 
-// R[a][c] += lam_v * V[idx[F[a]]][c].  grid (ceil(t*D/256), B).
+// R[a][c] += lam_v * V[idx[F[a]]][c]  (R at Rb, stride ld).  grid (ceil(t*D/256), B).
 template <class In>
-__global__ void k_rhs_ridge(double* __restrict__ R, const In* __restrict__ V,
+__global__ void k_rhs_ridge(double* __restrict__ Rb, size_t sS, int ld, const In* __restrict__ V,
                             const int32_t* __restrict__ idx, const int32_t* __restrict__ Fidx,
                             const int32_t* __restrict__ msz, const double* __restrict__ lam,
                             int T, int t, int D) {
@@ -1166,17 +1011,19 @@ __global__ void k_rhs_ridge(double* __restrict__ R, const In* __restrict__ V,
   const int a = e / D, c = e % D;
   if (a >= m) return;
   const int j = idx[static_cast<size_t>(b) * t + Fidx[static_cast<size_t>(b) * t + a]];
-  R[(static_cast<size_t>(b) * t + a) * D + c] +=
+  Rb[b * sS + static_cast<size_t>(a) * ld + c] +=
       lam[2 * b + 1] * to_f64<In>(V[(static_cast<size_t>(b) * T + j) * D + c]);
 }
 
-// out_V[b][a][c] = fitted value for passive keys, V row (the prior) for keys
-// whose multiplier is zero; out_bias = log(max(w, 1e-30)).  grid (ceil(t*D/256), B).
+// out_V[b][a][c] = fitted value (row inv[a] of C at Cb, stride ld) for passive
+// keys, the V row (the prior) for keys whose multiplier is zero;
+// out_bias = log(max(w, 1e-30)).  grid (ceil(t*D/256), B).
 template <class In>
-__global__ void k_write_out(const double* __restrict__ R, const In* __restrict__ V,
-                            const int32_t* __restrict__ idx, const int32_t* __restrict__ inv,
-                            const double* __restrict__ wv, float* __restrict__ out_V,
-                            float* __restrict__ out_bias, int T, int t, int D) {
+__global__ void k_write_out(const double* __restrict__ Cb, size_t sS, int ld,
+                            const In* __restrict__ V, const int32_t* __restrict__ idx,
+                            const int32_t* __restrict__ inv, const double* __restrict__ wv,
+                            float* __restrict__ out_V, float* __restrict__ out_bias, int T, int t,
+                            int D) {
   const int b = blockIdx.y;
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   const int a = e / D, c = e % D;
@@ -1184,7 +1031,7 @@ __global__ void k_write_out(const double* __restrict__ R, const In* __restrict__
   const int p = inv[static_cast<size_t>(b) * t + a];
   float v;
   if (p >= 0) {
-    v = static_cast<float>(R[(static_cast<size_t>(b) * t + p) * D + c]);
+    v = static_cast<float>(Cb[b * sS + static_cast<size_t>(p) * ld + c]);
   } else {
     const int j = idx[static_cast<size_t>(b) * t + a];
     v = to_f32<In>(V[(static_cast<size_t>(b) * T + j) * D + c]);
@@ -1202,12 +1049,13 @@ __global__ void k_write_out(const double* __restrict__ R, const In* __restrict__
 // Co-resident workgroups of a team kernel on the current device (cached).
 static int coop_capacity(const void* func) {
   static int cache[2][64] = {};
-  const int which = func == reinterpret_cast<const void*>(&k_nnls_team) ? 0 : 1;
+  const int which = func == reinterpret_cast<const void*>(&k_nnls_sweep) ? 0 : 1;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   if (cache[which][dev] == 0) {
     int nb = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, func, 256, 0) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, func, kTeamThreads, 0) != hipSuccess)
+      return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
     cache[which][dev] = nb * cus < kMaxTeamGrid ? nb * cus : kMaxTeamGrid;
@@ -1216,12 +1064,10 @@ static int coop_capacity(const void* func) {
 }
 
 // Team shape: nteams = 8*tx teams (a multiple of the XCD count, so each team
-// stays on one XCD), g members each: enough for the first trailing update (up
-// to 64), no more than the device holds.  Returns the grid size.
-static int team_shape(int B, int t, int cap, int& tx) {
-  const int nt = (t + kNB - 1) / kNB;
-  int tiles = nt * (nt - 1) / 2;
-  tiles = tiles < 1 ? 1 : (tiles > 64 ? 64 : tiles);
+// stays on one XCD), g members each: no more than the tiles of a sweep step,
+// no more than the device holds.  Returns the grid size.
+static int team_shape(int B, int tiles, int cap, int& tx) {
+  tiles = tiles < 1 ? 1 : tiles;
   tx = (B + kXcds - 1) / kXcds;
   if (kXcds * tx > cap) tx = cap / kXcds > 0 ? cap / kXcds : 1;
   const int nteams = kXcds * tx;
@@ -1253,6 +1099,10 @@ static void launch_atb(const double* A, size_t sA, int lda, const int32_t* colA,
                        msz, mA, mB, tb, ntiles, ksplit);
 }
 
+int sweep_ld(int t, int D) {
+  return (t + kSB - 1) / kSB * kSB + (D + kSB - 1) / kSB * kSB;
+}
+
 template <class In, int D>
 hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const double* lse,
                       const float* O, const int32_t* idx, FitBufs fb, float* out_bias,
@@ -1262,74 +1112,75 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
   const In* K = static_cast<const In*>(Kv);
   const In* V = static_cast<const In*>(Vv);
   const int tt = (t + kTile - 1) / kTile, tn = (n + kTile - 1) / kTile;
-  const size_t tsq = static_cast<size_t>(t) * t;
-  // P_S, M = P_S^T P_S (into H), column sums (into cvec)
+  int ld = sweep_ld(t, D);
+  size_t sS = static_cast<size_t>(ld) * ld, sUV = static_cast<size_t>(ld) * kSB;
+  constexpr int rv = (D + kSB - 1) / kSB * kSB;  // right-hand-side rows of the value system
+  const size_t sPS = static_cast<size_t>(n) * t;
+  // P_S, M = P_S^T P_S (into the bias system's variable block), column sums
   prof_mark(3, false, st);
   hipLaunchKernelGGL((k_ps<In, D>), dim3(tn * tt, B), dim3(256), 0, st, Q, K, idx, lse, fb.PS, n,
                      T, t, tt);
   prof_mark(3, true, st);
   prof_mark(4, false, st);
-  launch_atb<double, true>(fb.PS, static_cast<size_t>(n) * t, t, nullptr, 0, fb.PS,
-                           static_cast<size_t>(n) * t, t, fb.H, tsq, t, n, nullptr, t, t, fb.part,
-                           fb.part_cap, B, st);
+  launch_atb<double, true>(fb.PS, sPS, t, nullptr, 0, fb.PS, sPS, t,
+                           fb.S + static_cast<size_t>(kSB) * ld + kSB, sS, ld, n, nullptr, t, t,
+                           fb.part, fb.part_cap, B, st);
   prof_mark(4, true, st);
   const int nslab = (n + 255) / 256;
   hipLaunchKernelGGL(k_colsum_part, dim3(tt, nslab, B), dim3(64, 4), 0, st, fb.PS, fb.colpart, n,
                      t);
   hipLaunchKernelGGL(k_colsum_final, dim3((t + 255) / 256, B), dim3(256), 0, st, fb.colpart,
                      fb.cvec, nslab, t);
-  hipLaunchKernelGGL(k_bias_prep, dim3(B), dim3(1024), 0, st, fb.H, fb.cvec, fb.lam, fb.mask,
-                     fb.state, fb.wv, t, ridge);
+  hipLaunchKernelGGL(k_bias_prep, dim3(B), dim3(1024), 0, st, fb.S, sS, ld, fb.cvec, fb.lam, t,
+                     ridge);
   // pivoting rounds: one cooperative launch, a team per head
   prof_mark(5, false, st);
-  int cap = coop_capacity(reinterpret_cast<const void*>(&k_nnls_team));
+  int cap = coop_capacity(reinterpret_cast<const void*>(&k_nnls_sweep));
   if (cap <= 0) return hipErrorLaunchFailure;
   int tx;
-  int grid = team_shape(B, t, cap, tx);
+  const int nvb = (t + kSB - 1) / kSB;
+  int grid = team_shape(B, nvb + nvb * (nvb + 1) / 2, cap, tx);
   hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(fb.bar), 0, kBarWords, st);
   if (e != hipSuccess) return e;
+  int* err = reinterpret_cast<int*>(fb.bar + kBarWords - 1);
   {
-    const double* H = fb.H;
-    const double* cv = fb.cvec;
-    int* err = reinterpret_cast<int*>(fb.bar + kBarWords - 1);
-    int* xcc = fb.xcc;
-    void* args[] = {&H,        &cv,        &fb.W,    &fb.xs,   &fb.mask, &fb.Fidx, &fb.inv,
-                    &fb.msz,   &fb.state,  &fb.tolv, &fb.wv,   &fb.viol, &status,  &fb.bar,
-                    &err,      &xcc,       &fb.flops, &B,      &t,       &max_iters, &tx};
-    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_nnls_team), dim3(grid),
-                                   dim3(256), args, 0, st);
+    void* args[] = {&fb.S,   &sS,      &ld,        &fb.U,   &fb.V,  &sUV,     &fb.wv,
+                    &fb.Fidx, &fb.inv, &fb.msz,    &status, &fb.bar, &err,    &fb.xcc,
+                    &fb.flops, &B,     &t,         &max_iters, &tx};
+    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_nnls_sweep), dim3(grid),
+                                   dim3(kTeamThreads), args, 0, st);
     if (e != hipSuccess) return e;
   }
   prof_mark(5, true, st);
-  // value fit on the passive set
+  // value fit on the passive set: G = X_F^T X_F + lam_v I, R = X_F^T O + lam_v V_F
   prof_mark(6, false, st);
   hipLaunchKernelGGL(k_value_prep, dim3(n, B), dim3(256), 0, st, fb.PS, fb.wv, n, t);
-  launch_atb<double, true>(fb.PS, static_cast<size_t>(n) * t, t, fb.Fidx, t, fb.PS,
-                           static_cast<size_t>(n) * t, t, fb.W, tsq, t, n, fb.msz, t, t, fb.part,
-                           fb.part_cap, B, st);
-  hipLaunchKernelGGL(k_ridge_v, dim3(B), dim3(256), 0, st, fb.W, fb.msz, fb.lam, t, ridge);
-  launch_atb<float, false>(fb.PS, static_cast<size_t>(n) * t, t, fb.Fidx, t, O,
-                           static_cast<size_t>(n) * D, D, fb.R, static_cast<size_t>(t) * D, D, n,
-                           fb.msz, t, D, fb.part, fb.part_cap, B, st);
-  hipLaunchKernelGGL((k_rhs_ridge<In>), dim3((t * D + 255) / 256, B), dim3(256), 0, st, fb.R, V,
-                     idx, fb.Fidx, fb.msz, fb.lam, T, t, D);
-  cap = coop_capacity(reinterpret_cast<const void*>(&k_value_team));
+  double* G0 = fb.S + static_cast<size_t>(rv) * ld + rv;
+  double* R0 = fb.S + static_cast<size_t>(rv) * ld;
+  launch_atb<double, true>(fb.PS, sPS, t, fb.Fidx, t, fb.PS, sPS, t, G0, sS, ld, n, fb.msz, t, t,
+                           fb.part, fb.part_cap, B, st);
+  hipLaunchKernelGGL(k_ridge_v, dim3(B), dim3(256), 0, st, G0, sS, ld, fb.msz, fb.lam, t, ridge);
+  launch_atb<float, false>(fb.PS, sPS, t, fb.Fidx, t, O, static_cast<size_t>(n) * D, D, R0, sS, ld,
+                           n, fb.msz, t, D, fb.part, fb.part_cap, B, st);
+  hipLaunchKernelGGL((k_rhs_ridge<In>), dim3((t * D + 255) / 256, B), dim3(256), 0, st, R0, sS,
+                     ld, V, idx, fb.Fidx, fb.msz, fb.lam, T, t, D);
+  cap = coop_capacity(reinterpret_cast<const void*>(&k_value_sweep));
   if (cap <= 0) return hipErrorLaunchFailure;
-  grid = team_shape(B, t, cap, tx);
+  constexpr int nrb = rv / kSB;
+  grid = team_shape(B, nvb * nrb + nvb * (nvb + 1) / 2, cap, tx);
   e = launch_fill_i32(reinterpret_cast<int32_t*>(fb.bar), 0, kBarWords, st);
   if (e != hipSuccess) return e;
   {
-    int* err = reinterpret_cast<int*>(fb.bar + kBarWords - 1);
+    int r_al = rv, Dv = D;
     const int32_t* ms = fb.msz;
-    int Dv = D;
-    int* xcc = fb.xcc;
-    void* args[] = {&fb.W, &fb.R, &ms, &status, &fb.bar, &err, &xcc, &fb.flops, &B, &t, &Dv, &tx};
-    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_value_team), dim3(grid),
-                                   dim3(256), args, 0, st);
+    void* args[] = {&fb.S, &sS,     &ld,  &r_al, &fb.U,     &fb.V, &sUV, &ms,
+                    &status, &fb.bar, &err, &fb.xcc, &fb.flops, &B,    &Dv,  &tx};
+    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_value_sweep), dim3(grid),
+                                   dim3(kTeamThreads), args, 0, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_write_out<In>), dim3((t * D + 255) / 256, B), dim3(256), 0, st, fb.R, V,
-                     idx, fb.inv, fb.wv, out_V, out_bias, T, t, D);
+  hipLaunchKernelGGL((k_write_out<In>), dim3((t * D + 255) / 256, B), dim3(256), 0, st, R0, sS,
+                     ld, V, idx, fb.inv, fb.wv, out_V, out_bias, T, t, D);
   prof_mark(6, true, st);
   return hipGetLastError();
 }

@@ -77,8 +77,8 @@ Plan make_plan(const kvc_params_t* p) {
 }
 
 struct Layout {
-  size_t ml, lse, Opart, O, imp_part, imp, idx, status, PS, H, W, cvec, xs, R, wv, lam, tolv,
-      colpart, mask, Fidx, inv, msz, state, viol, bar, xcc, flops, part, total;
+  size_t ml, lse, Opart, O, imp_part, imp, idx, status, PS, S, U, V, cvec, wv, lam, colpart, Fidx,
+      inv, msz, bar, xcc, flops, part, total;
   size_t part_cap;
 };
 
@@ -103,21 +103,19 @@ Layout make_layout(const kvc_params_t* p) {
   L.idx = take(B * t * 4);
   L.status = take(B * 4);
   L.PS = take(B * n * t * 8);
-  L.H = take(B * t * t * 8);
-  L.W = take(B * t * t * 8);
+  {
+    const size_t ld = static_cast<size_t>(kvc::sweep_ld(static_cast<int>(t), static_cast<int>(d)));
+    L.S = take(B * ld * ld * 8);
+    L.U = take(B * ld * 64 * 8);
+    L.V = take(B * ld * 64 * 8);
+  }
   L.cvec = take(B * t * 8);
-  L.xs = take(B * t * 8);
-  L.R = take(B * t * d * 8);
   L.wv = take(B * t * 8);
   L.lam = take(B * 2 * 8);
-  L.tolv = take(B * 8);
   L.colpart = take(B * ((n + 255) / 256) * t * 8);
-  L.mask = take(B * t * 4);
   L.Fidx = take(B * t * 4);
   L.inv = take(B * t * 4);
   L.msz = take(B * 4);
-  L.state = take(B * 4 * 4);
-  L.viol = take(B * t * 4);
   L.bar = take(static_cast<size_t>(kvc::kBarWords) * 4);
   L.xcc = take(static_cast<size_t>(kvc::kMaxTeamGrid) * 4);
   L.flops = take(B * 2 * 8);
@@ -158,26 +156,21 @@ T* at(void* ws, size_t off) {
 kvc::FitBufs fit_bufs(void* ws, const Layout& L) {
   kvc::FitBufs fb;
   fb.PS = at<double>(ws, L.PS);
-  fb.H = at<double>(ws, L.H);
-  fb.W = at<double>(ws, L.W);
+  fb.S = at<double>(ws, L.S);
+  fb.U = at<double>(ws, L.U);
+  fb.V = at<double>(ws, L.V);
   fb.cvec = at<double>(ws, L.cvec);
-  fb.xs = at<double>(ws, L.xs);
-  fb.R = at<double>(ws, L.R);
   fb.wv = at<double>(ws, L.wv);
   fb.lam = at<double>(ws, L.lam);
-  fb.tolv = at<double>(ws, L.tolv);
   fb.colpart = at<double>(ws, L.colpart);
-  fb.viol = at<int32_t>(ws, L.viol);
   fb.bar = at<unsigned>(ws, L.bar);
   fb.xcc = at<int32_t>(ws, L.xcc);
   fb.flops = at<double>(ws, L.flops);
   fb.part = at<double>(ws, L.part);
   fb.part_cap = L.part_cap;
-  fb.mask = at<int32_t>(ws, L.mask);
   fb.Fidx = at<int32_t>(ws, L.Fidx);
   fb.inv = at<int32_t>(ws, L.inv);
   fb.msz = at<int32_t>(ws, L.msz);
-  fb.state = at<int32_t>(ws, L.state);
   return fb;
 }
 

@@ -19,14 +19,20 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t count, hipStream_t st);
 
 // Float64 work buffers of the fits (device pointers into the workspace).
 struct FitBufs {
-  double *PS, *H, *W, *cvec, *xs, *R, *wv, *lam, *tolv, *colpart;
-  int32_t *mask, *Fidx, *inv, *msz, *state, *viol;
+  double *PS, *cvec, *wv, *lam, *colpart;
+  double* S;  // [B][ld][ld] sweep matrices (lower triangle), ld = sweep_ld(t, d)
+  double* U;  // [B][ld][64] staged pivot columns of a sweep step
+  double* V;  // [B][ld][64] the same times the inverse pivot block
+  int32_t *Fidx, *inv, *msz;
   unsigned* bar;  // kBarWords words: team barrier counters, the last one the timeout flag
   int32_t* xcc;   // kMaxTeamGrid words: each team workgroup's XCC id
-  double* flops;    // [B][2] fp64 work of the NNLS rounds and of the value solve
+  double* flops;    // [B][2] fp64 work of the NNLS sweeps and of the value sweeps
   double* part;     // split-K partial tiles of the fit GEMMs
   size_t part_cap;  // its capacity in doubles
 };
+// Order of a head's sweep matrix: right-hand-side rows (d rounded up to 64)
+// plus the variables (t rounded up to 64).
+int sweep_ld(int t, int d);
 constexpr int kMaxTeamGrid = 8192;
 constexpr int kBarWords = kMaxTeamGrid + 1;
 template <class In, int D>

@@ -491,9 +491,12 @@ constexpr int kTeamThreads = 256;
 
 struct __align__(16) SweepSmem {
   double pp[kSB][kSB + 1];         // pivot block, then its inverse B
-  double li[kSB * (kSB - 1) / 2];  // strictly lower part of L^-1, rows packed
+  double li[kSB][kSB + 1];         // L^-1 (unit lower; identity past k)
   double rD[kSB];                  // 1 / D (0 past k)
-  double bc[2][kSB];               // pivot-row broadcast of the small sweeps
+  double sW[kSB][17];              // small inverse: panel of a 16-pivot block,
+  double sV[kSB][17];              // and L[b, <b] L^-1[<b, <b] (16 x 48)
+  double sLb[16][17];              // L^-1 of a 16 x 16 diagonal block, its pivot row
+  double mbc[16];
   double sgn[kSB];                 // s_q
   int piv[kSB];                    // matrix row of pivot q
   int16_t list[kMaxTeamT];         // NNLS: variables exchanged this round
@@ -520,11 +523,7 @@ __device__ __forceinline__ double s_at(const SweepMat& M, int i, int j) {
 __device__ __forceinline__ bool s_active(const SweepMat& M, int s) {
   return s < M.n_rhs || (s >= M.r_al && s < M.r_al + M.n_var);
 }
-// L^-1[c][q] for c, q < 64 (identity past k)
-__device__ __forceinline__ double li_at(int c, int q, int k) {
-  if (c >= k || q >= k) return c == q ? 1.0 : 0.0;
-  return c > q ? g_sw.li[c * (c - 1) / 2 + q] : (c == q ? 1.0 : 0.0);
-}
+
 
 __device__ double wg_max(double v) {
   SweepSmem& sm = g_sw;
@@ -575,54 +574,176 @@ __device__ int wg_append(bool f, int base, int* slot) {
   return tot;
 }
 
-// sm.pp[0:k][0:k] <- its inverse (the rest 0), by k single sweeps on 256
-// threads (thread: row tid/4, 16 columns).  The block is symmetric, so the
-// pivot row doubles as the pivot column.  Before sweep p, row p holds
-// -L^-1[p][j] at the swept columns j < p and the pivot D[p] on the diagonal
-// (A_PP = L D L^T); both are recorded (sm.li, sm.rD).  A pivot without the
-// sign s_p is replaced by s_p (the system is not numerically definite);
-// returns whether that happened.
-__device__ __noinline__ bool small_inverse(int k) {
+// sm.pp[0:k][0:k] <- its inverse B (the rest 0) through A_PP = L D L^T:
+// a right-looking blocked factorization (blocks of 16 pivots), L^-1 by
+// blocked triangular inversion, then B = L^-T D^-1 L^-1 on fp64 MFMA.  Per
+// block: one wave sweeps the current 16 x 16 diagonal block pivot by pivot
+// (the pivot row goes through LDS; a wave's LDS accesses are performed in
+// order, so no barrier is needed); before sweep p its pivot row holds
+// -L_bb^-1[p][j] at the swept columns j < p and the pivot on the diagonal.
+// Then the rows of L^-1 left of the block, -L_bb^-1 (L[b, <b] L^-1[<b, <b]),
+// the panel L[>b, b] = A[>b, b] L_bb^-T D_b^-1 and the trailing update
+// A[>b, >b] -= W D_b^-1 W^T (W = A[>b, b] L_bb^-T).  Inverting the pivot block
+// by a blocked sweep instead would form its off-diagonal parts through
+// explicit inverses of the 16 x 16 blocks and lose them when those are
+// ill-conditioned.  Results: sm.pp = B, sm.li = L^-1 (identity past k),
+// sm.rD = 1/D (0 past k).  A pivot without the sign s_p is replaced by s_p (the system is
+// not numerically definite); the return value, meaningful in wave 0, says
+// whether that happened.
+__device__ __forceinline__ bool small_inverse(int k) {
   SweepSmem& sm = g_sw;
-  const int tid = threadIdx.x, r = tid >> 2, c0 = (tid & 3) * 16;
-  double a[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) a[j] = sm.pp[r][c0 + j];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wr = wave >> 1, wc = wave & 1, g16 = lane >> 4, l16 = lane & 15;
   bool bad = false;
-  for (int p = 0; p < k; ++p) {
-    double* bc = sm.bc[p & 1];
-    if (r == p) {
+  const int nb = (k + 15) >> 4;
+  for (int e = tid; e < kSB * kSB; e += kTeamThreads) {
+    const int r = e >> 6, c = e & 63;
+    if (r >= 16 * nb || c >= r) sm.li[r][c] = r == c ? 1.0 : 0.0;
+  }
+  for (int b = 0; b < nb; ++b) {
+    const int o = b * 16, o2 = o + 16;
+    if (wave == 0) {
+      const int r = lane >> 2, c4 = (lane & 3) * 4;
+      double a[4];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        bc[c0 + j] = a[j];
-        if (c0 + j < p) sm.li[p * (p - 1) / 2 + c0 + j] = -a[j];
+      for (int j = 0; j < 4; ++j) a[j] = sm.pp[o + r][o + c4 + j];
+      for (int m = 0; m < 16; ++m) {
+        if (r == m) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            sm.mbc[c4 + j] = a[j];
+            sm.sLb[m][c4 + j] = c4 + j < m ? -a[j] : (c4 + j == m ? 1.0 : 0.0);
+          }
+        }
+        double d = sm.mbc[m];
+        const double sg = o + m < k ? sm.sgn[o + m] : 1.0;
+        if (!(d * sg > 0.0)) {
+          bad = true;
+          d = sg;
+        }
+        const double rd = 1.0 / d;
+        if (lane == 0) sm.rD[o + m] = rd;
+        const double f = sm.mbc[r] * rd;
+        const bool isrow = r == m;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const double rc = sm.mbc[c4 + j];
+          const double gen = fma(-f, rc, a[j]);
+          const double v = isrow ? rc * rd : gen;
+          const double vp = isrow ? -rd : f;
+          a[j] = c4 + j == m ? vp : v;
+        }
       }
     }
     __syncthreads();
-    double d = bc[p];
-    const double sg = sm.sgn[p];
-    if (!(d * sg > 0.0)) {
-      bad = true;
-      d = sg;
-    }
-    const double rd = 1.0 / d;
-    if (tid == 0) sm.rD[p] = rd;
-    const double f = bc[r] * rd;
+    // T = L[b, <b] L^-1[<b, <b] (into sV, 16 x o) and the panel
+    // W = A[>b, b] L_bb^-T (into sW, zero above the panel)
+    double* T = &sm.sV[0][0];
+    if (wave < b) {  // wave w: columns 16w.. of T; L^-1 rows are zero left of their column
+      const int jb = wave * 16;
+      f64x4 t4 = {};
+      for (int i0 = jb; i0 < o; i0 += 4) {
+        const int i = i0 + g16;
+        t4 = __builtin_amdgcn_mfma_f64_16x16x4f64(sm.pp[o + l16][i], sm.li[i][jb + l16], t4, 0, 0, 0);
+      }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int c = c0 + j;
-      const double rc = bc[c];
-      const double upd = fma(-f, rc, a[j]);
-      a[j] = r == p ? (c == p ? -rd : rc * rd) : (c == p ? f : upd);
+      for (int x = 0; x < 4; ++x) T[(g16 + 4 * x) * 48 + jb + l16] = t4[x];
     }
+    {
+      const int i = tid >> 2, q0 = (tid & 3) * 4;
+      double u[16];
+#pragma unroll
+      for (int m = 0; m < 16; ++m) u[m] = i >= o2 ? sm.pp[i][o + m] : 0.0;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int q = q0 + qq;
+        double w = 0.0;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) w = fma(u[m], sm.sLb[q][m], w);
+        sm.sW[i][q] = w;
+      }
+    }
+    __syncthreads();
+    // rows o..o+15 of L^-1: -L_bb^-1 T left of the block
+    if (wave < b) {
+      const int jb = wave * 16;
+      f64x4 t4 = {};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int m2 = 4 * ks + g16;
+        t4 = __builtin_amdgcn_mfma_f64_16x16x4f64(sm.sLb[l16][m2], T[m2 * 48 + jb + l16], t4, 0, 0, 0);
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x) sm.li[o + g16 + 4 * x][jb + l16] = -t4[x];
+    }
+    {
+      const int m = tid >> 4, j = tid & 15;
+      if (j < m) sm.li[o + m][o + j] = sm.sLb[m][j];
+    }
+    // panel of L and trailing update on MFMA
+    f64x4 acc[2][2] = {};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int q = 4 * ks + g16;
+      const double rdq = sm.rD[o + q];
+      double av[2], bv[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        av[x] = sm.sW[wr * 32 + x * 16 + l16][q] * rdq;
+        bv[x] = sm.sW[wc * 32 + x * 16 + l16][q];
+      }
+#pragma unroll
+      for (int ra = 0; ra < 2; ++ra)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          acc[ra][rb] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ra], bv[rb], acc[ra][rb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int ra = 0; ra < 2; ++ra)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = wr * 32 + ra * 16 + g16 + 4 * i, col = wc * 32 + rb * 16 + l16;
+          if (row < o2) continue;
+          if (col >= o2) sm.pp[row][col] -= acc[ra][rb][i];
+          else if (col >= o) sm.pp[row][col] = sm.sW[row][col - o] * sm.rD[col];
+        }
+    __syncthreads();
   }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int c = c0 + j;
-    sm.pp[r][c] = (r < k && c < k) ? -a[j] : 0.0;
+  // past k: identity rows and columns of L^-1, no pivot
+  for (int e = tid; e < kSB * kSB; e += kTeamThreads) {
+    const int r = e >> 6, c = e & 63;
+    if ((r >= k || c >= k) && c <= r) sm.li[r][c] = r == c ? 1.0 : 0.0;
   }
   if (tid >= k && tid < kSB) sm.rD[tid] = 0.0;
+  __syncthreads();
+  // B = L^-T D^-1 L^-1
+  f64x4 acc[2][2] = {};
+  for (int ks = 0; ks < (k + 3) / 4; ++ks) {
+    const int m = 4 * ks + g16;
+    const double rdm = sm.rD[m];
+    double av[2], bv[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      av[x] = sm.li[m][wr * 32 + x * 16 + l16] * rdm;
+      bv[x] = sm.li[m][wc * 32 + x * 16 + l16];
+    }
+#pragma unroll
+    for (int ra = 0; ra < 2; ++ra)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+        acc[ra][rb] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ra], bv[rb], acc[ra][rb], 0, 0, 0);
+  }
+#pragma unroll
+  for (int ra = 0; ra < 2; ++ra)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wr * 32 + ra * 16 + g16 + 4 * i, col = wc * 32 + rb * 16 + l16;
+        sm.pp[row][col] = (row < k && col < k) ? acc[ra][rb][i] : 0.0;
+      }
   __syncthreads();
   return bad;
 }
@@ -632,7 +753,7 @@ __device__ __noinline__ bool small_inverse(int k) {
 // to M.U / M.V.
 // The contraction index is permuted so that each lane's 16 values of a row
 // are contiguous: in MFMA step kk, lane l supplies q = 16*(l/16) + kk.
-__device__ __noinline__ void v_band(const SweepMat& M, int band, int k) {
+__device__ __forceinline__ void v_band(const SweepMat& M, int band, int k) {
   SweepSmem& sm = g_sw;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wr = wave >> 1, wc = wave & 1, g16 = lane >> 4, l16 = lane & 15;
@@ -656,7 +777,7 @@ __device__ __noinline__ void v_band(const SweepMat& M, int band, int k) {
     for (int rb = 0; rb < 2; ++rb) {
       const int c = wc * 32 + rb * 16 + l16;
       bb[rb] = sm.pp[q][c];
-      bl[rb] = li_at(c, q, k);
+      bl[rb] = sm.li[c][q];
     }
 #pragma unroll
     for (int ra = 0; ra < 2; ++ra)
@@ -683,29 +804,27 @@ __device__ __noinline__ void v_band(const SweepMat& M, int band, int k) {
 // Phase B for tile (I, J) of the lower triangle (bands I >= J): entries off
 // the pivots get T -= W_I D^-1 W_J^T; pivot columns V_iq s_q, pivot rows
 // V_jq s_q and the pivot block -s_q s_q' B[q][q'] are written directly.
-__device__ __noinline__ void sweep_tile(const SweepMat& M, int I, int J) {
+__device__ __forceinline__ void sweep_tile(const SweepMat& M, int I, int J) {
   SweepSmem& sm = g_sw;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wr = wave >> 1, wc = wave & 1, g16 = lane >> 4, l16 = lane & 15;
   const bool diag = I == J;
   if (diag && wr < wc) return;  // strictly upper quadrant of a diagonal tile
+  // every load of the tile is issued before the first MFMA
   double va[2][16], ub[2][16], tv[2][2][4];
+  int pr[2][4], pc[2];
 #pragma unroll
   for (int ra = 0; ra < 2; ++ra) {
     const double* p = M.U + static_cast<size_t>(I * kSB + wr * 32 + ra * 16 + l16) * kSB + g16 * 16;
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) va[ra][kk] = p[kk] * sm.rD[g16 * 16 + kk];
+    for (int kk = 0; kk < 16; ++kk) va[ra][kk] = p[kk];
   }
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const double* p = M.U + static_cast<size_t>(J * kSB + wc * 32 + rb * 16 + l16) * kSB + g16 * 16;
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) ub[rb][kk] = p[kk];
-  }
-  int pc[2];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int c = J * kSB + wc * 32 + rb * 16 + l16;
+    const double* p = M.U + static_cast<size_t>(c) * kSB + g16 * 16;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) ub[rb][kk] = p[kk];
     pc[rb] = s_active(M, c) ? sm.pos[c] : -1;
   }
 #pragma unroll
@@ -713,18 +832,28 @@ __device__ __noinline__ void sweep_tile(const SweepMat& M, int I, int J) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = I * kSB + wr * 32 + ra * 16 + g16 + 4 * i;
-      const int pr = s_active(M, r) ? sm.pos[r] : -1;
+      pr[ra][i] = s_active(M, r) ? sm.pos[r] : -1;
+    }
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+  for (int ra = 0; ra < 2; ++ra)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = I * kSB + wr * 32 + ra * 16 + g16 + 4 * i;
         const int c = J * kSB + wc * 32 + rb * 16 + l16;
+        const int q = pr[ra][i], qc = pc[rb];
         double v = 0.0;
-        if (pr >= 0 && pc[rb] >= 0) v = -sm.sgn[pr] * sm.sgn[pc[rb]] * sm.pp[pr][pc[rb]];
-        else if (pc[rb] >= 0) v = sm.sgn[pc[rb]] * M.V[static_cast<size_t>(r) * kSB + pc[rb]];
-        else if (pr >= 0) v = sm.sgn[pr] * M.V[static_cast<size_t>(c) * kSB + pr];
+        if (q >= 0 && qc >= 0) v = -sm.sgn[q] * sm.sgn[qc] * sm.pp[q][qc];
+        else if (qc >= 0) v = sm.sgn[qc] * M.V[static_cast<size_t>(r) * kSB + qc];
+        else if (q >= 0) v = sm.sgn[q] * M.V[static_cast<size_t>(c) * kSB + q];
         else if (!diag || r >= c) v = M.S[static_cast<size_t>(r) * M.ld + c];
         tv[ra][rb][i] = v;
       }
-    }
+#pragma unroll
+  for (int ra = 0; ra < 2; ++ra)
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) va[ra][kk] *= sm.rD[g16 * 16 + kk];
   f64x4 acc[2][2] = {};
 #pragma unroll
   for (int kk = 0; kk < 16; ++kk)
@@ -736,17 +865,15 @@ __device__ __noinline__ void sweep_tile(const SweepMat& M, int I, int J) {
 #pragma unroll
   for (int ra = 0; ra < 2; ++ra)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = I * kSB + wr * 32 + ra * 16 + g16 + 4 * i;
-      const bool prow = s_active(M, r) && sm.pos[r] >= 0;
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int i = 0; i < 4; ++i) {
+        const int r = I * kSB + wr * 32 + ra * 16 + g16 + 4 * i;
         const int c = J * kSB + wc * 32 + rb * 16 + l16;
         if (diag && r < c) continue;
-        const double v = (prow || pc[rb] >= 0) ? tv[ra][rb][i] : tv[ra][rb][i] - acc[ra][rb][i];
+        const double v = (pr[ra][i] >= 0 || pc[rb] >= 0) ? tv[ra][rb][i] : tv[ra][rb][i] - acc[ra][rb][i];
         M.S[static_cast<size_t>(r) * M.ld + c] = v;
       }
-    }
 }
 
 // One sweep step over the k pivots in sm.piv / sm.sgn / sm.pos, by the team.
@@ -768,8 +895,11 @@ __device__ __noinline__ bool sweep_step(const SweepMat& M, Team& tm, int k, int 
   // tiles: variable band I (0..nvb-1) owns nrb right-hand-side tiles, then
   // variable tiles J = 0..I
   const int ntiles = nvb * nrb + nvb * (nvb + 1) / 2;
+  // each member takes a contiguous run of tiles (mostly one row band)
+  const int t0 = static_cast<int>((static_cast<long long>(ntiles) * tm.rank) / tm.size);
+  const int t1 = static_cast<int>((static_cast<long long>(ntiles) * (tm.rank + 1)) / tm.size);
   int I = 0, first = 0;
-  for (int tau = tm.rank; tau < ntiles; tau += tm.size) {
+  for (int tau = t0; tau < t1; ++tau) {
     while (tau - first >= nrb + I + 1) {
       first += nrb + I + 1;
       ++I;

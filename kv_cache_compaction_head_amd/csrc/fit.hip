@@ -499,6 +499,8 @@ struct __align__(16) SweepSmem {
   double mbc[16];
   double sgn[kSB];                 // s_q
   int piv[kSB];                    // matrix row of pivot q
+  double sgn2[kSB];                // the next step's pivots (lookahead)
+  int piv2[kSB];
   int16_t list[kMaxTeamT];         // NNLS: variables exchanged this round
   int16_t pos[kMaxRows];           // matrix row -> pivot slot, -1 if not a pivot
   uint8_t inF[kMaxTeamT];   // NNLS: passive set
@@ -510,15 +512,33 @@ struct __align__(16) SweepSmem {
 // address it as LDS rather than through generic pointers.
 __shared__ SweepSmem g_sw;
 
+// Global-memory doubles: the helpers below are not inlined into the kernels,
+// so their pointers must say which address space they point into, or every
+// access becomes a generic (flat) one that the compiler has to order against
+// LDS traffic.
+typedef __attribute__((address_space(1))) double gdouble;
+
 struct SweepMat {
-  double* S;  // lower triangle, ld x ld
-  double* U;  // [rows][64] W = A[:, P] L^-T of the step
-  double* V;  // [rows][64] A[:, P] B
+  gdouble* S;      // lower triangle, ld x ld
+  gdouble* U;      // [rows][64] W = A[:, P] L^-T of the step
+  gdouble* V;      // [rows][64] A[:, P] B
+  gdouble* stage;  // [kStage] B, L^-1, 1/D of the next step (lookahead)
   int ld, r_al, n_rhs, n_var;
 };
+constexpr int kStage = kSweepStage;
+static_assert(kSweepStage == 2 * kSB * kSB + kSB, "staging layout");
+__device__ __forceinline__ gdouble* gptr(double* p) { return (gdouble*)p; }
 
-__device__ __forceinline__ double s_at(const SweepMat& M, int i, int j) {
-  return i >= j ? M.S[static_cast<size_t>(i) * M.ld + j] : M.S[static_cast<size_t>(j) * M.ld + i];
+__device__ __forceinline__ size_t s_idx(const SweepMat& M, int i, int j) {
+  return i >= j ? static_cast<size_t>(i) * M.ld + j : static_cast<size_t>(j) * M.ld + i;
+}
+__device__ __forceinline__ double s_at(const SweepMat& M, int i, int j) { return M.S[s_idx(M, i, j)]; }
+// A(i, j) if ok, else 0: the load is issued unconditionally (from element 0
+// when !ok), so a batch of these stays one batch of loads instead of a chain
+// of branches that each wait for their load.
+__device__ __forceinline__ double s_at_or0(const SweepMat& M, bool ok, int i, int j) {
+  const double v = M.S[ok ? s_idx(M, i, j) : 0];
+  return ok ? v : 0.0;
 }
 __device__ __forceinline__ bool s_active(const SweepMat& M, int s) {
   return s < M.n_rhs || (s >= M.r_al && s < M.r_al + M.n_var);
@@ -720,7 +740,8 @@ __device__ __forceinline__ bool small_inverse(int k) {
   __syncthreads();
   // B = L^-T D^-1 L^-1
   f64x4 acc[2][2] = {};
-  for (int ks = 0; ks < (k + 3) / 4; ++ks) {
+  // L^-1 is lower triangular: rows m below this wave's quadrant contribute nothing
+  for (int ks = max(wr, wc) * 8; ks < (k + 3) / 4; ++ks) {
     const int m = 4 * ks + g16;
     const double rdm = sm.rD[m];
     double av[2], bv[2];
@@ -765,7 +786,8 @@ __device__ __forceinline__ void v_band(const SweepMat& M, int band, int k) {
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
       const int q = g16 * 16 + kk;
-      u[ra][kk] = (act && q < k) ? s_at(M, s, sm.piv[q]) : 0.0;
+      const bool ok = act && q < k;
+      u[ra][kk] = s_at_or0(M, ok, s, ok ? sm.piv[q] : 0);
     }
   }
   f64x4 acc[2][2] = {}, accw[2][2] = {};
@@ -801,112 +823,293 @@ __device__ __forceinline__ void v_band(const SweepMat& M, int band, int k) {
     }
 }
 
-// Phase B for tile (I, J) of the lower triangle (bands I >= J): entries off
-// the pivots get T -= W_I D^-1 W_J^T; pivot columns V_iq s_q, pivot rows
-// V_jq s_q and the pivot block -s_q s_q' B[q][q'] are written directly.
-__device__ __forceinline__ void sweep_tile(const SweepMat& M, int I, int J) {
-  SweepSmem& sm = g_sw;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wr = wave >> 1, wc = wave & 1, g16 = lane >> 4, l16 = lane & 15;
-  const bool diag = I == J;
-  if (diag && wr < wc) return;  // strictly upper quadrant of a diagonal tile
-  // every load of the tile is issued before the first MFMA
-  double va[2][16], ub[2][16], tv[2][2][4];
-  int pr[2][4], pc[2];
+// Phase B, one wave per 64 x 64 tile, no barriers: the wave streams the
+// contraction in eight chunks of 8 (the next chunk's operands in flight while
+// the current one's MFMAs run), accumulating all sixteen 16 x 16 blocks, then
+// loads the tile's current values (32 rows at a time, one batch each) and
+// stores the update.  Entries off the pivots get T -= W_I D^-1 W_J^T; pivot
+// columns V_iq s_q, pivot rows V_jq s_q and the pivot block -s_q s_q' B[q][q']
+// are written directly.  In MFMA step kk of chunk c, lane l supplies
+// contraction index q = 8 c + 2 (l/16) + kk, so each lane reads 2 contiguous
+// values per row.
+// A wave's part of a tile: NRA x NRB blocks of 16 x 16 starting at block
+// (ro, co) of tile (I, J) (the whole tile, a half or a quadrant).
+template <int NRA, int NRB>
+__device__ __forceinline__ void wave_tile_chunk(const SweepMat& M, int I, int J, int ro, int co,
+                                                int c, double (&a)[NRA][2], double (&b)[NRB][2]) {
+  const int lane = threadIdx.x & 63, g16 = lane >> 4, l16 = lane & 15;
 #pragma unroll
-  for (int ra = 0; ra < 2; ++ra) {
-    const double* p = M.U + static_cast<size_t>(I * kSB + wr * 32 + ra * 16 + l16) * kSB + g16 * 16;
+  for (int x = 0; x < NRA; ++x) {
+    const gdouble* pa =
+        M.U + static_cast<size_t>(I * kSB + 16 * (ro + x) + l16) * kSB + 8 * c + 2 * g16;
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) va[ra][kk] = p[kk];
+    for (int kk = 0; kk < 2; ++kk) a[x][kk] = pa[kk];
   }
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int c = J * kSB + wc * 32 + rb * 16 + l16;
-    const double* p = M.U + static_cast<size_t>(c) * kSB + g16 * 16;
+  for (int x = 0; x < NRB; ++x) {
+    const gdouble* pb =
+        M.U + static_cast<size_t>(J * kSB + 16 * (co + x) + l16) * kSB + 8 * c + 2 * g16;
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) ub[rb][kk] = p[kk];
+    for (int kk = 0; kk < 2; ++kk) b[x][kk] = pb[kk];
+  }
+}
+
+template <int NRA, int NRB>
+__device__ __forceinline__ void wave_tile_mfma(int c, bool diag, int ro, int co,
+                                               const double (&a)[NRA][2],
+                                               const double (&b)[NRB][2],
+                                               f64x4 (&acc)[NRA][NRB]) {
+  const int lane = threadIdx.x & 63, g16 = lane >> 4;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const double rdq = g_sw.rD[8 * c + 2 * g16 + kk];
+#pragma unroll
+    for (int ra = 0; ra < NRA; ++ra) {
+      const double av = a[ra][kk] * rdq;
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+        if (!diag || co + rb <= ro + ra)
+          acc[ra][rb] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, b[rb][kk], acc[ra][rb], 0, 0, 0);
+    }
+  }
+}
+
+template <int NRA, int NRB>
+__device__ __forceinline__ void wave_tile(const SweepMat& M, int I, int J, int ro, int co) {
+  SweepSmem& sm = g_sw;
+  const int lane = threadIdx.x & 63, g16 = lane >> 4, l16 = lane & 15;
+  const bool diag = I == J;
+  if (diag && co > ro + NRA - 1) return;  // strictly upper part of a diagonal tile
+  f64x4 acc[NRA][NRB];
+#pragma unroll
+  for (int ra = 0; ra < NRA; ++ra)
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) acc[ra][rb] = f64x4{0.0, 0.0, 0.0, 0.0};
+  {
+    double a0[NRA][2], b0[NRB][2], a1[NRA][2], b1[NRB][2];
+    wave_tile_chunk<NRA, NRB>(M, I, J, ro, co, 0, a0, b0);
+#pragma unroll
+    for (int c = 0; c < 8; c += 2) {
+      wave_tile_chunk<NRA, NRB>(M, I, J, ro, co, c + 1, a1, b1);
+      wave_tile_mfma<NRA, NRB>(c, diag, ro, co, a0, b0, acc);
+      if (c + 2 < 8) wave_tile_chunk<NRA, NRB>(M, I, J, ro, co, c + 2, a0, b0);
+      wave_tile_mfma<NRA, NRB>(c + 1, diag, ro, co, a1, b1, acc);
+    }
+  }
+  int pc[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int c = J * kSB + 16 * (co + rb) + l16;
     pc[rb] = s_active(M, c) ? sm.pos[c] : -1;
   }
 #pragma unroll
-  for (int ra = 0; ra < 2; ++ra)
+  for (int rh = 0; rh < NRA; rh += 2) {
+    // current values (or the V entries that replace them), one batch of loads
+    double x[2][NRB][4];
+    int pr[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = I * kSB + wr * 32 + ra * 16 + g16 + 4 * i;
-      pr[ra][i] = s_active(M, r) ? sm.pos[r] : -1;
-    }
-#pragma unroll
-  for (int ra = 0; ra < 2; ++ra)
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = I * kSB + wr * 32 + ra * 16 + g16 + 4 * i;
-        const int c = J * kSB + wc * 32 + rb * 16 + l16;
-        const int q = pr[ra][i], qc = pc[rb];
-        double v = 0.0;
-        if (q >= 0 && qc >= 0) v = -sm.sgn[q] * sm.sgn[qc] * sm.pp[q][qc];
-        else if (qc >= 0) v = sm.sgn[qc] * M.V[static_cast<size_t>(r) * kSB + qc];
-        else if (q >= 0) v = sm.sgn[q] * M.V[static_cast<size_t>(c) * kSB + q];
-        else if (!diag || r >= c) v = M.S[static_cast<size_t>(r) * M.ld + c];
-        tv[ra][rb][i] = v;
+        const int r = I * kSB + 16 * (ro + rh + h) + g16 + 4 * i;
+        pr[h][i] = s_active(M, r) ? sm.pos[r] : -1;
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          const int c = J * kSB + 16 * (co + rb) + l16;
+          const int q = pr[h][i], qc = pc[rb];
+          const gdouble* src = qc >= 0 ? M.V + (static_cast<size_t>(r) * kSB + qc)
+                             : q >= 0  ? M.V + (static_cast<size_t>(c) * kSB + q)
+                                       : M.S + (static_cast<size_t>(r) * M.ld + c);
+          x[h][rb][i] = *src;
+        }
       }
 #pragma unroll
-  for (int ra = 0; ra < 2; ++ra)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) va[ra][kk] *= sm.rD[g16 * 16 + kk];
-  f64x4 acc[2][2] = {};
+      for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-  for (int kk = 0; kk < 16; ++kk)
-#pragma unroll
-    for (int ra = 0; ra < 2; ++ra)
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-        acc[ra][rb] = __builtin_amdgcn_mfma_f64_16x16x4f64(va[ra][kk], ub[rb][kk], acc[ra][rb], 0, 0, 0);
-#pragma unroll
-  for (int ra = 0; ra < 2; ++ra)
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = I * kSB + wr * 32 + ra * 16 + g16 + 4 * i;
-        const int c = J * kSB + wc * 32 + rb * 16 + l16;
-        if (diag && r < c) continue;
-        const double v = (pr[ra][i] >= 0 || pc[rb] >= 0) ? tv[ra][rb][i] : tv[ra][rb][i] - acc[ra][rb][i];
-        M.S[static_cast<size_t>(r) * M.ld + c] = v;
-      }
+        for (int i = 0; i < 4; ++i) {
+          const int r = I * kSB + 16 * (ro + rh + h) + g16 + 4 * i;
+          const int c = J * kSB + 16 * (co + rb) + l16;
+          if (diag && r < c) continue;
+          const int q = pr[h][i], qc = pc[rb];
+          double v;
+          if (q >= 0 && qc >= 0) v = -sm.sgn[q] * sm.sgn[qc] * sm.pp[q][qc];
+          else if (qc >= 0) v = sm.sgn[qc] * x[h][rb][i];
+          else if (q >= 0) v = sm.sgn[q] * x[h][rb][i];
+          else v = x[h][rb][i] - acc[rh + h][rb][i];
+          M.S[static_cast<size_t>(r) * M.ld + c] = v;
+        }
+  }
 }
+
+// Active tiles of a step in row-major order: variable band Iv (0..nvb-1) has
+// nrb right-hand-side tiles, then, unless Iv < skip, variable tiles 0..Iv.
+struct TileWalk {
+  int Iv, j, nrb, skip, vb0;
+  __device__ int count(int iv) const { return nrb + (iv >= skip ? iv + 1 : 0); }
+  __device__ void seek(int a) {
+    Iv = 0;
+    while (a >= count(Iv)) {
+      a -= count(Iv);
+      ++Iv;
+    }
+    j = a;
+  }
+  __device__ void next() {
+    if (++j >= count(Iv)) {
+      ++Iv;
+      j = 0;
+    }
+  }
+  __device__ int I() const { return vb0 + Iv; }
+  __device__ int J() const { return j < nrb ? j : vb0 + j - nrb; }
+};
 
 // One sweep step over the k pivots in sm.piv / sm.sgn / sm.pos, by the team.
 // Tiles whose row band is a variable band below skip_below (and whose column
 // is a variable band) are left alone: the value fit never reads them again.
-// Returns whether a pivot had the wrong sign.
-__device__ __noinline__ bool sweep_step(const SweepMat& M, Team& tm, int k, int skip_below) {
+//
+// Lookahead: when the next step's kn pivots are already known (sm.piv2,
+// sm.sgn2) and the team has more than one member, its last member does no
+// tiles; it takes the next pivot block from S before this step's update,
+// applies the update to it from the staged W rows (A' = A - W D^-1 W^T; the
+// two pivot sets are disjoint), inverts it and publishes B, L^-1 and 1/D in
+// M.stage, which the next step loads instead of inverting (pre = true).
+// Returns whether a pivot of this step had the wrong sign (a lookahead
+// member flags its own into *status).
+__device__ __noinline__ bool sweep_step(const SweepMat M, Team& tm, int k, int skip_below, int kn,
+                                        bool pre, int32_t* status) {
   SweepSmem& sm = g_sw;
-  for (int e = threadIdx.x; e < kSB * kSB; e += kTeamThreads) {
-    const int a = e >> 6, c = e & 63;
-    sm.pp[a][c] = (a < k && c < k) ? s_at(M, sm.piv[a], sm.piv[c]) : (a == c ? 1.0 : 0.0);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const bool la = kn > 0 && tm.size > 1;
+  const bool me_la = la && tm.rank == tm.size - 1;
+  bool bad = false;
+  if (pre) {
+    for (int e = tid; e < kSB * kSB; e += kTeamThreads) {
+      const int r = e >> 6, c = e & 63;
+      sm.pp[r][c] = M.stage[e];
+      sm.li[r][c] = M.stage[kSB * kSB + e];
+    }
+    if (tid < kSB) sm.rD[tid] = M.stage[2 * kSB * kSB + tid];
+    __syncthreads();
+  } else {
+    for (int e = tid; e < kSB * kSB; e += kTeamThreads) {
+      const int a = e >> 6, c = e & 63;
+      const bool in = a < k && c < k;
+      const double v = s_at_or0(M, in, in ? sm.piv[a] : 0, in ? sm.piv[c] : 0);
+      sm.pp[a][c] = in ? v : (a == c ? 1.0 : 0.0);
+    }
+    __syncthreads();
+    bad = small_inverse(k);
   }
-  __syncthreads();
-  const bool bad = small_inverse(k);
   const int nrb = (M.n_rhs + kSB - 1) / kSB, nvb = (M.n_var + kSB - 1) / kSB;
   const int vb0 = M.r_al / kSB;
-  for (int bi = tm.rank; bi < nrb + nvb; bi += tm.size) v_band(M, bi < nrb ? bi : vb0 + bi - nrb, k);
-  team_sync(tm);
-  // tiles: variable band I (0..nvb-1) owns nrb right-hand-side tiles, then
-  // variable tiles J = 0..I
-  const int ntiles = nvb * nrb + nvb * (nvb + 1) / 2;
-  // each member takes a contiguous run of tiles (mostly one row band)
-  const int t0 = static_cast<int>((static_cast<long long>(ntiles) * tm.rank) / tm.size);
-  const int t1 = static_cast<int>((static_cast<long long>(ntiles) * (tm.rank + 1)) / tm.size);
-  int I = 0, first = 0;
-  for (int tau = t0; tau < t1; ++tau) {
-    while (tau - first >= nrb + I + 1) {
-      first += nrb + I + 1;
-      ++I;
+  const int vmembers = la ? tm.size - 1 : tm.size;
+  if (!me_la) {
+    for (int bi = tm.rank; bi < nrb + nvb; bi += vmembers) v_band(M, bi < nrb ? bi : vb0 + bi - nrb, k);
+  } else {
+    // the next pivot block after this step's update, A' = A[P', P'] -
+    // W' D^-1 W'^T with W' = A[P', P] L^-T, taken from S before any member
+    // updates it and formed in LDS while the others build the bands
+    const int wr = wave >> 1, wc = wave & 1, g16 = lane >> 4, l16 = lane & 15;
+    double ua[2][16];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int ra = wr * 32 + x * 16 + l16;
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) {
+        const int q = g16 * 16 + kk;
+        const bool ok = ra < kn && q < k;
+        ua[x][kk] = s_at_or0(M, ok, ok ? sm.piv2[ra] : 0, ok ? sm.piv[q] : 0);
+      }
     }
-    const int j = tau - first;
-    if (j >= nrb && I < skip_below) continue;
-    sweep_tile(M, vb0 + I, j < nrb ? j : vb0 + j - nrb);
+    f64x4 wa[2][2] = {};
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const int q = g16 * 16 + kk;
+#pragma unroll
+      for (int y = 0; y < 2; ++y) {
+        const double l = sm.li[wc * 32 + y * 16 + l16][q];
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+          wa[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(ua[x][kk], l, wa[x][y], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // B and L^-1 of this step are no longer read here
+    for (int e = tid; e < kSB * kSB; e += kTeamThreads) {
+      const int a = e >> 6, c = e & 63;
+      const bool in = a < kn && c < kn;
+      const double v = s_at_or0(M, in, in ? sm.piv2[a] : 0, in ? sm.piv2[c] : 0);
+      sm.pp[a][c] = in ? v : (a == c ? 1.0 : 0.0);
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sm.li[wr * 32 + x * 16 + g16 + 4 * i][wc * 32 + y * 16 + l16] = wa[x][y][i];
+    __syncthreads();
+    f64x4 acc[2][2] = {};
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const int q = g16 * 16 + kk;
+      const double rdq = sm.rD[q];
+      double av[2], bv[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        av[x] = sm.li[wr * 32 + x * 16 + l16][q] * rdq;
+        bv[x] = sm.li[wc * 32 + x * 16 + l16][q];
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[x], bv[y], acc[x][y], 0, 0, 0);
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = wr * 32 + x * 16 + g16 + 4 * i, col = wc * 32 + y * 16 + l16;
+          if (row < kn && col < kn) sm.pp[row][col] -= acc[x][y][i];
+        }
+  }
+  team_sync(tm);
+  if (me_la) {
+    if (tid < kSB) sm.sgn[tid] = sm.sgn2[tid];
+    __syncthreads();
+    const bool bad2 = small_inverse(kn);
+    for (int e = tid; e < kSB * kSB; e += kTeamThreads) {
+      const int r = e >> 6, c = e & 63;
+      M.stage[e] = sm.pp[r][c];
+      M.stage[kSB * kSB + e] = sm.li[r][c];
+    }
+    if (tid < kSB) M.stage[2 * kSB * kSB + tid] = sm.rD[tid];
+    if (bad2 && tid == 0 && status) atomicOr(status, 1);
+  } else {
+    // every wave of the tile workers takes a contiguous run of the active
+    // tiles; when there are fewer tiles than waves, of their halves or quarters
+    int total = 0;
+    for (int iv = 0; iv < nvb; ++iv) total += nrb + (iv >= skip_below ? iv + 1 : 0);
+    const int workers = la ? tm.size - 1 : tm.size;
+    const int nw = workers * (kTeamThreads / 64), gw = tm.rank * (kTeamThreads / 64) + wave;
+    const int parts = 2 * total <= nw ? 4 : (total < nw ? 2 : 1);
+    const int tasks = total * parts;
+    const int a0 = static_cast<int>((static_cast<long long>(tasks) * gw) / nw);
+    const int a1 = static_cast<int>((static_cast<long long>(tasks) * (gw + 1)) / nw);
+    TileWalk w{0, 0, nrb, skip_below, vb0};
+    w.seek(a0 / parts);
+    for (int a = a0; a < a1; ++a) {
+      const int part = a % parts;
+      if (parts == 1) wave_tile<4, 4>(M, w.I(), w.J(), 0, 0);
+      else if (parts == 2) wave_tile<2, 4>(M, w.I(), w.J(), 2 * part, 0);
+      else wave_tile<2, 2>(M, w.I(), w.J(), 2 * (part >> 1), 2 * (part & 1));
+      if (part == parts - 1) w.next();
+    }
   }
   team_sync(tm);
   return bad;
@@ -931,7 +1134,8 @@ __device__ __forceinline__ double sweep_flops(int k, int n) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_nnls_sweep(
     double* __restrict__ S, size_t sS, int ld, double* __restrict__ Ub, double* __restrict__ Vb,
-    size_t sUV, double* __restrict__ wv, int32_t* __restrict__ Fidx, int32_t* __restrict__ inv,
+    size_t sUV, double* __restrict__ stage, double* __restrict__ wv, int32_t* __restrict__ Fidx,
+    int32_t* __restrict__ inv,
     int32_t* __restrict__ msz, int32_t* __restrict__ status, unsigned* __restrict__ bar,
     int* __restrict__ err, int* __restrict__ xcc, double* __restrict__ flops, int B, int t,
     int max_iters, int tx) {
@@ -943,11 +1147,12 @@ __global__ __launch_bounds__(256) void k_nnls_sweep(
   for (int s = tid; s < kMaxRows; s += kTeamThreads) sm.pos[s] = -1;
   constexpr int NV = kMaxTeamT / kTeamThreads;
   for (int b = team; b < B; b += nteams) {
-    const SweepMat M{S + b * sS, Ub + b * sUV, Vb + b * sUV, ld, kSB, 1, t};
+    const SweepMat M{gptr(S + b * sS), gptr(Ub + b * sUV), gptr(Vb + b * sUV),
+                     gptr(stage + static_cast<size_t>(b) * kStage), ld, kSB, 1, t};
     for (int j = tid; j < t; j += kTeamThreads) sm.inF[j] = 0;
     double cm = 0.0, hm = 0.0;
     for (int j = tid; j < t; j += kTeamThreads) {
-      const double* row = M.S + static_cast<size_t>(kSB + j) * ld;
+      const gdouble* row = M.S + static_cast<size_t>(kSB + j) * ld;
       cm = fmax(cm, fabs(row[0]));
       hm = fmax(hm, row[kSB + j]);
     }
@@ -961,7 +1166,8 @@ __global__ __launch_bounds__(256) void k_nnls_sweep(
 #pragma unroll
       for (int q = 0; q < NV; ++q) {
         const int j = tid + q * kTeamThreads;
-        val[q] = j < t ? M.S[static_cast<size_t>(kSB + j) * ld] : 0.0;
+        const double v = M.S[static_cast<size_t>(kSB + (j < t ? j : 0)) * ld];
+        val[q] = j < t ? v : 0.0;
         if (j < t && sm.inF[j]) xm = fmax(xm, fabs(val[q]));
       }
       const double tol = 1e-13 * scale * fmax(1.0, wg_max(xm));
@@ -1002,14 +1208,20 @@ __global__ __launch_bounds__(256) void k_nnls_sweep(
       __syncthreads();
       for (int s0 = 0; s0 < nflip; s0 += kSB) {
         const int k = min(kSB, nflip - s0);
+        const int kn = min(kSB, nflip - s0 - k);
         if (tid < k) {
           const int j = sm.list[s0 + tid];
           sm.piv[tid] = kSB + j;
           sm.sgn[tid] = sm.inF[j] ? -1.0 : 1.0;
           sm.pos[kSB + j] = static_cast<int16_t>(tid);
         }
+        if (tid < kn) {
+          const int j = sm.list[s0 + k + tid];
+          sm.piv2[tid] = kSB + j;
+          sm.sgn2[tid] = sm.inF[j] ? -1.0 : 1.0;
+        }
         __syncthreads();
-        bad |= sweep_step(M, tm, k, 0);
+        bad |= sweep_step(M, tm, k, 0, kn, s0 > 0 && tm.size > 1, status ? status + b : nullptr);
         if (tid < k) {
           const int j = sm.list[s0 + tid];
           sm.inF[j] ^= 1;
@@ -1062,7 +1274,7 @@ __global__ __launch_bounds__(256) void k_nnls_sweep(
 // sweep the m variables in bands of 64; afterwards rows r_al + a hold C_v[a].
 __global__ __launch_bounds__(256) void k_value_sweep(
     double* __restrict__ S, size_t sS, int ld, int r_al, double* __restrict__ Ub,
-    double* __restrict__ Vb, size_t sUV, const int32_t* __restrict__ msz,
+    double* __restrict__ Vb, size_t sUV, double* __restrict__ stage, const int32_t* __restrict__ msz,
     int32_t* __restrict__ status, unsigned* __restrict__ bar, int* __restrict__ err,
     int* __restrict__ xcc, double* __restrict__ flops, int B, int D, int tx) {
   SweepSmem& sm = g_sw;
@@ -1073,17 +1285,24 @@ __global__ __launch_bounds__(256) void k_value_sweep(
   for (int s = tid; s < kMaxRows; s += kTeamThreads) sm.pos[s] = -1;
   for (int b = team; b < B; b += nteams) {
     const int m = msz[b];
-    const SweepMat M{S + b * sS, Ub + b * sUV, Vb + b * sUV, ld, r_al, D, m};
+    const SweepMat M{gptr(S + b * sS), gptr(Ub + b * sUV), gptr(Vb + b * sUV),
+                     gptr(stage + static_cast<size_t>(b) * kStage), ld, r_al, D, m};
     bool bad = false;
     for (int s0 = 0; s0 < m; s0 += kSB) {
       const int k = min(kSB, m - s0);
+      const int kn = min(kSB, m - s0 - k);
       if (tid < k) {
         sm.piv[tid] = r_al + s0 + tid;
         sm.sgn[tid] = 1.0;
         sm.pos[r_al + s0 + tid] = static_cast<int16_t>(tid);
       }
+      if (tid < kn) {
+        sm.piv2[tid] = r_al + s0 + k + tid;
+        sm.sgn2[tid] = 1.0;
+      }
       __syncthreads();
-      bad |= sweep_step(M, tm, k, s0 / kSB);
+      bad |= sweep_step(M, tm, k, s0 / kSB, kn, s0 > 0 && tm.size > 1,
+                        status ? status + b : nullptr);
       if (tid < k) sm.pos[r_al + s0 + tid] = -1;
       __syncthreads();
     }
@@ -1274,7 +1493,7 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
   if (e != hipSuccess) return e;
   int* err = reinterpret_cast<int*>(fb.bar + kBarWords - 1);
   {
-    void* args[] = {&fb.S,   &sS,      &ld,        &fb.U,   &fb.V,  &sUV,     &fb.wv,
+    void* args[] = {&fb.S,   &sS,      &ld,        &fb.U,   &fb.V,  &sUV,     &fb.stage, &fb.wv,
                     &fb.Fidx, &fb.inv, &fb.msz,    &status, &fb.bar, &err,    &fb.xcc,
                     &fb.flops, &B,     &t,         &max_iters, &tx};
     e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_nnls_sweep), dim3(grid),
@@ -1303,7 +1522,7 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
   {
     int r_al = rv, Dv = D;
     const int32_t* ms = fb.msz;
-    void* args[] = {&fb.S, &sS,     &ld,  &r_al, &fb.U,     &fb.V, &sUV, &ms,
+    void* args[] = {&fb.S, &sS,     &ld,  &r_al, &fb.U,     &fb.V, &sUV, &fb.stage, &ms,
                     &status, &fb.bar, &err, &fb.xcc, &fb.flops, &B,    &Dv,  &tx};
     e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_value_sweep), dim3(grid),
                                    dim3(kTeamThreads), args, 0, st);

@@ -77,7 +77,7 @@ Plan make_plan(const kvc_params_t* p) {
 }
 
 struct Layout {
-  size_t ml, lse, Opart, O, imp_part, imp, idx, status, PS, S, U, V, cvec, wv, lam, colpart, Fidx,
+  size_t ml, lse, Opart, O, imp_part, imp, idx, status, PS, S, U, V, stage, cvec, wv, lam, colpart, Fidx,
       inv, msz, bar, xcc, flops, part, total;
   size_t part_cap;
 };
@@ -109,6 +109,7 @@ Layout make_layout(const kvc_params_t* p) {
     L.U = take(B * ld * 64 * 8);
     L.V = take(B * ld * 64 * 8);
   }
+  L.stage = take(B * static_cast<size_t>(kvc::kSweepStage) * 8);
   L.cvec = take(B * t * 8);
   L.wv = take(B * t * 8);
   L.lam = take(B * 2 * 8);
@@ -159,6 +160,7 @@ kvc::FitBufs fit_bufs(void* ws, const Layout& L) {
   fb.S = at<double>(ws, L.S);
   fb.U = at<double>(ws, L.U);
   fb.V = at<double>(ws, L.V);
+  fb.stage = at<double>(ws, L.stage);
   fb.cvec = at<double>(ws, L.cvec);
   fb.wv = at<double>(ws, L.wv);
   fb.lam = at<double>(ws, L.lam);

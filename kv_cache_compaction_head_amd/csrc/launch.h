@@ -23,6 +23,7 @@ struct FitBufs {
   double* S;  // [B][ld][ld] sweep matrices (lower triangle), ld = sweep_ld(t, d)
   double* U;  // [B][ld][64] staged pivot columns of a sweep step
   double* V;  // [B][ld][64] the same times the inverse pivot block
+  double* stage;  // [B][kSweepStage] inverse of the next pivot block (lookahead)
   int32_t *Fidx, *inv, *msz;
   unsigned* bar;  // kBarWords words: team barrier counters, the last one the timeout flag
   int32_t* xcc;   // kMaxTeamGrid words: each team workgroup's XCC id
@@ -33,6 +34,7 @@ struct FitBufs {
 // Order of a head's sweep matrix: right-hand-side rows (d rounded up to 64)
 // plus the variables (t rounded up to 64).
 int sweep_ld(int t, int d);
+constexpr int kSweepStage = 2 * 64 * 64 + 64;
 constexpr int kMaxTeamGrid = 8192;
 constexpr int kBarWords = kMaxTeamGrid + 1;
 template <class In, int D>

@@ -50,6 +50,27 @@ template <> struct Frag<float> {
 
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;  // reference queries per workgroup
+constexpr int kXcd = 8;           // workgroups are dispatched round-robin over 8 XCDs
+
+// Score-kernel grid: one workgroup per (query block, key split, head), laid
+// out so that all query blocks of one (split, head) pair run on the same XCD
+// in consecutive slots: the K/V tiles they all read are then shared through
+// that XCD's L2 instead of being fetched once per query block.  Pair p goes
+// to XCD p mod 8; the grid has roundup(pairs, 8) * nqb workgroups.
+__device__ __forceinline__ bool score_grid(int nqb, int nsplit, int B, int& qb, int& split,
+                                           int& b) {
+  const int w = blockIdx.x, xcd = w % kXcd, slot = w / kXcd;
+  qb = slot % nqb;
+  const int p = (slot / nqb) * kXcd + xcd;
+  if (p >= nsplit * B) return false;
+  split = p % nsplit;
+  b = p / nsplit;
+  return true;
+}
+static int score_grid_size(int nqb, int nsplit, int B) {
+  const int pairs = nsplit * B;
+  return (pairs + kXcd - 1) / kXcd * kXcd * nqb;
+}
 
 // Copy a [rows x D] tile of a row-major [*, D] matrix into LDS (row stride LD),
 // zero-filling rows at or past `valid`.
@@ -84,12 +105,13 @@ template <class In, int D>
 __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
                                                    const In* __restrict__ K,
                                                    double2* __restrict__ ml, int n, int T,
-                                                   int keys_per_split) {
+                                                   int keys_per_split, int nqb, int nsplit, int B) {
   constexpr int KS = Frag<In>::KS, NK = D / KS, BN = 64, LD = D + 16 / sizeof(In);
   __shared__ __align__(16) In sK[BN * LD];
-  const int b = blockIdx.z, split = blockIdx.y;
+  int qb, split, b;
+  if (!score_grid(nqb, nsplit, B, qb, split, b)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5;
-  const int q = blockIdx.x * kBM + wave * 32 + (lane & 31);
+  const int q = qb * kBM + wave * 32 + (lane & 31);
   const In* Qb = Q + static_cast<size_t>(b) * n * D;
   const In* Kb = K + static_cast<size_t>(b) * T * D;
 
@@ -148,7 +170,7 @@ __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
       if (m != -INFINITY) ll += l * exp(static_cast<double>(m) - mm);
       if (mo != -INFINITY) ll += lo * exp(static_cast<double>(mo) - mm);
     }
-    ml[(static_cast<size_t>(b) * gridDim.y + split) * n + q] = make_double2(mm, ll);
+    ml[(static_cast<size_t>(b) * nsplit + split) * n + q] = make_double2(mm, ll);
   }
 }
 
@@ -183,7 +205,39 @@ __device__ __forceinline__ int vt_pos(int kk) {
 // grid (ceil(n/128), nsplit, B), block 256.
 //   Opart[b][split][dd][q]  partial (P V)^T over the split's keys
 //   imp_part[b][qb][j]      sum over the 128 queries of block qb of p^2 (or p)
+// Keys go in tiles of 64: the next tile's K and V rows are fetched into
+// registers while the current one is computed, then written to the other
+// half of a double-buffered LDS tile, so each tile needs one barrier.  Each
+// wave reduces its 32 queries' p^2 per key with a butterfly that halves the
+// kept key slots at every exchange (16 shuffles for 16 keys); the four waves'
+// partials are added after the tile's barrier.
 // ---------------------------------------------------------------------------
+
+// Sum of v[0..15] (accumulator rows) over the 32 lanes of this lane's half
+// wave; the result for row 8*b4 + 4*b3 + 2*b2 + b1 (b_i = bit i of the lane)
+// ends up in both lanes of the pair differing in bit 0.
+__device__ __forceinline__ float half_wave_rowsum(const float (&v)[16], int lane) {
+  const bool b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+  float w[8], x[4], y[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float keep = b4 ? v[8 + i] : v[i], send = b4 ? v[i] : v[8 + i];
+    w[i] = keep + __shfl_xor(send, 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float keep = b3 ? w[4 + i] : w[i], send = b3 ? w[i] : w[4 + i];
+    x[i] = keep + __shfl_xor(send, 8);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float keep = b2 ? x[2 + i] : x[i], send = b2 ? x[i] : x[2 + i];
+    y[i] = keep + __shfl_xor(send, 4);
+  }
+  const float z = (b1 ? y[1] : y[0]) + __shfl_xor(b1 ? y[0] : y[1], 2);
+  return z + __shfl_xor(z, 1);
+}
+
 template <class In, int D, bool RMS>
 __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
                                                    const In* __restrict__ K,
@@ -191,18 +245,23 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
                                                    const double* __restrict__ lse,
                                                    float* __restrict__ Opart,
                                                    float* __restrict__ imp_part, int n, int T,
-                                                   int keys_per_split) {
-  constexpr int KS = Frag<In>::KS, NK = D / KS, BN = 32;
+                                                   int keys_per_split, int nqb, int nsplit,
+                                                   int B) {
+  constexpr int KS = Frag<In>::KS, NK = D / KS, BN = 64;
   constexpr int LD = D + 16 / sizeof(In);
   constexpr int LDV = BN + 16 / sizeof(In);
   constexpr int ND = D / 32;
-  __shared__ __align__(16) In sK[BN * LD];
-  __shared__ __align__(16) In sVt[D * LDV];
-  __shared__ float sImp[kWaves * 16 * 64];
+  constexpr int VEC = 16 / sizeof(In), CPR = D / VEC;  // 16-byte chunks per row
+  constexpr int NCH = BN * CPR / 256;                   // chunks per thread per tile
+  static_assert(BN == 64 && NCH * 4 == CPR, "V fetch: a wave per column chunk of 64 keys");
+  __shared__ __align__(16) In sK[2][BN * LD];
+  __shared__ __align__(16) In sVt[2][D * LDV];
+  __shared__ float sImp[2][kWaves][BN];
 
-  const int b = blockIdx.z, split = blockIdx.y, nsplit = gridDim.y, nqb = gridDim.x;
+  int qb, split, b;
+  if (!score_grid(nqb, nsplit, B, qb, split, b)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5;
-  const int q = blockIdx.x * kBM + wave * 32 + (lane & 31);
+  const int q = qb * kBM + wave * 32 + (lane & 31);
   const In* Qb = Q + static_cast<size_t>(b) * n * D;
   const In* Kb = K + static_cast<size_t>(b) * T * D;
   const In* Vb = V + static_cast<size_t>(b) * T * D;
@@ -221,88 +280,112 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
 
   const int j0 = split * keys_per_split;
   const int j1 = min(T, j0 + keys_per_split);
-  for (int jt = j0; jt < j1; jt += BN) {
-    const int valid = j1 - jt;
-    __syncthreads();
-    load_tile<In, D, LD>(sK, Kb + static_cast<size_t>(jt) * D, BN, valid);
-    {  // V tile, transposed to [dd][key slot]
-      constexpr int VEC = 16 / sizeof(In), CPR = D / VEC;
-      for (int c = threadIdx.x; c < BN * CPR; c += blockDim.x) {
-        const int r = c / CPR, col = (c % CPR) * VEC;
-        In v[VEC];
-        if (r < valid) {
-          *reinterpret_cast<uint4*>(v) =
-              *reinterpret_cast<const uint4*>(Vb + static_cast<size_t>(jt + r) * D + col);
-        } else {
+  const int ntile = (j1 - j0 + BN - 1) / BN;
+  uint4 pk[NCH], pv[NCH];
+  // rows past the split end read row j1-1 (always valid) and are zeroed, so
+  // the fetch is one unconditional batch of loads
+  // K rows go to LDS as they are (consecutive lanes: consecutive 16-byte
+  // chunks of a row).  V is transposed on the way in, so a wave takes one
+  // 16-byte column chunk of 64 consecutive keys: each of its transposed
+  // writes then covers one contiguous 128-byte run of a V^T row, free of
+  // bank conflicts.
+  auto fetch = [&](int jt) {
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) v[e] = In(0);
-        }
-        const int pos = sizeof(In) == 2 ? vt_pos(r) : r;
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = threadIdx.x + c * 256, r = idx / CPR, col = (idx % CPR) * VEC;
+      const bool ok = jt + r < j1;
+      const uint4 kv = *reinterpret_cast<const uint4*>(
+          Kb + static_cast<size_t>(ok ? jt + r : j1 - 1) * D + col);
+      pk[c] = ok ? kv : make_uint4(0, 0, 0, 0);
+      const int rv = threadIdx.x & (BN - 1), colv = ((threadIdx.x >> 6) + 4 * c) * VEC;
+      const bool okv = jt + rv < j1;
+      const uint4 vv = *reinterpret_cast<const uint4*>(
+          Vb + static_cast<size_t>(okv ? jt + rv : j1 - 1) * D + colv);
+      pv[c] = okv ? vv : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto stash = [&](int buf) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) sVt[(col + e) * LDV + pos] = v[e];
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = threadIdx.x + c * 256, r = idx / CPR, col = (idx % CPR) * VEC;
+      *reinterpret_cast<uint4*>(&sK[buf][r * LD + col]) = pk[c];
+      const int rv = threadIdx.x & (BN - 1), colv = ((threadIdx.x >> 6) + 4 * c) * VEC;
+      In v[VEC];
+      *reinterpret_cast<uint4*>(v) = pv[c];
+      // V^T [dd][key slot]; bf16 slots follow the accumulator rows
+      const int pos = sizeof(In) == 2 ? (rv >> 5) * 32 + vt_pos(rv & 31) : rv;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) sVt[buf][(colv + e) * LDV + pos] = v[e];
+    }
+  };
+  if (ntile > 0) {
+    fetch(j0);
+    stash(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntile; ++it) {
+    const int cur = it & 1, jt = j0 + it * BN, valid = j1 - jt;
+    if (it + 1 < ntile) fetch(jt + BN);
+#pragma unroll 1
+    for (int st = 0; st < 2; ++st) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) {
+        auto a = Frag<In>::load(&sK[cur][(st * 32 + (lane & 31)) * LD + ks * KS + g * (KS / 2)]);
+        acc = Frag<In>::mma(a, bq[ks], acc);
       }
-    }
-    __syncthreads();
-
-    f32x16 acc = {};
-#pragma unroll
-    for (int ks = 0; ks < NK; ++ks) {
-      auto a = Frag<In>::load(&sK[(lane & 31) * LD + ks * KS + g * (KS / 2)]);
-      acc = Frag<In>::mma(a, bq[ks], acc);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kk = mfma32_row(r, lane);
-      float p = 0.f;
-      if (kk < valid && q < n)
-        p = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2) - ml2lo);
-      acc[r] = p;
-      sImp[(wave * 16 + r) * 64 + lane] = RMS ? p * p : p;
-    }
-    __syncthreads();
-    {  // column sums over the workgroup's 128 queries, fixed order
-      const int kk = threadIdx.x >> 3, part = threadIdx.x & 7;
-      const int gk = (kk >> 2) & 1, rk = ((kk >> 3) << 2) | (kk & 3);
-      const int w = part >> 1, lb = gk * 32 + (part & 1) * 16;
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s += sImp[(w * 16 + rk) * 64 + lb + i];
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
-      if (part == 0 && kk < valid)
-        imp_part[(static_cast<size_t>(b) * nqb + blockIdx.x) * T + jt + kk] = s;
-    }
-
-    if constexpr (sizeof(In) == 2) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        bf16x8 hi, lo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = acc[h * 8 + e];
-          const __bf16 ph = static_cast<__bf16>(p);
-          hi[e] = ph;
-          lo[e] = static_cast<__bf16>(p - static_cast<float>(ph));
-        }
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              &sVt[(dt * 32 + (lane & 31)) * LDV + h * 16 + g * 8]);
-          accO[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, hi, accO[dt], 0, 0, 0);
-          accO[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, lo, accO[dt], 0, 0, 0);
-        }
-      }
-    } else {
+      float w[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kk = mfma32_row(r, lane);
+        const int kk = st * 32 + mfma32_row(r, lane);
+        const float e = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2) - ml2lo);
+        const float p = (kk < valid && q < n) ? e : 0.f;
+        acc[r] = p;
+        w[r] = RMS ? p * p : p;
+      }
+      {
+        const float tot = half_wave_rowsum(w, lane);
+        const int r = ((lane >> 4) & 1) * 8 + ((lane >> 3) & 1) * 4 + ((lane >> 2) & 1) * 2 +
+                      ((lane >> 1) & 1);
+        if ((lane & 1) == 0) sImp[cur][wave][st * 32 + mfma32_row(r, lane)] = tot;
+      }
+      if constexpr (sizeof(In) == 2) {
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt) {
-          const float a = static_cast<float>(sVt[(dt * 32 + (lane & 31)) * LDV + kk]);
-          accO[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, acc[r], accO[dt], 0, 0, 0);
+        for (int h = 0; h < 2; ++h) {
+          bf16x8 hi, lo;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float p = acc[h * 8 + e];
+            const __bf16 ph = static_cast<__bf16>(p);
+            hi[e] = ph;
+            lo[e] = static_cast<__bf16>(p - static_cast<float>(ph));
+          }
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                &sVt[cur][(dt * 32 + (lane & 31)) * LDV + st * 32 + h * 16 + g * 8]);
+            accO[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, hi, accO[dt], 0, 0, 0);
+            accO[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, lo, accO[dt], 0, 0, 0);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = st * 32 + mfma32_row(r, lane);
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt) {
+            const float a = static_cast<float>(sVt[cur][(dt * 32 + (lane & 31)) * LDV + kk]);
+            accO[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, acc[r], accO[dt], 0, 0, 0);
+          }
         }
       }
+    }
+    if (it + 1 < ntile) stash(cur ^ 1);
+    __syncthreads();
+    if (threadIdx.x < BN && static_cast<int>(threadIdx.x) < valid) {
+      const int t = threadIdx.x;
+      imp_part[(static_cast<size_t>(b) * nqb + qb) * T + jt + t] =
+          ((sImp[cur][0][t] + sImp[cur][1][t]) + sImp[cur][2][t]) + sImp[cur][3][t];
     }
   }
   if (q < n) {
@@ -361,18 +444,20 @@ hipError_t launch_score(const void* Q, const void* K, const void* V, double2* ml
   const In* k = static_cast<const In*>(K);
   const In* v = static_cast<const In*>(V);
   prof_mark(0, false, st);
-  hipLaunchKernelGGL((k_score_lse<In, D>), dim3(nqb, nsplit1, B), dim3(256), 0, st, q, k, ml, n,
-                     T, kps1);
+  hipLaunchKernelGGL((k_score_lse<In, D>), dim3(score_grid_size(nqb, nsplit1, B)), dim3(256), 0,
+                     st, q, k, ml, n, T, kps1, nqb, nsplit1, B);
   prof_mark(0, true, st);
   hipLaunchKernelGGL(k_lse_merge, dim3((B * n + 255) / 256), dim3(256), 0, st, ml, lse, n,
                      nsplit1, B);
   prof_mark(1, false, st);
   if (rms)
-    hipLaunchKernelGGL((k_expweight<In, D, true>), dim3(nqb, nsplit2, B), dim3(256), 0, st, q, k,
-                       v, lse, Opart, imp_part, n, T, kps2);
+    hipLaunchKernelGGL((k_expweight<In, D, true>), dim3(score_grid_size(nqb, nsplit2, B)),
+                       dim3(256), 0, st, q, k, v, lse, Opart, imp_part, n, T, kps2, nqb, nsplit2,
+                       B);
   else
-    hipLaunchKernelGGL((k_expweight<In, D, false>), dim3(nqb, nsplit2, B), dim3(256), 0, st, q,
-                       k, v, lse, Opart, imp_part, n, T, kps2);
+    hipLaunchKernelGGL((k_expweight<In, D, false>), dim3(score_grid_size(nqb, nsplit2, B)),
+                       dim3(256), 0, st, q, k, v, lse, Opart, imp_part, n, T, kps2, nqb, nsplit2,
+                       B);
   prof_mark(1, true, st);
   hipLaunchKernelGGL(k_o_reduce, dim3((n + 31) / 32, D / 32, B), dim3(32, 8), 0, st, Opart, O, n,
                      D, nsplit2);

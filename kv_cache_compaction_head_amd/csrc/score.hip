@@ -107,7 +107,8 @@ __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
                                                    double2* __restrict__ ml, int n, int T,
                                                    int keys_per_split, int nqb, int nsplit, int B) {
   constexpr int KS = Frag<In>::KS, NK = D / KS, BN = 64, LD = D + 16 / sizeof(In);
-  __shared__ __align__(16) In sK[BN * LD];
+  constexpr int VEC = 16 / sizeof(In), CPR = D / VEC, NCH = BN * CPR / 256;
+  __shared__ __align__(16) In sK[2][BN * LD];
   int qb, split, b;
   if (!score_grid(nqb, nsplit, B, qb, split, b)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5;
@@ -120,21 +121,46 @@ __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
 
   const int j0 = split * keys_per_split;
   const int j1 = min(T, j0 + keys_per_split);
+  const int ntile = (j1 - j0 + BN - 1) / BN;
+  // next tile's K rows in registers while the current tile is computed;
+  // rows past the split end read row j1-1 and are zeroed (one batch of loads)
+  uint4 pk[NCH];
+  auto fetch = [&](int jt) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = threadIdx.x + c * 256, r = idx / CPR, col = (idx % CPR) * VEC;
+      const bool ok = jt + r < j1;
+      const uint4 kv = *reinterpret_cast<const uint4*>(
+          Kb + static_cast<size_t>(ok ? jt + r : j1 - 1) * D + col);
+      pk[c] = ok ? kv : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = threadIdx.x + c * 256, r = idx / CPR, col = (idx % CPR) * VEC;
+      *reinterpret_cast<uint4*>(&sK[buf][r * LD + col]) = pk[c];
+    }
+  };
   // running max m (a score, exact in fp32) and sum l = sum exp(s - m) in fp64:
   // each 16-term tile sum is formed in fp32, then accumulated in double, and
   // the rare rescale on a new maximum uses a double exp.
   float m = -INFINITY;
   double l = 0.0;
-  for (int jt = j0; jt < j1; jt += BN) {
-    __syncthreads();
-    load_tile<In, D, LD>(sK, Kb + static_cast<size_t>(jt) * D, BN, j1 - jt);
-    __syncthreads();
+  if (ntile > 0) {
+    fetch(j0);
+    stash(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntile; ++it) {
+    const int cur = it & 1, jt = j0 + it * BN;
+    if (it + 1 < ntile) fetch(jt + BN);
 #pragma unroll
     for (int st = 0; st < BN / 32; ++st) {
       f32x16 acc = {};
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks) {
-        auto a = Frag<In>::load(&sK[(st * 32 + (lane & 31)) * LD + ks * KS + g * (KS / 2)]);
+        auto a = Frag<In>::load(&sK[cur][(st * 32 + (lane & 31)) * LD + ks * KS + g * (KS / 2)]);
         acc = Frag<In>::mma(a, bq[ks], acc);
       }
       float tmax = -INFINITY;
@@ -159,6 +185,8 @@ __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
         l += static_cast<double>(sum);
       }
     }
+    if (it + 1 < ntile) stash(cur ^ 1);
+    __syncthreads();
   }
   // lanes l and l+32 hold the same query over different keys: merge them
   const float mo = __shfl_xor(m, 32);

@@ -53,7 +53,9 @@ extern "C" {
 
 /* Per-head numerical status written to out_status[b] (0 = ok). */
 #define KVC_STATUS_OK            0
-#define KVC_STATUS_NOT_SPD       1  /* a Cholesky pivot was <= 0                */
+#define KVC_STATUS_NOT_SPD       1  /* a sweep pivot had the wrong sign (the
+                                       regularized Gram is not numerically
+                                       positive definite)                      */
 #define KVC_STATUS_NNLS_CAP      2  /* NNLS stopped at max_nnls_iters           */
 #define KVC_STATUS_NONFINITE     4  /* a non-finite value reached the fits      */
 #define KVC_STATUS_SYNC_TIMEOUT  8  /* a fit team's barrier wait ran out (the
@@ -105,6 +107,34 @@ int kvc_compact(const kvc_params_t* p, const void* Q_ref, const void* K, const v
 int kvc_fit(const kvc_params_t* p, const void* Q_ref, const void* K, const void* V,
             const int32_t* idx, float* out_bias, float* out_V, int32_t* out_status,
             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Chunked compaction ("Compaction par blocs" of the same summary): each head's
+ * cache is cut into n_chunks contiguous chunks of T / n_chunks keys, every
+ * chunk is compacted on its own to t entries against the head's full Q_ref
+ * (lse, output, importance and both fits are taken over the chunk alone), and
+ * the results are concatenated in chunk order.  Attention over concatenated
+ * blocks splits into per-block (output, mass) pairs (the block-concatenation
+ * decomposition of the main objective), so the concatenated (C_k, beta, C_v)
+ * matches the whole cache's attention as each chunk matches its own; no bias
+ * is re-fit after the merge.
+ *   p          sizes of the whole problem: B heads of T keys, t kept keys PER
+ *              CHUNK; T must be a multiple of n_chunks and t <= T / n_chunks
+ *   n_chunks   >= 1; 1 gives exactly kvc_compact
+ *   Q_ref      [B, n, d]             in_dtype
+ *   K, V       [B, T, d]             in_dtype
+ *   out_K      [B, n_chunks * t, d]  in_dtype   kept keys, chunk-major
+ *   out_bias   [B, n_chunks * t]     float32
+ *   out_V      [B, n_chunks * t, d]  float32
+ *   out_idx    [B, n_chunks * t]     int32      positions in the head's cache
+ *                                               (ascending); may be NULL
+ *   out_status [B, n_chunks]         int32      KVC_STATUS_* per chunk; may be NULL
+ *   workspace  >= kvc_workspace_bytes_chunked(p, n_chunks) bytes
+ * Returns as kvc_compact; KVC_EINVAL also when T % n_chunks != 0. */
+size_t kvc_workspace_bytes_chunked(const kvc_params_t* p, int64_t n_chunks);
+int kvc_compact_chunked(const kvc_params_t* p, int64_t n_chunks, const void* Q_ref,
+                        const void* K, const void* V, void* out_K, float* out_bias, float* out_V,
+                        int32_t* out_idx, int32_t* out_status, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
 
 /* Where the intermediates of the last call live inside its workspace (byte
  * offsets), for inspection after the stream completes:

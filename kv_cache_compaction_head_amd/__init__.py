@@ -13,10 +13,10 @@ import dataclasses
 from . import _lib
 from ._lib import (KVC_AGG_MEAN, KVC_AGG_RMS, KVC_BF16, KVC_F32, STATUS_NNLS_CAP,
                    STATUS_NONFINITE, STATUS_NOT_SPD, Params, load, make_params, strerror,
-                   workspace_bytes, workspace_layout)
+                   workspace_bytes, workspace_bytes_chunked, workspace_layout)
 
-__all__ = ["compact", "fit", "Compacted", "intermediates", "load", "make_params",
-           "workspace_bytes", "workspace_layout", "strerror", "Params"]
+__all__ = ["compact", "compact_chunked", "fit", "Compacted", "intermediates", "load", "make_params",
+           "workspace_bytes", "workspace_bytes_chunked", "workspace_layout", "strerror", "Params"]
 
 
 @dataclasses.dataclass
@@ -57,9 +57,9 @@ def _stream(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _workspace(p, device, workspace):
+def _workspace(p, device, workspace, need=None):
     import torch
-    need = workspace_bytes(p)
+    need = workspace_bytes(p) if need is None else need
     if need == 0:
         raise ValueError("invalid compaction parameters")
     if workspace is None:
@@ -90,6 +90,41 @@ def compact(Q, K, V, t: int, *, agg: str = "rms", ridge_rel: float = 1e-6,
                             ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(stream, dev))
     _lib.check(rc)
     return Compacted(keys, bias, values, idx, status, ws, p)
+
+
+def compact_chunked(Q, K, V, t: int, n_chunks: int, *, agg: str = "rms",
+                    ridge_rel: float = 1e-6, max_nnls_iters: int = 32, workspace=None,
+                    stream=None) -> Compacted:
+    """Cut each head's cache into n_chunks contiguous chunks, compact every chunk
+    to t entries on its own, concatenate.  keys/bias/values/idx are
+    [B, n_chunks * t, ...] (idx in whole-cache positions); status is
+    [B, n_chunks]."""
+    import torch
+    Q, K, V, _ = _prep(Q, K, V)
+    B, n, d = Q.shape
+    T = K.shape[1]
+    dt = "bf16" if Q.dtype == torch.bfloat16 else "f32"
+    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters)
+    dev = Q.device
+    need = workspace_bytes_chunked(p, n_chunks)
+    if need == 0:
+        raise ValueError("invalid chunked compaction parameters (T % n_chunks, t <= T/n_chunks)")
+    ws = _workspace(p, dev, workspace, need)
+    m = n_chunks * t
+    keys = torch.empty((B, m, d), dtype=Q.dtype, device=dev)
+    bias = torch.empty((B, m), dtype=torch.float32, device=dev)
+    values = torch.empty((B, m, d), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, m), dtype=torch.int32, device=dev)
+    status = torch.empty((B, n_chunks), dtype=torch.int32, device=dev)
+    rc = load().kvc_compact_chunked(ctypes.byref(p), ctypes.c_int64(n_chunks), _vp(Q), _vp(K),
+                                    _vp(V), _vp(keys), _vp(bias), _vp(values), _vp(idx),
+                                    _vp(status), _vp(ws),
+                                    ctypes.c_size_t(ws.numel() * ws.element_size()),
+                                    _stream(stream, dev))
+    _lib.check(rc)
+    # intermediates() of this result index (head, chunk) entries b * n_chunks + c
+    pc = make_params(B * n_chunks, T // n_chunks, n, d, t, dt, agg, ridge_rel, max_nnls_iters)
+    return Compacted(keys, bias, values, idx, status, ws, pc)
 
 
 def fit(Q, K, V, idx, *, ridge_rel: float = 1e-6, max_nnls_iters: int = 32,

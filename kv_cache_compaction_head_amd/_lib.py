@@ -15,7 +15,7 @@ KVC_AGG_RMS, KVC_AGG_MEAN = 0, 1
 STATUS_NOT_SPD, STATUS_NNLS_CAP, STATUS_NONFINITE = 1, 2, 4
 
 EXPORTS = ("kvc_params_default", "kvc_workspace_bytes", "kvc_compact", "kvc_fit",
-           "kvc_workspace_layout", "kvc_profile_enable", "kvc_profile_read", "kvc_strerror")
+           "kvc_workspace_bytes_chunked", "kvc_compact_chunked", "kvc_workspace_layout", "kvc_profile_enable", "kvc_profile_read", "kvc_strerror")
 STAGES = {"score_lse": 0, "expweight": 1, "select": 2, "ps": 3, "gram": 4, "nnls": 5,
           "value": 6, "total": 7}
 
@@ -54,6 +54,11 @@ def load() -> ctypes.CDLL:
     lib.kvc_compact.restype = ctypes.c_int
     lib.kvc_fit.argtypes = [P, vp, vp, vp, i32p, f32p, f32p, i32p, vp, ctypes.c_size_t, vp]
     lib.kvc_fit.restype = ctypes.c_int
+    lib.kvc_workspace_bytes_chunked.argtypes = [P, ctypes.c_int64]
+    lib.kvc_workspace_bytes_chunked.restype = ctypes.c_size_t
+    lib.kvc_compact_chunked.argtypes = [P, ctypes.c_int64, vp, vp, vp, vp, f32p, f32p, i32p, i32p,
+                                        vp, ctypes.c_size_t, vp]
+    lib.kvc_compact_chunked.restype = ctypes.c_int
     lib.kvc_workspace_layout.argtypes = [P, ctypes.POINTER(WsLayout)]
     lib.kvc_workspace_layout.restype = ctypes.c_int
     lib.kvc_profile_enable.argtypes = [ctypes.c_uint32]
@@ -80,6 +85,10 @@ def make_params(B, T, n, d, t, dtype, agg="rms", ridge_rel=1e-6, max_nnls_iters=
 
 def workspace_bytes(p: Params) -> int:
     return int(load().kvc_workspace_bytes(ctypes.byref(p)))
+
+
+def workspace_bytes_chunked(p: Params, n_chunks: int) -> int:
+    return int(load().kvc_workspace_bytes_chunked(ctypes.byref(p), int(n_chunks)))
 
 
 def workspace_layout(p: Params) -> WsLayout:

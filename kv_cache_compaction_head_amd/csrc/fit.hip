@@ -80,12 +80,12 @@ __global__ __launch_bounds__(256) void k_ps(const In* __restrict__ Q, const In* 
                                             const int32_t* __restrict__ idx,
                                             const double* __restrict__ lse,
                                             double* __restrict__ PS, int n, int T, int t,
-                                            int tiles_a) {
+                                            int tiles_a, int qg) {
   __shared__ double sA[kKC * kTile], sB[kKC * kTile];
   const int b = blockIdx.y, ti = blockIdx.x / tiles_a, ta = blockIdx.x % tiles_a;
   const int i0 = ti * kTile, a0 = ta * kTile;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const In* Qb = Q + static_cast<size_t>(b) * n * D;
+  const In* Qb = Q + static_cast<size_t>(b / qg) * n * D;
   const In* Kb = K + static_cast<size_t>(b) * T * D;
   const int32_t* ib = idx + static_cast<size_t>(b) * t;
   f64x4 acc[2][2] = {};
@@ -1456,7 +1456,7 @@ template <class In, int D>
 hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const double* lse,
                       const float* O, const int32_t* idx, FitBufs fb, float* out_bias,
                       float* out_V, int32_t* status, int B, int n, int T, int t, double ridge,
-                      int max_iters, hipStream_t st) {
+                      int max_iters, int qg, hipStream_t st) {
   const In* Q = static_cast<const In*>(Qv);
   const In* K = static_cast<const In*>(Kv);
   const In* V = static_cast<const In*>(Vv);
@@ -1468,7 +1468,7 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
   // P_S, M = P_S^T P_S (into the bias system's variable block), column sums
   prof_mark(3, false, st);
   hipLaunchKernelGGL((k_ps<In, D>), dim3(tn * tt, B), dim3(256), 0, st, Q, K, idx, lse, fb.PS, n,
-                     T, t, tt);
+                     T, t, tt, qg);
   prof_mark(3, true, st);
   prof_mark(4, false, st);
   launch_atb<double, true>(fb.PS, sPS, t, nullptr, 0, fb.PS, sPS, t,
@@ -1537,7 +1537,8 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
 #define KVC_INST_FIT(In, D)                                                                   \
   template hipError_t launch_fit<In, D>(const void*, const void*, const void*, const double*, \
                                         const float*, const int32_t*, FitBufs, float*, float*, \
-                                        int32_t*, int, int, int, int, double, int, hipStream_t);
+                                        int32_t*, int, int, int, int, double, int, int,      \
+                                        hipStream_t);
 KVC_INST_FIT(bf16_t, 128)
 KVC_INST_FIT(bf16_t, 64)
 KVC_INST_FIT(float, 128)

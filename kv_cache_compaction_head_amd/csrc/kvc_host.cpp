@@ -176,27 +176,29 @@ kvc::FitBufs fit_bufs(void* ws, const Layout& L) {
   return fb;
 }
 
+// qg: batch entries per reference-query set.  Entry b reads Q_ref[b / qg]
+// (chunked compaction runs every chunk of a head against that head's queries).
 template <class In, int D>
 hipError_t run_score(const kvc_params_t* p, const void* Q, const void* K, const void* V,
-                     void* ws, const Layout& L, hipStream_t st) {
+                     void* ws, const Layout& L, int qg, hipStream_t st) {
   const Plan pl = make_plan(p);
   return kvc::launch_score<In, D>(Q, K, V, at<double2>(ws, L.ml), at<double>(ws, L.lse),
                                   at<float>(ws, L.Opart), at<float>(ws, L.O),
                                   at<float>(ws, L.imp_part), at<float>(ws, L.imp),
                                   static_cast<int>(p->B), static_cast<int>(p->n),
                                   static_cast<int>(p->T), pl.nsplit1, pl.kps1, pl.nsplit2,
-                                  pl.kps2, p->agg == KVC_AGG_RMS, st);
+                                  pl.kps2, p->agg == KVC_AGG_RMS, qg, st);
 }
 
 template <class In, int D>
 hipError_t run_fit(const kvc_params_t* p, const void* Q, const void* K, const void* V,
                    const int32_t* idx, float* out_bias, float* out_V, int32_t* status, void* ws,
-                   const Layout& L, hipStream_t st) {
+                   const Layout& L, int qg, hipStream_t st) {
   return kvc::launch_fit<In, D>(Q, K, V, at<double>(ws, L.lse), at<float>(ws, L.O), idx,
                                 fit_bufs(ws, L), out_bias, out_V, status,
                                 static_cast<int>(p->B), static_cast<int>(p->n),
                                 static_cast<int>(p->T), static_cast<int>(p->t), p->ridge_rel,
-                                p->max_nnls_iters, st);
+                                p->max_nnls_iters, qg, st);
 }
 
 // Dispatch on (dtype, head dim).
@@ -213,16 +215,16 @@ hipError_t dispatch(const kvc_params_t* p, A... args) {
 template <class In, int D>
 struct ScoreOp {
   static hipError_t run(const kvc_params_t* p, const void* Q, const void* K, const void* V,
-                        void* ws, const Layout* L, hipStream_t st) {
-    return run_score<In, D>(p, Q, K, V, ws, *L, st);
+                        void* ws, const Layout* L, int qg, hipStream_t st) {
+    return run_score<In, D>(p, Q, K, V, ws, *L, qg, st);
   }
 };
 template <class In, int D>
 struct FitOp {
   static hipError_t run(const kvc_params_t* p, const void* Q, const void* K, const void* V,
                         const int32_t* idx, float* ob, float* ov, int32_t* status, void* ws,
-                        const Layout* L, hipStream_t st) {
-    return run_fit<In, D>(p, Q, K, V, idx, ob, ov, status, ws, *L, st);
+                        const Layout* L, int qg, hipStream_t st) {
+    return run_fit<In, D>(p, Q, K, V, idx, ob, ov, status, ws, *L, qg, st);
   }
 };
 
@@ -234,6 +236,44 @@ int common_checks(const kvc_params_t* p, const void* Q, const void* K, const voi
     return KVC_EINVAL;
   if (ws_bytes < make_layout(p).total) return KVC_EWORKSPACE;
   return KVC_OK;
+}
+
+// Chunked compaction as a batch: entry b' = head * C + chunk is the chunk's
+// T / C contiguous keys (a view of the head's K and V, no copy) with the same
+// per-entry budget t.  False when the split is not representable.
+bool chunk_params(const kvc_params_t* p, int64_t C, kvc_params_t* out) {
+  if (!p || C < 1 || C > kMaxB) return false;
+  if (p->T < 1 || p->T % C != 0) return false;
+  *out = *p;
+  out->B = p->B * C;
+  out->T = p->T / C;
+  return params_ok(out) && p->B >= 1;
+}
+
+// Select, gather and fit for every batch entry of p; qg as in run_score.
+int compact_impl(const kvc_params_t* p, int qg, const void* Q_ref, const void* K, const void* V,
+                 void* out_K, float* out_bias, float* out_V, int32_t* out_idx,
+                 int32_t* out_status, void* workspace, hipStream_t stream) {
+  const Layout L = make_layout(p);
+  int32_t* idx = out_idx ? out_idx : at<int32_t>(workspace, L.idx);
+  int32_t* status = out_status ? out_status : at<int32_t>(workspace, L.status);
+  const int B = static_cast<int>(p->B), T = static_cast<int>(p->T), t = static_cast<int>(p->t);
+  const int es = p->in_dtype == KVC_BF16 ? 2 : 4;
+  kvc::prof_mark(KVC_STAGE_TOTAL, false, stream);
+  hipError_t e = kvc::launch_fill_i32(status, 0, p->B, stream);
+  if (e == hipSuccess) e = dispatch<ScoreOp>(p, Q_ref, K, V, workspace, &L, qg, stream);
+  kvc::prof_mark(KVC_STAGE_SELECT, false, stream);
+  if (e == hipSuccess) e = kvc::launch_select(at<float>(workspace, L.imp), idx, status, B, T, t, stream);
+  if (e == hipSuccess)
+    e = kvc::launch_gather(K, idx, out_K, B, T, t, static_cast<int>(p->d) * es, stream);
+  kvc::prof_mark(KVC_STAGE_SELECT, true, stream);
+  if (e == hipSuccess)
+    e = dispatch<FitOp>(p, Q_ref, K, V, static_cast<const int32_t*>(idx), out_bias, out_V,
+                        status, workspace, &L, qg, stream);
+  if (e == hipSuccess && qg > 1 && out_idx)
+    e = kvc::launch_idx_offset(out_idx, B, t, qg, T, stream);
+  kvc::prof_mark(KVC_STAGE_TOTAL, true, stream);
+  return e == hipSuccess ? KVC_OK : KVC_EHIP;
 }
 
 }  // namespace
@@ -274,24 +314,28 @@ int kvc_compact(const kvc_params_t* p, const void* Q_ref, const void* K, const v
   if (rc) return rc;
   if (!aligned(out_K) || (out_idx && !aligned(out_idx)) || (out_status && !aligned(out_status)))
     return KVC_EINVAL;
-  const Layout L = make_layout(p);
-  int32_t* idx = out_idx ? out_idx : at<int32_t>(workspace, L.idx);
-  int32_t* status = out_status ? out_status : at<int32_t>(workspace, L.status);
-  const int B = static_cast<int>(p->B), T = static_cast<int>(p->T), t = static_cast<int>(p->t);
-  const int es = p->in_dtype == KVC_BF16 ? 2 : 4;
-  kvc::prof_mark(KVC_STAGE_TOTAL, false, stream);
-  hipError_t e = kvc::launch_fill_i32(status, 0, p->B, stream);
-  if (e == hipSuccess) e = dispatch<ScoreOp>(p, Q_ref, K, V, workspace, &L, stream);
-  kvc::prof_mark(KVC_STAGE_SELECT, false, stream);
-  if (e == hipSuccess) e = kvc::launch_select(at<float>(workspace, L.imp), idx, status, B, T, t, stream);
-  if (e == hipSuccess)
-    e = kvc::launch_gather(K, idx, out_K, B, T, t, static_cast<int>(p->d) * es, stream);
-  kvc::prof_mark(KVC_STAGE_SELECT, true, stream);
-  if (e == hipSuccess)
-    e = dispatch<FitOp>(p, Q_ref, K, V, static_cast<const int32_t*>(idx), out_bias, out_V,
-                        status, workspace, &L, stream);
-  kvc::prof_mark(KVC_STAGE_TOTAL, true, stream);
-  return e == hipSuccess ? KVC_OK : KVC_EHIP;
+  return compact_impl(p, 1, Q_ref, K, V, out_K, out_bias, out_V, out_idx, out_status, workspace,
+                      stream);
+}
+
+size_t kvc_workspace_bytes_chunked(const kvc_params_t* p, int64_t n_chunks) {
+  kvc_params_t pc;
+  if (!chunk_params(p, n_chunks, &pc)) return 0;
+  return make_layout(&pc).total;
+}
+
+int kvc_compact_chunked(const kvc_params_t* p, int64_t n_chunks, const void* Q_ref,
+                        const void* K, const void* V, void* out_K, float* out_bias, float* out_V,
+                        int32_t* out_idx, int32_t* out_status, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  kvc_params_t pc;
+  if (!chunk_params(p, n_chunks, &pc)) return KVC_EINVAL;
+  int rc = common_checks(&pc, Q_ref, K, V, out_bias, out_V, workspace, workspace_bytes);
+  if (rc) return rc;
+  if (!aligned(out_K) || (out_idx && !aligned(out_idx)) || (out_status && !aligned(out_status)))
+    return KVC_EINVAL;
+  return compact_impl(&pc, static_cast<int>(n_chunks), Q_ref, K, V, out_K, out_bias, out_V,
+                      out_idx, out_status, workspace, stream);
 }
 
 int kvc_fit(const kvc_params_t* p, const void* Q_ref, const void* K, const void* V,
@@ -304,9 +348,9 @@ int kvc_fit(const kvc_params_t* p, const void* Q_ref, const void* K, const void*
   int32_t* status = out_status ? out_status : at<int32_t>(workspace, L.status);
   kvc::prof_mark(KVC_STAGE_TOTAL, false, stream);
   hipError_t e = kvc::launch_fill_i32(status, 0, p->B, stream);
-  if (e == hipSuccess) e = dispatch<ScoreOp>(p, Q_ref, K, V, workspace, &L, stream);
+  if (e == hipSuccess) e = dispatch<ScoreOp>(p, Q_ref, K, V, workspace, &L, 1, stream);
   if (e == hipSuccess)
-    e = dispatch<FitOp>(p, Q_ref, K, V, idx, out_bias, out_V, status, workspace, &L, stream);
+    e = dispatch<FitOp>(p, Q_ref, K, V, idx, out_bias, out_V, status, workspace, &L, 1, stream);
   kvc::prof_mark(KVC_STAGE_TOTAL, true, stream);
   return e == hipSuccess ? KVC_OK : KVC_EHIP;
 }

@@ -10,7 +10,8 @@ using bf16_t = uint16_t;
 template <class In, int D>
 hipError_t launch_score(const void* Q, const void* K, const void* V, double2* ml, double* lse,
                         float* Opart, float* O, float* imp_part, float* imp, int B, int n, int T,
-                        int nsplit1, int kps1, int nsplit2, int kps2, bool rms, hipStream_t st);
+                        int nsplit1, int kps1, int nsplit2, int kps2, bool rms, int qg,
+                        hipStream_t st);
 hipError_t launch_select(const float* imp, int32_t* idx, int32_t* status, int B, int T, int t,
                          hipStream_t st);
 hipError_t launch_gather(const void* K, const int32_t* idx, void* outK, int B, int T, int t,
@@ -41,7 +42,9 @@ template <class In, int D>
 hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const double* lse,
                       const float* O, const int32_t* idx, FitBufs fb, float* out_bias,
                       float* out_V, int32_t* status, int B, int n, int T, int t, double ridge,
-                      int max_iters, hipStream_t st);
+                      int max_iters, int qg, hipStream_t st);
+// kept indices of (head, chunk) b' made global: idx[b'][a] += (b' mod C) * Tc
+hipError_t launch_idx_offset(int32_t* idx, int Bc, int t, int C, int Tc, hipStream_t st);
 // Event-pair instrumentation (defined with the C ABI): no-op unless enabled.
 void prof_mark(int stage, bool end, hipStream_t st);
 }  // namespace kvc

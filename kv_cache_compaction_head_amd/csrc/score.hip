@@ -105,7 +105,8 @@ template <class In, int D>
 __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
                                                    const In* __restrict__ K,
                                                    double2* __restrict__ ml, int n, int T,
-                                                   int keys_per_split, int nqb, int nsplit, int B) {
+                                                   int keys_per_split, int nqb, int nsplit, int B,
+                                                   int qg) {
   constexpr int KS = Frag<In>::KS, NK = D / KS, BN = 64, LD = D + 16 / sizeof(In);
   constexpr int VEC = 16 / sizeof(In), CPR = D / VEC, NCH = BN * CPR / 256;
   __shared__ __align__(16) In sK[2][BN * LD];
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
   if (!score_grid(nqb, nsplit, B, qb, split, b)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5;
   const int q = qb * kBM + wave * 32 + (lane & 31);
-  const In* Qb = Q + static_cast<size_t>(b) * n * D;
+  const In* Qb = Q + static_cast<size_t>(b / qg) * n * D;
   const In* Kb = K + static_cast<size_t>(b) * T * D;
 
   typename Frag<In>::T bq[NK];
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
                                                    float* __restrict__ Opart,
                                                    float* __restrict__ imp_part, int n, int T,
                                                    int keys_per_split, int nqb, int nsplit,
-                                                   int B) {
+                                                   int B, int qg) {
   constexpr int KS = Frag<In>::KS, NK = D / KS, BN = 64;
   constexpr int LD = D + 16 / sizeof(In);
   constexpr int LDV = BN + 16 / sizeof(In);
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
   if (!score_grid(nqb, nsplit, B, qb, split, b)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5;
   const int q = qb * kBM + wave * 32 + (lane & 31);
-  const In* Qb = Q + static_cast<size_t>(b) * n * D;
+  const In* Qb = Q + static_cast<size_t>(b / qg) * n * D;
   const In* Kb = K + static_cast<size_t>(b) * T * D;
   const In* Vb = V + static_cast<size_t>(b) * T * D;
 
@@ -465,7 +466,7 @@ __global__ void k_imp_reduce(const float* __restrict__ part, float* __restrict__
 template <class In, int D>
 hipError_t launch_score(const void* Q, const void* K, const void* V, double2* ml, double* lse,
                         float* Opart, float* O, float* imp_part, float* imp, int B, int n, int T,
-                        int nsplit1, int kps1, int nsplit2, int kps2, bool rms,
+                        int nsplit1, int kps1, int nsplit2, int kps2, bool rms, int qg,
                         hipStream_t st) {
   const int nqb = (n + kBM - 1) / kBM;
   const In* q = static_cast<const In*>(Q);
@@ -473,7 +474,7 @@ hipError_t launch_score(const void* Q, const void* K, const void* V, double2* ml
   const In* v = static_cast<const In*>(V);
   prof_mark(0, false, st);
   hipLaunchKernelGGL((k_score_lse<In, D>), dim3(score_grid_size(nqb, nsplit1, B)), dim3(256), 0,
-                     st, q, k, ml, n, T, kps1, nqb, nsplit1, B);
+                     st, q, k, ml, n, T, kps1, nqb, nsplit1, B, qg);
   prof_mark(0, true, st);
   hipLaunchKernelGGL(k_lse_merge, dim3((B * n + 255) / 256), dim3(256), 0, st, ml, lse, n,
                      nsplit1, B);
@@ -481,11 +482,11 @@ hipError_t launch_score(const void* Q, const void* K, const void* V, double2* ml
   if (rms)
     hipLaunchKernelGGL((k_expweight<In, D, true>), dim3(score_grid_size(nqb, nsplit2, B)),
                        dim3(256), 0, st, q, k, v, lse, Opart, imp_part, n, T, kps2, nqb, nsplit2,
-                       B);
+                       B, qg);
   else
     hipLaunchKernelGGL((k_expweight<In, D, false>), dim3(score_grid_size(nqb, nsplit2, B)),
                        dim3(256), 0, st, q, k, v, lse, Opart, imp_part, n, T, kps2, nqb, nsplit2,
-                       B);
+                       B, qg);
   prof_mark(1, true, st);
   hipLaunchKernelGGL(k_o_reduce, dim3((n + 31) / 32, D / 32, B), dim3(32, 8), 0, st, Opart, O, n,
                      D, nsplit2);
@@ -497,15 +498,15 @@ hipError_t launch_score(const void* Q, const void* K, const void* V, double2* ml
 
 template hipError_t launch_score<bf16_t, 128>(const void*, const void*, const void*, double2*,
                                               double*, float*, float*, float*, float*, int, int,
-                                              int, int, int, int, int, bool, hipStream_t);
+                                              int, int, int, int, int, bool, int, hipStream_t);
 template hipError_t launch_score<bf16_t, 64>(const void*, const void*, const void*, double2*,
                                              double*, float*, float*, float*, float*, int, int,
-                                             int, int, int, int, int, bool, hipStream_t);
+                                             int, int, int, int, int, bool, int, hipStream_t);
 template hipError_t launch_score<float, 128>(const void*, const void*, const void*, double2*,
                                              double*, float*, float*, float*, float*, int, int,
-                                             int, int, int, int, int, bool, hipStream_t);
+                                             int, int, int, int, int, bool, int, hipStream_t);
 template hipError_t launch_score<float, 64>(const void*, const void*, const void*, double2*,
                                             double*, float*, float*, float*, float*, int, int,
-                                            int, int, int, int, int, bool, hipStream_t);
+                                            int, int, int, int, int, bool, int, hipStream_t);
 
 }  // namespace kvc

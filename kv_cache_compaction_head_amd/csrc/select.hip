@@ -164,4 +164,19 @@ hipError_t launch_gather(const void* K, const int32_t* idx, void* outK, int B, i
   return hipGetLastError();
 }
 
+// Chunked compaction: batch entry b' = head * C + chunk holds the chunk's
+// kept indices relative to the chunk; make them positions in the head's cache.
+__global__ void k_idx_offset(int32_t* __restrict__ idx, int Bc, int t, int C, int Tc) {
+  const size_t e = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= static_cast<size_t>(Bc) * t) return;
+  const int bc = static_cast<int>(e / t);
+  idx[e] += (bc % C) * Tc;
+}
+
+hipError_t launch_idx_offset(int32_t* idx, int Bc, int t, int C, int Tc, hipStream_t st) {
+  const size_t tot = static_cast<size_t>(Bc) * t;
+  hipLaunchKernelGGL(k_idx_offset, dim3((tot + 255) / 256), dim3(256), 0, st, idx, Bc, t, C, Tc);
+  return hipGetLastError();
+}
+
 }  // namespace kvc

@@ -228,6 +228,32 @@ def compact(Q, K, V, t: int, agg: str = "rms", ridge_rel: float = DEFAULT_RIDGE_
             "lse": lse, "O": O, "imp": imp, **info}
 
 
+def compact_chunked(Q, K, V, t: int, n_chunks: int, agg: str = "rms",
+                    ridge_rel: float = DEFAULT_RIDGE_REL):
+    """Chunked compaction ("Compaction par blocs" paragraph of the same summary):
+    the KV states of one head are cut into n_chunks contiguous chunks of equal
+    length, each chunk is compacted on its own against all reference queries
+    (its own lse, output, importance and fits), and the compact chunks are
+    concatenated in order.  Kept indices are returned as positions in the
+    whole cache.  The merge needs no re-fit: attention over concatenated blocks
+    is the mass-weighted mix of the per-block attentions (main objective,
+    block-concatenation decomposition)."""
+    Q, K, V = (np.asarray(a, dtype=np.float64) for a in (Q, K, V))
+    T = K.shape[0]
+    if n_chunks < 1 or T % n_chunks:
+        raise ValueError("T must be a positive multiple of n_chunks")
+    Tc = T // n_chunks
+    parts = []
+    for c in range(n_chunks):
+        lo = c * Tc
+        r = compact(Q, K[lo:lo + Tc], V[lo:lo + Tc], t, agg, ridge_rel)
+        r["idx"] = r["idx"] + lo
+        parts.append(r)
+    out = {k: np.concatenate([r[k] for r in parts]) for k in ("idx", "Ck", "beta", "w", "Cv")}
+    out["chunks"] = parts
+    return out
+
+
 def attend(Q, K, V, bias=None):
     """softmax(Q K^T + bias) V in float64 (the consumer's attention)."""
     s = np.asarray(Q, float) @ np.asarray(K, float).T

@@ -2,6 +2,8 @@
 the same seeded inputs.  Bars: kept indices identical up to near-ties below
 1e-6 relative importance gap; multipliers w, fitted values and the compacted
 attention output within 2e-3 relative L2 for bf16 inputs, 1e-4 for float32."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -112,7 +114,7 @@ def test_nonfinite_input_is_flagged():
     assert gpu["status"][1] & 4
 
 
-@pytest.mark.parametrize("cfg,heads", [(2, [0, 7]), (3, [0, 5]), (4, [0, 131, 255])])
+@pytest.mark.parametrize("cfg,heads", [(2, [0, 7]), (3, [0, 5]), (4, [0, 131, 255]), (5, [3])])
 def test_full_configs_sampled_heads(cfg, heads):
     """The full-size workloads, launched exactly as the benchmark times them;
     the oracle checks a sample of heads."""
@@ -124,3 +126,92 @@ def test_full_configs_sampled_heads(cfg, heads):
         err = compare_head(gpu, h, data, w.t, _tol(w), tight=False)
         print(f"C{cfg} head {h}:", {k: (float(f"{v:.3g}") if isinstance(v, float) else v)
                                     for k, v in err.items()}, flush=True)
+
+
+def _chunk_view(w, data, gpu_res, C):
+    """Recast a chunked result as B*C independent heads (entry h*C + c is chunk c
+    of head h, with chunk-local indices) so each entry compares against the
+    oracle's compaction of that chunk alone."""
+    import kv_cache_compaction_head_amd as kvc
+    B, T, t = w.B, w.T, w.t
+    Tc = T // C
+    cd = {"Q": np.repeat(data["Q"], C, axis=0),
+          "K": data["K"].reshape(B * C, Tc, -1), "V": data["V"].reshape(B * C, Tc, -1)}
+    idx = gpu_res.idx.cpu().numpy().astype(np.int64).reshape(B, C, t)
+    off = (np.arange(C) * Tc)[None, :, None]
+    assert np.all((idx >= off) & (idx < off + Tc)), "kept index outside its chunk"
+    inter = {k: v.cpu().numpy() for k, v in kvc.intermediates(gpu_res).items()}
+    g = {"keys": gpu_res.keys.cpu().reshape(B * C, t, -1),
+         "bias": gpu_res.bias.cpu().numpy().astype(np.float64).reshape(B * C, t),
+         "values": gpu_res.values.cpu().numpy().astype(np.float64).reshape(B * C, t, -1),
+         "idx": (idx - off).reshape(B * C, t),
+         "status": gpu_res.status.cpu().numpy().reshape(B * C), **inter}
+    return cd, g
+
+
+@pytest.mark.parametrize("w,C", [
+    (synth.custom(12, 2, 3000, 200, 128, 77, "bf16", "clusters"), 3),
+    (synth.custom(13, 1, 2048, 96, 64, 40, "f32", "sinks"), 4),
+], ids=["bf16_C3", "f32_d64_C4"])
+def test_chunked_matches_oracle_per_chunk(w, C):
+    import torch
+    import kv_cache_compaction_head_amd as kvc
+    data = synth.batch(w)
+    Q, K, V = (to_device(data[k]) for k in ("Q", "K", "V"))
+    res = kvc.compact_chunked(Q, K, V, w.t, C)
+    torch.cuda.synchronize()
+    assert res.idx.shape == (w.B, C * w.t) and res.status.shape == (w.B, C)
+    cd, g = _chunk_view(w, data, res, C)
+    for e in range(w.B * C):
+        err = compare_head(g, e, cd, w.t, _tol(w))
+        print(w.name, "head", e // C, "chunk", e % C,
+              {k: (float(f"{v:.3g}") if isinstance(v, float) else v) for k, v in err.items()},
+              flush=True)
+    # the merged cache, read as one head, against the oracle's merged cache
+    for h in range(w.B):
+        Qh, Kh, Vh = (synth.to_f64(data[k][h]) for k in ("Q", "K", "V"))
+        ref = orc.compact_chunked(Qh, Kh, Vh, w.t, C)
+        o_gpu = orc.attend(Qh, res.keys[h].float().cpu().numpy().astype(np.float64),
+                           res.values[h].cpu().numpy().astype(np.float64),
+                           res.bias[h].cpu().numpy().astype(np.float64))
+        o_ref = orc.attend(Qh, ref["Ck"], ref["Cv"], ref["beta"])
+        assert orc.rel_l2(o_gpu, o_ref) <= _tol(w)
+
+
+def test_chunked_one_chunk_is_bitwise_compact():
+    import torch
+    import kv_cache_compaction_head_amd as kvc
+    w = synth.custom(14, 2, 1200, 128, 128, 60, "bf16", "clusters")
+    data = synth.batch(w)
+    Q, K, V = (to_device(data[k]) for k in ("Q", "K", "V"))
+    a = kvc.compact(Q, K, V, w.t)
+    b = kvc.compact_chunked(Q, K, V, w.t, 1)
+    torch.cuda.synchronize()
+    for k in ("keys", "bias", "values", "idx"):
+        assert torch.equal(getattr(a, k), getattr(b, k)), k
+    assert torch.equal(a.status, b.status.view(-1))
+    with pytest.raises(ValueError):
+        kvc.compact_chunked(Q, K, V, w.t, 7)      # 1200 % 7 != 0
+    with pytest.raises(ValueError):
+        kvc.compact_chunked(Q, K, V, 601, 2)      # t > T / C
+
+
+def test_chunked_long_context_sampled():
+    """131072 keys per head in 4 chunks of 32768 (each kept at 50x), the
+    long-context shape the chunking is for; a sample of (head, chunk) entries
+    against the oracle."""
+    import torch
+    import kv_cache_compaction_head_amd as kvc
+    w0 = synth.CONFIGS[5]
+    C = 4
+    w = dataclasses.replace(w0, t=w0.t // C)
+    data = synth.batch(w)
+    Q, K, V = (to_device(data[k]) for k in ("Q", "K", "V"))
+    res = kvc.compact_chunked(Q, K, V, w.t, C)
+    torch.cuda.synchronize()
+    assert (res.status.cpu().numpy() == 0).all()
+    cd, g = _chunk_view(w, data, res, C)
+    for e in (3 * C + 0, 3 * C + 3, 6 * C + 1):
+        err = compare_head(g, e, cd, w.t, _tol(w), tight=False)
+        print("C5/4 entry", e, {k: (float(f"{v:.3g}") if isinstance(v, float) else v)
+                                for k, v in err.items()}, flush=True)

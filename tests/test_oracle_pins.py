@@ -374,3 +374,75 @@ def test_workload_shapes_and_determinism():
     assert a["K"].shape == (2, 512, 128) and a["K"].dtype == np.uint16
     assert w.T // w.t == 50
     assert synth.CONFIGS[4].B == 256 and synth.CONFIGS[5].T == 131072
+
+
+# ------------------------------------------------------------ chunked (f1)
+def test_chunked_one_chunk_is_compact():
+    w = synth.custom(9, 1, 256, 24, 16, 20, "f32", "normal")
+    a = synth.head(w, 0)
+    Q, K, V = (synth.to_f64(a[k]) for k in ("Q", "K", "V"))
+    r1, rc = orc.compact(Q, K, V, 20), orc.compact_chunked(Q, K, V, 20, 1)
+    for k in ("idx", "beta", "w", "Cv"):
+        assert np.array_equal(r1[k], rc[k])
+
+
+def test_chunked_chunks_partition_the_cache():
+    """The chunks' own log-sum-exps combine to the whole cache's (the chunks
+    are disjoint and cover every key), and every kept index lies in its own
+    chunk's range, ascending overall."""
+    Q, K, V = _rand(60, 7, 8, scale=0.5), _rand(61, 96, 8), _rand(62, 96, 4)
+    r = orc.compact_chunked(Q, K, V, 5, 4)
+    lses = np.stack([c["lse"] for c in r["chunks"]])
+    assert np.allclose(np.logaddexp.reduce(lses, axis=0), orc.row_lse(Q, K), atol=1e-13)
+    idx = r["idx"]
+    assert idx.shape == (20,) and np.all(np.diff(idx) > 0)
+    assert np.array_equal(idx // 24, np.repeat(np.arange(4), 5))
+    assert np.array_equal(r["Ck"], K[idx])
+
+
+@pytest.mark.parametrize("C", [2, 3, 6])
+def test_chunked_keep_everything_reproduces_full_attention(C):
+    """t = T / C keeps every key of every chunk with w = 1 and C_v = V, so the
+    merged cache is the original one and attention on fresh queries is
+    unchanged (no re-fit after the merge)."""
+    T, d = 36, 6
+    Q, K, V = _rand(63, 30, d, scale=0.4), _rand(64, T, d), _rand(65, T, 3)
+    r = orc.compact_chunked(Q, K, V, T // C, C)
+    assert list(r["idx"]) == list(range(T))
+    assert np.allclose(r["beta"], 0.0, atol=1e-9)
+    assert np.allclose(r["Cv"], V, atol=1e-8)
+    Qn = _rand(66, 11, d, scale=0.4)
+    assert np.allclose(orc.attend(Qn, r["Ck"], r["Cv"], r["beta"]), orc.attend(Qn, K, V),
+                       atol=1e-8)
+
+
+def test_chunked_merge_is_mass_weighted_mix_of_chunks():
+    """Attention over the merged compact cache = the per-chunk compact
+    attentions mixed by their compact masses (block decomposition applied to
+    the compacted blocks), and each chunk's bias brings its compact mass on the
+    reference queries closer to that chunk's own mass than plain eviction
+    (w = 1 is feasible for the chunk's NNLS)."""
+    Q, K, V = _rand(67, 40, 8, scale=0.5), _rand(68, 120, 8), _rand(69, 120, 3)
+    r = orc.compact_chunked(Q, K, V, 10, 3)
+    Qn = _rand(70, 9, 8, scale=0.5)
+    num, den = 0.0, 0.0
+    for c in r["chunks"]:
+        s = Qn @ c["Ck"].T + c["beta"][None, :]
+        z = np.exp(s).sum(axis=1)[:, None]
+        num = num + z * orc.attend(Qn, c["Ck"], c["Cv"], c["beta"])
+        den = den + z
+    assert np.allclose(orc.attend(Qn, r["Ck"], r["Cv"], r["beta"]), num / den, atol=1e-13)
+    for j, c in enumerate(r["chunks"]):
+        Kc = K[j * 40:(j + 1) * 40]
+        m_true = np.exp(orc.row_lse(Q, Kc))
+        m_comp = np.exp(Q @ c["Ck"].T + c["beta"][None, :]).sum(axis=1)
+        m_evict = np.exp(Q @ c["Ck"].T).sum(axis=1)
+        e_am = np.sum((m_comp / m_true - 1) ** 2)
+        assert e_am < 0.5 * np.sum((m_evict / m_true - 1) ** 2)
+
+
+def test_chunked_argument_checks():
+    with pytest.raises(ValueError):
+        orc.compact_chunked(np.zeros((2, 3)), np.zeros((10, 3)), np.zeros((10, 3)), 2, 3)
+    with pytest.raises(ValueError):
+        orc.compact_chunked(np.zeros((2, 3)), np.zeros((10, 3)), np.zeros((10, 3)), 6, 2)

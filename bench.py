@@ -15,7 +15,9 @@ attention's relative L2 error on held-out queries.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -29,6 +31,8 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3      # MI355X fp32 MFMA
 PEAK_F64_TFLOPS = 78.6       # MI355X fp64 (vector and matrix)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_nnls_sweep_T32k_50x_hbm_traffic.md")
+FIT_SRC = os.path.join(ROOT, "kv_cache_compaction_head_amd", "csrc", "fit.hip")
 
 
 def parse():
@@ -62,6 +66,40 @@ def cpu_baseline(w, data, heads):
             "kind": "oracle",
             "sample": f"{heads} of {w.B} heads of {w.name} through the float64 oracle "
                       f"({dt:.1f} s; BLAS threads={cores}, numpy exp single-threaded)"}
+
+
+def copy_probe(torch, nbytes=1 << 30, reps=10):
+    """Device-to-device copy of nbytes (read nbytes + write nbytes), timed with
+    events on torch's stream: the measured HBM rate beside the spec peak, and
+    the known-size kernel the FETCH_SIZE / WRITE_SIZE counters are scaled by."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    b.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return 2.0 * nbytes / (ms * 1e-3) / 1e9
+
+
+def traffic_record():
+    """HBM bytes per launch of the NNLS kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"^traffic_json: (\{.*\})$", text, re.M)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    sha = hashlib.sha256(open(FIT_SRC, "rb").read()).hexdigest()
+    return rec if rec.get("fit_hip_sha256") == sha else None
 
 
 def main():
@@ -107,6 +145,7 @@ def main():
             prof[s] = ms / max(cnt, 1)
         _lib.profile_enable([])
 
+    copy_gbs = copy_probe(torch)
     status = res.status.cpu().numpy()
     # quality on held-out queries (head 0): full vs compacted attention, float64
     import oracle as orc
@@ -126,10 +165,14 @@ def main():
     # algorithmic work per launch of each separately timed kernel:
     #   k_score_lse: S = Q K^T once (2 n T d per head)
     #   k_expweight: S recomputed + P V (4 n T d per head)
-    #   k_nnls_team: the pivoting rounds' factorizations and solves (counted on device)
+    #   k_nnls_sweep: the block sweeps of the pivoting rounds (counted on device:
+    #     k pivots on an order-m system cost k m^2 + 2 m k^2 + k^3)
+    #   value stage: the value sweep's count over the stage (Grams and prep included
+    #     in the time, not in the count)
     work = {"score_lse": ("k_score_lse", 2.0 * n * T * d * B, mm_peak),
             "expweight": ("k_expweight", 4.0 * n * T * d * B, mm_peak),
-            "nnls": ("k_nnls_team", float(fit_flops[0]), PEAK_F64_TFLOPS)}
+            "nnls": ("k_nnls_sweep", float(fit_flops[0]), PEAK_F64_TFLOPS),
+            "value": ("value stage (k_value_sweep)", float(fit_flops[1]), PEAK_F64_TFLOPS)}
     kernels = []
     for stage, (kname, flops, peak) in work.items():
         if stage not in prof:
@@ -140,10 +183,14 @@ def main():
                         "frac": round(ach / peak, 5)})
     roof = None
     if kernels:
-        dom = max(kernels, key=lambda k: k["ms"])
+        dom = max((k for k in kernels if k["kernel"].startswith("k_")), key=lambda k: k["ms"])
+        tr = traffic_record() if (dom["kernel"] == "k_nnls_sweep" and args.config == 3) else None
         roof = {"bound": dom["bound"], "kernel": dom["kernel"], "achieved": dom["achieved"],
-                "peak": dom["peak"], "unit": "TFLOP/s", "frac": dom["frac"], "traffic": None,
-                "kernels": kernels, "stage_ms": {k: round(v, 4) for k, v in prof.items()}}
+                "peak": dom["peak"], "unit": "TFLOP/s", "frac": dom["frac"],
+                "traffic": tr["bytes_per_launch"] if tr else None,
+                "traffic_detail": tr,
+                "kernels": kernels, "stage_ms": {k: round(v, 4) for k, v in prof.items()},
+                "hbm_copy_measured_GBs": round(copy_gbs, 1), "hbm_peak_GBs": PEAK_HBM_GBS}
     out = {
         "metric": "KV tokens compacted/sec (1 GPU) at T=32k, 50x; compacted-attn rel. L2 error",
         "value": B * T / dt,

@@ -60,6 +60,8 @@ extern "C" {
 #define KVC_STATUS_NONFINITE     4  /* a non-finite value reached the fits      */
 #define KVC_STATUS_SYNC_TIMEOUT  8  /* a fit team's barrier wait ran out (the
                                        head's fit is incomplete)               */
+#define KVC_STATUS_BUDGET       16  /* kvc_compact_ragged: the head's budget was
+                                       outside [1, p->t] and was clamped       */
 
 typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype_t;
 typedef enum { KVC_AGG_RMS = 0, KVC_AGG_MEAN = 1 } kvc_agg_t;
@@ -107,6 +109,25 @@ int kvc_compact(const kvc_params_t* p, const void* Q_ref, const void* K, const v
 int kvc_fit(const kvc_params_t* p, const void* Q_ref, const void* K, const void* V,
             const int32_t* idx, float* out_bias, float* out_V, int32_t* out_status,
             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Ragged per-head budgets: head b keeps t_heads[b] keys, 1 <= t_heads[b] <=
+ * p->t, so one call serves a non-uniform head/layer schedule (the per-head
+ * retention ratios of the method's schedule; the per-segment budgets of the
+ * thought-aware variant's budget rule).  Each head is compacted exactly as
+ * kvc_compact would with t = t_heads[b].
+ *   t_heads  [B] int32, DEVICE memory, 4-byte aligned; read on the stream, so
+ *            the values may come from earlier work on it.  A value outside
+ *            [1, p->t] is clamped and flags KVC_STATUS_BUDGET for that head.
+ *   Outputs have kvc_compact's shapes with t = p->t (the largest budget).
+ *   Head b's first t_heads[b] slots hold its compact cache; the remaining
+ *   slots are padding that attention ignores: out_idx = -1, out_K and out_V
+ *   rows of zeros, out_bias = -inf (a zero softmax weight).
+ *   workspace  >= kvc_workspace_bytes(p) bytes.
+ * Returns as kvc_compact. */
+int kvc_compact_ragged(const kvc_params_t* p, const int32_t* t_heads, const void* Q_ref,
+                       const void* K, const void* V, void* out_K, float* out_bias, float* out_V,
+                       int32_t* out_idx, int32_t* out_status, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
 
 /* Chunked compaction ("Compaction par blocs" of the same summary): each head's
  * cache is cut into n_chunks contiguous chunks of T / n_chunks keys, every

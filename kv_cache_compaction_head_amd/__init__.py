@@ -15,7 +15,7 @@ from ._lib import (KVC_AGG_MEAN, KVC_AGG_RMS, KVC_BF16, KVC_F32, STATUS_NNLS_CAP
                    STATUS_NONFINITE, STATUS_NOT_SPD, Params, load, make_params, strerror,
                    workspace_bytes, workspace_bytes_chunked, workspace_layout)
 
-__all__ = ["compact", "compact_chunked", "fit", "Compacted", "intermediates", "load", "make_params",
+__all__ = ["compact", "compact_chunked", "compact_ragged", "fit", "Compacted", "intermediates", "load", "make_params",
            "workspace_bytes", "workspace_bytes_chunked", "workspace_layout", "strerror", "Params"]
 
 
@@ -88,6 +88,37 @@ def compact(Q, K, V, t: int, *, agg: str = "rms", ridge_rel: float = 1e-6,
     rc = load().kvc_compact(ctypes.byref(p), _vp(Q), _vp(K), _vp(V), _vp(keys), _vp(bias),
                             _vp(values), _vp(idx), _vp(status), _vp(ws),
                             ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(stream, dev))
+    _lib.check(rc)
+    return Compacted(keys, bias, values, idx, status, ws, p)
+
+
+def compact_ragged(Q, K, V, t_heads, *, agg: str = "rms", ridge_rel: float = 1e-6,
+                   max_nnls_iters: int = 32, workspace=None, stream=None) -> Compacted:
+    """Compact head b to t_heads[b] keys (a per-head budget).  Outputs are
+    padded to max(t_heads): head b's slots from t_heads[b] on hold idx -1,
+    zero keys and values and bias -inf, which attention ignores."""
+    import torch
+    Q, K, V, _ = _prep(Q, K, V)
+    B, n, d = Q.shape
+    T = K.shape[1]
+    tv = torch.as_tensor(t_heads, dtype=torch.int32)
+    if tv.shape != (B,):
+        raise ValueError(f"t_heads must hold one budget per head ({B})")
+    t = int(tv.max())
+    tv = tv.to(Q.device).contiguous()
+    dt = "bf16" if Q.dtype == torch.bfloat16 else "f32"
+    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters)
+    dev = Q.device
+    ws = _workspace(p, dev, workspace)
+    keys = torch.empty((B, t, d), dtype=Q.dtype, device=dev)
+    bias = torch.empty((B, t), dtype=torch.float32, device=dev)
+    values = torch.empty((B, t, d), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, t), dtype=torch.int32, device=dev)
+    status = torch.empty((B,), dtype=torch.int32, device=dev)
+    rc = load().kvc_compact_ragged(ctypes.byref(p), _vp(tv), _vp(Q), _vp(K), _vp(V), _vp(keys),
+                                   _vp(bias), _vp(values), _vp(idx), _vp(status), _vp(ws),
+                                   ctypes.c_size_t(ws.numel() * ws.element_size()),
+                                   _stream(stream, dev))
     _lib.check(rc)
     return Compacted(keys, bias, values, idx, status, ws, p)
 

@@ -79,7 +79,8 @@ template <class In, int D>
 __global__ __launch_bounds__(256) void k_ps(const In* __restrict__ Q, const In* __restrict__ K,
                                             const int32_t* __restrict__ idx,
                                             const double* __restrict__ lse,
-                                            double* __restrict__ PS, int n, int T, int t,
+                                            double* __restrict__ PS,
+                                            const int32_t* __restrict__ tv, int n, int T, int t,
                                             int tiles_a, int qg) {
   __shared__ double sA[kKC * kTile], sB[kKC * kTile];
   const int b = blockIdx.y, ti = blockIdx.x / tiles_a, ta = blockIdx.x % tiles_a;
@@ -88,6 +89,7 @@ __global__ __launch_bounds__(256) void k_ps(const In* __restrict__ Q, const In* 
   const In* Qb = Q + static_cast<size_t>(b / qg) * n * D;
   const In* Kb = K + static_cast<size_t>(b) * T * D;
   const int32_t* ib = idx + static_cast<size_t>(b) * t;
+  const int tb = tv ? tv[b] : t;  // columns from tb on are zero (unused budget)
   f64x4 acc[2][2] = {};
   for (int c0 = 0; c0 < D; c0 += kKC) {
     __syncthreads();
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(256) void k_ps(const In* __restrict__ Q, const In* 
       const int r = e / kKC, c = e % kKC;  // r: tile row, c: contraction index
       const int i = i0 + r, a = a0 + r;
       sA[c * kTile + r] = i < n ? to_f64<In>(Qb[static_cast<size_t>(i) * D + c0 + c]) : 0.0;
-      sB[c * kTile + r] = a < t ? to_f64<In>(Kb[static_cast<size_t>(ib[a]) * D + c0 + c]) : 0.0;
+      sB[c * kTile + r] = a < tb ? to_f64<In>(Kb[static_cast<size_t>(ib[a]) * D + c0 + c]) : 0.0;
     }
     __syncthreads();
     tile_mma(sA, sB, acc, wave, lane);
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(256) void k_ps(const In* __restrict__ Q, const In* 
         const int r = i0 + tile_row(wave, lane, ra, i), a = a0 + tile_col(wave, lane, rb);
         if (r < n && a < t)
           PS[(static_cast<size_t>(b) * n + r) * t + a] =
-              exp(acc[ra][rb][i] - lse[static_cast<size_t>(b) * n + r]);
+              a < tb ? exp(acc[ra][rb][i] - lse[static_cast<size_t>(b) * n + r]) : 0.0;
       }
 }
 
@@ -317,10 +319,12 @@ __device__ int block_count(int v, int* sh) {
 // clear columns 1..63 (unused right-hand-side slots).  grid (B), block 1024.
 __global__ __launch_bounds__(1024) void k_bias_prep(double* __restrict__ S, size_t sS, int ld,
                                                     const double* __restrict__ colsum,
-                                                    double* __restrict__ lam, int t,
+                                                    double* __restrict__ lam,
+                                                    const int32_t* __restrict__ tv, int t_str,
                                                     double ridge) {
   __shared__ double sh[16];
   const int b = blockIdx.x;
+  const int t = tv ? tv[b] : t_str;
   double* Sb = S + b * sS;
   double tr = 0.0;
   for (int a = threadIdx.x; a < t; a += blockDim.x)
@@ -330,7 +334,7 @@ __global__ __launch_bounds__(1024) void k_bias_prep(double* __restrict__ S, size
   for (int a = threadIdx.x; a < t; a += blockDim.x) {
     double* row = Sb + static_cast<size_t>(kSB + a) * ld;
     row[kSB + a] += lw;
-    row[0] = colsum[static_cast<size_t>(b) * t + a] + lw;
+    row[0] = colsum[static_cast<size_t>(b) * t_str + a] + lw;
     for (int c = 1; c < kSB; ++c) row[c] = 0.0;
   }
   if (threadIdx.x == 0) lam[2 * b] = lw;
@@ -1137,8 +1141,8 @@ __global__ __launch_bounds__(256) void k_nnls_sweep(
     size_t sUV, double* __restrict__ stage, double* __restrict__ wv, int32_t* __restrict__ Fidx,
     int32_t* __restrict__ inv,
     int32_t* __restrict__ msz, int32_t* __restrict__ status, unsigned* __restrict__ bar,
-    int* __restrict__ err, int* __restrict__ xcc, double* __restrict__ flops, int B, int t,
-    int max_iters, int tx) {
+    int* __restrict__ err, int* __restrict__ xcc, double* __restrict__ flops,
+    const int32_t* __restrict__ tv, int B, int t_str, int max_iters, int tx) {
   SweepSmem& sm = g_sw;
   Team tm;
   int team, nteams;
@@ -1147,6 +1151,7 @@ __global__ __launch_bounds__(256) void k_nnls_sweep(
   for (int s = tid; s < kMaxRows; s += kTeamThreads) sm.pos[s] = -1;
   constexpr int NV = kMaxTeamT / kTeamThreads;
   for (int b = team; b < B; b += nteams) {
+    const int t = tv ? tv[b] : t_str;
     const SweepMat M{gptr(S + b * sS), gptr(Ub + b * sUV), gptr(Vb + b * sUV),
                      gptr(stage + static_cast<size_t>(b) * kStage), ld, kSB, 1, t};
     for (int j = tid; j < t; j += kTeamThreads) sm.inF[j] = 0;
@@ -1232,9 +1237,9 @@ __global__ __launch_bounds__(256) void k_nnls_sweep(
       }
     }
     if (tm.rank == 0) {
-      double* w = wv + static_cast<size_t>(b) * t;
-      int32_t* Fb = Fidx + static_cast<size_t>(b) * t;
-      int32_t* ib = inv + static_cast<size_t>(b) * t;
+      double* w = wv + static_cast<size_t>(b) * t_str;
+      int32_t* Fb = Fidx + static_cast<size_t>(b) * t_str;
+      int32_t* ib = inv + static_cast<size_t>(b) * t_str;
       int m = 0, slot;
 #pragma unroll
       for (int q = 0; q < NV; ++q) {
@@ -1253,6 +1258,10 @@ __global__ __launch_bounds__(256) void k_nnls_sweep(
             if (f) Fb[slot] = j;
           }
         }
+      }
+      for (int j = t + tid; j < t_str; j += kTeamThreads) {
+        w[j] = 0.0;
+        ib[j] = -1;
       }
       if (tid == 0) {
         msz[b] = m;
@@ -1336,10 +1345,11 @@ __global__ __launch_bounds__(256) void k_value_prep(double* __restrict__ PS,
 // lam_v = ridge * trace(G) / t; G += lam_v I (G at Gb, order msz, stride ld).
 // grid (B), block 256.
 __global__ void k_ridge_v(double* __restrict__ Gb, size_t sS, int ld,
-                          const int32_t* __restrict__ msz, double* __restrict__ lam, int t,
-                          double ridge) {
+                          const int32_t* __restrict__ msz, double* __restrict__ lam,
+                          const int32_t* __restrict__ tv, int t_str, double ridge) {
   __shared__ double sh[16];
   const int b = blockIdx.x, m = msz[b];
+  const int t = tv ? tv[b] : t_str;
   double* G = Gb + b * sS;
   double tr = 0.0;
   for (int a = threadIdx.x; a < m; a += blockDim.x) tr += G[static_cast<size_t>(a) * ld + a];
@@ -1378,17 +1388,15 @@ __global__ void k_write_out(const double* __restrict__ Cb, size_t sS, int ld,
   const int a = e / D, c = e % D;
   if (a >= t) return;
   const int p = inv[static_cast<size_t>(b) * t + a];
-  float v;
-  if (p >= 0) {
-    v = static_cast<float>(Cb[b * sS + static_cast<size_t>(p) * ld + c]);
-  } else {
-    const int j = idx[static_cast<size_t>(b) * t + a];
-    v = to_f32<In>(V[(static_cast<size_t>(b) * T + j) * D + c]);
-  }
+  const int j = idx[static_cast<size_t>(b) * t + a];  // -1: slot past this head's budget
+  float v = 0.f;
+  if (p >= 0) v = static_cast<float>(Cb[b * sS + static_cast<size_t>(p) * ld + c]);
+  else if (j >= 0) v = to_f32<In>(V[(static_cast<size_t>(b) * T + j) * D + c]);
   out_V[(static_cast<size_t>(b) * t + a) * D + c] = v;
   if (c == 0)
     out_bias[static_cast<size_t>(b) * t + a] =
-        static_cast<float>(log(fmax(wv[static_cast<size_t>(b) * t + a], 1e-30)));
+        j >= 0 ? static_cast<float>(log(fmax(wv[static_cast<size_t>(b) * t + a], 1e-30)))
+               : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -1467,12 +1475,12 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
   const size_t sPS = static_cast<size_t>(n) * t;
   // P_S, M = P_S^T P_S (into the bias system's variable block), column sums
   prof_mark(3, false, st);
-  hipLaunchKernelGGL((k_ps<In, D>), dim3(tn * tt, B), dim3(256), 0, st, Q, K, idx, lse, fb.PS, n,
-                     T, t, tt, qg);
+  hipLaunchKernelGGL((k_ps<In, D>), dim3(tn * tt, B), dim3(256), 0, st, Q, K, idx, lse, fb.PS,
+                     fb.tv, n, T, t, tt, qg);
   prof_mark(3, true, st);
   prof_mark(4, false, st);
   launch_atb<double, true>(fb.PS, sPS, t, nullptr, 0, fb.PS, sPS, t,
-                           fb.S + static_cast<size_t>(kSB) * ld + kSB, sS, ld, n, nullptr, t, t,
+                           fb.S + static_cast<size_t>(kSB) * ld + kSB, sS, ld, n, fb.tv, t, t,
                            fb.part, fb.part_cap, B, st);
   prof_mark(4, true, st);
   const int nslab = (n + 255) / 256;
@@ -1480,8 +1488,8 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
                      t);
   hipLaunchKernelGGL(k_colsum_final, dim3((t + 255) / 256, B), dim3(256), 0, st, fb.colpart,
                      fb.cvec, nslab, t);
-  hipLaunchKernelGGL(k_bias_prep, dim3(B), dim3(1024), 0, st, fb.S, sS, ld, fb.cvec, fb.lam, t,
-                     ridge);
+  hipLaunchKernelGGL(k_bias_prep, dim3(B), dim3(1024), 0, st, fb.S, sS, ld, fb.cvec, fb.lam, fb.tv,
+                     t, ridge);
   // pivoting rounds: one cooperative launch, a team per head
   prof_mark(5, false, st);
   int cap = coop_capacity(reinterpret_cast<const void*>(&k_nnls_sweep));
@@ -1492,10 +1500,11 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
   hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(fb.bar), 0, kBarWords, st);
   if (e != hipSuccess) return e;
   int* err = reinterpret_cast<int*>(fb.bar + kBarWords - 1);
+  const int32_t* tvp = fb.tv;
   {
     void* args[] = {&fb.S,   &sS,      &ld,        &fb.U,   &fb.V,  &sUV,     &fb.stage, &fb.wv,
                     &fb.Fidx, &fb.inv, &fb.msz,    &status, &fb.bar, &err,    &fb.xcc,
-                    &fb.flops, &B,     &t,         &max_iters, &tx};
+                    &fb.flops, &tvp,   &B,        &t,         &max_iters, &tx};
     e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_nnls_sweep), dim3(grid),
                                    dim3(kTeamThreads), args, 0, st);
     if (e != hipSuccess) return e;
@@ -1508,7 +1517,8 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
   double* R0 = fb.S + static_cast<size_t>(rv) * ld;
   launch_atb<double, true>(fb.PS, sPS, t, fb.Fidx, t, fb.PS, sPS, t, G0, sS, ld, n, fb.msz, t, t,
                            fb.part, fb.part_cap, B, st);
-  hipLaunchKernelGGL(k_ridge_v, dim3(B), dim3(256), 0, st, G0, sS, ld, fb.msz, fb.lam, t, ridge);
+  hipLaunchKernelGGL(k_ridge_v, dim3(B), dim3(256), 0, st, G0, sS, ld, fb.msz, fb.lam, fb.tv, t,
+                     ridge);
   launch_atb<float, false>(fb.PS, sPS, t, fb.Fidx, t, O, static_cast<size_t>(n) * D, D, R0, sS, ld,
                            n, fb.msz, t, D, fb.part, fb.part_cap, B, st);
   hipLaunchKernelGGL((k_rhs_ridge<In>), dim3((t * D + 255) / 256, B), dim3(256), 0, st, R0, sS,

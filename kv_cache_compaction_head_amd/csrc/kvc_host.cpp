@@ -77,8 +77,8 @@ Plan make_plan(const kvc_params_t* p) {
 }
 
 struct Layout {
-  size_t ml, lse, Opart, O, imp_part, imp, idx, status, PS, S, U, V, stage, cvec, wv, lam, colpart, Fidx,
-      inv, msz, bar, xcc, flops, part, total;
+  size_t ml, lse, Opart, O, imp_part, imp, idx, status, tv, PS, S, U, V, stage, cvec, wv, lam,
+      colpart, Fidx, inv, msz, bar, xcc, flops, part, total;
   size_t part_cap;
 };
 
@@ -102,6 +102,7 @@ Layout make_layout(const kvc_params_t* p) {
   L.imp = take(B * T * 4);
   L.idx = take(B * t * 4);
   L.status = take(B * 4);
+  L.tv = take(B * 4);
   L.PS = take(B * n * t * 8);
   {
     const size_t ld = static_cast<size_t>(kvc::sweep_ld(static_cast<int>(t), static_cast<int>(d)));
@@ -173,6 +174,7 @@ kvc::FitBufs fit_bufs(void* ws, const Layout& L) {
   fb.Fidx = at<int32_t>(ws, L.Fidx);
   fb.inv = at<int32_t>(ws, L.inv);
   fb.msz = at<int32_t>(ws, L.msz);
+  fb.tv = nullptr;
   return fb;
 }
 
@@ -193,9 +195,11 @@ hipError_t run_score(const kvc_params_t* p, const void* Q, const void* K, const 
 template <class In, int D>
 hipError_t run_fit(const kvc_params_t* p, const void* Q, const void* K, const void* V,
                    const int32_t* idx, float* out_bias, float* out_V, int32_t* status, void* ws,
-                   const Layout& L, int qg, hipStream_t st) {
+                   const Layout& L, int qg, const int32_t* tv, hipStream_t st) {
+  kvc::FitBufs fb = fit_bufs(ws, L);
+  fb.tv = tv;
   return kvc::launch_fit<In, D>(Q, K, V, at<double>(ws, L.lse), at<float>(ws, L.O), idx,
-                                fit_bufs(ws, L), out_bias, out_V, status,
+                                fb, out_bias, out_V, status,
                                 static_cast<int>(p->B), static_cast<int>(p->n),
                                 static_cast<int>(p->T), static_cast<int>(p->t), p->ridge_rel,
                                 p->max_nnls_iters, qg, st);
@@ -223,8 +227,8 @@ template <class In, int D>
 struct FitOp {
   static hipError_t run(const kvc_params_t* p, const void* Q, const void* K, const void* V,
                         const int32_t* idx, float* ob, float* ov, int32_t* status, void* ws,
-                        const Layout* L, int qg, hipStream_t st) {
-    return run_fit<In, D>(p, Q, K, V, idx, ob, ov, status, ws, *L, qg, st);
+                        const Layout* L, int qg, const int32_t* tv, hipStream_t st) {
+    return run_fit<In, D>(p, Q, K, V, idx, ob, ov, status, ws, *L, qg, tv, st);
   }
 };
 
@@ -250,10 +254,11 @@ bool chunk_params(const kvc_params_t* p, int64_t C, kvc_params_t* out) {
   return params_ok(out) && p->B >= 1;
 }
 
-// Select, gather and fit for every batch entry of p; qg as in run_score.
-int compact_impl(const kvc_params_t* p, int qg, const void* Q_ref, const void* K, const void* V,
-                 void* out_K, float* out_bias, float* out_V, int32_t* out_idx,
-                 int32_t* out_status, void* workspace, hipStream_t stream) {
+// Select, gather and fit for every batch entry of p; qg as in run_score;
+// t_in: per-entry budgets (device) or null for p->t everywhere.
+int compact_impl(const kvc_params_t* p, int qg, const int32_t* t_in, const void* Q_ref,
+                 const void* K, const void* V, void* out_K, float* out_bias, float* out_V,
+                 int32_t* out_idx, int32_t* out_status, void* workspace, hipStream_t stream) {
   const Layout L = make_layout(p);
   int32_t* idx = out_idx ? out_idx : at<int32_t>(workspace, L.idx);
   int32_t* status = out_status ? out_status : at<int32_t>(workspace, L.status);
@@ -261,15 +266,21 @@ int compact_impl(const kvc_params_t* p, int qg, const void* Q_ref, const void* K
   const int es = p->in_dtype == KVC_BF16 ? 2 : 4;
   kvc::prof_mark(KVC_STAGE_TOTAL, false, stream);
   hipError_t e = kvc::launch_fill_i32(status, 0, p->B, stream);
+  int32_t* tv = nullptr;
+  if (t_in) {
+    tv = at<int32_t>(workspace, L.tv);
+    if (e == hipSuccess) e = kvc::launch_budgets(t_in, tv, status, B, t, stream);
+  }
   if (e == hipSuccess) e = dispatch<ScoreOp>(p, Q_ref, K, V, workspace, &L, qg, stream);
   kvc::prof_mark(KVC_STAGE_SELECT, false, stream);
-  if (e == hipSuccess) e = kvc::launch_select(at<float>(workspace, L.imp), idx, status, B, T, t, stream);
+  if (e == hipSuccess)
+    e = kvc::launch_select(at<float>(workspace, L.imp), idx, status, tv, B, T, t, stream);
   if (e == hipSuccess)
     e = kvc::launch_gather(K, idx, out_K, B, T, t, static_cast<int>(p->d) * es, stream);
   kvc::prof_mark(KVC_STAGE_SELECT, true, stream);
   if (e == hipSuccess)
     e = dispatch<FitOp>(p, Q_ref, K, V, static_cast<const int32_t*>(idx), out_bias, out_V,
-                        status, workspace, &L, qg, stream);
+                        status, workspace, &L, qg, tv, stream);
   if (e == hipSuccess && qg > 1 && out_idx)
     e = kvc::launch_idx_offset(out_idx, B, t, qg, T, stream);
   kvc::prof_mark(KVC_STAGE_TOTAL, true, stream);
@@ -314,8 +325,21 @@ int kvc_compact(const kvc_params_t* p, const void* Q_ref, const void* K, const v
   if (rc) return rc;
   if (!aligned(out_K) || (out_idx && !aligned(out_idx)) || (out_status && !aligned(out_status)))
     return KVC_EINVAL;
-  return compact_impl(p, 1, Q_ref, K, V, out_K, out_bias, out_V, out_idx, out_status, workspace,
-                      stream);
+  return compact_impl(p, 1, nullptr, Q_ref, K, V, out_K, out_bias, out_V, out_idx, out_status,
+                      workspace, stream);
+}
+
+int kvc_compact_ragged(const kvc_params_t* p, const int32_t* t_heads, const void* Q_ref,
+                       const void* K, const void* V, void* out_K, float* out_bias, float* out_V,
+                       int32_t* out_idx, int32_t* out_status, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  int rc = common_checks(p, Q_ref, K, V, out_bias, out_V, workspace, workspace_bytes);
+  if (rc) return rc;
+  if (!t_heads || (reinterpret_cast<uintptr_t>(t_heads) & 3u) || !aligned(out_K) ||
+      (out_idx && !aligned(out_idx)) || (out_status && !aligned(out_status)))
+    return KVC_EINVAL;
+  return compact_impl(p, 1, t_heads, Q_ref, K, V, out_K, out_bias, out_V, out_idx, out_status,
+                      workspace, stream);
 }
 
 size_t kvc_workspace_bytes_chunked(const kvc_params_t* p, int64_t n_chunks) {
@@ -334,8 +358,8 @@ int kvc_compact_chunked(const kvc_params_t* p, int64_t n_chunks, const void* Q_r
   if (rc) return rc;
   if (!aligned(out_K) || (out_idx && !aligned(out_idx)) || (out_status && !aligned(out_status)))
     return KVC_EINVAL;
-  return compact_impl(&pc, static_cast<int>(n_chunks), Q_ref, K, V, out_K, out_bias, out_V,
-                      out_idx, out_status, workspace, stream);
+  return compact_impl(&pc, static_cast<int>(n_chunks), nullptr, Q_ref, K, V, out_K, out_bias,
+                      out_V, out_idx, out_status, workspace, stream);
 }
 
 int kvc_fit(const kvc_params_t* p, const void* Q_ref, const void* K, const void* V,
@@ -350,7 +374,8 @@ int kvc_fit(const kvc_params_t* p, const void* Q_ref, const void* K, const void*
   hipError_t e = kvc::launch_fill_i32(status, 0, p->B, stream);
   if (e == hipSuccess) e = dispatch<ScoreOp>(p, Q_ref, K, V, workspace, &L, 1, stream);
   if (e == hipSuccess)
-    e = dispatch<FitOp>(p, Q_ref, K, V, idx, out_bias, out_V, status, workspace, &L, 1, stream);
+    e = dispatch<FitOp>(p, Q_ref, K, V, idx, out_bias, out_V, status, workspace, &L, 1,
+                        static_cast<const int32_t*>(nullptr), stream);
   kvc::prof_mark(KVC_STAGE_TOTAL, true, stream);
   return e == hipSuccess ? KVC_OK : KVC_EHIP;
 }

@@ -12,8 +12,12 @@ hipError_t launch_score(const void* Q, const void* K, const void* V, double2* ml
                         float* Opart, float* O, float* imp_part, float* imp, int B, int n, int T,
                         int nsplit1, int kps1, int nsplit2, int kps2, bool rms, int qg,
                         hipStream_t st);
-hipError_t launch_select(const float* imp, int32_t* idx, int32_t* status, int B, int T, int t,
-                         hipStream_t st);
+// tv: per-head budgets (device, each in [1, t]) or null for t everywhere
+hipError_t launch_select(const float* imp, int32_t* idx, int32_t* status, const int32_t* tv,
+                         int B, int T, int t, hipStream_t st);
+// tv[b] = tin[b] clamped to [1, t]; status[b] |= 16 where clamped
+hipError_t launch_budgets(const int32_t* tin, int32_t* tv, int32_t* status, int B, int t,
+                          hipStream_t st);
 hipError_t launch_gather(const void* K, const int32_t* idx, void* outK, int B, int T, int t,
                          int row_bytes, hipStream_t st);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t count, hipStream_t st);
@@ -26,6 +30,7 @@ struct FitBufs {
   double* V;  // [B][ld][64] the same times the inverse pivot block
   double* stage;  // [B][kSweepStage] inverse of the next pivot block (lookahead)
   int32_t *Fidx, *inv, *msz;
+  const int32_t* tv;  // [B] per-head budgets (<= t), or null: t for every head
   unsigned* bar;  // kBarWords words: team barrier counters, the last one the timeout flag
   int32_t* xcc;   // kMaxTeamGrid words: each team workgroup's XCC id
   double* flops;    // [B][2] fp64 work of the NNLS sweeps and of the value sweeps

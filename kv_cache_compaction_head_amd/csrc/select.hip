@@ -48,11 +48,13 @@ __device__ int block_exclusive_scan(int v, int* scratch, int* total) {
   return before;
 }
 
-// grid (B), block kSelThreads.  imp [B][T] (non-negative floats), idx [B][t].
+// grid (B), block kSelThreads.  imp [B][T] (non-negative floats), idx [B][t]:
+// the tb = tv[b] (or t) kept indices ascending, then -1 in the remaining slots.
 // status[b] |= 4 if an importance is not finite (NaN/Inf input upstream).
 __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict__ imp,
                                                         int32_t* __restrict__ idx,
-                                                        int32_t* __restrict__ status, int T,
+                                                        int32_t* __restrict__ status,
+                                                        const int32_t* __restrict__ tv, int T,
                                                         int t) {
   __shared__ unsigned int hist[256];
   __shared__ int scratch[64];
@@ -61,10 +63,11 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
   const int b = blockIdx.x, tid = threadIdx.x;
   const unsigned int* u = reinterpret_cast<const unsigned int*>(imp) + static_cast<size_t>(b) * T;
 
+  const int tb = tv ? tv[b] : t;
   if (tid == 0) {
     s_prefix = 0;
     s_mask = 0;
-    s_need = t;
+    s_need = tb;
     s_bad = 0;
   }
   __syncthreads();
@@ -123,10 +126,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
     }
     if (keep) out[pos++] = j;
   }
+  for (int a = tb + tid; a < t; a += kSelThreads) out[a] = -1;
   if (tid == 0 && status && s_bad) status[b] |= 4;
 }
 
-// out_K[b][a][:] = K[b][idx[b][a]][:].  grid (ceil(t*D*es/16/256), B).
+// out_K[b][a][:] = K[b][idx[b][a]][:], zeros where idx is -1 (unused slots
+// of a smaller per-head budget).  grid (ceil(t*D*es/16/256), B).
 __global__ void k_gather_rows(const uint4* __restrict__ K, const int32_t* __restrict__ idx,
                               uint4* __restrict__ out, int T, int t, int row_vecs) {
   const int b = blockIdx.y;
@@ -135,7 +140,25 @@ __global__ void k_gather_rows(const uint4* __restrict__ K, const int32_t* __rest
   const int a = i / row_vecs, c = i % row_vecs;
   const int j = idx[static_cast<size_t>(b) * t + a];
   out[(static_cast<size_t>(b) * t + a) * row_vecs + c] =
-      K[(static_cast<size_t>(b) * T + j) * row_vecs + c];
+      j >= 0 ? K[(static_cast<size_t>(b) * T + j) * row_vecs + c] : make_uint4(0, 0, 0, 0);
+}
+
+// Per-head budgets: tv[b] = tin[b] clamped to [1, t]; status |= 16 where it
+// had to be clamped.  grid (ceil(B/256)).
+__global__ void k_budgets(const int32_t* __restrict__ tin, int32_t* __restrict__ tv,
+                          int32_t* __restrict__ status, int B, int t) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int v = tin[b];
+  const int c = v < 1 ? 1 : (v > t ? t : v);
+  tv[b] = c;
+  if (c != v && status) status[b] |= 16;
+}
+
+hipError_t launch_budgets(const int32_t* tin, int32_t* tv, int32_t* status, int B, int t,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(k_budgets, dim3((B + 255) / 256), dim3(256), 0, st, tin, tv, status, B, t);
+  return hipGetLastError();
 }
 
 __global__ void k_fill_i32(int32_t* __restrict__ p, int32_t v, size_t count) {
@@ -148,9 +171,9 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t count, hipStream_t st) 
   return hipGetLastError();
 }
 
-hipError_t launch_select(const float* imp, int32_t* idx, int32_t* status, int B, int T, int t,
-                         hipStream_t st) {
-  hipLaunchKernelGGL(k_select, dim3(B), dim3(kSelThreads), 0, st, imp, idx, status, T, t);
+hipError_t launch_select(const float* imp, int32_t* idx, int32_t* status, const int32_t* tv,
+                         int B, int T, int t, hipStream_t st) {
+  hipLaunchKernelGGL(k_select, dim3(B), dim3(kSelThreads), 0, st, imp, idx, status, tv, T, t);
   return hipGetLastError();
 }
 
@@ -170,7 +193,7 @@ __global__ void k_idx_offset(int32_t* __restrict__ idx, int Bc, int t, int C, in
   const size_t e = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (e >= static_cast<size_t>(Bc) * t) return;
   const int bc = static_cast<int>(e / t);
-  idx[e] += (bc % C) * Tc;
+  if (idx[e] >= 0) idx[e] += (bc % C) * Tc;
 }
 
 hipError_t launch_idx_offset(int32_t* idx, int Bc, int t, int C, int Tc, hipStream_t st) {

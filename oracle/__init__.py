@@ -1,6 +1,5 @@
 """Independent float64 CPU oracle (test infrastructure only; see am.py)."""
 from .am import *  # noqa: F401,F403
 from .am import (row_lse, attention_stats, select_topt, compact_probs, nnls_normal,
-                 fit_bias, compacted_weights, fit_values, fit, compact, compact_chunked, attend,
-                 rel_l2,
-                 W_FLOOR, DEFAULT_RIDGE_REL)
+                 fit_bias, compacted_weights, fit_values, fit, compact, compact_chunked,
+                 compact_ragged, attend, rel_l2, W_FLOOR, DEFAULT_RIDGE_REL)

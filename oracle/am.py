@@ -254,6 +254,29 @@ def compact_chunked(Q, K, V, t: int, n_chunks: int, agg: str = "rms",
     return out
 
 
+def compact_ragged(Qs, Ks, Vs, budgets, agg: str = "rms",
+                   ridge_rel: float = DEFAULT_RIDGE_REL):
+    """Per-head budgets (the per-head retention ratios of the non-uniform
+    schedule in section 2 of the same summary): head b is compacted on its own
+    with t = budgets[b].  Results are padded to max(budgets): a padded slot
+    holds index -1, zero key and value rows and bias -inf, whose softmax weight
+    is exactly zero, so attention over the padded cache equals attention over
+    the head's own compact cache."""
+    budgets = [int(x) for x in budgets]
+    tm = max(budgets)
+    B = len(budgets)
+    d, dv = np.asarray(Ks[0]).shape[1], np.asarray(Vs[0]).shape[1]
+    out = {"idx": np.full((B, tm), -1, np.int64), "Ck": np.zeros((B, tm, d)),
+           "beta": np.full((B, tm), -np.inf), "w": np.zeros((B, tm)),
+           "Cv": np.zeros((B, tm, dv)), "heads": []}
+    for h, tb in enumerate(budgets):
+        r = compact(Qs[h], Ks[h], Vs[h], tb, agg, ridge_rel)
+        for k in ("idx", "Ck", "beta", "w", "Cv"):
+            out[k][h, :tb] = r[k]
+        out["heads"].append(r)
+    return out
+
+
 def attend(Q, K, V, bias=None):
     """softmax(Q K^T + bias) V in float64 (the consumer's attention)."""
     s = np.asarray(Q, float) @ np.asarray(K, float).T

@@ -215,3 +215,60 @@ def test_chunked_long_context_sampled():
         err = compare_head(g, e, cd, w.t, _tol(w), tight=False)
         print("C5/4 entry", e, {k: (float(f"{v:.3g}") if isinstance(v, float) else v)
                                 for k, v in err.items()}, flush=True)
+
+
+@pytest.mark.parametrize("w,budgets", [
+    (synth.custom(15, 4, 2000, 160, 128, 0, "bf16", "clusters"), [40, 131, 1, 64]),
+    (synth.custom(16, 3, 900, 96, 64, 0, "f32", "normal"), [200, 65, 128]),
+], ids=["bf16", "f32_d64"])
+def test_ragged_budgets_match_oracle_per_head(w, budgets):
+    """kvc_compact_ragged: head b against the oracle's compaction at its own
+    budget; the padded slots are inert (index -1, zero rows, bias -inf)."""
+    import torch
+    import kv_cache_compaction_head_amd as kvc
+    data = synth.batch(w)
+    Q, K, V = (to_device(data[k]) for k in ("Q", "K", "V"))
+    res = kvc.compact_ragged(Q, K, V, budgets)
+    torch.cuda.synchronize()
+    tm = max(budgets)
+    assert res.idx.shape == (w.B, tm)
+    inter = {k: v.cpu().numpy() for k, v in kvc.intermediates(res).items()}
+    idx = res.idx.cpu().numpy().astype(np.int64)
+    bias = res.bias.cpu().numpy().astype(np.float64)
+    vals = res.values.cpu().numpy().astype(np.float64)
+    keys = res.keys.float().cpu().numpy()
+    st = res.status.cpu().numpy()
+    for h, tb in enumerate(budgets):
+        assert np.all(idx[h, tb:] == -1) and np.all(np.isneginf(bias[h, tb:]))
+        assert not keys[h, tb:].any() and not vals[h, tb:].any()
+        g = {"keys": res.keys[h:h + 1, :tb].cpu(), "bias": bias[h:h + 1, :tb],
+             "values": vals[h:h + 1, :tb], "idx": idx[h:h + 1, :tb], "status": st[h:h + 1],
+             "lse": inter["lse"][h:h + 1], "O": inter["O"][h:h + 1],
+             "imp": inter["imp"][h:h + 1], "w": inter["w"][h:h + 1, :tb]}
+        hd = {k: data[k][h:h + 1] for k in ("Q", "K", "V")}
+        err = compare_head(g, 0, hd, tb, _tol(w))
+        print(w.name, "head", h, "t", tb, {k: (float(f"{v:.3g}") if isinstance(v, float) else v)
+                                            for k, v in err.items()}, flush=True)
+        Qh = synth.to_f64(data["Q"][h])
+        o_pad = orc.attend(Qh, keys[h].astype(np.float64), vals[h], bias[h])
+        o_own = orc.attend(Qh, keys[h, :tb].astype(np.float64), vals[h, :tb], bias[h, :tb])
+        assert orc.rel_l2(o_pad, o_own) < 1e-12
+
+
+def test_ragged_equal_budgets_is_bitwise_compact_and_clamps():
+    import torch
+    import kv_cache_compaction_head_amd as kvc
+    w = synth.custom(17, 3, 1100, 128, 128, 70, "bf16", "sinks")
+    data = synth.batch(w)
+    Q, K, V = (to_device(data[k]) for k in ("Q", "K", "V"))
+    a = kvc.compact(Q, K, V, w.t)
+    b = kvc.compact_ragged(Q, K, V, [w.t] * w.B)
+    torch.cuda.synchronize()
+    for k in ("keys", "bias", "values", "idx", "status"):
+        assert torch.equal(getattr(a, k), getattr(b, k)), k
+    # a budget of 0 is clamped to 1 and flagged (status bit 16)
+    c = kvc.compact_ragged(Q, K, V, [0, 5, 70])
+    torch.cuda.synchronize()
+    st = c.status.cpu().numpy()
+    assert st[0] == 16 and st[1] == 0 and st[2] == 0
+    assert (c.idx[0, 1:] == -1).all() and c.idx[0, 0] >= 0

@@ -446,3 +446,25 @@ def test_chunked_argument_checks():
         orc.compact_chunked(np.zeros((2, 3)), np.zeros((10, 3)), np.zeros((10, 3)), 2, 3)
     with pytest.raises(ValueError):
         orc.compact_chunked(np.zeros((2, 3)), np.zeros((10, 3)), np.zeros((10, 3)), 6, 2)
+
+
+# ------------------------------------------------------ ragged budgets (f2)
+def test_ragged_heads_are_independent_compactions_and_padding_is_inert():
+    """Each head's slots equal compact() at its own budget; the padding
+    (index -1, zero rows, bias -inf) gives attention over the padded cache
+    exactly the value over the head's own compact cache, for fresh queries."""
+    rng = np.random.default_rng(71)
+    budgets = [7, 19, 1, 12]
+    Qs = [rng.standard_normal((16, 8)) * 0.4 for _ in budgets]
+    Ks = [rng.standard_normal((60, 8)) for _ in budgets]
+    Vs = [rng.standard_normal((60, 3)) for _ in budgets]
+    r = orc.compact_ragged(Qs, Ks, Vs, budgets)
+    assert r["idx"].shape == (4, 19)
+    for h, tb in enumerate(budgets):
+        own = orc.compact(Qs[h], Ks[h], Vs[h], tb)
+        assert np.array_equal(r["idx"][h, :tb], own["idx"])
+        assert np.all(r["idx"][h, tb:] == -1) and np.all(np.isneginf(r["beta"][h, tb:]))
+        Qn = rng.standard_normal((5, 8)) * 0.4
+        padded = orc.attend(Qn, r["Ck"][h], r["Cv"][h], r["beta"][h])
+        trimmed = orc.attend(Qn, own["Ck"], own["Cv"], own["beta"])
+        assert np.allclose(padded, trimmed, atol=1e-14, rtol=0)

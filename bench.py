@@ -45,11 +45,19 @@ def parse():
                     help="heads of the workload the CPU oracle times")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--variant", default="compact",
+                    choices=["compact", "chunked", "ragged", "protected"],
+                    help="chunked: the cache cut into --chunks equal chunks, t/chunks kept per "
+                         "chunk; ragged: per-head budgets from 0.5t to 1.5t (mean t); "
+                         "protected: 1%% of the keys (and the first) kept exactly")
+    ap.add_argument("--chunks", type=int, default=4)
     return ap.parse_args()
 
 
-def cpu_baseline(w, data, heads):
-    """The oracle as it stands, on `heads` heads of the same workload."""
+def cpu_baseline(w, data, heads, one_head=None):
+    """The oracle as it stands, on `heads` heads of the same workload.
+    one_head(orc, h, Q, K, V) runs the oracle's form of the benchmarked call on
+    head h (default: compact at budget t)."""
     import oracle as orc
     import synth
     try:
@@ -60,7 +68,10 @@ def cpu_baseline(w, data, heads):
     t0 = time.perf_counter()
     for h in range(heads):
         Q, K, V = (synth.to_f64(data[k][h]) for k in ("Q", "K", "V"))
-        orc.compact(Q, K, V, w.t)
+        if one_head is None:
+            orc.compact(Q, K, V, w.t)
+        else:
+            one_head(orc, h, Q, K, V)
     dt = time.perf_counter() - t0
     return {"value": heads * w.T / dt, "unit": "KV tokens/s", "cores": int(cores),
             "kind": "oracle",
@@ -124,9 +135,53 @@ def main():
 
     Q, K, V = dev(data["Q"]), dev(data["K"]), dev(data["V"])
     p = kvc.make_params(w.B, w.T, w.n, w.d, w.t, w.dtype)
-    ws = torch.empty(kvc.workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    variant = {"workload": w.name}
+    oracle_head = None
+    if args.variant == "chunked":
+        tc = w.t // args.chunks
+        need = kvc.workspace_bytes_chunked(kvc.make_params(w.B, w.T, w.n, w.d, tc, w.dtype),
+                                           args.chunks)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        variant.update(variant="chunked", chunks=args.chunks, t_per_chunk=tc)
+
+        def oracle_head(orc, h, Qh, Kh, Vh):
+            orc.compact_chunked(Qh, Kh, Vh, tc, args.chunks)
+
+        def call():
+            return kvc.compact_chunked(Q, K, V, tc, args.chunks, workspace=ws)
+    elif args.variant == "ragged":
+        budgets = [max(1, int(round(w.t * (0.5 + h / max(1, w.B - 1))))) for h in range(w.B)]
+        pr = kvc.make_params(w.B, w.T, w.n, w.d, max(budgets), w.dtype)
+        ws = torch.empty(kvc.workspace_bytes(pr), dtype=torch.uint8, device="cuda")
+        tv = torch.tensor(budgets, dtype=torch.int32, device="cuda")
+        variant.update(variant="ragged", budgets=budgets)
+
+        def oracle_head(orc, h, Qh, Kh, Vh):
+            orc.compact(Qh, Kh, Vh, budgets[h])
+
+        def call():
+            return kvc.compact_ragged(Q, K, V, tv, workspace=ws)
+    elif args.variant == "protected":
+        g = torch.Generator().manual_seed(w.cfg)
+        prot = (torch.rand((w.B, w.T), generator=g) < 0.01)
+        prot[:, 0] = True
+        prot = prot.to(torch.uint8).cuda()
+        ws = torch.empty(kvc.workspace_bytes(p), dtype=torch.uint8, device="cuda")
+        variant.update(variant="protected", protected_frac=0.01)
+        prot_host = prot.cpu().numpy()
+
+        def oracle_head(orc, h, Qh, Kh, Vh):
+            orc.compact_protected(Qh, Kh, Vh, w.t, prot_host[h])
+
+        def call():
+            return kvc.compact_protected(Q, K, V, w.t, prot, workspace=ws)
+    else:
+        ws = torch.empty(kvc.workspace_bytes(p), dtype=torch.uint8, device="cuda")
+
+        def call():
+            return kvc.compact(Q, K, V, w.t, workspace=ws)
     for _ in range(args.warmup):
-        res = kvc.compact(Q, K, V, w.t, workspace=ws)
+        res = call()
     torch.cuda.synchronize()
 
     stages = list(_lib.STAGES)
@@ -135,7 +190,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        res = kvc.compact(Q, K, V, w.t, workspace=ws)
+        res = call()
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / args.steps
     prof = {}
@@ -154,9 +209,11 @@ def main():
     Vf = synth.to_f64(data["V"][h])
     Qh = synth.to_f64(data["Qhold"][h])
     full = orc.attend(Qh, Kf, Vf)
-    comp = orc.attend(Qh, Kf[res.idx[h].cpu().numpy()], res.values[h].cpu().numpy(),
-                      res.bias[h].cpu().numpy())
-    evict = orc.attend(Qh, Kf[res.idx[h].cpu().numpy()], Vf[res.idx[h].cpu().numpy()])
+    ih = res.idx[h].cpu().numpy()
+    live = ih >= 0
+    comp = orc.attend(Qh, Kf[ih[live]], res.values[h].cpu().numpy()[live],
+                      res.bias[h].cpu().numpy()[live])
+    evict = orc.attend(Qh, Kf[ih[live]], Vf[ih[live]])
 
     B, T, n, d = w.B, w.T, w.n, w.d
     mm_peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -184,7 +241,8 @@ def main():
     roof = None
     if kernels:
         dom = max((k for k in kernels if k["kernel"].startswith("k_")), key=lambda k: k["ms"])
-        tr = traffic_record() if (dom["kernel"] == "k_nnls_sweep" and args.config == 3) else None
+        tr = (traffic_record() if (dom["kernel"] == "k_nnls_sweep" and args.config == 3 and
+                                   args.variant == "compact") else None)
         roof = {"bound": dom["bound"], "kernel": dom["kernel"], "achieved": dom["achieved"],
                 "peak": dom["peak"], "unit": "TFLOP/s", "frac": dom["frac"],
                 "traffic": tr["bytes_per_launch"] if tr else None,
@@ -199,7 +257,7 @@ def main():
         "ms_per_step": dt * 1e3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "B": B, "T": T, "n": n, "d": d, "t": w.t,
+        "config": {**variant, "B": B, "T": T, "n": n, "d": d, "t": w.t,
                    "ratio": T / w.t},
         "quality": {"heldout_rel_l2": orc.rel_l2(comp, full),
                     "eviction_only_rel_l2": orc.rel_l2(evict, full),
@@ -207,7 +265,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(w, data, min(args.cpu_heads, w.B))
+        out["cpu_baseline"] = cpu_baseline(w, data, min(args.cpu_heads, w.B), oracle_head)
     print(json.dumps(out), flush=True)
 
 

@@ -62,6 +62,9 @@ extern "C" {
                                        head's fit is incomplete)               */
 #define KVC_STATUS_BUDGET       16  /* kvc_compact_ragged: the head's budget was
                                        outside [1, p->t] and was clamped       */
+#define KVC_STATUS_PROTECT      32  /* kvc_compact_protected: more than t - 1
+                                       keys were marked; only the first t - 1
+                                       (by position) were kept as protected    */
 
 typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype_t;
 typedef enum { KVC_AGG_RMS = 0, KVC_AGG_MEAN = 1 } kvc_agg_t;
@@ -128,6 +131,27 @@ int kvc_compact_ragged(const kvc_params_t* p, const int32_t* t_heads, const void
                        const void* K, const void* V, void* out_K, float* out_bias, float* out_V,
                        int32_t* out_idx, int32_t* out_status, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
+
+/* Protected keys ("Thought-Aware KV Cache Compaction for Reasoning via
+ * Adaptive Attention Matching", section 2C: pivot tokens are kept exactly,
+ * with zero bias, and the rest of the budget goes to the other tokens).
+ * For head b let P be the marked keys (at most t - 1 of them, the first by
+ * position; more sets KVC_STATUS_PROTECT) and R the others.  P is kept as is;
+ * R is compacted to t - |P| keys exactly as kvc_compact compacts a cache,
+ * with R's own log-sum-exp, output and importance (P's exact block carries
+ * its own mass and output, so by the block decomposition of the main
+ * objective the fitted part only has to match R).
+ *   protect_mask [B, T] uint8, DEVICE memory: nonzero marks a protected key.
+ *   Outputs have kvc_compact's shapes.  Head b's slots [0, t - |P|) hold the
+ *   fitted part (indices ascending), slots [t - |P|, t) the protected keys
+ *   (ascending): out_K and out_V their K and V rows (V as float32),
+ *   out_bias 0.
+ *   workspace  >= kvc_workspace_bytes(p) bytes.
+ * Returns as kvc_compact. */
+int kvc_compact_protected(const kvc_params_t* p, const uint8_t* protect_mask, const void* Q_ref,
+                          const void* K, const void* V, void* out_K, float* out_bias,
+                          float* out_V, int32_t* out_idx, int32_t* out_status, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
 
 /* Chunked compaction ("Compaction par blocs" of the same summary): each head's
  * cache is cut into n_chunks contiguous chunks of T / n_chunks keys, every

@@ -15,7 +15,7 @@ from ._lib import (KVC_AGG_MEAN, KVC_AGG_RMS, KVC_BF16, KVC_F32, STATUS_NNLS_CAP
                    STATUS_NONFINITE, STATUS_NOT_SPD, Params, load, make_params, strerror,
                    workspace_bytes, workspace_bytes_chunked, workspace_layout)
 
-__all__ = ["compact", "compact_chunked", "compact_ragged", "fit", "Compacted", "intermediates", "load", "make_params",
+__all__ = ["compact", "compact_chunked", "compact_ragged", "compact_protected", "fit", "Compacted", "intermediates", "load", "make_params",
            "workspace_bytes", "workspace_bytes_chunked", "workspace_layout", "strerror", "Params"]
 
 
@@ -119,6 +119,36 @@ def compact_ragged(Q, K, V, t_heads, *, agg: str = "rms", ridge_rel: float = 1e-
                                    _vp(bias), _vp(values), _vp(idx), _vp(status), _vp(ws),
                                    ctypes.c_size_t(ws.numel() * ws.element_size()),
                                    _stream(stream, dev))
+    _lib.check(rc)
+    return Compacted(keys, bias, values, idx, status, ws, p)
+
+
+def compact_protected(Q, K, V, t: int, protect, *, agg: str = "rms", ridge_rel: float = 1e-6,
+                      max_nnls_iters: int = 32, workspace=None, stream=None) -> Compacted:
+    """Keep the marked keys of protect [B, T] (bool/uint8) exactly with bias 0
+    (at most t - 1 per head, the first by position) and compact the others
+    into the remaining slots.  Head b's slots [0, t - p_b) hold the fitted
+    part, slots [t - p_b, t) the protected keys, both ascending."""
+    import torch
+    Q, K, V, _ = _prep(Q, K, V)
+    B, n, d = Q.shape
+    T = K.shape[1]
+    if tuple(protect.shape) != (B, T):
+        raise ValueError(f"protect must be [B, T] = [{B}, {T}]")
+    m = protect.to(device=Q.device, dtype=torch.uint8).contiguous()
+    dt = "bf16" if Q.dtype == torch.bfloat16 else "f32"
+    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters)
+    dev = Q.device
+    ws = _workspace(p, dev, workspace)
+    keys = torch.empty((B, t, d), dtype=Q.dtype, device=dev)
+    bias = torch.empty((B, t), dtype=torch.float32, device=dev)
+    values = torch.empty((B, t, d), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, t), dtype=torch.int32, device=dev)
+    status = torch.empty((B,), dtype=torch.int32, device=dev)
+    rc = load().kvc_compact_protected(ctypes.byref(p), _vp(m), _vp(Q), _vp(K), _vp(V), _vp(keys),
+                                      _vp(bias), _vp(values), _vp(idx), _vp(status), _vp(ws),
+                                      ctypes.c_size_t(ws.numel() * ws.element_size()),
+                                      _stream(stream, dev))
     _lib.check(rc)
     return Compacted(keys, bias, values, idx, status, ws, p)
 

@@ -12,10 +12,12 @@ LIB_PATH = os.path.join(HERE, "libkvc.so")
 KVC_OK, KVC_EINVAL, KVC_EWORKSPACE, KVC_EHIP, KVC_EUNSUPPORTED = 0, -1, -2, -3, -4
 KVC_F32, KVC_BF16 = 0, 1
 KVC_AGG_RMS, KVC_AGG_MEAN = 0, 1
-STATUS_NOT_SPD, STATUS_NNLS_CAP, STATUS_NONFINITE, STATUS_SYNC_TIMEOUT, STATUS_BUDGET = 1, 2, 4, 8, 16
+(STATUS_NOT_SPD, STATUS_NNLS_CAP, STATUS_NONFINITE, STATUS_SYNC_TIMEOUT, STATUS_BUDGET,
+ STATUS_PROTECT) = 1, 2, 4, 8, 16, 32
 
 EXPORTS = ("kvc_params_default", "kvc_workspace_bytes", "kvc_compact", "kvc_fit",
            "kvc_workspace_bytes_chunked", "kvc_compact_chunked", "kvc_compact_ragged",
+           "kvc_compact_protected",
            "kvc_workspace_layout", "kvc_profile_enable", "kvc_profile_read", "kvc_strerror")
 STAGES = {"score_lse": 0, "expweight": 1, "select": 2, "ps": 3, "gram": 4, "nnls": 5,
           "value": 6, "total": 7}
@@ -63,6 +65,9 @@ def load() -> ctypes.CDLL:
     lib.kvc_compact_ragged.argtypes = [P, vp, vp, vp, vp, vp, f32p, f32p, i32p, i32p, vp,
                                        ctypes.c_size_t, vp]
     lib.kvc_compact_ragged.restype = ctypes.c_int
+    lib.kvc_compact_protected.argtypes = [P, vp, vp, vp, vp, vp, f32p, f32p, i32p, i32p, vp,
+                                          ctypes.c_size_t, vp]
+    lib.kvc_compact_protected.restype = ctypes.c_int
     lib.kvc_workspace_layout.argtypes = [P, ctypes.POINTER(WsLayout)]
     lib.kvc_workspace_layout.restype = ctypes.c_int
     lib.kvc_profile_enable.argtypes = [ctypes.c_uint32]

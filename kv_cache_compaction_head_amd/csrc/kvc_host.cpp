@@ -77,7 +77,7 @@ Plan make_plan(const kvc_params_t* p) {
 }
 
 struct Layout {
-  size_t ml, lse, Opart, O, imp_part, imp, idx, status, tv, PS, S, U, V, stage, cvec, wv, lam,
+  size_t ml, lse, Opart, O, imp_part, imp, idx, status, tv, emask, plist, PS, S, U, V, stage, cvec, wv, lam,
       colpart, Fidx, inv, msz, bar, xcc, flops, part, total;
   size_t part_cap;
 };
@@ -103,6 +103,8 @@ Layout make_layout(const kvc_params_t* p) {
   L.idx = take(B * t * 4);
   L.status = take(B * 4);
   L.tv = take(B * 4);
+  L.emask = take(B * T);
+  L.plist = take(B * t * 4);
   L.PS = take(B * n * t * 8);
   {
     const size_t ld = static_cast<size_t>(kvc::sweep_ld(static_cast<int>(t), static_cast<int>(d)));
@@ -182,14 +184,14 @@ kvc::FitBufs fit_bufs(void* ws, const Layout& L) {
 // (chunked compaction runs every chunk of a head against that head's queries).
 template <class In, int D>
 hipError_t run_score(const kvc_params_t* p, const void* Q, const void* K, const void* V,
-                     void* ws, const Layout& L, int qg, hipStream_t st) {
+                     void* ws, const Layout& L, int qg, const uint8_t* mask, hipStream_t st) {
   const Plan pl = make_plan(p);
   return kvc::launch_score<In, D>(Q, K, V, at<double2>(ws, L.ml), at<double>(ws, L.lse),
                                   at<float>(ws, L.Opart), at<float>(ws, L.O),
                                   at<float>(ws, L.imp_part), at<float>(ws, L.imp),
                                   static_cast<int>(p->B), static_cast<int>(p->n),
                                   static_cast<int>(p->T), pl.nsplit1, pl.kps1, pl.nsplit2,
-                                  pl.kps2, p->agg == KVC_AGG_RMS, qg, st);
+                                  pl.kps2, p->agg == KVC_AGG_RMS, qg, mask, st);
 }
 
 template <class In, int D>
@@ -219,8 +221,9 @@ hipError_t dispatch(const kvc_params_t* p, A... args) {
 template <class In, int D>
 struct ScoreOp {
   static hipError_t run(const kvc_params_t* p, const void* Q, const void* K, const void* V,
-                        void* ws, const Layout* L, int qg, hipStream_t st) {
-    return run_score<In, D>(p, Q, K, V, ws, *L, qg, st);
+                        void* ws, const Layout* L, int qg, const uint8_t* mask,
+                        hipStream_t st) {
+    return run_score<In, D>(p, Q, K, V, ws, *L, qg, mask, st);
   }
 };
 template <class In, int D>
@@ -255,10 +258,12 @@ bool chunk_params(const kvc_params_t* p, int64_t C, kvc_params_t* out) {
 }
 
 // Select, gather and fit for every batch entry of p; qg as in run_score;
-// t_in: per-entry budgets (device) or null for p->t everywhere.
-int compact_impl(const kvc_params_t* p, int qg, const int32_t* t_in, const void* Q_ref,
-                 const void* K, const void* V, void* out_K, float* out_bias, float* out_V,
-                 int32_t* out_idx, int32_t* out_status, void* workspace, hipStream_t stream) {
+// t_in: per-entry budgets (device) or null for p->t everywhere; protect: the
+// caller's protected-key mask [B][T] (device) or null.
+int compact_impl(const kvc_params_t* p, int qg, const int32_t* t_in, const uint8_t* protect,
+                 const void* Q_ref, const void* K, const void* V, void* out_K, float* out_bias,
+                 float* out_V, int32_t* out_idx, int32_t* out_status, void* workspace,
+                 hipStream_t stream) {
   const Layout L = make_layout(p);
   int32_t* idx = out_idx ? out_idx : at<int32_t>(workspace, L.idx);
   int32_t* status = out_status ? out_status : at<int32_t>(workspace, L.status);
@@ -267,20 +272,30 @@ int compact_impl(const kvc_params_t* p, int qg, const int32_t* t_in, const void*
   kvc::prof_mark(KVC_STAGE_TOTAL, false, stream);
   hipError_t e = kvc::launch_fill_i32(status, 0, p->B, stream);
   int32_t* tv = nullptr;
+  const uint8_t* emask = nullptr;
+  int32_t* plist = at<int32_t>(workspace, L.plist);
   if (t_in) {
     tv = at<int32_t>(workspace, L.tv);
     if (e == hipSuccess) e = kvc::launch_budgets(t_in, tv, status, B, t, stream);
+  } else if (protect) {
+    tv = at<int32_t>(workspace, L.tv);
+    uint8_t* em = at<uint8_t>(workspace, L.emask);
+    emask = em;
+    if (e == hipSuccess) e = kvc::launch_protect_prep(protect, em, plist, tv, status, B, T, t, stream);
   }
-  if (e == hipSuccess) e = dispatch<ScoreOp>(p, Q_ref, K, V, workspace, &L, qg, stream);
+  if (e == hipSuccess) e = dispatch<ScoreOp>(p, Q_ref, K, V, workspace, &L, qg, emask, stream);
   kvc::prof_mark(KVC_STAGE_SELECT, false, stream);
   if (e == hipSuccess)
-    e = kvc::launch_select(at<float>(workspace, L.imp), idx, status, tv, B, T, t, stream);
+    e = kvc::launch_select(at<float>(workspace, L.imp), idx, status, tv, emask, B, T, t, stream);
   if (e == hipSuccess)
     e = kvc::launch_gather(K, idx, out_K, B, T, t, static_cast<int>(p->d) * es, stream);
   kvc::prof_mark(KVC_STAGE_SELECT, true, stream);
   if (e == hipSuccess)
     e = dispatch<FitOp>(p, Q_ref, K, V, static_cast<const int32_t*>(idx), out_bias, out_V,
                         status, workspace, &L, qg, tv, stream);
+  if (e == hipSuccess && protect)
+    e = kvc::launch_fill_protected(plist, tv, K, V, out_K, out_V, out_bias, idx, B, T, t,
+                                   static_cast<int>(p->d), p->in_dtype == KVC_BF16, stream);
   if (e == hipSuccess && qg > 1 && out_idx)
     e = kvc::launch_idx_offset(out_idx, B, t, qg, T, stream);
   kvc::prof_mark(KVC_STAGE_TOTAL, true, stream);
@@ -325,8 +340,21 @@ int kvc_compact(const kvc_params_t* p, const void* Q_ref, const void* K, const v
   if (rc) return rc;
   if (!aligned(out_K) || (out_idx && !aligned(out_idx)) || (out_status && !aligned(out_status)))
     return KVC_EINVAL;
-  return compact_impl(p, 1, nullptr, Q_ref, K, V, out_K, out_bias, out_V, out_idx, out_status,
-                      workspace, stream);
+  return compact_impl(p, 1, nullptr, nullptr, Q_ref, K, V, out_K, out_bias, out_V, out_idx,
+                      out_status, workspace, stream);
+}
+
+int kvc_compact_protected(const kvc_params_t* p, const uint8_t* protect_mask, const void* Q_ref,
+                          const void* K, const void* V, void* out_K, float* out_bias,
+                          float* out_V, int32_t* out_idx, int32_t* out_status, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  int rc = common_checks(p, Q_ref, K, V, out_bias, out_V, workspace, workspace_bytes);
+  if (rc) return rc;
+  if (!protect_mask || !aligned(out_K) || (out_idx && !aligned(out_idx)) ||
+      (out_status && !aligned(out_status)))
+    return KVC_EINVAL;
+  return compact_impl(p, 1, nullptr, protect_mask, Q_ref, K, V, out_K, out_bias, out_V, out_idx,
+                      out_status, workspace, stream);
 }
 
 int kvc_compact_ragged(const kvc_params_t* p, const int32_t* t_heads, const void* Q_ref,
@@ -338,8 +366,8 @@ int kvc_compact_ragged(const kvc_params_t* p, const int32_t* t_heads, const void
   if (!t_heads || (reinterpret_cast<uintptr_t>(t_heads) & 3u) || !aligned(out_K) ||
       (out_idx && !aligned(out_idx)) || (out_status && !aligned(out_status)))
     return KVC_EINVAL;
-  return compact_impl(p, 1, t_heads, Q_ref, K, V, out_K, out_bias, out_V, out_idx, out_status,
-                      workspace, stream);
+  return compact_impl(p, 1, t_heads, nullptr, Q_ref, K, V, out_K, out_bias, out_V, out_idx,
+                      out_status, workspace, stream);
 }
 
 size_t kvc_workspace_bytes_chunked(const kvc_params_t* p, int64_t n_chunks) {
@@ -358,8 +386,8 @@ int kvc_compact_chunked(const kvc_params_t* p, int64_t n_chunks, const void* Q_r
   if (rc) return rc;
   if (!aligned(out_K) || (out_idx && !aligned(out_idx)) || (out_status && !aligned(out_status)))
     return KVC_EINVAL;
-  return compact_impl(&pc, static_cast<int>(n_chunks), nullptr, Q_ref, K, V, out_K, out_bias,
-                      out_V, out_idx, out_status, workspace, stream);
+  return compact_impl(&pc, static_cast<int>(n_chunks), nullptr, nullptr, Q_ref, K, V, out_K,
+                      out_bias, out_V, out_idx, out_status, workspace, stream);
 }
 
 int kvc_fit(const kvc_params_t* p, const void* Q_ref, const void* K, const void* V,
@@ -372,7 +400,9 @@ int kvc_fit(const kvc_params_t* p, const void* Q_ref, const void* K, const void*
   int32_t* status = out_status ? out_status : at<int32_t>(workspace, L.status);
   kvc::prof_mark(KVC_STAGE_TOTAL, false, stream);
   hipError_t e = kvc::launch_fill_i32(status, 0, p->B, stream);
-  if (e == hipSuccess) e = dispatch<ScoreOp>(p, Q_ref, K, V, workspace, &L, 1, stream);
+  if (e == hipSuccess)
+    e = dispatch<ScoreOp>(p, Q_ref, K, V, workspace, &L, 1, static_cast<const uint8_t*>(nullptr),
+                          stream);
   if (e == hipSuccess)
     e = dispatch<FitOp>(p, Q_ref, K, V, idx, out_bias, out_V, status, workspace, &L, 1,
                         static_cast<const int32_t*>(nullptr), stream);

@@ -11,10 +11,22 @@ template <class In, int D>
 hipError_t launch_score(const void* Q, const void* K, const void* V, double2* ml, double* lse,
                         float* Opart, float* O, float* imp_part, float* imp, int B, int n, int T,
                         int nsplit1, int kps1, int nsplit2, int kps2, bool rms, int qg,
-                        hipStream_t st);
-// tv: per-head budgets (device, each in [1, t]) or null for t everywhere
+                        const uint8_t* mask, hipStream_t st);
+// tv: per-head budgets (device, each in [1, t]) or null for t everywhere;
+// mask: [B][T] keys never selected (nonzero), or null
 hipError_t launch_select(const float* imp, int32_t* idx, int32_t* status, const int32_t* tv,
-                         int B, int T, int t, hipStream_t st);
+                         const uint8_t* mask, int B, int T, int t, hipStream_t st);
+// Protected keys: from the caller's mask [B][T], per head the first (by
+// position) pp_b = min(count, t - 1) protected keys are listed in plist [B][t]
+// and marked in emask [B][T] (the rest of the mask is dropped, status |= 32);
+// tv[b] = t - pp_b is the budget left for the fitted keys.
+hipError_t launch_protect_prep(const uint8_t* mask, uint8_t* emask, int32_t* plist, int32_t* tv,
+                               int32_t* status, int B, int T, int t, hipStream_t st);
+// Slots [tv[b], t) of head b: the protected keys, exact (K, V as float, bias 0).
+hipError_t launch_fill_protected(const int32_t* plist, const int32_t* tv, const void* K,
+                                 const void* V, void* out_K, float* out_V, float* out_bias,
+                                 int32_t* out_idx, int B, int T, int t, int D, bool bf16,
+                                 hipStream_t st);
 // tv[b] = tin[b] clamped to [1, t]; status[b] |= 16 where clamped
 hipError_t launch_budgets(const int32_t* tin, int32_t* tv, int32_t* status, int B, int t,
                           hipStream_t st);

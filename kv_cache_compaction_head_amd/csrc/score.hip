@@ -101,21 +101,24 @@ __device__ __forceinline__ void load_q_frags(typename Frag<In>::T* bq, const In*
 // grid (ceil(n/128), nsplit, B), block 256.  ml[b][split][q] = (m, l) with
 // sum_{j in split} exp(s_qj) = l * exp(m).
 // ---------------------------------------------------------------------------
-template <class In, int D>
+template <class In, int D, bool MASK>
 __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
                                                    const In* __restrict__ K,
+                                                   const uint8_t* __restrict__ mask,
                                                    double2* __restrict__ ml, int n, int T,
                                                    int keys_per_split, int nqb, int nsplit, int B,
                                                    int qg) {
   constexpr int KS = Frag<In>::KS, NK = D / KS, BN = 64, LD = D + 16 / sizeof(In);
   constexpr int VEC = 16 / sizeof(In), CPR = D / VEC, NCH = BN * CPR / 256;
   __shared__ __align__(16) In sK[2][BN * LD];
+  __shared__ uint64_t sMb[2];  // excluded keys of the tile, one bit per key
   int qb, split, b;
   if (!score_grid(nqb, nsplit, B, qb, split, b)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 5;
   const int q = qb * kBM + wave * 32 + (lane & 31);
   const In* Qb = Q + static_cast<size_t>(b / qg) * n * D;
   const In* Kb = K + static_cast<size_t>(b) * T * D;
+  const uint8_t* Mb = mask ? mask + static_cast<size_t>(b) * T : nullptr;
 
   typename Frag<In>::T bq[NK];
   load_q_frags<In, D>(bq, Qb, q, n, g);
@@ -126,6 +129,7 @@ __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
   // next tile's K rows in registers while the current tile is computed;
   // rows past the split end read row j1-1 and are zeroed (one batch of loads)
   uint4 pk[NCH];
+  uint64_t pm = 0;
   auto fetch = [&](int jt) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -135,6 +139,7 @@ __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
           Kb + static_cast<size_t>(ok ? jt + r : j1 - 1) * D + col);
       pk[c] = ok ? kv : make_uint4(0, 0, 0, 0);
     }
+    if (MASK && wave == 0) pm = __ballot(Mb[min(jt + lane, j1 - 1)] != 0);
   };
   auto stash = [&](int buf) {
 #pragma unroll
@@ -142,6 +147,7 @@ __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
       const int idx = threadIdx.x + c * 256, r = idx / CPR, col = (idx % CPR) * VEC;
       *reinterpret_cast<uint4*>(&sK[buf][r * LD + col]) = pk[c];
     }
+    if (MASK && threadIdx.x == 0) sMb[buf] = pm;
   };
   // running max m (a score, exact in fp32) and sum l = sum exp(s - m) in fp64:
   // each 16-term tile sum is formed in fp32, then accumulated in double, and
@@ -165,10 +171,11 @@ __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
         acc = Frag<In>::mma(a, bq[ks], acc);
       }
       float tmax = -INFINITY;
+      const uint64_t mb = MASK ? sMb[cur] : 0;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int j = jt + st * 32 + mfma32_row(r, lane);
-        const float s = j < j1 ? acc[r] : -INFINITY;
+        const int kk = st * 32 + mfma32_row(r, lane), j = jt + kk;
+        const float s = (j < j1 && !((mb >> kk) & 1)) ? acc[r] : -INFINITY;
         acc[r] = s;
         tmax = fmaxf(tmax, s);
       }
@@ -267,11 +274,12 @@ __device__ __forceinline__ float half_wave_rowsum(const float (&v)[16], int lane
   return z + __shfl_xor(z, 1);
 }
 
-template <class In, int D, bool RMS>
+template <class In, int D, bool RMS, bool MASK>
 __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
                                                    const In* __restrict__ K,
                                                    const In* __restrict__ V,
                                                    const double* __restrict__ lse,
+                                                   const uint8_t* __restrict__ mask,
                                                    float* __restrict__ Opart,
                                                    float* __restrict__ imp_part, int n, int T,
                                                    int keys_per_split, int nqb, int nsplit,
@@ -286,6 +294,7 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
   __shared__ __align__(16) In sK[2][BN * LD];
   __shared__ __align__(16) In sVt[2][D * LDV];
   __shared__ float sImp[2][kWaves][BN];
+  __shared__ uint64_t sMb[2];  // excluded keys of the tile, one bit per key
 
   int qb, split, b;
   if (!score_grid(nqb, nsplit, B, qb, split, b)) return;
@@ -294,6 +303,7 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
   const In* Qb = Q + static_cast<size_t>(b / qg) * n * D;
   const In* Kb = K + static_cast<size_t>(b) * T * D;
   const In* Vb = V + static_cast<size_t>(b) * T * D;
+  const uint8_t* Mb = mask ? mask + static_cast<size_t>(b) * T : nullptr;
 
   typename Frag<In>::T bq[NK];
   load_q_frags<In, D>(bq, Qb, q, n, g);
@@ -311,6 +321,7 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
   const int j1 = min(T, j0 + keys_per_split);
   const int ntile = (j1 - j0 + BN - 1) / BN;
   uint4 pk[NCH], pv[NCH];
+  uint64_t pm = 0;
   // rows past the split end read row j1-1 (always valid) and are zeroed, so
   // the fetch is one unconditional batch of loads
   // K rows go to LDS as they are (consecutive lanes: consecutive 16-byte
@@ -332,6 +343,7 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
           Vb + static_cast<size_t>(okv ? jt + rv : j1 - 1) * D + colv);
       pv[c] = okv ? vv : make_uint4(0, 0, 0, 0);
     }
+    if (MASK && wave == 0) pm = __ballot(Mb[min(jt + lane, j1 - 1)] != 0);
   };
   auto stash = [&](int buf) {
 #pragma unroll
@@ -346,6 +358,7 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
 #pragma unroll
       for (int e = 0; e < VEC; ++e) sVt[buf][(colv + e) * LDV + pos] = v[e];
     }
+    if (MASK && threadIdx.x == 0) sMb[buf] = pm;
   };
   if (ntile > 0) {
     fetch(j0);
@@ -364,11 +377,12 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
         acc = Frag<In>::mma(a, bq[ks], acc);
       }
       float w[16];
+      const uint64_t mb = MASK ? sMb[cur] : 0;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kk = st * 32 + mfma32_row(r, lane);
         const float e = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2) - ml2lo);
-        const float p = (kk < valid && q < n) ? e : 0.f;
+        const float p = (kk < valid && q < n && !((mb >> kk) & 1)) ? e : 0.f;
         acc[r] = p;
         w[r] = RMS ? p * p : p;
       }
@@ -467,26 +481,34 @@ template <class In, int D>
 hipError_t launch_score(const void* Q, const void* K, const void* V, double2* ml, double* lse,
                         float* Opart, float* O, float* imp_part, float* imp, int B, int n, int T,
                         int nsplit1, int kps1, int nsplit2, int kps2, bool rms, int qg,
-                        hipStream_t st) {
+                        const uint8_t* mask, hipStream_t st) {
   const int nqb = (n + kBM - 1) / kBM;
   const In* q = static_cast<const In*>(Q);
   const In* k = static_cast<const In*>(K);
   const In* v = static_cast<const In*>(V);
   prof_mark(0, false, st);
-  hipLaunchKernelGGL((k_score_lse<In, D>), dim3(score_grid_size(nqb, nsplit1, B)), dim3(256), 0,
-                     st, q, k, ml, n, T, kps1, nqb, nsplit1, B, qg);
+  const dim3 g1(score_grid_size(nqb, nsplit1, B)), g2(score_grid_size(nqb, nsplit2, B));
+  if (mask)
+    hipLaunchKernelGGL((k_score_lse<In, D, true>), g1, dim3(256), 0, st, q, k, mask, ml, n, T, kps1,
+                       nqb, nsplit1, B, qg);
+  else
+    hipLaunchKernelGGL((k_score_lse<In, D, false>), g1, dim3(256), 0, st, q, k, mask, ml, n, T,
+                       kps1, nqb, nsplit1, B, qg);
   prof_mark(0, true, st);
   hipLaunchKernelGGL(k_lse_merge, dim3((B * n + 255) / 256), dim3(256), 0, st, ml, lse, n,
                      nsplit1, B);
   prof_mark(1, false, st);
-  if (rms)
-    hipLaunchKernelGGL((k_expweight<In, D, true>), dim3(score_grid_size(nqb, nsplit2, B)),
-                       dim3(256), 0, st, q, k, v, lse, Opart, imp_part, n, T, kps2, nqb, nsplit2,
-                       B, qg);
-  else
-    hipLaunchKernelGGL((k_expweight<In, D, false>), dim3(score_grid_size(nqb, nsplit2, B)),
-                       dim3(256), 0, st, q, k, v, lse, Opart, imp_part, n, T, kps2, nqb, nsplit2,
-                       B, qg);
+#define KVC_K2(R, M)                                                                           \
+  hipLaunchKernelGGL((k_expweight<In, D, R, M>), g2, dim3(256), 0, st, q, k, v, lse, mask, Opart, \
+                     imp_part, n, T, kps2, nqb, nsplit2, B, qg)
+  if (rms) {
+    if (mask) KVC_K2(true, true);
+    else KVC_K2(true, false);
+  } else {
+    if (mask) KVC_K2(false, true);
+    else KVC_K2(false, false);
+  }
+#undef KVC_K2
   prof_mark(1, true, st);
   hipLaunchKernelGGL(k_o_reduce, dim3((n + 31) / 32, D / 32, B), dim3(32, 8), 0, st, Opart, O, n,
                      D, nsplit2);
@@ -498,15 +520,19 @@ hipError_t launch_score(const void* Q, const void* K, const void* V, double2* ml
 
 template hipError_t launch_score<bf16_t, 128>(const void*, const void*, const void*, double2*,
                                               double*, float*, float*, float*, float*, int, int,
-                                              int, int, int, int, int, bool, int, hipStream_t);
+                                              int, int, int, int, int, bool, int, const uint8_t*,
+                                             hipStream_t);
 template hipError_t launch_score<bf16_t, 64>(const void*, const void*, const void*, double2*,
                                              double*, float*, float*, float*, float*, int, int,
-                                             int, int, int, int, int, bool, int, hipStream_t);
+                                             int, int, int, int, int, bool, int, const uint8_t*,
+                                             hipStream_t);
 template hipError_t launch_score<float, 128>(const void*, const void*, const void*, double2*,
                                              double*, float*, float*, float*, float*, int, int,
-                                             int, int, int, int, int, bool, int, hipStream_t);
+                                             int, int, int, int, int, bool, int, const uint8_t*,
+                                             hipStream_t);
 template hipError_t launch_score<float, 64>(const void*, const void*, const void*, double2*,
                                             double*, float*, float*, float*, float*, int, int,
-                                            int, int, int, int, int, bool, int, hipStream_t);
+                                            int, int, int, int, int, bool, int, const uint8_t*,
+                                             hipStream_t);
 
 }  // namespace kvc

@@ -50,11 +50,15 @@ __device__ int block_exclusive_scan(int v, int* scratch, int* total) {
 
 // grid (B), block kSelThreads.  imp [B][T] (non-negative floats), idx [B][t]:
 // the tb = tv[b] (or t) kept indices ascending, then -1 in the remaining slots.
+// Keys marked in mask (if given) are never kept: the ranking key is the bit
+// pattern plus one, and 0 for a marked key, which keeps the order of the
+// others (patterns of finite non-negative floats stay below 0x7f800000).
 // status[b] |= 4 if an importance is not finite (NaN/Inf input upstream).
 __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict__ imp,
                                                         int32_t* __restrict__ idx,
                                                         int32_t* __restrict__ status,
-                                                        const int32_t* __restrict__ tv, int T,
+                                                        const int32_t* __restrict__ tv,
+                                                        const uint8_t* __restrict__ mask, int T,
                                                         int t) {
   __shared__ unsigned int hist[256];
   __shared__ int scratch[64];
@@ -62,6 +66,11 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
   __shared__ int s_need, s_bad;
   const int b = blockIdx.x, tid = threadIdx.x;
   const unsigned int* u = reinterpret_cast<const unsigned int*>(imp) + static_cast<size_t>(b) * T;
+  const uint8_t* mb = mask ? mask + static_cast<size_t>(b) * T : nullptr;
+  auto key = [&](int j) -> unsigned int {
+    const unsigned int v = u[j];
+    return mb ? (mb[j] ? 0u : v + 1u) : v;
+  };
 
   const int tb = tv ? tv[b] : t;
   if (tid == 0) {
@@ -76,8 +85,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
     __syncthreads();
     const unsigned int prefix = s_prefix, mask = s_mask;
     for (int j = tid; j < T; j += kSelThreads) {
-      const unsigned int v = u[j];
-      if (shift == 24 && v >= 0x7f800000u) s_bad = 1;  // inf / nan (non-negative inputs)
+      if (shift == 24 && u[j] >= 0x7f800000u) s_bad = 1;  // inf / nan (non-negative inputs)
+      const unsigned int v = key(j);
       if ((v & mask) == prefix) atomicAdd(&hist[(v >> shift) & 255u], 1u);
     }
     __syncthreads();
@@ -107,7 +116,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
   const int c0 = min(T, tid * chunk), c1 = min(T, c0 + chunk);
   int n_gt = 0, n_eq = 0;
   for (int j = c0; j < c1; ++j) {
-    const unsigned int v = u[j];
+    const unsigned int v = key(j);
     n_gt += v > tau;
     n_eq += v == tau;
   }
@@ -118,7 +127,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
   int32_t* out = idx + static_cast<size_t>(b) * t;
   int pos = pos0, eq_taken = 0;
   for (int j = c0; j < c1; ++j) {
-    const unsigned int v = u[j];
+    const unsigned int v = key(j);
     bool keep = v > tau;
     if (v == tau && eq_taken < take_eq) {
       keep = true;
@@ -172,8 +181,9 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t count, hipStream_t st) 
 }
 
 hipError_t launch_select(const float* imp, int32_t* idx, int32_t* status, const int32_t* tv,
-                         int B, int T, int t, hipStream_t st) {
-  hipLaunchKernelGGL(k_select, dim3(B), dim3(kSelThreads), 0, st, imp, idx, status, tv, T, t);
+                         const uint8_t* mask, int B, int T, int t, hipStream_t st) {
+  hipLaunchKernelGGL(k_select, dim3(B), dim3(kSelThreads), 0, st, imp, idx, status, tv, mask, T,
+                     t);
   return hipGetLastError();
 }
 
@@ -199,6 +209,90 @@ __global__ void k_idx_offset(int32_t* __restrict__ idx, int Bc, int t, int C, in
 hipError_t launch_idx_offset(int32_t* idx, int Bc, int t, int C, int Tc, hipStream_t st) {
   const size_t tot = static_cast<size_t>(Bc) * t;
   hipLaunchKernelGGL(k_idx_offset, dim3((tot + 255) / 256), dim3(256), 0, st, idx, Bc, t, C, Tc);
+  return hipGetLastError();
+}
+
+// Protected keys ("Thought-Aware KV Cache Compaction ...", section 2C: pivot
+// tokens kept exactly, with zero bias, and the rest of the budget spread over
+// the others).  One workgroup per head scans the caller's mask in order: the
+// first pp = min(count, t - 1) marked keys are listed in plist and marked in
+// emask, so the fitted part always keeps at least one key; marks beyond them
+// are dropped (status |= 32).  tv[b] = t - pp.  grid (B), block kSelThreads.
+__global__ __launch_bounds__(kSelThreads) void k_protect_prep(const uint8_t* __restrict__ mask,
+                                                              uint8_t* __restrict__ emask,
+                                                              int32_t* __restrict__ plist,
+                                                              int32_t* __restrict__ tv,
+                                                              int32_t* __restrict__ status, int T,
+                                                              int t) {
+  __shared__ int scratch[64];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const uint8_t* mb = mask + static_cast<size_t>(b) * T;
+  uint8_t* eb = emask + static_cast<size_t>(b) * T;
+  int32_t* pl = plist + static_cast<size_t>(b) * t;
+  const int chunk = (T + kSelThreads - 1) / kSelThreads;
+  const int c0 = min(T, tid * chunk), c1 = min(T, c0 + chunk);
+  int cnt = 0;
+  for (int j = c0; j < c1; ++j) cnt += mb[j] != 0;
+  int total;
+  int pos = block_exclusive_scan(cnt, scratch, &total);
+  const int cap = t - 1;
+  for (int j = c0; j < c1; ++j) {
+    const bool m = mb[j] != 0 && pos < cap;
+    if (m) pl[pos] = j;
+    pos += mb[j] != 0;
+    eb[j] = m;
+  }
+  if (tid == 0) {
+    const int pp = min(total, cap);
+    tv[b] = t - pp;
+    if (total > cap && status) status[b] |= 32;
+  }
+}
+
+hipError_t launch_protect_prep(const uint8_t* mask, uint8_t* emask, int32_t* plist, int32_t* tv,
+                               int32_t* status, int B, int T, int t, hipStream_t st) {
+  hipLaunchKernelGGL(k_protect_prep, dim3(B), dim3(kSelThreads), 0, st, mask, emask, plist, tv,
+                     status, T, t);
+  return hipGetLastError();
+}
+
+// Slots a in [tv[b], t) of head b hold protected key plist[b][a - tv[b]]:
+// out_K = K row (bytes), out_V = V row as float, bias 0, idx = position.
+// grid (ceil(t*D/256), B).
+template <class In>
+__global__ void k_fill_protected(const int32_t* __restrict__ plist, const int32_t* __restrict__ tv,
+                                 const In* __restrict__ K, const In* __restrict__ V,
+                                 In* __restrict__ out_K, float* __restrict__ out_V,
+                                 float* __restrict__ out_bias, int32_t* __restrict__ out_idx,
+                                 int T, int t, int D) {
+  const int b = blockIdx.y;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  const int a = e / D, c = e % D, a0 = tv[b];
+  if (a >= t || a < a0) return;
+  const int j = plist[static_cast<size_t>(b) * t + (a - a0)];
+  const size_t src = (static_cast<size_t>(b) * T + j) * D + c;
+  const size_t dst = (static_cast<size_t>(b) * t + a) * D + c;
+  out_K[dst] = K[src];
+  out_V[dst] = to_f32<In>(V[src]);
+  if (c == 0) {
+    out_bias[static_cast<size_t>(b) * t + a] = 0.f;
+    if (out_idx) out_idx[static_cast<size_t>(b) * t + a] = j;
+  }
+}
+
+hipError_t launch_fill_protected(const int32_t* plist, const int32_t* tv, const void* K,
+                                 const void* V, void* out_K, float* out_V, float* out_bias,
+                                 int32_t* out_idx, int B, int T, int t, int D, bool bf16,
+                                 hipStream_t st) {
+  const dim3 grid((static_cast<size_t>(t) * D + 255) / 256, B);
+  if (bf16)
+    hipLaunchKernelGGL(k_fill_protected<bf16_t>, grid, dim3(256), 0, st, plist, tv,
+                       static_cast<const bf16_t*>(K), static_cast<const bf16_t*>(V),
+                       static_cast<bf16_t*>(out_K), out_V, out_bias, out_idx, T, t, D);
+  else
+    hipLaunchKernelGGL(k_fill_protected<float>, grid, dim3(256), 0, st, plist, tv,
+                       static_cast<const float*>(K), static_cast<const float*>(V),
+                       static_cast<float*>(out_K), out_V, out_bias, out_idx, T, t, D);
   return hipGetLastError();
 }
 

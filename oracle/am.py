@@ -277,6 +277,32 @@ def compact_ragged(Qs, Ks, Vs, budgets, agg: str = "rms",
     return out
 
 
+def compact_protected(Q, K, V, t: int, protect, agg: str = "rms",
+                      ridge_rel: float = DEFAULT_RIDGE_REL):
+    """Protected (pivot) keys, "Thought-Aware KV Cache Compaction ...",
+    section 2C: the marked keys are kept exactly with zero bias and the rest of
+    the budget goes to the other keys.  At most t - 1 keys are protected (the
+    first by position), so at least one slot is fitted.  The unprotected keys
+    R form their own block: they are compacted to t - |P| slots against their
+    own log-sum-exp and output (the protected block is exact, so by the block
+    decomposition of the main objective the fitted part has to match R alone).
+    Slots: the fitted part first (ascending), then the protected keys
+    (ascending)."""
+    Q, K, V = (np.asarray(a, dtype=np.float64) for a in (Q, K, V))
+    T = K.shape[0]
+    if not 1 <= t <= T:
+        raise ValueError("t must lie in [1, T]")
+    marked = np.flatnonzero(np.asarray(protect, dtype=bool))
+    P = marked[:t - 1]
+    R = np.setdiff1d(np.arange(T), P)
+    r = compact(Q, K[R], V[R], t - P.size, agg, ridge_rel)
+    idx = np.concatenate([R[r["idx"]], P])
+    return {"idx": idx, "Ck": K[idx], "beta": np.concatenate([r["beta"], np.zeros(P.size)]),
+            "w": np.concatenate([r["w"], np.ones(P.size)]),
+            "Cv": np.concatenate([r["Cv"], V[P]]), "n_protected": int(P.size),
+            "dropped": int(marked.size - P.size), "rest": r}
+
+
 def attend(Q, K, V, bias=None):
     """softmax(Q K^T + bias) V in float64 (the consumer's attention)."""
     s = np.asarray(Q, float) @ np.asarray(K, float).T

@@ -272,3 +272,77 @@ def test_ragged_equal_budgets_is_bitwise_compact_and_clamps():
     st = c.status.cpu().numpy()
     assert st[0] == 16 and st[1] == 0 and st[2] == 0
     assert (c.idx[0, 1:] == -1).all() and c.idx[0, 0] >= 0
+
+
+@pytest.mark.parametrize("w,frac", [
+    (synth.custom(18, 3, 2400, 192, 128, 90, "bf16", "clusters"), 0.01),
+    (synth.custom(19, 2, 1000, 64, 64, 48, "f32", "sinks"), 0.02),
+], ids=["bf16", "f32_d64"])
+def test_protected_keys_match_oracle(w, frac):
+    """kvc_compact_protected against the oracle: protected slots exact (bias 0),
+    the fitted part against the oracle's compaction of the unprotected keys
+    (their own lse, output and importance; protected keys carry importance 0)."""
+    import torch
+    import kv_cache_compaction_head_amd as kvc
+    data = synth.batch(w)
+    rng = np.random.default_rng(w.cfg)
+    prot = rng.random((w.B, w.T)) < frac
+    prot[:, 0] = True                      # a sink-like first token
+    Q, K, V = (to_device(data[k]) for k in ("Q", "K", "V"))
+    res = kvc.compact_protected(Q, K, V, w.t, torch.from_numpy(prot))
+    torch.cuda.synchronize()
+    inter = {k: v.cpu().numpy() for k, v in kvc.intermediates(res).items()}
+    idx = res.idx.cpu().numpy().astype(np.int64)
+    bias = res.bias.cpu().numpy().astype(np.float64)
+    vals = res.values.cpu().numpy().astype(np.float64)
+    st = res.status.cpu().numpy()
+    for h in range(w.B):
+        P = np.flatnonzero(prot[h])
+        assert P.size <= w.t - 1
+        R = np.flatnonzero(~prot[h])
+        tb = w.t - P.size
+        Kf, Vf = synth.to_f64(data["K"][h]), synth.to_f64(data["V"][h])
+        assert np.array_equal(idx[h, tb:], P)
+        assert np.all(bias[h, tb:] == 0.0)
+        assert np.array_equal(vals[h, tb:], Vf[P])
+        assert np.array_equal(res.keys[h, tb:].float().cpu().numpy().astype(np.float64), Kf[P])
+        assert np.all(inter["imp"][h][P] == 0.0)
+        loc = np.searchsorted(R, idx[h, :tb])
+        assert np.array_equal(R[loc], idx[h, :tb])
+        g = {"keys": res.keys[h:h + 1, :tb].cpu(), "bias": bias[h:h + 1, :tb],
+             "values": vals[h:h + 1, :tb], "idx": loc[None], "status": st[h:h + 1],
+             "lse": inter["lse"][h:h + 1], "O": inter["O"][h:h + 1],
+             "imp": inter["imp"][h:h + 1][:, R], "w": inter["w"][h:h + 1, :tb]}
+        hd = {"Q": data["Q"][h:h + 1], "K": data["K"][h:h + 1][:, R],
+              "V": data["V"][h:h + 1][:, R]}
+        err = compare_head(g, 0, hd, tb, _tol(w))
+        print(w.name, "head", h, "protected", P.size,
+              {k: (float(f"{v:.3g}") if isinstance(v, float) else v) for k, v in err.items()},
+              flush=True)
+        Qh = synth.to_f64(data["Q"][h])
+        ref = orc.compact_protected(Qh, Kf, Vf, w.t, prot[h])
+        o_gpu = orc.attend(Qh, res.keys[h].float().cpu().numpy().astype(np.float64), vals[h],
+                           bias[h])
+        o_ref = orc.attend(Qh, ref["Ck"], ref["Cv"], ref["beta"])
+        assert orc.rel_l2(o_gpu, o_ref) <= _tol(w)
+
+
+def test_protected_none_is_bitwise_compact_and_overflow_flags():
+    import torch
+    import kv_cache_compaction_head_amd as kvc
+    w = synth.custom(20, 2, 800, 96, 128, 40, "bf16", "normal")
+    data = synth.batch(w)
+    Q, K, V = (to_device(data[k]) for k in ("Q", "K", "V"))
+    a = kvc.compact(Q, K, V, w.t)
+    none = torch.zeros((w.B, w.T), dtype=torch.uint8)
+    b = kvc.compact_protected(Q, K, V, w.t, none)
+    torch.cuda.synchronize()
+    for k in ("keys", "bias", "values", "idx", "status"):
+        assert torch.equal(getattr(a, k), getattr(b, k)), k
+    many = torch.zeros((w.B, w.T), dtype=torch.uint8)
+    many[1, ::10] = 1                        # 80 marks > t - 1 = 39
+    c = kvc.compact_protected(Q, K, V, w.t, many)
+    torch.cuda.synchronize()
+    st = c.status.cpu().numpy()
+    assert st[0] == 0 and st[1] == 32
+    assert c.idx[1, 1:].cpu().tolist() == list(range(0, 390, 10))

@@ -468,3 +468,59 @@ def test_ragged_heads_are_independent_compactions_and_padding_is_inert():
         padded = orc.attend(Qn, r["Ck"][h], r["Cv"][h], r["beta"][h])
         trimmed = orc.attend(Qn, own["Ck"], own["Cv"], own["beta"])
         assert np.allclose(padded, trimmed, atol=1e-14, rtol=0)
+
+
+# --------------------------------------------------- protected keys (f4)
+def test_protected_none_is_compact_and_keep_rest_is_exact():
+    Q, K, V = _rand(80, 20, 8, scale=0.5), _rand(81, 50, 8), _rand(82, 50, 3)
+    r0 = orc.compact(Q, K, V, 12)
+    rp = orc.compact_protected(Q, K, V, 12, np.zeros(50, bool))
+    for k in ("idx", "beta", "Cv"):
+        assert np.array_equal(r0[k], rp[k])
+    # protect 8 keys and keep all 42 others: the compact cache is the cache
+    prot = np.zeros(50, bool)
+    prot[[1, 5, 9, 20, 33, 34, 40, 49]] = True
+    r = orc.compact_protected(Q, K, V, 50, prot)
+    assert sorted(r["idx"]) == list(range(50))
+    assert np.allclose(r["beta"], 0.0, atol=1e-9)
+    Qn = _rand(83, 7, 8, scale=0.5)
+    assert np.allclose(orc.attend(Qn, r["Ck"], r["Cv"], r["beta"]), orc.attend(Qn, K, V),
+                       atol=1e-8)
+
+
+def test_protected_keys_exact_and_rest_fitted_on_its_own_block():
+    """Protected slots: the key and value rows as they are with bias 0 (w = 1);
+    the fitted part equals compact() of the unprotected keys alone; the rest's
+    log-sum-exp and the protected block's combine to the whole cache's; and
+    attention over the result is the two blocks' attentions mixed by mass."""
+    Q, K, V = _rand(84, 30, 8, scale=0.5), _rand(85, 90, 8), _rand(86, 90, 3)
+    prot = np.zeros(90, bool)
+    prot[[3, 17, 18, 60, 88]] = True
+    t = 20
+    r = orc.compact_protected(Q, K, V, t, prot)
+    P = np.flatnonzero(prot)
+    R = np.flatnonzero(~prot)
+    assert r["n_protected"] == 5 and r["dropped"] == 0
+    assert np.array_equal(r["idx"][15:], P)
+    assert np.array_equal(r["Cv"][15:], V[P]) and np.all(r["beta"][15:] == 0)
+    own = orc.compact(Q, K[R], V[R], 15)
+    assert np.array_equal(r["idx"][:15], R[own["idx"]])
+    assert np.allclose(r["Cv"][:15], own["Cv"], atol=1e-12)
+    assert np.allclose(np.logaddexp(r["rest"]["lse"], orc.row_lse(Q, K[P])), orc.row_lse(Q, K),
+                       atol=1e-13)
+    Qn = _rand(87, 6, 8, scale=0.5)
+    za = np.exp(Qn @ own["Ck"].T + own["beta"]).sum(axis=1)[:, None]
+    zb = np.exp(Qn @ K[P].T).sum(axis=1)[:, None]
+    mix = (za * orc.attend(Qn, own["Ck"], own["Cv"], own["beta"]) +
+           zb * orc.attend(Qn, K[P], V[P])) / (za + zb)
+    assert np.allclose(orc.attend(Qn, r["Ck"], r["Cv"], r["beta"]), mix, atol=1e-13)
+
+
+def test_protected_overflow_keeps_first_t_minus_one():
+    Q, K, V = _rand(88, 10, 4, scale=0.5), _rand(89, 30, 4), _rand(90, 30, 2)
+    prot = np.zeros(30, bool)
+    prot[[2, 4, 6, 8, 10, 12]] = True
+    r = orc.compact_protected(Q, K, V, 4, prot)
+    assert r["n_protected"] == 3 and r["dropped"] == 3
+    assert list(r["idx"][1:]) == [2, 4, 6]
+    assert r["idx"][0] not in (2, 4, 6)

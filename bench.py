@@ -28,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
-PEAK_F32_TFLOPS = 157.3      # MI355X fp32 MFMA
+PEAK_F32_TFLOPS = 157.3      # MI355X fp32 (vector and MFMA)
 PEAK_F64_TFLOPS = 78.6       # MI355X fp64 (vector and matrix)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_nnls_sweep_T32k_50x_hbm_traffic.md")
@@ -46,10 +46,12 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--variant", default="compact",
-                    choices=["compact", "chunked", "ragged", "protected"],
+                    choices=["compact", "chunked", "ragged", "protected", "attend"],
                     help="chunked: the cache cut into --chunks equal chunks, t/chunks kept per "
                          "chunk; ragged: per-head budgets from 0.5t to 1.5t (mean t); "
-                         "protected: 1%% of the keys (and the first) kept exactly")
+                         "protected: 1%% of the keys (and the first) kept exactly; "
+                         "attend: the evaluation kernel over the whole cache plus an appended "
+                         "block of 1024 tokens, for the held-out queries")
     ap.add_argument("--chunks", type=int, default=4)
     return ap.parse_args()
 
@@ -113,6 +115,41 @@ def traffic_record():
     return rec if rec.get("fit_hip_sha256") == sha else None
 
 
+def bench_attend(args, torch, kvc, w, data, dev):
+    """kvc_attend over [K; K_fixed] for the held-out queries: float32 vector
+    arithmetic, 4 m (T + f) d flops per head (scores and the weighted sum)."""
+    rng = np.random.default_rng(7)
+    f = 1024
+    import synth
+    Kf = dev(synth.round_bf16_bits(rng.standard_normal((w.B, f, w.d))))
+    Vf = dev(synth.round_bf16_bits(rng.standard_normal((w.B, f, w.d))))
+    Qh, K, V = dev(data["Qhold"]), dev(data["K"]), dev(data["V"])
+    for _ in range(args.warmup):
+        kvc.attend(Qh, K, V, None, Kf, Vf)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        kvc.attend(Qh, K, V, None, Kf, Vf)
+    b.record()
+    b.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    m = w.n_hold
+    flops = 4.0 * m * (w.T + f) * w.d * w.B
+    ach = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "attention evaluation over cache + appended block: query-key pairs/s",
+        "value": m * (w.T + f) * w.B / (ms * 1e-3), "unit": "query-key pairs/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "variant": "attend", "B": w.B, "m": m, "T": w.T,
+                   "appended": f, "d": w.d},
+        "roofline": {"bound": "alu", "kernel": "k_attend", "achieved": round(ach, 3),
+                     "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_F32_TFLOPS, 5), "traffic": None}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -133,6 +170,9 @@ def main():
             return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
         return torch.from_numpy(a).cuda()
 
+    if args.variant == "attend":
+        bench_attend(args, torch, kvc, w, data, dev)
+        return
     Q, K, V = dev(data["Q"]), dev(data["K"]), dev(data["V"])
     p = kvc.make_params(w.B, w.T, w.n, w.d, w.t, w.dtype)
     variant = {"workload": w.name}

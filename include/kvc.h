@@ -181,6 +181,33 @@ int kvc_compact_chunked(const kvc_params_t* p, int64_t n_chunks, const void* Q_r
                         int32_t* out_idx, int32_t* out_status, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
 
+/* Attention over a cache followed by an appended fixed block, for queries Q:
+ *   out_i = softmax_j(q_i . k_j + bias_j) v_j over the t1 keys of block 1
+ *   (with bias1; e.g. a compact cache C_k, beta, C_v) and then the t2 keys of
+ *   block 2 (bias 0; e.g. the fixed or future tokens appended after it),
+ *   out_lse_i = log sum_j exp(q_i . k_j + bias_j).
+ * This is the consumer's side of the main objective ("for any query and any
+ * fixed block appended after the compact cache"): with the original cache as
+ * block 1 it gives the reference, with the compact cache the compacted
+ * attention, on the GPU.  float32 arithmetic, online softmax.
+ *   Q      [B, m, d]   in_dtype
+ *   K1     [B, t1, d]  in_dtype;  bias1 [B, t1] float32 or NULL (zeros; -inf
+ *                      gives a key zero weight);  V1 [B, t1, d] float32 when
+ *                      v1_f32 = 1 (fitted values), else in_dtype
+ *   K2, V2 [B, t2, d]  in_dtype; may be NULL when t2 = 0
+ *   out    [B, m, d]   float32;  out_lse [B, m] float64 or NULL
+ * t1 >= 0, t2 >= 0, t1 + t2 >= 1.  Returns KVC_OK once enqueued. */
+typedef struct {
+  int64_t B, m, d, t1, t2;
+  int32_t in_dtype;  /* kvc_dtype_t of Q, K1, K2, V2 (and V1 unless v1_f32) */
+  int32_t v1_f32;    /* 1: V1 is float32; 0: V1 has in_dtype */
+  int32_t reserved;  /* must be 0 */
+  int32_t reserved2; /* must be 0 */
+} kvc_attend_params_t;
+int kvc_attend(const kvc_attend_params_t* p, const void* Q, const void* K1, const float* bias1,
+               const void* V1, const void* K2, const void* V2, float* out, double* out_lse,
+               hipStream_t stream);
+
 /* Where the intermediates of the last call live inside its workspace (byte
  * offsets), for inspection after the stream completes:
  *   lse [B, n] f64; O [B, n, d] f32 (full-cache output); imp [B, T] f32 holding

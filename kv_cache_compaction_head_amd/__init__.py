@@ -15,7 +15,7 @@ from ._lib import (KVC_AGG_MEAN, KVC_AGG_RMS, KVC_BF16, KVC_F32, STATUS_NNLS_CAP
                    STATUS_NONFINITE, STATUS_NOT_SPD, Params, load, make_params, strerror,
                    workspace_bytes, workspace_bytes_chunked, workspace_layout)
 
-__all__ = ["compact", "compact_chunked", "compact_ragged", "compact_protected", "fit", "Compacted", "intermediates", "load", "make_params",
+__all__ = ["compact", "compact_chunked", "compact_ragged", "compact_protected", "attend", "fit", "Compacted", "intermediates", "load", "make_params",
            "workspace_bytes", "workspace_bytes_chunked", "workspace_layout", "strerror", "Params"]
 
 
@@ -211,6 +211,44 @@ def fit(Q, K, V, idx, *, ridge_rel: float = 1e-6, max_nnls_iters: int = 32,
     _lib.check(rc)
     keys = None
     return Compacted(keys, bias, values, idx, status, ws, p)
+
+
+def attend(Q, K1, V1, bias1=None, K2=None, V2=None, *, stream=None):
+    """Attention of Q [B,m,d] over block 1 (K1, V1, optional per-key bias1)
+    followed by block 2 (K2, V2, no bias): returns (out [B,m,d] float32,
+    lse [B,m] float64).  K1, K2, V2 and Q share one dtype (bfloat16 or
+    float32); V1 may also be float32 (fitted values)."""
+    import torch
+    if Q.dim() != 3 or K1.dim() != 3 or V1.dim() != 3:
+        raise ValueError("expected Q [B,m,d], K1 and V1 [B,t1,d]")
+    B, m, d = Q.shape
+    t1 = K1.shape[1]
+    if Q.dtype not in (torch.bfloat16, torch.float32) or K1.dtype != Q.dtype:
+        raise ValueError("Q and K1 must share one dtype: bfloat16 or float32")
+    if V1.shape != K1.shape or V1.dtype not in (Q.dtype, torch.float32):
+        raise ValueError("V1 must match K1's shape, in Q's dtype or float32")
+    t2 = 0 if K2 is None else K2.shape[1]
+    if t2:
+        if K2.dtype != Q.dtype or V2 is None or V2.dtype != Q.dtype or V2.shape != K2.shape:
+            raise ValueError("K2 and V2 must be [B,t2,d] in Q's dtype")
+    if bias1 is not None and (bias1.dtype != torch.float32 or tuple(bias1.shape) != (B, t1)):
+        raise ValueError("bias1 must be float32 [B, t1]")
+    p = _lib.AttendParams()
+    p.B, p.m, p.d, p.t1, p.t2 = B, m, d, t1, t2
+    p.in_dtype = KVC_BF16 if Q.dtype == torch.bfloat16 else KVC_F32
+    p.v1_f32 = 1 if (V1.dtype == torch.float32 and Q.dtype != torch.float32) else 0
+    dev = Q.device
+    Q, K1, V1 = Q.contiguous(), K1.contiguous(), V1.contiguous()
+    out = torch.empty((B, m, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, m), dtype=torch.float64, device=dev)
+    null = ctypes.c_void_p(None)
+    b1 = _vp(bias1.contiguous()) if bias1 is not None else null
+    k2 = _vp(K2.contiguous()) if t2 else null
+    v2 = _vp(V2.contiguous()) if t2 else null
+    rc = load().kvc_attend(ctypes.byref(p), _vp(Q), _vp(K1), b1, _vp(V1), k2, v2, _vp(out),
+                           _vp(lse), _stream(stream, dev))
+    _lib.check(rc)
+    return out, lse
 
 
 def intermediates(res: Compacted) -> dict:

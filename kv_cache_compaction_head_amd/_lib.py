@@ -17,7 +17,7 @@ KVC_AGG_RMS, KVC_AGG_MEAN = 0, 1
 
 EXPORTS = ("kvc_params_default", "kvc_workspace_bytes", "kvc_compact", "kvc_fit",
            "kvc_workspace_bytes_chunked", "kvc_compact_chunked", "kvc_compact_ragged",
-           "kvc_compact_protected",
+           "kvc_compact_protected", "kvc_attend",
            "kvc_workspace_layout", "kvc_profile_enable", "kvc_profile_read", "kvc_strerror")
 STAGES = {"score_lse": 0, "expweight": 1, "select": 2, "ps": 3, "gram": 4, "nnls": 5,
           "value": 6, "total": 7}
@@ -28,6 +28,13 @@ class Params(ctypes.Structure):
                 ("d", ctypes.c_int64), ("t", ctypes.c_int64), ("in_dtype", ctypes.c_int32),
                 ("agg", ctypes.c_int32), ("ridge_rel", ctypes.c_double),
                 ("max_nnls_iters", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class AttendParams(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("m", ctypes.c_int64), ("d", ctypes.c_int64),
+                ("t1", ctypes.c_int64), ("t2", ctypes.c_int64), ("in_dtype", ctypes.c_int32),
+                ("v1_f32", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("reserved2", ctypes.c_int32)]
 
 
 class WsLayout(ctypes.Structure):
@@ -68,6 +75,9 @@ def load() -> ctypes.CDLL:
     lib.kvc_compact_protected.argtypes = [P, vp, vp, vp, vp, vp, f32p, f32p, i32p, i32p, vp,
                                           ctypes.c_size_t, vp]
     lib.kvc_compact_protected.restype = ctypes.c_int
+    lib.kvc_attend.argtypes = [ctypes.POINTER(AttendParams), vp, vp, f32p, vp, vp, vp, f32p, vp,
+                               vp]
+    lib.kvc_attend.restype = ctypes.c_int
     lib.kvc_workspace_layout.argtypes = [P, ctypes.POINTER(WsLayout)]
     lib.kvc_workspace_layout.restype = ctypes.c_int
     lib.kvc_profile_enable.argtypes = [ctypes.c_uint32]

@@ -62,6 +62,11 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
                       int max_iters, int qg, hipStream_t st);
 // kept indices of (head, chunk) b' made global: idx[b'][a] += (b' mod C) * Tc
 hipError_t launch_idx_offset(int32_t* idx, int Bc, int t, int C, int Tc, hipStream_t st);
+// Attention over block 1 (K1, V1 with a per-key bias) then block 2 (K2, V2).
+template <class In, int D>
+hipError_t launch_attend(const void* Q, const void* K1, const float* bias, const void* V1,
+                         bool v1_f32, const void* K2, const void* V2, float* out,
+                         double* out_lse, int B, int m, int t1, int t2, hipStream_t st);
 // Event-pair instrumentation (defined with the C ABI): no-op unless enabled.
 void prof_mark(int stage, bool end, hipStream_t st);
 }  // namespace kvc

@@ -313,6 +313,22 @@ def attend(Q, K, V, bias=None):
     return (e / e.sum(axis=1, keepdims=True)) @ np.asarray(V, float)
 
 
+def attend_appended(Q, K1, V1, bias1, K2, V2):
+    """Attention over a cache (K1, V1, per-key bias1) followed by an appended
+    block (K2, V2) with no bias: the setting of the main objective, where a
+    compact cache must keep the output for any fixed or future block appended
+    after it.  Returns (output, lse)."""
+    K = np.vstack([np.asarray(K1, float), np.asarray(K2, float)])
+    V = np.vstack([np.asarray(V1, float), np.asarray(V2, float)])
+    b1 = np.zeros(len(K1)) if bias1 is None else np.asarray(bias1, float)
+    bias = np.concatenate([b1, np.zeros(len(K2))])
+    s = np.asarray(Q, float) @ K.T + bias[None, :]
+    mx = s.max(axis=1, keepdims=True)
+    e = np.exp(s - mx)
+    z = e.sum(axis=1, keepdims=True)
+    return (e / z) @ V, (mx + np.log(z))[:, 0]
+
+
 def rel_l2(a, b) -> float:
     a = np.asarray(a, float)
     b = np.asarray(b, float)

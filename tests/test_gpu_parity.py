@@ -346,3 +346,76 @@ def test_protected_none_is_bitwise_compact_and_overflow_flags():
     st = c.status.cpu().numpy()
     assert st[0] == 0 and st[1] == 32
     assert c.idx[1, 1:].cpu().tolist() == list(range(0, 390, 10))
+
+
+@pytest.mark.parametrize("dtype,d,t1,t2,m", [("bf16", 128, 700, 37, 130), ("f32", 64, 65, 0, 64),
+                                             ("bf16", 64, 0, 200, 1), ("f32", 128, 1, 1, 300)])
+def test_attend_matches_oracle(dtype, d, t1, t2, m):
+    """kvc_attend: the float32 online-softmax kernel against the float64
+    definition, with a bias that includes -inf (a zero-weight key)."""
+    import torch
+    import kv_cache_compaction_head_amd as kvc
+    rng = np.random.default_rng(t1 * 7 + t2)
+    B = 2
+
+    def arr(*shape, scale=1.0):
+        x = rng.standard_normal(shape) * scale
+        return synth.round_bf16_bits(x) if dtype == "bf16" else x.astype(np.float32)
+
+    Q, K1, K2, V2 = arr(B, m, d, scale=d ** -0.5), arr(B, t1, d), arr(B, t2, d), arr(B, t2, d)
+    V1 = rng.standard_normal((B, t1, d)).astype(np.float32)
+    b1 = (rng.standard_normal((B, t1)) * 2).astype(np.float32)
+    if t1 > 3:
+        b1[:, 3] = -np.inf
+    out, lse = kvc.attend(to_device(Q), to_device(K1), torch.from_numpy(V1).cuda(),
+                          torch.from_numpy(b1).cuda(),
+                          to_device(K2) if t2 else None, to_device(V2) if t2 else None)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy().astype(np.float64), lse.cpu().numpy()
+    f = synth.to_f64 if dtype == "bf16" else (lambda x: x.astype(np.float64))
+    for h in range(B):
+        o_ref, l_ref = orc.attend_appended(f(Q[h]), f(K1[h]), V1[h].astype(np.float64),
+                                           b1[h].astype(np.float64), f(K2[h]), f(V2[h]))
+        assert orc.rel_l2(out[h], o_ref) < 2e-6
+        assert np.max(np.abs(lse[h] - l_ref)) < 1e-4
+
+
+def test_compacted_cache_with_appended_block_on_gpu():
+    """The evaluation path end to end: compact on the GPU, then attend over
+    [compact cache; appended block] and [full cache; appended block] with
+    kvc_attend.  Each equals the float64 value of the same cache within float32
+    rounding, and the compaction error with the block appended stays within
+    the oracle's own error for the same setting (x1.05)."""
+    import torch
+    import kv_cache_compaction_head_amd as kvc
+    w = synth.custom(21, 2, 3000, 256, 128, 150, "bf16", "clusters", n_hold=96)
+    data = synth.batch(w)
+    Q, K, V = (to_device(data[k]) for k in ("Q", "K", "V"))
+    res = kvc.compact(Q, K, V, w.t)
+    rng = np.random.default_rng(5)
+    Kf = synth.round_bf16_bits(rng.standard_normal((w.B, 64, w.d)))
+    Vf = synth.round_bf16_bits(rng.standard_normal((w.B, 64, w.d)))
+    Qh = to_device(data["Qhold"])
+    oc, _ = kvc.attend(Qh, res.keys, res.values, res.bias, to_device(Kf), to_device(Vf))
+    of, _ = kvc.attend(Qh, K, V, None, to_device(Kf), to_device(Vf))
+    torch.cuda.synchronize()
+    oc, of = oc.cpu().numpy().astype(np.float64), of.cpu().numpy().astype(np.float64)
+    for h in range(w.B):
+        Qn = synth.to_f64(data["Qhold"][h])
+        Kh, Vh = synth.to_f64(data["K"][h]), synth.to_f64(data["V"][h])
+        full_ref, _ = orc.attend_appended(Qn, Kh, Vh, None, synth.to_f64(Kf[h]),
+                                          synth.to_f64(Vf[h]))
+        assert orc.rel_l2(of[h], full_ref) < 2e-6
+        ck = res.keys[h].float().cpu().numpy().astype(np.float64)
+        comp_ref, _ = orc.attend_appended(Qn, ck, res.values[h].cpu().numpy().astype(np.float64),
+                                          res.bias[h].cpu().numpy().astype(np.float64),
+                                          synth.to_f64(Kf[h]), synth.to_f64(Vf[h]))
+        assert orc.rel_l2(oc[h], comp_ref) < 2e-6
+        ref = orc.compact(synth.to_f64(data["Q"][h]), Kh, Vh, w.t)
+        oracle_err = orc.rel_l2(orc.attend_appended(Qn, ref["Ck"], ref["Cv"], ref["beta"],
+                                                    synth.to_f64(Kf[h]), synth.to_f64(Vf[h]))[0],
+                                full_ref)
+        gpu_err = orc.rel_l2(oc[h], of[h])
+        print(f"head {h}: appended-block compaction error gpu {gpu_err:.4g} oracle {oracle_err:.4g}",
+              flush=True)
+        assert gpu_err <= oracle_err * 1.05 + 1e-5

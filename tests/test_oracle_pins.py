@@ -524,3 +524,42 @@ def test_protected_overflow_keeps_first_t_minus_one():
     assert r["n_protected"] == 3 and r["dropped"] == 3
     assert list(r["idx"][1:]) == [2, 4, 6]
     assert r["idx"][0] not in (2, 4, 6)
+
+
+# ------------------------------------------ appended fixed block (f4, P7)
+def test_exact_compaction_survives_any_appended_block():
+    """Duplicated keys fitted exactly (w = multiplicity, C_v = mean over the
+    copies) match output and mass for every query; by the block decomposition
+    the attention then stays exact with any block appended after the cache."""
+    rng = np.random.default_rng(91)
+    t, d = 6, 5
+    base = rng.standard_normal((t, d))
+    mult = np.array([2, 1, 4, 3, 1, 2])
+    rows = rng.permutation(np.repeat(np.arange(t), mult))
+    K, V = base[rows], rng.standard_normal((rows.size, 3))
+    first = np.sort([np.flatnonzero(rows == j)[0] for j in range(t)])
+    Q = rng.standard_normal((20, d)) * 0.5
+    w, beta, Cv, _ = orc.fit(Q, K, V, first, ridge_rel=1e-12)
+    Kf, Vf = rng.standard_normal((7, d)), rng.standard_normal((7, 3))
+    Qn = rng.standard_normal((9, d)) * 0.5
+    o_c, l_c = orc.attend_appended(Qn, K[first], Cv, beta, Kf, Vf)
+    o_f, l_f = orc.attend_appended(Qn, K, V, None, Kf, Vf)
+    assert np.allclose(o_c, o_f, atol=1e-7) and np.allclose(l_c, l_f, atol=1e-7)
+    # and the lse is the whole concatenation's (block identity)
+    assert np.allclose(l_f, np.logaddexp(orc.row_lse(Qn, K), orc.row_lse(Qn, Kf)), atol=1e-13)
+
+
+def test_attend_appended_matches_scalar_loops():
+    rng = np.random.default_rng(92)
+    Q, K1, V1 = rng.standard_normal((3, 4)), rng.standard_normal((5, 4)), rng.standard_normal((5, 2))
+    K2, V2 = rng.standard_normal((2, 4)), rng.standard_normal((2, 2))
+    b1 = np.array([0.5, -np.inf, 0.0, 1.5, -2.0])
+    o, lse = orc.attend_appended(Q, K1, V1, b1, K2, V2)
+    for i in range(3):
+        s = [math.fsum(Q[i, c] * K1[j, c] for c in range(4)) + b1[j] for j in range(5)]
+        s += [math.fsum(Q[i, c] * K2[j, c] for c in range(4)) for j in range(2)]
+        vs = list(V1) + list(V2)
+        z = math.fsum(math.exp(x) for x in s)
+        assert abs(lse[i] - math.log(z)) < 1e-13
+        for c in range(2):
+            assert abs(o[i, c] - math.fsum(math.exp(x) * v[c] for x, v in zip(s, vs)) / z) < 1e-13

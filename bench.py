@@ -46,8 +46,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--variant", default="compact",
-                    choices=["compact", "chunked", "ragged", "protected", "attend"],
-                    help="chunked: the cache cut into --chunks equal chunks, t/chunks kept per "
+                    choices=["compact", "omp", "chunked", "ragged", "protected", "attend"],
+                    help="omp: keys chosen by orthogonal matching pursuit; chunked: the cache cut into --chunks equal chunks, t/chunks kept per "
                          "chunk; ragged: per-head budgets from 0.5t to 1.5t (mean t); "
                          "protected: 1%% of the keys (and the first) kept exactly; "
                          "attend: the evaluation kernel over the whole cache plus an appended "
@@ -201,6 +201,15 @@ def main():
 
         def call():
             return kvc.compact_ragged(Q, K, V, tv, workspace=ws)
+    elif args.variant == "omp":
+        ws = torch.empty(kvc.workspace_bytes_omp(p), dtype=torch.uint8, device="cuda")
+        variant.update(variant="omp")
+
+        def oracle_head(orc, h, Qh, Kh, Vh):
+            orc.compact_omp(Qh, Kh, Vh, w.t)
+
+        def call():
+            return kvc.compact_omp(Q, K, V, w.t, workspace=ws)
     elif args.variant == "protected":
         g = torch.Generator().manual_seed(w.cfg)
         prot = (torch.rand((w.B, w.T), generator=g) < 0.01)
@@ -270,21 +279,28 @@ def main():
             "expweight": ("k_expweight", 4.0 * n * T * d * B, mm_peak),
             "nnls": ("k_nnls_sweep", float(fit_flops[0]), PEAK_F64_TFLOPS),
             "value": ("value stage (k_value_sweep)", float(fit_flops[1]), PEAK_F64_TFLOPS)}
+    if args.variant == "omp":
+        # the pursuit's t correlation passes read P (n T float32 per head) once
+        # each, plus P's write and the norms pass: HBM-bound by design
+        work["select"] = ("omp selection (k_ps<float>, k_omp_*)",
+                          float((w.t + 2) * n * T * 4 * B), PEAK_HBM_GBS)
     kernels = []
     for stage, (kname, flops, peak) in work.items():
         if stage not in prof:
             continue
-        ach = flops / (prof[stage] * 1e-3) / 1e12
-        kernels.append({"kernel": kname, "bound": "mfma", "ms": round(prof[stage], 4),
-                        "achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s",
-                        "frac": round(ach / peak, 5)})
+        hbm = peak == PEAK_HBM_GBS
+        ach = flops / (prof[stage] * 1e-3) / (1e9 if hbm else 1e12)
+        kernels.append({"kernel": kname, "bound": "hbm" if hbm else "mfma",
+                        "ms": round(prof[stage], 4), "achieved": round(ach, 3), "peak": peak,
+                        "unit": "GB/s" if hbm else "TFLOP/s", "frac": round(ach / peak, 5)})
     roof = None
     if kernels:
-        dom = max((k for k in kernels if k["kernel"].startswith("k_")), key=lambda k: k["ms"])
+        dom = max((k for k in kernels if k["kernel"].startswith("k_") or k["bound"] == "hbm"),
+                  key=lambda k: k["ms"])
         tr = (traffic_record() if (dom["kernel"] == "k_nnls_sweep" and args.config == 3 and
                                    args.variant == "compact") else None)
         roof = {"bound": dom["bound"], "kernel": dom["kernel"], "achieved": dom["achieved"],
-                "peak": dom["peak"], "unit": "TFLOP/s", "frac": dom["frac"],
+                "peak": dom["peak"], "unit": dom["unit"], "frac": dom["frac"],
                 "traffic": tr["bytes_per_launch"] if tr else None,
                 "traffic_detail": tr,
                 "kernels": kernels, "stage_ms": {k: round(v, 4) for k, v in prof.items()},

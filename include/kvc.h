@@ -132,6 +132,25 @@ int kvc_compact_ragged(const kvc_params_t* p, const int32_t* t_heads, const void
                        int32_t* out_idx, int32_t* out_status, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 
+/* Greedy key selection by orthogonal matching pursuit (the summary's second
+ * key-selection option: choose keys greedily to best satisfy the mass
+ * matching, then fit weights by NNLS).  The dictionary is the whole-cache
+ * softmax weights p_j = P[:, j] (over the reference queries) stored in
+ * float32; the target is the relative mass y = 1.  For t steps: pick the key
+ * not yet chosen with the largest p_j . r / ||p_j|| (float64; ties to the
+ * lower index; keys whose column is all zero only when nothing else is
+ * left), then set r to y minus its orthogonal projection on the chosen
+ * columns.  The chosen set (ascending) then gets kvc_compact's bias and value
+ * fits.  p->agg is ignored.
+ * Cost: t passes over P (n * T * 4 bytes per head each); the workspace holds P
+ * and an n x t basis per head: use kvc_workspace_bytes_omp.
+ * Arguments and outputs as kvc_compact. */
+size_t kvc_workspace_bytes_omp(const kvc_params_t* p);
+int kvc_compact_omp(const kvc_params_t* p, const void* Q_ref, const void* K, const void* V,
+                    void* out_K, float* out_bias, float* out_V, int32_t* out_idx,
+                    int32_t* out_status, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
 /* Protected keys ("Thought-Aware KV Cache Compaction for Reasoning via
  * Adaptive Attention Matching", section 2C: pivot tokens are kept exactly,
  * with zero bias, and the rest of the budget goes to the other tokens).
@@ -217,6 +236,9 @@ int kvc_attend(const kvc_attend_params_t* p, const void* Q, const void* K1, cons
  *   (factorizations and solves) and the value solve performed for each head. */
 typedef struct {
   size_t lse, O, imp, w, fit_flops;
+  size_t omp_order; /* [B, t] int32: after kvc_compact_omp, the keys in the
+                       order the pursuit chose them (workspace of
+                       kvc_workspace_bytes_omp) */
 } kvc_ws_layout_t;
 int kvc_workspace_layout(const kvc_params_t* p, kvc_ws_layout_t* out);
 

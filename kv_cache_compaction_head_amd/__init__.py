@@ -13,10 +13,11 @@ import dataclasses
 from . import _lib
 from ._lib import (KVC_AGG_MEAN, KVC_AGG_RMS, KVC_BF16, KVC_F32, STATUS_NNLS_CAP,
                    STATUS_NONFINITE, STATUS_NOT_SPD, Params, load, make_params, strerror,
-                   workspace_bytes, workspace_bytes_chunked, workspace_layout)
+                   workspace_bytes, workspace_bytes_chunked, workspace_bytes_omp,
+                   workspace_layout)
 
-__all__ = ["compact", "compact_chunked", "compact_ragged", "compact_protected", "attend", "fit", "Compacted", "intermediates", "load", "make_params",
-           "workspace_bytes", "workspace_bytes_chunked", "workspace_layout", "strerror", "Params"]
+__all__ = ["compact", "compact_omp", "compact_chunked", "compact_ragged", "compact_protected", "attend", "fit", "Compacted", "intermediates", "load", "make_params",
+           "workspace_bytes", "workspace_bytes_chunked", "workspace_bytes_omp", "workspace_layout", "strerror", "Params"]
 
 
 @dataclasses.dataclass
@@ -29,6 +30,7 @@ class Compacted:
     status: "object"     # [B] int32, KVC_STATUS_* bits per head
     workspace: "object"  # uint8 device buffer holding the intermediates
     params: Params
+    omp: bool = False    # keys chosen by the greedy pursuit (intermediates: omp_order)
 
 
 def _vp(x):
@@ -90,6 +92,35 @@ def compact(Q, K, V, t: int, *, agg: str = "rms", ridge_rel: float = 1e-6,
                             ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(stream, dev))
     _lib.check(rc)
     return Compacted(keys, bias, values, idx, status, ws, p)
+
+
+def compact_omp(Q, K, V, t: int, *, ridge_rel: float = 1e-6, max_nnls_iters: int = 32,
+                workspace=None, stream=None) -> Compacted:
+    """Compact each head to t keys chosen by orthogonal matching pursuit on
+    the attention mass (t greedy steps), then the same bias and value fits as
+    compact()."""
+    import torch
+    Q, K, V, _ = _prep(Q, K, V)
+    B, n, d = Q.shape
+    T = K.shape[1]
+    dt = "bf16" if Q.dtype == torch.bfloat16 else "f32"
+    p = make_params(B, T, n, d, t, dt, "rms", ridge_rel, max_nnls_iters)
+    dev = Q.device
+    need = workspace_bytes_omp(p)
+    if need == 0:
+        raise ValueError("invalid compaction parameters")
+    ws = _workspace(p, dev, workspace, need)
+    keys = torch.empty((B, t, d), dtype=Q.dtype, device=dev)
+    bias = torch.empty((B, t), dtype=torch.float32, device=dev)
+    values = torch.empty((B, t, d), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, t), dtype=torch.int32, device=dev)
+    status = torch.empty((B,), dtype=torch.int32, device=dev)
+    rc = load().kvc_compact_omp(ctypes.byref(p), _vp(Q), _vp(K), _vp(V), _vp(keys), _vp(bias),
+                                _vp(values), _vp(idx), _vp(status), _vp(ws),
+                                ctypes.c_size_t(ws.numel() * ws.element_size()),
+                                _stream(stream, dev))
+    _lib.check(rc)
+    return Compacted(keys, bias, values, idx, status, ws, p, omp=True)
 
 
 def compact_ragged(Q, K, V, t_heads, *, agg: str = "rms", ridge_rel: float = 1e-6,
@@ -269,4 +300,5 @@ def intermediates(res: Compacted) -> dict:
             "O": view(L.O, B * n * d, torch.float32, (B, n, d)),
             "imp": view(L.imp, B * T, torch.float32, (B, T)),
             "w": view(L.w, B * t, torch.float64, (B, t)),
-            "fit_flops": view(L.fit_flops, B * 2, torch.float64, (B, 2))}
+            "fit_flops": view(L.fit_flops, B * 2, torch.float64, (B, 2)),
+            **({"omp_order": view(L.omp_order, B * t, torch.int32, (B, t))} if res.omp else {})}

@@ -17,7 +17,8 @@ KVC_AGG_RMS, KVC_AGG_MEAN = 0, 1
 
 EXPORTS = ("kvc_params_default", "kvc_workspace_bytes", "kvc_compact", "kvc_fit",
            "kvc_workspace_bytes_chunked", "kvc_compact_chunked", "kvc_compact_ragged",
-           "kvc_compact_protected", "kvc_attend",
+           "kvc_compact_protected", "kvc_attend", "kvc_workspace_bytes_omp",
+           "kvc_compact_omp",
            "kvc_workspace_layout", "kvc_profile_enable", "kvc_profile_read", "kvc_strerror")
 STAGES = {"score_lse": 0, "expweight": 1, "select": 2, "ps": 3, "gram": 4, "nnls": 5,
           "value": 6, "total": 7}
@@ -39,7 +40,8 @@ class AttendParams(ctypes.Structure):
 
 class WsLayout(ctypes.Structure):
     _fields_ = [("lse", ctypes.c_size_t), ("O", ctypes.c_size_t), ("imp", ctypes.c_size_t),
-                ("w", ctypes.c_size_t), ("fit_flops", ctypes.c_size_t)]
+                ("w", ctypes.c_size_t), ("fit_flops", ctypes.c_size_t),
+                ("omp_order", ctypes.c_size_t)]
 
 
 _lib = None
@@ -75,6 +77,11 @@ def load() -> ctypes.CDLL:
     lib.kvc_compact_protected.argtypes = [P, vp, vp, vp, vp, vp, f32p, f32p, i32p, i32p, vp,
                                           ctypes.c_size_t, vp]
     lib.kvc_compact_protected.restype = ctypes.c_int
+    lib.kvc_workspace_bytes_omp.argtypes = [P]
+    lib.kvc_workspace_bytes_omp.restype = ctypes.c_size_t
+    lib.kvc_compact_omp.argtypes = [P, vp, vp, vp, vp, f32p, f32p, i32p, i32p, vp, ctypes.c_size_t,
+                                    vp]
+    lib.kvc_compact_omp.restype = ctypes.c_int
     lib.kvc_attend.argtypes = [ctypes.POINTER(AttendParams), vp, vp, f32p, vp, vp, vp, f32p, vp,
                                vp]
     lib.kvc_attend.restype = ctypes.c_int
@@ -108,6 +115,10 @@ def workspace_bytes(p: Params) -> int:
 
 def workspace_bytes_chunked(p: Params, n_chunks: int) -> int:
     return int(load().kvc_workspace_bytes_chunked(ctypes.byref(p), int(n_chunks)))
+
+
+def workspace_bytes_omp(p: Params) -> int:
+    return int(load().kvc_workspace_bytes_omp(ctypes.byref(p)))
 
 
 def workspace_layout(p: Params) -> WsLayout:

@@ -12,7 +12,7 @@ LIB = os.path.join(HERE, "libkvc.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["score.hip", "select.hip", "fit.hip", "attend.hip", "kvc_host.cpp"]
+SOURCES = ["score.hip", "select.hip", "fit.hip", "attend.hip", "omp.hip", "kvc_host.cpp"]
 
 
 def build(verbose: bool = False) -> str:

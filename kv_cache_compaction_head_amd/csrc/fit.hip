@@ -73,13 +73,16 @@ __device__ __forceinline__ void tri_decode(int bid, int& ty, int& tx) {
 }
 
 // ---------------------------------------------------------------------------
-// P_S[b][i][a] = exp(q_i . k_{idx[a]} - lse_i), fp64.  grid (ceil(n/64)*ceil(t/64), B).
+// P_S[b][i][a] = exp(q_i . k_{idx[a]} - lse_i), computed in fp64 and stored as
+// Out (double for the fits; float for the whole-cache P of the greedy
+// selection, where idx is null: every key, a = j).
+// grid (ceil(n/64)*ceil(t/64), B).
 // ---------------------------------------------------------------------------
-template <class In, int D>
+template <class In, int D, class Out>
 __global__ __launch_bounds__(256) void k_ps(const In* __restrict__ Q, const In* __restrict__ K,
                                             const int32_t* __restrict__ idx,
                                             const double* __restrict__ lse,
-                                            double* __restrict__ PS,
+                                            Out* __restrict__ PS,
                                             const int32_t* __restrict__ tv, int n, int T, int t,
                                             int tiles_a, int qg) {
   __shared__ double sA[kKC * kTile], sB[kKC * kTile];
@@ -88,7 +91,7 @@ __global__ __launch_bounds__(256) void k_ps(const In* __restrict__ Q, const In* 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const In* Qb = Q + static_cast<size_t>(b / qg) * n * D;
   const In* Kb = K + static_cast<size_t>(b) * T * D;
-  const int32_t* ib = idx + static_cast<size_t>(b) * t;
+  const int32_t* ib = idx ? idx + static_cast<size_t>(b) * t : nullptr;
   const int tb = tv ? tv[b] : t;  // columns from tb on are zero (unused budget)
   f64x4 acc[2][2] = {};
   for (int c0 = 0; c0 < D; c0 += kKC) {
@@ -97,7 +100,8 @@ __global__ __launch_bounds__(256) void k_ps(const In* __restrict__ Q, const In* 
       const int r = e / kKC, c = e % kKC;  // r: tile row, c: contraction index
       const int i = i0 + r, a = a0 + r;
       sA[c * kTile + r] = i < n ? to_f64<In>(Qb[static_cast<size_t>(i) * D + c0 + c]) : 0.0;
-      sB[c * kTile + r] = a < tb ? to_f64<In>(Kb[static_cast<size_t>(ib[a]) * D + c0 + c]) : 0.0;
+      sB[c * kTile + r] =
+          a < tb ? to_f64<In>(Kb[static_cast<size_t>(ib ? ib[a] : a) * D + c0 + c]) : 0.0;
     }
     __syncthreads();
     tile_mma(sA, sB, acc, wave, lane);
@@ -110,8 +114,8 @@ __global__ __launch_bounds__(256) void k_ps(const In* __restrict__ Q, const In* 
       for (int i = 0; i < 4; ++i) {
         const int r = i0 + tile_row(wave, lane, ra, i), a = a0 + tile_col(wave, lane, rb);
         if (r < n && a < t)
-          PS[(static_cast<size_t>(b) * n + r) * t + a] =
-              a < tb ? exp(acc[ra][rb][i] - lse[static_cast<size_t>(b) * n + r]) : 0.0;
+          PS[(static_cast<size_t>(b) * n + r) * t + a] = static_cast<Out>(
+              a < tb ? exp(acc[ra][rb][i] - lse[static_cast<size_t>(b) * n + r]) : 0.0);
       }
 }
 
@@ -1475,7 +1479,7 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
   const size_t sPS = static_cast<size_t>(n) * t;
   // P_S, M = P_S^T P_S (into the bias system's variable block), column sums
   prof_mark(3, false, st);
-  hipLaunchKernelGGL((k_ps<In, D>), dim3(tn * tt, B), dim3(256), 0, st, Q, K, idx, lse, fb.PS,
+  hipLaunchKernelGGL((k_ps<In, D, double>), dim3(tn * tt, B), dim3(256), 0, st, Q, K, idx, lse, fb.PS,
                      fb.tv, n, T, t, tt, qg);
   prof_mark(3, true, st);
   prof_mark(4, false, st);
@@ -1544,11 +1548,29 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
   return hipGetLastError();
 }
 
+// P [B][n][T] float32 of every key (the dictionary of the greedy selection).
+template <class In, int D>
+hipError_t launch_probs_all(const void* Q, const void* K, const double* lse, float* P, int B,
+                            int n, int T, int qg, hipStream_t st) {
+  const int tt = (T + kTile - 1) / kTile, tn = (n + kTile - 1) / kTile;
+  hipLaunchKernelGGL((k_ps<In, D, float>), dim3(tn * tt, B), dim3(256), 0, st,
+                     static_cast<const In*>(Q), static_cast<const In*>(K), nullptr, lse, P,
+                     nullptr, n, T, T, tt, qg);
+  return hipGetLastError();
+}
+
 #define KVC_INST_FIT(In, D)                                                                   \
   template hipError_t launch_fit<In, D>(const void*, const void*, const void*, const double*, \
                                         const float*, const int32_t*, FitBufs, float*, float*, \
                                         int32_t*, int, int, int, int, double, int, int,      \
                                         hipStream_t);
+#define KVC_INST_PROBS(In, D)                                                          \
+  template hipError_t launch_probs_all<In, D>(const void*, const void*, const double*, \
+                                              float*, int, int, int, int, hipStream_t);
+KVC_INST_PROBS(bf16_t, 128)
+KVC_INST_PROBS(bf16_t, 64)
+KVC_INST_PROBS(float, 128)
+KVC_INST_PROBS(float, 64)
 KVC_INST_FIT(bf16_t, 128)
 KVC_INST_FIT(bf16_t, 64)
 KVC_INST_FIT(float, 128)

@@ -80,14 +80,16 @@ struct Layout {
   size_t ml, lse, Opart, O, imp_part, imp, idx, status, tv, emask, plist, PS, S, U, V, stage, cvec, wv, lam,
       colpart, Fidx, inv, msz, bar, xcc, flops, part, total;
   size_t part_cap;
+  // greedy selection only (zero otherwise)
+  size_t P32, o_nrm, o_r, o_chosen, o_part, o_order, o_a, o_Q, o_h, o_q, o_part2;
 };
 
 size_t align_up(size_t x) { return (x + 255) / 256 * 256; }
 
-Layout make_layout(const kvc_params_t* p) {
+Layout make_layout(const kvc_params_t* p, bool omp = false) {
   const Plan pl = make_plan(p);
   const size_t B = p->B, T = p->T, n = p->n, d = p->d, t = p->t;
-  Layout L;
+  Layout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -130,6 +132,19 @@ Layout make_layout(const kvc_params_t* p) {
     const size_t lim = 4 * B * t * t + 64 * 64;
     L.part_cap = cap < lim ? cap : lim;
     L.part = take(L.part_cap * 8);
+  }
+  if (omp) {
+    L.P32 = take(B * n * T * 4);
+    L.o_nrm = take(B * T * 8);
+    L.o_r = take(B * n * 8);
+    L.o_chosen = take(B * T);
+    L.o_part = take(B * ((T + 1023) / 1024) * 16);
+    L.o_order = take(B * t * 4);
+    L.o_a = take(B * n * 8);
+    L.o_Q = take(B * t * n * 8);
+    L.o_h = take(B * t * 8);
+    L.o_q = take(B * n * 8);
+    L.o_part2 = take(B * ((n + 255) / 256) * 16);
   }
   L.total = off;
   return L;
@@ -235,6 +250,30 @@ struct FitOp {
   }
 };
 
+template <class In, int D>
+struct ProbsOp {
+  static hipError_t run(const kvc_params_t* p, const void* Q, const void* K, const double* lse,
+                        float* P, hipStream_t st) {
+    return kvc::launch_probs_all<In, D>(Q, K, lse, P, static_cast<int>(p->B),
+                                        static_cast<int>(p->n), static_cast<int>(p->T), 1, st);
+  }
+};
+
+kvc::OmpBufs omp_bufs(void* ws, const Layout& L) {
+  kvc::OmpBufs ob;
+  ob.nrm = at<double>(ws, L.o_nrm);
+  ob.r = at<double>(ws, L.o_r);
+  ob.chosen = at<uint8_t>(ws, L.o_chosen);
+  ob.part = at<double2>(ws, L.o_part);
+  ob.order = at<int32_t>(ws, L.o_order);
+  ob.a = at<double>(ws, L.o_a);
+  ob.Q = at<double>(ws, L.o_Q);
+  ob.h = at<double>(ws, L.o_h);
+  ob.q = at<double>(ws, L.o_q);
+  ob.part2 = at<double2>(ws, L.o_part2);
+  return ob;
+}
+
 int common_checks(const kvc_params_t* p, const void* Q, const void* K, const void* V,
                   const void* out_bias, const void* out_V, void* ws, size_t ws_bytes) {
   if (!params_ok(p)) return KVC_EINVAL;
@@ -263,8 +302,8 @@ bool chunk_params(const kvc_params_t* p, int64_t C, kvc_params_t* out) {
 int compact_impl(const kvc_params_t* p, int qg, const int32_t* t_in, const uint8_t* protect,
                  const void* Q_ref, const void* K, const void* V, void* out_K, float* out_bias,
                  float* out_V, int32_t* out_idx, int32_t* out_status, void* workspace,
-                 hipStream_t stream) {
-  const Layout L = make_layout(p);
+                 hipStream_t stream, bool omp = false) {
+  const Layout L = make_layout(p, omp);
   int32_t* idx = out_idx ? out_idx : at<int32_t>(workspace, L.idx);
   int32_t* status = out_status ? out_status : at<int32_t>(workspace, L.status);
   const int B = static_cast<int>(p->B), T = static_cast<int>(p->T), t = static_cast<int>(p->t);
@@ -285,8 +324,16 @@ int compact_impl(const kvc_params_t* p, int qg, const int32_t* t_in, const uint8
   }
   if (e == hipSuccess) e = dispatch<ScoreOp>(p, Q_ref, K, V, workspace, &L, qg, emask, stream);
   kvc::prof_mark(KVC_STAGE_SELECT, false, stream);
-  if (e == hipSuccess)
+  if (e == hipSuccess && omp) {
+    float* P32 = at<float>(workspace, L.P32);
+    e = dispatch<ProbsOp>(p, Q_ref, K, static_cast<const double*>(at<double>(workspace, L.lse)),
+                          P32, stream);
+    if (e == hipSuccess)
+      e = kvc::launch_omp(P32, omp_bufs(workspace, L), idx, B, static_cast<int>(p->n), T, t,
+                          stream);
+  } else if (e == hipSuccess) {
     e = kvc::launch_select(at<float>(workspace, L.imp), idx, status, tv, emask, B, T, t, stream);
+  }
   if (e == hipSuccess)
     e = kvc::launch_gather(K, idx, out_K, B, T, t, static_cast<int>(p->d) * es, stream);
   kvc::prof_mark(KVC_STAGE_SELECT, true, stream);
@@ -329,6 +376,7 @@ int kvc_workspace_layout(const kvc_params_t* p, kvc_ws_layout_t* out) {
   out->imp = L.imp;
   out->w = L.wv;
   out->fit_flops = L.flops;
+  out->omp_order = make_layout(p, true).o_order;
   return KVC_OK;
 }
 
@@ -342,6 +390,24 @@ int kvc_compact(const kvc_params_t* p, const void* Q_ref, const void* K, const v
     return KVC_EINVAL;
   return compact_impl(p, 1, nullptr, nullptr, Q_ref, K, V, out_K, out_bias, out_V, out_idx,
                       out_status, workspace, stream);
+}
+
+size_t kvc_workspace_bytes_omp(const kvc_params_t* p) {
+  if (!params_ok(p)) return 0;
+  return make_layout(p, true).total;
+}
+
+int kvc_compact_omp(const kvc_params_t* p, const void* Q_ref, const void* K, const void* V,
+                    void* out_K, float* out_bias, float* out_V, int32_t* out_idx,
+                    int32_t* out_status, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  int rc = common_checks(p, Q_ref, K, V, out_bias, out_V, workspace, workspace_bytes);
+  if (rc) return rc;
+  if (workspace_bytes < make_layout(p, true).total) return KVC_EWORKSPACE;
+  if (!aligned(out_K) || (out_idx && !aligned(out_idx)) || (out_status && !aligned(out_status)))
+    return KVC_EINVAL;
+  return compact_impl(p, 1, nullptr, nullptr, Q_ref, K, V, out_K, out_bias, out_V, out_idx,
+                      out_status, workspace, stream, true);
 }
 
 int kvc_compact_protected(const kvc_params_t* p, const uint8_t* protect_mask, const void* Q_ref,

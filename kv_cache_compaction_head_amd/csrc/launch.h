@@ -67,6 +67,26 @@ template <class In, int D>
 hipError_t launch_attend(const void* Q, const void* K1, const float* bias, const void* V1,
                          bool v1_f32, const void* K2, const void* V2, float* out,
                          double* out_lse, int B, int m, int t1, int t2, hipStream_t st);
+// P [B][n][T] float32 of every key: exp(q_i . k_j - lse_i).
+template <class In, int D>
+hipError_t launch_probs_all(const void* Q, const void* K, const double* lse, float* P, int B,
+                            int n, int T, int qg, hipStream_t st);
+// Work buffers of the greedy (matching pursuit) selection.
+struct OmpBufs {
+  double* nrm;     // [B][T] column norms of P
+  double* r;       // [B][n] residual
+  uint8_t* chosen; // [B][T] flags
+  double2* part;   // [B][ceil(T/1024)] workgroup bests (value, key)
+  int32_t* order;  // [B][t] keys in the order chosen
+  double* a;       // [B][n] the chosen column
+  double* Q;       // [B][t][n] orthonormal basis of the chosen columns
+  double* h;       // [B][t] projections
+  double* q;       // [B][n] new basis vector before normalisation
+  double2* part2;  // [B][ceil(n/256)] partial sums (q.q, q.r)
+};
+// t greedy steps over P; writes the chosen keys ascending to idx [B][t].
+hipError_t launch_omp(const float* P, OmpBufs ob, int32_t* idx, int B, int n, int T, int t,
+                      hipStream_t st);
 // Event-pair instrumentation (defined with the C ABI): no-op unless enabled.
 void prof_mark(int stage, bool end, hipStream_t st);
 }  // namespace kvc

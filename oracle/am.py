@@ -228,6 +228,56 @@ def compact(Q, K, V, t: int, agg: str = "rms", ridge_rel: float = DEFAULT_RIDGE_
             "lse": lse, "O": O, "imp": imp, **info}
 
 
+def omp_dictionary(Q, K, lse):
+    """The whole-cache softmax weights P [n, T] as the greedy selection stores
+    them: computed in float64, rounded to float32 (the pages leave the
+    precision open; both sides take the argmax decisions on these values)."""
+    P = np.exp(np.asarray(Q, float) @ np.asarray(K, float).T - np.asarray(lse, float)[:, None])
+    return P.astype(np.float32).astype(np.float64)
+
+
+def omp_select(P: np.ndarray, t: int):
+    """Orthogonal matching pursuit on the attention mass (section 2, key
+    selection, the greedy alternative to the highest-attention keys): target
+    y = 1 over the reference queries (relative mass), dictionary columns p_j.
+    Each step picks the unchosen key with the largest p_j . r / ||p_j|| (ties
+    to the lower index; all-zero columns only when nothing else is left) and
+    sets r to y minus its least-squares projection on the chosen columns.
+    Returns (chosen keys ascending, keys in the order chosen, residual norms)."""
+    n, T = P.shape
+    if not 1 <= t <= T:
+        raise ValueError("t must lie in [1, T]")
+    y = np.ones(n)
+    nrm = np.sqrt((P * P).sum(axis=0))
+    r = y.copy()
+    order, norms = [], []
+    taken = np.zeros(T, bool)
+    for _ in range(t):
+        with np.errstate(divide="ignore", invalid="ignore"):
+            c = np.where(nrm > 0, (P.T @ r) / nrm, -np.inf)
+        c[taken] = -np.inf
+        j = int(np.argmax(c)) if np.isfinite(c.max()) else int(np.flatnonzero(~taken)[0])
+        order.append(j)
+        taken[j] = True
+        A = P[:, order]
+        w = np.linalg.lstsq(A, y, rcond=None)[0]
+        r = y - A @ w
+        norms.append(float(np.linalg.norm(r)))
+    return np.sort(np.array(order)), np.array(order), np.array(norms)
+
+
+def compact_omp(Q, K, V, t: int, ridge_rel: float = DEFAULT_RIDGE_REL):
+    """One head with the greedy selection: keys by omp_select on the float32
+    dictionary, then the same bias (NNLS) and value fits as compact()."""
+    Q, K, V = (np.asarray(a, dtype=np.float64) for a in (Q, K, V))
+    lse = row_lse(Q, K)
+    O, _ = attention_stats(Q, K, V, lse)
+    idx, order, norms = omp_select(omp_dictionary(Q, K, lse), t)
+    w, beta, Cv, info = fit(Q, K, V, idx, lse=lse, O=O, ridge_rel=ridge_rel)
+    return {"idx": idx, "order": order, "res_norms": norms, "Ck": K[idx], "beta": beta, "w": w,
+            "Cv": Cv, "lse": lse, "O": O, **info}
+
+
 def compact_chunked(Q, K, V, t: int, n_chunks: int, agg: str = "rms",
                     ridge_rel: float = DEFAULT_RIDGE_REL):
     """Chunked compaction ("Compaction par blocs" paragraph of the same summary):

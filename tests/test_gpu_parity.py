@@ -419,3 +419,92 @@ def test_compacted_cache_with_appended_block_on_gpu():
         print(f"head {h}: appended-block compaction error gpu {gpu_err:.4g} oracle {oracle_err:.4g}",
               flush=True)
         assert gpu_err <= oracle_err * 1.05 + 1e-5
+
+
+def _omp_replay(P, order, steps, rel=1e-9):
+    """Check that each sampled step k of a pursuit run picked a best key given
+    the run's own earlier picks: its score is within rel of the top score the
+    oracle computes (float64) for the same prefix."""
+    n, T = P.shape
+    y = np.ones(n)
+    nrm = np.sqrt((P * P).sum(axis=0))
+    for k in steps:
+        pre = list(order[:k])
+        if pre:
+            A = P[:, pre]
+            r = y - A @ np.linalg.lstsq(A, y, rcond=None)[0]
+        else:
+            r = y
+        with np.errstate(divide="ignore", invalid="ignore"):
+            c = np.where(nrm > 0, (P.T @ r) / nrm, -np.inf)
+        c[pre] = -np.inf
+        best = c.max()
+        got = c[order[k]]
+        assert got >= best - rel * max(abs(best), 1e-300), (k, order[k], got, best)
+
+
+@pytest.mark.parametrize("w", [
+    synth.custom(22, 2, 1000, 128, 128, 40, "bf16", "clusters"),
+    synth.custom(23, 2, 777, 96, 64, 33, "f32", "normal"),
+], ids=["bf16", "f32_d64"])
+def test_omp_matches_oracle(w):
+    """kvc_compact_omp against the oracle's pursuit: the same keys in the same
+    order (each pick also replayed against the oracle given the GPU's prefix),
+    then the fits on that set within the usual bar."""
+    import torch
+    import kv_cache_compaction_head_amd as kvc
+    data = synth.batch(w)
+    Q, K, V = (to_device(data[k]) for k in ("Q", "K", "V"))
+    res = kvc.compact_omp(Q, K, V, w.t)
+    torch.cuda.synchronize()
+    inter = {k: v.cpu().numpy() for k, v in kvc.intermediates(res).items()}
+    idx = res.idx.cpu().numpy().astype(np.int64)
+    assert (res.status.cpu().numpy() == 0).all()
+    for h in range(w.B):
+        Qh, Kh, Vh = (synth.to_f64(data[k][h]) for k in ("Q", "K", "V"))
+        ref = orc.compact_omp(Qh, Kh, Vh, w.t)
+        order = inter["omp_order"][h].astype(np.int64)
+        assert np.array_equal(np.sort(order), idx[h]) and np.all(np.diff(idx[h]) > 0)
+        P = orc.omp_dictionary(Qh, Kh, ref["lse"])
+        _omp_replay(P, order, range(w.t))
+        same = np.array_equal(order, ref["order"])
+        wv, beta, Cv, _ = orc.fit(Qh, Kh, Vh, idx[h])
+        err_w = orc.rel_l2(inter["w"][h], wv)
+        err_c = orc.rel_l2(res.values[h].cpu().numpy().astype(np.float64), Cv)
+        o_gpu = orc.attend(Qh, Kh[idx[h]], res.values[h].cpu().numpy().astype(np.float64),
+                           res.bias[h].cpu().numpy().astype(np.float64))
+        err_o = orc.rel_l2(o_gpu, orc.attend(Qh, Kh[idx[h]], Cv, beta))
+        print(w.name, "head", h, "same order", same, "w", err_w, "Cv", err_c, "Ohat", err_o,
+              flush=True)
+        assert same
+        assert max(err_w, err_c, err_o) <= _tol(w)
+
+
+def test_omp_full_size_sampled_steps():
+    """32768 keys, 2048 queries, 655 picks per head (the 32k/50x workload):
+    sampled steps of the GPU's pursuit replayed against the oracle given the
+    GPU's own earlier picks; the fits of one head against the oracle."""
+    import torch
+    import kv_cache_compaction_head_amd as kvc
+    w = dataclasses.replace(synth.CONFIGS[3], B=2)
+    data = synth.batch(w)
+    Q, K, V = (to_device(data[k]) for k in ("Q", "K", "V"))
+    res = kvc.compact_omp(Q, K, V, w.t)
+    torch.cuda.synchronize()
+    assert (res.status.cpu().numpy() == 0).all()
+    inter = {k: v.cpu().numpy() for k, v in kvc.intermediates(res).items()}
+    h = 1
+    Qh, Kh, Vh = (synth.to_f64(data[k][h]) for k in ("Q", "K", "V"))
+    lse = orc.row_lse(Qh, Kh)
+    assert np.max(np.abs(inter["lse"][h] - lse)) < 1e-4
+    P = orc.omp_dictionary(Qh, Kh, lse)
+    order = inter["omp_order"][h].astype(np.int64)
+    assert len(set(order.tolist())) == w.t
+    _omp_replay(P, order, [0, 1, 2, 50, 300, w.t - 1])
+    idx = res.idx[h].cpu().numpy().astype(np.int64)
+    wv, beta, Cv, _ = orc.fit(Qh, Kh, Vh, idx)
+    o_gpu = orc.attend(Qh, Kh[idx], res.values[h].cpu().numpy().astype(np.float64),
+                       res.bias[h].cpu().numpy().astype(np.float64))
+    err = orc.rel_l2(o_gpu, orc.attend(Qh, Kh[idx], Cv, beta))
+    print("omp C3 head 1: Ohat vs oracle fits", err, flush=True)
+    assert orc.rel_l2(inter["w"][h], wv) <= TOL_BF16 and err <= TOL_BF16

@@ -563,3 +563,65 @@ def test_attend_appended_matches_scalar_loops():
         assert abs(lse[i] - math.log(z)) < 1e-13
         for c in range(2):
             assert abs(o[i, c] - math.fsum(math.exp(x) * v[c] for x, v in zip(s, vs)) / z) < 1e-13
+
+
+# ------------------------------------------------ greedy selection (f3)
+@pytest.mark.parametrize("seed", range(4))
+def test_omp_first_pick_is_best_single_key_fit(seed):
+    """Step 1 of the pursuit = the key whose column alone fits y = 1 best in
+    least squares (brute force over keys: ||y||^2 - (p.y)^2 / ||p||^2)."""
+    rng = np.random.default_rng(100 + seed)
+    P = rng.random((15, 40)) ** 3
+    _, order, norms = orc.omp_select(P, 1)
+    res = [np.linalg.norm(np.ones(15) - P[:, [j]] @ np.linalg.lstsq(P[:, [j]], np.ones(15),
+                                                                       rcond=None)[0])
+           for j in range(40)]
+    assert order[0] == int(np.argmin(res))
+    assert abs(norms[0] - min(res)) < 1e-12
+
+
+def test_omp_orthogonal_dictionary_recovers_exact_support():
+    """Columns with disjoint supports are orthogonal: if y = 1 is a positive
+    combination of k of them, the pursuit picks exactly those k (textbook
+    exact recovery) and the residual vanishes; distractors overlap no more
+    than half a block."""
+    n = 24
+    blocks = [range(0, 6), range(6, 10), range(10, 18), range(18, 24)]
+    P = np.zeros((n, 9))
+    for c, blk in zip((1, 4, 6, 8), blocks):
+        P[list(blk), c] = 0.5
+    P[[0, 1, 2], 0] = 0.9       # distractors: part of one block each
+    P[[6, 7], 2] = 0.4
+    P[[10, 11, 12], 3] = 0.3
+    P[[18, 19, 20], 5] = 0.7
+    P[[12], 7] = 1.0
+    idx, order, norms = orc.omp_select(P, 4)
+    assert list(idx) == [1, 4, 6, 8]
+    assert norms[-1] < 1e-12
+    assert np.all(np.diff(norms) <= 1e-15)
+
+
+def test_omp_residual_orthogonal_and_duplicates_skipped():
+    """After each step the residual is orthogonal to every chosen column (the
+    'orthogonal' of the pursuit), so an exact duplicate of a chosen column
+    scores zero and is not picked while another column correlates."""
+    rng = np.random.default_rng(7)
+    P = rng.random((30, 12))
+    P[:, 5] = P[:, 2]
+    for t in range(1, 8):
+        _, order, _ = orc.omp_select(P, t)
+        A = P[:, order]
+        r = np.ones(30) - A @ np.linalg.lstsq(A, np.ones(30), rcond=None)[0]
+        assert np.max(np.abs(A.T @ r)) < 1e-10
+        assert not (2 in order and 5 in order)
+
+
+def test_omp_keep_everything_is_exact_and_zero_columns_last():
+    Q, K, V = _rand(110, 20, 6, scale=0.4), _rand(111, 16, 6), _rand(112, 16, 3)
+    r = orc.compact_omp(Q, K, V, 16)
+    assert list(r["idx"]) == list(range(16))
+    assert np.allclose(r["Cv"], V, atol=1e-8)
+    P = np.abs(_rand(113, 10, 6))
+    P[:, [1, 4]] = 0.0
+    _, order, _ = orc.omp_select(P, 6)
+    assert list(order[-2:]) == [1, 4]

@@ -200,7 +200,9 @@ int kvc_compact_chunked(const kvc_params_t* p, int64_t n_chunks, const void* Q_r
                         int32_t* out_idx, int32_t* out_status, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
 
-/* Attention over a cache followed by an appended fixed block, for queries Q:
+/* Attention over a cache followed by an appended fixed block, for queries Q
+ * (the keys are split across workgroups; workspace: at least
+ * kvc_attend_workspace_bytes(p) bytes, may be NULL when that is 0):
  *   out_i = softmax_j(q_i . k_j + bias_j) v_j over the t1 keys of block 1
  *   (with bias1; e.g. a compact cache C_k, beta, C_v) and then the t2 keys of
  *   block 2 (bias 0; e.g. the fixed or future tokens appended after it),
@@ -223,9 +225,10 @@ typedef struct {
   int32_t reserved;  /* must be 0 */
   int32_t reserved2; /* must be 0 */
 } kvc_attend_params_t;
+size_t kvc_attend_workspace_bytes(const kvc_attend_params_t* p);
 int kvc_attend(const kvc_attend_params_t* p, const void* Q, const void* K1, const float* bias1,
                const void* V1, const void* K2, const void* V2, float* out, double* out_lse,
-               hipStream_t stream);
+               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Where the intermediates of the last call live inside its workspace (byte
  * offsets), for inspection after the stream completes:

@@ -244,7 +244,7 @@ def fit(Q, K, V, idx, *, ridge_rel: float = 1e-6, max_nnls_iters: int = 32,
     return Compacted(keys, bias, values, idx, status, ws, p)
 
 
-def attend(Q, K1, V1, bias1=None, K2=None, V2=None, *, stream=None):
+def attend(Q, K1, V1, bias1=None, K2=None, V2=None, *, workspace=None, stream=None):
     """Attention of Q [B,m,d] over block 1 (K1, V1, optional per-key bias1)
     followed by block 2 (K2, V2, no bias): returns (out [B,m,d] float32,
     lse [B,m] float64).  K1, K2, V2 and Q share one dtype (bfloat16 or
@@ -273,11 +273,17 @@ def attend(Q, K1, V1, bias1=None, K2=None, V2=None, *, stream=None):
     out = torch.empty((B, m, d), dtype=torch.float32, device=dev)
     lse = torch.empty((B, m), dtype=torch.float64, device=dev)
     null = ctypes.c_void_p(None)
+    need = int(load().kvc_attend_workspace_bytes(ctypes.byref(p)))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if need and workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    wsp = _vp(workspace) if need else null
     b1 = _vp(bias1.contiguous()) if bias1 is not None else null
     k2 = _vp(K2.contiguous()) if t2 else null
     v2 = _vp(V2.contiguous()) if t2 else null
     rc = load().kvc_attend(ctypes.byref(p), _vp(Q), _vp(K1), b1, _vp(V1), k2, v2, _vp(out),
-                           _vp(lse), _stream(stream, dev))
+                           _vp(lse), wsp, ctypes.c_size_t(need), _stream(stream, dev))
     _lib.check(rc)
     return out, lse
 

@@ -17,7 +17,7 @@ KVC_AGG_RMS, KVC_AGG_MEAN = 0, 1
 
 EXPORTS = ("kvc_params_default", "kvc_workspace_bytes", "kvc_compact", "kvc_fit",
            "kvc_workspace_bytes_chunked", "kvc_compact_chunked", "kvc_compact_ragged",
-           "kvc_compact_protected", "kvc_attend", "kvc_workspace_bytes_omp",
+           "kvc_compact_protected", "kvc_attend", "kvc_attend_workspace_bytes", "kvc_workspace_bytes_omp",
            "kvc_compact_omp",
            "kvc_workspace_layout", "kvc_profile_enable", "kvc_profile_read", "kvc_strerror")
 STAGES = {"score_lse": 0, "expweight": 1, "select": 2, "ps": 3, "gram": 4, "nnls": 5,
@@ -82,8 +82,10 @@ def load() -> ctypes.CDLL:
     lib.kvc_compact_omp.argtypes = [P, vp, vp, vp, vp, f32p, f32p, i32p, i32p, vp, ctypes.c_size_t,
                                     vp]
     lib.kvc_compact_omp.restype = ctypes.c_int
+    lib.kvc_attend_workspace_bytes.argtypes = [ctypes.POINTER(AttendParams)]
+    lib.kvc_attend_workspace_bytes.restype = ctypes.c_size_t
     lib.kvc_attend.argtypes = [ctypes.POINTER(AttendParams), vp, vp, f32p, vp, vp, vp, f32p, vp,
-                               vp]
+                               vp, ctypes.c_size_t, vp]
     lib.kvc_attend.restype = ctypes.c_int
     lib.kvc_workspace_layout.argtypes = [P, ctypes.POINTER(WsLayout)]
     lib.kvc_workspace_layout.restype = ctypes.c_int

@@ -476,16 +476,28 @@ int kvc_fit(const kvc_params_t* p, const void* Q_ref, const void* K, const void*
   return e == hipSuccess ? KVC_OK : KVC_EHIP;
 }
 
+static bool attend_ok(const kvc_attend_params_t* p) {
+  if (!p || p->B < 1 || p->B > kMaxB || p->m < 1 || p->m > kMaxT || (p->d != 64 && p->d != 128))
+    return false;
+  if (p->t1 < 0 || p->t2 < 0 || p->t1 + p->t2 < 1 || p->t1 + p->t2 > kMaxT) return false;
+  if (p->in_dtype != KVC_F32 && p->in_dtype != KVC_BF16) return false;
+  if ((p->v1_f32 != 0 && p->v1_f32 != 1) || p->reserved != 0 || p->reserved2 != 0) return false;
+  return true;
+}
+
+size_t kvc_attend_workspace_bytes(const kvc_attend_params_t* p) {
+  if (!attend_ok(p)) return 0;
+  return kvc::attend_ws_bytes(static_cast<int>(p->B), static_cast<int>(p->m),
+                              static_cast<int>(p->t1 + p->t2), static_cast<int>(p->d));
+}
+
 int kvc_attend(const kvc_attend_params_t* p, const void* Q, const void* K1, const float* bias1,
                const void* V1, const void* K2, const void* V2, float* out, double* out_lse,
-               hipStream_t stream) {
-  if (!p || p->B < 1 || p->B > kMaxB || p->m < 1 || p->m > kMaxT || (p->d != 64 && p->d != 128))
-    return KVC_EINVAL;
-  if (p->t1 < 0 || p->t2 < 0 || p->t1 + p->t2 < 1 || p->t1 > kMaxT || p->t2 > kMaxT)
-    return KVC_EINVAL;
-  if (p->in_dtype != KVC_F32 && p->in_dtype != KVC_BF16) return KVC_EINVAL;
-  if ((p->v1_f32 != 0 && p->v1_f32 != 1) || p->reserved != 0 || p->reserved2 != 0)
-    return KVC_EINVAL;
+               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!attend_ok(p)) return KVC_EINVAL;
+  const size_t need = kvc_attend_workspace_bytes(p);
+  if (need > 0 && (!workspace || !aligned(workspace))) return KVC_EINVAL;
+  if (workspace_bytes < need) return KVC_EWORKSPACE;
   if (!aligned(Q) || !aligned(out) || (out_lse && !aligned(out_lse))) return KVC_EINVAL;
   if (p->t1 > 0 && (!aligned(K1) || !aligned(V1) || (bias1 && !aligned(bias1)))) return KVC_EINVAL;
   if (p->t2 > 0 && (!aligned(K2) || !aligned(V2))) return KVC_EINVAL;
@@ -495,14 +507,16 @@ int kvc_attend(const kvc_attend_params_t* p, const void* Q, const void* K1, cons
   hipError_t e;
   if (p->in_dtype == KVC_BF16)
     e = p->d == 128 ? kvc::launch_attend<kvc::bf16_t, 128>(Q, K1, bias1, V1, v1f, K2, V2, out,
-                                                           out_lse, B, m, t1, t2, stream)
+                                                           out_lse, workspace, B, m, t1, t2,
+                                                           stream)
                     : kvc::launch_attend<kvc::bf16_t, 64>(Q, K1, bias1, V1, v1f, K2, V2, out,
-                                                          out_lse, B, m, t1, t2, stream);
+                                                          out_lse, workspace, B, m, t1, t2,
+                                                          stream);
   else
     e = p->d == 128 ? kvc::launch_attend<float, 128>(Q, K1, bias1, V1, v1f, K2, V2, out, out_lse,
-                                                     B, m, t1, t2, stream)
+                                                     workspace, B, m, t1, t2, stream)
                     : kvc::launch_attend<float, 64>(Q, K1, bias1, V1, v1f, K2, V2, out, out_lse,
-                                                    B, m, t1, t2, stream);
+                                                    workspace, B, m, t1, t2, stream);
   return e == hipSuccess ? KVC_OK : KVC_EHIP;
 }
 

@@ -62,11 +62,14 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
                       int max_iters, int qg, hipStream_t st);
 // kept indices of (head, chunk) b' made global: idx[b'][a] += (b' mod C) * Tc
 hipError_t launch_idx_offset(int32_t* idx, int Bc, int t, int C, int Tc, hipStream_t st);
-// Attention over block 1 (K1, V1 with a per-key bias) then block 2 (K2, V2).
+// Attention over block 1 (K1, V1 with a per-key bias) then block 2 (K2, V2);
+// ws holds attend_ws_bytes() of split partials.
+size_t attend_ws_bytes(int B, int m, int keys, int D);
 template <class In, int D>
 hipError_t launch_attend(const void* Q, const void* K1, const float* bias, const void* V1,
                          bool v1_f32, const void* K2, const void* V2, float* out,
-                         double* out_lse, int B, int m, int t1, int t2, hipStream_t st);
+                         double* out_lse, void* ws, int B, int m, int t1, int t2,
+                         hipStream_t st);
 // P [B][n][T] float32 of every key: exp(q_i . k_j - lse_i).
 template <class In, int D>
 hipError_t launch_probs_all(const void* Q, const void* K, const double* lse, float* P, int B,

@@ -398,16 +398,27 @@ __device__ __forceinline__ int hw_xcc_id() {
   return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xf;  // HW_REG_XCC_ID[3:0]
 }
 
-__device__ void team_sync(Team& tm) {
-  if (tm.size == 1) {
-    __syncthreads();
-    return;
-  }
+// A barrier is an arrival (count this workgroup in, after its stores) and a
+// wait (until every member of the team has arrived).  team_sync does both; a
+// member that needs nothing the others produce before the barrier may arrive,
+// keep working, and wait later (team_wait before its next arrival, so the
+// cumulative count can never let a barrier pass early).
+__device__ void team_arrive(Team& tm) {
+  if (tm.size == 1) return;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are done
   __syncthreads();
   if (threadIdx.x == 0) {
     if (!tm.fast) __threadfence();
     atomicAdd(tm.ctr, 1u);
+  }
+}
+
+__device__ void team_wait(Team& tm) {
+  if (tm.size == 1) {
+    __syncthreads();
+    return;
+  }
+  if (threadIdx.x == 0) {
     const unsigned target = (tm.gen + 1) * static_cast<unsigned>(tm.size);
     const uint64_t t0 = wall_clock64();
     while (__hip_atomic_load(tm.ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
@@ -423,6 +434,11 @@ __device__ void team_sync(Team& tm) {
   }
   tm.gen++;
   __syncthreads();
+}
+
+__device__ void team_sync(Team& tm) {
+  team_arrive(tm);
+  team_wait(tm);
 }
 
 // Team of this workgroup from the XCD-aligned mapping, then one agent-fenced
@@ -530,7 +546,7 @@ struct SweepMat {
   gdouble* S;      // lower triangle, ld x ld
   gdouble* U;      // [rows][64] W = A[:, P] L^-T of the step
   gdouble* V;      // [rows][64] A[:, P] B
-  gdouble* stage;  // [kStage] B, L^-1, 1/D of the next step (lookahead)
+  gdouble* stage;  // [kStage] L^-1 (at kSB*kSB) and 1/D (at 2*kSB*kSB) of the next step
   int ld, r_al, n_rhs, n_var;
 };
 constexpr int kStage = kSweepStage;
@@ -602,9 +618,10 @@ __device__ int wg_append(bool f, int base, int* slot) {
   return tot;
 }
 
-// sm.pp[0:k][0:k] <- its inverse B (the rest 0) through A_PP = L D L^T:
-// a right-looking blocked factorization (blocks of 16 pivots), L^-1 by
-// blocked triangular inversion, then B = L^-T D^-1 L^-1 on fp64 MFMA.  Per
+// The pivot block sm.pp[0:k][0:k] = A_PP = L D L^T (overwritten): a
+// right-looking blocked factorization (blocks of 16 pivots) with L^-1 by
+// blocked triangular inversion; small_b then forms B = A_PP^-1 =
+// L^-T D^-1 L^-1 on fp64 MFMA.  Per
 // block: one wave sweeps the current 16 x 16 diagonal block pivot by pivot
 // (the pivot row goes through LDS; a wave's LDS accesses are performed in
 // order, so no barrier is needed); before sweep p its pivot row holds
@@ -614,11 +631,19 @@ __device__ int wg_append(bool f, int base, int* slot) {
 // A[>b, >b] -= W D_b^-1 W^T (W = A[>b, b] L_bb^-T).  Inverting the pivot block
 // by a blocked sweep instead would form its off-diagonal parts through
 // explicit inverses of the 16 x 16 blocks and lose them when those are
-// ill-conditioned.  Results: sm.pp = B, sm.li = L^-1 (identity past k),
-// sm.rD = 1/D (0 past k).  A pivot without the sign s_p is replaced by s_p (the system is
+// ill-conditioned.  Results: sm.li = L^-1 (identity past k), sm.rD = 1/D
+// (0 past k).  A pivot without the sign s_p is replaced by s_p (the system is
 // not numerically definite); the return value, meaningful in wave 0, says
 // whether that happened.
-__device__ __forceinline__ bool small_inverse(int k) {
+// Lane src's value of v, for the whole wave (two 32-bit lane reads).
+__device__ __forceinline__ double rdlane(double v, int src) {
+  const unsigned long long u = __double_as_longlong(v);
+  const unsigned lo = __builtin_amdgcn_readlane(static_cast<unsigned>(u), src);
+  const unsigned hi = __builtin_amdgcn_readlane(static_cast<unsigned>(u >> 32), src);
+  return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
+}
+
+__device__ __forceinline__ bool small_ldl(int k) {
   SweepSmem& sm = g_sw;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wr = wave >> 1, wc = wave & 1, g16 = lane >> 4, l16 = lane & 15;
@@ -631,33 +656,42 @@ __device__ __forceinline__ bool small_inverse(int k) {
   for (int b = 0; b < nb; ++b) {
     const int o = b * 16, o2 = o + 16;
     if (wave == 0) {
+      // lane l holds row r = l/4, columns c4..c4+3 of the block; the pivot
+      // row's entries reach the other lanes by lane shuffles (row m lives in
+      // lanes 4m..4m+3, and the block stays symmetric under sweeping, so
+      // A[r][m] sits in lane 4r + m/4)
       const int r = lane >> 2, c4 = (lane & 3) * 4;
-      double a[4];
+      double a[4], sgv[16];
 #pragma unroll
       for (int j = 0; j < 4; ++j) a[j] = sm.pp[o + r][o + c4 + j];
+#pragma unroll
+      for (int m = 0; m < 16; ++m) sgv[m] = o + m < k ? sm.sgn[o + m] : 1.0;
+#pragma unroll
       for (int m = 0; m < 16; ++m) {
+        // the pivot (lane 4m + m/4, slot m%4) as a wave-uniform value, read
+        // directly so the division overlaps the shuffles below
+        double d = rdlane(a[m & 3], 4 * m + (m >> 2));
+        double rc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rc[j] = __shfl(a[j], 4 * m + (lane & 3));
+        const double arm = __shfl(a[m & 3], (lane & ~3) + (m >> 2));
         if (r == m) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            sm.mbc[c4 + j] = a[j];
+          for (int j = 0; j < 4; ++j)
             sm.sLb[m][c4 + j] = c4 + j < m ? -a[j] : (c4 + j == m ? 1.0 : 0.0);
-          }
         }
-        double d = sm.mbc[m];
-        const double sg = o + m < k ? sm.sgn[o + m] : 1.0;
-        if (!(d * sg > 0.0)) {
+        if (!(d * sgv[m] > 0.0)) {
           bad = true;
-          d = sg;
+          d = sgv[m];
         }
         const double rd = 1.0 / d;
         if (lane == 0) sm.rD[o + m] = rd;
-        const double f = sm.mbc[r] * rd;
+        const double f = arm * rd;
         const bool isrow = r == m;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const double rc = sm.mbc[c4 + j];
-          const double gen = fma(-f, rc, a[j]);
-          const double v = isrow ? rc * rd : gen;
+          const double gen = fma(-f, rc[j], a[j]);
+          const double v = isrow ? rc[j] * rd : gen;
           const double vp = isrow ? -rd : f;
           a[j] = c4 + j == m ? vp : v;
         }
@@ -746,7 +780,14 @@ __device__ __forceinline__ bool small_inverse(int k) {
   }
   if (tid >= k && tid < kSB) sm.rD[tid] = 0.0;
   __syncthreads();
-  // B = L^-T D^-1 L^-1
+  return bad;
+}
+
+// sm.pp <- B = L^-T D^-1 L^-1 from sm.li and sm.rD (identity and 0 past k).
+__device__ __forceinline__ void small_b(int k) {
+  SweepSmem& sm = g_sw;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wr = wave >> 1, wc = wave & 1, g16 = lane >> 4, l16 = lane & 15;
   f64x4 acc[2][2] = {};
   // L^-1 is lower triangular: rows m below this wave's quadrant contribute nothing
   for (int ks = max(wr, wc) * 8; ks < (k + 3) / 4; ++ks) {
@@ -774,7 +815,6 @@ __device__ __forceinline__ bool small_inverse(int k) {
         sm.pp[row][col] = (row < k && col < k) ? acc[ra][rb][i] : 0.0;
       }
   __syncthreads();
-  return bad;
 }
 
 // Phase A for one 64-row band (matrix rows band*64 ..): U = A[rows, P]
@@ -982,8 +1022,9 @@ struct TileWalk {
 // sm.sgn2) and the team has more than one member, its last member does no
 // tiles; it takes the next pivot block from S before this step's update,
 // applies the update to it from the staged W rows (A' = A - W D^-1 W^T; the
-// two pivot sets are disjoint), inverts it and publishes B, L^-1 and 1/D in
-// M.stage, which the next step loads instead of inverting (pre = true).
+// two pivot sets are disjoint), factors it and publishes L^-1 and 1/D in
+// M.stage, which the next step loads instead of factoring (pre = true); the
+// members that build bands and tiles form B from them.
 // Returns whether a pivot of this step had the wrong sign (a lookahead
 // member flags its own into *status).
 __device__ __noinline__ bool sweep_step(const SweepMat M, Team& tm, int k, int skip_below, int kn,
@@ -996,7 +1037,6 @@ __device__ __noinline__ bool sweep_step(const SweepMat M, Team& tm, int k, int s
   if (pre) {
     for (int e = tid; e < kSB * kSB; e += kTeamThreads) {
       const int r = e >> 6, c = e & 63;
-      sm.pp[r][c] = M.stage[e];
       sm.li[r][c] = M.stage[kSB * kSB + e];
     }
     if (tid < kSB) sm.rD[tid] = M.stage[2 * kSB * kSB + tid];
@@ -1009,11 +1049,14 @@ __device__ __noinline__ bool sweep_step(const SweepMat M, Team& tm, int k, int s
       sm.pp[a][c] = in ? v : (a == c ? 1.0 : 0.0);
     }
     __syncthreads();
-    bad = small_inverse(k);
+    bad = small_ldl(k);
   }
   const int nrb = (M.n_rhs + kSB - 1) / kSB, nvb = (M.n_var + kSB - 1) / kSB;
   const int vb0 = M.r_al / kSB;
   const int vmembers = la ? tm.size - 1 : tm.size;
+  // B (for V = U B and the pivot block) only where the bands and tiles are
+  // built: the lookahead member needs L^-1 and D alone
+  if (!me_la) small_b(k);
   if (!me_la) {
     for (int bi = tm.rank; bi < nrb + nvb; bi += vmembers) v_band(M, bi < nrb ? bi : vb0 + bi - nrb, k);
   } else {
@@ -1086,19 +1129,23 @@ __device__ __noinline__ bool sweep_step(const SweepMat M, Team& tm, int k, int s
           if (row < kn && col < kn) sm.pp[row][col] -= acc[x][y][i];
         }
   }
-  team_sync(tm);
   if (me_la) {
+    // the lookahead member has read all it needs from S: count it in at the
+    // first barrier and invert at once (the tile updates start when the
+    // others have arrived); it waits for that barrier only before the next
+    team_arrive(tm);
     if (tid < kSB) sm.sgn[tid] = sm.sgn2[tid];
     __syncthreads();
-    const bool bad2 = small_inverse(kn);
+    const bool bad2 = small_ldl(kn);
     for (int e = tid; e < kSB * kSB; e += kTeamThreads) {
       const int r = e >> 6, c = e & 63;
-      M.stage[e] = sm.pp[r][c];
       M.stage[kSB * kSB + e] = sm.li[r][c];
     }
     if (tid < kSB) M.stage[2 * kSB * kSB + tid] = sm.rD[tid];
     if (bad2 && tid == 0 && status) atomicOr(status, 1);
+    team_wait(tm);
   } else {
+    team_sync(tm);
     // every wave of the tile workers takes a contiguous run of the active
     // tiles; when there are fewer tiles than waves, of their halves or quarters
     int total = 0;

@@ -55,10 +55,10 @@ struct Plan {
   int nqb, nsplit1, kps1, nsplit2, kps2;
 };
 
-// Split the key range so the score grid has ~1024 workgroups; splits are a
-// multiple of 64 keys (a whole number of K1 tiles).
-void split_keys(int64_t T, int64_t work_per_split, int& nsplit, int& kps) {
-  int64_t want = (1024 + work_per_split - 1) / work_per_split;
+// Split the key range so the score grid has about `target` workgroups;
+// splits are a multiple of 64 keys (a whole number of tiles).
+void split_keys(int64_t T, int64_t work_per_split, int64_t target, int& nsplit, int& kps) {
+  int64_t want = (target + work_per_split - 1) / work_per_split;
   int64_t maxs = T / 512 > 0 ? T / 512 : 1;
   if (want > maxs) want = maxs;
   if (want < 1) want = 1;
@@ -71,8 +71,12 @@ void split_keys(int64_t T, int64_t work_per_split, int& nsplit, int& kps) {
 Plan make_plan(const kvc_params_t* p) {
   Plan pl;
   pl.nqb = static_cast<int>((p->n + kBM - 1) / kBM);
-  split_keys(p->T, static_cast<int64_t>(pl.nqb) * p->B, pl.nsplit1, pl.kps1);
-  split_keys(p->T, static_cast<int64_t>(pl.nqb) * p->B, pl.nsplit2, pl.kps2);
+  // K1's partials are one (max, sum) pair per query and split, so it takes
+  // ~4 rounds of its 3-workgroups-per-CU residency (a short tail); K2's carry
+  // a d x n output slice per split, so it keeps ~1024 workgroups (two full
+  // rounds at 2 per CU)
+  split_keys(p->T, static_cast<int64_t>(pl.nqb) * p->B, 3072, pl.nsplit1, pl.kps1);
+  split_keys(p->T, static_cast<int64_t>(pl.nqb) * p->B, 1024, pl.nsplit2, pl.kps2);
   return pl;
 }
 

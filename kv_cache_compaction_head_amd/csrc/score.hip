@@ -151,9 +151,11 @@ __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
   };
   // running max m (a score, exact in fp32) and sum l = sum exp(s - m) in fp64:
   // each 16-term tile sum is formed in fp32, then accumulated in double, and
-  // the rare rescale on a new maximum uses a double exp.
-  float m = -INFINITY;
-  double l = 0.0;
+  // the rare rescale on a new maximum uses a double exp.  The exponent is
+  // s*log2e - m2 with m*log2e = m2 + m2lo (m2 the fp32 rounding); the factor
+  // 2^-m2lo is applied once per sum, in double (cm).
+  float m = -INFINITY, m2 = 0.f;
+  double l = 0.0, cm = 1.0;
   if (ntile > 0) {
     fetch(j0);
     stash(0);
@@ -171,26 +173,31 @@ __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
         acc = Frag<In>::mma(a, bq[ks], acc);
       }
       float tmax = -INFINITY;
-      const uint64_t mb = MASK ? sMb[cur] : 0;
+      if (!MASK && jt + BN <= j1) {  // a whole tile: no key past the split
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = st * 32 + mfma32_row(r, lane), j = jt + kk;
-        const float s = (j < j1 && !((mb >> kk) & 1)) ? acc[r] : -INFINITY;
-        acc[r] = s;
-        tmax = fmaxf(tmax, s);
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, acc[r]);
+      } else {
+        const uint64_t mb = MASK ? sMb[cur] : 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = st * 32 + mfma32_row(r, lane), j = jt + kk;
+          const float s = (j < j1 && !((mb >> kk) & 1)) ? acc[r] : -INFINITY;
+          acc[r] = s;
+          tmax = fmaxf(tmax, s);
+        }
       }
       if (tmax > m) {
         if (m != -INFINITY) l *= exp(static_cast<double>(m) - static_cast<double>(tmax));
         m = tmax;
+        m2 = m * KVC_LOG2E;
+        const float m2lo = fmaf(m, KVC_LOG2E, -m2);  // m*log2e = m2 + m2lo exactly
+        cm = exp2(-static_cast<double>(m2lo));
       }
       if (m != -INFINITY) {
-        const float m2 = m * KVC_LOG2E;
-        const float m2lo = fmaf(m, KVC_LOG2E, -m2);  // m*log2e = m2 + m2lo exactly
         float sum = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          sum += __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -m2) - m2lo);
-        l += static_cast<double>(sum);
+        for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -m2));
+        l = fma(static_cast<double>(sum), cm, l);
       }
     }
     if (it + 1 < ntile) stash(cur ^ 1);
@@ -312,6 +319,7 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
   const double l2 = q < n ? lse[static_cast<size_t>(b) * n + q] * 1.4426950408889634 : 0.0;
   const float ml2 = static_cast<float>(l2);
   const float ml2lo = static_cast<float>(l2 - static_cast<double>(ml2));
+  const bool qok = q < n;
 
   f32x16 accO[ND];
 #pragma unroll
@@ -377,14 +385,24 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
         acc = Frag<In>::mma(a, bq[ks], acc);
       }
       float w[16];
-      const uint64_t mb = MASK ? sMb[cur] : 0;
+      if (!MASK && valid >= BN) {  // a whole tile: only the query bound
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = st * 32 + mfma32_row(r, lane);
-        const float e = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2) - ml2lo);
-        const float p = (kk < valid && q < n && !((mb >> kk) & 1)) ? e : 0.f;
-        acc[r] = p;
-        w[r] = RMS ? p * p : p;
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2) - ml2lo);
+          const float p = qok ? e : 0.f;
+          acc[r] = p;
+          w[r] = RMS ? p * p : p;
+        }
+      } else {
+        const uint64_t mb = MASK ? sMb[cur] : 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = st * 32 + mfma32_row(r, lane);
+          const float e = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2) - ml2lo);
+          const float p = (kk < valid && qok && !((mb >> kk) & 1)) ? e : 0.f;
+          acc[r] = p;
+          w[r] = RMS ? p * p : p;
+        }
       }
       {
         const float tot = half_wave_rowsum(w, lane);

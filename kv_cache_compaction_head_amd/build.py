@@ -22,6 +22,9 @@ def build(verbose: bool = False) -> str:
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # packed fp32 arithmetic stays off: plain scalar/float2 code only
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # MFMA results in ordinary VGPRs: no accumulator-register copies
+           # around the softmax arithmetic, fewer spills in the sweep kernels
+           "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            *srcs, "-o", tmp]
     if verbose:

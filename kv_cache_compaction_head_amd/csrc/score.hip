@@ -258,27 +258,40 @@ __device__ __forceinline__ int vt_pos(int kk) {
 
 // Sum of v[0..15] (accumulator rows) over the 32 lanes of this lane's half
 // wave; the result for row 8*b4 + 4*b3 + 2*b2 + b1 (b_i = bit i of the lane)
-// ends up in both lanes of the pair differing in bit 0.
+// ends up in both lanes of the pair differing in bit 0.  Each level halves the
+// values a lane keeps and adds its partner's copy of the same rows, with
+// VALU cross-lane moves only: v_permlane16_swap pairs lane l with l ^ 16 (it
+// exchanges odd 16-lane rows of one register with even rows of another, so
+// swapping v[i] and v[8+i] leaves each lane its kept half plus the partner's
+// matching half), DPP row_ror:8 pairs l with l ^ 8 within a row,
+// row_half_mirror pairs l with 7 - l within 8 lanes (the partner has the
+// other bit 2), and quad permutations pair bits 1 and 0.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
 __device__ __forceinline__ float half_wave_rowsum(const float (&v)[16], int lane) {
-  const bool b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+  const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
   float w[8], x[4], y[2];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float keep = b4 ? v[8 + i] : v[i], send = b4 ? v[i] : v[8 + i];
-    w[i] = keep + __shfl_xor(send, 16);
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[8 + i]),
+                                                    false, false);
+    w[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float keep = b3 ? w[4 + i] : w[i], send = b3 ? w[i] : w[4 + i];
-    x[i] = keep + __shfl_xor(send, 8);
+    x[i] = keep + dpp_f32<0x128>(send);  // row_ror:8
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const float keep = b2 ? x[2 + i] : x[i], send = b2 ? x[i] : x[2 + i];
-    y[i] = keep + __shfl_xor(send, 4);
+    y[i] = keep + dpp_f32<0x141>(send);  // row_half_mirror
   }
-  const float z = (b1 ? y[1] : y[0]) + __shfl_xor(b1 ? y[0] : y[1], 2);
-  return z + __shfl_xor(z, 1);
+  const float z = (b1 ? y[1] : y[0]) + dpp_f32<0x4E>(b1 ? y[0] : y[1]);  // quad_perm 2,3,0,1
+  return z + dpp_f32<0xB1>(z);                                           // quad_perm 1,0,3,2
 }
 
 template <class In, int D, bool RMS, bool MASK>

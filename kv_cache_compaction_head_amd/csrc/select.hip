@@ -60,11 +60,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
                                                         const int32_t* __restrict__ tv,
                                                         const uint8_t* __restrict__ mask, int T,
                                                         int t) {
-  __shared__ unsigned int hist[256];
+  // one 256-bin histogram per wave: no contention between waves on the few
+  // top-byte bins most keys share; the digit is then found by a parallel scan
+  // of the combined bins
+  __shared__ unsigned int hist[kSelThreads / 64][256];
   __shared__ int scratch[64];
   __shared__ unsigned int s_prefix, s_mask;
   __shared__ int s_need, s_bad;
-  const int b = blockIdx.x, tid = threadIdx.x;
+  const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
   const unsigned int* u = reinterpret_cast<const unsigned int*>(imp) + static_cast<size_t>(b) * T;
   const uint8_t* mb = mask ? mask + static_cast<size_t>(b) * T : nullptr;
   auto key = [&](int j) -> unsigned int {
@@ -81,29 +84,34 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
   }
   __syncthreads();
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+    for (int i = tid; i < (kSelThreads / 64) * 256; i += kSelThreads) (&hist[0][0])[i] = 0;
     __syncthreads();
     const unsigned int prefix = s_prefix, mask = s_mask;
-    for (int j = tid; j < T; j += kSelThreads) {
-      if (shift == 24 && u[j] >= 0x7f800000u) s_bad = 1;  // inf / nan (non-negative inputs)
-      const unsigned int v = key(j);
-      if ((v & mask) == prefix) atomicAdd(&hist[(v >> shift) & 255u], 1u);
+    unsigned int* hw = hist[wave];
+    for (int j0 = 0; j0 < T; j0 += kSelThreads) {
+      const int j = j0 + tid;
+      bool in = false;
+      unsigned int dig = 0;
+      if (j < T) {
+        if (shift == 24 && u[j] >= 0x7f800000u) s_bad = 1;  // inf / nan (non-negative inputs)
+        const unsigned int v = key(j);
+        in = (v & mask) == prefix;
+        dig = (v >> shift) & 255u;
+      }
+      if (in) atomicAdd(&hw[dig], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      int need = s_need;
-      unsigned int cum = 0;
-      int digit = 0;
-      for (int bin = 255; bin >= 0; --bin) {
-        const unsigned int h = hist[bin];
-        if (cum + h >= static_cast<unsigned int>(need)) {
-          digit = bin;
-          break;
-        }
-        cum += h;
-      }
-      s_need = need - static_cast<int>(cum);
-      s_prefix = prefix | (static_cast<unsigned int>(digit) << shift);
+    // digit of the need-th largest: scan the bins from the top (bin 255 first)
+    unsigned int h = 0;
+    if (tid < 256)
+      for (int w = 0; w < kSelThreads / 64; ++w) h += hist[w][255 - tid];
+    int tot;
+    const int above = block_exclusive_scan(static_cast<int>(h), scratch, &tot);
+    const int need = s_need;
+    __syncthreads();
+    if (tid < 256 && above < need && above + static_cast<int>(h) >= need) {
+      s_need = need - above;
+      s_prefix = prefix | (static_cast<unsigned int>(255 - tid) << shift);
       s_mask = mask | (255u << shift);
     }
     __syncthreads();

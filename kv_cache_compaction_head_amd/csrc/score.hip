@@ -389,7 +389,7 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
   for (int it = 0; it < ntile; ++it) {
     const int cur = it & 1, jt = j0 + it * BN, valid = j1 - jt;
     if (it + 1 < ntile) fetch(jt + BN);
-#pragma unroll 1
+#pragma unroll
     for (int st = 0; st < 2; ++st) {
       f32x16 acc = {};
 #pragma unroll

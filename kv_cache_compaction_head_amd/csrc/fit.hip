@@ -656,45 +656,35 @@ __device__ __forceinline__ bool small_ldl(int k) {
   for (int b = 0; b < nb; ++b) {
     const int o = b * 16, o2 = o + 16;
     if (wave == 0) {
-      // lane l holds row r = l/4, columns c4..c4+3 of the block; the pivot
-      // row's entries reach the other lanes by lane shuffles (row m lives in
-      // lanes 4m..4m+3, and the block stays symmetric under sweeping, so
-      // A[r][m] sits in lane 4r + m/4)
-      const int r = lane >> 2, c4 = (lane & 3) * 4;
-      double a[4], sgv[16];
+      // lane c < 16 holds column c of the block in registers; pivot m's
+      // column (= its row, the block staying symmetric under sweeping)
+      // reaches every lane as wave-uniform values read from lane m
+      const int c = lane & 15;
+      double a[16];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) a[j] = sm.pp[o + r][o + c4 + j];
-#pragma unroll
-      for (int m = 0; m < 16; ++m) sgv[m] = o + m < k ? sm.sgn[o + m] : 1.0;
+      for (int r = 0; r < 16; ++r) a[r] = sm.pp[o + r][o + c];
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
-        // the pivot (lane 4m + m/4, slot m%4) as a wave-uniform value, read
-        // directly so the division overlaps the shuffles below
-        double d = rdlane(a[m & 3], 4 * m + (m >> 2));
-        double rc[4];
+        double sr[16];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) rc[j] = __shfl(a[j], 4 * m + (lane & 3));
-        const double arm = __shfl(a[m & 3], (lane & ~3) + (m >> 2));
-        if (r == m) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            sm.sLb[m][c4 + j] = c4 + j < m ? -a[j] : (c4 + j == m ? 1.0 : 0.0);
-        }
-        if (!(d * sgv[m] > 0.0)) {
+        for (int r = 0; r < 16; ++r) sr[r] = rdlane(a[r], m);
+        const double sg = o + m < k ? sm.sgn[o + m] : 1.0;
+        double d = sr[m];
+        if (!(d * sg > 0.0)) {
           bad = true;
-          d = sgv[m];
+          d = sg;
         }
         const double rd = 1.0 / d;
+        if (lane < 16) sm.sLb[m][c] = c < m ? -a[m] : (c == m ? 1.0 : 0.0);
         if (lane == 0) sm.rD[o + m] = rd;
-        const double f = arm * rd;
-        const bool isrow = r == m;
+        const bool piv = c == m;
+        const double tm = a[m] * rd;  // row m of this column, scaled
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const double gen = fma(-f, rc[j], a[j]);
-          const double v = isrow ? rc[j] * rd : gen;
-          const double vp = isrow ? -rd : f;
-          a[j] = c4 + j == m ? vp : v;
+        for (int r = 0; r < 16; ++r) {
+          if (r == m) continue;
+          a[r] = piv ? sr[r] * rd : fma(-sr[r], tm, a[r]);
         }
+        a[m] = piv ? -rd : tm;
       }
     }
     __syncthreads();
@@ -1064,7 +1054,8 @@ __device__ __noinline__ bool sweep_step(const SweepMat M, Team& tm, int k, int s
     // W' D^-1 W'^T with W' = A[P', P] L^-T, taken from S before any member
     // updates it and formed in LDS while the others build the bands
     const int wr = wave >> 1, wc = wave & 1, g16 = lane >> 4, l16 = lane & 15;
-    double ua[2][16];
+    double ua[2][16], app[kSB * kSB / kTeamThreads];
+    // both gathers at once: A[P', P] for W' and A[P', P'] for the block
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int ra = wr * 32 + x * 16 + l16;
@@ -1074,6 +1065,12 @@ __device__ __noinline__ bool sweep_step(const SweepMat M, Team& tm, int k, int s
         const bool ok = ra < kn && q < k;
         ua[x][kk] = s_at_or0(M, ok, ok ? sm.piv2[ra] : 0, ok ? sm.piv[q] : 0);
       }
+    }
+#pragma unroll
+    for (int i = 0; i < kSB * kSB / kTeamThreads; ++i) {
+      const int e = tid + i * kTeamThreads, a = e >> 6, c = e & 63;
+      const bool in = a < kn && c < kn;
+      app[i] = s_at_or0(M, in, in ? sm.piv2[a] : 0, in ? sm.piv2[c] : 0);
     }
     f64x4 wa[2][2] = {};
 #pragma unroll
@@ -1088,11 +1085,11 @@ __device__ __noinline__ bool sweep_step(const SweepMat M, Team& tm, int k, int s
       }
     }
     __syncthreads();  // B and L^-1 of this step are no longer read here
-    for (int e = tid; e < kSB * kSB; e += kTeamThreads) {
-      const int a = e >> 6, c = e & 63;
+#pragma unroll
+    for (int i = 0; i < kSB * kSB / kTeamThreads; ++i) {
+      const int e = tid + i * kTeamThreads, a = e >> 6, c = e & 63;
       const bool in = a < kn && c < kn;
-      const double v = s_at_or0(M, in, in ? sm.piv2[a] : 0, in ? sm.piv2[c] : 0);
-      sm.pp[a][c] = in ? v : (a == c ? 1.0 : 0.0);
+      sm.pp[a][c] = in ? app[i] : (a == c ? 1.0 : 0.0);
     }
 #pragma unroll
     for (int x = 0; x < 2; ++x)

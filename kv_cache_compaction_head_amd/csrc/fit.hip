@@ -219,34 +219,34 @@ __global__ __launch_bounds__(256) void k_atb(const double* __restrict__ A, size_
 }
 
 // Sum the ksplit row slices of each tile in order and store (mirrored for
-// symmetric products).  grid (tiles, B), block 256.
+// symmetric products).  grid (tiles * 16, B), block 256: one element of a
+// tile per thread, its ksplit partials loaded together.
 template <bool SYM>
 __global__ __launch_bounds__(256) void k_atb_reduce(const double* __restrict__ part,
                                                     double* __restrict__ C, size_t sC, int ldc,
                                                     const int32_t* __restrict__ msz, int mA_const,
                                                     int mB_const, int tiles_x, int ntiles,
                                                     int ksplit) {
-  const int b = blockIdx.y;
+  const int b = blockIdx.y, tile = blockIdx.x >> 4;
   const int mA = msz ? msz[b] : mA_const;
   const int mB = SYM ? mA : mB_const;
   int ty, tx;
-  if (SYM) tri_decode(blockIdx.x, ty, tx);
+  if (SYM) tri_decode(tile, ty, tx);
   else {
-    ty = blockIdx.x / tiles_x;
-    tx = blockIdx.x % tiles_x;
+    ty = tile / tiles_x;
+    tx = tile % tiles_x;
   }
   const int a0 = ty * kTile, c0 = tx * kTile;
   if (a0 >= mA || c0 >= mB) return;
   double* Cb = C + b * sC;
-  const double* P = part + (static_cast<size_t>(b) * ksplit * ntiles + blockIdx.x) * (kTile * kTile);
-  for (int e = threadIdx.x; e < kTile * kTile; e += 256) {
-    const int r = a0 + e / kTile, c = c0 + e % kTile;
-    double v = 0.0;
-    for (int sp = 0; sp < ksplit; ++sp) v += P[static_cast<size_t>(sp) * ntiles * kTile * kTile + e];
-    if (r < mA && c < mB) {
-      Cb[static_cast<size_t>(r) * ldc + c] = v;
-      if (SYM && tx != ty) Cb[static_cast<size_t>(c) * ldc + r] = v;
-    }
+  const double* P = part + (static_cast<size_t>(b) * ksplit * ntiles + tile) * (kTile * kTile);
+  const int e = (blockIdx.x & 15) * 256 + threadIdx.x;
+  const int r = a0 + e / kTile, c = c0 + e % kTile;
+  double v = 0.0;
+  for (int sp = 0; sp < ksplit; ++sp) v += P[static_cast<size_t>(sp) * ntiles * kTile * kTile + e];
+  if (r < mA && c < mB) {
+    Cb[static_cast<size_t>(r) * ldc + c] = v;
+    if (SYM && tx != ty) Cb[static_cast<size_t>(c) * ldc + r] = v;
   }
 }
 
@@ -1500,8 +1500,8 @@ static void launch_atb(const double* A, size_t sA, int lda, const int32_t* colA,
   hipLaunchKernelGGL((k_atb<TB, SYM>), dim3(ntiles, ksplit, B), dim3(256), 0, st, A, sA, lda,
                      colA, sColA, Bm, sB, ldb, C, sC, ldc, nrows, msz, mA, mB, tb, part, ntiles);
   if (ksplit > 1)
-    hipLaunchKernelGGL((k_atb_reduce<SYM>), dim3(ntiles, B), dim3(256), 0, st, part, C, sC, ldc,
-                       msz, mA, mB, tb, ntiles, ksplit);
+    hipLaunchKernelGGL((k_atb_reduce<SYM>), dim3(ntiles * 16, B), dim3(256), 0, st, part, C, sC,
+                       ldc, msz, mA, mB, tb, ntiles, ksplit);
 }
 
 int sweep_ld(int t, int D) {

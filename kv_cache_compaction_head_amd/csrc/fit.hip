@@ -519,7 +519,7 @@ struct __align__(16) SweepSmem {
   double rD[kSB];                  // 1 / D (0 past k)
   double sW[kSB][17];              // small inverse: panel of a 16-pivot block,
   double sV[kSB][17];              // and L[b, <b] L^-1[<b, <b] (16 x 48)
-  double sLb[16][17];              // L^-1 of a 16 x 16 diagonal block, its pivot row
+  double sLb[2][16][17];           // L^-1 of a 16 x 16 diagonal block (two in flight)
   double mbc[16];
   double sgn[kSB];                 // s_q
   int piv[kSB];                    // matrix row of pivot q
@@ -618,23 +618,17 @@ __device__ int wg_append(bool f, int base, int* slot) {
   return tot;
 }
 
-// The pivot block sm.pp[0:k][0:k] = A_PP = L D L^T (overwritten): a
-// right-looking blocked factorization (blocks of 16 pivots) with L^-1 by
-// blocked triangular inversion; small_b then forms B = A_PP^-1 =
-// L^-T D^-1 L^-1 on fp64 MFMA.  Per
-// block: one wave sweeps the current 16 x 16 diagonal block pivot by pivot
-// (the pivot row goes through LDS; a wave's LDS accesses are performed in
-// order, so no barrier is needed); before sweep p its pivot row holds
-// -L_bb^-1[p][j] at the swept columns j < p and the pivot on the diagonal.
-// Then the rows of L^-1 left of the block, -L_bb^-1 (L[b, <b] L^-1[<b, <b]),
-// the panel L[>b, b] = A[>b, b] L_bb^-T D_b^-1 and the trailing update
-// A[>b, >b] -= W D_b^-1 W^T (W = A[>b, b] L_bb^-T).  Inverting the pivot block
-// by a blocked sweep instead would form its off-diagonal parts through
-// explicit inverses of the 16 x 16 blocks and lose them when those are
-// ill-conditioned.  Results: sm.li = L^-1 (identity past k), sm.rD = 1/D
-// (0 past k).  A pivot without the sign s_p is replaced by s_p (the system is
-// not numerically definite); the return value, meaningful in wave 0, says
-// whether that happened.
+// The pivot block sm.pp[0:k][0:k] = A_PP = L D L^T (small_ldl; sm.pp is
+// overwritten) gives sm.li = L^-1 (identity past k) and sm.rD = 1/D (0 past
+// k); small_b then forms B = A_PP^-1 = L^-T D^-1 L^-1 on fp64 MFMA.  The
+// factorization is blocked by 16 pivots; a diagonal block is swept pivot by
+// pivot, and before sweep p its pivot row holds -L_bb^-1[p][j] at the swept
+// columns j < p and the pivot on the diagonal.  Inverting the pivot block by
+// a blocked sweep instead would form its off-diagonal parts through explicit
+// inverses of the 16 x 16 blocks and lose them when those are
+// ill-conditioned.  A pivot without the sign s_p is replaced by s_p (the
+// system is not numerically definite); small_ldl's return value, meaningful
+// in wave 0, says whether that happened.
 // Lane src's value of v, for the whole wave (two 32-bit lane reads).
 __device__ __forceinline__ double rdlane(double v, int src) {
   const unsigned long long u = __double_as_longlong(v);
@@ -643,130 +637,159 @@ __device__ __forceinline__ double rdlane(double v, int src) {
   return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
 }
 
+// Wave 0 sweeps the 16 x 16 diagonal block at o of sm.pp: lane c < 16 holds
+// column c in registers; pivot m's column (= its row, the block staying
+// symmetric under sweeping) reaches every lane as wave-uniform values read
+// from lane m.  Records -L^-1 of the block (the pivot rows at their turn)
+// into sL and 1/D into sm.rD[o..o+15].  Returns whether a pivot lacked its
+// sign (replaced by the sign).
+__device__ __forceinline__ bool diag_sweep(int o, int k, double (*sL)[17]) {
+  SweepSmem& sm = g_sw;
+  const int lane = threadIdx.x & 63, c = lane & 15;
+  bool bad = false;
+  double a[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) a[r] = sm.pp[o + r][o + c];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    double sr[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sr[r] = rdlane(a[r], m);
+    const double sg = o + m < k ? sm.sgn[o + m] : 1.0;
+    double d = sr[m];
+    if (!(d * sg > 0.0)) {
+      bad = true;
+      d = sg;
+    }
+    const double rd = 1.0 / d;
+    if (lane < 16) sL[m][c] = c < m ? -a[m] : (c == m ? 1.0 : 0.0);
+    if (lane == 0) sm.rD[o + m] = rd;
+    const bool piv = c == m;
+    const double tm = a[m] * rd;  // row m of this column, scaled
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (r == m) continue;
+      a[r] = piv ? sr[r] * rd : fma(-sr[r], tm, a[r]);
+    }
+    a[m] = piv ? -rd : tm;
+  }
+  return bad;
+}
+
+// Pipelined blocked L D L^T of the pivot block (16-pivot blocks b): wave 0
+// runs the chain the next block waits for -- the sweep of diagonal block b,
+// then block b+1's panel rows W = A[b+1, b] L_bb^-T and its diagonal update
+// A[b+1, b+1] -= W D_b^-1 W^T -- while waves 1-3 do the rest of block b:
+// rows b of L^-1 (-L_bb^-1 L[b, <b] L^-1[<b, <b]), the diagonal block of
+// L^-1, the trailing lower blocks other than (b+1, b+1), and the panel L[>b+1,
+// b] = W D_b^-1.  Each bulk wave forms the panel rows it needs itself, so one
+// workgroup barrier per block suffices; L is parked above the diagonal of
+// sm.li, transposed (L[r][c] at li[c][r]), and cleared at the end.
 __device__ __forceinline__ bool small_ldl(int k) {
   SweepSmem& sm = g_sw;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wr = wave >> 1, wc = wave & 1, g16 = lane >> 4, l16 = lane & 15;
+  const int g16 = lane >> 4, l16 = lane & 15;
   bool bad = false;
-  const int nb = (k + 15) >> 4;
+  const int nb = (k + 15) >> 4, kb = 16 * nb;
   for (int e = tid; e < kSB * kSB; e += kTeamThreads) {
     const int r = e >> 6, c = e & 63;
-    if (r >= 16 * nb || c >= r) sm.li[r][c] = r == c ? 1.0 : 0.0;
+    if (r >= kb || c >= r) sm.li[r][c] = r == c ? 1.0 : 0.0;
   }
-  for (int b = 0; b < nb; ++b) {
-    const int o = b * 16, o2 = o + 16;
+  if (wave == 0) bad = diag_sweep(0, k, sm.sLb[0]);
+  for (int j = 0; j < nb; ++j) {
+    const int o = 16 * j, o2 = o + 16;
+    __syncthreads();  // block j swept, the bulk work of block j - 1 done
+    double(*sL)[17] = sm.sLb[j & 1];
     if (wave == 0) {
-      // lane c < 16 holds column c of the block in registers; pivot m's
-      // column (= its row, the block staying symmetric under sweeping)
-      // reaches every lane as wave-uniform values read from lane m
-      const int c = lane & 15;
-      double a[16];
+      if (j + 1 < nb) {
+        // W = A[b+1, b] L_bb^-T (W[i][q] = sum_m A[o2+i][o+m] sL[q][m]) and
+        // then A[b+1, b+1] -= W D^-1 W^T, each four fp64 MFMAs
+        f64x4 w4 = {};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) a[r] = sm.pp[o + r][o + c];
-#pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        double sr[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sr[r] = rdlane(a[r], m);
-        const double sg = o + m < k ? sm.sgn[o + m] : 1.0;
-        double d = sr[m];
-        if (!(d * sg > 0.0)) {
-          bad = true;
-          d = sg;
+        for (int ks = 0; ks < 4; ++ks) {
+          const int m = 4 * ks + g16;
+          w4 = __builtin_amdgcn_mfma_f64_16x16x4f64(sm.pp[o2 + l16][o + m], sL[l16][m], w4, 0, 0, 0);
         }
-        const double rd = 1.0 / d;
-        if (lane < 16) sm.sLb[m][c] = c < m ? -a[m] : (c == m ? 1.0 : 0.0);
-        if (lane == 0) sm.rD[o + m] = rd;
-        const bool piv = c == m;
-        const double tm = a[m] * rd;  // row m of this column, scaled
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (r == m) continue;
-          a[r] = piv ? sr[r] * rd : fma(-sr[r], tm, a[r]);
+        for (int x = 0; x < 4; ++x) {
+          const int i = g16 + 4 * x;  // W[i][l16]
+          sm.sW[i][l16] = w4[x];
+          sm.li[o + l16][o2 + i] = w4[x] * sm.rD[o + l16];  // L[o2 + i][o + l16], parked
         }
-        a[m] = piv ? -rd : tm;
-      }
-    }
-    __syncthreads();
-    // T = L[b, <b] L^-1[<b, <b] (into sV, 16 x o) and the panel
-    // W = A[>b, b] L_bb^-T (into sW, zero above the panel)
-    double* T = &sm.sV[0][0];
-    if (wave < b) {  // wave w: columns 16w.. of T; L^-1 rows are zero left of their column
-      const int jb = wave * 16;
-      f64x4 t4 = {};
-      for (int i0 = jb; i0 < o; i0 += 4) {
-        const int i = i0 + g16;
-        t4 = __builtin_amdgcn_mfma_f64_16x16x4f64(sm.pp[o + l16][i], sm.li[i][jb + l16], t4, 0, 0, 0);
-      }
+        f64x4 d4 = {};
 #pragma unroll
-      for (int x = 0; x < 4; ++x) T[(g16 + 4 * x) * 48 + jb + l16] = t4[x];
-    }
-    {
-      const int i = tid >> 2, q0 = (tid & 3) * 4;
-      double u[16];
-#pragma unroll
-      for (int m = 0; m < 16; ++m) u[m] = i >= o2 ? sm.pp[i][o + m] : 0.0;
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int q = q0 + qq;
-        double w = 0.0;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) w = fma(u[m], sm.sLb[q][m], w);
-        sm.sW[i][q] = w;
-      }
-    }
-    __syncthreads();
-    // rows o..o+15 of L^-1: -L_bb^-1 T left of the block
-    if (wave < b) {
-      const int jb = wave * 16;
-      f64x4 t4 = {};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int m2 = 4 * ks + g16;
-        t4 = __builtin_amdgcn_mfma_f64_16x16x4f64(sm.sLb[l16][m2], T[m2 * 48 + jb + l16], t4, 0, 0, 0);
-      }
-#pragma unroll
-      for (int x = 0; x < 4; ++x) sm.li[o + g16 + 4 * x][jb + l16] = -t4[x];
-    }
-    {
-      const int m = tid >> 4, j = tid & 15;
-      if (j < m) sm.li[o + m][o + j] = sm.sLb[m][j];
-    }
-    // panel of L and trailing update on MFMA
-    f64x4 acc[2][2] = {};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int q = 4 * ks + g16;
-      const double rdq = sm.rD[o + q];
-      double av[2], bv[2];
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        av[x] = sm.sW[wr * 32 + x * 16 + l16][q] * rdq;
-        bv[x] = sm.sW[wc * 32 + x * 16 + l16][q];
-      }
-#pragma unroll
-      for (int ra = 0; ra < 2; ++ra)
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          acc[ra][rb] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ra], bv[rb], acc[ra][rb], 0, 0, 0);
-    }
-#pragma unroll
-    for (int ra = 0; ra < 2; ++ra)
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = wr * 32 + ra * 16 + g16 + 4 * i, col = wc * 32 + rb * 16 + l16;
-          if (row < o2) continue;
-          if (col >= o2) sm.pp[row][col] -= acc[ra][rb][i];
-          else if (col >= o) sm.pp[row][col] = sm.sW[row][col - o] * sm.rD[col];
+        for (int ks = 0; ks < 4; ++ks) {
+          const int q = 4 * ks + g16;
+          d4 = __builtin_amdgcn_mfma_f64_16x16x4f64(sm.sW[l16][q] * sm.rD[o + q], sm.sW[l16][q], d4,
+                                                    0, 0, 0);
         }
-    __syncthreads();
+#pragma unroll
+        for (int x = 0; x < 4; ++x) sm.pp[o2 + g16 + 4 * x][o2 + l16] -= d4[x];
+        bad |= diag_sweep(o2, k, sm.sLb[(j + 1) & 1]);
+      }
+    } else {
+      const int w = wave - 1;
+      if (w < j) {  // rows o..o+15 of L^-1, columns 16w..16w+15
+        const int jb = 16 * w;
+        double* T = &sm.sV[0][0];
+        f64x4 t4 = {};
+        for (int i0 = jb; i0 < o; i0 += 4) {
+          const int i = i0 + g16;
+          t4 = __builtin_amdgcn_mfma_f64_16x16x4f64(sm.li[i][o + l16], sm.li[i][jb + l16], t4, 0, 0, 0);
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) T[(g16 + 4 * x) * 48 + jb + l16] = t4[x];
+        f64x4 u4 = {};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int m2 = 4 * ks + g16;
+          u4 = __builtin_amdgcn_mfma_f64_16x16x4f64(sL[l16][m2], T[m2 * 48 + jb + l16], u4, 0, 0, 0);
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) sm.li[o + g16 + 4 * x][jb + l16] = -u4[x];
+      }
+      for (int e = tid - 64; e < 256; e += 192) {
+        const int m = e >> 4, jj = e & 15;
+        if (jj < m) sm.li[o + m][o + jj] = sL[m][jj];
+      }
+      // trailing lower blocks (r, c), r >= c > j, but (j + 1, j + 1)
+      int idx = 0;
+      for (int r = j + 1; r < nb; ++r)
+        for (int c = j + 1; c <= r; ++c) {
+          if (r == j + 1 && c == j + 1) continue;
+          if (idx++ % 3 != w) continue;
+          f64x4 acc = {};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const int q = 4 * ks + g16;
+            double wa = 0.0, wb = 0.0;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+              const double lq = sL[q][m];
+              wa = fma(sm.pp[16 * r + l16][o + m], lq, wa);
+              wb = fma(sm.pp[16 * c + l16][o + m], lq, wb);
+            }
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(wa * sm.rD[o + q], wb, acc, 0, 0, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sm.pp[16 * r + g16 + 4 * i][16 * c + l16] -= acc[i];
+        }
+      // the panel of L for rows past block j + 1, parked
+      for (int e = tid - 64; e < (kb - o2 - 16) * 16; e += 192) {
+        const int row = o2 + 16 + (e >> 4), q = e & 15;
+        double w2 = 0.0;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) w2 = fma(sm.pp[row][o + m], sL[q][m], w2);
+        sm.li[o + q][row] = w2 * sm.rD[o + q];
+      }
+    }
   }
-  // past k: identity rows and columns of L^-1, no pivot
+  __syncthreads();
+  // clear the parked L; past k: identity rows and columns of L^-1, no pivot
   for (int e = tid; e < kSB * kSB; e += kTeamThreads) {
     const int r = e >> 6, c = e & 63;
-    if ((r >= k || c >= k) && c <= r) sm.li[r][c] = r == c ? 1.0 : 0.0;
+    if (c > r) sm.li[r][c] = 0.0;
+    else if (r >= k || c >= k) sm.li[r][c] = r == c ? 1.0 : 0.0;
   }
   if (tid >= k && tid < kSB) sm.rD[tid] = 0.0;
   __syncthreads();

@@ -347,7 +347,7 @@ __global__ __launch_bounds__(1024) void k_bias_prep(double* __restrict__ S, size
 // Teams.  The iterative parts of the fits (the NNLS pivoting rounds and the
 // value system's sweeps) run in cooperative launches:
 // each head gets a team of g co-resident workgroups synchronised by
-// team_sync, a barrier through a counter in global memory.
+// team_sync, a barrier through per-member flags in global memory.
 //
 // Placement and coherence: workgroups are dispatched round-robin over the
 // XCDs, so with nteams a multiple of 8, team = blockIdx mod nteams keeps a
@@ -388,7 +388,9 @@ __device__ __forceinline__ void sta(int32_t* p, int v) {
 
 struct Team {
   int rank, size;
-  unsigned* ctr;
+  unsigned* flag0;  // rank 0's arrival flag; rank r's is fstride * r words on
+  unsigned* mine;   // this workgroup's arrival flag
+  int fstride;      // words between consecutive ranks' flags
   unsigned gen;
   int* err;
   bool fast;
@@ -398,18 +400,22 @@ __device__ __forceinline__ int hw_xcc_id() {
   return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xf;  // HW_REG_XCC_ID[3:0]
 }
 
-// A barrier is an arrival (count this workgroup in, after its stores) and a
-// wait (until every member of the team has arrived).  team_sync does both; a
-// member that needs nothing the others produce before the barrier may arrive,
-// keep working, and wait later (team_wait before its next arrival, so the
-// cumulative count can never let a barrier pass early).
+// A barrier is an arrival (after its stores, the workgroup writes the number
+// of barriers it has reached into its own flag, a 64-byte slot) and a wait
+// (wave 0 reads every member's flag, one lane per member, until all have
+// reached this barrier).  One flag per member instead of one shared counter:
+// no atomic read-modify-writes queue on one address, and a single vector load
+// per poll sees every member.  team_sync does both; a member that needs
+// nothing the others produce before the barrier may arrive, keep working, and
+// wait later (team_wait before its next arrival: flags only grow, so a member
+// already at the next barrier still counts as arrived at this one).
 __device__ void team_arrive(Team& tm) {
   if (tm.size == 1) return;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are done
   __syncthreads();
   if (threadIdx.x == 0) {
     if (!tm.fast) __threadfence();
-    atomicAdd(tm.ctr, 1u);
+    __hip_atomic_store(tm.mine, tm.gen + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -418,19 +424,32 @@ __device__ void team_wait(Team& tm) {
     __syncthreads();
     return;
   }
-  if (threadIdx.x == 0) {
-    const unsigned target = (tm.gen + 1) * static_cast<unsigned>(tm.size);
+  if (threadIdx.x < 64) {
+    const unsigned target = tm.gen + 1;
+    const int lane = threadIdx.x;
     const uint64_t t0 = wall_clock64();
-    while (__hip_atomic_load(tm.ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      if (__hip_atomic_load(tm.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
-      if (wall_clock64() - t0 > kSpinTicks) {
-        atomicOr(tm.err, 1);
-        break;
+    unsigned spins = 0;
+    for (;;) {
+      bool in = true;
+      for (int r = lane; r < tm.size; r += 64)
+        in &= __hip_atomic_load(tm.flag0 + static_cast<size_t>(r) * tm.fstride, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT) >= target;
+      if (__all(in)) break;
+      // the time-out and the error flag every 32 polls: each is another round
+      // trip that would otherwise delay seeing the last arrival
+      if ((++spins & 31u) == 0) {
+        if (__hip_atomic_load(tm.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+        if (wall_clock64() - t0 > kSpinTicks) {
+          if (lane == 0) atomicOr(tm.err, 1);
+          break;
+        }
       }
       __builtin_amdgcn_s_sleep(1);
     }
-    if (tm.fast) asm volatile("buffer_inv sc1" ::: "memory");
-    else __threadfence();
+    if (lane == 0) {
+      if (tm.fast) asm volatile("buffer_inv sc1" ::: "memory");
+      else __threadfence();
+    }
   }
   tm.gen++;
   __syncthreads();
@@ -449,7 +468,9 @@ __device__ void team_setup(Team& tm, int& team, int& nteams, unsigned* bar, int*
   team = static_cast<int>(blockIdx.x % nteams);
   tm.rank = static_cast<int>(blockIdx.x / nteams);
   tm.size = static_cast<int>(gridDim.x / nteams);
-  tm.ctr = bar + team;
+  tm.fstride = kFlagStride * nteams;
+  tm.flag0 = bar + static_cast<size_t>(team) * kFlagStride;
+  tm.mine = bar + static_cast<size_t>(blockIdx.x) * kFlagStride;
   tm.gen = 0;
   tm.err = err;
   tm.fast = false;

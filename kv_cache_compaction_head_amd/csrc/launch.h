@@ -43,7 +43,7 @@ struct FitBufs {
   double* stage;  // [B][kSweepStage] inverse of the next pivot block (lookahead)
   int32_t *Fidx, *inv, *msz;
   const int32_t* tv;  // [B] per-head budgets (<= t), or null: t for every head
-  unsigned* bar;  // kBarWords words: team barrier counters, the last one the timeout flag
+  unsigned* bar;  // kBarWords words: team barrier flags (kFlagStride words per team workgroup), the last one the timeout flag
   int32_t* xcc;   // kMaxTeamGrid words: each team workgroup's XCC id
   double* flops;    // [B][2] fp64 work of the NNLS sweeps and of the value sweeps
   double* part;     // split-K partial tiles of the fit GEMMs
@@ -54,7 +54,8 @@ struct FitBufs {
 int sweep_ld(int t, int d);
 constexpr int kSweepStage = 2 * 64 * 64 + 64;
 constexpr int kMaxTeamGrid = 8192;
-constexpr int kBarWords = kMaxTeamGrid + 1;
+constexpr int kFlagStride = 16;  // one 64-byte slot per team workgroup's barrier flag
+constexpr int kBarWords = kMaxTeamGrid * kFlagStride + 1;
 template <class In, int D>
 hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const double* lse,
                       const float* O, const int32_t* idx, FitBufs fb, float* out_bias,

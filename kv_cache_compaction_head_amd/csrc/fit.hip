@@ -978,27 +978,66 @@ __device__ __forceinline__ void wave_tile(const SweepMat& M, int I, int J, int r
       wave_tile_mfma<NRA, NRB>(c + 1, diag, ro, co, a1, b1, acc);
     }
   }
-  int pc[NRB];
+  // pivot slots of this part's rows and columns (sm.pos is -1 off the
+  // pivots, inactive rows and columns included)
+  int pc[NRB], pr[NRA][4];
+  bool touch = false;
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
-    const int c = J * kSB + 16 * (co + rb) + l16;
-    pc[rb] = s_active(M, c) ? sm.pos[c] : -1;
+    pc[rb] = sm.pos[J * kSB + 16 * (co + rb) + l16];
+    touch |= pc[rb] >= 0;
+  }
+#pragma unroll
+  for (int ra = 0; ra < NRA; ++ra)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pr[ra][i] = sm.pos[I * kSB + 16 * (ro + ra) + g16 + 4 * i];
+      touch |= pr[ra][i] >= 0;
+    }
+  if (!__any(touch)) {
+    // no pivot row or column here: every entry takes T -= W_I D^-1 W_J^T.
+    // Entries of a row sit 16 doubles apart (immediate offsets from one row
+    // pointer).  Blocks strictly above the diagonal of a diagonal tile are
+    // skipped; inside a diagonal 16 x 16 block the upper entries are written
+    // too (their update is the mirror image and only the lower triangle is
+    // ever read).
+#pragma unroll
+    for (int rh = 0; rh < NRA; rh += 2) {
+      double x[2][NRB][4];
+      gdouble* row[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = I * kSB + 16 * (ro + rh + h) + g16 + 4 * i;
+          row[h][i] = M.S + static_cast<size_t>(r) * M.ld + J * kSB + 16 * co + l16;
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb)
+            if (!diag || co + rb <= ro + rh + h) x[h][rb][i] = row[h][i][16 * rb];
+        }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb)
+            if (!diag || co + rb <= ro + rh + h) row[h][i][16 * rb] = x[h][rb][i] - acc[rh + h][rb][i];
+    }
+    return;
   }
 #pragma unroll
   for (int rh = 0; rh < NRA; rh += 2) {
     // current values (or the V entries that replace them), one batch of loads
     double x[2][NRB][4];
-    int pr[2][4];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = I * kSB + 16 * (ro + rh + h) + g16 + 4 * i;
-        pr[h][i] = s_active(M, r) ? sm.pos[r] : -1;
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
           const int c = J * kSB + 16 * (co + rb) + l16;
-          const int q = pr[h][i], qc = pc[rb];
+          const int q = pr[rh + h][i], qc = pc[rb];
           const gdouble* src = qc >= 0 ? M.V + (static_cast<size_t>(r) * kSB + qc)
                              : q >= 0  ? M.V + (static_cast<size_t>(c) * kSB + q)
                                        : M.S + (static_cast<size_t>(r) * M.ld + c);
@@ -1014,7 +1053,7 @@ __device__ __forceinline__ void wave_tile(const SweepMat& M, int I, int J, int r
           const int r = I * kSB + 16 * (ro + rh + h) + g16 + 4 * i;
           const int c = J * kSB + 16 * (co + rb) + l16;
           if (diag && r < c) continue;
-          const int q = pr[h][i], qc = pc[rb];
+          const int q = pr[rh + h][i], qc = pc[rb];
           double v;
           if (q >= 0 && qc >= 0) v = -sm.sgn[q] * sm.sgn[qc] * sm.pp[q][qc];
           else if (qc >= 0) v = sm.sgn[qc] * x[h][rb][i];

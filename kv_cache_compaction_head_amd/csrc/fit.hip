@@ -525,7 +525,8 @@ constexpr int kTeamThreads = 256;
 //   A. every member gathers A_PP and inverts it in LDS by k single sweeps
 //      (the pivot blocks are quasi-definite, so each pivot is nonzero with
 //      the sign s_q); the pivot rows of those sweeps also give L^-1 and D.
-//      The members split the 64-row bands, gather U for theirs, form
+//      The members split the 32-row halves of the 64-row bands, gather U
+//      for theirs, form
 //      W = U L^-T and V = U B on fp64 MFMA and stage both in global memory;
 //   -- team barrier --
 //   B. the members split the 64 x 64 tiles of the lower triangle and update
@@ -851,58 +852,49 @@ __device__ __forceinline__ void small_b(int k) {
   __syncthreads();
 }
 
-// Phase A for one 64-row band (matrix rows band*64 ..): U = A[rows, P]
-// gathered from the lower triangle, W = U L^-T and V = U B on MFMA, stored
-// to M.U / M.V.
+// Phase A for one half of a 64-row band (matrix rows band*64 + 32*half ..,
+// 16 per wave pair): U = A[rows, P] gathered from the lower triangle, W =
+// U L^-T and V = U B on MFMA, stored to M.U / M.V.  Half bands, so that the
+// members share the bands evenly when there are fewer bands than members.
 // The contraction index is permuted so that each lane's 16 values of a row
 // are contiguous: in MFMA step kk, lane l supplies q = 16*(l/16) + kk.
-__device__ __forceinline__ void v_band(const SweepMat& M, int band, int k) {
+__device__ __forceinline__ void v_band(const SweepMat& M, int band, int half, int k) {
   SweepSmem& sm = g_sw;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wr = wave >> 1, wc = wave & 1, g16 = lane >> 4, l16 = lane & 15;
-  double u[2][16];
-#pragma unroll
-  for (int ra = 0; ra < 2; ++ra) {
-    const int s = band * kSB + wr * 32 + ra * 16 + l16;
+  const int s0 = band * kSB + 32 * half + 16 * wr;
+  double u[16];
+  {
+    const int s = s0 + l16;
     const bool act = s_active(M, s);
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
       const int q = g16 * 16 + kk;
       const bool ok = act && q < k;
-      u[ra][kk] = s_at_or0(M, ok, s, ok ? sm.piv[q] : 0);
+      u[kk] = s_at_or0(M, ok, s, ok ? sm.piv[q] : 0);
     }
   }
-  f64x4 acc[2][2] = {}, accw[2][2] = {};
+  f64x4 acc[2] = {}, accw[2] = {};
 #pragma unroll
   for (int kk = 0; kk < 16; ++kk) {
     const int q = g16 * 16 + kk;
-    double bb[2], bl[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const int c = wc * 32 + rb * 16 + l16;
-      bb[rb] = sm.pp[q][c];
-      bl[rb] = sm.li[c][q];
+      acc[rb] = __builtin_amdgcn_mfma_f64_16x16x4f64(u[kk], sm.pp[q][c], acc[rb], 0, 0, 0);
+      accw[rb] = __builtin_amdgcn_mfma_f64_16x16x4f64(u[kk], sm.li[c][q], accw[rb], 0, 0, 0);
     }
-#pragma unroll
-    for (int ra = 0; ra < 2; ++ra)
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        acc[ra][rb] = __builtin_amdgcn_mfma_f64_16x16x4f64(u[ra][kk], bb[rb], acc[ra][rb], 0, 0, 0);
-        accw[ra][rb] = __builtin_amdgcn_mfma_f64_16x16x4f64(u[ra][kk], bl[rb], accw[ra][rb], 0, 0, 0);
-      }
   }
 #pragma unroll
-  for (int ra = 0; ra < 2; ++ra)
+  for (int i = 0; i < 4; ++i) {
+    const size_t s = static_cast<size_t>(s0 + g16 + 4 * i);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t s = static_cast<size_t>(band * kSB + wr * 32 + ra * 16 + g16 + 4 * i);
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int c = wc * 32 + rb * 16 + l16;
-        M.V[s * kSB + c] = acc[ra][rb][i];
-        M.U[s * kSB + c] = accw[ra][rb][i];
-      }
+    for (int rb = 0; rb < 2; ++rb) {
+      const int c = wc * 32 + rb * 16 + l16;
+      M.V[s * kSB + c] = acc[rb][i];
+      M.U[s * kSB + c] = accw[rb][i];
     }
+  }
 }
 
 // Phase B, one wave per 64 x 64 tile, no barriers: the wave streams the
@@ -1107,13 +1099,17 @@ __device__ __noinline__ bool sweep_step(const SweepMat M, Team& tm, int k, int s
   const bool la = kn > 0 && tm.size > 1;
   const bool me_la = la && tm.rank == tm.size - 1;
   bool bad = false;
+  // pre: the previous step's lookahead member (the last rank) factored this
+  // pivot block and left L^-1 and 1/D in its own LDS; the others load them
   if (pre) {
-    for (int e = tid; e < kSB * kSB; e += kTeamThreads) {
-      const int r = e >> 6, c = e & 63;
-      sm.li[r][c] = M.stage[kSB * kSB + e];
+    if (tm.rank != tm.size - 1) {
+      for (int e = tid; e < kSB * kSB; e += kTeamThreads) {
+        const int r = e >> 6, c = e & 63;
+        sm.li[r][c] = M.stage[kSB * kSB + e];
+      }
+      if (tid < kSB) sm.rD[tid] = M.stage[2 * kSB * kSB + tid];
+      __syncthreads();
     }
-    if (tid < kSB) sm.rD[tid] = M.stage[2 * kSB * kSB + tid];
-    __syncthreads();
   } else {
     for (int e = tid; e < kSB * kSB; e += kTeamThreads) {
       const int a = e >> 6, c = e & 63;
@@ -1131,7 +1127,10 @@ __device__ __noinline__ bool sweep_step(const SweepMat M, Team& tm, int k, int s
   // built: the lookahead member needs L^-1 and D alone
   if (!me_la) small_b(k);
   if (!me_la) {
-    for (int bi = tm.rank; bi < nrb + nvb; bi += vmembers) v_band(M, bi < nrb ? bi : vb0 + bi - nrb, k);
+    for (int bi = tm.rank; bi < 2 * (nrb + nvb); bi += vmembers) {
+      const int b = bi >> 1;
+      v_band(M, b < nrb ? b : vb0 + b - nrb, bi & 1, k);
+    }
   } else {
     // the next pivot block after this step's update, A' = A[P', P'] -
     // W' D^-1 W'^T with W' = A[P', P] L^-T, taken from S before any member

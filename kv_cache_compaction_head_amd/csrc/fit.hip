@@ -574,6 +574,17 @@ struct SweepMat {
 constexpr int kStage = kSweepStage;
 static_assert(kSweepStage == 2 * kSB * kSB + kSB, "staging layout");
 __device__ __forceinline__ gdouble* gptr(double* p) { return (gdouble*)p; }
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ gdouble* uniform(gdouble* p) {
+  const unsigned long long u = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(u));
+  const unsigned hi = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(u >> 32));
+  return reinterpret_cast<gdouble*>((static_cast<unsigned long long>(hi) << 32) | lo);
+}
+__device__ __forceinline__ SweepMat uniform_mat(const SweepMat& m) {
+  return SweepMat{uniform(m.S),     uniform(m.U),    uniform(m.V),     uniform(m.stage),
+                  uniform(m.ld),    uniform(m.r_al), uniform(m.n_rhs), uniform(m.n_var)};
+}
 
 __device__ __forceinline__ size_t s_idx(const SweepMat& M, int i, int j) {
   return i >= j ? static_cast<size_t>(i) * M.ld + j : static_cast<size_t>(j) * M.ld + i;
@@ -651,6 +662,13 @@ __device__ int wg_append(bool f, int base, int* slot) {
 // ill-conditioned.  A pivot without the sign s_p is replaced by s_p (the
 // system is not numerically definite); small_ldl's return value, meaningful
 // in wave 0, says whether that happened.
+// The wave's index in the workgroup as a wave-uniform value: the compiler
+// cannot tell that threadIdx.x / 64 is the same across a wave, and would
+// otherwise treat every branch and address derived from it as divergent.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+}
+
 // Lane src's value of v, for the whole wave (two 32-bit lane reads).
 __device__ __forceinline__ double rdlane(double v, int src) {
   const unsigned long long u = __double_as_longlong(v);
@@ -709,7 +727,7 @@ __device__ __forceinline__ bool diag_sweep(int o, int k, double (*sL)[17]) {
 // sm.li, transposed (L[r][c] at li[c][r]), and cleared at the end.
 __device__ __forceinline__ bool small_ldl(int k) {
   SweepSmem& sm = g_sw;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int g16 = lane >> 4, l16 = lane & 15;
   bool bad = false;
   const int nb = (k + 15) >> 4, kb = 16 * nb;
@@ -821,7 +839,7 @@ __device__ __forceinline__ bool small_ldl(int k) {
 // sm.pp <- B = L^-T D^-1 L^-1 from sm.li and sm.rD (identity and 0 past k).
 __device__ __forceinline__ void small_b(int k) {
   SweepSmem& sm = g_sw;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int wr = wave >> 1, wc = wave & 1, g16 = lane >> 4, l16 = lane & 15;
   f64x4 acc[2][2] = {};
   // L^-1 is lower triangular: rows m below this wave's quadrant contribute nothing
@@ -860,7 +878,7 @@ __device__ __forceinline__ void small_b(int k) {
 // are contiguous: in MFMA step kk, lane l supplies q = 16*(l/16) + kk.
 __device__ __forceinline__ void v_band(const SweepMat& M, int band, int half, int k) {
   SweepSmem& sm = g_sw;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int wr = wave >> 1, wc = wave & 1, g16 = lane >> 4, l16 = lane & 15;
   const int s0 = band * kSB + 32 * half + 16 * wr;
   double u[16];
@@ -1092,17 +1110,24 @@ struct TileWalk {
 // members that build bands and tiles form B from them.
 // Returns whether a pivot of this step had the wrong sign (a lookahead
 // member flags its own into *status).
-__device__ __noinline__ bool sweep_step(const SweepMat M, Team& tm, int k, int skip_below, int kn,
-                                        bool pre, int32_t* status) {
+__device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& tm, int k_arg, int skip_arg,
+                                        int kn_arg, bool pre_arg, int32_t* status) {
   SweepSmem& sm = g_sw;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const bool la = kn > 0 && tm.size > 1;
-  const bool me_la = la && tm.rank == tm.size - 1;
+  // every argument is the same in all lanes; a called function receives them
+  // in vector registers, so say so, or every branch and address derived from
+  // them is compiled as divergent (exec-masked)
+  const SweepMat M = uniform_mat(M_arg);
+  const int k = uniform(k_arg), skip_below = uniform(skip_arg), kn = uniform(kn_arg);
+  const bool pre = uniform(static_cast<int>(pre_arg)) != 0;
+  const int trank = uniform(tm.rank), tsize = uniform(tm.size);
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+  const bool la = kn > 0 && tsize > 1;
+  const bool me_la = la && trank == tsize - 1;
   bool bad = false;
   // pre: the previous step's lookahead member (the last rank) factored this
   // pivot block and left L^-1 and 1/D in its own LDS; the others load them
   if (pre) {
-    if (tm.rank != tm.size - 1) {
+    if (trank != tsize - 1) {
       for (int e = tid; e < kSB * kSB; e += kTeamThreads) {
         const int r = e >> 6, c = e & 63;
         sm.li[r][c] = M.stage[kSB * kSB + e];
@@ -1122,12 +1147,12 @@ __device__ __noinline__ bool sweep_step(const SweepMat M, Team& tm, int k, int s
   }
   const int nrb = (M.n_rhs + kSB - 1) / kSB, nvb = (M.n_var + kSB - 1) / kSB;
   const int vb0 = M.r_al / kSB;
-  const int vmembers = la ? tm.size - 1 : tm.size;
+  const int vmembers = la ? tsize - 1 : tsize;
   // B (for V = U B and the pivot block) only where the bands and tiles are
   // built: the lookahead member needs L^-1 and D alone
   if (!me_la) small_b(k);
   if (!me_la) {
-    for (int bi = tm.rank; bi < 2 * (nrb + nvb); bi += vmembers) {
+    for (int bi = trank; bi < 2 * (nrb + nvb); bi += vmembers) {
       const int b = bi >> 1;
       v_band(M, b < nrb ? b : vb0 + b - nrb, bi & 1, k);
     }
@@ -1229,8 +1254,8 @@ __device__ __noinline__ bool sweep_step(const SweepMat M, Team& tm, int k, int s
     // tiles; when there are fewer tiles than waves, of their halves or quarters
     int total = 0;
     for (int iv = 0; iv < nvb; ++iv) total += nrb + (iv >= skip_below ? iv + 1 : 0);
-    const int workers = la ? tm.size - 1 : tm.size;
-    const int nw = workers * (kTeamThreads / 64), gw = tm.rank * (kTeamThreads / 64) + wave;
+    const int workers = la ? tsize - 1 : tsize;
+    const int nw = workers * (kTeamThreads / 64), gw = trank * (kTeamThreads / 64) + wave;
     const int parts = 2 * total <= nw ? 4 : (total < nw ? 2 : 1);
     const int tasks = total * parts;
     const int a0 = static_cast<int>((static_cast<long long>(tasks) * gw) / nw);

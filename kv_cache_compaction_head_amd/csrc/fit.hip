@@ -391,6 +391,8 @@ struct Team {
   unsigned* flag0;  // rank 0's arrival flag; rank r's is fstride * r words on
   unsigned* mine;   // this workgroup's arrival flag
   int fstride;      // words between consecutive ranks' flags
+  unsigned* tickets;  // the team's tile-task counter
+  unsigned tbase;     // its value at the start of the current step's tile phase
   unsigned gen;
   int* err;
   bool fast;
@@ -460,6 +462,13 @@ __device__ void team_sync(Team& tm) {
   team_wait(tm);
 }
 
+// The next number from the team's ticket counter, for the whole wave.
+__device__ __forceinline__ unsigned draw_ticket(const Team& tm) {
+  unsigned v = 0;
+  if ((threadIdx.x & 63) == 0) v = atomicAdd(tm.tickets, 1u);
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
 // Team of this workgroup from the XCD-aligned mapping, then one agent-fenced
 // barrier to compare the members' XCC ids (fast barrier if they all match).
 __device__ void team_setup(Team& tm, int& team, int& nteams, unsigned* bar, int* err, int* xcc,
@@ -471,6 +480,8 @@ __device__ void team_setup(Team& tm, int& team, int& nteams, unsigned* bar, int*
   tm.fstride = kFlagStride * nteams;
   tm.flag0 = bar + static_cast<size_t>(team) * kFlagStride;
   tm.mine = bar + static_cast<size_t>(blockIdx.x) * kFlagStride;
+  tm.tickets = bar + kTicketOffset + static_cast<size_t>(team) * kFlagStride;
+  tm.tbase = 0;
   tm.gen = 0;
   tm.err = err;
   tm.fast = false;
@@ -1233,6 +1244,12 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& tm, int k_ar
           if (row < kn && col < kn) sm.pp[row][col] -= acc[x][y][i];
         }
   }
+  int total = 0;
+  for (int iv = 0; iv < nvb; ++iv) total += nrb + (iv >= skip_below ? iv + 1 : 0);
+  const int workers = la ? tsize - 1 : tsize;
+  const int nw = workers * (kTeamThreads / 64);
+  const int parts = 2 * total <= nw ? 4 : (total < nw ? 2 : 1);
+  const int tasks = total * parts;
   if (me_la) {
     // the lookahead member has read all it needs from S: count it in at the
     // first barrier and invert at once (the tile updates start when the
@@ -1249,27 +1266,31 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& tm, int k_ar
     if (bad2 && tid == 0 && status) atomicOr(status, 1);
     team_wait(tm);
   } else {
-    team_sync(tm);
-    // every wave of the tile workers takes a contiguous run of the active
-    // tiles; when there are fewer tiles than waves, of their halves or quarters
-    int total = 0;
-    for (int iv = 0; iv < nvb; ++iv) total += nrb + (iv >= skip_below ? iv + 1 : 0);
-    const int workers = la ? tsize - 1 : tsize;
-    const int nw = workers * (kTeamThreads / 64), gw = trank * (kTeamThreads / 64) + wave;
-    const int parts = 2 * total <= nw ? 4 : (total < nw ? 2 : 1);
-    const int tasks = total * parts;
-    const int a0 = static_cast<int>((static_cast<long long>(tasks) * gw) / nw);
-    const int a1 = static_cast<int>((static_cast<long long>(tasks) * (gw + 1)) / nw);
-    TileWalk w{0, 0, nrb, skip_below, vb0};
-    w.seek(a0 / parts);
-    for (int a = a0; a < a1; ++a) {
-      const int part = a % parts;
-      if (parts == 1) wave_tile<4, 4>(M, w.I(), w.J(), 0, 0);
-      else if (parts == 2) wave_tile<2, 4>(M, w.I(), w.J(), 2 * part, 0);
-      else wave_tile<2, 2>(M, w.I(), w.J(), 2 * (part >> 1), 2 * (part & 1));
-      if (part == parts - 1) w.next();
+    // Tile tasks (the active tiles, or their halves or quarters when there
+    // are fewer tiles than waves) are handed out by ticket: each wave of the
+    // tile workers draws task numbers from the team's counter, the next one
+    // while it works on the current, until a number runs past the step's
+    // tasks.  Waves that draw cheap tiles (no pivot rows or columns) take
+    // more of them.  Each wave overshoots exactly once, so every member
+    // advances the step's base by tasks + waves without reading the counter.
+    team_arrive(tm);
+    unsigned tk = draw_ticket(tm);  // the previous step's draws all ended before its barrier
+    team_wait(tm);
+    const unsigned base = uniform(static_cast<int>(tm.tbase)), end = base + tasks;
+    while (tk < end) {
+      const unsigned nx = draw_ticket(tm);
+      if (tk >= base) {  // (always, unless a timed-out barrier let the members drift apart)
+        const int a = static_cast<int>(tk - base), part = a % parts;
+        TileWalk w{0, 0, nrb, skip_below, vb0};
+        w.seek(a / parts);
+        if (parts == 1) wave_tile<4, 4>(M, w.I(), w.J(), 0, 0);
+        else if (parts == 2) wave_tile<2, 4>(M, w.I(), w.J(), 2 * part, 0);
+        else wave_tile<2, 2>(M, w.I(), w.J(), 2 * (part >> 1), 2 * (part & 1));
+      }
+      tk = nx;
     }
   }
+  tm.tbase += tasks + nw;
   team_sync(tm);
   return bad;
 }

@@ -21,6 +21,8 @@
 // Keys whose multiplier is pinned at zero carry a factor 1e-30 in X; their
 // coupling to the rest is ~1e-30 relative, so the value system is solved on
 // the passive set only and those keys keep C_v = V (the ridge prior).
+#include <utility>
+
 #include "common.h"
 #include "launch.h"
 
@@ -688,42 +690,78 @@ __device__ __forceinline__ double rdlane(double v, int src) {
   return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
 }
 
-// Wave 0 sweeps the 16 x 16 diagonal block at o of sm.pp: lane c < 16 holds
-// column c in registers; pivot m's column (= its row, the block staying
-// symmetric under sweeping) reaches every lane as wave-uniform values read
-// from lane m.  Records -L^-1 of the block (the pivot rows at their turn)
-// into sL and 1/D into sm.rD[o..o+15].  Returns whether a pivot lacked its
-// sign (replaced by the sign).
+// Wave 0 sweeps the 16 x 16 diagonal block at o of sm.pp.  Lane (g, c) =
+// (lane / 16, lane % 16) holds rows 4g .. 4g+3 of column c.  For pivot m the
+// pivot column's entries of a lane's rows come from lane m of its 16-lane row
+// (DPP row broadcast), and the pivot row's entry of its column from row group
+// m / 4 (two lane-half swaps); the pivot itself is read from its lane.
+// Records -L^-1 of the block (the pivot rows at their turn) into sL and 1/D
+// into sm.rD[o..o+15].  Returns whether a pivot lacked its sign (replaced by
+// the sign).
+template <int N>
+__device__ __forceinline__ double row_bcast(double v) {  // lane N of each 16-lane row
+  const unsigned long long u = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0x150 + N, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), 0x150 + N, 0xF, 0xF, false);
+  return __longlong_as_double(static_cast<long long>(
+      (static_cast<unsigned long long>(static_cast<unsigned>(hi)) << 32) | static_cast<unsigned>(lo)));
+}
+template <int G>
+__device__ __forceinline__ unsigned group_bcast32(unsigned x) {  // 16-lane row G to all four
+  const auto s16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);  // rows (0,0,2,2) / (1,1,3,3)
+  const unsigned w = (G & 1) ? s16[1] : s16[0];
+  const auto s32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);  // halves (lo,lo) / (hi,hi)
+  return (G >> 1) ? s32[1] : s32[0];
+}
+template <int G>
+__device__ __forceinline__ double group_bcast(double v) {
+  const unsigned long long u = __double_as_longlong(v);
+  const unsigned lo = group_bcast32<G>(static_cast<unsigned>(u));
+  const unsigned hi = group_bcast32<G>(static_cast<unsigned>(u >> 32));
+  return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
+}
+template <int M>
+__device__ __forceinline__ void diag_pivot(double (&a)[4], int g, int c, int o, int k,
+                                           double (*sL)[17], bool& bad) {
+  constexpr int GM = M >> 2, IM = M & 3;
+  SweepSmem& sm = g_sw;
+  double colm[4];  // A[4g + i][m]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) colm[i] = row_bcast<M>(a[i]);
+  const double rowm = group_bcast<GM>(a[IM]);  // A[m][c]
+  const double sg = o + M < k ? sm.sgn[o + M] : 1.0;
+  double d = rdlane(a[IM], 16 * GM + M);
+  if (!(d * sg > 0.0)) {
+    bad = true;
+    d = sg;
+  }
+  const double rd = 1.0 / d;
+  if (g == 0) sL[M][c] = c < M ? -rowm : (c == M ? 1.0 : 0.0);
+  if (g == 0 && c == 0) sm.rD[o + M] = rd;
+  const bool piv = c == M;
+  const double tm = rowm * rd;  // row m of this column, scaled
+  // off the pivot row: the pivot column scales by 1/D, the others lose
+  // A[r][m] * A[m][c] / D (a * 1 and colm * 0 are exact)
+  const double al = piv ? rd : 1.0, be = piv ? 0.0 : -tm;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const double nv = fma(colm[i], be, a[i] * al);
+    a[i] = (i == IM && g == GM) ? (piv ? -rd : tm) : nv;
+  }
+}
+template <int... Ms>
+__device__ __forceinline__ void diag_pivots(std::integer_sequence<int, Ms...>, double (&a)[4], int g,
+                                            int c, int o, int k, double (*sL)[17], bool& bad) {
+  (diag_pivot<Ms>(a, g, c, o, k, sL, bad), ...);
+}
 __device__ __forceinline__ bool diag_sweep(int o, int k, double (*sL)[17]) {
   SweepSmem& sm = g_sw;
-  const int lane = threadIdx.x & 63, c = lane & 15;
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   bool bad = false;
-  double a[16];
+  double a[4];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) a[r] = sm.pp[o + r][o + c];
-#pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    double sr[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sr[r] = rdlane(a[r], m);
-    const double sg = o + m < k ? sm.sgn[o + m] : 1.0;
-    double d = sr[m];
-    if (!(d * sg > 0.0)) {
-      bad = true;
-      d = sg;
-    }
-    const double rd = 1.0 / d;
-    if (lane < 16) sL[m][c] = c < m ? -a[m] : (c == m ? 1.0 : 0.0);
-    if (lane == 0) sm.rD[o + m] = rd;
-    const bool piv = c == m;
-    const double tm = a[m] * rd;  // row m of this column, scaled
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (r == m) continue;
-      a[r] = piv ? sr[r] * rd : fma(-sr[r], tm, a[r]);
-    }
-    a[m] = piv ? -rd : tm;
-  }
+  for (int i = 0; i < 4; ++i) a[i] = sm.pp[o + 4 * g + i][o + c];
+  diag_pivots(std::make_integer_sequence<int, 16>{}, a, g, c, o, k, sL, bad);
   return bad;
 }
 

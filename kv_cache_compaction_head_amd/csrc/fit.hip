@@ -720,9 +720,20 @@ __device__ __forceinline__ double group_bcast(double v) {
   const unsigned hi = group_bcast32<G>(static_cast<unsigned>(u >> 32));
   return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
 }
+// 1/d by Newton-Raphson from the hardware estimate (two steps, each squaring
+// the relative error: within an ulp or so of the rounded quotient).  The
+// pivot chain waits on this reciprocal at every pivot; the IEEE division
+// sequence is twice as long.
+__device__ __forceinline__ double recip(double d) {
+  double r = __builtin_amdgcn_rcp(d);
+  double e = fma(-d, r, 1.0);
+  r = fma(r, e, r);
+  e = fma(-d, r, 1.0);
+  return fma(r, e, r);
+}
 template <int M>
 __device__ __forceinline__ void diag_pivot(double (&a)[4], int g, int c, int o, int k,
-                                           double (*sL)[17], bool& bad) {
+                                           double (*sL)[17], double& myrd, bool& bad) {
   constexpr int GM = M >> 2, IM = M & 3;
   SweepSmem& sm = g_sw;
   double colm[4];  // A[4g + i][m]
@@ -730,15 +741,16 @@ __device__ __forceinline__ void diag_pivot(double (&a)[4], int g, int c, int o, 
   for (int i = 0; i < 4; ++i) colm[i] = row_bcast<M>(a[i]);
   const double rowm = group_bcast<GM>(a[IM]);  // A[m][c]
   const double sg = o + M < k ? sm.sgn[o + M] : 1.0;
-  double d = rdlane(a[IM], 16 * GM + M);
-  if (!(d * sg > 0.0)) {
-    bad = true;
-    d = sg;
-  }
-  const double rd = 1.0 / d;
-  if (g == 0) sL[M][c] = c < M ? -rowm : (c == M ? 1.0 : 0.0);
-  if (g == 0 && c == 0) sm.rD[o + M] = rd;
+  const double d = rdlane(a[IM], 16 * GM + M);
+  // a pivot without its sign is replaced by the sign (1/s = s); the test
+  // runs beside the reciprocal instead of ahead of it
+  const bool ok = d * sg > 0.0;
+  bad |= !ok;
+  const double rd = ok ? recip(d) : sg;
+  // the four row groups write the same values (no branch on the pivot chain)
+  sL[M][c] = c < M ? -rowm : (c == M ? 1.0 : 0.0);
   const bool piv = c == M;
+  if (piv) myrd = rd;
   const double tm = rowm * rd;  // row m of this column, scaled
   // off the pivot row: the pivot column scales by 1/D, the others lose
   // A[r][m] * A[m][c] / D (a * 1 and colm * 0 are exact)
@@ -751,17 +763,19 @@ __device__ __forceinline__ void diag_pivot(double (&a)[4], int g, int c, int o, 
 }
 template <int... Ms>
 __device__ __forceinline__ void diag_pivots(std::integer_sequence<int, Ms...>, double (&a)[4], int g,
-                                            int c, int o, int k, double (*sL)[17], bool& bad) {
-  (diag_pivot<Ms>(a, g, c, o, k, sL, bad), ...);
+                                            int c, int o, int k, double (*sL)[17], double& myrd,
+                                            bool& bad) {
+  (diag_pivot<Ms>(a, g, c, o, k, sL, myrd, bad), ...);
 }
 __device__ __forceinline__ bool diag_sweep(int o, int k, double (*sL)[17]) {
   SweepSmem& sm = g_sw;
   const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   bool bad = false;
-  double a[4];
+  double a[4], myrd = 0.0;  // lane c keeps 1/D of pivot c
 #pragma unroll
   for (int i = 0; i < 4; ++i) a[i] = sm.pp[o + 4 * g + i][o + c];
-  diag_pivots(std::make_integer_sequence<int, 16>{}, a, g, c, o, k, sL, bad);
+  diag_pivots(std::make_integer_sequence<int, 16>{}, a, g, c, o, k, sL, myrd, bad);
+  if (g == 0) sm.rD[o + c] = myrd;
   return bad;
 }
 

@@ -1242,6 +1242,10 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& tm, int k_ar
       const bool in = a < kn && c < kn;
       app[i] = s_at_or0(M, in, in ? sm.piv2[a] : 0, in ? sm.piv2[c] : 0);
     }
+    // all the lookahead member reads from S is in registers once these loads
+    // land (the arrival waits for them): count it in at the first barrier now
+    // and form the block while the others update the tiles
+    team_arrive(tm);
     f64x4 wa[2][2] = {};
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
@@ -1303,10 +1307,9 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& tm, int k_ar
   const int parts = 2 * total <= nw ? 4 : (total < nw ? 2 : 1);
   const int tasks = total * parts;
   if (me_la) {
-    // the lookahead member has read all it needs from S: count it in at the
-    // first barrier and invert at once (the tile updates start when the
-    // others have arrived); it waits for that barrier only before the next
-    team_arrive(tm);
+    // the lookahead member arrived at the first barrier after its gathers;
+    // it factors the next block and waits for that barrier only before the
+    // next
     if (tid < kSB) sm.sgn[tid] = sm.sgn2[tid];
     __syncthreads();
     const bool bad2 = small_ldl(kn);

@@ -464,11 +464,16 @@ __device__ void team_sync(Team& tm) {
   team_wait(tm);
 }
 
-// The next number from the team's ticket counter, for the whole wave.
+// Draws the next number from the team's ticket counter: lane 0 holds it once
+// the atomic returns, and ticket_value gives it to the whole wave (only
+// there does the wave wait for the atomic).
 __device__ __forceinline__ unsigned draw_ticket(const Team& tm) {
   unsigned v = 0;
   if ((threadIdx.x & 63) == 0) v = atomicAdd(tm.tickets, 1u);
-  return __builtin_amdgcn_readfirstlane(v);
+  return v;
+}
+__device__ __forceinline__ unsigned ticket_value(unsigned drawn) {
+  return __builtin_amdgcn_readfirstlane(drawn);
 }
 
 // Team of this workgroup from the XCD-aligned mapping, then one agent-fenced
@@ -1329,11 +1334,12 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& tm, int k_ar
     // more of them.  Each wave overshoots exactly once, so every member
     // advances the step's base by tasks + waves without reading the counter.
     team_arrive(tm);
-    unsigned tk = draw_ticket(tm);  // the previous step's draws all ended before its barrier
+    unsigned pend = draw_ticket(tm);  // the previous step's draws all ended before its barrier
     team_wait(tm);
     const unsigned base = uniform(static_cast<int>(tm.tbase)), end = base + tasks;
+    unsigned tk = ticket_value(pend);
     while (tk < end) {
-      const unsigned nx = draw_ticket(tm);
+      pend = draw_ticket(tm);
       if (tk >= base) {  // (always, unless a timed-out barrier let the members drift apart)
         const int a = static_cast<int>(tk - base), part = a % parts;
         TileWalk w{0, 0, nrb, skip_below, vb0};
@@ -1342,7 +1348,7 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& tm, int k_ar
         else if (parts == 2) wave_tile<2, 4>(M, w.I(), w.J(), 2 * part, 0);
         else wave_tile<2, 2>(M, w.I(), w.J(), 2 * (part >> 1), 2 * (part & 1));
       }
-      tk = nx;
+      tk = ticket_value(pend);
     }
   }
   tm.tbase += tasks + nw;

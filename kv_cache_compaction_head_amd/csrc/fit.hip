@@ -87,7 +87,10 @@ __global__ __launch_bounds__(256) void k_ps(const In* __restrict__ Q, const In* 
                                             Out* __restrict__ PS,
                                             const int32_t* __restrict__ tv, int n, int T, int t,
                                             int tiles_a, int qg) {
-  __shared__ double sA[kKC * kTile], sB[kKC * kTile];
+  // the whole 64 x D tiles of queries and (gathered) keys, staged once in the
+  // input type with 16-byte loads and widened to fp64 as they leave LDS
+  constexpr int VEC = 16 / sizeof(In), CPR = D / VEC, LDR = D + VEC;
+  __shared__ __align__(16) In sQ[kTile * LDR], sK[kTile * LDR];
   const int b = blockIdx.y, ti = blockIdx.x / tiles_a, ta = blockIdx.x % tiles_a;
   const int i0 = ti * kTile, a0 = ta * kTile;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -95,18 +98,42 @@ __global__ __launch_bounds__(256) void k_ps(const In* __restrict__ Q, const In* 
   const In* Kb = K + static_cast<size_t>(b) * T * D;
   const int32_t* ib = idx ? idx + static_cast<size_t>(b) * t : nullptr;
   const int tb = tv ? tv[b] : t;  // columns from tb on are zero (unused budget)
+#pragma unroll
+  for (int e = threadIdx.x; e < kTile * CPR; e += 256) {
+    const int r = e / CPR, c = (e % CPR) * VEC;
+    const int i = i0 + r, a = a0 + r;
+    const uint4 qv = *reinterpret_cast<const uint4*>(Qb + static_cast<size_t>(i < n ? i : 0) * D + c);
+    const uint4 kv = *reinterpret_cast<const uint4*>(
+        Kb + static_cast<size_t>(a < tb ? (ib ? ib[a] : a) : 0) * D + c);
+    *reinterpret_cast<uint4*>(&sQ[r * LDR + c]) = i < n ? qv : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(&sK[r * LDR + c]) = a < tb ? kv : make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+  // fp64 MFMA 16x16x4 over the contraction, permuted so that in step kk of
+  // group ks lane l supplies index 16 ks + 4 (l / 16) + kk: each lane reads
+  // four consecutive values of a row at once
+  const int wy = wave >> 1, wx = wave & 1, g = lane >> 4, l16 = lane & 15;
   f64x4 acc[2][2] = {};
-  for (int c0 = 0; c0 < D; c0 += kKC) {
-    __syncthreads();
-    for (int e = threadIdx.x; e < kKC * kTile; e += 256) {
-      const int r = e / kKC, c = e % kKC;  // r: tile row, c: contraction index
-      const int i = i0 + r, a = a0 + r;
-      sA[c * kTile + r] = i < n ? to_f64<In>(Qb[static_cast<size_t>(i) * D + c0 + c]) : 0.0;
-      sB[c * kTile + r] =
-          a < tb ? to_f64<In>(Kb[static_cast<size_t>(ib ? ib[a] : a) * D + c0 + c]) : 0.0;
-    }
-    __syncthreads();
-    tile_mma(sA, sB, acc, wave, lane);
+#pragma unroll 2
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const int k = 16 * ks + 4 * g;
+    In av[2][4], bv[2][4];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        av[r][kk] = sQ[(wy * 32 + r * 16 + l16) * LDR + k + kk];
+        bv[r][kk] = sK[(wx * 32 + r * 16 + l16) * LDR + k + kk];
+      }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int ra = 0; ra < 2; ++ra)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          acc[ra][rb] = __builtin_amdgcn_mfma_f64_16x16x4f64(to_f64<In>(av[ra][kk]),
+                                                             to_f64<In>(bv[rb][kk]), acc[ra][rb],
+                                                             0, 0, 0);
   }
 #pragma unroll
   for (int ra = 0; ra < 2; ++ra)

@@ -440,7 +440,7 @@ __device__ __forceinline__ int hw_xcc_id() {
 // nothing the others produce before the barrier may arrive, keep working, and
 // wait later (team_wait before its next arrival: flags only grow, so a member
 // already at the next barrier still counts as arrived at this one).
-__device__ void team_arrive(Team& tm) {
+__device__ __forceinline__ void team_arrive(Team& tm) {
   if (tm.size == 1) return;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are done
   __syncthreads();
@@ -450,7 +450,7 @@ __device__ void team_arrive(Team& tm) {
   }
 }
 
-__device__ void team_wait(Team& tm) {
+__device__ __forceinline__ void team_wait(Team& tm) {
   if (tm.size == 1) {
     __syncthreads();
     return;
@@ -486,9 +486,30 @@ __device__ void team_wait(Team& tm) {
   __syncthreads();
 }
 
-__device__ void team_sync(Team& tm) {
+__device__ __forceinline__ void team_sync(Team& tm) {
   team_arrive(tm);
   team_wait(tm);
+}
+
+__device__ __forceinline__ unsigned* uniform(unsigned* p) {
+  const unsigned long long u = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(u));
+  const unsigned hi = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(u >> 32));
+  return reinterpret_cast<unsigned*>((static_cast<unsigned long long>(hi) << 32) | lo);
+}
+__device__ __forceinline__ Team uniform_team(const Team& t) {
+  Team u;
+  u.rank = __builtin_amdgcn_readfirstlane(t.rank);
+  u.size = __builtin_amdgcn_readfirstlane(t.size);
+  u.flag0 = uniform(t.flag0);
+  u.mine = uniform(t.mine);
+  u.fstride = __builtin_amdgcn_readfirstlane(t.fstride);
+  u.tickets = uniform(t.tickets);
+  u.tbase = __builtin_amdgcn_readfirstlane(t.tbase);
+  u.gen = __builtin_amdgcn_readfirstlane(t.gen);
+  u.err = reinterpret_cast<int*>(uniform(reinterpret_cast<unsigned*>(t.err)));
+  u.fast = __builtin_amdgcn_readfirstlane(static_cast<int>(t.fast)) != 0;
+  return u;
 }
 
 // Draws the next number from the team's ticket counter: lane 0 holds it once
@@ -1205,8 +1226,8 @@ struct TileWalk {
 // members that build bands and tiles form B from them.
 // Returns whether a pivot of this step had the wrong sign (a lookahead
 // member flags its own into *status).
-__device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& tm, int k_arg, int skip_arg,
-                                        int kn_arg, bool pre_arg, int32_t* status) {
+__device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& team_ref, int k_arg,
+                                        int skip_arg, int kn_arg, bool pre_arg, int32_t* status) {
   SweepSmem& sm = g_sw;
   // every argument is the same in all lanes; a called function receives them
   // in vector registers, so say so, or every branch and address derived from
@@ -1214,7 +1235,11 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& tm, int k_ar
   const SweepMat M = uniform_mat(M_arg);
   const int k = uniform(k_arg), skip_below = uniform(skip_arg), kn = uniform(kn_arg);
   const bool pre = uniform(static_cast<int>(pre_arg)) != 0;
-  const int trank = uniform(tm.rank), tsize = uniform(tm.size);
+  // the team in registers for the step: the caller's copy lives in scratch,
+  // and every scratch access is a vector memory operation whose wait also
+  // waits for all older loads and stores (the ticket atomic, a tile's stores)
+  Team tm = uniform_team(team_ref);
+  const int trank = tm.rank, tsize = tm.size;
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const bool la = kn > 0 && tsize > 1;
   const bool me_la = la && trank == tsize - 1;
@@ -1380,6 +1405,8 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& tm, int k_ar
   }
   tm.tbase += tasks + nw;
   team_sync(tm);
+  team_ref.gen = tm.gen;
+  team_ref.tbase = tm.tbase;
   return bad;
 }
 

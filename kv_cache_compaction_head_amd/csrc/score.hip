@@ -329,10 +329,11 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
   load_q_frags<In, D>(bq, Qb, q, n, g);
   // lse*log2e as an unevaluated fp32 pair, so exp2(s*log2e - hi - lo) keeps
   // the float64 log-sum-exp's accuracy
+  // (a query past n gets an infinite lse: its zero scores give p = 0 with no
+  // per-element test)
   const double l2 = q < n ? lse[static_cast<size_t>(b) * n + q] * 1.4426950408889634 : 0.0;
-  const float ml2 = static_cast<float>(l2);
-  const float ml2lo = static_cast<float>(l2 - static_cast<double>(ml2));
-  const bool qok = q < n;
+  const float ml2 = q < n ? static_cast<float>(l2) : INFINITY;
+  const float ml2lo = q < n ? static_cast<float>(l2 - static_cast<double>(ml2)) : 0.f;
 
   f32x16 accO[ND];
 #pragma unroll
@@ -398,11 +399,10 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
         acc = Frag<In>::mma(a, bq[ks], acc);
       }
       float w[16];
-      if (!MASK && valid >= BN) {  // a whole tile: only the query bound
+      if (!MASK && valid >= BN) {  // a whole tile: no bound to test
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2) - ml2lo);
-          const float p = qok ? e : 0.f;
+          const float p = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2) - ml2lo);
           acc[r] = p;
           w[r] = RMS ? p * p : p;
         }
@@ -412,7 +412,7 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
         for (int r = 0; r < 16; ++r) {
           const int kk = st * 32 + mfma32_row(r, lane);
           const float e = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2) - ml2lo);
-          const float p = (kk < valid && qok && !((mb >> kk) & 1)) ? e : 0.f;
+          const float p = (kk < valid && !((mb >> kk) & 1)) ? e : 0.f;
           acc[r] = p;
           w[r] = RMS ? p * p : p;
         }

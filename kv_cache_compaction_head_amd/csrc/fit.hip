@@ -1617,20 +1617,40 @@ __global__ __launch_bounds__(256) void k_value_sweep(
     for (int b = team; b < B; b += nteams) atomicOr(&status[b], 8);
 }
 
-// r_i = sum_a P_S[i][a] w'_a, X = P_S diag(w') / r (in place), w' = max(w, 1e-30).
+// r_i = sum_a P_S[i][a] w'_a, X = P_S diag(w') / r, w' = max(w, 1e-30); the
+// passive columns X_F are written compacted to the front of each row (column
+// inv[a] for passive a; the row stride stays t), so the value system's
+// products read them contiguously.  The whole row is read before any of it
+// is written (block_sum's barrier), which makes the in-place rewrite safe.
 // grid (n, B), block 256.
 __global__ __launch_bounds__(256) void k_value_prep(double* __restrict__ PS,
-                                                    const double* __restrict__ wv, int n,
+                                                    const double* __restrict__ wv,
+                                                    const int32_t* __restrict__ inv, int n,
                                                     int t) {
+  constexpr int NV = kMaxTeamT / 256;
   __shared__ double sh[16];
   const int b = blockIdx.y, i = blockIdx.x;
   double* row = PS + (static_cast<size_t>(b) * n + i) * t;
   const double* w = wv + static_cast<size_t>(b) * t;
+  const int32_t* ib = inv + static_cast<size_t>(b) * t;
+  double v[NV];
   double s = 0.0;
-  for (int a = threadIdx.x; a < t; a += blockDim.x) s += row[a] * fmax(w[a], 1e-30);
+#pragma unroll
+  for (int q = 0; q < NV; ++q) {
+    const int a = threadIdx.x + q * 256;
+    v[q] = a < t ? row[a] * fmax(w[a], 1e-30) : 0.0;
+    s += v[q];
+  }
   s = block_sum(s, sh);
-  const double inv = 1.0 / s;
-  for (int a = threadIdx.x; a < t; a += blockDim.x) row[a] = row[a] * fmax(w[a], 1e-30) * inv;
+  const double rs = 1.0 / s;
+#pragma unroll
+  for (int q = 0; q < NV; ++q) {
+    const int a = threadIdx.x + q * 256;
+    if (a < t) {
+      const int slot = ib[a];
+      if (slot >= 0) row[slot] = v[q] * rs;
+    }
+  }
 }
 
 // lam_v = ridge * trace(G) / t; G += lam_v I (G at Gb, order msz, stride ld).
@@ -1803,14 +1823,14 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
   prof_mark(5, true, st);
   // value fit on the passive set: G = X_F^T X_F + lam_v I, R = X_F^T O + lam_v V_F
   prof_mark(6, false, st);
-  hipLaunchKernelGGL(k_value_prep, dim3(n, B), dim3(256), 0, st, fb.PS, fb.wv, n, t);
+  hipLaunchKernelGGL(k_value_prep, dim3(n, B), dim3(256), 0, st, fb.PS, fb.wv, fb.inv, n, t);
   double* G0 = fb.S + static_cast<size_t>(rv) * ld + rv;
   double* R0 = fb.S + static_cast<size_t>(rv) * ld;
-  launch_atb<double, true>(fb.PS, sPS, t, fb.Fidx, t, fb.PS, sPS, t, G0, sS, ld, n, fb.msz, t, t,
+  launch_atb<double, true>(fb.PS, sPS, t, nullptr, 0, fb.PS, sPS, t, G0, sS, ld, n, fb.msz, t, t,
                            fb.part, fb.part_cap, B, st);
   hipLaunchKernelGGL(k_ridge_v, dim3(B), dim3(256), 0, st, G0, sS, ld, fb.msz, fb.lam, fb.tv, t,
                      ridge);
-  launch_atb<float, false>(fb.PS, sPS, t, fb.Fidx, t, O, static_cast<size_t>(n) * D, D, R0, sS, ld,
+  launch_atb<float, false>(fb.PS, sPS, t, nullptr, 0, O, static_cast<size_t>(n) * D, D, R0, sS, ld,
                            n, fb.msz, t, D, fb.part, fb.part_cap, B, st);
   hipLaunchKernelGGL((k_rhs_ridge<In>), dim3((t * D + 255) / 256, B), dim3(256), 0, st, R0, sS,
                      ld, V, idx, fb.Fidx, fb.msz, fb.lam, T, t, D);

@@ -422,6 +422,8 @@ struct Team {
   int fstride;      // words between consecutive ranks' flags
   unsigned* tickets;  // the team's tile-task counter
   unsigned tbase;     // its value at the start of the current step's tile phase
+  unsigned* ready;    // number of lookahead factors the team's lookahead member has published
+  unsigned pubs;      // ... that this member has seen published
   unsigned gen;
   int* err;
   bool fast;
@@ -506,6 +508,8 @@ __device__ __forceinline__ Team uniform_team(const Team& t) {
   u.fstride = __builtin_amdgcn_readfirstlane(t.fstride);
   u.tickets = uniform(t.tickets);
   u.tbase = __builtin_amdgcn_readfirstlane(t.tbase);
+  u.ready = uniform(t.ready);
+  u.pubs = __builtin_amdgcn_readfirstlane(t.pubs);
   u.gen = __builtin_amdgcn_readfirstlane(t.gen);
   u.err = reinterpret_cast<int*>(uniform(reinterpret_cast<unsigned*>(t.err)));
   u.fast = __builtin_amdgcn_readfirstlane(static_cast<int>(t.fast)) != 0;
@@ -537,6 +541,8 @@ __device__ void team_setup(Team& tm, int& team, int& nteams, unsigned* bar, int*
   tm.mine = bar + static_cast<size_t>(blockIdx.x) * kFlagStride;
   tm.tickets = bar + kTicketOffset + static_cast<size_t>(team) * kFlagStride;
   tm.tbase = 0;
+  tm.ready = bar + kReadyOffset + static_cast<size_t>(team) * kFlagStride;
+  tm.pubs = 0;
   tm.gen = 0;
   tm.err = err;
   tm.fast = false;
@@ -1245,9 +1251,10 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& team_ref, in
   const bool me_la = la && trank == tsize - 1;
   bool bad = false;
   // pre: the previous step's lookahead member (the last rank) factored this
-  // pivot block and left L^-1 and 1/D in its own LDS; the others load them
+  // pivot block; it kept L^-1 and 1/D in its LDS, and in a single-XCD team the
+  // others fetched them at the end of the previous step (below)
   if (pre) {
-    if (trank != tsize - 1) {
+    if (trank != tsize - 1 && !tm.fast) {
       for (int e = tid; e < kSB * kSB; e += kTeamThreads) {
         const int r = e >> 6, c = e & 63;
         sm.li[r][c] = M.stage[kSB * kSB + e];
@@ -1376,6 +1383,14 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& team_ref, in
     }
     if (tid < kSB) M.stage[2 * kSB * kSB + tid] = sm.rD[tid];
     if (bad2 && tid == 0 && status) atomicOr(status, 1);
+    // the factors are out: raise the team's ready count (after every wave's
+    // stores have landed)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+      if (!tm.fast) __threadfence();
+      __hip_atomic_store(tm.ready, tm.pubs + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     team_wait(tm);
   } else {
     // Tile tasks (the active tiles, or their halves or quarters when there
@@ -1404,9 +1419,51 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& team_ref, in
     }
   }
   tm.tbase += tasks + nw;
+  // A worker of a single-XCD team fetches the next step's L^-1 and 1/D as
+  // soon as the lookahead member has published them (normally before the
+  // worker's last tile is done), into registers while the closing barrier
+  // completes; L1-bypassing loads, since the same staging area was read a
+  // step ago.
+  const bool fetch = la && !me_la && tm.fast;
+  double nli[kSB * kSB / kTeamThreads], nrd = 0.0;
+  if (fetch) {
+    if (tid == 0) {
+      const uint64_t t0 = wall_clock64();
+      unsigned spins = 0;
+      while (__hip_atomic_load(tm.ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < tm.pubs + 1) {
+        if ((++spins & 31u) == 0) {
+          if (__hip_atomic_load(tm.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+          if (wall_clock64() - t0 > kSpinTicks) {
+            atomicOr(tm.err, 1);
+            break;
+          }
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kSB * kSB / kTeamThreads; ++i)
+      nli[i] = __hip_atomic_load(&M.stage[kSB * kSB + tid + i * kTeamThreads], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < kSB)
+      nrd = __hip_atomic_load(&M.stage[2 * kSB * kSB + tid], __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+  }
   team_sync(tm);
+  if (fetch) {  // this step's 1/D is no longer read: every wave is past its tiles
+#pragma unroll
+    for (int i = 0; i < kSB * kSB / kTeamThreads; ++i) {
+      const int e = tid + i * kTeamThreads;
+      sm.li[e >> 6][e & 63] = nli[i];
+    }
+    if (tid < kSB) sm.rD[tid] = nrd;
+    __syncthreads();
+  }
+  if (la) tm.pubs += 1;
   team_ref.gen = tm.gen;
   team_ref.tbase = tm.tbase;
+  team_ref.pubs = tm.pubs;
   return bad;
 }
 

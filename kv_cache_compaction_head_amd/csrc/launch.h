@@ -44,7 +44,8 @@ struct FitBufs {
   int32_t *Fidx, *inv, *msz;
   const int32_t* tv;  // [B] per-head budgets (<= t), or null: t for every head
   unsigned* bar;  // kBarWords words: team barrier flags (kFlagStride words per team workgroup), tile-task
-                  // counters (kFlagStride words per team, from kTicketOffset), the last word the timeout flag
+                  // counters and lookahead ready counts (kFlagStride words per team, from
+                  // kTicketOffset and kReadyOffset), the last word the timeout flag
   int32_t* xcc;   // kMaxTeamGrid words: each team workgroup's XCC id
   double* flops;    // [B][2] fp64 work of the NNLS sweeps and of the value sweeps
   double* part;     // split-K partial tiles of the fit GEMMs
@@ -57,7 +58,8 @@ constexpr int kSweepStage = 2 * 64 * 64 + 64;
 constexpr int kMaxTeamGrid = 8192;
 constexpr int kFlagStride = 16;  // one 64-byte slot per team workgroup's barrier flag
 constexpr int kTicketOffset = kMaxTeamGrid * kFlagStride;
-constexpr int kBarWords = 2 * kMaxTeamGrid * kFlagStride + 1;
+constexpr int kReadyOffset = 2 * kMaxTeamGrid * kFlagStride;
+constexpr int kBarWords = 3 * kMaxTeamGrid * kFlagStride + 1;
 template <class In, int D>
 hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const double* lse,
                       const float* O, const int32_t* idx, FitBufs fb, float* out_bias,

@@ -54,6 +54,10 @@ __device__ int block_exclusive_scan(int v, int* scratch, int* total) {
 // pattern plus one, and 0 for a marked key, which keeps the order of the
 // others (patterns of finite non-negative floats stay below 0x7f800000).
 // status[b] |= 4 if an importance is not finite (NaN/Inf input upstream).
+// PER > 0: every thread holds its contiguous chunk of ceil(T / kSelThreads)
+// <= PER keys in registers, read once, for all passes and the compaction;
+// PER == 0 streams the keys from memory in every pass (any T).
+template <int PER>
 __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict__ imp,
                                                         int32_t* __restrict__ idx,
                                                         int32_t* __restrict__ status,
@@ -82,23 +86,46 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
     s_need = tb;
     s_bad = 0;
   }
+  // the thread's contiguous chunk (also the compaction's)
+  const int chunk = (T + kSelThreads - 1) / kSelThreads;
+  const int c0 = min(T, tid * chunk), c1 = min(T, c0 + chunk);
+  constexpr int NR = PER > 0 ? PER : 1;
+  unsigned int kv[NR];
+  if (PER > 0) {
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int j = c0 + i;
+      const unsigned int raw = j < c1 ? u[j] : 0u;
+      bad |= raw >= 0x7f800000u;  // inf / nan (non-negative inputs)
+      kv[i] = j < c1 ? (mb ? (mb[j] ? 0u : raw + 1u) : raw) : 0u;
+    }
+    __syncthreads();
+    if (bad) s_bad = 1;
+  }
   __syncthreads();
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = tid; i < (kSelThreads / 64) * 256; i += kSelThreads) (&hist[0][0])[i] = 0;
     __syncthreads();
     const unsigned int prefix = s_prefix, mask = s_mask;
     unsigned int* hw = hist[wave];
-    for (int j0 = 0; j0 < T; j0 += kSelThreads) {
-      const int j = j0 + tid;
-      bool in = false;
-      unsigned int dig = 0;
-      if (j < T) {
-        if (shift == 24 && u[j] >= 0x7f800000u) s_bad = 1;  // inf / nan (non-negative inputs)
-        const unsigned int v = key(j);
-        in = (v & mask) == prefix;
-        dig = (v >> shift) & 255u;
+    if (PER > 0) {
+#pragma unroll
+      for (int i = 0; i < NR; ++i)
+        if (c0 + i < c1 && (kv[i] & mask) == prefix) atomicAdd(&hw[(kv[i] >> shift) & 255u], 1u);
+    } else {
+      for (int j0 = 0; j0 < T; j0 += kSelThreads) {
+        const int j = j0 + tid;
+        bool in = false;
+        unsigned int dig = 0;
+        if (j < T) {
+          if (shift == 24 && u[j] >= 0x7f800000u) s_bad = 1;  // inf / nan (non-negative inputs)
+          const unsigned int v = key(j);
+          in = (v & mask) == prefix;
+          dig = (v >> shift) & 255u;
+        }
+        if (in) atomicAdd(&hw[dig], 1u);
       }
-      if (in) atomicAdd(&hw[dig], 1u);
     }
     __syncthreads();
     // digit of the need-th largest: scan the bins from the top (bin 255 first)
@@ -119,14 +146,21 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
   const unsigned int tau = s_prefix;
   const int need_eq = s_need;  // how many values equal to tau are kept
 
-  // order-preserving compaction over contiguous chunks
-  const int chunk = (T + kSelThreads - 1) / kSelThreads;
-  const int c0 = min(T, tid * chunk), c1 = min(T, c0 + chunk);
+  // order-preserving compaction over the contiguous chunks
   int n_gt = 0, n_eq = 0;
-  for (int j = c0; j < c1; ++j) {
-    const unsigned int v = key(j);
-    n_gt += v > tau;
-    n_eq += v == tau;
+  if (PER > 0) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      if (c0 + i < c1) {
+        n_gt += kv[i] > tau;
+        n_eq += kv[i] == tau;
+      }
+  } else {
+    for (int j = c0; j < c1; ++j) {
+      const unsigned int v = key(j);
+      n_gt += v > tau;
+      n_eq += v == tau;
+    }
   }
   int tot;
   const int eq_before = block_exclusive_scan(n_eq, scratch, &tot);
@@ -134,14 +168,27 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
   const int pos0 = block_exclusive_scan(n_gt + take_eq, scratch, &tot);
   int32_t* out = idx + static_cast<size_t>(b) * t;
   int pos = pos0, eq_taken = 0;
-  for (int j = c0; j < c1; ++j) {
-    const unsigned int v = key(j);
-    bool keep = v > tau;
-    if (v == tau && eq_taken < take_eq) {
-      keep = true;
-      ++eq_taken;
+  if (PER > 0) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      if (c0 + i < c1) {
+        bool keep = kv[i] > tau;
+        if (kv[i] == tau && eq_taken < take_eq) {
+          keep = true;
+          ++eq_taken;
+        }
+        if (keep) out[pos++] = c0 + i;
+      }
+  } else {
+    for (int j = c0; j < c1; ++j) {
+      const unsigned int v = key(j);
+      bool keep = v > tau;
+      if (v == tau && eq_taken < take_eq) {
+        keep = true;
+        ++eq_taken;
+      }
+      if (keep) out[pos++] = j;
     }
-    if (keep) out[pos++] = j;
   }
   for (int a = tb + tid; a < t; a += kSelThreads) out[a] = -1;
   if (tid == 0 && status && s_bad) status[b] |= 4;
@@ -190,8 +237,13 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t count, hipStream_t st) 
 
 hipError_t launch_select(const float* imp, int32_t* idx, int32_t* status, const int32_t* tv,
                          const uint8_t* mask, int B, int T, int t, hipStream_t st) {
-  hipLaunchKernelGGL(k_select, dim3(B), dim3(kSelThreads), 0, st, imp, idx, status, tv, mask, T,
-                     t);
+  // keys in registers up to 32 per thread (T <= 32768), streamed beyond
+  if (T <= 32 * kSelThreads)
+    hipLaunchKernelGGL(k_select<32>, dim3(B), dim3(kSelThreads), 0, st, imp, idx, status, tv, mask,
+                       T, t);
+  else
+    hipLaunchKernelGGL(k_select<0>, dim3(B), dim3(kSelThreads), 0, st, imp, idx, status, tv, mask,
+                       T, t);
   return hipGetLastError();
 }
 

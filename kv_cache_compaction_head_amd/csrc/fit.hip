@@ -11,7 +11,8 @@
 //
 // Kernels (batched over heads; per-head sizes stay on the device, so nothing
 // syncs with the host):
-//   k_ps           P_S = exp(Q C_k^T - lse) on fp64 MFMA (16x16x4)
+//   k_ps           P_S = exp(Q C_k^T - lse) on fp64 MFMA (16x16x4), with the
+//                  partial column sums of each 64-query tile
 //   k_atb          C = A^T B tiles on fp64 MFMA (Grams, X^T O), split-K
 //   k_bias_prep    lam_w, H = M + lam_w I, c = P_S^T 1 + lam_w
 //   k_nnls_sweep   block principal pivoting on the swept bias system
@@ -85,6 +86,7 @@ __global__ __launch_bounds__(256) void k_ps(const In* __restrict__ Q, const In* 
                                             const int32_t* __restrict__ idx,
                                             const double* __restrict__ lse,
                                             Out* __restrict__ PS,
+                                            double* __restrict__ colpart,
                                             const int32_t* __restrict__ tv, int n, int T, int t,
                                             int tiles_a, int qg) {
   // the whole 64 x D tiles of queries and (gathered) keys, staged once in the
@@ -135,6 +137,7 @@ __global__ __launch_bounds__(256) void k_ps(const In* __restrict__ Q, const In* 
                                                              to_f64<In>(bv[rb][kk]), acc[ra][rb],
                                                              0, 0, 0);
   }
+  double cs[2] = {0.0, 0.0};  // this lane's part of the tile's column sums
 #pragma unroll
   for (int ra = 0; ra < 2; ++ra)
 #pragma unroll
@@ -142,10 +145,28 @@ __global__ __launch_bounds__(256) void k_ps(const In* __restrict__ Q, const In* 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = i0 + tile_row(wave, lane, ra, i), a = a0 + tile_col(wave, lane, rb);
-        if (r < n && a < t)
-          PS[(static_cast<size_t>(b) * n + r) * t + a] = static_cast<Out>(
-              a < tb ? exp(acc[ra][rb][i] - lse[static_cast<size_t>(b) * n + r]) : 0.0);
+        if (r < n && a < t) {
+          const double v = a < tb ? exp(acc[ra][rb][i] - lse[static_cast<size_t>(b) * n + r]) : 0.0;
+          PS[(static_cast<size_t>(b) * n + r) * t + a] = static_cast<Out>(v);
+          cs[rb] += v;
+        }
       }
+  // column sums of the tile's 64 rows, in a fixed order, one partial per
+  // (query tile, column): c = P_S^T 1 without reading P_S again
+  if (colpart) {
+    __shared__ double sCol[2][kTile];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      cs[rb] += __shfl_xor(cs[rb], 16);
+      cs[rb] += __shfl_xor(cs[rb], 32);
+      if (lane < 16) sCol[wave >> 1][(wave & 1) * 32 + rb * 16 + lane] = cs[rb];
+    }
+    __syncthreads();
+    const int a = a0 + static_cast<int>(threadIdx.x);
+    if (threadIdx.x < kTile && a < t)
+      colpart[(static_cast<size_t>(b) * (gridDim.x / tiles_a) + ti) * t + a] =
+          sCol[0][threadIdx.x] + sCol[1][threadIdx.x];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -279,23 +300,8 @@ __global__ __launch_bounds__(256) void k_atb_reduce(const double* __restrict__ p
   }
 }
 
-// Column sums of P_S in two fixed-order stages: partial sums over 256-row
-// slabs, then over slabs.  grid (ceil(t/64), ceil(n/256), B), block (64, 4).
-__global__ void k_colsum_part(const double* __restrict__ PS, double* __restrict__ part, int n,
-                              int t) {
-  __shared__ double sh[4][64];
-  const int b = blockIdx.z, a = blockIdx.x * 64 + threadIdx.x;
-  const int i0 = blockIdx.y * 256, i1 = min(n, i0 + 256);
-  double s = 0.0;
-  if (a < t)
-    for (int i = i0 + threadIdx.y; i < i1; i += 4) s += PS[(static_cast<size_t>(b) * n + i) * t + a];
-  sh[threadIdx.y][threadIdx.x] = s;
-  __syncthreads();
-  if (threadIdx.y == 0 && a < t)
-    part[(static_cast<size_t>(b) * gridDim.y + blockIdx.y) * t + a] =
-        ((sh[0][threadIdx.x] + sh[1][threadIdx.x]) + sh[2][threadIdx.x]) + sh[3][threadIdx.x];
-}
-
+// c = P_S^T 1 from the partial column sums k_ps writes per 64-query tile,
+// added in tile order.  grid (ceil(t/256), B).
 __global__ void k_colsum_final(const double* __restrict__ part, double* __restrict__ out, int nslab,
                                int t) {
   const int b = blockIdx.y, a = blockIdx.x * blockDim.x + threadIdx.x;
@@ -364,11 +370,12 @@ __global__ __launch_bounds__(1024) void k_bias_prep(double* __restrict__ S, size
     tr += Sb[static_cast<size_t>(kSB + a) * ld + kSB + a];
   tr = block_sum(tr, sh);
   const double lw = ridge * tr / t;
-  for (int a = threadIdx.x; a < t; a += blockDim.x) {
+  // one wave per row: lane c writes entry c of the right-hand-side band
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int a = wave; a < t; a += nw) {
     double* row = Sb + static_cast<size_t>(kSB + a) * ld;
-    row[kSB + a] += lw;
-    row[0] = colsum[static_cast<size_t>(b) * t_str + a] + lw;
-    for (int c = 1; c < kSB; ++c) row[c] = 0.0;
+    row[lane] = lane == 0 ? colsum[static_cast<size_t>(b) * t_str + a] + lw : 0.0;
+    if (lane == 0) row[kSB + a] += lw;
   }
   if (threadIdx.x == 0) lam[2 * b] = lw;
 }
@@ -1844,18 +1851,15 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
   // P_S, M = P_S^T P_S (into the bias system's variable block), column sums
   prof_mark(3, false, st);
   hipLaunchKernelGGL((k_ps<In, D, double>), dim3(tn * tt, B), dim3(256), 0, st, Q, K, idx, lse, fb.PS,
-                     fb.tv, n, T, t, tt, qg);
+                     fb.colpart, fb.tv, n, T, t, tt, qg);
   prof_mark(3, true, st);
   prof_mark(4, false, st);
   launch_atb<double, true>(fb.PS, sPS, t, nullptr, 0, fb.PS, sPS, t,
                            fb.S + static_cast<size_t>(kSB) * ld + kSB, sS, ld, n, fb.tv, t, t,
                            fb.part, fb.part_cap, B, st);
   prof_mark(4, true, st);
-  const int nslab = (n + 255) / 256;
-  hipLaunchKernelGGL(k_colsum_part, dim3(tt, nslab, B), dim3(64, 4), 0, st, fb.PS, fb.colpart, n,
-                     t);
   hipLaunchKernelGGL(k_colsum_final, dim3((t + 255) / 256, B), dim3(256), 0, st, fb.colpart,
-                     fb.cvec, nslab, t);
+                     fb.cvec, tn, t);
   hipLaunchKernelGGL(k_bias_prep, dim3(B), dim3(1024), 0, st, fb.S, sS, ld, fb.cvec, fb.lam, fb.tv,
                      t, ridge);
   // pivoting rounds: one cooperative launch, a team per head
@@ -1919,7 +1923,7 @@ hipError_t launch_probs_all(const void* Q, const void* K, const double* lse, flo
   const int tt = (T + kTile - 1) / kTile, tn = (n + kTile - 1) / kTile;
   hipLaunchKernelGGL((k_ps<In, D, float>), dim3(tn * tt, B), dim3(256), 0, st,
                      static_cast<const In*>(Q), static_cast<const In*>(K), nullptr, lse, P,
-                     nullptr, n, T, T, tt, qg);
+                     nullptr, nullptr, n, T, T, tt, qg);
   return hipGetLastError();
 }
 

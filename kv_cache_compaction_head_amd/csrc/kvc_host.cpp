@@ -122,7 +122,7 @@ Layout make_layout(const kvc_params_t* p, bool omp = false) {
   L.cvec = take(B * t * 8);
   L.wv = take(B * t * 8);
   L.lam = take(B * 2 * 8);
-  L.colpart = take(B * ((n + 255) / 256) * t * 8);
+  L.colpart = take(B * ((n + 63) / 64) * t * 8);
   L.Fidx = take(B * t * 4);
   L.inv = take(B * t * 4);
   L.msz = take(B * 4);

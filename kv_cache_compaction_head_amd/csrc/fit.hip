@@ -1107,13 +1107,19 @@ __device__ __forceinline__ void wave_tile(const SweepMat& M, int I, int J, int r
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) acc[ra][rb] = f64x4{0.0, 0.0, 0.0, 0.0};
   {
+    // the next chunk's loads are issued ahead of the current chunk's MFMAs;
+    // the scheduling barriers keep the compiler from sinking them below
+    // (it would, to shorten register live ranges, and every chunk would then
+    // wait a whole L2 round trip)
     double a0[NRA][2], b0[NRB][2], a1[NRA][2], b1[NRB][2];
     wave_tile_chunk<NRA, NRB>(M, I, J, ro, co, 0, a0, b0);
 #pragma unroll
     for (int c = 0; c < 8; c += 2) {
       wave_tile_chunk<NRA, NRB>(M, I, J, ro, co, c + 1, a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
       wave_tile_mfma<NRA, NRB>(c, diag, ro, co, a0, b0, acc);
       if (c + 2 < 8) wave_tile_chunk<NRA, NRB>(M, I, J, ro, co, c + 2, a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
       wave_tile_mfma<NRA, NRB>(c + 1, diag, ro, co, a1, b1, acc);
     }
   }

@@ -14,7 +14,7 @@
 //   k_ps           P_S = exp(Q C_k^T - lse) on fp64 MFMA (16x16x4), with the
 //                  partial column sums of each 64-query tile
 //   k_atb          C = A^T B tiles on fp64 MFMA (Grams, X^T O), split-K
-//   k_bias_prep    lam_w, H = M + lam_w I, c = P_S^T 1 + lam_w
+//   k_bias_lam, k_bias_prep   lam_w; H = M + lam_w I, c = P_S^T 1 + lam_w
 //   k_nnls_sweep   block principal pivoting on the swept bias system
 //   k_value_prep, k_ridge_v, k_rhs_ridge   the value system
 //   k_value_sweep  its solve by the same block sweeps
@@ -300,15 +300,21 @@ __global__ __launch_bounds__(256) void k_atb_reduce(const double* __restrict__ p
   }
 }
 
-// c = P_S^T 1 from the partial column sums k_ps writes per 64-query tile,
-// added in tile order.  grid (ceil(t/256), B).
-__global__ void k_colsum_final(const double* __restrict__ part, double* __restrict__ out, int nslab,
-                               int t) {
-  const int b = blockIdx.y, a = blockIdx.x * blockDim.x + threadIdx.x;
-  if (a >= t) return;
+// c = P_S^T 1 from the partial column sums k_ps writes per 64-query tile:
+// four threads per column each add a quarter of the tiles in order, then the
+// quarters are added in order.  grid (ceil(t/64), B), block 256.
+__global__ __launch_bounds__(256) void k_colsum_final(const double* __restrict__ part,
+                                                      double* __restrict__ out, int nslab, int t) {
+  __shared__ double sh[4][64];
+  const int b = blockIdx.y, col = threadIdx.x & 63, qt = threadIdx.x >> 6;
+  const int a = blockIdx.x * 64 + col;
+  const int per = (nslab + 3) / 4, k0 = qt * per, k1 = min(nslab, k0 + per);
   double s = 0.0;
-  for (int k = 0; k < nslab; ++k) s += part[(static_cast<size_t>(b) * nslab + k) * t + a];
-  out[static_cast<size_t>(b) * t + a] = s;
+  if (a < t)
+    for (int k = k0; k < k1; ++k) s += part[(static_cast<size_t>(b) * nslab + k) * t + a];
+  sh[qt][col] = s;
+  __syncthreads();
+  if (qt == 0 && a < t) out[static_cast<size_t>(b) * t + a] = ((sh[0][col] + sh[1][col]) + sh[2][col]) + sh[3][col];
 }
 
 // Block-wide sum (blockDim 256..1024), deterministic tree order.
@@ -353,31 +359,37 @@ __device__ int block_count(int v, int* sh) {
 
 // Bias system of head b in its sweep matrix (right-hand side in row 0,
 // variables from row 64; see the sweep engine below): the Gram M = P_S^T P_S
-// is already in the variable block; add lam_w = ridge * tr(M) / t to its
-// diagonal, store c = P_S^T 1 + lam_w in column 0 of the variable rows and
-// clear columns 1..63 (unused right-hand-side slots).  grid (B), block 1024.
-__global__ __launch_bounds__(1024) void k_bias_prep(double* __restrict__ S, size_t sS, int ld,
-                                                    const double* __restrict__ colsum,
-                                                    double* __restrict__ lam,
-                                                    const int32_t* __restrict__ tv, int t_str,
-                                                    double ridge) {
+// is already in the variable block.  k_bias_lam: lam_w = ridge * tr(M) / t
+// (grid (B), block 1024).  k_bias_prep then adds lam_w to the diagonal,
+// stores c = P_S^T 1 + lam_w in column 0 of the variable rows and clears
+// columns 1..63 (unused right-hand-side slots), one wave per row (grid
+// (ceil(t/16), B), block 1024).
+__global__ __launch_bounds__(1024) void k_bias_lam(const double* __restrict__ S, size_t sS, int ld,
+                                                   double* __restrict__ lam,
+                                                   const int32_t* __restrict__ tv, int t_str,
+                                                   double ridge) {
   __shared__ double sh[16];
   const int b = blockIdx.x;
   const int t = tv ? tv[b] : t_str;
-  double* Sb = S + b * sS;
+  const double* Sb = S + b * sS;
   double tr = 0.0;
   for (int a = threadIdx.x; a < t; a += blockDim.x)
     tr += Sb[static_cast<size_t>(kSB + a) * ld + kSB + a];
   tr = block_sum(tr, sh);
-  const double lw = ridge * tr / t;
-  // one wave per row: lane c writes entry c of the right-hand-side band
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  for (int a = wave; a < t; a += nw) {
-    double* row = Sb + static_cast<size_t>(kSB + a) * ld;
-    row[lane] = lane == 0 ? colsum[static_cast<size_t>(b) * t_str + a] + lw : 0.0;
-    if (lane == 0) row[kSB + a] += lw;
-  }
-  if (threadIdx.x == 0) lam[2 * b] = lw;
+  if (threadIdx.x == 0) lam[2 * b] = ridge * tr / t;
+}
+__global__ __launch_bounds__(1024) void k_bias_prep(double* __restrict__ S, size_t sS, int ld,
+                                                    const double* __restrict__ colsum,
+                                                    const double* __restrict__ lam,
+                                                    const int32_t* __restrict__ tv, int t_str) {
+  const int b = blockIdx.y;
+  const int t = tv ? tv[b] : t_str;
+  const double lw = lam[2 * b];
+  const int lane = threadIdx.x & 63, a = blockIdx.x * 16 + (threadIdx.x >> 6);
+  if (a >= t) return;
+  double* row = S + b * sS + static_cast<size_t>(kSB + a) * ld;
+  row[lane] = lane == 0 ? colsum[static_cast<size_t>(b) * t_str + a] + lw : 0.0;
+  if (lane == 0) row[kSB + a] += lw;
 }
 
 // Teams.  The iterative parts of the fits (the NNLS pivoting rounds and the
@@ -1864,10 +1876,12 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
                            fb.S + static_cast<size_t>(kSB) * ld + kSB, sS, ld, n, fb.tv, t, t,
                            fb.part, fb.part_cap, B, st);
   prof_mark(4, true, st);
-  hipLaunchKernelGGL(k_colsum_final, dim3((t + 255) / 256, B), dim3(256), 0, st, fb.colpart,
+  hipLaunchKernelGGL(k_colsum_final, dim3((t + 63) / 64, B), dim3(256), 0, st, fb.colpart,
                      fb.cvec, tn, t);
-  hipLaunchKernelGGL(k_bias_prep, dim3(B), dim3(1024), 0, st, fb.S, sS, ld, fb.cvec, fb.lam, fb.tv,
-                     t, ridge);
+  hipLaunchKernelGGL(k_bias_lam, dim3(B), dim3(1024), 0, st, fb.S, sS, ld, fb.lam, fb.tv, t,
+                     ridge);
+  hipLaunchKernelGGL(k_bias_prep, dim3((t + 15) / 16, B), dim3(1024), 0, st, fb.S, sS, ld, fb.cvec,
+                     fb.lam, fb.tv, t);
   // pivoting rounds: one cooperative launch, a team per head
   prof_mark(5, false, st);
   int cap = coop_capacity(reinterpret_cast<const void*>(&k_nnls_sweep));

@@ -218,20 +218,28 @@ __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
 }
 
 // lse[b][q] (float64) from the split partials, merged in split order.
+// Four lanes per query, each taking every fourth split: the maximum over
+// all splits, then each lane's sum in split order, then the four sums added
+// in lane order.  grid (ceil(4 B n / 256)), block 256.
 __global__ void k_lse_merge(const double2* __restrict__ ml, double* __restrict__ lse, int n,
                             int nsplit, int B) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= B * n) return;
-  const int b = i / n, q = i % n;
+  const int g = blockIdx.x * blockDim.x + threadIdx.x, i = g >> 2, part = g & 3;
+  const bool ok = i < B * n;
+  const int b = ok ? i / n : 0, q = ok ? i % n : 0;
   const double2* p = ml + static_cast<size_t>(b) * nsplit * n + q;
   double m = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) m = fmax(m, p[static_cast<size_t>(s) * n].x);
+  if (ok)
+    for (int s = part; s < nsplit; s += 4) m = fmax(m, p[static_cast<size_t>(s) * n].x);
+  m = fmax(m, __shfl_xor(m, 1));
+  m = fmax(m, __shfl_xor(m, 2));
   double l = 0.0;
-  for (int s = 0; s < nsplit; ++s) {
-    const double2 v = p[static_cast<size_t>(s) * n];
-    if (v.x != -INFINITY) l += v.y * exp(v.x - m);
-  }
-  lse[i] = m + log(l);
+  if (ok)
+    for (int s = part; s < nsplit; s += 4) {
+      const double2 v = p[static_cast<size_t>(s) * n];
+      if (v.x != -INFINITY) l += v.y * exp(v.x - m);
+    }
+  const double l1 = __shfl_down(l, 1), l2 = __shfl_down(l, 2), l3 = __shfl_down(l, 3);
+  if (ok && part == 0) lse[i] = m + log(((l + l1) + l2) + l3);
 }
 
 // Position of key kk (0..31 inside a tile) in the transposed V tile: the
@@ -526,7 +534,7 @@ hipError_t launch_score(const void* Q, const void* K, const void* V, double2* ml
     hipLaunchKernelGGL((k_score_lse<In, D, false>), g1, dim3(256), 0, st, q, k, mask, ml, n, T,
                        kps1, nqb, nsplit1, B, qg);
   prof_mark(0, true, st);
-  hipLaunchKernelGGL(k_lse_merge, dim3((B * n + 255) / 256), dim3(256), 0, st, ml, lse, n,
+  hipLaunchKernelGGL(k_lse_merge, dim3((4 * B * n + 255) / 256), dim3(256), 0, st, ml, lse, n,
                      nsplit1, B);
   prof_mark(1, false, st);
 #define KVC_K2(R, M)                                                                           \

@@ -613,16 +613,19 @@ constexpr int kTeamThreads = 256;
 // pivoting rule reads), or the value fit's G^-1 R.
 //
 // One step (pivot set P, k <= 64) by a team:
-//   A. every member gathers A_PP and inverts it in LDS by k single sweeps
-//      (the pivot blocks are quasi-definite, so each pivot is nonzero with
-//      the sign s_q); the pivot rows of those sweeps also give L^-1 and D.
-//      The members split the 32-row halves of the 64-row bands, gather U
-//      for theirs, form
-//      W = U L^-T and V = U B on fp64 MFMA and stage both in global memory;
+//   A. the members hold L^-1 and 1/D of the pivot block A_PP = L D L^T,
+//      either from the previous step's lookahead member (see sweep_step) or
+//      by gathering A_PP and factoring it in LDS (small_ldl: 16-pivot
+//      diagonal sweeps, panels on fp64 MFMA; the pivot blocks are
+//      quasi-definite, so each pivot is nonzero with the sign s_q), and form
+//      B = L^-T D^-1 L^-1 on MFMA.  They split the 32-row halves of the
+//      64-row bands, gather U = A[rows, P] for theirs, form W = U L^-T and
+//      V = U B on fp64 MFMA and stage both in global memory;
 //   -- team barrier --
-//   B. the members split the 64 x 64 tiles of the lower triangle and update
-//      them in place, A -= W D^-1 W^T on fp64 MFMA off the pivots (phase A
-//      copied every pivot column, so no tile is read by another member here);
+//   B. the members' waves take tile tasks of the lower triangle by ticket
+//      and update them in place, A -= W D^-1 W^T on fp64 MFMA off the pivots
+//      (phase A copied every pivot column, so no tile is read by another
+//      member here);
 //   -- team barrier --
 // ---------------------------------------------------------------------------
 

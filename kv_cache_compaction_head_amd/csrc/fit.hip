@@ -1397,7 +1397,12 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& team_ref, in
   const int workers = la ? tsize - 1 : tsize;
   const int nw = workers * (kTeamThreads / 64);
   const int parts = 2 * total <= nw ? 4 : (total < nw ? 2 : 1);
-  const int tasks = total * parts;
+  // With at most 16 right-hand sides (the bias system has one), a
+  // right-hand-side tile is one task over its first 16 columns (the others
+  // are inactive: zero and never updated), ahead of the variable tiles.
+  const bool narrow = nrb == 1 && M.n_rhs <= 16;
+  const int rtasks = narrow ? nvb : 0;
+  const int tasks = narrow ? rtasks + (total - nvb) * parts : total * parts;
   if (me_la) {
     // the lookahead member arrived at the first barrier after its gathers;
     // it factors the next block and waits for that barrier only before the
@@ -1436,12 +1441,17 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& team_ref, in
     while (tk < end) {
       pend = draw_ticket(tm);
       if (tk >= base) {  // (always, unless a timed-out barrier let the members drift apart)
-        const int a = static_cast<int>(tk - base), part = a % parts;
-        TileWalk w{0, 0, nrb, skip_below, vb0};
-        w.seek(a / parts);
-        if (parts == 1) wave_tile<4, 4>(M, w.I(), w.J(), 0, 0);
-        else if (parts == 2) wave_tile<2, 4>(M, w.I(), w.J(), 2 * part, 0);
-        else wave_tile<2, 2>(M, w.I(), w.J(), 2 * (part >> 1), 2 * (part & 1));
+        const int a = static_cast<int>(tk - base);
+        if (a < rtasks) {
+          wave_tile<4, 1>(M, vb0 + a, 0, 0, 0);
+        } else {
+          const int av = a - rtasks, part = av % parts;
+          TileWalk w{0, 0, narrow ? 0 : nrb, skip_below, vb0};
+          w.seek(av / parts);
+          if (parts == 1) wave_tile<4, 4>(M, w.I(), w.J(), 0, 0);
+          else if (parts == 2) wave_tile<2, 4>(M, w.I(), w.J(), 2 * part, 0);
+          else wave_tile<2, 2>(M, w.I(), w.J(), 2 * (part >> 1), 2 * (part & 1));
+        }
       }
       tk = ticket_value(pend);
     }

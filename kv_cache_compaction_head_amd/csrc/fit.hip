@@ -1121,7 +1121,24 @@ __device__ __forceinline__ void wave_tile(const SweepMat& M, int I, int J, int r
   for (int ra = 0; ra < NRA; ++ra)
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) acc[ra][rb] = f64x4{0.0, 0.0, 0.0, 0.0};
-  {
+  // When every row of the part (or every column) is a pivot or inactive, no
+  // entry takes the W D^-1 W^T update (pivot entries come from V and the
+  // pivot block; inactive rows and columns of W are zero), so the
+  // contraction is skipped.  The value fit's pivot blocks are whole bands.
+  bool rfree = true, cfree = true;
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int c = J * kSB + 16 * (co + rb) + l16;
+    cfree &= sm.pos[c] >= 0 || !s_active(M, c);
+  }
+#pragma unroll
+  for (int ra = 0; ra < NRA; ++ra)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = I * kSB + 16 * (ro + ra) + g16 + 4 * i;
+      rfree &= sm.pos[r] >= 0 || !s_active(M, r);
+    }
+  if (!__all(rfree) && !__all(cfree)) {
     // the next chunk's loads are issued ahead of the current chunk's MFMAs;
     // the scheduling barriers keep the compiler from sinking them below
     // (it would, to shorten register live ranges, and every chunk would then

@@ -242,6 +242,21 @@ __global__ void k_lse_merge(const double2* __restrict__ ml, double* __restrict__
   if (ok && part == 0) lse[i] = m + log(((l + l1) + l2) + l3);
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes
+// land at dst + 16 l (dst the same for the whole wave).
+__device__ __forceinline__ void lds_copy16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+// XOR swizzle of the 16-byte chunks of a key row in an unpadded LDS tile
+// with CPR chunks per row: the 16 rows an MFMA operand read takes at once
+// land in 16 distinct 16-byte bank groups of a 256-byte bank row.
+template <int CPR>
+__device__ __forceinline__ int k_swz(int r) {
+  static_assert(CPR == 8 || CPR == 16, "16-byte chunks per row");
+  return (r / (16 / CPR)) & (CPR - 1);
+}
+
 // Position of key kk (0..31 inside a tile) in the transposed V tile: the
 // k-slots of lane group g for MFMA half h are the accumulator rows
 // 8*(e/4) + 4*g + e%4 + 16*h, e = 0..7; store those 8 keys contiguously.
@@ -279,12 +294,14 @@ __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
-__device__ __forceinline__ float half_wave_rowsum(const float (&v)[16], int lane) {
+template <bool SQ, class Vec>
+__device__ __forceinline__ float half_wave_rowsum(const Vec& v, int lane) {
   const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
   float w[8], x[4], y[2];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[8 + i]),
+    const float a = SQ ? v[i] * v[i] : v[i], c = SQ ? v[8 + i] * v[8 + i] : v[8 + i];
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(c),
                                                     false, false);
     w[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
@@ -313,7 +330,12 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
                                                    int keys_per_split, int nqb, int nsplit,
                                                    int B, int qg) {
   constexpr int KS = Frag<In>::KS, NK = D / KS, BN = 64;
-  constexpr int LD = D + 16 / sizeof(In);
+  // bf16 K tiles go global -> LDS directly (no registers), unpadded, with
+  // the 16-byte chunks of a row XOR-swizzled; fp32 tiles are staged through
+  // registers into padded rows
+  constexpr bool DMA = sizeof(In) == 2;
+  constexpr bool EARLY = DMA && !MASK;
+  constexpr int LD = DMA ? D : D + 16 / sizeof(In);
   constexpr int LDV = BN + 16 / sizeof(In);
   constexpr int ND = D / 32;
   constexpr int VEC = 16 / sizeof(In), CPR = D / VEC;  // 16-byte chunks per row
@@ -350,7 +372,7 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
   const int j0 = split * keys_per_split;
   const int j1 = min(T, j0 + keys_per_split);
   const int ntile = (j1 - j0 + BN - 1) / BN;
-  uint4 pk[NCH], pv[NCH];
+  uint4 pk[DMA ? 1 : NCH], pv[NCH];
   uint64_t pm = 0;
   // rows past the split end read row j1-1 (always valid) and are zeroed, so
   // the fetch is one unconditional batch of loads
@@ -359,14 +381,24 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
   // 16-byte column chunk of 64 consecutive keys: each of its transposed
   // writes then covers one contiguous 128-byte run of a V^T row, free of
   // bank conflicts.
-  auto fetch = [&](int jt) {
+  auto fetch = [&](int jt, int buf) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int idx = threadIdx.x + c * 256, r = idx / CPR, col = (idx % CPR) * VEC;
+      const int idx = threadIdx.x + c * 256, r = idx / CPR;
       const bool ok = jt + r < j1;
-      const uint4 kv = *reinterpret_cast<const uint4*>(
-          Kb + static_cast<size_t>(ok ? jt + r : j1 - 1) * D + col);
-      pk[c] = ok ? kv : make_uint4(0, 0, 0, 0);
+      if constexpr (DMA) {
+        // one wave's 64 lanes fill 1 KB of the tile (slots idx of the wave,
+        // 16 bytes each); slot (r, p) holds chunk p ^ swz(r) of key row r.
+        // Rows past the split end copy row j1-1: their p is masked to zero.
+        const int lc = (idx % CPR) ^ k_swz<CPR>(r);
+        lds_copy16(Kb + static_cast<size_t>(ok ? jt + r : j1 - 1) * D + lc * VEC,
+                   &sK[buf][(c * 256 + (threadIdx.x & ~63)) * VEC]);
+      } else {
+        const int col = (idx % CPR) * VEC;
+        const uint4 kv = *reinterpret_cast<const uint4*>(
+            Kb + static_cast<size_t>(ok ? jt + r : j1 - 1) * D + col);
+        pk[c] = ok ? kv : make_uint4(0, 0, 0, 0);
+      }
       const int rv = threadIdx.x & (BN - 1), colv = ((threadIdx.x >> 6) + 4 * c) * VEC;
       const bool okv = jt + rv < j1;
       const uint4 vv = *reinterpret_cast<const uint4*>(
@@ -378,8 +410,10 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
   auto stash = [&](int buf) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int idx = threadIdx.x + c * 256, r = idx / CPR, col = (idx % CPR) * VEC;
-      *reinterpret_cast<uint4*>(&sK[buf][r * LD + col]) = pk[c];
+      if constexpr (!DMA) {
+        const int idx = threadIdx.x + c * 256, r = idx / CPR, col = (idx % CPR) * VEC;
+        *reinterpret_cast<uint4*>(&sK[buf][r * LD + col]) = pk[c];
+      }
       const int rv = threadIdx.x & (BN - 1), colv = ((threadIdx.x >> 6) + 4 * c) * VEC;
       In v[VEC];
       *reinterpret_cast<uint4*>(v) = pv[c];
@@ -391,28 +425,40 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
     if (MASK && threadIdx.x == 0) sMb[buf] = pm;
   };
   if (ntile > 0) {
-    fetch(j0);
+    fetch(j0, 0);
     stash(0);
   }
+  if constexpr (DMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int it = 0; it < ntile; ++it) {
     const int cur = it & 1, jt = j0 + it * BN, valid = j1 - jt;
-    if (it + 1 < ntile) fetch(jt + BN);
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      f32x16 acc = {};
+    if (it + 1 < ntile) fetch(jt + BN, cur ^ 1);
+    auto scores = [&](int st, f32x16& acc) {
+      acc = f32x16{};
+      const int row = st * 32 + (lane & 31);
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks) {
-        auto a = Frag<In>::load(&sK[cur][(st * 32 + (lane & 31)) * LD + ks * KS + g * (KS / 2)]);
-        acc = Frag<In>::mma(a, bq[ks], acc);
+        int col = ks * KS + g * (KS / 2);
+        if constexpr (DMA) col = (col / VEC ^ k_swz<CPR>(row)) * VEC;
+        acc = Frag<In>::mma(Frag<In>::load(&sK[cur][row * LD + col]), bq[ks], acc);
       }
-      float w[16];
+    };
+    // where the registers allow, both 32-key halves' scores are issued
+    // first: the second half's MFMAs run while the first half's
+    // exponentials are computed
+    f32x16 accS[EARLY ? 2 : 1];
+    if constexpr (EARLY) {
+      scores(0, accS[0]);
+      scores(1, accS[1]);
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      f32x16& acc = accS[EARLY ? st : 0];
+      if constexpr (!EARLY) scores(st, acc);
       if (!MASK && valid >= BN) {  // a whole tile: no bound to test
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2) - ml2lo);
-          acc[r] = p;
-          w[r] = RMS ? p * p : p;
+          acc[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2) - ml2lo);
         }
       } else {
         const uint64_t mb = MASK ? sMb[cur] : 0;
@@ -420,13 +466,11 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
         for (int r = 0; r < 16; ++r) {
           const int kk = st * 32 + mfma32_row(r, lane);
           const float e = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2) - ml2lo);
-          const float p = (kk < valid && !((mb >> kk) & 1)) ? e : 0.f;
-          acc[r] = p;
-          w[r] = RMS ? p * p : p;
+          acc[r] = (kk < valid && !((mb >> kk) & 1)) ? e : 0.f;
         }
       }
       {
-        const float tot = half_wave_rowsum(w, lane);
+        const float tot = half_wave_rowsum<RMS>(acc, lane);
         const int r = ((lane >> 4) & 1) * 8 + ((lane >> 3) & 1) * 4 + ((lane >> 2) & 1) * 2 +
                       ((lane >> 1) & 1);
         if ((lane & 1) == 0) sImp[cur][wave][st * 32 + mfma32_row(r, lane)] = tot;
@@ -463,6 +507,8 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
       }
     }
     if (it + 1 < ntile) stash(cur ^ 1);
+    // the next tile's K copies must have landed before the barrier
+    if constexpr (DMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x < BN && static_cast<int>(threadIdx.x) < valid) {
       const int t = threadIdx.x;

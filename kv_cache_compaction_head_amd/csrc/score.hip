@@ -96,6 +96,21 @@ __device__ __forceinline__ void load_q_frags(typename Frag<In>::T* bq, const In*
                    : Frag<In>::zero();
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes
+// land at dst + 16 l (dst the same for the whole wave).
+__device__ __forceinline__ void lds_copy16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+// XOR swizzle of the 16-byte chunks of a key row in an unpadded LDS tile
+// with CPR chunks per row: the 16 rows an MFMA operand read takes at once
+// land in 16 distinct 16-byte bank groups of a 256-byte bank row.
+template <int CPR>
+__device__ __forceinline__ int k_swz(int r) {
+  static_assert(CPR == 8 || CPR == 16, "16-byte chunks per row");
+  return (r / (16 / CPR)) & (CPR - 1);
+}
+
 // ---------------------------------------------------------------------------
 // K1: partial log-sum-exp per (query, key split).
 // grid (ceil(n/128), nsplit, B), block 256.  ml[b][split][q] = (m, l) with
@@ -108,7 +123,10 @@ __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
                                                    double2* __restrict__ ml, int n, int T,
                                                    int keys_per_split, int nqb, int nsplit, int B,
                                                    int qg) {
-  constexpr int KS = Frag<In>::KS, NK = D / KS, BN = 64, LD = D + 16 / sizeof(In);
+  // bf16 K tiles go global -> LDS directly into swizzled unpadded rows (as
+  // in K2); fp32 tiles are staged through registers into padded rows
+  constexpr bool DMA = sizeof(In) == 2;
+  constexpr int KS = Frag<In>::KS, NK = D / KS, BN = 64, LD = DMA ? D : D + 16 / sizeof(In);
   constexpr int VEC = 16 / sizeof(In), CPR = D / VEC, NCH = BN * CPR / 256;
   __shared__ __align__(16) In sK[2][BN * LD];
   __shared__ uint64_t sMb[2];  // excluded keys of the tile, one bit per key
@@ -126,26 +144,36 @@ __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
   const int j0 = split * keys_per_split;
   const int j1 = min(T, j0 + keys_per_split);
   const int ntile = (j1 - j0 + BN - 1) / BN;
-  // next tile's K rows in registers while the current tile is computed;
-  // rows past the split end read row j1-1 and are zeroed (one batch of loads)
-  uint4 pk[NCH];
+  // next tile's K rows in flight while the current tile is computed; rows
+  // past the split end read row j1-1 (one batch of loads) and their scores
+  // are masked
+  uint4 pk[DMA ? 1 : NCH];
   uint64_t pm = 0;
-  auto fetch = [&](int jt) {
+  auto fetch = [&](int jt, int buf) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int idx = threadIdx.x + c * 256, r = idx / CPR, col = (idx % CPR) * VEC;
+      const int idx = threadIdx.x + c * 256, r = idx / CPR;
       const bool ok = jt + r < j1;
-      const uint4 kv = *reinterpret_cast<const uint4*>(
-          Kb + static_cast<size_t>(ok ? jt + r : j1 - 1) * D + col);
-      pk[c] = ok ? kv : make_uint4(0, 0, 0, 0);
+      if constexpr (DMA) {
+        const int lc = (idx % CPR) ^ k_swz<CPR>(r);
+        lds_copy16(Kb + static_cast<size_t>(ok ? jt + r : j1 - 1) * D + lc * VEC,
+                   &sK[buf][(c * 256 + (threadIdx.x & ~63)) * VEC]);
+      } else {
+        const int col = (idx % CPR) * VEC;
+        const uint4 kv = *reinterpret_cast<const uint4*>(
+            Kb + static_cast<size_t>(ok ? jt + r : j1 - 1) * D + col);
+        pk[c] = ok ? kv : make_uint4(0, 0, 0, 0);
+      }
     }
     if (MASK && wave == 0) pm = __ballot(Mb[min(jt + lane, j1 - 1)] != 0);
   };
   auto stash = [&](int buf) {
+    if constexpr (!DMA) {
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int idx = threadIdx.x + c * 256, r = idx / CPR, col = (idx % CPR) * VEC;
-      *reinterpret_cast<uint4*>(&sK[buf][r * LD + col]) = pk[c];
+      for (int c = 0; c < NCH; ++c) {
+        const int idx = threadIdx.x + c * 256, r = idx / CPR, col = (idx % CPR) * VEC;
+        *reinterpret_cast<uint4*>(&sK[buf][r * LD + col]) = pk[c];
+      }
     }
     if (MASK && threadIdx.x == 0) sMb[buf] = pm;
   };
@@ -157,21 +185,35 @@ __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
   float m = -INFINITY, m2 = 0.f;
   double l = 0.0, cm = 1.0;
   if (ntile > 0) {
-    fetch(j0);
+    fetch(j0, 0);
     stash(0);
   }
+  if constexpr (DMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int it = 0; it < ntile; ++it) {
     const int cur = it & 1, jt = j0 + it * BN;
-    if (it + 1 < ntile) fetch(jt + BN);
-#pragma unroll
-    for (int st = 0; st < BN / 32; ++st) {
-      f32x16 acc = {};
+    if (it + 1 < ntile) fetch(jt + BN, cur ^ 1);
+    auto scores = [&](int st, f32x16& acc) {
+      acc = f32x16{};
+      const int row = st * 32 + (lane & 31);
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks) {
-        auto a = Frag<In>::load(&sK[cur][(st * 32 + (lane & 31)) * LD + ks * KS + g * (KS / 2)]);
-        acc = Frag<In>::mma(a, bq[ks], acc);
+        int col = ks * KS + g * (KS / 2);
+        if constexpr (DMA) col = (col / VEC ^ k_swz<CPR>(row)) * VEC;
+        acc = Frag<In>::mma(Frag<In>::load(&sK[cur][row * LD + col]), bq[ks], acc);
       }
+    };
+    // bf16: both halves' scores are issued first, so the second half's
+    // MFMAs run under the first half's exponentials
+    f32x16 accS[DMA ? 2 : 1];
+    if constexpr (DMA) {
+      scores(0, accS[0]);
+      scores(1, accS[1]);
+    }
+#pragma unroll
+    for (int st = 0; st < BN / 32; ++st) {
+      f32x16& acc = accS[DMA ? st : 0];
+      if constexpr (!DMA) scores(st, acc);
       float tmax = -INFINITY;
       if (!MASK && jt + BN <= j1) {  // a whole tile: no key past the split
 #pragma unroll
@@ -201,6 +243,7 @@ __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
       }
     }
     if (it + 1 < ntile) stash(cur ^ 1);
+    if constexpr (DMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
   // lanes l and l+32 hold the same query over different keys: merge them
@@ -240,21 +283,6 @@ __global__ void k_lse_merge(const double2* __restrict__ ml, double* __restrict__
     }
   const double l1 = __shfl_down(l, 1), l2 = __shfl_down(l, 2), l3 = __shfl_down(l, 3);
   if (ok && part == 0) lse[i] = m + log(((l + l1) + l2) + l3);
-}
-
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes
-// land at dst + 16 l (dst the same for the whole wave).
-__device__ __forceinline__ void lds_copy16(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-}
-
-// XOR swizzle of the 16-byte chunks of a key row in an unpadded LDS tile
-// with CPR chunks per row: the 16 rows an MFMA operand read takes at once
-// land in 16 distinct 16-byte bank groups of a 256-byte bank row.
-template <int CPR>
-__device__ __forceinline__ int k_swz(int r) {
-  static_assert(CPR == 8 || CPR == 16, "16-byte chunks per row");
-  return (r / (16 / CPR)) & (CPR - 1);
 }
 
 // Position of key kk (0..31 inside a tile) in the transposed V tile: the

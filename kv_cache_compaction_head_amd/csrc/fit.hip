@@ -1111,7 +1111,8 @@ __device__ __forceinline__ void wave_tile_mfma(int c, bool diag, int ro, int co,
 }
 
 template <int NRA, int NRB>
-__device__ __forceinline__ void wave_tile(const SweepMat& M, int I, int J, int ro, int co) {
+__device__ __forceinline__ void wave_tile(const SweepMat& M, int I, int J, int ro, int co,
+                                          int nch) {
   SweepSmem& sm = g_sw;
   const int lane = threadIdx.x & 63, g16 = lane >> 4, l16 = lane & 15;
   const bool diag = I == J;
@@ -1143,16 +1144,32 @@ __device__ __forceinline__ void wave_tile(const SweepMat& M, int I, int J, int r
     // the scheduling barriers keep the compiler from sinking them below
     // (it would, to shorten register live ranges, and every chunk would then
     // wait a whole L2 round trip)
+    // (only the first nch chunks: W and 1/D are zero past the step's k
+    // pivots)
+    // (a full step's eight chunks unrolled, fewer in a loop over pairs)
     double a0[NRA][2], b0[NRB][2], a1[NRA][2], b1[NRB][2];
     wave_tile_chunk<NRA, NRB>(M, I, J, ro, co, 0, a0, b0);
+    if (nch >= 8) {
 #pragma unroll
-    for (int c = 0; c < 8; c += 2) {
-      wave_tile_chunk<NRA, NRB>(M, I, J, ro, co, c + 1, a1, b1);
-      __builtin_amdgcn_sched_barrier(0);
-      wave_tile_mfma<NRA, NRB>(c, diag, ro, co, a0, b0, acc);
-      if (c + 2 < 8) wave_tile_chunk<NRA, NRB>(M, I, J, ro, co, c + 2, a0, b0);
-      __builtin_amdgcn_sched_barrier(0);
-      wave_tile_mfma<NRA, NRB>(c + 1, diag, ro, co, a1, b1, acc);
+      for (int c = 0; c < 8; c += 2) {
+        wave_tile_chunk<NRA, NRB>(M, I, J, ro, co, c + 1, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        wave_tile_mfma<NRA, NRB>(c, diag, ro, co, a0, b0, acc);
+        if (c + 2 < 8) wave_tile_chunk<NRA, NRB>(M, I, J, ro, co, c + 2, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        wave_tile_mfma<NRA, NRB>(c + 1, diag, ro, co, a1, b1, acc);
+      }
+    } else {
+      const int nc = (nch + 1) & ~1;  // whole pairs of chunks
+#pragma unroll 1
+      for (int c = 0; c < nc; c += 2) {
+        wave_tile_chunk<NRA, NRB>(M, I, J, ro, co, c + 1, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        wave_tile_mfma<NRA, NRB>(c, diag, ro, co, a0, b0, acc);
+        if (c + 2 < nc) wave_tile_chunk<NRA, NRB>(M, I, J, ro, co, c + 2, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        wave_tile_mfma<NRA, NRB>(c + 1, diag, ro, co, a1, b1, acc);
+      }
     }
   }
   // pivot slots of this part's rows and columns (sm.pos is -1 off the
@@ -1420,6 +1437,7 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& team_ref, in
   const bool narrow = nrb == 1 && M.n_rhs <= 16;
   const int rtasks = narrow ? nvb : 0;
   const int tasks = narrow ? rtasks + (total - nvb) * parts : total * parts;
+  const int nch = (k + 7) / 8;  // contraction chunks of 8 that hold pivots
   if (me_la) {
     // the lookahead member arrived at the first barrier after its gathers;
     // it factors the next block and waits for that barrier only before the
@@ -1460,14 +1478,14 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& team_ref, in
       if (tk >= base) {  // (always, unless a timed-out barrier let the members drift apart)
         const int a = static_cast<int>(tk - base);
         if (a < rtasks) {
-          wave_tile<4, 1>(M, vb0 + a, 0, 0, 0);
+          wave_tile<4, 1>(M, vb0 + a, 0, 0, 0, nch);
         } else {
           const int av = a - rtasks, part = av % parts;
           TileWalk w{0, 0, narrow ? 0 : nrb, skip_below, vb0};
           w.seek(av / parts);
-          if (parts == 1) wave_tile<4, 4>(M, w.I(), w.J(), 0, 0);
-          else if (parts == 2) wave_tile<2, 4>(M, w.I(), w.J(), 2 * part, 0);
-          else wave_tile<2, 2>(M, w.I(), w.J(), 2 * (part >> 1), 2 * (part & 1));
+          if (parts == 1) wave_tile<4, 4>(M, w.I(), w.J(), 0, 0, nch);
+          else if (parts == 2) wave_tile<2, 4>(M, w.I(), w.J(), 2 * part, 0, nch);
+          else wave_tile<2, 2>(M, w.I(), w.J(), 2 * (part >> 1), 2 * (part & 1), nch);
         }
       }
       tk = ticket_value(pend);

@@ -172,39 +172,55 @@ __global__ __launch_bounds__(256) void k_ps(const In* __restrict__ Q, const In* 
 // ---------------------------------------------------------------------------
 // C[b][a][c] = sum_i A[b][i][ca(a)] * Bm[b][i][c]  for a < mA_b, c < mB_b.
 // ca: optional per-head column map of A.  SYM: B = A, lower tiles only,
-// mirrored.  grid (tiles, ksplit, B): with ksplit > 1 each workgroup sums a
-// slice of the rows into part[b][split][tile][64*64] and k_atb_reduce adds
-// the slices in order.  The next 16-row chunk is fetched into registers while
-// the MFMAs consume the current one.
+// mirrored.  Each head has G workgroups.  Its split into row slices follows
+// its own sizes (atb_shape), which only the device knows for the value fit's
+// passive set: with ks > 1 workgroup g sums slice g / nt of tile g % nt into
+// part[b][slice][tile][64*64] and k_atb_reduce adds the slices in order;
+// with ks = 1 workgroup g computes tile g whole (G is at least every head's
+// tile count).  The next
+// 16-row chunk is fetched into registers while the MFMAs consume the current
+// one.
 // ---------------------------------------------------------------------------
-template <class TB, bool SYM>
-__global__ __launch_bounds__(256) void k_atb(const double* __restrict__ A, size_t sA, int lda,
-                                             const int32_t* __restrict__ colA, size_t sColA,
-                                             const TB* __restrict__ Bm, size_t sB, int ldb,
-                                             double* __restrict__ C, size_t sC, int ldc,
-                                             int nrows, const int32_t* __restrict__ msz,
-                                             int mA_const, int mB_const, int tiles_x,
-                                             double* __restrict__ part, int ntiles) {
-  __shared__ double sAt[kKC * kTile], sBt[kKC * kTile];
-  const int b = blockIdx.z, split = blockIdx.y, ksplit = gridDim.y;
-  const int mA = msz ? msz[b] : mA_const;
-  const int mB = SYM ? mA : mB_const;
-  int ty, tx;
-  if (SYM) tri_decode(blockIdx.x, ty, tx);
-  else {
-    ty = blockIdx.x / tiles_x;
-    tx = blockIdx.x % tiles_x;
-  }
-  const int a0 = ty * kTile, c0 = tx * kTile;
-  if (a0 >= mA || c0 >= mB) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const double* Ab = A + b * sA;
-  const TB* Bb = Bm + b * sB;
-  const int32_t* ca = colA ? colA + b * sColA : nullptr;
-  // this slice's rows, whole 16-row chunks
+struct AtbShape {
+  int nt, ks, per;  // tiles, row slices, 16-row chunks per slice
+};
+constexpr int kAtbGrid = 2048;  // workgroups a product aims for, over all heads
+__host__ __device__ inline AtbShape atb_shape(int mA, int mB, bool sym, int G, int cap_tiles,
+                                              int nrows, int B) {
+  const int ta = (mA + kTile - 1) / kTile, tb = (mB + kTile - 1) / kTile;
   const int nchunk = (nrows + kKC - 1) / kKC;
-  const int per = (nchunk + ksplit - 1) / ksplit;
-  const int k0 = split * per * kKC, k1 = min(nrows, (split + 1) * per * kKC);
+  AtbShape sh;
+  sh.nt = sym ? ta * (ta + 1) / 2 : ta * tb;
+  int ks = 1;
+  if (sh.nt > 0) {
+    ks = G / sh.nt;
+    if (ks > kAtbGrid / (B * sh.nt)) ks = kAtbGrid / (B * sh.nt);  // enough work already
+    if (ks > cap_tiles / sh.nt) ks = cap_tiles / sh.nt;  // partials of a head
+    if (ks > 16) ks = 16;
+    if (ks > nchunk / 4) ks = nchunk / 4;  // at least 4 chunks a slice
+    if (ks < 1) ks = 1;
+  }
+  sh.ks = ks;
+  sh.per = (nchunk + ks - 1) / ks;
+  return sh;
+}
+
+__device__ __forceinline__ void atb_decode(bool sym, int tile, int tb, int& ty, int& tx) {
+  if (sym) tri_decode(tile, ty, tx);
+  else {
+    ty = tile / tb;
+    tx = tile % tb;
+  }
+}
+
+// One 64 x 64 tile (a0, c0) over rows [k0, k1) into acc.
+template <class TB, bool SYM>
+__device__ __forceinline__ void atb_tile(const double* __restrict__ Ab, int lda,
+                                         const int32_t* __restrict__ ca,
+                                         const TB* __restrict__ Bb, int ldb, int mA, int mB,
+                                         int a0, int c0, int k0, int k1, double* sAt, double* sBt,
+                                         f64x4 (&acc)[2][2]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   constexpr int NE = kKC * kTile / 256;
   int colA_r[NE], colB_r[NE];
 #pragma unroll
@@ -228,7 +244,10 @@ __global__ __launch_bounds__(256) void k_atb(const double* __restrict__ A, size_
                     : 0.0;
     }
   };
-  f64x4 acc[2][2] = {};
+#pragma unroll
+  for (int ra = 0; ra < 2; ++ra)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) acc[ra][rb] = f64x4{0.0, 0.0, 0.0, 0.0};
   if (k0 < k1) fetch(k0);
   for (int k = k0; k < k1; k += kKC) {
     __syncthreads();
@@ -242,58 +261,83 @@ __global__ __launch_bounds__(256) void k_atb(const double* __restrict__ A, size_
     if (k + kKC < k1) fetch(k + kKC);
     tile_mma(sAt, sBt, acc, wave, lane);
   }
-  if (ksplit == 1) {
-    double* Cb = C + b * sC;
+}
+
+template <class TB, bool SYM>
+__global__ __launch_bounds__(256) void k_atb(const double* __restrict__ A, size_t sA, int lda,
+                                             const int32_t* __restrict__ colA, size_t sColA,
+                                             const TB* __restrict__ Bm, size_t sB, int ldb,
+                                             double* __restrict__ C, size_t sC, int ldc,
+                                             int nrows, const int32_t* __restrict__ msz,
+                                             int mA_const, int mB_const,
+                                             double* __restrict__ part, int G, int cap_tiles) {
+  __shared__ double sAt[kKC * kTile], sBt[kKC * kTile];
+  const int b = blockIdx.x / G, g = blockIdx.x % G;
+  const int mA = msz ? msz[b] : mA_const;
+  const int mB = SYM ? mA : mB_const;
+  const AtbShape sh = atb_shape(mA, mB, SYM, G, cap_tiles, nrows, gridDim.x / G);
+  if (g >= sh.nt * sh.ks && sh.ks > 1) return;
+  const int tb = (mB + kTile - 1) / kTile;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const double* Ab = A + b * sA;
+  const TB* Bb = Bm + b * sB;
+  const int32_t* ca = colA ? colA + b * sColA : nullptr;
+  // ks = 1: tile g over all rows, into C; else tile g % nt over row slice
+  // g / nt, into the partials (G is at least the tile count of every head)
+  const bool whole = sh.ks == 1;
+  const int split = whole ? 0 : g / sh.nt, tile = whole ? g : g % sh.nt;
+  if (tile >= sh.nt) return;
+  const int k0 = whole ? 0 : split * sh.per * kKC;
+  const int k1 = whole ? nrows : min(nrows, (split + 1) * sh.per * kKC);
+  double* Cb = C + b * sC;
+  f64x4 acc[2][2];
+  {
+    int ty, tx;
+    atb_decode(SYM, tile, tb, ty, tx);
+    const int a0 = ty * kTile, c0 = tx * kTile;
+    atb_tile<TB, SYM>(Ab, lda, ca, Bb, ldb, mA, mB, a0, c0, k0, k1, sAt, sBt, acc);
+    double* P = part + (static_cast<size_t>(b) * cap_tiles + split * sh.nt + tile) * (kTile * kTile);
 #pragma unroll
     for (int ra = 0; ra < 2; ++ra)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = a0 + tile_row(wave, lane, ra, i), c = c0 + tile_col(wave, lane, rb);
-          if (r < mA && c < mB) {
+          const int rr = tile_row(wave, lane, ra, i), cc = tile_col(wave, lane, rb);
+          const int r = a0 + rr, c = c0 + cc;
+          if (!whole) {
+            P[rr * kTile + cc] = acc[ra][rb][i];
+          } else if (r < mA && c < mB) {
             Cb[static_cast<size_t>(r) * ldc + c] = acc[ra][rb][i];
             if (SYM && tx != ty) Cb[static_cast<size_t>(c) * ldc + r] = acc[ra][rb][i];
           }
         }
-  } else {
-    double* P = part + ((static_cast<size_t>(b) * ksplit + split) * ntiles + blockIdx.x) * (kTile * kTile);
-#pragma unroll
-    for (int ra = 0; ra < 2; ++ra)
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          P[tile_row(wave, lane, ra, i) * kTile + tile_col(wave, lane, rb)] = acc[ra][rb][i];
   }
 }
 
-// Sum the ksplit row slices of each tile in order and store (mirrored for
-// symmetric products).  grid (tiles * 16, B), block 256: one element of a
-// tile per thread, its ksplit partials loaded together.
+// Sum a head's row slices of each tile in order and store (mirrored for
+// symmetric products); nothing to do for heads computed whole.  grid
+// (tiles that may split * 16, B), block 256: one element per thread.
 template <bool SYM>
 __global__ __launch_bounds__(256) void k_atb_reduce(const double* __restrict__ part,
                                                     double* __restrict__ C, size_t sC, int ldc,
                                                     const int32_t* __restrict__ msz, int mA_const,
-                                                    int mB_const, int tiles_x, int ntiles,
-                                                    int ksplit) {
+                                                    int mB_const, int nrows, int G,
+                                                    int cap_tiles) {
   const int b = blockIdx.y, tile = blockIdx.x >> 4;
   const int mA = msz ? msz[b] : mA_const;
   const int mB = SYM ? mA : mB_const;
+  const AtbShape sh = atb_shape(mA, mB, SYM, G, cap_tiles, nrows, gridDim.y);
+  if (sh.ks == 1 || tile >= sh.nt) return;
   int ty, tx;
-  if (SYM) tri_decode(tile, ty, tx);
-  else {
-    ty = tile / tiles_x;
-    tx = tile % tiles_x;
-  }
+  atb_decode(SYM, tile, (mB + kTile - 1) / kTile, ty, tx);
   const int a0 = ty * kTile, c0 = tx * kTile;
-  if (a0 >= mA || c0 >= mB) return;
   double* Cb = C + b * sC;
-  const double* P = part + (static_cast<size_t>(b) * ksplit * ntiles + tile) * (kTile * kTile);
+  const double* P = part + (static_cast<size_t>(b) * cap_tiles + tile) * (kTile * kTile);
   const int e = (blockIdx.x & 15) * 256 + threadIdx.x;
   const int r = a0 + e / kTile, c = c0 + e % kTile;
   double v = 0.0;
-  for (int sp = 0; sp < ksplit; ++sp) v += P[static_cast<size_t>(sp) * ntiles * kTile * kTile + e];
+  for (int sp = 0; sp < sh.ks; ++sp) v += P[static_cast<size_t>(sp) * sh.nt * kTile * kTile + e];
   if (r < mA && c < mB) {
     Cb[static_cast<size_t>(r) * ldc + c] = v;
     if (SYM && tx != ty) Cb[static_cast<size_t>(c) * ldc + r] = v;
@@ -1874,7 +1918,8 @@ static int team_shape(int B, int tiles, int cap, int& tx) {
   return g * nteams;
 }
 
-// A^T B over heads with split-K chosen so the grid has ~2048 workgroups.
+// A^T B over heads: G workgroups a head (~2048 in all, at least one a tile
+// of the largest product); each head's split-K follows its own sizes.
 template <class TB, bool SYM>
 static void launch_atb(const double* A, size_t sA, int lda, const int32_t* colA, size_t sColA,
                        const TB* Bm, size_t sB, int ldb, double* C, size_t sC, int ldc, int nrows,
@@ -1882,19 +1927,26 @@ static void launch_atb(const double* A, size_t sA, int lda, const int32_t* colA,
                        hipStream_t st) {
   const int ta = (mA + kTile - 1) / kTile, tb = (mB + kTile - 1) / kTile;
   const int ntiles = SYM ? ta * (ta + 1) / 2 : ta * tb;
-  const int nchunk = (nrows + kKC - 1) / kKC;
-  int ksplit = 2048 / (ntiles * B);
-  if (ksplit > 16) ksplit = 16;
-  if (ksplit > nchunk / 4) ksplit = nchunk / 4;
-  while (ksplit > 1 &&
-         static_cast<size_t>(B) * ksplit * ntiles * kTile * kTile > part_cap)
-    --ksplit;
-  if (ksplit < 1) ksplit = 1;
-  hipLaunchKernelGGL((k_atb<TB, SYM>), dim3(ntiles, ksplit, B), dim3(256), 0, st, A, sA, lda,
-                     colA, sColA, Bm, sB, ldb, C, sC, ldc, nrows, msz, mA, mB, tb, part, ntiles);
-  if (ksplit > 1)
-    hipLaunchKernelGGL((k_atb_reduce<SYM>), dim3(ntiles * 16, B), dim3(256), 0, st, part, C, sC,
-                       ldc, msz, mA, mB, tb, ntiles, ksplit);
+  if (ntiles == 0 || B == 0) return;
+  int G = (kAtbGrid + B - 1) / B;
+  if (G > 16 * ntiles) G = 16 * ntiles;
+  if (G < ntiles) G = ntiles;
+  // odd, so that consecutive heads start on different XCDs (workgroups go
+  // round-robin over 8) and their busy workgroups spread evenly
+  G |= 1;
+  const size_t ct = part_cap / (static_cast<size_t>(B) * kTile * kTile);
+  const int cap_tiles = ct > (1u << 20) ? (1 << 20) : static_cast<int>(ct);
+  hipLaunchKernelGGL((k_atb<TB, SYM>), dim3(B * G), dim3(256), 0, st, A, sA, lda, colA, sColA, Bm,
+                     sB, ldb, C, sC, ldc, nrows, msz, mA, mB, part, G, cap_tiles);
+  // sizes known here (no per-head column count): skip the reduction when no
+  // head splits
+  if (!msz && atb_shape(mA, mB, SYM, G, cap_tiles, nrows, B).ks == 1) return;
+  // a head splits only with fewer than kAtbGrid / (2 B) tiles
+  int rt = kAtbGrid / (2 * B);
+  if (rt > ntiles) rt = ntiles;
+  if (rt < 1) return;
+  hipLaunchKernelGGL((k_atb_reduce<SYM>), dim3(rt * 16, B), dim3(256), 0, st, part, C, sC, ldc,
+                     msz, mA, mB, nrows, G, cap_tiles);
 }
 
 int sweep_ld(int t, int D) {

@@ -111,6 +111,18 @@ __device__ __forceinline__ int k_swz(int r) {
   return (r / (16 / CPR)) & (CPR - 1);
 }
 
+// Bit r set when accumulator row r of this lane holds a live key: tile key
+// st*32 + mfma32_row(r, lane) below `valid` and not excluded (bit set in excl).
+__device__ __forceinline__ unsigned live_rows(int st, int valid, uint64_t excl, int lane) {
+  const uint64_t vm = valid >= 64 ? ~0ull : ((1ull << (valid > 0 ? valid : 0)) - 1ull);
+  const unsigned h = static_cast<unsigned>((vm & ~excl) >> (32 * st));
+  const int gs = 4 * (lane >> 5);
+  unsigned k = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) k |= ((h >> (8 * j + gs)) & 0xFu) << (4 * j);
+  return k;
+}
+
 // ---------------------------------------------------------------------------
 // K1: partial log-sum-exp per (query, key split).
 // grid (ceil(n/128), nsplit, B), block 256.  ml[b][split][q] = (m, l) with
@@ -215,15 +227,22 @@ __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
       f32x16& acc = accS[DMA ? st : 0];
       if constexpr (!DMA) scores(st, acc);
       float tmax = -INFINITY;
-      if (!MASK && jt + BN <= j1) {  // a whole tile: no key past the split
+      const uint64_t mb = MASK ? sMb[cur] : 0;
+      if (mb == 0 && jt + BN <= j1) {  // a whole tile, nothing excluded
 #pragma unroll
         for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, acc[r]);
-      } else {
-        const uint64_t mb = MASK ? sMb[cur] : 0;
+      } else if constexpr (MASK) {
+        const unsigned live = live_rows(st, j1 - jt, mb, lane);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kk = st * 32 + mfma32_row(r, lane), j = jt + kk;
-          const float s = (j < j1 && !((mb >> kk) & 1)) ? acc[r] : -INFINITY;
+          const float s = ((live >> r) & 1u) ? acc[r] : -INFINITY;
+          acc[r] = s;
+          tmax = fmaxf(tmax, s);
+        }
+      } else {  // the split's last, partial tile
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float s = jt + st * 32 + mfma32_row(r, lane) < j1 ? acc[r] : -INFINITY;
           acc[r] = s;
           tmax = fmaxf(tmax, s);
         }
@@ -362,7 +381,7 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
   // the 16-byte chunks of a row XOR-swizzled; fp32 tiles are staged through
   // registers into padded rows
   constexpr bool DMA = sizeof(In) == 2;
-  constexpr bool EARLY = DMA && !MASK;
+  constexpr bool EARLY = DMA;
   constexpr int LD = DMA ? D : D + 16 / sizeof(In);
   constexpr int LDV = BN + 16 / sizeof(In);
   constexpr int ND = D / 32;
@@ -471,9 +490,8 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
         acc = Frag<In>::mma(Frag<In>::load(&sK[cur][row * LD + col]), bq[ks], acc);
       }
     };
-    // where the registers allow, both 32-key halves' scores are issued
-    // first: the second half's MFMAs run while the first half's
-    // exponentials are computed
+    // bf16: both 32-key halves' scores are issued first, so the second
+    // half's MFMAs run while the first half's exponentials are computed
     f32x16 accS[EARLY ? 2 : 1];
     if constexpr (EARLY) {
       scores(0, accS[0]);
@@ -483,18 +501,24 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
     for (int st = 0; st < 2; ++st) {
       f32x16& acc = accS[EARLY ? st : 0];
       if constexpr (!EARLY) scores(st, acc);
-      if (!MASK && valid >= BN) {  // a whole tile: no bound to test
+      const uint64_t mb = MASK ? sMb[cur] : 0;
+      if (mb == 0 && valid >= BN) {  // a whole tile, nothing excluded: no test
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           acc[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2) - ml2lo);
         }
-      } else {
-        const uint64_t mb = MASK ? sMb[cur] : 0;
+      } else if constexpr (MASK) {
+        const unsigned live = live_rows(st, valid, mb, lane);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kk = st * 32 + mfma32_row(r, lane);
           const float e = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2) - ml2lo);
-          acc[r] = (kk < valid && !((mb >> kk) & 1)) ? e : 0.f;
+          acc[r] = ((live >> r) & 1u) ? e : 0.f;
+        }
+      } else {  // the split's last, partial tile
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2) - ml2lo);
+          acc[r] = st * 32 + mfma32_row(r, lane) < valid ? e : 0.f;
         }
       }
       {

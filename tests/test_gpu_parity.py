@@ -277,7 +277,8 @@ def test_ragged_equal_budgets_is_bitwise_compact_and_clamps():
 @pytest.mark.parametrize("w,frac", [
     (synth.custom(18, 3, 2400, 192, 128, 90, "bf16", "clusters"), 0.01),
     (synth.custom(19, 2, 1000, 64, 64, 48, "f32", "sinks"), 0.02),
-], ids=["bf16", "f32_d64"])
+    (synth.custom(24, 2, 1500, 96, 64, 60, "bf16", "normal"), 0.03),   # ragged T, d = 64
+], ids=["bf16", "f32_d64", "bf16_d64"])
 def test_protected_keys_match_oracle(w, frac):
     """kvc_compact_protected against the oracle: protected slots exact (bias 0),
     the fitted part against the oracle's compaction of the unprotected keys

@@ -826,8 +826,9 @@ __device__ __forceinline__ double rdlane(double v, int src) {
 template <int N>
 __device__ __forceinline__ double row_bcast(double v) {  // lane N of each 16-lane row
   const unsigned long long u = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0x150 + N, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), 0x150 + N, 0xF, 0xF, false);
+  // every lane is written (all rows and banks enabled), so no old value
+  const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(u), 0x150 + N, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(u >> 32), 0x150 + N, 0xF, 0xF, true);
   return __longlong_as_double(static_cast<long long>(
       (static_cast<unsigned long long>(static_cast<unsigned>(hi)) << 32) | static_cast<unsigned>(lo)));
 }

@@ -229,11 +229,10 @@ def compact(Q, K, V, t: int, agg: str = "rms", ridge_rel: float = DEFAULT_RIDGE_
 
 
 def omp_dictionary(Q, K, lse):
-    """The whole-cache softmax weights P [n, T] as the greedy selection stores
-    them: computed in float64, rounded to float32 (the pages leave the
-    precision open; both sides take the argmax decisions on these values)."""
-    P = np.exp(np.asarray(Q, float) @ np.asarray(K, float).T - np.asarray(lse, float)[:, None])
-    return P.astype(np.float32).astype(np.float64)
+    """The dictionary of the greedy selection: the whole-cache softmax weights
+    P [n, T] in float64 (column j = key j's weight on every reference query;
+    each row sums to one over the T keys)."""
+    return np.exp(np.asarray(Q, float) @ np.asarray(K, float).T - np.asarray(lse, float)[:, None])
 
 
 def omp_select(P: np.ndarray, t: int):
@@ -267,7 +266,7 @@ def omp_select(P: np.ndarray, t: int):
 
 
 def compact_omp(Q, K, V, t: int, ridge_rel: float = DEFAULT_RIDGE_REL):
-    """One head with the greedy selection: keys by omp_select on the float32
+    """One head with the greedy selection: keys by omp_select on the float64
     dictionary, then the same bias (NNLS) and value fits as compact()."""
     Q, K, V = (np.asarray(a, dtype=np.float64) for a in (Q, K, V))
     lse = row_lse(Q, K)

@@ -422,13 +422,21 @@ def test_compacted_cache_with_appended_block_on_gpu():
         assert gpu_err <= oracle_err * 1.05 + 1e-5
 
 
-def _omp_replay(P, order, steps, rel=1e-9):
+OMP_PICK_TOL = 1e-6   # GPU pick vs float64 best, relative to the residual norm
+
+
+def _omp_replay(P, order, steps, tol=OMP_PICK_TOL):
     """Check that each sampled step k of a pursuit run picked a best key given
-    the run's own earlier picks: its score is within rel of the top score the
-    oracle computes (float64) for the same prefix."""
+    the run's own earlier picks.  P is the float64 dictionary; the scores
+    p_j . r / ||p_j|| are bounded by ||r|| (Cauchy-Schwarz), and the GPU stores
+    P in float32, which moves a score by at most 2 * 2^-24 * ||r|| plus what
+    the rounded columns change in the residual; a pick is valid when its
+    float64 score is within tol * ||r|| of the float64 best.  Returns the steps
+    where the GPU's pick was not the float64 argmax (near-ties)."""
     n, T = P.shape
     y = np.ones(n)
     nrm = np.sqrt((P * P).sum(axis=0))
+    near = []
     for k in steps:
         pre = list(order[:k])
         if pre:
@@ -441,7 +449,10 @@ def _omp_replay(P, order, steps, rel=1e-9):
         c[pre] = -np.inf
         best = c.max()
         got = c[order[k]]
-        assert got >= best - rel * max(abs(best), 1e-300), (k, order[k], got, best)
+        assert got >= best - tol * np.linalg.norm(r), (k, order[k], got, best)
+        if order[k] != int(np.argmax(c)):
+            near.append(k)
+    return near
 
 
 @pytest.mark.parametrize("w", [
@@ -449,9 +460,10 @@ def _omp_replay(P, order, steps, rel=1e-9):
     synth.custom(23, 2, 777, 96, 64, 33, "f32", "normal"),
 ], ids=["bf16", "f32_d64"])
 def test_omp_matches_oracle(w):
-    """kvc_compact_omp against the oracle's pursuit: the same keys in the same
-    order (each pick also replayed against the oracle given the GPU's prefix),
-    then the fits on that set within the usual bar."""
+    """kvc_compact_omp against the float64 oracle's pursuit: every GPU pick is
+    a best key (within the float32 dictionary's rounding bound) given the
+    GPU's own earlier picks, the order matches the oracle's up to such
+    near-ties, and the fits on the GPU's set are within the usual bar."""
     import torch
     import kv_cache_compaction_head_amd as kvc
     data = synth.batch(w)
@@ -467,17 +479,19 @@ def test_omp_matches_oracle(w):
         order = inter["omp_order"][h].astype(np.int64)
         assert np.array_equal(np.sort(order), idx[h]) and np.all(np.diff(idx[h]) > 0)
         P = orc.omp_dictionary(Qh, Kh, ref["lse"])
-        _omp_replay(P, order, range(w.t))
+        near = _omp_replay(P, order, range(w.t))
         same = np.array_equal(order, ref["order"])
+        if not same:  # the first divergence is a near-tie of the float64 scores
+            k = int(np.flatnonzero(order != ref["order"])[0])
+            assert k in near, (k, near)
         wv, beta, Cv, _ = orc.fit(Qh, Kh, Vh, idx[h])
         err_w = orc.rel_l2(inter["w"][h], wv)
         err_c = orc.rel_l2(res.values[h].cpu().numpy().astype(np.float64), Cv)
         o_gpu = orc.attend(Qh, Kh[idx[h]], res.values[h].cpu().numpy().astype(np.float64),
                            res.bias[h].cpu().numpy().astype(np.float64))
         err_o = orc.rel_l2(o_gpu, orc.attend(Qh, Kh[idx[h]], Cv, beta))
-        print(w.name, "head", h, "same order", same, "w", err_w, "Cv", err_c, "Ohat", err_o,
-              flush=True)
-        assert same
+        print(w.name, "head", h, "same order", same, "near-ties", near, "w", err_w, "Cv", err_c,
+              "Ohat", err_o, flush=True)
         assert max(err_w, err_c, err_o) <= _tol(w)
 
 

@@ -625,3 +625,85 @@ def test_omp_keep_everything_is_exact_and_zero_columns_last():
     P[:, [1, 4]] = 0.0
     _, order, _ = orc.omp_select(P, 6)
     assert list(order[-2:]) == [1, 4]
+
+
+def _softmax_weights_by_loops(Q, K):
+    """p_ij = exp(q_i . k_j) / sum_k exp(q_i . k_k), scalar math.fsum loops."""
+    n, T, d = Q.shape[0], K.shape[0], Q.shape[1]
+    P = np.zeros((n, T))
+    for i in range(n):
+        s = [math.fsum(Q[i, c] * K[j, c] for c in range(d)) for j in range(T)]
+        z = math.fsum(math.exp(x) for x in s)
+        for j in range(T):
+            P[i, j] = math.exp(s[j]) / z
+    return P
+
+
+def test_omp_dictionary_is_the_full_cache_softmax():
+    """The greedy selection's dictionary is the whole-cache softmax weights in
+    float64: scalar loops agree to 1e-15, every row sums to one over the T keys
+    (a dropped log-sum-exp breaks this), zero queries give 1/T everywhere, and
+    its column RMS and column mean are the two aggregators' importances."""
+    Q, K, V = _rand(120, 6, 4, scale=0.8), _rand(121, 13, 4), _rand(122, 13, 2)
+    lse = orc.row_lse(Q, K)
+    P = orc.omp_dictionary(Q, K, lse)
+    assert P.dtype == np.float64 and P.shape == (6, 13)
+    assert np.max(np.abs(P - _softmax_weights_by_loops(Q, K))) < 1e-15
+    assert np.allclose(P.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    _, imp_rms = orc.attention_stats(Q, K, V, lse, agg="rms")
+    _, imp_mean = orc.attention_stats(Q, K, V, lse, agg="mean")
+    assert np.allclose(np.sqrt((P * P).mean(axis=0)), imp_rms, rtol=1e-13, atol=0)
+    assert np.allclose(P.mean(axis=0), imp_mean, rtol=1e-13, atol=0)
+    Z = np.zeros((3, 4))
+    assert np.allclose(orc.omp_dictionary(Z, K, orc.row_lse(Z, K)), 1.0 / 13, rtol=1e-14, atol=0)
+    # not rounded to a storage precision: weights that differ below float32's
+    # resolution stay distinct
+    K2 = np.zeros((3, 1))
+    K2[:, 0] = [0.0, 1e-9, 2e-9]
+    Q2 = np.ones((1, 1))
+    P2 = orc.omp_dictionary(Q2, K2, orc.row_lse(Q2, K2))
+    assert P2[0, 0] < P2[0, 1] < P2[0, 2]
+
+
+def _greedy_by_brute_force(Q, K, t):
+    """Matching pursuit written out by hand: softmax weights by scalar loops;
+    at each step every unchosen key's column is scored by
+    sum_i p_ij r_i / sqrt(sum_i p_ij^2) with math.fsum (the reduction of
+    ||r||^2 a non-negative single-column fit would give, signed), the first
+    best key (lowest index on equal scores) is taken, and the residual is
+    y = 1 minus its least-squares fit on the chosen columns, solved through
+    the normal equations (a different route from the oracle's lstsq)."""
+    P = _softmax_weights_by_loops(Q, K)
+    n, T = P.shape
+    y = np.ones(n)
+    r = y.copy()
+    order = []
+    for _ in range(t):
+        best, bj = -math.inf, -1
+        for j in range(T):
+            if j in order:
+                continue
+            nrm = math.sqrt(math.fsum(P[i, j] ** 2 for i in range(n)))
+            c = math.fsum(P[i, j] * r[i] for i in range(n)) / nrm
+            if c > best:
+                best, bj = c, j
+        order.append(bj)
+        A = P[:, order]
+        w = np.linalg.solve(A.T @ A, A.T @ y)
+        r = y - A @ w
+    return order
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_compact_omp_matches_brute_force_greedy(seed):
+    """compact_omp at t < T picks, in order, the keys the hand-written pursuit
+    picks (softmax by loops, scores by fsum, residual by normal equations)."""
+    rng = np.random.default_rng(130 + seed)
+    T, t = 11, 4
+    Q = rng.standard_normal((16, 5)) * 0.9
+    K = rng.standard_normal((T, 5))
+    V = rng.standard_normal((T, 3))
+    ref = _greedy_by_brute_force(Q, K, t)
+    r = orc.compact_omp(Q, K, V, t)
+    assert list(r["order"]) == ref
+    assert list(r["idx"]) == sorted(ref)

@@ -28,7 +28,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
-PEAK_F32_TFLOPS = 157.3      # MI355X fp32 (vector and MFMA)
+PEAK_F32_TFLOPS = 157.3      # MI355X fp32 MFMA (and packed-fp32 vector)
+PEAK_F32_VALU_TFLOPS = 78.6  # fp32 vector FMA without packed ops: 256 CU x 64 lanes x 2 x 2.4 GHz
 PEAK_F64_TFLOPS = 78.6       # MI355X fp64 (vector and matrix)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_nnls_sweep_T32k_50x_hbm_traffic.md")
@@ -41,8 +42,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, help="synthetic workload (1-5)")
-    ap.add_argument("--cpu-heads", type=int, default=3,
-                    help="heads of the workload the CPU oracle times")
+    ap.add_argument("--cpu-budget", type=float, default=20.0,
+                    help="seconds of CPU oracle work: heads are timed in order until this is "
+                         "spent (at least one, at most all)")
+    ap.add_argument("--prof-steps", type=int, default=3,
+                    help="calls of the separate instrumented pass (per-kernel times)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--variant", default="compact",
@@ -56,8 +60,9 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(w, data, heads, one_head=None):
-    """The oracle as it stands, on `heads` heads of the same workload.
+def cpu_baseline(w, data, budget_s, one_head=None):
+    """The oracle as it stands, head after head of the same workload until
+    budget_s seconds are spent (at least one head, at most all of them).
     one_head(orc, h, Q, K, V) runs the oracle's form of the benchmarked call on
     head h (default: compact at budget t)."""
     import oracle as orc
@@ -68,17 +73,20 @@ def cpu_baseline(w, data, heads, one_head=None):
     except Exception:
         cores = os.cpu_count()
     t0 = time.perf_counter()
-    for h in range(heads):
-        Q, K, V = (synth.to_f64(data[k][h]) for k in ("Q", "K", "V"))
+    heads = 0
+    while heads < w.B and (heads == 0 or time.perf_counter() - t0 < budget_s):
+        Q, K, V = (synth.to_f64(data[k][heads]) for k in ("Q", "K", "V"))
         if one_head is None:
             orc.compact(Q, K, V, w.t)
         else:
-            one_head(orc, h, Q, K, V)
+            one_head(orc, heads, Q, K, V)
+        heads += 1
     dt = time.perf_counter() - t0
     return {"value": heads * w.T / dt, "unit": "KV tokens/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"{heads} of {w.B} heads of {w.name} through the float64 oracle "
-                      f"({dt:.1f} s; BLAS threads={cores}, numpy exp single-threaded)"}
+            "sample": f"{heads} of {w.B} heads of {w.name} through the float64 oracle, in order "
+                      f"until {budget_s:.0f} s were spent ({dt:.1f} s; BLAS threads={cores}, "
+                      f"numpy exp single-threaded)"}
 
 
 def copy_probe(torch, nbytes=1 << 30, reps=10):
@@ -146,8 +154,10 @@ def bench_attend(args, torch, kvc, w, data, dev):
         "config": {"workload": w.name, "variant": "attend", "B": w.B, "m": m, "T": w.T,
                    "appended": f, "d": w.d},
         "roofline": {"bound": "alu", "kernel": "k_attend", "achieved": round(ach, 3),
-                     "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / PEAK_F32_TFLOPS, 5), "traffic": None}}), flush=True)
+                     "peak": PEAK_F32_VALU_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_F32_VALU_TFLOPS, 5), "traffic": None,
+                     "peak_note": "fp32 vector FMA, packed fp32 ops off in this build"}}),
+          flush=True)
 
 
 def main():
@@ -233,78 +243,98 @@ def main():
         res = call()
     torch.cuda.synchronize()
 
-    stages = list(_lib.STAGES)
-    if not args.no_profile:
-        _lib.profile_enable(stages)
+    # timed region: the calls alone (no instrumentation)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         res = call()
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / args.steps
+
+    # a separate instrumented pass: HIP event pairs on the library's stream
+    # around each kernel stage
+    stages = list(_lib.STAGES)
     prof = {}
-    if not args.no_profile:
+    if not args.no_profile and args.prof_steps > 0:
+        _lib.profile_enable(stages)
+        for _ in range(args.prof_steps):
+            res = call()
+        torch.cuda.synchronize()
         for s in stages:
             ms, cnt = _lib.profile_read(s)
-            prof[s] = ms / max(cnt, 1)
+            if cnt:
+                prof[s] = ms / cnt
         _lib.profile_enable([])
 
     copy_gbs = copy_probe(torch)
     status = res.status.cpu().numpy()
-    # quality on held-out queries (head 0): full vs compacted attention, float64
-    import oracle as orc
-    h = 0
-    Kf = synth.to_f64(data["K"][h])
-    Vf = synth.to_f64(data["V"][h])
-    Qh = synth.to_f64(data["Qhold"][h])
-    full = orc.attend(Qh, Kf, Vf)
-    ih = res.idx[h].cpu().numpy()
-    live = ih >= 0
-    comp = orc.attend(Qh, Kf[ih[live]], res.values[h].cpu().numpy()[live],
-                      res.bias[h].cpu().numpy()[live])
-    evict = orc.attend(Qh, Kf[ih[live]], Vf[ih[live]])
-
     B, T, n, d = w.B, w.T, w.n, w.d
+    es = 2 if w.dtype == "bf16" else 4
+    # per-entry shapes of the batched call (a chunked call runs B*C entries of
+    # T/C keys, t/C kept each)
+    Be, Te, te = B, T, w.t
+    if args.variant == "chunked":
+        Be, Te, te = B * args.chunks, T // args.chunks, w.t // args.chunks
+    elif args.variant == "ragged":
+        te = max(variant["budgets"])
+    nqb = -(-n // 128)
     mm_peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     inter = kvc.intermediates(res)
-    fit_flops = inter["fit_flops"].cpu().numpy().sum(axis=0)  # [nnls, value] over heads
-    # algorithmic work per launch of each separately timed kernel:
-    #   k_score_lse: S = Q K^T once (2 n T d per head)
-    #   k_expweight: S recomputed + P V (4 n T d per head)
-    #   k_nnls_sweep: the block sweeps of the pivoting rounds (counted on device:
-    #     k pivots on an order-m system cost k m^2 + 2 m k^2 + k^3)
-    #   value stage: the value sweep's count over the stage (Grams and prep included
-    #     in the time, not in the count)
-    work = {"score_lse": ("k_score_lse", 2.0 * n * T * d * B, mm_peak),
-            "expweight": ("k_expweight", 4.0 * n * T * d * B, mm_peak),
-            "nnls": ("k_nnls_sweep", float(fit_flops[0]), PEAK_F64_TFLOPS),
-            "value": ("value stage (k_value_sweep)", float(fit_flops[1]), PEAK_F64_TFLOPS)}
+    fit_flops = inter["fit_flops"].cpu().numpy().sum(axis=0)  # [nnls, value] over entries
+    wv = inter["w"].cpu().numpy()
+    m_pass = (wv > 0).sum(axis=1)                           # value-system order per entry
+    # algorithmic work per launch of each separately timed kernel (formulas and
+    # units in the design notes):
+    #   k_score_lse    2 n T d per entry (S = Q K^T once)
+    #   k_expweight    4 n T d per entry (S recomputed + P V)
+    #   k_imp_reduce   reads the ceil(n/128) partials of every key, writes imp: 4 T (nqb + 1) B
+    #   k_select       reads imp once, writes idx: 4 T B + 4 t B
+    #   k_gather_rows  reads and writes the kept K rows: 2 t d es B
+    #   Grams          n t^2 per entry (symmetric half; value Gram: n m^2, m passive)
+    #   k_nnls_sweep   the block sweeps of the pivoting rounds (counted on device)
+    #   k_value_sweep  the value system's block sweeps (counted on device)
+    work = {"score_lse": ("k_score_lse", 2.0 * n * Te * d * Be, mm_peak, "mfma"),
+            "expweight": ("k_expweight", 4.0 * n * Te * d * Be, mm_peak, "mfma"),
+            "imp_reduce": ("k_imp_reduce", 4.0 * Te * (nqb + 1) * Be, PEAK_HBM_GBS, "hbm"),
+            "topt": ("k_select", 4.0 * (Te + te) * Be, PEAK_HBM_GBS, "hbm"),
+            "gather": ("k_gather_rows", 2.0 * te * d * es * Be, PEAK_HBM_GBS, "hbm"),
+            "gram": ("k_atb (mass Gram)", float(n) * te * te * Be, PEAK_F64_TFLOPS, "mfma"),
+            "value_gram": ("k_atb (value Gram)", float(n * (m_pass.astype(float) ** 2).sum()),
+                           PEAK_F64_TFLOPS, "mfma"),
+            "nnls": ("k_nnls_sweep", float(fit_flops[0]), PEAK_F64_TFLOPS, "mfma"),
+            "value_sweep": ("k_value_sweep", float(fit_flops[1]), PEAK_F64_TFLOPS, "mfma")}
     if args.variant == "omp":
         # the pursuit's t correlation passes read P (n T float32 per head) once
         # each, plus P's write and the norms pass: HBM-bound by design
         work["select"] = ("omp selection (k_ps<float>, k_omp_*)",
-                          float((w.t + 2) * n * T * 4 * B), PEAK_HBM_GBS)
+                          float((w.t + 2) * n * T * 4 * B), PEAK_HBM_GBS, "hbm")
     kernels = []
-    for stage, (kname, flops, peak) in work.items():
-        if stage not in prof:
+    for stage, (kname, amount, peak, bound) in work.items():
+        if stage not in prof or amount <= 0:
             continue
-        hbm = peak == PEAK_HBM_GBS
-        ach = flops / (prof[stage] * 1e-3) / (1e9 if hbm else 1e12)
-        kernels.append({"kernel": kname, "bound": "hbm" if hbm else "mfma",
-                        "ms": round(prof[stage], 4), "achieved": round(ach, 3), "peak": peak,
-                        "unit": "GB/s" if hbm else "TFLOP/s", "frac": round(ach / peak, 5)})
+        hbm = bound == "hbm"
+        ach = amount / (prof[stage] * 1e-3) / (1e9 if hbm else 1e12)
+        k = {"kernel": kname, "bound": bound, "ms": round(prof[stage], 4),
+             "achieved": round(ach, 3), "peak": peak, "unit": "GB/s" if hbm else "TFLOP/s",
+             "frac": round(ach / peak, 5), "work": amount}
+        if kname in ("k_nnls_sweep", "k_value_sweep"):
+            k["limited_by"] = "latency of the chain of dependent block steps"
+        kernels.append(k)
     roof = None
     if kernels:
-        dom = max((k for k in kernels if k["kernel"].startswith("k_") or k["bound"] == "hbm"),
-                  key=lambda k: k["ms"])
+        dom = max((k for k in kernels if k["kernel"].startswith("k_") and " " not in k["kernel"]
+                   or k["bound"] == "hbm"), key=lambda k: k["ms"])
         tr = (traffic_record() if (dom["kernel"] == "k_nnls_sweep" and args.config == 3 and
                                    args.variant == "compact") else None)
         roof = {"bound": dom["bound"], "kernel": dom["kernel"], "achieved": dom["achieved"],
                 "peak": dom["peak"], "unit": dom["unit"], "frac": dom["frac"],
                 "traffic": tr["bytes_per_launch"] if tr else None,
                 "traffic_detail": tr,
+                **({"limited_by": dom["limited_by"]} if "limited_by" in dom else {}),
                 "kernels": kernels, "stage_ms": {k: round(v, 4) for k, v in prof.items()},
                 "hbm_copy_measured_GBs": round(copy_gbs, 1), "hbm_peak_GBs": PEAK_HBM_GBS}
+
+    quality = diagnostics(w, data, res, inter, args.variant, B, status)
     out = {
         "metric": "KV tokens compacted/sec (1 GPU) at T=32k, 50x; compacted-attn rel. L2 error",
         "value": B * T / dt,
@@ -315,14 +345,71 @@ def main():
         "dtype": w.dtype, "data": "synthetic",
         "config": {**variant, "B": B, "T": T, "n": n, "d": d, "t": w.t,
                    "ratio": T / w.t},
-        "quality": {"heldout_rel_l2": orc.rel_l2(comp, full),
-                    "eviction_only_rel_l2": orc.rel_l2(evict, full),
-                    "status_nonzero_heads": int((status != 0).sum())},
+        "quality": quality,
         "roofline": roof,
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(w, data, min(args.cpu_heads, w.B), oracle_head)
+        out["cpu_baseline"] = cpu_baseline(w, data, args.cpu_budget, oracle_head)
     print(json.dumps(out), flush=True)
+
+
+def diagnostics(w, data, res, inter, variant, B, status, max_heads=8):
+    """Quality of the compacted cache on the first max_heads heads (float64 on
+    the host): the relative L2 error of the compacted attention output on
+    held-out queries (and of keeping the same keys without fitting), and, for
+    kvc_compact, on the reference queries themselves, the mass ratio r_i =
+    sum_{j kept} p_ij w_j per reference query (1 = exact mass), and the
+    condition numbers of the two regularised Grams."""
+    import oracle as orc
+    import synth
+    heads = list(range(min(B, max_heads)))
+    held, evict, qref, r_all, cond_m, cond_g = [], [], [], [], [], []
+    lse_all = inter["lse"].cpu().numpy() if variant == "compact" else None
+    O_all = inter["O"].cpu().numpy() if variant == "compact" else None
+    wv_all = inter["w"].cpu().numpy()
+    for h in heads:
+        Kf = synth.to_f64(data["K"][h])
+        Vf = synth.to_f64(data["V"][h])
+        Qh = synth.to_f64(data["Qhold"][h])
+        ih = res.idx[h].cpu().numpy()
+        live = ih >= 0
+        vals = res.values[h].float().cpu().numpy().astype(np.float64)[live]
+        bias = res.bias[h].cpu().numpy().astype(np.float64)[live]
+        Ck = Kf[ih[live]]
+        full = orc.attend(Qh, Kf, Vf)
+        held.append(orc.rel_l2(orc.attend(Qh, Ck, vals, bias), full))
+        evict.append(orc.rel_l2(orc.attend(Qh, Ck, Vf[ih[live]]), full))
+        if variant != "compact":
+            continue
+        Q = synth.to_f64(data["Q"][h])
+        qref.append(orc.rel_l2(orc.attend(Q, Ck, vals, bias), O_all[h].astype(np.float64)))
+        PS = np.exp(Q @ Ck.T - lse_all[h][:, None])
+        wh = wv_all[h]
+        r = PS @ wh
+        r_all.append(r)
+        M = PS.T @ PS
+        t = M.shape[0]
+        ev = np.linalg.eigvalsh(M + 1e-6 * np.trace(M) / t * np.eye(t))
+        cond_m.append(float(ev[-1] / ev[0]))
+        F = wh > 0
+        X = PS[:, F] * wh[F][None, :] / r[:, None]
+        G = X.T @ X
+        ev = np.linalg.eigvalsh(G + 1e-6 * np.trace(G) / t * np.eye(G.shape[0]))
+        cond_g.append(float(ev[-1] / ev[0]))
+    q = {"heads": len(heads), "of_heads": B,
+         "heldout_rel_l2": float(np.mean(held)), "heldout_rel_l2_max": float(np.max(held)),
+         "heldout_rel_l2_head0": held[0],
+         "eviction_only_rel_l2": float(np.mean(evict)),
+         "status_nonzero_heads": int((status != 0).sum())}
+    if qref:
+        r = np.concatenate(r_all)
+        pct = lambda x: [float(np.percentile(x, p)) for p in (0, 50, 90, 100)]
+        q.update({"qref_rel_l2": float(np.mean(qref)), "qref_rel_l2_max": float(np.max(qref)),
+                  "mass_ratio": {"min": float(r.min()), "mean": float(r.mean()),
+                                 "max": float(r.max())},
+                  "cond_mass_gram_p0_50_90_100": pct(cond_m),
+                  "cond_value_gram_p0_50_90_100": pct(cond_g)})
+    return q
 
 
 if __name__ == "__main__":

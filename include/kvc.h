@@ -22,17 +22,28 @@
  *      least-squares value fit given keys and bias).
  *   lam_w = ridge_rel * trace(P_S^T P_S) / t and lam_v = ridge_rel *
  *   trace(X^T X) / t: a vanishing ridge toward the prior (w = 1, C_v = V_S).
+ *   ridge_rel = 0 is the pipeline's literal NNLS and least squares; it needs
+ *   the Grams to be positive definite (n >= t, no duplicated kept keys).
  *
  * Conventions for every entry point below:
  *   - every array pointer is a DEVICE pointer to row-major, contiguous data,
- *     aligned to 16 bytes; the caller owns every buffer; the library keeps no
- *     state between calls and allocates no device memory in these calls;
+ *     aligned to 16 bytes; the caller owns every buffer; the library
+ *     allocates no device memory in these calls;
  *   - work is enqueued on `stream` and is asynchronous: outputs are valid once
  *     the stream has completed;
  *   - argument errors (KVC_EINVAL, KVC_EWORKSPACE, KVC_EUNSUPPORTED) are
  *     detected before anything is enqueued;
- *   - calls are reentrant across distinct workspaces; two calls that share a
- *     workspace must be ordered on one stream.
+ *   - the library keeps no state between calls (apart from the benchmark
+ *     instrumentation and the wait limit below), so calls with distinct
+ *     workspaces may be issued from several host threads; two calls that
+ *     share a workspace must be ordered on one stream;
+ *   - the fits run as cooperative launches (hipLaunchCooperativeKernel) whose
+ *     grid is sized to what the whole device holds at once; HIP guarantees
+ *     co-residency only within one such launch, so compactions that should
+ *     all succeed must not overlap in time on the device (issue them on one
+ *     stream, or synchronize between streams).  If they do overlap, a fit
+ *     team's wait may run out: every wait is bounded, so the call still ends,
+ *     and the affected heads report KVC_STATUS_SYNC_TIMEOUT.
  */
 #ifndef KVC_H_
 #define KVC_H_
@@ -53,9 +64,9 @@ extern "C" {
 
 /* Per-head numerical status written to out_status[b] (0 = ok). */
 #define KVC_STATUS_OK            0
-#define KVC_STATUS_NOT_SPD       1  /* a sweep pivot had the wrong sign (the
-                                       regularized Gram is not numerically
-                                       positive definite)                      */
+#define KVC_STATUS_NOT_SPD       1  /* a sweep pivot had the wrong sign or
+                                       vanished (the regularized Gram is not
+                                       numerically positive definite)          */
 #define KVC_STATUS_NNLS_CAP      2  /* NNLS stopped at max_nnls_iters           */
 #define KVC_STATUS_NONFINITE     4  /* a non-finite value reached the fits      */
 #define KVC_STATUS_SYNC_TIMEOUT  8  /* a fit team's barrier wait ran out (the
@@ -78,8 +89,12 @@ typedef struct {
   int32_t in_dtype;       /* kvc_dtype_t of Q_ref, K, V (out_K has the same)      */
   int32_t agg;            /* kvc_agg_t, default KVC_AGG_RMS                       */
   double  ridge_rel;      /* ridge weight relative to the Gram's mean diagonal,
-                             default 1e-6; must be > 0                            */
+                             default 1e-6; >= 0 (0: no ridge)                     */
   int32_t max_nnls_iters; /* cap on NNLS pivoting rounds, default 32              */
+  int32_t out_v_dtype;    /* kvc_dtype_t of out_V, default KVC_F32; KVC_BF16
+                             stores the float32 result rounded to nearest-even   */
+  int32_t refine_steps;   /* refinement steps of the value fit, default 0; must
+                             be 0 in this version                                 */
   int32_t reserved;       /* must be 0                                            */
 } kvc_params_t;
 
@@ -95,13 +110,13 @@ size_t kvc_workspace_bytes(const kvc_params_t* p);
  *   K, V    [B, T, d]  in_dtype   full cache (keys as stored, e.g. post-RoPE)
  *   out_K   [B, t, d]  in_dtype   kept keys: exact copies of K rows
  *   out_bias[B, t]     float32    beta, an additive logit bias per kept key
- *   out_V   [B, t, d]  float32    fitted values
+ *   out_V   [B, t, d]  out_v_dtype fitted values
  *   out_idx [B, t]     int32      kept indices, ascending; may be NULL
  *   out_status [B]     int32      per-head KVC_STATUS_* bits; may be NULL
  *   workspace          >= kvc_workspace_bytes(p) bytes of device memory
  * Returns KVC_OK once everything is enqueued, or a negative KVC_E* code. */
 int kvc_compact(const kvc_params_t* p, const void* Q_ref, const void* K, const void* V,
-                void* out_K, float* out_bias, float* out_V, int32_t* out_idx,
+                void* out_K, float* out_bias, void* out_V, int32_t* out_idx,
                 int32_t* out_status, void* workspace, size_t workspace_bytes,
                 hipStream_t stream);
 
@@ -110,7 +125,7 @@ int kvc_compact(const kvc_params_t* p, const void* Q_ref, const void* K, const v
  *   kvc_compact.  Used to check the fits in isolation and to re-fit a cache
  *   whose keys were chosen elsewhere. */
 int kvc_fit(const kvc_params_t* p, const void* Q_ref, const void* K, const void* V,
-            const int32_t* idx, float* out_bias, float* out_V, int32_t* out_status,
+            const int32_t* idx, float* out_bias, void* out_V, int32_t* out_status,
             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Ragged per-head budgets: head b keeps t_heads[b] keys, 1 <= t_heads[b] <=
@@ -128,7 +143,7 @@ int kvc_fit(const kvc_params_t* p, const void* Q_ref, const void* K, const void*
  *   workspace  >= kvc_workspace_bytes(p) bytes.
  * Returns as kvc_compact. */
 int kvc_compact_ragged(const kvc_params_t* p, const int32_t* t_heads, const void* Q_ref,
-                       const void* K, const void* V, void* out_K, float* out_bias, float* out_V,
+                       const void* K, const void* V, void* out_K, float* out_bias, void* out_V,
                        int32_t* out_idx, int32_t* out_status, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 
@@ -147,7 +162,7 @@ int kvc_compact_ragged(const kvc_params_t* p, const int32_t* t_heads, const void
  * Arguments and outputs as kvc_compact. */
 size_t kvc_workspace_bytes_omp(const kvc_params_t* p);
 int kvc_compact_omp(const kvc_params_t* p, const void* Q_ref, const void* K, const void* V,
-                    void* out_K, float* out_bias, float* out_V, int32_t* out_idx,
+                    void* out_K, float* out_bias, void* out_V, int32_t* out_idx,
                     int32_t* out_status, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
 
@@ -163,13 +178,13 @@ int kvc_compact_omp(const kvc_params_t* p, const void* Q_ref, const void* K, con
  *   protect_mask [B, T] uint8, DEVICE memory: nonzero marks a protected key.
  *   Outputs have kvc_compact's shapes.  Head b's slots [0, t - |P|) hold the
  *   fitted part (indices ascending), slots [t - |P|, t) the protected keys
- *   (ascending): out_K and out_V their K and V rows (V as float32),
- *   out_bias 0.
+ *   (ascending): out_K and out_V their K and V rows (V converted to
+ *   out_v_dtype), out_bias 0.
  *   workspace  >= kvc_workspace_bytes(p) bytes.
  * Returns as kvc_compact. */
 int kvc_compact_protected(const kvc_params_t* p, const uint8_t* protect_mask, const void* Q_ref,
                           const void* K, const void* V, void* out_K, float* out_bias,
-                          float* out_V, int32_t* out_idx, int32_t* out_status, void* workspace,
+                          void* out_V, int32_t* out_idx, int32_t* out_status, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
 /* Chunked compaction ("Compaction par blocs" of the same summary): each head's
@@ -188,7 +203,7 @@ int kvc_compact_protected(const kvc_params_t* p, const uint8_t* protect_mask, co
  *   K, V       [B, T, d]             in_dtype
  *   out_K      [B, n_chunks * t, d]  in_dtype   kept keys, chunk-major
  *   out_bias   [B, n_chunks * t]     float32
- *   out_V      [B, n_chunks * t, d]  float32
+ *   out_V      [B, n_chunks * t, d]  out_v_dtype
  *   out_idx    [B, n_chunks * t]     int32      positions in the head's cache
  *                                               (ascending); may be NULL
  *   out_status [B, n_chunks]         int32      KVC_STATUS_* per chunk; may be NULL
@@ -196,7 +211,7 @@ int kvc_compact_protected(const kvc_params_t* p, const uint8_t* protect_mask, co
  * Returns as kvc_compact; KVC_EINVAL also when T % n_chunks != 0. */
 size_t kvc_workspace_bytes_chunked(const kvc_params_t* p, int64_t n_chunks);
 int kvc_compact_chunked(const kvc_params_t* p, int64_t n_chunks, const void* Q_ref,
-                        const void* K, const void* V, void* out_K, float* out_bias, float* out_V,
+                        const void* K, const void* V, void* out_K, float* out_bias, void* out_V,
                         int32_t* out_idx, int32_t* out_status, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
 
@@ -248,20 +263,34 @@ int kvc_workspace_layout(const kvc_params_t* p, kvc_ws_layout_t* out);
 /* Instrumentation for benchmarks (not thread-safe; leave off in production).
  * While the stage mask is non-zero, every kvc_compact / kvc_fit call records a
  * HIP event pair on its stream around each selected stage; events are created
- * on first use and reused.  kvc_profile_enable() resets the counters;
- * kvc_profile_read() waits for the recorded events of one stage and returns
- * the summed elapsed time and the number of recorded launches. */
-#define KVC_STAGE_SCORE_LSE 0  /* scores + online log-sum-exp kernel          */
-#define KVC_STAGE_EXPWEIGHT 1  /* p = exp(s - lse), P V, importance kernel     */
-#define KVC_STAGE_SELECT    2  /* importance reduction, top-t select, gather  */
-#define KVC_STAGE_PS        3  /* kept-key softmax weights P_S (fp64)          */
-#define KVC_STAGE_GRAM      4  /* mass Gram P_S^T P_S (fp64 MFMA)              */
-#define KVC_STAGE_NNLS      5  /* pivoting rounds incl. their Cholesky solves  */
-#define KVC_STAGE_VALUE     6  /* value fit: Gram, right-hand side, solve      */
-#define KVC_STAGE_TOTAL     7  /* the whole call                               */
-#define KVC_NUM_STAGES      8
+ * on first use and reused.  kvc_profile_enable() resets the counters, and a
+ * zero mask also destroys the events; kvc_profile_read() waits for the
+ * recorded events of one stage and returns the summed elapsed time and the
+ * number of recorded launches. */
+#define KVC_STAGE_SCORE_LSE   0  /* scores + online log-sum-exp kernel           */
+#define KVC_STAGE_EXPWEIGHT   1  /* p = exp(s - lse), P V, importance kernel      */
+#define KVC_STAGE_SELECT      2  /* top-t select and gather (or the greedy pass) */
+#define KVC_STAGE_PS          3  /* kept-key softmax weights P_S (fp64)           */
+#define KVC_STAGE_GRAM        4  /* mass Gram P_S^T P_S (fp64 MFMA)               */
+#define KVC_STAGE_NNLS        5  /* pivoting rounds incl. their Cholesky solves   */
+#define KVC_STAGE_VALUE       6  /* value fit: Gram, right-hand side, solve       */
+#define KVC_STAGE_TOTAL       7  /* the whole call                                */
+#define KVC_STAGE_IMP_REDUCE  8  /* importance partials summed per key            */
+#define KVC_STAGE_TOPT        9  /* the top-t select kernel alone                 */
+#define KVC_STAGE_GATHER     10  /* kept-key row gather alone                     */
+#define KVC_STAGE_VALUE_GRAM 11  /* value Gram X_F^T X_F alone (fp64 MFMA)        */
+#define KVC_STAGE_VALUE_SWEEP 12 /* value system solve alone                      */
+#define KVC_NUM_STAGES       13
 int kvc_profile_enable(uint32_t stage_mask);
 int kvc_profile_read(int stage, double* total_ms, int64_t* launches);
+
+/* Upper bound on each wait of a fit team (in ticks of the 100 MHz constant
+ * clock; default 2e9, i.e. 20 s).  A wait that runs out turns the later waits
+ * of that launch into no-ops, so every kernel still ends, and flags
+ * KVC_STATUS_SYNC_TIMEOUT on the launch's heads, whose fits are then
+ * incomplete.  0 restores the default.  Applies to calls enqueued after it;
+ * process-wide and not thread-safe: meant for exercising the time-out path. */
+int kvc_set_wait_limit(uint64_t ticks);
 
 /* Static text for a KVC_* return code. */
 const char* kvc_strerror(int code);

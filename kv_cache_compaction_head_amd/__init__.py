@@ -12,12 +12,13 @@ import dataclasses
 
 from . import _lib
 from ._lib import (KVC_AGG_MEAN, KVC_AGG_RMS, KVC_BF16, KVC_F32, STATUS_NNLS_CAP,
-                   STATUS_NONFINITE, STATUS_NOT_SPD, Params, load, make_params, strerror,
-                   workspace_bytes, workspace_bytes_chunked, workspace_bytes_omp,
-                   workspace_layout)
+                   STATUS_NONFINITE, STATUS_NOT_SPD, STATUS_SYNC_TIMEOUT, Params, load,
+                   make_params, set_wait_limit, strerror, workspace_bytes,
+                   workspace_bytes_chunked, workspace_bytes_omp, workspace_layout)
 
 __all__ = ["compact", "compact_omp", "compact_chunked", "compact_ragged", "compact_protected", "attend", "fit", "Compacted", "intermediates", "load", "make_params",
-           "workspace_bytes", "workspace_bytes_chunked", "workspace_bytes_omp", "workspace_layout", "strerror", "Params"]
+           "workspace_bytes", "workspace_bytes_chunked", "workspace_bytes_omp", "workspace_layout", "strerror", "Params",
+           "set_wait_limit"]
 
 
 @dataclasses.dataclass
@@ -35,6 +36,17 @@ class Compacted:
 
 def _vp(x):
     return ctypes.c_void_p(x.data_ptr())
+
+
+def _vdt(out_v_dtype):
+    """Storage of the fitted values: float32 (default) or bfloat16 (the
+    float32 result rounded to nearest-even)."""
+    import torch
+    if out_v_dtype is None or out_v_dtype == torch.float32:
+        return "f32", torch.float32
+    if out_v_dtype == torch.bfloat16:
+        return "bf16", torch.bfloat16
+    raise ValueError("out_v_dtype must be torch.float32 or torch.bfloat16")
 
 
 def _prep(Q, K, V):
@@ -72,19 +84,20 @@ def _workspace(p, device, workspace, need=None):
 
 
 def compact(Q, K, V, t: int, *, agg: str = "rms", ridge_rel: float = 1e-6,
-            max_nnls_iters: int = 32, workspace=None, stream=None) -> Compacted:
+            max_nnls_iters: int = 32, out_v_dtype=None, workspace=None, stream=None) -> Compacted:
     """Compact each head's cache to t kept keys with fitted bias and values."""
     import torch
     Q, K, V, _ = _prep(Q, K, V)
     B, n, d = Q.shape
     T = K.shape[1]
     dt = "bf16" if Q.dtype == torch.bfloat16 else "f32"
-    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters)
+    vs, vt = _vdt(out_v_dtype)
+    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters, vs)
     dev = Q.device
     ws = _workspace(p, dev, workspace)
     keys = torch.empty((B, t, d), dtype=Q.dtype, device=dev)
     bias = torch.empty((B, t), dtype=torch.float32, device=dev)
-    values = torch.empty((B, t, d), dtype=torch.float32, device=dev)
+    values = torch.empty((B, t, d), dtype=vt, device=dev)
     idx = torch.empty((B, t), dtype=torch.int32, device=dev)
     status = torch.empty((B,), dtype=torch.int32, device=dev)
     rc = load().kvc_compact(ctypes.byref(p), _vp(Q), _vp(K), _vp(V), _vp(keys), _vp(bias),
@@ -95,7 +108,7 @@ def compact(Q, K, V, t: int, *, agg: str = "rms", ridge_rel: float = 1e-6,
 
 
 def compact_omp(Q, K, V, t: int, *, ridge_rel: float = 1e-6, max_nnls_iters: int = 32,
-                workspace=None, stream=None) -> Compacted:
+                out_v_dtype=None, workspace=None, stream=None) -> Compacted:
     """Compact each head to t keys chosen by orthogonal matching pursuit on
     the attention mass (t greedy steps), then the same bias and value fits as
     compact()."""
@@ -104,7 +117,8 @@ def compact_omp(Q, K, V, t: int, *, ridge_rel: float = 1e-6, max_nnls_iters: int
     B, n, d = Q.shape
     T = K.shape[1]
     dt = "bf16" if Q.dtype == torch.bfloat16 else "f32"
-    p = make_params(B, T, n, d, t, dt, "rms", ridge_rel, max_nnls_iters)
+    vs, vt = _vdt(out_v_dtype)
+    p = make_params(B, T, n, d, t, dt, "rms", ridge_rel, max_nnls_iters, vs)
     dev = Q.device
     need = workspace_bytes_omp(p)
     if need == 0:
@@ -112,7 +126,7 @@ def compact_omp(Q, K, V, t: int, *, ridge_rel: float = 1e-6, max_nnls_iters: int
     ws = _workspace(p, dev, workspace, need)
     keys = torch.empty((B, t, d), dtype=Q.dtype, device=dev)
     bias = torch.empty((B, t), dtype=torch.float32, device=dev)
-    values = torch.empty((B, t, d), dtype=torch.float32, device=dev)
+    values = torch.empty((B, t, d), dtype=vt, device=dev)
     idx = torch.empty((B, t), dtype=torch.int32, device=dev)
     status = torch.empty((B,), dtype=torch.int32, device=dev)
     rc = load().kvc_compact_omp(ctypes.byref(p), _vp(Q), _vp(K), _vp(V), _vp(keys), _vp(bias),
@@ -124,7 +138,7 @@ def compact_omp(Q, K, V, t: int, *, ridge_rel: float = 1e-6, max_nnls_iters: int
 
 
 def compact_ragged(Q, K, V, t_heads, *, agg: str = "rms", ridge_rel: float = 1e-6,
-                   max_nnls_iters: int = 32, workspace=None, stream=None) -> Compacted:
+                   max_nnls_iters: int = 32, out_v_dtype=None, workspace=None, stream=None) -> Compacted:
     """Compact head b to t_heads[b] keys (a per-head budget).  Outputs are
     padded to max(t_heads): head b's slots from t_heads[b] on hold idx -1,
     zero keys and values and bias -inf, which attention ignores."""
@@ -138,12 +152,13 @@ def compact_ragged(Q, K, V, t_heads, *, agg: str = "rms", ridge_rel: float = 1e-
     t = int(tv.max())
     tv = tv.to(Q.device).contiguous()
     dt = "bf16" if Q.dtype == torch.bfloat16 else "f32"
-    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters)
+    vs, vt = _vdt(out_v_dtype)
+    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters, vs)
     dev = Q.device
     ws = _workspace(p, dev, workspace)
     keys = torch.empty((B, t, d), dtype=Q.dtype, device=dev)
     bias = torch.empty((B, t), dtype=torch.float32, device=dev)
-    values = torch.empty((B, t, d), dtype=torch.float32, device=dev)
+    values = torch.empty((B, t, d), dtype=vt, device=dev)
     idx = torch.empty((B, t), dtype=torch.int32, device=dev)
     status = torch.empty((B,), dtype=torch.int32, device=dev)
     rc = load().kvc_compact_ragged(ctypes.byref(p), _vp(tv), _vp(Q), _vp(K), _vp(V), _vp(keys),
@@ -155,7 +170,7 @@ def compact_ragged(Q, K, V, t_heads, *, agg: str = "rms", ridge_rel: float = 1e-
 
 
 def compact_protected(Q, K, V, t: int, protect, *, agg: str = "rms", ridge_rel: float = 1e-6,
-                      max_nnls_iters: int = 32, workspace=None, stream=None) -> Compacted:
+                      max_nnls_iters: int = 32, out_v_dtype=None, workspace=None, stream=None) -> Compacted:
     """Keep the marked keys of protect [B, T] (bool/uint8) exactly with bias 0
     (at most t - 1 per head, the first by position) and compact the others
     into the remaining slots.  Head b's slots [0, t - p_b) hold the fitted
@@ -168,12 +183,13 @@ def compact_protected(Q, K, V, t: int, protect, *, agg: str = "rms", ridge_rel: 
         raise ValueError(f"protect must be [B, T] = [{B}, {T}]")
     m = protect.to(device=Q.device, dtype=torch.uint8).contiguous()
     dt = "bf16" if Q.dtype == torch.bfloat16 else "f32"
-    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters)
+    vs, vt = _vdt(out_v_dtype)
+    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters, vs)
     dev = Q.device
     ws = _workspace(p, dev, workspace)
     keys = torch.empty((B, t, d), dtype=Q.dtype, device=dev)
     bias = torch.empty((B, t), dtype=torch.float32, device=dev)
-    values = torch.empty((B, t, d), dtype=torch.float32, device=dev)
+    values = torch.empty((B, t, d), dtype=vt, device=dev)
     idx = torch.empty((B, t), dtype=torch.int32, device=dev)
     status = torch.empty((B,), dtype=torch.int32, device=dev)
     rc = load().kvc_compact_protected(ctypes.byref(p), _vp(m), _vp(Q), _vp(K), _vp(V), _vp(keys),
@@ -185,7 +201,7 @@ def compact_protected(Q, K, V, t: int, protect, *, agg: str = "rms", ridge_rel: 
 
 
 def compact_chunked(Q, K, V, t: int, n_chunks: int, *, agg: str = "rms",
-                    ridge_rel: float = 1e-6, max_nnls_iters: int = 32, workspace=None,
+                    ridge_rel: float = 1e-6, max_nnls_iters: int = 32, out_v_dtype=None, workspace=None,
                     stream=None) -> Compacted:
     """Cut each head's cache into n_chunks contiguous chunks, compact every chunk
     to t entries on its own, concatenate.  keys/bias/values/idx are
@@ -196,7 +212,8 @@ def compact_chunked(Q, K, V, t: int, n_chunks: int, *, agg: str = "rms",
     B, n, d = Q.shape
     T = K.shape[1]
     dt = "bf16" if Q.dtype == torch.bfloat16 else "f32"
-    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters)
+    vs, vt = _vdt(out_v_dtype)
+    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters, vs)
     dev = Q.device
     need = workspace_bytes_chunked(p, n_chunks)
     if need == 0:
@@ -205,7 +222,7 @@ def compact_chunked(Q, K, V, t: int, n_chunks: int, *, agg: str = "rms",
     m = n_chunks * t
     keys = torch.empty((B, m, d), dtype=Q.dtype, device=dev)
     bias = torch.empty((B, m), dtype=torch.float32, device=dev)
-    values = torch.empty((B, m, d), dtype=torch.float32, device=dev)
+    values = torch.empty((B, m, d), dtype=vt, device=dev)
     idx = torch.empty((B, m), dtype=torch.int32, device=dev)
     status = torch.empty((B, n_chunks), dtype=torch.int32, device=dev)
     rc = load().kvc_compact_chunked(ctypes.byref(p), ctypes.c_int64(n_chunks), _vp(Q), _vp(K),
@@ -215,12 +232,13 @@ def compact_chunked(Q, K, V, t: int, n_chunks: int, *, agg: str = "rms",
                                     _stream(stream, dev))
     _lib.check(rc)
     # intermediates() of this result index (head, chunk) entries b * n_chunks + c
-    pc = make_params(B * n_chunks, T // n_chunks, n, d, t, dt, agg, ridge_rel, max_nnls_iters)
+    pc = make_params(B * n_chunks, T // n_chunks, n, d, t, dt, agg, ridge_rel, max_nnls_iters,
+                     vs)
     return Compacted(keys, bias, values, idx, status, ws, pc)
 
 
 def fit(Q, K, V, idx, *, ridge_rel: float = 1e-6, max_nnls_iters: int = 32,
-        workspace=None, stream=None) -> Compacted:
+        out_v_dtype=None, workspace=None, stream=None) -> Compacted:
     """Bias and value fit for a given kept set idx [B, t] (int32, ascending)."""
     import torch
     Q, K, V, _ = _prep(Q, K, V)
@@ -230,11 +248,12 @@ def fit(Q, K, V, idx, *, ridge_rel: float = 1e-6, max_nnls_iters: int = 32,
     B, n, d = Q.shape
     T, t = K.shape[1], idx.shape[1]
     dt = "bf16" if Q.dtype == torch.bfloat16 else "f32"
-    p = make_params(B, T, n, d, t, dt, "rms", ridge_rel, max_nnls_iters)
+    vs, vt = _vdt(out_v_dtype)
+    p = make_params(B, T, n, d, t, dt, "rms", ridge_rel, max_nnls_iters, vs)
     dev = Q.device
     ws = _workspace(p, dev, workspace)
     bias = torch.empty((B, t), dtype=torch.float32, device=dev)
-    values = torch.empty((B, t, d), dtype=torch.float32, device=dev)
+    values = torch.empty((B, t, d), dtype=vt, device=dev)
     status = torch.empty((B,), dtype=torch.int32, device=dev)
     rc = load().kvc_fit(ctypes.byref(p), _vp(Q), _vp(K), _vp(V), _vp(idx), _vp(bias),
                         _vp(values), _vp(status), _vp(ws),

@@ -19,16 +19,19 @@ EXPORTS = ("kvc_params_default", "kvc_workspace_bytes", "kvc_compact", "kvc_fit"
            "kvc_workspace_bytes_chunked", "kvc_compact_chunked", "kvc_compact_ragged",
            "kvc_compact_protected", "kvc_attend", "kvc_attend_workspace_bytes", "kvc_workspace_bytes_omp",
            "kvc_compact_omp",
-           "kvc_workspace_layout", "kvc_profile_enable", "kvc_profile_read", "kvc_strerror")
+           "kvc_workspace_layout", "kvc_profile_enable", "kvc_profile_read", "kvc_set_wait_limit",
+           "kvc_strerror")
 STAGES = {"score_lse": 0, "expweight": 1, "select": 2, "ps": 3, "gram": 4, "nnls": 5,
-          "value": 6, "total": 7}
+          "value": 6, "total": 7, "imp_reduce": 8, "topt": 9, "gather": 10, "value_gram": 11,
+          "value_sweep": 12}
 
 
 class Params(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("n", ctypes.c_int64),
                 ("d", ctypes.c_int64), ("t", ctypes.c_int64), ("in_dtype", ctypes.c_int32),
                 ("agg", ctypes.c_int32), ("ridge_rel", ctypes.c_double),
-                ("max_nnls_iters", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("max_nnls_iters", ctypes.c_int32), ("out_v_dtype", ctypes.c_int32),
+                ("refine_steps", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class AttendParams(ctypes.Structure):
@@ -94,13 +97,16 @@ def load() -> ctypes.CDLL:
     lib.kvc_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_int64)]
     lib.kvc_profile_read.restype = ctypes.c_int
+    lib.kvc_set_wait_limit.argtypes = [ctypes.c_uint64]
+    lib.kvc_set_wait_limit.restype = ctypes.c_int
     lib.kvc_strerror.argtypes = [ctypes.c_int]
     lib.kvc_strerror.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
 
-def make_params(B, T, n, d, t, dtype, agg="rms", ridge_rel=1e-6, max_nnls_iters=32) -> Params:
+def make_params(B, T, n, d, t, dtype, agg="rms", ridge_rel=1e-6, max_nnls_iters=32,
+                out_v_dtype="f32") -> Params:
     p = Params()
     load().kvc_params_default(ctypes.byref(p))
     p.B, p.T, p.n, p.d, p.t = int(B), int(T), int(n), int(d), int(t)
@@ -108,7 +114,13 @@ def make_params(B, T, n, d, t, dtype, agg="rms", ridge_rel=1e-6, max_nnls_iters=
     p.agg = {"rms": KVC_AGG_RMS, "mean": KVC_AGG_MEAN}[agg]
     p.ridge_rel = float(ridge_rel)
     p.max_nnls_iters = int(max_nnls_iters)
+    p.out_v_dtype = {"bf16": KVC_BF16, "f32": KVC_F32}[out_v_dtype]
     return p
+
+
+def set_wait_limit(ticks: int) -> None:
+    """Bound on each fit-team wait, in 100 MHz ticks (0: the 20 s default)."""
+    check(load().kvc_set_wait_limit(int(ticks)))
 
 
 def workspace_bytes(p: Params) -> int:

@@ -26,6 +26,20 @@ template <class In> __device__ __forceinline__ double to_f64(In v) {
   return static_cast<double>(to_f32<In>(v));
 }
 
+// float32 -> bfloat16 bit pattern, rounded to nearest, ties to even (a NaN
+// stays a quiet NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// Store a fitted value as float32 or as its bfloat16 rounding.
+template <class OutT> __device__ __forceinline__ OutT from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16_rne(v); }
+
 // Output layout of a 32x32 MFMA accumulator (16 floats per lane): element r of
 // lane l sits at row 8*(r/4) + 4*(l/32) + (r%4), column l%32.
 __device__ __forceinline__ int mfma32_row(int r, int lane) {

@@ -452,12 +452,12 @@ __global__ __launch_bounds__(1024) void k_bias_prep(double* __restrict__ S, size
 // few control words (sizes, tolerances, pivoting state) are always read and
 // written with agent-scope atomics.
 //
-// Every wait is bounded by the constant-rate wall clock; a wait that runs out
-// raises a flag that turns every later wait into a no-op and flags the heads,
-// so no workgroup can spin forever.
+// Every wait is bounded by the constant-rate wall clock (the bound is a kernel
+// argument, 20 s unless the host sets another); a wait that runs out raises a
+// flag that turns every later wait into a no-op and flags the heads, so no
+// workgroup can spin forever.
 // ---------------------------------------------------------------------------
-constexpr uint64_t kSpinTicks = 2000000000ull;  // 20 s at the 100 MHz wall clock
-constexpr int kXcds = 8;                        // round-robin dispatch period
+constexpr int kXcds = 8;  // round-robin dispatch period
 
 // bulk data: ordinary accesses (made coherent by team_sync)
 __device__ __forceinline__ double ldc(const double* p) { return *p; }
@@ -490,6 +490,7 @@ struct Team {
   unsigned gen;
   int* err;
   bool fast;
+  uint64_t spin;  // bound on each wait, in ticks of the 100 MHz wall clock
 };
 
 __device__ __forceinline__ int hw_xcc_id() {
@@ -531,15 +532,16 @@ __device__ __forceinline__ void team_wait(Team& tm) {
         in &= __hip_atomic_load(tm.flag0 + static_cast<size_t>(r) * tm.fstride, __ATOMIC_RELAXED,
                                 __HIP_MEMORY_SCOPE_AGENT) >= target;
       if (__all(in)) break;
-      // the time-out and the error flag every 32 polls: each is another round
-      // trip that would otherwise delay seeing the last arrival
-      if ((++spins & 31u) == 0) {
-        if (__hip_atomic_load(tm.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
-        if (wall_clock64() - t0 > kSpinTicks) {
-          if (lane == 0) atomicOr(tm.err, 1);
-          break;
-        }
+      // the time-out on every poll (a scalar clock read); the error flag every
+      // 32 polls: it is another memory round trip that would otherwise delay
+      // seeing the last arrival
+      if (wall_clock64() - t0 > tm.spin) {
+        if (lane == 0) atomicOr(tm.err, 1);
+        break;
       }
+      if ((++spins & 31u) == 0 &&
+          __hip_atomic_load(tm.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        break;
       __builtin_amdgcn_s_sleep(1);
     }
     if (lane == 0) {
@@ -576,6 +578,8 @@ __device__ __forceinline__ Team uniform_team(const Team& t) {
   u.gen = __builtin_amdgcn_readfirstlane(t.gen);
   u.err = reinterpret_cast<int*>(uniform(reinterpret_cast<unsigned*>(t.err)));
   u.fast = __builtin_amdgcn_readfirstlane(static_cast<int>(t.fast)) != 0;
+  u.spin = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(t.spin >> 32))) << 32) |
+           __builtin_amdgcn_readfirstlane(static_cast<unsigned>(t.spin));
   return u;
 }
 
@@ -594,7 +598,7 @@ __device__ __forceinline__ unsigned ticket_value(unsigned drawn) {
 // Team of this workgroup from the XCD-aligned mapping, then one agent-fenced
 // barrier to compare the members' XCC ids (fast barrier if they all match).
 __device__ void team_setup(Team& tm, int& team, int& nteams, unsigned* bar, int* err, int* xcc,
-                           int tx) {
+                           int tx, uint64_t spin) {
   nteams = kXcds * tx;
   team = static_cast<int>(blockIdx.x % nteams);
   tm.rank = static_cast<int>(blockIdx.x / nteams);
@@ -609,6 +613,7 @@ __device__ void team_setup(Team& tm, int& team, int& nteams, unsigned* bar, int*
   tm.gen = 0;
   tm.err = err;
   tm.fast = false;
+  tm.spin = spin;
   if (tm.size == 1) return;
   __shared__ int s_ok;
   if (threadIdx.x == 0) sta(&xcc[blockIdx.x], hw_xcc_id());
@@ -1549,13 +1554,13 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& team_ref, in
       const uint64_t t0 = wall_clock64();
       unsigned spins = 0;
       while (__hip_atomic_load(tm.ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < tm.pubs + 1) {
-        if ((++spins & 31u) == 0) {
-          if (__hip_atomic_load(tm.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
-          if (wall_clock64() - t0 > kSpinTicks) {
-            atomicOr(tm.err, 1);
-            break;
-          }
+        if (wall_clock64() - t0 > tm.spin) {
+          atomicOr(tm.err, 1);
+          break;
         }
+        if ((++spins & 31u) == 0 &&
+            __hip_atomic_load(tm.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+          break;
         __builtin_amdgcn_s_sleep(1);
       }
     }
@@ -1608,11 +1613,11 @@ __global__ __launch_bounds__(256) void k_nnls_sweep(
     int32_t* __restrict__ inv,
     int32_t* __restrict__ msz, int32_t* __restrict__ status, unsigned* __restrict__ bar,
     int* __restrict__ err, int* __restrict__ xcc, double* __restrict__ flops,
-    const int32_t* __restrict__ tv, int B, int t_str, int max_iters, int tx) {
+    const int32_t* __restrict__ tv, int B, int t_str, int max_iters, int tx, uint64_t spin) {
   SweepSmem& sm = g_sw;
   Team tm;
   int team, nteams;
-  team_setup(tm, team, nteams, bar, err, xcc, tx);
+  team_setup(tm, team, nteams, bar, err, xcc, tx, spin);
   const int tid = threadIdx.x;
   for (int s = tid; s < kMaxRows; s += kTeamThreads) sm.pos[s] = -1;
   constexpr int NV = kMaxTeamT / kTeamThreads;
@@ -1751,11 +1756,11 @@ __global__ __launch_bounds__(256) void k_value_sweep(
     double* __restrict__ S, size_t sS, int ld, int r_al, double* __restrict__ Ub,
     double* __restrict__ Vb, size_t sUV, double* __restrict__ stage, const int32_t* __restrict__ msz,
     int32_t* __restrict__ status, unsigned* __restrict__ bar, int* __restrict__ err,
-    int* __restrict__ xcc, double* __restrict__ flops, int B, int D, int tx) {
+    int* __restrict__ xcc, double* __restrict__ flops, int B, int D, int tx, uint64_t spin) {
   SweepSmem& sm = g_sw;
   Team tm;
   int team, nteams;
-  team_setup(tm, team, nteams, bar, err, xcc, tx);
+  team_setup(tm, team, nteams, bar, err, xcc, tx, spin);
   const int tid = threadIdx.x;
   for (int s = tid; s < kMaxRows; s += kTeamThreads) sm.pos[s] = -1;
   for (int b = team; b < B; b += nteams) {
@@ -1861,13 +1866,14 @@ __global__ void k_rhs_ridge(double* __restrict__ Rb, size_t sS, int ld, const In
 }
 
 // out_V[b][a][c] = fitted value (row inv[a] of C at Cb, stride ld) for passive
-// keys, the V row (the prior) for keys whose multiplier is zero;
-// out_bias = log(max(w, 1e-30)).  grid (ceil(t*D/256), B).
-template <class In>
+// keys, the V row (the prior) for keys whose multiplier is zero, as float32 or
+// as the bfloat16 rounding of that float32 value; out_bias = log(max(w,
+// 1e-30)).  grid (ceil(t*D/256), B).
+template <class In, class OutT>
 __global__ void k_write_out(const double* __restrict__ Cb, size_t sS, int ld,
                             const In* __restrict__ V, const int32_t* __restrict__ idx,
                             const int32_t* __restrict__ inv, const double* __restrict__ wv,
-                            float* __restrict__ out_V, float* __restrict__ out_bias, int T, int t,
+                            OutT* __restrict__ out_V, float* __restrict__ out_bias, int T, int t,
                             int D) {
   const int b = blockIdx.y;
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
@@ -1878,7 +1884,7 @@ __global__ void k_write_out(const double* __restrict__ Cb, size_t sS, int ld,
   float v = 0.f;
   if (p >= 0) v = static_cast<float>(Cb[b * sS + static_cast<size_t>(p) * ld + c]);
   else if (j >= 0) v = to_f32<In>(V[(static_cast<size_t>(b) * T + j) * D + c]);
-  out_V[(static_cast<size_t>(b) * t + a) * D + c] = v;
+  out_V[(static_cast<size_t>(b) * t + a) * D + c] = from_f32<OutT>(v);
   if (c == 0)
     out_bias[static_cast<size_t>(b) * t + a] =
         j >= 0 ? static_cast<float>(log(fmax(wv[static_cast<size_t>(b) * t + a], 1e-30)))
@@ -1957,8 +1963,8 @@ int sweep_ld(int t, int D) {
 template <class In, int D>
 hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const double* lse,
                       const float* O, const int32_t* idx, FitBufs fb, float* out_bias,
-                      float* out_V, int32_t* status, int B, int n, int T, int t, double ridge,
-                      int max_iters, int qg, hipStream_t st) {
+                      void* out_V, bool v_bf16, int32_t* status, int B, int n, int T, int t,
+                      double ridge, int max_iters, int qg, hipStream_t st) {
   const In* Q = static_cast<const In*>(Qv);
   const In* K = static_cast<const In*>(Kv);
   const In* V = static_cast<const In*>(Vv);
@@ -1997,7 +2003,7 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
   {
     void* args[] = {&fb.S,   &sS,      &ld,        &fb.U,   &fb.V,  &sUV,     &fb.stage, &fb.wv,
                     &fb.Fidx, &fb.inv, &fb.msz,    &status, &fb.bar, &err,    &fb.xcc,
-                    &fb.flops, &tvp,   &B,        &t,         &max_iters, &tx};
+                    &fb.flops, &tvp,   &B,        &t,         &max_iters, &tx, &fb.wait_ticks};
     e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_nnls_sweep), dim3(grid),
                                    dim3(kTeamThreads), args, 0, st);
     if (e != hipSuccess) return e;
@@ -2008,8 +2014,10 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
   hipLaunchKernelGGL(k_value_prep, dim3(n, B), dim3(256), 0, st, fb.PS, fb.wv, fb.inv, n, t);
   double* G0 = fb.S + static_cast<size_t>(rv) * ld + rv;
   double* R0 = fb.S + static_cast<size_t>(rv) * ld;
+  prof_mark(11, false, st);
   launch_atb<double, true>(fb.PS, sPS, t, nullptr, 0, fb.PS, sPS, t, G0, sS, ld, n, fb.msz, t, t,
                            fb.part, fb.part_cap, B, st);
+  prof_mark(11, true, st);
   hipLaunchKernelGGL(k_ridge_v, dim3(B), dim3(256), 0, st, G0, sS, ld, fb.msz, fb.lam, fb.tv, t,
                      ridge);
   launch_atb<float, false>(fb.PS, sPS, t, nullptr, 0, O, static_cast<size_t>(n) * D, D, R0, sS, ld,
@@ -2022,17 +2030,25 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
   grid = team_shape(B, nvb * nrb + nvb * (nvb + 1) / 2, cap, tx);
   e = launch_fill_i32(reinterpret_cast<int32_t*>(fb.bar), 0, kBarWords, st);
   if (e != hipSuccess) return e;
+  prof_mark(12, false, st);
   {
     int r_al = rv, Dv = D;
     const int32_t* ms = fb.msz;
     void* args[] = {&fb.S, &sS,     &ld,  &r_al, &fb.U,     &fb.V, &sUV, &fb.stage, &ms,
-                    &status, &fb.bar, &err, &fb.xcc, &fb.flops, &B,    &Dv,  &tx};
+                    &status, &fb.bar, &err, &fb.xcc, &fb.flops, &B,    &Dv,  &tx, &fb.wait_ticks};
     e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_value_sweep), dim3(grid),
                                    dim3(kTeamThreads), args, 0, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_write_out<In>), dim3((t * D + 255) / 256, B), dim3(256), 0, st, R0, sS,
-                     ld, V, idx, fb.inv, fb.wv, out_V, out_bias, T, t, D);
+  prof_mark(12, true, st);
+  if (v_bf16)
+    hipLaunchKernelGGL((k_write_out<In, bf16_t>), dim3((t * D + 255) / 256, B), dim3(256), 0, st,
+                       R0, sS, ld, V, idx, fb.inv, fb.wv, static_cast<bf16_t*>(out_V), out_bias, T,
+                       t, D);
+  else
+    hipLaunchKernelGGL((k_write_out<In, float>), dim3((t * D + 255) / 256, B), dim3(256), 0, st,
+                       R0, sS, ld, V, idx, fb.inv, fb.wv, static_cast<float*>(out_V), out_bias, T,
+                       t, D);
   prof_mark(6, true, st);
   return hipGetLastError();
 }
@@ -2050,8 +2066,8 @@ hipError_t launch_probs_all(const void* Q, const void* K, const double* lse, flo
 
 #define KVC_INST_FIT(In, D)                                                                   \
   template hipError_t launch_fit<In, D>(const void*, const void*, const void*, const double*, \
-                                        const float*, const int32_t*, FitBufs, float*, float*, \
-                                        int32_t*, int, int, int, int, double, int, int,      \
+                                        const float*, const int32_t*, FitBufs, float*, void*,  \
+                                        bool, int32_t*, int, int, int, int, double, int, int, \
                                         hipStream_t);
 #define KVC_INST_PROBS(In, D)                                                          \
   template hipError_t launch_probs_all<In, D>(const void*, const void*, const double*, \

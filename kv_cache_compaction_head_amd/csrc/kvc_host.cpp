@@ -26,6 +26,10 @@ struct ProfState {
 };
 ProfState g_prof;
 
+// bound on each wait of a fit team (100 MHz ticks); kvc_set_wait_limit
+constexpr uint64_t kDefaultWaitTicks = 2000000000ull;
+uint64_t g_wait_ticks = kDefaultWaitTicks;
+
 }  // namespace
 
 namespace kvc {
@@ -163,8 +167,10 @@ bool params_ok(const kvc_params_t* p) {
   if (p->t < 1 || p->t > p->T || p->t > kMaxT_keep) return false;
   if (p->in_dtype != KVC_F32 && p->in_dtype != KVC_BF16) return false;
   if (p->agg != KVC_AGG_RMS && p->agg != KVC_AGG_MEAN) return false;
-  if (!(p->ridge_rel > 0.0) || !std::isfinite(p->ridge_rel)) return false;
+  if (!(p->ridge_rel >= 0.0) || !std::isfinite(p->ridge_rel)) return false;
   if (p->max_nnls_iters < 1 || p->max_nnls_iters > 1000) return false;
+  if (p->out_v_dtype != KVC_F32 && p->out_v_dtype != KVC_BF16) return false;
+  if (p->refine_steps != 0) return false;
   if (p->reserved != 0) return false;
   return true;
 }
@@ -215,12 +221,13 @@ hipError_t run_score(const kvc_params_t* p, const void* Q, const void* K, const 
 
 template <class In, int D>
 hipError_t run_fit(const kvc_params_t* p, const void* Q, const void* K, const void* V,
-                   const int32_t* idx, float* out_bias, float* out_V, int32_t* status, void* ws,
+                   const int32_t* idx, float* out_bias, void* out_V, int32_t* status, void* ws,
                    const Layout& L, int qg, const int32_t* tv, hipStream_t st) {
   kvc::FitBufs fb = fit_bufs(ws, L);
   fb.tv = tv;
+  fb.wait_ticks = g_wait_ticks;
   return kvc::launch_fit<In, D>(Q, K, V, at<double>(ws, L.lse), at<float>(ws, L.O), idx,
-                                fb, out_bias, out_V, status,
+                                fb, out_bias, out_V, p->out_v_dtype == KVC_BF16, status,
                                 static_cast<int>(p->B), static_cast<int>(p->n),
                                 static_cast<int>(p->T), static_cast<int>(p->t), p->ridge_rel,
                                 p->max_nnls_iters, qg, st);
@@ -248,7 +255,7 @@ struct ScoreOp {
 template <class In, int D>
 struct FitOp {
   static hipError_t run(const kvc_params_t* p, const void* Q, const void* K, const void* V,
-                        const int32_t* idx, float* ob, float* ov, int32_t* status, void* ws,
+                        const int32_t* idx, float* ob, void* ov, int32_t* status, void* ws,
                         const Layout* L, int qg, const int32_t* tv, hipStream_t st) {
     return run_fit<In, D>(p, Q, K, V, idx, ob, ov, status, ws, *L, qg, tv, st);
   }
@@ -305,7 +312,7 @@ bool chunk_params(const kvc_params_t* p, int64_t C, kvc_params_t* out) {
 // caller's protected-key mask [B][T] (device) or null.
 int compact_impl(const kvc_params_t* p, int qg, const int32_t* t_in, const uint8_t* protect,
                  const void* Q_ref, const void* K, const void* V, void* out_K, float* out_bias,
-                 float* out_V, int32_t* out_idx, int32_t* out_status, void* workspace,
+                 void* out_V, int32_t* out_idx, int32_t* out_status, void* workspace,
                  hipStream_t stream, bool omp = false) {
   const Layout L = make_layout(p, omp);
   int32_t* idx = out_idx ? out_idx : at<int32_t>(workspace, L.idx);
@@ -336,17 +343,22 @@ int compact_impl(const kvc_params_t* p, int qg, const int32_t* t_in, const uint8
       e = kvc::launch_omp(P32, omp_bufs(workspace, L), idx, B, static_cast<int>(p->n), T, t,
                           stream);
   } else if (e == hipSuccess) {
+    kvc::prof_mark(KVC_STAGE_TOPT, false, stream);
     e = kvc::launch_select(at<float>(workspace, L.imp), idx, status, tv, emask, B, T, t, stream);
+    kvc::prof_mark(KVC_STAGE_TOPT, true, stream);
   }
+  kvc::prof_mark(KVC_STAGE_GATHER, false, stream);
   if (e == hipSuccess)
     e = kvc::launch_gather(K, idx, out_K, B, T, t, static_cast<int>(p->d) * es, stream);
+  kvc::prof_mark(KVC_STAGE_GATHER, true, stream);
   kvc::prof_mark(KVC_STAGE_SELECT, true, stream);
   if (e == hipSuccess)
     e = dispatch<FitOp>(p, Q_ref, K, V, static_cast<const int32_t*>(idx), out_bias, out_V,
                         status, workspace, &L, qg, tv, stream);
   if (e == hipSuccess && protect)
     e = kvc::launch_fill_protected(plist, tv, K, V, out_K, out_V, out_bias, idx, B, T, t,
-                                   static_cast<int>(p->d), p->in_dtype == KVC_BF16, stream);
+                                   static_cast<int>(p->d), p->in_dtype == KVC_BF16,
+                                   p->out_v_dtype == KVC_BF16, stream);
   if (e == hipSuccess && qg > 1 && out_idx)
     e = kvc::launch_idx_offset(out_idx, B, t, qg, T, stream);
   kvc::prof_mark(KVC_STAGE_TOTAL, true, stream);
@@ -364,6 +376,8 @@ void kvc_params_default(kvc_params_t* p) {
   p->agg = KVC_AGG_RMS;
   p->ridge_rel = 1e-6;
   p->max_nnls_iters = 32;
+  p->out_v_dtype = KVC_F32;
+  p->refine_steps = 0;
   p->reserved = 0;
 }
 
@@ -385,7 +399,7 @@ int kvc_workspace_layout(const kvc_params_t* p, kvc_ws_layout_t* out) {
 }
 
 int kvc_compact(const kvc_params_t* p, const void* Q_ref, const void* K, const void* V,
-                void* out_K, float* out_bias, float* out_V, int32_t* out_idx,
+                void* out_K, float* out_bias, void* out_V, int32_t* out_idx,
                 int32_t* out_status, void* workspace, size_t workspace_bytes,
                 hipStream_t stream) {
   int rc = common_checks(p, Q_ref, K, V, out_bias, out_V, workspace, workspace_bytes);
@@ -402,7 +416,7 @@ size_t kvc_workspace_bytes_omp(const kvc_params_t* p) {
 }
 
 int kvc_compact_omp(const kvc_params_t* p, const void* Q_ref, const void* K, const void* V,
-                    void* out_K, float* out_bias, float* out_V, int32_t* out_idx,
+                    void* out_K, float* out_bias, void* out_V, int32_t* out_idx,
                     int32_t* out_status, void* workspace, size_t workspace_bytes,
                     hipStream_t stream) {
   int rc = common_checks(p, Q_ref, K, V, out_bias, out_V, workspace, workspace_bytes);
@@ -416,7 +430,7 @@ int kvc_compact_omp(const kvc_params_t* p, const void* Q_ref, const void* K, con
 
 int kvc_compact_protected(const kvc_params_t* p, const uint8_t* protect_mask, const void* Q_ref,
                           const void* K, const void* V, void* out_K, float* out_bias,
-                          float* out_V, int32_t* out_idx, int32_t* out_status, void* workspace,
+                          void* out_V, int32_t* out_idx, int32_t* out_status, void* workspace,
                           size_t workspace_bytes, hipStream_t stream) {
   int rc = common_checks(p, Q_ref, K, V, out_bias, out_V, workspace, workspace_bytes);
   if (rc) return rc;
@@ -428,7 +442,7 @@ int kvc_compact_protected(const kvc_params_t* p, const uint8_t* protect_mask, co
 }
 
 int kvc_compact_ragged(const kvc_params_t* p, const int32_t* t_heads, const void* Q_ref,
-                       const void* K, const void* V, void* out_K, float* out_bias, float* out_V,
+                       const void* K, const void* V, void* out_K, float* out_bias, void* out_V,
                        int32_t* out_idx, int32_t* out_status, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
   int rc = common_checks(p, Q_ref, K, V, out_bias, out_V, workspace, workspace_bytes);
@@ -447,7 +461,7 @@ size_t kvc_workspace_bytes_chunked(const kvc_params_t* p, int64_t n_chunks) {
 }
 
 int kvc_compact_chunked(const kvc_params_t* p, int64_t n_chunks, const void* Q_ref,
-                        const void* K, const void* V, void* out_K, float* out_bias, float* out_V,
+                        const void* K, const void* V, void* out_K, float* out_bias, void* out_V,
                         int32_t* out_idx, int32_t* out_status, void* workspace,
                         size_t workspace_bytes, hipStream_t stream) {
   kvc_params_t pc;
@@ -461,7 +475,7 @@ int kvc_compact_chunked(const kvc_params_t* p, int64_t n_chunks, const void* Q_r
 }
 
 int kvc_fit(const kvc_params_t* p, const void* Q_ref, const void* K, const void* V,
-            const int32_t* idx, float* out_bias, float* out_V, int32_t* out_status,
+            const int32_t* idx, float* out_bias, void* out_V, int32_t* out_status,
             void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int rc = common_checks(p, Q_ref, K, V, out_bias, out_V, workspace, workspace_bytes);
   if (rc) return rc;
@@ -524,9 +538,20 @@ int kvc_attend(const kvc_attend_params_t* p, const void* Q, const void* K1, cons
   return e == hipSuccess ? KVC_OK : KVC_EHIP;
 }
 
+int kvc_set_wait_limit(uint64_t ticks) {
+  g_wait_ticks = ticks == 0 ? kDefaultWaitTicks : ticks;
+  return KVC_OK;
+}
+
 int kvc_profile_enable(uint32_t stage_mask) {
   g_prof.mask = stage_mask & ((1u << KVC_NUM_STAGES) - 1);
-  for (int s = 0; s < KVC_NUM_STAGES; ++s) g_prof.used[s] = 0;
+  for (int s = 0; s < KVC_NUM_STAGES; ++s) {
+    g_prof.used[s] = 0;
+    if (g_prof.mask == 0) {  // off: release the events (none outlive their use)
+      for (hipEvent_t e : g_prof.ev[s]) (void)hipEventDestroy(e);
+      g_prof.ev[s].clear();
+    }
+  }
   return KVC_OK;
 }
 

@@ -22,11 +22,12 @@ hipError_t launch_select(const float* imp, int32_t* idx, int32_t* status, const 
 // tv[b] = t - pp_b is the budget left for the fitted keys.
 hipError_t launch_protect_prep(const uint8_t* mask, uint8_t* emask, int32_t* plist, int32_t* tv,
                                int32_t* status, int B, int T, int t, hipStream_t st);
-// Slots [tv[b], t) of head b: the protected keys, exact (K, V as float, bias 0).
+// Slots [tv[b], t) of head b: the protected keys, exact (K, V converted to
+// float32, or to bfloat16 when v_bf16; bias 0).
 hipError_t launch_fill_protected(const int32_t* plist, const int32_t* tv, const void* K,
-                                 const void* V, void* out_K, float* out_V, float* out_bias,
+                                 const void* V, void* out_K, void* out_V, float* out_bias,
                                  int32_t* out_idx, int B, int T, int t, int D, bool bf16,
-                                 hipStream_t st);
+                                 bool v_bf16, hipStream_t st);
 // tv[b] = tin[b] clamped to [1, t]; status[b] |= 16 where clamped
 hipError_t launch_budgets(const int32_t* tin, int32_t* tv, int32_t* status, int B, int t,
                           hipStream_t st);
@@ -50,6 +51,7 @@ struct FitBufs {
   double* flops;    // [B][2] fp64 work of the NNLS sweeps and of the value sweeps
   double* part;     // split-K partial tiles of the fit GEMMs
   size_t part_cap;  // its capacity in doubles
+  uint64_t wait_ticks;  // bound on each team wait (100 MHz constant clock)
 };
 // Order of a head's sweep matrix: right-hand-side rows (d rounded up to 64)
 // plus the variables (t rounded up to 64).
@@ -61,10 +63,12 @@ constexpr int kTicketOffset = kMaxTeamGrid * kFlagStride;
 constexpr int kReadyOffset = 2 * kMaxTeamGrid * kFlagStride;
 constexpr int kBarWords = 3 * kMaxTeamGrid * kFlagStride + 1;
 template <class In, int D>
+// out_V: float32, or bfloat16 (the float32 value rounded to nearest-even)
+// when v_bf16
 hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const double* lse,
                       const float* O, const int32_t* idx, FitBufs fb, float* out_bias,
-                      float* out_V, int32_t* status, int B, int n, int T, int t, double ridge,
-                      int max_iters, int qg, hipStream_t st);
+                      void* out_V, bool v_bf16, int32_t* status, int B, int n, int T, int t,
+                      double ridge, int max_iters, int qg, hipStream_t st);
 // kept indices of (head, chunk) b' made global: idx[b'][a] += (b' mod C) * Tc
 hipError_t launch_idx_offset(int32_t* idx, int Bc, int t, int C, int Tc, hipStream_t st);
 // Attention over block 1 (K1, V1 with a per-key bias) then block 2 (K2, V2);

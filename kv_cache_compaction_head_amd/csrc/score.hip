@@ -650,8 +650,10 @@ hipError_t launch_score(const void* Q, const void* K, const void* V, double2* ml
   hipLaunchKernelGGL(k_o_reduce, dim3((n + 31) / 32, D / 32, B), dim3(32, 8), 0, st, Opart, O, n,
                      D, nsplit2);
   const size_t tot = static_cast<size_t>(B) * T;
+  prof_mark(8, false, st);
   hipLaunchKernelGGL(k_imp_reduce, dim3((tot + 255) / 256), dim3(256), 0, st, imp_part, imp, T,
                      nqb, B);
+  prof_mark(8, true, st);
   return hipGetLastError();
 }
 

@@ -317,12 +317,12 @@ hipError_t launch_protect_prep(const uint8_t* mask, uint8_t* emask, int32_t* pli
 }
 
 // Slots a in [tv[b], t) of head b hold protected key plist[b][a - tv[b]]:
-// out_K = K row (bytes), out_V = V row as float, bias 0, idx = position.
-// grid (ceil(t*D/256), B).
-template <class In>
+// out_K = K row (bytes), out_V = V row as OutT (float, or bfloat16 of the
+// float value), bias 0, idx = position.  grid (ceil(t*D/256), B).
+template <class In, class OutT>
 __global__ void k_fill_protected(const int32_t* __restrict__ plist, const int32_t* __restrict__ tv,
                                  const In* __restrict__ K, const In* __restrict__ V,
-                                 In* __restrict__ out_K, float* __restrict__ out_V,
+                                 In* __restrict__ out_K, OutT* __restrict__ out_V,
                                  float* __restrict__ out_bias, int32_t* __restrict__ out_idx,
                                  int T, int t, int D) {
   const int b = blockIdx.y;
@@ -333,26 +333,34 @@ __global__ void k_fill_protected(const int32_t* __restrict__ plist, const int32_
   const size_t src = (static_cast<size_t>(b) * T + j) * D + c;
   const size_t dst = (static_cast<size_t>(b) * t + a) * D + c;
   out_K[dst] = K[src];
-  out_V[dst] = to_f32<In>(V[src]);
+  out_V[dst] = from_f32<OutT>(to_f32<In>(V[src]));
   if (c == 0) {
     out_bias[static_cast<size_t>(b) * t + a] = 0.f;
     if (out_idx) out_idx[static_cast<size_t>(b) * t + a] = j;
   }
 }
 
-hipError_t launch_fill_protected(const int32_t* plist, const int32_t* tv, const void* K,
-                                 const void* V, void* out_K, float* out_V, float* out_bias,
-                                 int32_t* out_idx, int B, int T, int t, int D, bool bf16,
-                                 hipStream_t st) {
+template <class In, class OutT>
+static void fill_protected(const int32_t* plist, const int32_t* tv, const void* K, const void* V,
+                           void* out_K, void* out_V, float* out_bias, int32_t* out_idx, int B,
+                           int T, int t, int D, hipStream_t st) {
   const dim3 grid((static_cast<size_t>(t) * D + 255) / 256, B);
-  if (bf16)
-    hipLaunchKernelGGL(k_fill_protected<bf16_t>, grid, dim3(256), 0, st, plist, tv,
-                       static_cast<const bf16_t*>(K), static_cast<const bf16_t*>(V),
-                       static_cast<bf16_t*>(out_K), out_V, out_bias, out_idx, T, t, D);
-  else
-    hipLaunchKernelGGL(k_fill_protected<float>, grid, dim3(256), 0, st, plist, tv,
-                       static_cast<const float*>(K), static_cast<const float*>(V),
-                       static_cast<float*>(out_K), out_V, out_bias, out_idx, T, t, D);
+  hipLaunchKernelGGL((k_fill_protected<In, OutT>), grid, dim3(256), 0, st, plist, tv,
+                     static_cast<const In*>(K), static_cast<const In*>(V), static_cast<In*>(out_K),
+                     static_cast<OutT*>(out_V), out_bias, out_idx, T, t, D);
+}
+
+hipError_t launch_fill_protected(const int32_t* plist, const int32_t* tv, const void* K,
+                                 const void* V, void* out_K, void* out_V, float* out_bias,
+                                 int32_t* out_idx, int B, int T, int t, int D, bool bf16,
+                                 bool v_bf16, hipStream_t st) {
+  if (bf16) {
+    if (v_bf16) fill_protected<bf16_t, bf16_t>(plist, tv, K, V, out_K, out_V, out_bias, out_idx, B, T, t, D, st);
+    else fill_protected<bf16_t, float>(plist, tv, K, V, out_K, out_V, out_bias, out_idx, B, T, t, D, st);
+  } else {
+    if (v_bf16) fill_protected<float, bf16_t>(plist, tv, K, V, out_K, out_V, out_bias, out_idx, B, T, t, D, st);
+    else fill_protected<float, float>(plist, tv, K, V, out_K, out_V, out_bias, out_idx, B, T, t, D, st);
+  }
   return hipGetLastError();
 }
 

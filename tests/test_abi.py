@@ -31,18 +31,21 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_params_struct_layout_and_defaults():
-    assert ctypes.sizeof(_lib.Params) == 64
+    assert ctypes.sizeof(_lib.Params) == 72
     p = _lib.Params()
     kvc.load().kvc_params_default(ctypes.byref(p))
     assert p.in_dtype == _lib.KVC_BF16 and p.agg == _lib.KVC_AGG_RMS
     assert p.ridge_rel == 1e-6 and p.max_nnls_iters == 32 and p.reserved == 0
+    assert p.out_v_dtype == _lib.KVC_F32 and p.refine_steps == 0
     assert p.B == p.T == p.n == p.d == p.t == 0
 
 
 @pytest.mark.parametrize("field,value", [("B", 0), ("T", 0), ("n", 0), ("d", 96), ("t", 0),
                                          ("t", 1025), ("in_dtype", 7), ("agg", 3),
-                                         ("ridge_rel", 0.0), ("ridge_rel", float("nan")),
-                                         ("max_nnls_iters", 0), ("reserved", 1)])
+                                         ("ridge_rel", -1e-9), ("ridge_rel", float("nan")),
+                                         ("ridge_rel", float("inf")), ("max_nnls_iters", 0),
+                                         ("out_v_dtype", 2), ("refine_steps", -1),
+                                         ("reserved", 1)])
 def test_invalid_params_have_no_workspace(field, value):
     p = kvc.make_params(2, 1024, 64, 128, 16, "bf16")
     assert kvc.workspace_bytes(p) > 0
@@ -98,3 +101,17 @@ def test_header_documents_each_entry_point():
     assert "Fast KV Compaction via Attention Matching" in src
     for name in _declared():
         assert src.count(name) >= 1
+
+
+def test_ridge_zero_and_bf16_values_are_valid_parameters():
+    """ridge_rel = 0 is the literal NNLS / least squares; fitted values may be
+    stored as bfloat16."""
+    p = kvc.make_params(2, 1024, 64, 128, 16, "bf16", ridge_rel=0.0, out_v_dtype="bf16")
+    assert kvc.workspace_bytes(p) == kvc.workspace_bytes(kvc.make_params(2, 1024, 64, 128, 16,
+                                                                          "bf16"))
+    assert kvc.workspace_layout(p).lse >= 0
+
+
+def test_wait_limit_setter():
+    kvc.set_wait_limit(5)
+    kvc.set_wait_limit(0)   # back to the default

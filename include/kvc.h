@@ -120,6 +120,24 @@ int kvc_compact(const kvc_params_t* p, const void* Q_ref, const void* K, const v
                 int32_t* out_status, void* workspace, size_t workspace_bytes,
                 hipStream_t stream);
 
+/* kvc_compact for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and outputs, with the workspace taken from a device array
+ * of KVC_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs
+ * on until the process ends.  Allocates nothing.
+ *   Arguments as kvc_compact, without the workspace.
+ *   Returns KVC_EWORKSPACE when kvc_workspace_bytes(p) exceeds
+ *   KVC_NOALLOC_SCRATCH_BYTES (64 MiB; e.g. one head of 4096 tokens with
+ *   t = 256, or a few heads of 8192), KVC_EHIP if the array's device address
+ *   cannot be obtained, else as kvc_compact.
+ *   All calls on one device share its array, which keeps the last call's
+ *   contents: calls that overlap in time on one device race (order them on one
+ *   stream). */
+#define KVC_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int kvc_compact_noalloc(const kvc_params_t* p, const void* Q_ref, const void* K, const void* V,
+                        void* out_K, float* out_bias, void* out_V, int32_t* out_idx,
+                        int32_t* out_status, hipStream_t stream);
+
 /* Bias and value fit for a caller-given kept set (steps 3-4 only).
  *   idx [B, t] int32, strictly ascending, in [0, T).  Other arguments as in
  *   kvc_compact.  Used to check the fits in isolation and to re-fit a cache

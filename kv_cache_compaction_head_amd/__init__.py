@@ -16,7 +16,7 @@ from ._lib import (KVC_AGG_MEAN, KVC_AGG_RMS, KVC_BF16, KVC_F32, STATUS_NNLS_CAP
                    make_params, set_wait_limit, strerror, workspace_bytes,
                    workspace_bytes_chunked, workspace_bytes_omp, workspace_layout)
 
-__all__ = ["compact", "compact_omp", "compact_chunked", "compact_ragged", "compact_protected", "attend", "fit", "Compacted", "intermediates", "load", "make_params",
+__all__ = ["compact", "compact_noalloc", "compact_omp", "compact_chunked", "compact_ragged", "compact_protected", "attend", "fit", "Compacted", "intermediates", "load", "make_params",
            "workspace_bytes", "workspace_bytes_chunked", "workspace_bytes_omp", "workspace_layout", "strerror", "Params",
            "set_wait_limit"]
 
@@ -105,6 +105,31 @@ def compact(Q, K, V, t: int, *, agg: str = "rms", ridge_rel: float = 1e-6,
                             ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(stream, dev))
     _lib.check(rc)
     return Compacted(keys, bias, values, idx, status, ws, p)
+
+
+def compact_noalloc(Q, K, V, t: int, *, agg: str = "rms", ridge_rel: float = 1e-6,
+                    max_nnls_iters: int = 32, out_v_dtype=None, stream=None) -> Compacted:
+    """compact() through kvc_compact_noalloc: the library takes its workspace
+    from its own per-device scratch array (at most _lib.NOALLOC_SCRATCH_BYTES)
+    instead of a caller buffer.  Only the outputs are allocated here."""
+    import torch
+    Q, K, V, _ = _prep(Q, K, V)
+    B, n, d = Q.shape
+    T = K.shape[1]
+    dt = "bf16" if Q.dtype == torch.bfloat16 else "f32"
+    vs, vt = _vdt(out_v_dtype)
+    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters, vs)
+    dev = Q.device
+    keys = torch.empty((B, t, d), dtype=Q.dtype, device=dev)
+    bias = torch.empty((B, t), dtype=torch.float32, device=dev)
+    values = torch.empty((B, t, d), dtype=vt, device=dev)
+    idx = torch.empty((B, t), dtype=torch.int32, device=dev)
+    status = torch.empty((B,), dtype=torch.int32, device=dev)
+    rc = load().kvc_compact_noalloc(ctypes.byref(p), _vp(Q), _vp(K), _vp(V), _vp(keys),
+                                    _vp(bias), _vp(values), _vp(idx), _vp(status),
+                                    _stream(stream, dev))
+    _lib.check(rc)
+    return Compacted(keys, bias, values, idx, status, None, p)
 
 
 def compact_omp(Q, K, V, t: int, *, ridge_rel: float = 1e-6, max_nnls_iters: int = 32,

@@ -10,12 +10,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvc.so")
 
 KVC_OK, KVC_EINVAL, KVC_EWORKSPACE, KVC_EHIP, KVC_EUNSUPPORTED = 0, -1, -2, -3, -4
+NOALLOC_SCRATCH_BYTES = 64 << 20  # KVC_NOALLOC_SCRATCH_BYTES
 KVC_F32, KVC_BF16 = 0, 1
 KVC_AGG_RMS, KVC_AGG_MEAN = 0, 1
 (STATUS_NOT_SPD, STATUS_NNLS_CAP, STATUS_NONFINITE, STATUS_SYNC_TIMEOUT, STATUS_BUDGET,
  STATUS_PROTECT) = 1, 2, 4, 8, 16, 32
 
-EXPORTS = ("kvc_params_default", "kvc_workspace_bytes", "kvc_compact", "kvc_fit",
+EXPORTS = ("kvc_params_default", "kvc_workspace_bytes", "kvc_compact", "kvc_compact_noalloc",
+           "kvc_fit",
            "kvc_workspace_bytes_chunked", "kvc_compact_chunked", "kvc_compact_ragged",
            "kvc_compact_protected", "kvc_attend", "kvc_attend_workspace_bytes", "kvc_workspace_bytes_omp",
            "kvc_compact_omp",
@@ -67,6 +69,8 @@ def load() -> ctypes.CDLL:
     lib.kvc_workspace_bytes.restype = ctypes.c_size_t
     lib.kvc_compact.argtypes = [P, vp, vp, vp, vp, f32p, f32p, i32p, i32p, vp, ctypes.c_size_t, vp]
     lib.kvc_compact.restype = ctypes.c_int
+    lib.kvc_compact_noalloc.argtypes = [P, vp, vp, vp, vp, f32p, f32p, i32p, i32p, vp]
+    lib.kvc_compact_noalloc.restype = ctypes.c_int
     lib.kvc_fit.argtypes = [P, vp, vp, vp, i32p, f32p, f32p, i32p, vp, ctypes.c_size_t, vp]
     lib.kvc_fit.restype = ctypes.c_int
     lib.kvc_workspace_bytes_chunked.argtypes = [P, ctypes.c_int64]

@@ -115,3 +115,15 @@ def test_ridge_zero_and_bf16_values_are_valid_parameters():
 def test_wait_limit_setter():
     kvc.set_wait_limit(5)
     kvc.set_wait_limit(0)   # back to the default
+
+
+def test_noalloc_rejects_a_workspace_past_its_scratch_before_any_device_work():
+    """A problem whose workspace exceeds the static scratch array is refused on
+    the host (the fake device addresses are never used)."""
+    lib = kvc.load()
+    p = kvc.make_params(8, 32768, 2048, 128, 655, "bf16")
+    assert kvc.workspace_bytes(p) > _lib.NOALLOC_SCRATCH_BYTES
+    A = [_fake(0x10000 * (i + 1)) for i in range(8)]
+    assert lib.kvc_compact_noalloc(ctypes.byref(p), *A, None) == _lib.KVC_EWORKSPACE
+    q = kvc.make_params(2, 1024, 64, 128, 2000, "bf16")  # t > T
+    assert lib.kvc_compact_noalloc(ctypes.byref(q), *A, None) == _lib.KVC_EINVAL

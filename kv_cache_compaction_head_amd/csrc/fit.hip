@@ -682,10 +682,7 @@ struct __align__(16) SweepSmem {
   double pp[kSB][kSB + 1];         // pivot block, then its inverse B
   double li[kSB][kSB + 1];         // L^-1 (unit lower; identity past k)
   double rD[kSB];                  // 1 / D (0 past k)
-  double sW[kSB][17];              // small inverse: panel of a 16-pivot block,
-  double sV[kSB][17];              // and L[b, <b] L^-1[<b, <b] (16 x 48)
-  double sLb[2][16][17];           // L^-1 of a 16 x 16 diagonal block (two in flight)
-  double mbc[16];
+  double sV[kSB][17];              // LDL scratch: a 16 x 17 block per wave
   double sgn[kSB];                 // s_q
   int piv[kSB];                    // matrix row of pivot q
   double sgn2[kSB];                // the next step's pivots (lookahead)
@@ -798,13 +795,13 @@ __device__ int wg_append(bool f, int base, int* slot) {
 // overwritten) gives sm.li = L^-1 (identity past k) and sm.rD = 1/D (0 past
 // k); small_b then forms B = A_PP^-1 = L^-T D^-1 L^-1 on fp64 MFMA.  The
 // factorization is blocked by 16 pivots; a diagonal block is swept pivot by
-// pivot, and before sweep p its pivot row holds -L_bb^-1[p][j] at the swept
-// columns j < p and the pivot on the diagonal.  Inverting the pivot block by
-// a blocked sweep instead would form its off-diagonal parts through explicit
-// inverses of the 16 x 16 blocks and lose them when those are
-// ill-conditioned.  A pivot without the sign s_p is replaced by s_p (the
-// system is not numerically definite); small_ldl's return value, meaningful
-// in wave 0, says whether that happened.
+// pivot (Gauss-Jordan), and before sweep p its pivot row holds
+// -L_bb^-1[p][j] at the swept columns j < p and the pivot on the diagonal.
+// Inverting the pivot block by a blocked sweep instead would form its
+// off-diagonal parts through explicit inverses of the 16 x 16 blocks and lose
+// them when those are ill-conditioned.  A pivot without the sign s_p is
+// replaced by s_p (the system is not numerically definite); small_ldl's
+// return value, meaningful in wave 0, says whether that happened.
 // The wave's index in the workgroup as a wave-uniform value: the compiler
 // cannot tell that threadIdx.x / 64 is the same across a wave, and would
 // otherwise treat every branch and address derived from it as divergent.
@@ -820,41 +817,10 @@ __device__ __forceinline__ double rdlane(double v, int src) {
   return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
 }
 
-// Wave 0 sweeps the 16 x 16 diagonal block at o of sm.pp.  Lane (g, c) =
-// (lane / 16, lane % 16) holds rows 4g .. 4g+3 of column c.  For pivot m the
-// pivot column's entries of a lane's rows come from lane m of its 16-lane row
-// (DPP row broadcast), and the pivot row's entry of its column from row group
-// m / 4 (two lane-half swaps); the pivot itself is read from its lane.
-// Records -L^-1 of the block (the pivot rows at their turn) into sL and 1/D
-// into sm.rD[o..o+15].  Returns whether a pivot lacked its sign (replaced by
-// the sign).
-template <int N>
-__device__ __forceinline__ double row_bcast(double v) {  // lane N of each 16-lane row
-  const unsigned long long u = __double_as_longlong(v);
-  // every lane is written (all rows and banks enabled), so no old value
-  const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(u), 0x150 + N, 0xF, 0xF, true);
-  const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(u >> 32), 0x150 + N, 0xF, 0xF, true);
-  return __longlong_as_double(static_cast<long long>(
-      (static_cast<unsigned long long>(static_cast<unsigned>(hi)) << 32) | static_cast<unsigned>(lo)));
-}
-template <int G>
-__device__ __forceinline__ unsigned group_bcast32(unsigned x) {  // 16-lane row G to all four
-  const auto s16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);  // rows (0,0,2,2) / (1,1,3,3)
-  const unsigned w = (G & 1) ? s16[1] : s16[0];
-  const auto s32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);  // halves (lo,lo) / (hi,hi)
-  return (G >> 1) ? s32[1] : s32[0];
-}
-template <int G>
-__device__ __forceinline__ double group_bcast(double v) {
-  const unsigned long long u = __double_as_longlong(v);
-  const unsigned lo = group_bcast32<G>(static_cast<unsigned>(u));
-  const unsigned hi = group_bcast32<G>(static_cast<unsigned>(u >> 32));
-  return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
-}
-// 1/d by Newton-Raphson from the hardware estimate (two steps, each squaring
-// the relative error: within an ulp or so of the rounded quotient).  The
-// pivot chain waits on this reciprocal at every pivot; the IEEE division
-// sequence is twice as long.
+// 1/d by Newton-Raphson from the hardware estimate (about 2^-24 relative;
+// two steps, each squaring the relative error: within an ulp or so of the
+// rounded quotient).  The pivot chain waits on this reciprocal at every
+// pivot; the IEEE division sequence is twice as long.
 __device__ __forceinline__ double recip(double d) {
   double r = __builtin_amdgcn_rcp(d);
   double e = fma(-d, r, 1.0);
@@ -862,168 +828,314 @@ __device__ __forceinline__ double recip(double d) {
   e = fma(-d, r, 1.0);
   return fma(r, e, r);
 }
+
+// Sweep of a 16 x 16 diagonal block by the 16 lanes of each 16-lane row of a
+// wave: lane c holds column c of the block, a[r] = A[o + r][o + c] (the
+// four rows of lanes compute the same thing; the first one stores).  The
+// pivot row is then lane-local (A[M][c] = a[M]); the pivot column A[r][M]
+// comes from lane M through a DPP row broadcast fused into the update FMA,
+// v_fmac_f64 with row_newbcast on its first source, so a pivot costs one
+// FMA per row and no separate data movement.
+//
+// a[r] += a[r] of lane M * be for the listed rows.  A VALU write of a DPP
+// source register needs two wait states before the DPP read: one s_nop 1
+// ahead of each group.  sweep_next<M> updates row M + 1 (the next pivot's
+// row, on the dependence chain) alone; sweep_rest<M> the rows other than M
+// and M + 1.
+#define KVC_FMAC_DPP(i) "v_fmac_f64_dpp %" #i ", %" #i ", %[be] row_newbcast:%[m] row_mask:0xf bank_mask:0xf\n"
+#define KVC_FMAC_DPP(i) "v_fmac_f64_dpp %" #i ", %" #i ", %[be] row_newbcast:%[m] row_mask:0xf bank_mask:0xf\n"
+template <int M> __device__ __forceinline__ void sweep_next(double (&a)[16], double be);
+template <int M> __device__ __forceinline__ void sweep_rest(double (&a)[16], double be);
+template <> __device__ __forceinline__ void sweep_next<0>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[1]) : [be] "v"(be), [m] "n"(0));
+}
+template <> __device__ __forceinline__ void sweep_rest<0>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
+      : "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
+      : [be] "v"(be), [m] "n"(0));
+}
+template <> __device__ __forceinline__ void sweep_next<1>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[2]) : [be] "v"(be), [m] "n"(1));
+}
+template <> __device__ __forceinline__ void sweep_rest<1>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
+      : "+v"(a[0]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
+      : [be] "v"(be), [m] "n"(1));
+}
+template <> __device__ __forceinline__ void sweep_next<2>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[3]) : [be] "v"(be), [m] "n"(2));
+}
+template <> __device__ __forceinline__ void sweep_rest<2>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
+      : "+v"(a[0]), "+v"(a[1]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
+      : [be] "v"(be), [m] "n"(2));
+}
+template <> __device__ __forceinline__ void sweep_next<3>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[4]) : [be] "v"(be), [m] "n"(3));
+}
+template <> __device__ __forceinline__ void sweep_rest<3>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
+      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
+      : [be] "v"(be), [m] "n"(3));
+}
+template <> __device__ __forceinline__ void sweep_next<4>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[5]) : [be] "v"(be), [m] "n"(4));
+}
+template <> __device__ __forceinline__ void sweep_rest<4>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
+      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
+      : [be] "v"(be), [m] "n"(4));
+}
+template <> __device__ __forceinline__ void sweep_next<5>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[6]) : [be] "v"(be), [m] "n"(5));
+}
+template <> __device__ __forceinline__ void sweep_rest<5>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
+      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
+      : [be] "v"(be), [m] "n"(5));
+}
+template <> __device__ __forceinline__ void sweep_next<6>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[7]) : [be] "v"(be), [m] "n"(6));
+}
+template <> __device__ __forceinline__ void sweep_rest<6>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
+      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
+      : [be] "v"(be), [m] "n"(6));
+}
+template <> __device__ __forceinline__ void sweep_next<7>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[8]) : [be] "v"(be), [m] "n"(7));
+}
+template <> __device__ __forceinline__ void sweep_rest<7>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
+      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
+      : [be] "v"(be), [m] "n"(7));
+}
+template <> __device__ __forceinline__ void sweep_next<8>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[9]) : [be] "v"(be), [m] "n"(8));
+}
+template <> __device__ __forceinline__ void sweep_rest<8>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
+      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
+      : [be] "v"(be), [m] "n"(8));
+}
+template <> __device__ __forceinline__ void sweep_next<9>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[10]) : [be] "v"(be), [m] "n"(9));
+}
+template <> __device__ __forceinline__ void sweep_rest<9>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
+      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
+      : [be] "v"(be), [m] "n"(9));
+}
+template <> __device__ __forceinline__ void sweep_next<10>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[11]) : [be] "v"(be), [m] "n"(10));
+}
+template <> __device__ __forceinline__ void sweep_rest<10>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
+      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
+      : [be] "v"(be), [m] "n"(10));
+}
+template <> __device__ __forceinline__ void sweep_next<11>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[12]) : [be] "v"(be), [m] "n"(11));
+}
+template <> __device__ __forceinline__ void sweep_rest<11>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
+      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
+      : [be] "v"(be), [m] "n"(11));
+}
+template <> __device__ __forceinline__ void sweep_next<12>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[13]) : [be] "v"(be), [m] "n"(12));
+}
+template <> __device__ __forceinline__ void sweep_rest<12>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
+      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[14]), "+v"(a[15])
+      : [be] "v"(be), [m] "n"(12));
+}
+template <> __device__ __forceinline__ void sweep_next<13>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[14]) : [be] "v"(be), [m] "n"(13));
+}
+template <> __device__ __forceinline__ void sweep_rest<13>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
+      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[15])
+      : [be] "v"(be), [m] "n"(13));
+}
+template <> __device__ __forceinline__ void sweep_next<14>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[15]) : [be] "v"(be), [m] "n"(14));
+}
+template <> __device__ __forceinline__ void sweep_rest<14>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
+      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13])
+      : [be] "v"(be), [m] "n"(14));
+}
+template <> __device__ __forceinline__ void sweep_rest<15>(double (&a)[16], double be) {
+  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13) KVC_FMAC_DPP(14)
+      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14])
+      : [be] "v"(be), [m] "n"(15));
+}
+#undef KVC_FMAC_DPP
+
+// Pivot M: d = A[M][M] (lane M), rd = 1/d.  The other columns lose
+// A[r][M] A[M][c]/d (be = -A[M][c]/d); the pivot row becomes A[M][c]/d; the
+// pivot column would scale by 1/d: instead of rewriting its rows, the pivot
+// lane records 1/d as its column scale sc (be = 0 leaves its rows as they
+// are).  A swept column's stored values are its true values over sc, and the
+// updates of later pivots need no correction (the scale of the pivot column
+// is still 1 when it is swept, and a lane's own scale cancels out of its
+// update); only the L^-1 record reads true values.  lcol[M] records row M of
+// the block's L^-1 at column c (-A[M][c] at the swept columns c < M, 1 at
+// c = M, 0 after).
 template <int M>
-__device__ __forceinline__ void diag_pivot(double (&a)[4], int g, int c, int o, int k,
-                                           double (*sL)[17], double& myrd, bool& bad) {
-  constexpr int GM = M >> 2, IM = M & 3;
-  SweepSmem& sm = g_sw;
-  double colm[4];  // A[4g + i][m]
-#pragma unroll
-  for (int i = 0; i < 4; ++i) colm[i] = row_bcast<M>(a[i]);
-  const double rowm = group_bcast<GM>(a[IM]);  // A[m][c]
-  const double sg = o + M < k ? sm.sgn[o + M] : 1.0;
-  const double d = rdlane(a[IM], 16 * GM + M);
+__device__ __forceinline__ void diag_pivot(double (&a)[16], double (&lcol)[16],
+                                           const double (&sgv)[16], int c, double& sc,
+                                           bool& bad) {
+  const double d = rdlane(a[M], M);
+  const double sg = sgv[M];
   // a pivot without its sign is replaced by the sign (1/s = s); the test
   // runs beside the reciprocal instead of ahead of it
   const bool ok = d * sg > 0.0;
   bad |= !ok;
   const double rd = ok ? recip(d) : sg;
-  // the four row groups write the same values (no branch on the pivot chain)
-  sL[M][c] = c < M ? -rowm : (c == M ? 1.0 : 0.0);
+  const double rowm = a[M];
+  lcol[M] = c < M ? -(rowm * sc) : (c == M ? 1.0 : 0.0);
   const bool piv = c == M;
-  if (piv) myrd = rd;
-  const double tm = rowm * rd;  // row m of this column, scaled
-  // off the pivot row: the pivot column scales by 1/D, the others lose
-  // A[r][m] * A[m][c] / D (a * 1 and colm * 0 are exact)
-  const double al = piv ? rd : 1.0, be = piv ? 0.0 : -tm;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const double nv = fma(colm[i], be, a[i] * al);
-    a[i] = (i == IM && g == GM) ? (piv ? -rd : tm) : nv;
-  }
+  const double tm = rowm * rd;
+  const double be = piv ? 0.0 : -tm;
+  if constexpr (M < 15) sweep_next<M>(a, be);
+  sweep_rest<M>(a, be);
+  a[M] = piv ? -1.0 : tm;
+  if (piv) sc = rd;
 }
 template <int... Ms>
-__device__ __forceinline__ void diag_pivots(std::integer_sequence<int, Ms...>, double (&a)[4], int g,
-                                            int c, int o, int k, double (*sL)[17], double& myrd,
-                                            bool& bad) {
-  (diag_pivot<Ms>(a, g, c, o, k, sL, myrd, bad), ...);
+__device__ __forceinline__ void diag_pivots(std::integer_sequence<int, Ms...>, double (&a)[16],
+                                            double (&lcol)[16], const double (&sgv)[16], int c,
+                                            double& sc, bool& bad) {
+  (diag_pivot<Ms>(a, lcol, sgv, c, sc, bad), ...);
 }
-__device__ __forceinline__ bool diag_sweep(int o, int k, double (*sL)[17]) {
+// Diagonal block at o: its L^-1 into the diagonal block of sm.li (upper part
+// zero), 1/D into sm.rD[o..o+15].  Run by one wave.
+__device__ __forceinline__ bool diag_sweep(int o, int k) {
   SweepSmem& sm = g_sw;
-  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-  bool bad = false;
-  double a[4], myrd = 0.0;  // lane c keeps 1/D of pivot c
+  const int c = threadIdx.x & 15;
+  double a[16], lcol[16], sgv[16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] = sm.pp[o + 4 * g + i][o + c];
-  diag_pivots(std::make_integer_sequence<int, 16>{}, a, g, c, o, k, sL, myrd, bad);
-  if (g == 0) sm.rD[o + c] = myrd;
+  for (int r = 0; r < 16; ++r) {
+    a[r] = sm.pp[o + r][o + c];
+    sgv[r] = o + r < k ? sm.sgn[o + r] : 1.0;
+  }
+  double sc = 1.0;  // after the sweep: 1/D of pivot c
+  bool bad = false;
+  diag_pivots(std::make_integer_sequence<int, 16>{}, a, lcol, sgv, c, sc, bad);
+  if ((threadIdx.x & 63) < 16) {
+    sm.rD[o + c] = sc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sm.li[o + r][o + c] = lcol[r];
+  }
   return bad;
 }
 
-// Pipelined blocked L D L^T of the pivot block (16-pivot blocks b): wave 0
-// runs the chain the next block waits for -- the sweep of diagonal block b,
-// then block b+1's panel rows W = A[b+1, b] L_bb^-T and its diagonal update
-// A[b+1, b+1] -= W D_b^-1 W^T -- while waves 1-3 do the rest of block b:
-// rows b of L^-1 (-L_bb^-1 L[b, <b] L^-1[<b, <b]), the diagonal block of
-// L^-1, the trailing lower blocks other than (b+1, b+1), and the panel L[>b+1,
-// b] = W D_b^-1.  Each bulk wave forms the panel rows it needs itself, so one
-// workgroup barrier per block suffices; L is parked above the diagonal of
-// sm.li, transposed (L[r][c] at li[c][r]), and cleared at the end.
+// Blocked LDL^T helpers, one wave each, fp64 MFMA 16x16x4 (lane l supplies
+// row l % 16, contraction index l / 16; results at rows l / 16 + 4 i).
+// W_rj = A[r][j] L_jj^-T, parked transposed above the diagonal of sm.li:
+// li[16 j + q][16 r + i] = W_rj[i][q] (that region is cleared at the end).
+__device__ __forceinline__ void ldl_panel(int r, int j) {
+  SweepSmem& sm = g_sw;
+  const int lane = threadIdx.x & 63, g16 = lane >> 4, l16 = lane & 15, o = 16 * j;
+  f64x4 w4 = {};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int m = 4 * ks + g16;
+    w4 = __builtin_amdgcn_mfma_f64_16x16x4f64(sm.pp[16 * r + l16][o + m], sm.li[o + l16][o + m], w4,
+                                              0, 0, 0);
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x) sm.li[o + l16][16 * r + g16 + 4 * x] = w4[x];
+}
+// A[r][c] -= W_rj D_j^-1 W_cj^T (a trailing block of step j)
+__device__ __forceinline__ void ldl_trail(int r, int c, int j) {
+  SweepSmem& sm = g_sw;
+  const int lane = threadIdx.x & 63, g16 = lane >> 4, l16 = lane & 15, o = 16 * j;
+  f64x4 u4 = {};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int q = o + 4 * ks + g16;
+    u4 = __builtin_amdgcn_mfma_f64_16x16x4f64(sm.li[q][16 * r + l16] * sm.rD[q],
+                                              sm.li[q][16 * c + l16], u4, 0, 0, 0);
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x) sm.pp[16 * r + g16 + 4 * x][16 * c + l16] -= u4[x];
+}
+// (L^-1)[j][c] = -L_jj^-1 sum_{m=c}^{j-1} L[j][m] (L^-1)[m][c], with
+// L[j][m] = W_jm D_m^-1; tmp is this wave's 16 x 17 LDS scratch.
+__device__ __forceinline__ void ldl_linv(int j, int c, double (*tmp)[17]) {
+  SweepSmem& sm = g_sw;
+  const int lane = threadIdx.x & 63, g16 = lane >> 4, l16 = lane & 15, o = 16 * j;
+  f64x4 t4 = {};
+  for (int m = c; m < j; ++m)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int q = 16 * m + 4 * ks + g16;
+      t4 = __builtin_amdgcn_mfma_f64_16x16x4f64(sm.li[q][o + l16] * sm.rD[q],
+                                                sm.li[q][16 * c + l16], t4, 0, 0, 0);
+    }
+#pragma unroll
+  for (int x = 0; x < 4; ++x) tmp[g16 + 4 * x][l16] = t4[x];
+  f64x4 r4 = {};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int kk = 4 * ks + g16;
+    r4 = __builtin_amdgcn_mfma_f64_16x16x4f64(sm.li[o + l16][o + kk], tmp[kk][l16], r4, 0, 0, 0);
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x) sm.li[o + g16 + 4 * x][16 * c + l16] = -r4[x];
+}
+
+// Blocked L D L^T of the pivot block by the workgroup, two barriers per
+// 16-pivot block j: first the panels W_rj (r > j) on every wave; then wave 0
+// updates diagonal block j + 1 and sweeps it (the chain the next block
+// waits for), while waves 1-3 update the other trailing blocks of step j and
+// form the L^-1 blocks of block row j.
 __device__ __forceinline__ bool small_ldl(int k) {
   SweepSmem& sm = g_sw;
-  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
-  const int g16 = lane >> 4, l16 = lane & 15;
+  const int tid = threadIdx.x, wave = wave_id();
+  const int nb = (k + 15) >> 4;
+  double(*tmp)[17] = reinterpret_cast<double(*)[17]>(&sm.sV[16 * wave][0]);
   bool bad = false;
-  const int nb = (k + 15) >> 4, kb = 16 * nb;
-  for (int e = tid; e < kSB * kSB; e += kTeamThreads) {
-    const int r = e >> 6, c = e & 63;
-    if (r >= kb || c >= r) sm.li[r][c] = r == c ? 1.0 : 0.0;
-  }
-  if (wave == 0) bad = diag_sweep(0, k, sm.sLb[0]);
+  if (wave == 0) bad = diag_sweep(0, k);
   for (int j = 0; j < nb; ++j) {
-    const int o = 16 * j, o2 = o + 16;
-    __syncthreads();  // block j swept, the bulk work of block j - 1 done
-    double(*sL)[17] = sm.sLb[j & 1];
+    __syncthreads();  // diagonal block j swept; every update of the steps before j done
+    for (int r = j + 1, item = 0; r < nb; ++r, ++item)
+      if (item % 4 == wave) ldl_panel(r, j);
+    __syncthreads();  // the panels of step j parked
     if (wave == 0) {
       if (j + 1 < nb) {
-        // W = A[b+1, b] L_bb^-T (W[i][q] = sum_m A[o2+i][o+m] sL[q][m]) and
-        // then A[b+1, b+1] -= W D^-1 W^T, each four fp64 MFMAs
-        f64x4 w4 = {};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int m = 4 * ks + g16;
-          w4 = __builtin_amdgcn_mfma_f64_16x16x4f64(sm.pp[o2 + l16][o + m], sL[l16][m], w4, 0, 0, 0);
-        }
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int i = g16 + 4 * x;  // W[i][l16]
-          sm.sW[i][l16] = w4[x];
-          sm.li[o + l16][o2 + i] = w4[x] * sm.rD[o + l16];  // L[o2 + i][o + l16], parked
-        }
-        f64x4 d4 = {};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int q = 4 * ks + g16;
-          d4 = __builtin_amdgcn_mfma_f64_16x16x4f64(sm.sW[l16][q] * sm.rD[o + q], sm.sW[l16][q], d4,
-                                                    0, 0, 0);
-        }
-#pragma unroll
-        for (int x = 0; x < 4; ++x) sm.pp[o2 + g16 + 4 * x][o2 + l16] -= d4[x];
-        bad |= diag_sweep(o2, k, sm.sLb[(j + 1) & 1]);
+        ldl_trail(j + 1, j + 1, j);
+        bad |= diag_sweep(16 * (j + 1), k);
       }
     } else {
-      const int w = wave - 1;
-      if (w < j) {  // rows o..o+15 of L^-1, columns 16w..16w+15
-        const int jb = 16 * w;
-        double* T = &sm.sV[0][0];
-        f64x4 t4 = {};
-        for (int i0 = jb; i0 < o; i0 += 4) {
-          const int i = i0 + g16;
-          t4 = __builtin_amdgcn_mfma_f64_16x16x4f64(sm.li[i][o + l16], sm.li[i][jb + l16], t4, 0, 0, 0);
-        }
-#pragma unroll
-        for (int x = 0; x < 4; ++x) T[(g16 + 4 * x) * 48 + jb + l16] = t4[x];
-        f64x4 u4 = {};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int m2 = 4 * ks + g16;
-          u4 = __builtin_amdgcn_mfma_f64_16x16x4f64(sL[l16][m2], T[m2 * 48 + jb + l16], u4, 0, 0, 0);
-        }
-#pragma unroll
-        for (int x = 0; x < 4; ++x) sm.li[o + g16 + 4 * x][jb + l16] = -u4[x];
-      }
-      for (int e = tid - 64; e < 256; e += 192) {
-        const int m = e >> 4, jj = e & 15;
-        if (jj < m) sm.li[o + m][o + jj] = sL[m][jj];
-      }
-      // trailing lower blocks (r, c), r >= c > j, but (j + 1, j + 1)
-      int idx = 0;
+      int item = 0;
       for (int r = j + 1; r < nb; ++r)
         for (int c = j + 1; c <= r; ++c) {
           if (r == j + 1 && c == j + 1) continue;
-          if (idx++ % 3 != w) continue;
-          f64x4 acc = {};
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const int q = 4 * ks + g16;
-            double wa = 0.0, wb = 0.0;
-#pragma unroll
-            for (int m = 0; m < 16; ++m) {
-              const double lq = sL[q][m];
-              wa = fma(sm.pp[16 * r + l16][o + m], lq, wa);
-              wb = fma(sm.pp[16 * c + l16][o + m], lq, wb);
-            }
-            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(wa * sm.rD[o + q], wb, acc, 0, 0, 0);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sm.pp[16 * r + g16 + 4 * i][16 * c + l16] -= acc[i];
+          if (item++ % 3 == wave - 1) ldl_trail(r, c, j);
         }
-      // the panel of L for rows past block j + 1, parked
-      for (int e = tid - 64; e < (kb - o2 - 16) * 16; e += 192) {
-        const int row = o2 + 16 + (e >> 4), q = e & 15;
-        double w2 = 0.0;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) w2 = fma(sm.pp[row][o + m], sL[q][m], w2);
-        sm.li[o + q][row] = w2 * sm.rD[o + q];
-      }
+      for (int c = 0; c < j; ++c)
+        if (item++ % 3 == wave - 1) ldl_linv(j, c, tmp);
     }
   }
   __syncthreads();
-  // clear the parked L; past k: identity rows and columns of L^-1, no pivot
-  for (int e = tid; e < kSB * kSB; e += kTeamThreads) {
-    const int r = e >> 6, c = e & 63;
-    if (c > r) sm.li[r][c] = 0.0;
-    else if (r >= k || c >= k) sm.li[r][c] = r == c ? 1.0 : 0.0;
+  // 16 x 16 blocks of sm.li: the parked panels (above the diagonal) cleared,
+  // blocks past the factored ones set to the identity (no pivots there);
+  // wave w takes block row w
+  {
+    const int lane = tid & 63, g16 = lane >> 4, l16 = lane & 15;
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+      if (wave < nb && bj <= wave) continue;  // written by the factorization
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int r = 16 * wave + g16 + 4 * x, c = 16 * bj + l16;
+        sm.li[r][c] = r == c ? 1.0 : 0.0;
+      }
+    }
   }
   if (tid >= k && tid < kSB) sm.rD[tid] = 0.0;
   __syncthreads();

@@ -558,6 +558,19 @@ __device__ __forceinline__ void team_sync(Team& tm) {
   team_wait(tm);
 }
 
+// Arrival at the next two barriers at once (the flag counts both), for a
+// member that writes nothing the others read between them; it then waits
+// for each of the two in turn.
+__device__ __forceinline__ void team_arrive2(Team& tm) {
+  if (tm.size == 1) return;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (!tm.fast) __threadfence();
+    __hip_atomic_store(tm.mine, tm.gen + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 __device__ __forceinline__ unsigned* uniform(unsigned* p) {
   const unsigned long long u = reinterpret_cast<unsigned long long>(p);
   const unsigned lo = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(u));
@@ -1532,8 +1545,14 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& team_ref, in
     }
     // all the lookahead member reads from S is in registers once these loads
     // land (the arrival waits for them): count it in at the first barrier now
-    // and form the block while the others update the tiles
-    team_arrive(tm);
+    // and form the block while the others update the tiles.  In a single-XCD
+    // team it also arrives at the closing barrier now: it writes nothing the
+    // tiles read, and the workers take its factors by the ready count, so the
+    // step closes when the tiles are done; elsewhere the others read the
+    // staged factors after the closing barrier, so it arrives there after
+    // publishing
+    if (tm.fast) team_arrive2(tm);
+    else team_arrive(tm);
     f64x4 wa[2][2] = {};
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
@@ -1654,13 +1673,13 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& team_ref, in
     }
   }
   tm.tbase += tasks + nw;
-  // A worker of a single-XCD team fetches the next step's L^-1 and 1/D as
-  // soon as the lookahead member has published them (normally before the
-  // worker's last tile is done), into registers while the closing barrier
-  // completes; L1-bypassing loads, since the same staging area was read a
-  // step ago.
+  // A tile worker arrives at the closing barrier as soon as its tiles are
+  // done.  In a single-XCD team it then fetches the next step's L^-1 and 1/D
+  // as soon as the lookahead member has published them (L1-bypassing loads,
+  // since the same staging area was read a step ago), while the barrier
+  // completes.
   const bool fetch = la && !me_la && tm.fast;
-  double nli[kSB * kSB / kTeamThreads], nrd = 0.0;
+  if (!me_la) team_arrive(tm);  // every wave of this member is past its tiles
   if (fetch) {
     if (tid == 0) {
       const uint64_t t0 = wall_clock64();
@@ -1677,6 +1696,7 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& team_ref, in
       }
     }
     __syncthreads();
+    double nli[kSB * kSB / kTeamThreads], nrd = 0.0;
 #pragma unroll
     for (int i = 0; i < kSB * kSB / kTeamThreads; ++i)
       nli[i] = __hip_atomic_load(&M.stage[kSB * kSB + tid + i * kTeamThreads], __ATOMIC_RELAXED,
@@ -1684,17 +1704,16 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& team_ref, in
     if (tid < kSB)
       nrd = __hip_atomic_load(&M.stage[2 * kSB * kSB + tid], __ATOMIC_RELAXED,
                               __HIP_MEMORY_SCOPE_AGENT);
-  }
-  team_sync(tm);
-  if (fetch) {  // this step's 1/D is no longer read: every wave is past its tiles
+    // this step's L^-1 and 1/D are no longer read (every wave is past its tiles)
 #pragma unroll
     for (int i = 0; i < kSB * kSB / kTeamThreads; ++i) {
       const int e = tid + i * kTeamThreads;
       sm.li[e >> 6][e & 63] = nli[i];
     }
     if (tid < kSB) sm.rD[tid] = nrd;
-    __syncthreads();
   }
+  if (me_la && !tm.fast) team_arrive(tm);
+  team_wait(tm);
   if (la) tm.pubs += 1;
   team_ref.gen = tm.gen;
   team_ref.tbase = tm.tbase;

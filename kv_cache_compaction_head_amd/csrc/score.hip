@@ -23,6 +23,8 @@
 // (keys as MFMA rows, queries as columns) so that each lane owns one query and
 // 16 keys: the per-query max/sum stays inside the lane, and the P fragment is
 // already the B operand of the O^T = V^T P^T product.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -277,6 +279,230 @@ __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
     }
     ml[(static_cast<size_t>(b) * nsplit + split) * n + q] = make_double2(mm, ll);
   }
+}
+
+// ---------------------------------------------------------------------------
+// K1 for bfloat16 input: the same partial (m, l) per (query, key split).
+//   * A wave owns 64 reference queries (two MFMA B-operand sets in
+//     registers), so every K fragment read from LDS feeds two MFMAs: one
+//     1 KB read per 64 MFMA cycles, half the LDS traffic of one query set.
+//   * K tiles go global -> LDS by DMA through a ring of three buffers, two
+//     tiles ahead of the one being computed; each thread's chunk offsets
+//     inside a tile are fixed, so a fetch is a scalar base plus precomputed
+//     32-bit offsets (clamped offsets only on the split's last, partial tile).
+//   * The tile loop is unrolled over the ring, so every LDS read address is
+//     one of NK registers plus an immediate offset.
+//   * Each query's running sum is kept against an integer reference k in
+//     the log2 domain: l = sum 2^(s log2e - k), with k = ceil(max s log2e)
+//     so every exponent is <= 0 (as accurate as against the exact maximum).
+//     A new maximum that moves k rescales l by an exact power of two
+//     (ldexp), so the loop needs no exp or exp2 of its own.
+// grid: score_grid over 256-query blocks, block 256.
+// ---------------------------------------------------------------------------
+constexpr int kBM1 = 256;  // reference queries per K1 workgroup (64 per wave)
+
+// The terms are exp2(fp32(s L - k)) with L = fp32(log2 e); the true ones
+// carry an extra factor 2^(s (log2 e - L)).  Taking that factor at the
+// reference score k ln2 for every term leaves a residual of relative size
+// |s - k ln2| * 1.3e-8 per term (negligible for the terms near the maximum
+// that carry the sum), and folds the rest into the stored reference:
+// m = k ln2 (1 + (log2 e - L) ln2).
+constexpr double kLn2Scaled =
+    0.6931471805599453 * (1.0 + (1.4426950408889634 - static_cast<double>(KVC_LOG2E)) *
+                                    0.6931471805599453);
+
+// running state of one query's partial log-sum-exp over its keys so far:
+// sum exp(s) = l 2^k, k an integer (float-valued; -inf before the first
+// live key), l in fp64 from fp32 sums of 16 terms.
+struct LseState {
+  float k = -INFINITY;
+  double l = 0.0;
+};
+
+// fold 16 scores of one query (one MFMA half tile) into its state; MASKED:
+// scores whose bit in `live` is clear count as -inf
+template <bool MASKED>
+__device__ __forceinline__ void lse_fold(LseState& s, f32x16& acc, unsigned live) {
+  float tmax = -INFINITY;
+  if constexpr (MASKED) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float v = ((live >> r) & 1u) ? acc[r] : -INFINITY;
+      acc[r] = v;
+      tmax = fmaxf(tmax, v);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, acc[r]);
+  }
+  const float kt = ceilf(tmax * KVC_LOG2E);
+  if (kt > s.k) {
+    s.l = s.k == -INFINITY ? 0.0 : ldexp(s.l, static_cast<int>(s.k - kt));
+    s.k = kt;
+  }
+  if (s.k != -INFINITY) {
+    float sum = __builtin_amdgcn_exp2f(fmaf(acc[0], KVC_LOG2E, -s.k));
+#pragma unroll
+    for (int r = 1; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -s.k));
+    s.l += static_cast<double>(sum);
+  }
+}
+
+template <int D, bool MASK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_score_lse_bf16(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const uint8_t* __restrict__ mask,
+    double2* __restrict__ ml, int n, int T, int keys_per_split, int nqb, int nsplit, int B,
+    int qg) {
+  constexpr int NK = D / 16, BN = 64, VEC = 8, CPR = D / VEC, NCH = BN * CPR / 256;
+  constexpr int TILE = BN * D;  // bf16 elements per LDS buffer
+  constexpr int NBUF = 3;
+  __shared__ __align__(16) bf16_t sK[NBUF * TILE];
+  __shared__ uint64_t sMb[NBUF];  // excluded keys of the tile, one bit per key
+  int qb, split, b;
+  if (!score_grid(nqb, nsplit, B, qb, split, b)) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, g = lane >> 5;
+  const int q0 = qb * kBM1 + wave * 64 + (lane & 31), q1 = q0 + 32;
+  const bf16_t* Qb = Q + static_cast<size_t>(b / qg) * n * D;
+  const bf16_t* Kb = K + static_cast<size_t>(b) * T * D;
+  const uint8_t* Mb = mask ? mask + static_cast<size_t>(b) * T : nullptr;
+
+  bf16x8 bq0[NK], bq1[NK];
+  load_q_frags<bf16_t, D>(bq0, Qb, q0, n, g);
+  load_q_frags<bf16_t, D>(bq1, Qb, q1, n, g);
+
+  // this thread's chunks of a tile: chunk c is slot threadIdx.x + 256 c of
+  // the tile, i.e. row r = slot / CPR, holding source chunk (slot % CPR) ^ swz(r)
+  uint32_t goff[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int idx = threadIdx.x + c * 256, r = idx / CPR, lc = (idx % CPR) ^ k_swz<CPR>(r);
+    goff[c] = static_cast<uint32_t>((r * D + lc * VEC) * 2);
+  }
+  // LDS element offset of this lane's MFMA A-operand chunk ks in half 0 of
+  // buffer 0 (row lane%32; half 1 adds 32 rows, buffer i adds i TILE)
+  uint32_t roff[NK];
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks) {
+    const int row = lane & 31;
+    roff[ks] = static_cast<uint32_t>(row * D + ((2 * ks + g) ^ k_swz<CPR>(row)) * VEC);
+  }
+
+  const int j0 = split * keys_per_split;
+  const int j1 = min(T, j0 + keys_per_split);
+  const int ntile = (j1 - j0 + BN - 1) / BN;
+  // tile at key jt with `valid` keys before the split end into buffer buf;
+  // rows at or past `valid` copy row valid-1 (their scores are masked).  The
+  // mask byte is loaded before the tile's copies and turned into the tile's
+  // bit set at the end of the current tile, so waiting for it never waits
+  // for the copies.
+  auto fetch = [&](int jt, int valid, int buf, uint8_t& mbyte) {
+    if (MASK && wave == 0) mbyte = Mb[min(jt + lane, j1 - 1)];
+    const char* base = reinterpret_cast<const char*>(Kb + static_cast<size_t>(jt) * D);
+    if (valid >= BN) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+        lds_copy16(base + goff[c], &sK[buf * TILE + (c * 256 + wave * 64) * VEC]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int idx = threadIdx.x + c * 256, r = idx / CPR;
+        const uint32_t o = goff[c] - static_cast<uint32_t>((r - min(r, valid - 1)) * D * 2);
+        lds_copy16(base + o, &sK[buf * TILE + (c * 256 + wave * 64) * VEC]);
+      }
+    }
+  };
+  LseState s0, s1;
+  // mask byte of the tile after the current one (loaded one tile earlier,
+  // with that tile's copies)
+  uint8_t mb_next = 0;
+  // one 32-key half of the tile in buffer CUR: both query sets' scores, then
+  // their folds
+  auto half = [&](auto cur_c, auto masked_c, int st, int valid, uint64_t mb) {
+    constexpr int cur = decltype(cur_c)::value;
+    const bf16_t* sb = sK + cur * TILE + st * 32 * D;
+    // nothing moves across: one half's K fragments live at a time
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 ka[NK];
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(sb + roff[ks]);
+    f32x16 a0{}, a1{};
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], bq0[ks], a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], bq1[ks], a1, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, NK, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NK, 0);
+    constexpr bool MASKED = decltype(masked_c)::value;
+    const unsigned live = MASKED ? live_rows(st, valid, mb, lane) : 0u;
+    lse_fold<MASKED>(s0, a0, live);
+    lse_fold<MASKED>(s1, a1, live);
+  };
+  auto tile = [&](auto cur_c, int it) {
+    constexpr int cur = decltype(cur_c)::value;
+    const int jt = j0 + it * BN, valid = j1 - jt;
+    uint8_t mb_new = 0;
+    if (it + 2 < ntile) fetch(jt + 2 * BN, valid - 2 * BN, (cur + 2) % NBUF, mb_new);
+    const uint64_t mb = MASK ? sMb[cur] : 0;
+    if (mb == 0 && valid >= BN) {
+      half(cur_c, std::false_type{}, 0, valid, mb);
+      half(cur_c, std::false_type{}, 1, valid, mb);
+    } else {
+      half(cur_c, std::true_type{}, 0, valid, mb);
+      half(cur_c, std::true_type{}, 1, valid, mb);
+    }
+    // publish the next tile's mask bits; the next tile's copies must have
+    // landed (the copies of the tile after it may stay in flight)
+    if (MASK && wave == 0 && it + 1 < ntile) {
+      const uint64_t pm = __ballot(mb_next != 0);
+      if (lane == 0) sMb[(cur + 1) % NBUF] = pm;
+    }
+    mb_next = mb_new;
+    if (it + 2 < ntile)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NCH) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  // prologue: tiles 0 and 1 in flight, tile 0's copies and mask bits ready
+  if (ntile > 0) {
+    uint8_t mb0 = 0;
+    fetch(j0, j1 - j0, 0, mb0);
+    if (ntile > 1) fetch(j0 + BN, j1 - j0 - BN, 1, mb_next);
+    if (MASK && wave == 0) {
+      const uint64_t pm = __ballot(mb0 != 0);
+      if (lane == 0) sMb[0] = pm;
+    }
+    if (ntile > 1)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NCH) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+  for (int it = 0; it < ntile; it += NBUF) {
+    tile(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < ntile) tile(std::integral_constant<int, 1>{}, it + 1);
+    if (it + 2 < ntile) tile(std::integral_constant<int, 2>{}, it + 2);
+  }
+  // lanes l and l+32 hold the same query over different keys: merge them
+  // (exactly, by powers of two) and store m = k ln2 with l
+  auto finish = [&](const LseState& s, int q) {
+    const float ko = __shfl_xor(s.k, 32);
+    const double lo = __shfl_xor(s.l, 32);
+    if (g == 0 && q < n) {
+      const float kk = fmaxf(s.k, ko);
+      double ll = 0.0, mm = -INFINITY;
+      if (kk != -INFINITY) {
+        if (s.k != -INFINITY) ll += ldexp(s.l, static_cast<int>(s.k - kk));
+        if (ko != -INFINITY) ll += ldexp(lo, static_cast<int>(ko - kk));
+        mm = static_cast<double>(kk) * kLn2Scaled;
+      }
+      ml[(static_cast<size_t>(b) * nsplit + split) * n + q] = make_double2(mm, ll);
+    }
+  };
+  finish(s0, q0);
+  finish(s1, q1);
 }
 
 // lse[b][q] (float64) from the split partials, merged in split order.
@@ -624,13 +850,23 @@ hipError_t launch_score(const void* Q, const void* K, const void* V, double2* ml
   const In* k = static_cast<const In*>(K);
   const In* v = static_cast<const In*>(V);
   prof_mark(0, false, st);
-  const dim3 g1(score_grid_size(nqb, nsplit1, B)), g2(score_grid_size(nqb, nsplit2, B));
-  if (mask)
-    hipLaunchKernelGGL((k_score_lse<In, D, true>), g1, dim3(256), 0, st, q, k, mask, ml, n, T, kps1,
-                       nqb, nsplit1, B, qg);
-  else
-    hipLaunchKernelGGL((k_score_lse<In, D, false>), g1, dim3(256), 0, st, q, k, mask, ml, n, T,
-                       kps1, nqb, nsplit1, B, qg);
+  const int nqb1 = sizeof(In) == 2 ? (n + kBM1 - 1) / kBM1 : nqb;
+  const dim3 g1(score_grid_size(nqb1, nsplit1, B)), g2(score_grid_size(nqb, nsplit2, B));
+  if constexpr (sizeof(In) == 2) {
+    if (mask)
+      hipLaunchKernelGGL((k_score_lse_bf16<D, true>), g1, dim3(256), 0, st, q, k, mask, ml, n, T,
+                         kps1, nqb1, nsplit1, B, qg);
+    else
+      hipLaunchKernelGGL((k_score_lse_bf16<D, false>), g1, dim3(256), 0, st, q, k, mask, ml, n,
+                         T, kps1, nqb1, nsplit1, B, qg);
+  } else {
+    if (mask)
+      hipLaunchKernelGGL((k_score_lse<In, D, true>), g1, dim3(256), 0, st, q, k, mask, ml, n, T,
+                         kps1, nqb, nsplit1, B, qg);
+    else
+      hipLaunchKernelGGL((k_score_lse<In, D, false>), g1, dim3(256), 0, st, q, k, mask, ml, n, T,
+                         kps1, nqb, nsplit1, B, qg);
+  }
   prof_mark(0, true, st);
   hipLaunchKernelGGL(k_lse_merge, dim3((4 * B * n + 255) / 256), dim3(256), 0, st, ml, lse, n,
                      nsplit1, B);

@@ -108,7 +108,7 @@ __device__ __forceinline__ void lds_copy16(const void* src, void* dst) {
 // with CPR chunks per row: the 16 rows an MFMA operand read takes at once
 // land in 16 distinct 16-byte bank groups of a 256-byte bank row.
 template <int CPR>
-__device__ __forceinline__ int k_swz(int r) {
+__host__ __device__ constexpr int k_swz(int r) {
   static_assert(CPR == 8 || CPR == 16, "16-byte chunks per row");
   return (r / (16 / CPR)) & (CPR - 1);
 }
@@ -285,18 +285,23 @@ __global__ __launch_bounds__(256) void k_score_lse(const In* __restrict__ Q,
 // K1 for bfloat16 input: the same partial (m, l) per (query, key split).
 //   * A wave owns 64 reference queries (two MFMA B-operand sets in
 //     registers), so every K fragment read from LDS feeds two MFMAs: one
-//     1 KB read per 64 MFMA cycles, half the LDS traffic of one query set.
-//   * K tiles go global -> LDS by DMA through a ring of three buffers, two
-//     tiles ahead of the one being computed; each thread's chunk offsets
-//     inside a tile are fixed, so a fetch is a scalar base plus precomputed
-//     32-bit offsets (clamped offsets only on the split's last, partial tile).
-//   * The tile loop is unrolled over the ring, so every LDS read address is
-//     one of NK registers plus an immediate offset.
+//     1 KB read per 64 MFMA cycles.
+//   * K tiles of 128 keys go global -> LDS by DMA, double-buffered one tile
+//     ahead; each thread's chunk offsets inside a tile are fixed, so a fetch
+//     is a scalar base plus precomputed 32-bit offsets.
 //   * Each query's running sum is kept against an integer reference k in
 //     the log2 domain: l = sum 2^(s log2e - k), with k = ceil(max s log2e)
 //     so every exponent is <= 0 (as accurate as against the exact maximum).
 //     A new maximum that moves k rescales l by an exact power of two
-//     (ldexp), so the loop needs no exp or exp2 of its own.
+//     (ldexp), so the fold of 16 scores into (k, l) has no branch and no exp
+//     or exp2 of its own.
+//   * Software pipeline over halves of 32 keys: the MFMAs
+//     of half h are issued interleaved with the fold of half h-1 (whose
+//     scores are complete), and the LDS reads of half h+2 follow the MFMAs
+//     that free their registers, so one wave keeps the matrix pipe and the
+//     VALU busy at once.  A tile with an excluded key or past the split end
+//     takes a plain path: pending fold, then its halves one by one with the
+//     exclusions applied.
 // grid: score_grid over 256-query blocks, block 256.
 // ---------------------------------------------------------------------------
 constexpr int kBM1 = 256;  // reference queries per K1 workgroup (64 per wave)
@@ -319,45 +324,41 @@ struct LseState {
   double l = 0.0;
 };
 
-// fold 16 scores of one query (one MFMA half tile) into its state; MASKED:
-// scores whose bit in `live` is clear count as -inf
-template <bool MASKED>
-__device__ __forceinline__ void lse_fold(LseState& s, f32x16& acc, unsigned live) {
+// fold 16 scores of one query (one MFMA half tile; -inf for excluded keys)
+// into its state, without branches: k' = max(k, ceil(max s log2e)),
+// l' = l 2^(k - k') + sum 2^(s log2e - k').  A state with k = -inf has
+// l = 0 and rescales to 0; k' = -inf means every score is -inf, whose terms
+// vanish against the stand-in reference 0.
+__device__ __forceinline__ void lse_fold(LseState& s, const f32x16& acc) {
   float tmax = -INFINITY;
-  if constexpr (MASKED) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float v = ((live >> r) & 1u) ? acc[r] : -INFINITY;
-      acc[r] = v;
-      tmax = fmaxf(tmax, v);
-    }
-  } else {
+  for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, acc[r]);
+  const float kn = fmaxf(s.k, ceilf(tmax * KVC_LOG2E));
+  const float d = fmaxf(s.k - kn, -1024.f);  // (-inf) - (-inf) is NaN: max gives -1024
+  const float kref = kn == -INFINITY ? 0.f : kn;
+  float sum = __builtin_amdgcn_exp2f(fmaf(acc[0], KVC_LOG2E, -kref));
 #pragma unroll
-    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, acc[r]);
-  }
-  const float kt = ceilf(tmax * KVC_LOG2E);
-  if (kt > s.k) {
-    s.l = s.k == -INFINITY ? 0.0 : ldexp(s.l, static_cast<int>(s.k - kt));
-    s.k = kt;
-  }
-  if (s.k != -INFINITY) {
-    float sum = __builtin_amdgcn_exp2f(fmaf(acc[0], KVC_LOG2E, -s.k));
+  for (int r = 1; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -kref));
+  s.l = ldexp(s.l, static_cast<int>(d)) + static_cast<double>(sum);
+  s.k = kn;
+}
+
+// scores whose bit in `live` is clear become -inf
+__device__ __forceinline__ void mask_scores(f32x16& acc, unsigned live) {
 #pragma unroll
-    for (int r = 1; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -s.k));
-    s.l += static_cast<double>(sum);
-  }
+  for (int r = 0; r < 16; ++r) acc[r] = ((live >> r) & 1u) ? acc[r] : -INFINITY;
 }
 
 template <int D, bool MASK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_score_lse_bf16(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_score_lse_bf16(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const uint8_t* __restrict__ mask,
     double2* __restrict__ ml, int n, int T, int keys_per_split, int nqb, int nsplit, int B,
     int qg) {
-  constexpr int NK = D / 16, BN = 64, VEC = 8, CPR = D / VEC, NCH = BN * CPR / 256;
+  constexpr int NK = D / 16, BN = 128, NH = BN / 32, VEC = 8, CPR = D / VEC;
+  constexpr int NCH = BN * CPR / 256;
   constexpr int TILE = BN * D;  // bf16 elements per LDS buffer
-  constexpr int NBUF = 3;
-  __shared__ __align__(16) bf16_t sK[NBUF * TILE];
-  __shared__ uint64_t sMb[NBUF];  // excluded keys of the tile, one bit per key
+  __shared__ __align__(16) bf16_t sK[2 * TILE];
+  __shared__ uint64_t sMb[2][2];  // excluded keys of the tile, one bit per key
   int qb, split, b;
   if (!score_grid(nqb, nsplit, B, qb, split, b)) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -372,15 +373,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   load_q_frags<bf16_t, D>(bq1, Qb, q1, n, g);
 
   // this thread's chunks of a tile: chunk c is slot threadIdx.x + 256 c of
-  // the tile, i.e. row r = slot / CPR, holding source chunk (slot % CPR) ^ swz(r)
-  uint32_t goff[NCH];
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int idx = threadIdx.x + c * 256, r = idx / CPR, lc = (idx % CPR) ^ k_swz<CPR>(r);
-    goff[c] = static_cast<uint32_t>((r * D + lc * VEC) * 2);
-  }
+  // the tile, i.e. row r0 + c (256 / CPR) (r0 = threadIdx.x / CPR), holding
+  // source chunk (threadIdx.x % CPR) ^ swz(r0): the swizzle is the same for
+  // every c, so chunk c sits 256 * 16 bytes after chunk 0
+  static_assert(k_swz<CPR>(0) == 0 && 256 % CPR == 0, "chunk rows");
+  const int r0 = threadIdx.x / CPR;
+  const uint32_t goff = static_cast<uint32_t>(
+      (r0 * D + ((threadIdx.x % CPR) ^ k_swz<CPR>(r0)) * VEC) * 2);
   // LDS element offset of this lane's MFMA A-operand chunk ks in half 0 of
-  // buffer 0 (row lane%32; half 1 adds 32 rows, buffer i adds i TILE)
+  // buffer 0 (row lane%32; half h adds 32 h rows, buffer 1 adds TILE)
   uint32_t roff[NK];
 #pragma unroll
   for (int ks = 0; ks < NK; ++ks) {
@@ -392,99 +393,133 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const int j1 = min(T, j0 + keys_per_split);
   const int ntile = (j1 - j0 + BN - 1) / BN;
   // tile at key jt with `valid` keys before the split end into buffer buf;
-  // rows at or past `valid` copy row valid-1 (their scores are masked).  The
-  // mask byte is loaded before the tile's copies and turned into the tile's
-  // bit set at the end of the current tile, so waiting for it never waits
-  // for the copies.
-  auto fetch = [&](int jt, int valid, int buf, uint8_t& mbyte) {
-    if (MASK && wave == 0) mbyte = Mb[min(jt + lane, j1 - 1)];
+  // rows at or past `valid` copy row valid-1 (their scores are masked).
+  // The mask bytes are loaded before the copies and turned into the tile's
+  // bit sets at the end of the current tile.
+  uint8_t mbyte[2] = {0, 0};
+  auto fetch = [&](int jt, int valid, int buf) {
+    if (MASK && wave == 0) {
+      mbyte[0] = Mb[min(jt + lane, j1 - 1)];
+      mbyte[1] = Mb[min(jt + 64 + lane, j1 - 1)];
+    }
     const char* base = reinterpret_cast<const char*>(Kb + static_cast<size_t>(jt) * D);
     if (valid >= BN) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
-        lds_copy16(base + goff[c], &sK[buf * TILE + (c * 256 + wave * 64) * VEC]);
+        lds_copy16(base + goff + c * 4096, &sK[buf * TILE + (c * 256 + wave * 64) * VEC]);
     } else {
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        const int idx = threadIdx.x + c * 256, r = idx / CPR;
-        const uint32_t o = goff[c] - static_cast<uint32_t>((r - min(r, valid - 1)) * D * 2);
+        const int r = r0 + c * (256 / CPR);
+        const uint32_t o = goff + c * 4096 - static_cast<uint32_t>((r - min(r, valid - 1)) * D * 2);
         lds_copy16(base + o, &sK[buf * TILE + (c * 256 + wave * 64) * VEC]);
       }
     }
   };
+  auto publish_mask = [&](int buf) {
+    if (MASK && wave == 0) {
+      const uint64_t m0 = __ballot(mbyte[0] != 0), m1 = __ballot(mbyte[1] != 0);
+      if (lane == 0) {
+        sMb[buf][0] = m0;
+        sMb[buf][1] = m1;
+      }
+    }
+  };
   LseState s0, s1;
-  // mask byte of the tile after the current one (loaded one tile earlier,
-  // with that tile's copies)
-  uint8_t mb_next = 0;
-  // one 32-key half of the tile in buffer CUR: both query sets' scores, then
-  // their folds
-  auto half = [&](auto cur_c, auto masked_c, int st, int valid, uint64_t mb) {
-    constexpr int cur = decltype(cur_c)::value;
-    const bf16_t* sb = sK + cur * TILE + st * 32 * D;
-    // nothing moves across: one half's K fragments live at a time
-    __builtin_amdgcn_sched_barrier(0);
-    bf16x8 ka[NK];
+  // K fragments of the next half (read while the current half's MFMAs
+  // release them), scores of the half whose fold is pending (-inf: none)
+  bf16x8 F[NK];
+  f32x16 A0[2], A1[2];
+  A0[1] = f32x16{} - INFINITY;
+  A1[1] = A0[1];
+  auto read_half = [&](int buf, int h, bf16x8* f) {
+    const bf16_t* sb = sK + buf * TILE + h * 32 * D;
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(sb + roff[ks]);
-    f32x16 a0{}, a1{};
+    for (int ks = 0; ks < NK; ++ks) f[ks] = *reinterpret_cast<const bf16x8*>(sb + roff[ks]);
+  };
+  // MFMAs of one half from f into (a0, a1), interleaved with the fold of
+  // (p0, p1); then, if `next` >= 0, the reads of half `next` into f
+  auto step = [&](bf16x8* f, f32x16& a0, f32x16& a1, const f32x16& p0, const f32x16& p1,
+                  int buf, int next) {
+    a0 = f32x16{};
+    a1 = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
-      a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], bq0[ks], a0, 0, 0, 0);
-      a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], bq1[ks], a1, 0, 0, 0);
+      a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[ks], bq0[ks], a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[ks], bq1[ks], a1, 0, 0, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, NK, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NK, 0);
-    constexpr bool MASKED = decltype(masked_c)::value;
-    const unsigned live = MASKED ? live_rows(st, valid, mb, lane) : 0u;
-    lse_fold<MASKED>(s0, a0, live);
-    lse_fold<MASKED>(s1, a1, live);
+    lse_fold(s0, p0);
+    lse_fold(s1, p1);
+    if (next >= 0) read_half(buf, next, f);
+    // per fragment: its two MFMAs with fold arithmetic between them, then
+    // the LDS read that reuses its registers for half `next`
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
   };
   auto tile = [&](auto cur_c, int it) {
     constexpr int cur = decltype(cur_c)::value;
     const int jt = j0 + it * BN, valid = j1 - jt;
-    uint8_t mb_new = 0;
-    if (it + 2 < ntile) fetch(jt + 2 * BN, valid - 2 * BN, (cur + 2) % NBUF, mb_new);
-    const uint64_t mb = MASK ? sMb[cur] : 0;
-    if (mb == 0 && valid >= BN) {
-      half(cur_c, std::false_type{}, 0, valid, mb);
-      half(cur_c, std::false_type{}, 1, valid, mb);
+    if (it + 1 < ntile) fetch(jt + BN, valid - BN, cur ^ 1);
+    const uint64_t mb0 = MASK ? sMb[cur][0] : 0, mb1 = MASK ? sMb[cur][1] : 0;
+    if ((mb0 | mb1) == 0 && valid >= BN) {
+      // halves 0..3: half 0's frags are in flight on entry
+      step(F, A0[0], A1[0], A0[1], A1[1], cur, 1);
+      step(F, A0[1], A1[1], A0[0], A1[0], cur, 2);
+      step(F, A0[0], A1[0], A0[1], A1[1], cur, 3);
+      step(F, A0[1], A1[1], A0[0], A1[0], cur, -1);
     } else {
-      half(cur_c, std::true_type{}, 0, valid, mb);
-      half(cur_c, std::true_type{}, 1, valid, mb);
+      // the pending fold, then halves one at a time with the exclusions
+      // applied; the last half's masked scores become the pending fold
+      lse_fold(s0, A0[1]);
+      lse_fold(s1, A1[1]);
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 f[NK];
+        read_half(cur, h, f);
+        f32x16 a0{}, a1{};
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) {
+          a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[ks], bq0[ks], a0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[ks], bq1[ks], a1, 0, 0, 0);
+        }
+        const unsigned live = live_rows(h & 1, valid - 64 * (h >> 1), h < 2 ? mb0 : mb1, lane);
+        mask_scores(a0, live);
+        mask_scores(a1, live);
+        if (h + 1 < NH) {
+          lse_fold(s0, a0);
+          lse_fold(s1, a1);
+        } else {
+          A0[1] = a0;
+          A1[1] = a1;
+        }
+      }
     }
-    // publish the next tile's mask bits; the next tile's copies must have
-    // landed (the copies of the tile after it may stay in flight)
-    if (MASK && wave == 0 && it + 1 < ntile) {
-      const uint64_t pm = __ballot(mb_next != 0);
-      if (lane == 0) sMb[(cur + 1) % NBUF] = pm;
-    }
-    mb_next = mb_new;
-    if (it + 2 < ntile)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NCH) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // the next tile's copies and mask bits, then its first half's frags
+    if (it + 1 < ntile) publish_mask(cur ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (it + 1 < ntile) read_half(cur ^ 1, 0, F);
   };
-  // prologue: tiles 0 and 1 in flight, tile 0's copies and mask bits ready
   if (ntile > 0) {
-    uint8_t mb0 = 0;
-    fetch(j0, j1 - j0, 0, mb0);
-    if (ntile > 1) fetch(j0 + BN, j1 - j0 - BN, 1, mb_next);
-    if (MASK && wave == 0) {
-      const uint64_t pm = __ballot(mb0 != 0);
-      if (lane == 0) sMb[0] = pm;
-    }
-    if (ntile > 1)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NCH) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    fetch(j0, j1 - j0, 0);
+    publish_mask(0);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int it = 0; it < ntile; it += NBUF) {
+  if (ntile > 0) read_half(0, 0, F);
+  for (int it = 0; it < ntile; it += 2) {
     tile(std::integral_constant<int, 0>{}, it);
     if (it + 1 < ntile) tile(std::integral_constant<int, 1>{}, it + 1);
-    if (it + 2 < ntile) tile(std::integral_constant<int, 2>{}, it + 2);
   }
+  lse_fold(s0, A0[1]);
+  lse_fold(s1, A1[1]);
   // lanes l and l+32 hold the same query over different keys: merge them
   // (exactly, by powers of two) and store m = k ln2 with l
   auto finish = [&](const LseState& s, int q) {
@@ -804,6 +839,215 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
   }
 }
 
+// ---------------------------------------------------------------------------
+// K2 for bfloat16 input: p = exp(s - lse); importance partials and partial O.
+// grid (score_grid over 128-query blocks), block 256; outputs as k_expweight.
+//   * K and V tiles both go global -> LDS by DMA, in the same XOR-swizzled
+//     row layout, double-buffered, one tile ahead.
+//   * The A operand of O^T += V^T P^T (32 value columns x 16 keys) is read
+//     straight from the key-major V tile with LDS transpose reads
+//     (ds_read_b64_tr_b16): in each 16-lane group, output lane i, element e
+//     comes from the 8-byte read of lane 4e + i/4 at position i % 4, so a lane
+//     whose group reads 4 consecutive key rows gets 4 consecutive keys of one
+//     value column.  Two such reads give the 8 keys of a lane's k-slots, in
+//     the order the score accumulator holds them (keys 4g..4g+3 and
+//     8+4g..8+4g+3 of each 16-key step, g = lane / 32), so P needs no
+//     permutation and V no transposed copy.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x4 lds_read_tr16(const bf16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (__attribute__((address_space(3))) bf16x4*)(p));
+}
+
+template <int D, bool RMS, bool MASK>
+__global__ __launch_bounds__(256) void k_expweight_bf16(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const double* __restrict__ lse, const uint8_t* __restrict__ mask, float* __restrict__ Opart,
+    float* __restrict__ imp_part, int n, int T, int keys_per_split, int nqb, int nsplit, int B,
+    int qg) {
+  constexpr int NK = D / 16, BN = 64, VEC = 8, CPR = D / VEC, NCH = BN * CPR / 256, ND = D / 32;
+  constexpr int TILE = BN * D;  // bf16 elements per LDS buffer
+  __shared__ __align__(16) bf16_t sK[2 * TILE];
+  __shared__ __align__(16) bf16_t sV[2 * TILE];
+  __shared__ float sImp[2][kWaves][BN];
+  __shared__ uint64_t sMb[2];  // excluded keys of the tile, one bit per key
+
+  int qb, split, b;
+  if (!score_grid(nqb, nsplit, B, qb, split, b)) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, g = lane >> 5;
+  const int q = qb * kBM + wave * 32 + (lane & 31);
+  const bf16_t* Qb = Q + static_cast<size_t>(b / qg) * n * D;
+  const bf16_t* Kb = K + static_cast<size_t>(b) * T * D;
+  const bf16_t* Vb = V + static_cast<size_t>(b) * T * D;
+  const uint8_t* Mb = mask ? mask + static_cast<size_t>(b) * T : nullptr;
+
+  bf16x8 bq[NK];
+  load_q_frags<bf16_t, D>(bq, Qb, q, n, g);
+  // lse*log2e as an unevaluated fp32 pair, so exp2(s*log2e - hi - lo) keeps
+  // the float64 log-sum-exp's accuracy (a query past n gets an infinite lse:
+  // its zero scores give p = 0 with no per-element test)
+  const double l2 = q < n ? lse[static_cast<size_t>(b) * n + q] * 1.4426950408889634 : 0.0;
+  const float ml2 = q < n ? static_cast<float>(l2) : INFINITY;
+  const float ml2lo = q < n ? static_cast<float>(l2 - static_cast<double>(ml2)) : 0.f;
+
+  // this thread's chunks of a tile (K and V alike): chunk c is slot
+  // threadIdx.x + 256 c, i.e. row r = slot / CPR holding source chunk
+  // (slot % CPR) ^ swz(r)
+  uint32_t goff[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int idx = threadIdx.x + c * 256, r = idx / CPR, lc = (idx % CPR) ^ k_swz<CPR>(r);
+    goff[c] = static_cast<uint32_t>((r * D + lc * VEC) * 2);
+  }
+  // K A-operand chunk ks of half 0 (row lane%32; half 1 adds 32 rows)
+  uint32_t roff[NK];
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks) {
+    const int row = lane & 31;
+    roff[ks] = static_cast<uint32_t>(row * D + ((2 * ks + g) ^ k_swz<CPR>(row)) * VEC);
+  }
+  // V transpose reads for value tile dt, part r2 (keys +0 / +8) of 16-key
+  // step 0 (step kk adds 16 rows): this lane reads key row
+  // 4 (G/2) + 8 r2 + j/4 at value column 32 dt + 16 (G%2) + 4 (j%4), where
+  // G = lane / 16 and j = lane % 16
+  uint32_t voff[ND][2];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int r2 = 0; r2 < 2; ++r2) {
+      const int G = lane >> 4, j = lane & 15;
+      const int row = 4 * (G >> 1) + 8 * r2 + (j >> 2);
+      const int col = 32 * dt + 16 * (G & 1) + 4 * (j & 3);
+      const int pos = (col / VEC) ^ k_swz<CPR>(row);
+      voff[dt][r2] = static_cast<uint32_t>(row * D + pos * VEC + col % VEC);
+    }
+
+  f32x16 accO[ND];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) accO[dt] = f32x16{};
+
+  const int j0 = split * keys_per_split;
+  const int j1 = min(T, j0 + keys_per_split);
+  const int ntile = (j1 - j0 + BN - 1) / BN;
+  // tile at key jt with `valid` keys before the split end into buffer buf;
+  // rows at or past `valid` copy row valid-1 (their p is masked to zero)
+  auto fetch = [&](int jt, int valid, int buf, uint8_t& mbyte) {
+    if (MASK && wave == 0) mbyte = Mb[min(jt + lane, j1 - 1)];
+    const char* kb = reinterpret_cast<const char*>(Kb + static_cast<size_t>(jt) * D);
+    const char* vb = reinterpret_cast<const char*>(Vb + static_cast<size_t>(jt) * D);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      uint32_t o = goff[c];
+      if (valid < BN) {
+        const int r = (threadIdx.x + c * 256) / CPR;
+        o -= static_cast<uint32_t>((r - min(r, valid - 1)) * D * 2);
+      }
+      const int dst = buf * TILE + (c * 256 + wave * 64) * VEC;
+      lds_copy16(kb + o, &sK[dst]);
+      lds_copy16(vb + o, &sV[dst]);
+    }
+  };
+  uint8_t mb_next = 0;
+  auto tile = [&](auto cur_c, int it) {
+    constexpr int cur = decltype(cur_c)::value;
+    const int jt = j0 + it * BN, valid = j1 - jt;
+    if (it + 1 < ntile) fetch(jt + BN, valid - BN, cur ^ 1, mb_next);
+    const bf16_t* sk = sK + cur * TILE;
+    const bf16_t* sv = sV + cur * TILE;
+    const uint64_t mb = MASK ? sMb[cur] : 0;
+    const bool whole = mb == 0 && valid >= BN;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 ka[NK];
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks)
+        ka[ks] = *reinterpret_cast<const bf16x8*>(sk + roff[ks] + st * 32 * D);
+      f32x16 acc{};
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], bq[ks], acc, 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, NK, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NK, 0);
+      if (whole) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2) - ml2lo);
+      } else {
+        const unsigned live = live_rows(st, valid, mb, lane);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2) - ml2lo);
+          acc[r] = ((live >> r) & 1u) ? e : 0.f;
+        }
+      }
+      {
+        const float tot = half_wave_rowsum<RMS>(acc, lane);
+        const int r = ((lane >> 4) & 1) * 8 + ((lane >> 3) & 1) * 4 + ((lane >> 2) & 1) * 2 +
+                      ((lane >> 1) & 1);
+        if ((lane & 1) == 0) sImp[cur][wave][st * 32 + mfma32_row(r, lane)] = tot;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = acc[h * 8 + e];
+          const __bf16 ph = static_cast<__bf16>(p);
+          hi[e] = ph;
+          lo[e] = static_cast<__bf16>(p - static_cast<float>(ph));
+        }
+        const int kk = 2 * st + h;  // 16-key step of the tile
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+          const bf16x4 v0 = lds_read_tr16(sv + voff[dt][0] + kk * 16 * D);
+          const bf16x4 v1 = lds_read_tr16(sv + voff[dt][1] + kk * 16 * D);
+          const bf16x8 a = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+          accO[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, hi, accO[dt], 0, 0, 0);
+          accO[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, lo, accO[dt], 0, 0, 0);
+        }
+      }
+    }
+    // publish the next tile's mask bits; its copies must have landed
+    if (MASK && wave == 0 && it + 1 < ntile) {
+      const uint64_t pm = __ballot(mb_next != 0);
+      if (lane == 0) sMb[cur ^ 1] = pm;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x < BN && static_cast<int>(threadIdx.x) < valid) {
+      const int t = threadIdx.x;
+      imp_part[(static_cast<size_t>(b) * nqb + qb) * T + jt + t] =
+          ((sImp[cur][0][t] + sImp[cur][1][t]) + sImp[cur][2][t]) + sImp[cur][3][t];
+    }
+  };
+  if (ntile > 0) {
+    uint8_t mb0 = 0;
+    fetch(j0, j1 - j0, 0, mb0);
+    if (MASK && wave == 0) {
+      const uint64_t pm = __ballot(mb0 != 0);
+      if (lane == 0) sMb[0] = pm;
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int it = 0; it < ntile; it += 2) {
+    tile(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < ntile) tile(std::integral_constant<int, 1>{}, it + 1);
+  }
+  if (q < n) {
+    float* Ob = Opart + (static_cast<size_t>(b) * nsplit + split) * D * n;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        Ob[static_cast<size_t>(dt * 32 + mfma32_row(r, lane)) * n + q] = accO[dt][r];
+  }
+}
+
 // O[b][q][dd] = sum over splits (in order) of Opart[b][s][dd][q]; 32x32 tiles
 // transposed through LDS.  grid (ceil(n/32), D/32, B), block (32, 8).
 __global__ void k_o_reduce(const float* __restrict__ Opart, float* __restrict__ O, int n, int D,
@@ -871,9 +1115,13 @@ hipError_t launch_score(const void* Q, const void* K, const void* V, double2* ml
   hipLaunchKernelGGL(k_lse_merge, dim3((4 * B * n + 255) / 256), dim3(256), 0, st, ml, lse, n,
                      nsplit1, B);
   prof_mark(1, false, st);
-#define KVC_K2(R, M)                                                                           \
-  hipLaunchKernelGGL((k_expweight<In, D, R, M>), g2, dim3(256), 0, st, q, k, v, lse, mask, Opart, \
-                     imp_part, n, T, kps2, nqb, nsplit2, B, qg)
+#define KVC_K2(R, M)                                                                          \
+  if constexpr (sizeof(In) == 2)                                                              \
+    hipLaunchKernelGGL((k_expweight_bf16<D, R, M>), g2, dim3(256), 0, st, q, k, v, lse, mask,  \
+                       Opart, imp_part, n, T, kps2, nqb, nsplit2, B, qg);                     \
+  else                                                                                        \
+    hipLaunchKernelGGL((k_expweight<In, D, R, M>), g2, dim3(256), 0, st, q, k, v, lse, mask,   \
+                       Opart, imp_part, n, T, kps2, nqb, nsplit2, B, qg)
   if (rms) {
     if (mask) KVC_K2(true, true);
     else KVC_K2(true, false);

@@ -76,6 +76,16 @@ extern "C" {
 #define KVC_STATUS_PROTECT      32  /* kvc_compact_protected: more than t - 1
                                        keys were marked; only the first t - 1
                                        (by position) were kept as protected    */
+#define KVC_STATUS_RIDGE_RAISED 64  /* a failed pivot in the bias NNLS made the
+                                       head restart with the ridge raised
+                                       tenfold (relative ridge max(10^e ridge,
+                                       10^(e-1) 1e-9) at the e-th raise, at
+                                       most 3); the count e is in bits 8-9
+                                       (KVC_STATUS_RAISES), the values are
+                                       fitted with the raised ridge, and
+                                       KVC_STATUS_NOT_SPD remains only if the
+                                       third raise still failed                */
+#define KVC_STATUS_RAISES(s)    (((s) >> 8) & 3)
 
 typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype_t;
 typedef enum { KVC_AGG_RMS = 0, KVC_AGG_MEAN = 1 } kvc_agg_t;

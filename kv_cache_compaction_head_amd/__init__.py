@@ -12,13 +12,14 @@ import dataclasses
 
 from . import _lib
 from ._lib import (KVC_AGG_MEAN, KVC_AGG_RMS, KVC_BF16, KVC_F32, STATUS_NNLS_CAP,
-                   STATUS_NONFINITE, STATUS_NOT_SPD, STATUS_SYNC_TIMEOUT, Params, load,
+                   STATUS_NONFINITE, STATUS_NOT_SPD, STATUS_RIDGE_RAISED, STATUS_SYNC_TIMEOUT,
+                   Params, load, status_raises,
                    make_params, set_wait_limit, strerror, workspace_bytes,
                    workspace_bytes_chunked, workspace_bytes_omp, workspace_layout)
 
 __all__ = ["compact", "compact_noalloc", "compact_omp", "compact_chunked", "compact_ragged", "compact_protected", "attend", "fit", "Compacted", "intermediates", "load", "make_params",
            "workspace_bytes", "workspace_bytes_chunked", "workspace_bytes_omp", "workspace_layout", "strerror", "Params",
-           "set_wait_limit"]
+           "set_wait_limit", "status_raises", "STATUS_RIDGE_RAISED"]
 
 
 @dataclasses.dataclass

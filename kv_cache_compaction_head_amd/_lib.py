@@ -14,7 +14,12 @@ NOALLOC_SCRATCH_BYTES = 64 << 20  # KVC_NOALLOC_SCRATCH_BYTES
 KVC_F32, KVC_BF16 = 0, 1
 KVC_AGG_RMS, KVC_AGG_MEAN = 0, 1
 (STATUS_NOT_SPD, STATUS_NNLS_CAP, STATUS_NONFINITE, STATUS_SYNC_TIMEOUT, STATUS_BUDGET,
- STATUS_PROTECT) = 1, 2, 4, 8, 16, 32
+ STATUS_PROTECT, STATUS_RIDGE_RAISED) = 1, 2, 4, 8, 16, 32, 64
+
+
+def status_raises(status: int) -> int:
+    """Number of tenfold ridge raises recorded in a status word (bits 8-9)."""
+    return (int(status) >> 8) & 3
 
 EXPORTS = ("kvc_params_default", "kvc_workspace_bytes", "kvc_compact", "kvc_compact_noalloc",
            "kvc_fit",

@@ -403,8 +403,8 @@ __device__ int block_count(int v, int* sh) {
 
 // Bias system of head b in its sweep matrix (right-hand side in row 0,
 // variables from row 64; see the sweep engine below): the Gram M = P_S^T P_S
-// is already in the variable block.  k_bias_lam: lam_w = ridge * tr(M) / t
-// (grid (B), block 1024).  k_bias_prep then adds lam_w to the diagonal,
+// is already in the variable block.  k_bias_lam: lam_w = ridge * tr(M) / t,
+// and the scale tr(M) / t beside it for a raised ridge (grid (B), block 1024).  k_bias_prep then adds lam_w to the diagonal,
 // stores c = P_S^T 1 + lam_w in column 0 of the variable rows and clears
 // columns 1..63 (unused right-hand-side slots), one wave per row (grid
 // (ceil(t/16), B), block 1024).
@@ -420,7 +420,10 @@ __global__ __launch_bounds__(1024) void k_bias_lam(const double* __restrict__ S,
   for (int a = threadIdx.x; a < t; a += blockDim.x)
     tr += Sb[static_cast<size_t>(kSB + a) * ld + kSB + a];
   tr = block_sum(tr, sh);
-  if (threadIdx.x == 0) lam[2 * b] = ridge * tr / t;
+  if (threadIdx.x == 0) {
+    lam[2 * b] = ridge * tr / t;
+    lam[2 * b + 1] = tr / t;
+  }
 }
 __global__ __launch_bounds__(1024) void k_bias_prep(double* __restrict__ S, size_t sS, int ld,
                                                     const double* __restrict__ colsum,
@@ -697,6 +700,7 @@ struct __align__(16) SweepSmem {
   double rD[kSB];                  // 1 / D (0 past k)
   double sV[kSB][17];              // LDL scratch: a 16 x 17 block per wave
   double sgn[kSB];                 // s_q
+  double dg[kSB];                  // pivot q's variable before any sweep (0: none)
   int piv[kSB];                    // matrix row of pivot q
   double sgn2[kSB];                // the next step's pivots (lookahead)
   int piv2[kSB];
@@ -723,6 +727,9 @@ struct SweepMat {
   gdouble* V;      // [rows][64] A[:, P] B
   gdouble* stage;  // [kStage] L^-1 (at kSB*kSB) and 1/D (at 2*kSB*kSB) of the next step
   int ld, r_al, n_rhs, n_var;
+  // the variables' diagonal before any sweep (the relative pivot test), or
+  // null: sign test only
+  const gdouble* dg0;
 };
 constexpr int kStage = kSweepStage;
 static_assert(kSweepStage == 2 * kSB * kSB + kSB, "staging layout");
@@ -986,6 +993,19 @@ template <> __device__ __forceinline__ void sweep_rest<15>(double (&a)[16], doub
 }
 #undef KVC_FMAC_DPP
 
+// The pivot test, as one product: pivot d passes when d * f > 1.  A variable
+// swept in (sign +1) needs d > kPivotRel * dg, dg its diagonal before any
+// sweep: d / dg is the squared sine of the angle between its column and the
+// span of the variables already swept, so a smaller ratio means the column
+// is numerically in that span (f = 1 / (kPivotRel dg); with no dg, f = inf
+// and only d > 0 is asked).  A variable swept out (sign -1) needs d < 0
+// (f = -1e300); an identity row past the block passes (d = 1, f = 2).
+constexpr double kPivotRel = 1e-12;
+__device__ __forceinline__ double pivot_test(bool in, double sgn, double dg) {
+  if (!in) return 2.0;
+  return sgn > 0.0 ? 1.0 / (kPivotRel * dg) : -1e300;
+}
+
 // Pivot M: d = A[M][M] (lane M), rd = 1/d.  The other columns lose
 // A[r][M] A[M][c]/d (be = -A[M][c]/d); the pivot row becomes A[M][c]/d; the
 // pivot column would scale by 1/d: instead of rewriting its rows, the pivot
@@ -1002,11 +1022,11 @@ __device__ __forceinline__ void diag_pivot(double (&a)[16], double (&lcol)[16],
                                            bool& bad) {
   const double d = rdlane(a[M], M);
   const double sg = sgv[M];
-  // a pivot without its sign is replaced by the sign (1/s = s); the test
-  // runs beside the reciprocal instead of ahead of it
-  const bool ok = d * sg > 0.0;
+  // a failed pivot is replaced by its sign (1/s = s); the test runs beside
+  // the reciprocal instead of ahead of it
+  const bool ok = d * sg > 1.0;
   bad |= !ok;
-  const double rd = ok ? recip(d) : sg;
+  const double rd = ok ? recip(d) : (sg > 0.0 ? 1.0 : -1.0);
   const double rowm = a[M];
   lcol[M] = c < M ? -(rowm * sc) : (c == M ? 1.0 : 0.0);
   const bool piv = c == M;
@@ -1032,7 +1052,7 @@ __device__ __forceinline__ bool diag_sweep(int o, int k) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     a[r] = sm.pp[o + r][o + c];
-    sgv[r] = o + r < k ? sm.sgn[o + r] : 1.0;
+    sgv[r] = pivot_test(o + r < k, sm.sgn[o + r], sm.dg[o + r]);
   }
   double sc = 1.0;  // after the sweep: 1/D of pivot c
   bool bad = false;
@@ -1470,7 +1490,7 @@ struct TileWalk {
 // Returns whether a pivot of this step had the wrong sign (a lookahead
 // member flags its own into *status).
 __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& team_ref, int k_arg,
-                                        int skip_arg, int kn_arg, bool pre_arg, int32_t* status) {
+                                        int skip_arg, int kn_arg, bool pre_arg) {
   SweepSmem& sm = g_sw;
   // every argument is the same in all lanes; a called function receives them
   // in vector registers, so say so, or every branch and address derived from
@@ -1506,6 +1526,7 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& team_ref, in
       const double v = s_at_or0(M, in, in ? sm.piv[a] : 0, in ? sm.piv[c] : 0);
       sm.pp[a][c] = in ? v : (a == c ? 1.0 : 0.0);
     }
+    if (tid < kSB) sm.dg[tid] = tid < k && M.dg0 ? M.dg0[sm.piv[tid] - M.r_al] : 0.0;
     __syncthreads();
     bad = small_ldl(k);
   }
@@ -1623,7 +1644,10 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& team_ref, in
     // the lookahead member arrived at the first barrier after its gathers;
     // it factors the next block and waits for that barrier only before the
     // next
-    if (tid < kSB) sm.sgn[tid] = sm.sgn2[tid];
+    if (tid < kSB) {
+      sm.sgn[tid] = sm.sgn2[tid];
+      sm.dg[tid] = tid < kn && M.dg0 ? M.dg0[sm.piv2[tid] - M.r_al] : 0.0;
+    }
     __syncthreads();
     const bool bad2 = small_ldl(kn);
     for (int e = tid; e < kSB * kSB; e += kTeamThreads) {
@@ -1631,7 +1655,7 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& team_ref, in
       M.stage[kSB * kSB + e] = sm.li[r][c];
     }
     if (tid < kSB) M.stage[2 * kSB * kSB + tid] = sm.rD[tid];
-    if (bad2 && tid == 0 && status) atomicOr(status, 1);
+    bad |= bad2;
     // the factors are out: raise the team's ready count (after every wave's
     // stores have landed)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1737,14 +1761,65 @@ __device__ __forceinline__ double sweep_flops(int k, int n) {
 // exchanges (status bit 2, w = max(x, 0)).  Every member runs the rule on the
 // same data, so the rule needs no barrier.  Output: w, and the passive list
 // (support of w) for the value fit.
+//
+// A failed pivot (H_FF not numerically positive definite: a pivot of the
+// wrong sign or zero) restarts the head with the ridge raised tenfold, at
+// most three times: relative ridge max(10^e ridge, 10^(e-1) 1e-9) at the
+// e-th raise, so that ridge 0 (the plain NNLS) also recovers.  The team
+// rebuilds H = P_S^T P_S + lam I and c = P_S^T 1 + lam from P_S and the
+// column sums (the sweeps overwrote them).  The raises are recorded in the
+// status word (KVC_STATUS_RIDGE_RAISED and the count in bits 8-9); bit 1
+// stays set only if the last attempt still failed.  The relative ridge in
+// use is left in lam[2b+1] for the value fit.
 // ---------------------------------------------------------------------------
+
+// Rebuild head b's bias system for relative ridge `rel`: the Gram tiles of
+// the lower triangle are dealt round-robin over the team's members (one
+// 64 x 64 fp64 MFMA tile product over all n rows each, staged through the
+// pivot-block LDS, which no sweep uses meanwhile); lam_w = rel tr(H)/t with
+// tr(H)/t from lam[2b+1]; column 0 of the variable rows = c + lam_w and
+// columns 1..15 cleared.
+__device__ __noinline__ void rebuild_bias(const SweepMat M, const Team tm,
+                                          const double* __restrict__ PSb, int t_str, int n,
+                                          int t, const double* __restrict__ cb, double lw) {
+  SweepSmem& sm = g_sw;
+  double* sAt = &sm.pp[0][0];
+  double* sBt = sAt + kKC * kTile;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tt = (t + kTile - 1) / kTile, ntl = tt * (tt + 1) / 2;
+  for (int tile = tm.rank; tile < ntl; tile += tm.size) {
+    int ty, tx;
+    tri_decode(tile, ty, tx);
+    const int a0 = ty * kTile, c0 = tx * kTile;
+    f64x4 acc[2][2];
+    atb_tile<double, true>(PSb, t_str, nullptr, PSb, t_str, t, t, a0, c0, 0, n, sAt, sBt, acc);
+#pragma unroll
+    for (int ra = 0; ra < 2; ++ra)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = a0 + tile_row(wave, lane, ra, i), c = c0 + tile_col(wave, lane, rb);
+          if (r < t && c < t)
+            M.S[static_cast<size_t>(kSB + r) * M.ld + kSB + c] =
+                acc[ra][rb][i] + (r == c ? lw : 0.0);
+        }
+  }
+  for (int e = tm.rank * kTeamThreads + threadIdx.x; e < t * 16; e += tm.size * kTeamThreads) {
+    const int r = e >> 4, c = e & 15;
+    M.S[static_cast<size_t>(kSB + r) * M.ld + c] = c == 0 ? cb[r] + lw : 0.0;
+  }
+}
+
 __global__ __launch_bounds__(256) void k_nnls_sweep(
     double* __restrict__ S, size_t sS, int ld, double* __restrict__ Ub, double* __restrict__ Vb,
     size_t sUV, double* __restrict__ stage, double* __restrict__ wv, int32_t* __restrict__ Fidx,
     int32_t* __restrict__ inv,
     int32_t* __restrict__ msz, int32_t* __restrict__ status, unsigned* __restrict__ bar,
     int* __restrict__ err, int* __restrict__ xcc, double* __restrict__ flops,
-    const int32_t* __restrict__ tv, int B, int t_str, int max_iters, int tx, uint64_t spin) {
+    const int32_t* __restrict__ tv, int B, int t_str, int max_iters, int tx, uint64_t spin,
+    const double* __restrict__ PS, int n, const double* __restrict__ cvec,
+    double* __restrict__ lam, double ridge) {
   SweepSmem& sm = g_sw;
   Team tm;
   int team, nteams;
@@ -1754,89 +1829,117 @@ __global__ __launch_bounds__(256) void k_nnls_sweep(
   constexpr int NV = kMaxTeamT / kTeamThreads;
   for (int b = team; b < B; b += nteams) {
     const int t = tv ? tv[b] : t_str;
+    // the diagonals before any sweep sit in the head's w output until w is
+    // written at the end
+    double* dg0 = wv + static_cast<size_t>(b) * t_str;
     const SweepMat M{gptr(S + b * sS), gptr(Ub + b * sUV), gptr(Vb + b * sUV),
-                     gptr(stage + static_cast<size_t>(b) * kStage), ld, kSB, 1, t};
-    for (int j = tid; j < t; j += kTeamThreads) sm.inF[j] = 0;
-    double cm = 0.0, hm = 0.0;
-    for (int j = tid; j < t; j += kTeamThreads) {
-      const gdouble* row = M.S + static_cast<size_t>(kSB + j) * ld;
-      cm = fmax(cm, fabs(row[0]));
-      hm = fmax(hm, row[kSB + j]);
-    }
-    const double scale = fmax(wg_max(cm), wg_max(hm));
-    int N = t + 1, bud = 3, done = 0;
-    bool bad = false;
-    double fl = 0.0;
+                     gptr(stage + static_cast<size_t>(b) * kStage), ld, kSB, 1, t, gptr(dg0)};
+    // the head's failure flag: the first word of its staging area, which
+    // the steps do not use (they stage at kSB*kSB and after)
+    unsigned long long* fail =
+        reinterpret_cast<unsigned long long*>(stage + static_cast<size_t>(b) * kStage);
+    double fl = 0.0, rel = ridge, floor_rel = 1e-9;
+    int done = 0, raises = 0;
+    bool failed = false;
     double val[NV];
-    for (int it = 0;; ++it) {
-      double xm = 0.0;
-#pragma unroll
-      for (int q = 0; q < NV; ++q) {
-        const int j = tid + q * kTeamThreads;
-        const double v = M.S[static_cast<size_t>(kSB + (j < t ? j : 0)) * ld];
-        val[q] = j < t ? v : 0.0;
-        if (j < t && sm.inF[j]) xm = fmax(xm, fabs(val[q]));
+    for (;;) {
+      // one attempt; the flag is cleared before this member's first step,
+      // so before any member can raise it (every step has a team barrier)
+      if (tm.rank == 0 && tid == 0)
+        __hip_atomic_store(fail, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int j = tid; j < t; j += kTeamThreads) sm.inF[j] = 0;
+      double cm = 0.0, hm = 0.0;
+      for (int j = tid; j < t; j += kTeamThreads) {
+        const gdouble* row = M.S + static_cast<size_t>(kSB + j) * ld;
+        cm = fmax(cm, fabs(row[0]));
+        hm = fmax(hm, row[kSB + j]);
+        dg0[j] = row[kSB + j];  // every member stores the same values
       }
-      const double tol = 1e-13 * scale * fmax(1.0, wg_max(xm));
-      int nv = 0, vmax = -1, slot;
+      const double scale = fmax(wg_max(cm), wg_max(hm));
+      int N = t + 1, bud = 3;
+      bool bad = false;
+      done = 0;
+      for (int it = 0;; ++it) {
+        double xm = 0.0;
 #pragma unroll
-      for (int q = 0; q < NV; ++q) {
-        const int j = tid + q * kTeamThreads;
-        bool f = false;
-        if (j < t) f = sm.inF[j] ? val[q] < 0.0 : val[q] > tol;
-        if (q * kTeamThreads < t) {
-          nv = wg_append(f, nv, &slot);
-          if (f) {
-            sm.list[slot] = static_cast<int16_t>(j);
-            vmax = j;
+        for (int q = 0; q < NV; ++q) {
+          const int j = tid + q * kTeamThreads;
+          const double v = M.S[static_cast<size_t>(kSB + (j < t ? j : 0)) * ld];
+          val[q] = j < t ? v : 0.0;
+          if (j < t && sm.inF[j]) xm = fmax(xm, fabs(val[q]));
+        }
+        const double tol = 1e-13 * scale * fmax(1.0, wg_max(xm));
+        int nv = 0, vmax = -1, slot;
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+          const int j = tid + q * kTeamThreads;
+          bool f = false;
+          if (j < t) f = sm.inF[j] ? val[q] < 0.0 : val[q] > tol;
+          if (q * kTeamThreads < t) {
+            nv = wg_append(f, nv, &slot);
+            if (f) {
+              sm.list[slot] = static_cast<int16_t>(j);
+              vmax = j;
+            }
           }
         }
-      }
-      if (nv == 0) {
-        done = 1;
-        break;
-      }
-      if (it >= max_iters) {
-        done = 2;
-        break;
-      }
-      int nflip = nv;
-      if (nv < N) {
-        N = nv;
-        bud = 3;
-      } else if (bud >= 1) {
-        --bud;
-      } else {
-        vmax = wg_imax(vmax);
-        __syncthreads();
-        if (tid == 0) sm.list[0] = static_cast<int16_t>(vmax);
-        nflip = 1;
-      }
-      __syncthreads();
-      for (int s0 = 0; s0 < nflip; s0 += kSB) {
-        const int k = min(kSB, nflip - s0);
-        const int kn = min(kSB, nflip - s0 - k);
-        if (tid < k) {
-          const int j = sm.list[s0 + tid];
-          sm.piv[tid] = kSB + j;
-          sm.sgn[tid] = sm.inF[j] ? -1.0 : 1.0;
-          sm.pos[kSB + j] = static_cast<int16_t>(tid);
+        if (nv == 0) {
+          done = 1;
+          break;
         }
-        if (tid < kn) {
-          const int j = sm.list[s0 + k + tid];
-          sm.piv2[tid] = kSB + j;
-          sm.sgn2[tid] = sm.inF[j] ? -1.0 : 1.0;
+        if (it >= max_iters) {
+          done = 2;
+          break;
+        }
+        int nflip = nv;
+        if (nv < N) {
+          N = nv;
+          bud = 3;
+        } else if (bud >= 1) {
+          --bud;
+        } else {
+          vmax = wg_imax(vmax);
+          __syncthreads();
+          if (tid == 0) sm.list[0] = static_cast<int16_t>(vmax);
+          nflip = 1;
         }
         __syncthreads();
-        bad |= sweep_step(M, tm, k, 0, kn, s0 > 0 && tm.size > 1, status ? status + b : nullptr);
-        if (tid < k) {
-          const int j = sm.list[s0 + tid];
-          sm.inF[j] ^= 1;
-          sm.pos[kSB + j] = -1;
+        for (int s0 = 0; s0 < nflip; s0 += kSB) {
+          const int k = min(kSB, nflip - s0);
+          const int kn = min(kSB, nflip - s0 - k);
+          if (tid < k) {
+            const int j = sm.list[s0 + tid];
+            sm.piv[tid] = kSB + j;
+            sm.sgn[tid] = sm.inF[j] ? -1.0 : 1.0;
+            sm.pos[kSB + j] = static_cast<int16_t>(tid);
+          }
+          if (tid < kn) {
+            const int j = sm.list[s0 + k + tid];
+            sm.piv2[tid] = kSB + j;
+            sm.sgn2[tid] = sm.inF[j] ? -1.0 : 1.0;
+          }
+          __syncthreads();
+          bad |= sweep_step(M, tm, k, 0, kn, s0 > 0 && tm.size > 1);
+          if (tid < k) {
+            const int j = sm.list[s0 + tid];
+            sm.inF[j] ^= 1;
+            sm.pos[kSB + j] = -1;
+          }
+          __syncthreads();
+          fl += sweep_flops(k, t + 1);
         }
-        __syncthreads();
-        fl += sweep_flops(k, t + 1);
       }
+      // the team's verdict: any member's failed pivot
+      if (bad && tid == 0) atomicOr(fail, 1ull);
+      team_sync(tm);
+      failed = __hip_atomic_load(fail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+      if (!failed || raises == 3) break;
+      ++raises;
+      rel = fmax(rel * 10.0, floor_rel);
+      floor_rel *= 10.0;
+      rebuild_bias(M, tm, PS + static_cast<size_t>(b) * n * t_str, t_str, n, t,
+                   cvec + static_cast<size_t>(b) * t_str, rel * lam[2 * b + 1]);
+      team_sync(tm);
     }
     if (tm.rank == 0) {
       double* w = wv + static_cast<size_t>(b) * t_str;
@@ -1868,9 +1971,12 @@ __global__ __launch_bounds__(256) void k_nnls_sweep(
       if (tid == 0) {
         msz[b] = m;
         flops[2 * b] = fl;
+        if (raises > 0) lam[2 * b] = rel * lam[2 * b + 1];
+        lam[2 * b + 1] = rel;  // the value fit's relative ridge
         if (status) {
           if (done == 2) atomicOr(&status[b], 2);
-          if (bad) atomicOr(&status[b], 1);
+          if (failed) atomicOr(&status[b], 1);
+          if (raises > 0) atomicOr(&status[b], 64 | (raises << 8));
         }
       }
     }
@@ -1897,7 +2003,7 @@ __global__ __launch_bounds__(256) void k_value_sweep(
   for (int b = team; b < B; b += nteams) {
     const int m = msz[b];
     const SweepMat M{gptr(S + b * sS), gptr(Ub + b * sUV), gptr(Vb + b * sUV),
-                     gptr(stage + static_cast<size_t>(b) * kStage), ld, r_al, D, m};
+                     gptr(stage + static_cast<size_t>(b) * kStage), ld, r_al, D, m, nullptr};
     bool bad = false;
     for (int s0 = 0; s0 < m; s0 += kSB) {
       const int k = min(kSB, m - s0);
@@ -1912,8 +2018,7 @@ __global__ __launch_bounds__(256) void k_value_sweep(
         sm.sgn2[tid] = 1.0;
       }
       __syncthreads();
-      bad |= sweep_step(M, tm, k, s0 / kSB, kn, s0 > 0 && tm.size > 1,
-                        status ? status + b : nullptr);
+      bad |= sweep_step(M, tm, k, s0 / kSB, kn, s0 > 0 && tm.size > 1);
       if (tid < k) sm.pos[r_al + s0 + tid] = -1;
       __syncthreads();
     }
@@ -1921,8 +2026,10 @@ __global__ __launch_bounds__(256) void k_value_sweep(
       double fl = 0.0;
       for (int s0 = 0; s0 < m; s0 += kSB) fl += sweep_flops(min(kSB, m - s0), m + D);
       flops[2 * b + 1] = fl;
-      if (bad && status) atomicOr(&status[b], 1);
     }
+    // every member reports the failed pivots it saw (the lookahead member,
+    // the last rank, factors the blocks after the first)
+    if (bad && tid == 0 && status) atomicOr(&status[b], 1);
   }
   if (tm.rank == 0 && tid == 0 && __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
     for (int b = team; b < B; b += nteams) atomicOr(&status[b], 8);
@@ -1964,19 +2071,21 @@ __global__ __launch_bounds__(256) void k_value_prep(double* __restrict__ PS,
   }
 }
 
-// lam_v = ridge * trace(G) / t; G += lam_v I (G at Gb, order msz, stride ld).
-// grid (B), block 256.
+// lam_v = ridge * trace(G) / t with the head's relative ridge (lam[2b+1], left
+// there by the NNLS: the caller's, or the raised one); G += lam_v I (G at Gb,
+// order msz, stride ld); lam[2b+1] = lam_v.  grid (B), block 256.
 __global__ void k_ridge_v(double* __restrict__ Gb, size_t sS, int ld,
                           const int32_t* __restrict__ msz, double* __restrict__ lam,
-                          const int32_t* __restrict__ tv, int t_str, double ridge) {
+                          const int32_t* __restrict__ tv, int t_str) {
   __shared__ double sh[16];
   const int b = blockIdx.x, m = msz[b];
   const int t = tv ? tv[b] : t_str;
+  const double rel = lam[2 * b + 1];  // read by every thread before thread 0 rewrites it
   double* G = Gb + b * sS;
   double tr = 0.0;
   for (int a = threadIdx.x; a < m; a += blockDim.x) tr += G[static_cast<size_t>(a) * ld + a];
   tr = block_sum(tr, sh);
-  const double lv = ridge * tr / t;
+  const double lv = rel * tr / t;
   for (int a = threadIdx.x; a < m; a += blockDim.x) G[static_cast<size_t>(a) * ld + a] += lv;
   if (threadIdx.x == 0) lam[2 * b + 1] = lv;
 }
@@ -2132,9 +2241,12 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
   int* err = reinterpret_cast<int*>(fb.bar + kBarWords - 1);
   const int32_t* tvp = fb.tv;
   {
+    const double* psp = fb.PS;
+    const double* cvp = fb.cvec;
     void* args[] = {&fb.S,   &sS,      &ld,        &fb.U,   &fb.V,  &sUV,     &fb.stage, &fb.wv,
                     &fb.Fidx, &fb.inv, &fb.msz,    &status, &fb.bar, &err,    &fb.xcc,
-                    &fb.flops, &tvp,   &B,        &t,         &max_iters, &tx, &fb.wait_ticks};
+                    &fb.flops, &tvp,   &B,        &t,         &max_iters, &tx, &fb.wait_ticks,
+                    &psp,     &n,      &cvp,      &fb.lam,   &ridge};
     e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_nnls_sweep), dim3(grid),
                                    dim3(kTeamThreads), args, 0, st);
     if (e != hipSuccess) return e;
@@ -2149,8 +2261,7 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
   launch_atb<double, true>(fb.PS, sPS, t, nullptr, 0, fb.PS, sPS, t, G0, sS, ld, n, fb.msz, t, t,
                            fb.part, fb.part_cap, B, st);
   prof_mark(11, true, st);
-  hipLaunchKernelGGL(k_ridge_v, dim3(B), dim3(256), 0, st, G0, sS, ld, fb.msz, fb.lam, fb.tv, t,
-                     ridge);
+  hipLaunchKernelGGL(k_ridge_v, dim3(B), dim3(256), 0, st, G0, sS, ld, fb.msz, fb.lam, fb.tv, t);
   launch_atb<float, false>(fb.PS, sPS, t, nullptr, 0, O, static_cast<size_t>(n) * D, D, R0, sS, ld,
                            n, fb.msz, t, D, fb.part, fb.part_cap, B, st);
   hipLaunchKernelGGL((k_rhs_ridge<In>), dim3((t * D + 255) / 256, B), dim3(256), 0, st, R0, sS,

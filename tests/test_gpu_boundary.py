@@ -104,3 +104,50 @@ def test_wait_time_out_is_reported_and_every_kernel_ends():
     gpu = run_gpu(w, data)
     for h in range(w.B):
         compare_head(gpu, h, data, w.t, TOL_BF16)
+
+
+def test_singular_bias_gram_raises_the_ridge():
+    """Two kept keys with identical rows make P_S's columns equal, so at
+    ridge 0 the bias Gram is singular and a pivot vanishes once both are
+    passive (adjacent slots 5 and 6 enter together in one 16-pivot block,
+    where both columns get bit-identical updates and the second pivot
+    cancels to rounding size, far under the relative pivot bound).  The NNLS restarts with the ridge raised (status bit 64, the
+    count in bits 8-9), ends without KVC_STATUS_NOT_SPD, gives both copies
+    the same bias, and its compacted attention matches the oracle's fit at
+    the raised relative ridge (1e-9 at the first raise from 0).  At the
+    default ridge the same Gram plus lam I is definite: no raise."""
+    import torch
+    import kv_cache_compaction_head_amd as kvc
+    w = synth.custom(34, 2, 700, 256, 128, 48, "bf16", "normal")
+    data = synth.batch(w)
+    rng = np.random.default_rng(34)
+    idx = np.sort(rng.choice(w.T, size=w.t, replace=False)).astype(np.int32)
+    idx = np.tile(idx, (w.B, 1))
+    for h in range(w.B):  # kept slots 5 and 6 share one key row
+        data["K"][h, idx[h, 6]] = data["K"][h, idx[h, 5]]
+    Q, K, V = (to_device(data[k]) for k in ("Q", "K", "V"))
+    tidx = torch.from_numpy(idx).cuda()
+    print("duplicated kept key: B=2 T=700 n=256 t=48, slots 5 and 6, ridge 0", flush=True)
+    res = kvc.fit(Q, K, V, tidx, ridge_rel=0.0)
+    torch.cuda.synchronize()
+    st = res.status.cpu().numpy()
+    print("status at ridge 0:", st, [kvc.status_raises(s) for s in st], flush=True)
+    bias = res.bias.cpu().numpy().astype(np.float64)
+    vals = res.values.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(bias)) and np.all(np.isfinite(vals))
+    for h in range(w.B):
+        assert st[h] & kvc.STATUS_RIDGE_RAISED, st
+        e = kvc.status_raises(st[h])
+        assert 1 <= e <= 3 and not st[h] & kvc.STATUS_NOT_SPD, st
+        assert abs(bias[h, 5] - bias[h, 6]) < 1e-3, (bias[h, 5], bias[h, 6])
+        rel = max(0.0, 1e-9 * 10.0 ** (e - 1))
+        Qh, Kh, Vh = (synth.to_f64(data[k][h]) for k in ("Q", "K", "V"))
+        _, beta, Cv, _ = orc.fit(Qh, Kh, Vh, idx[h], ridge_rel=rel)
+        o_gpu = orc.attend(Qh, Kh[idx[h]], vals[h], bias[h])
+        o_ref = orc.attend(Qh, Kh[idx[h]], Cv, beta)
+        err = orc.rel_l2(o_gpu, o_ref)
+        print(f"head {h}: raises {e}, Ohat vs oracle at ridge {rel:g}: {err:.3g}", flush=True)
+        assert err <= TOL_BF16
+    res2 = kvc.fit(Q, K, V, tidx)
+    torch.cuda.synchronize()
+    assert (res2.status.cpu().numpy() == 0).all(), res2.status

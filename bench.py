@@ -287,8 +287,11 @@ def main():
     # units in the design notes):
     #   k_score_lse    2 n T d per entry (S = Q K^T once)
     #   k_expweight    4 n T d per entry (S recomputed + P V)
-    #   k_imp_reduce   reads the ceil(n/128) partials of every key, writes imp: 4 T (nqb + 1) B
-    #   k_select       reads imp once, writes idx: 4 T B + 4 t B
+    #   k_imp_reduce   reads the ceil(n/128) partials of every key, writes imp (and
+    #                  the selection's first histogram): 4 T (nqb + 1) B
+    #   k_sel_*        the rest of the selection (two refining passes, the counts,
+    #                  the compaction: four launches), algorithmically one read of
+    #                  imp and the idx write: 4 T B + 4 t B
     #   k_gather_rows  reads and writes the kept K rows: 2 t d es B
     #   Grams          n t^2 per entry (symmetric half; value Gram: n m^2, m passive)
     #   k_nnls_sweep   the block sweeps of the pivoting rounds (counted on device)
@@ -296,7 +299,7 @@ def main():
     work = {"score_lse": ("k_score_lse", 2.0 * n * Te * d * Be, mm_peak, "mfma"),
             "expweight": ("k_expweight", 4.0 * n * Te * d * Be, mm_peak, "mfma"),
             "imp_reduce": ("k_imp_reduce", 4.0 * Te * (nqb + 1) * Be, PEAK_HBM_GBS, "hbm"),
-            "topt": ("k_select", 4.0 * (Te + te) * Be, PEAK_HBM_GBS, "hbm"),
+            "topt": ("k_sel_* (refine x2, count, compact)", 4.0 * (Te + te) * Be, PEAK_HBM_GBS, "hbm"),
             "gather": ("k_gather_rows", 2.0 * te * d * es * Be, PEAK_HBM_GBS, "hbm"),
             "gram": ("k_atb (mass Gram)", float(n) * te * te * Be, PEAK_F64_TFLOPS, "mfma"),
             "value_gram": ("k_atb (value Gram)", float(n * (m_pass.astype(float) ** 2).sum()),

@@ -85,7 +85,7 @@ Plan make_plan(const kvc_params_t* p) {
 }
 
 struct Layout {
-  size_t ml, lse, Opart, O, imp_part, imp, idx, status, tv, emask, plist, PS, S, U, V, stage, cvec, wv, lam,
+  size_t ml, lse, Opart, O, imp_part, imp, sel, idx, status, tv, emask, plist, PS, S, U, V, stage, cvec, wv, lam,
       colpart, Fidx, inv, msz, bar, xcc, flops, part, total;
   size_t part_cap;
   // greedy selection only (zero otherwise)
@@ -110,6 +110,7 @@ Layout make_layout(const kvc_params_t* p, bool omp = false) {
   L.O = take(B * n * d * 4);
   L.imp_part = take(B * pl.nqb * T * 4);
   L.imp = take(B * T * 4);
+  L.sel = take(B * kvc::sel_words(static_cast<int>(T)) * 4);
   L.idx = take(B * t * 4);
   L.status = take(B * 4);
   L.tv = take(B * 4);
@@ -209,11 +210,13 @@ kvc::FitBufs fit_bufs(void* ws, const Layout& L) {
 // (chunked compaction runs every chunk of a head against that head's queries).
 template <class In, int D>
 hipError_t run_score(const kvc_params_t* p, const void* Q, const void* K, const void* V,
-                     void* ws, const Layout& L, int qg, const uint8_t* mask, hipStream_t st) {
+                     void* ws, const Layout& L, int qg, const uint8_t* mask, int32_t* status,
+                     hipStream_t st) {
   const Plan pl = make_plan(p);
   return kvc::launch_score<In, D>(Q, K, V, at<double2>(ws, L.ml), at<double>(ws, L.lse),
                                   at<float>(ws, L.Opart), at<float>(ws, L.O),
                                   at<float>(ws, L.imp_part), at<float>(ws, L.imp),
+                                  at<uint32_t>(ws, L.sel), status,
                                   static_cast<int>(p->B), static_cast<int>(p->n),
                                   static_cast<int>(p->T), pl.nsplit1, pl.kps1, pl.nsplit2,
                                   pl.kps2, p->agg == KVC_AGG_RMS, qg, mask, st);
@@ -248,8 +251,8 @@ template <class In, int D>
 struct ScoreOp {
   static hipError_t run(const kvc_params_t* p, const void* Q, const void* K, const void* V,
                         void* ws, const Layout* L, int qg, const uint8_t* mask,
-                        hipStream_t st) {
-    return run_score<In, D>(p, Q, K, V, ws, *L, qg, mask, st);
+                        int32_t* status, hipStream_t st) {
+    return run_score<In, D>(p, Q, K, V, ws, *L, qg, mask, status, st);
   }
 };
 template <class In, int D>
@@ -333,7 +336,8 @@ int compact_impl(const kvc_params_t* p, int qg, const int32_t* t_in, const uint8
     emask = em;
     if (e == hipSuccess) e = kvc::launch_protect_prep(protect, em, plist, tv, status, B, T, t, stream);
   }
-  if (e == hipSuccess) e = dispatch<ScoreOp>(p, Q_ref, K, V, workspace, &L, qg, emask, stream);
+  if (e == hipSuccess)
+    e = dispatch<ScoreOp>(p, Q_ref, K, V, workspace, &L, qg, emask, status, stream);
   kvc::prof_mark(KVC_STAGE_SELECT, false, stream);
   if (e == hipSuccess && omp) {
     float* P32 = at<float>(workspace, L.P32);
@@ -344,7 +348,8 @@ int compact_impl(const kvc_params_t* p, int qg, const int32_t* t_in, const uint8
                           stream);
   } else if (e == hipSuccess) {
     kvc::prof_mark(KVC_STAGE_TOPT, false, stream);
-    e = kvc::launch_select(at<float>(workspace, L.imp), idx, status, tv, emask, B, T, t, stream);
+    e = kvc::launch_select(at<float>(workspace, L.imp), at<uint32_t>(workspace, L.sel), idx, tv,
+                           emask, B, T, t, stream);
     kvc::prof_mark(KVC_STAGE_TOPT, true, stream);
   }
   kvc::prof_mark(KVC_STAGE_GATHER, false, stream);
@@ -486,7 +491,7 @@ int kvc_fit(const kvc_params_t* p, const void* Q_ref, const void* K, const void*
   hipError_t e = kvc::launch_fill_i32(status, 0, p->B, stream);
   if (e == hipSuccess)
     e = dispatch<ScoreOp>(p, Q_ref, K, V, workspace, &L, 1, static_cast<const uint8_t*>(nullptr),
-                          stream);
+                          status, stream);
   if (e == hipSuccess)
     e = dispatch<FitOp>(p, Q_ref, K, V, idx, out_bias, out_V, status, workspace, &L, 1,
                         static_cast<const int32_t*>(nullptr), stream);

@@ -7,14 +7,33 @@
 namespace kvc {
 using bf16_t = uint16_t;
 
+// Selection state of a head, sel_words(T) uint32 words in the workspace: the
+// histograms of the radix select's three digits (bits 31-21, 20-10, 9-0 of
+// the ranking key), the threshold key tau and how many keys equal to it are
+// kept, then per chunk of kSelChunk keys its counts above and equal to tau.
+constexpr int kSelChunk = 4096;
+constexpr int kSelH1 = 2048, kSelH2 = 2048, kSelH3 = 1024;
+constexpr int kSelTau = kSelH1 + kSelH2 + kSelH3;  // tau, then need_eq
+constexpr int kSelCnt = kSelTau + 2;               // [chunk][2]: above, equal
+inline int sel_chunks(int T) { return (T + kSelChunk - 1) / kSelChunk; }
+inline size_t sel_words(int T) {
+  return (kSelCnt + 2 * static_cast<size_t>(sel_chunks(T)) + 63) / 64 * 64;
+}
+
+// The score path; its importance reduction also runs the selection's first
+// pass into sel (which the lse merge clears first) from the ranking keys
+// (mask: keys never selected, or null; status |= 4 for a non-finite
+// importance).
 template <class In, int D>
 hipError_t launch_score(const void* Q, const void* K, const void* V, double2* ml, double* lse,
-                        float* Opart, float* O, float* imp_part, float* imp, int B, int n, int T,
-                        int nsplit1, int kps1, int nsplit2, int kps2, bool rms, int qg,
-                        const uint8_t* mask, hipStream_t st);
-// tv: per-head budgets (device, each in [1, t]) or null for t everywhere;
-// mask: [B][T] keys never selected (nonzero), or null
-hipError_t launch_select(const float* imp, int32_t* idx, int32_t* status, const int32_t* tv,
+                        float* Opart, float* O, float* imp_part, float* imp, uint32_t* sel,
+                        int32_t* status, int B, int n, int T, int nsplit1, int kps1,
+                        int nsplit2, int kps2, bool rms, int qg, const uint8_t* mask,
+                        hipStream_t st);
+// The rest of the top-t selection, after launch_score.  tv: per-head budgets
+// (device, each in [1, t]) or null for t everywhere; mask: [B][T] keys never
+// selected (nonzero), or null (the one given to launch_score).
+hipError_t launch_select(const float* imp, uint32_t* sel, int32_t* idx, const int32_t* tv,
                          const uint8_t* mask, int B, int T, int t, hipStream_t st);
 // Protected keys: from the caller's mask [B][T], per head the first (by
 // position) pp_b = min(count, t - 1) protected keys are listed in plist [B][t]

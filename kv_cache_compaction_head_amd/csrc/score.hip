@@ -27,6 +27,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "sel.h"
 
 namespace kvc {
 
@@ -544,9 +545,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 // Four lanes per query, each taking every fourth split: the maximum over
 // all splits, then each lane's sum in split order, then the four sums added
 // in lane order.  grid (ceil(4 B n / 256)), block 256.
+// It also clears every head's first selection histogram (sel, stride
+// sstride words), which the importance reduction fills.
 __global__ void k_lse_merge(const double2* __restrict__ ml, double* __restrict__ lse, int n,
-                            int nsplit, int B) {
+                            int nsplit, int B, unsigned* __restrict__ sel, size_t sstride) {
   const int g = blockIdx.x * blockDim.x + threadIdx.x, i = g >> 2, part = g & 3;
+  for (size_t e = g; e < static_cast<size_t>(B) * kSelH1;
+       e += static_cast<size_t>(gridDim.x) * blockDim.x)
+    sel[(e / kSelH1) * sstride + e % kSelH1] = 0;
   const bool ok = i < B * n;
   const int b = ok ? i / n : 0, q = ok ? i % n : 0;
   const double2* p = ml + static_cast<size_t>(b) * nsplit * n + q;
@@ -1069,16 +1075,74 @@ __global__ void k_o_reduce(const float* __restrict__ Opart, float* __restrict__ 
   }
 }
 
-// imp[b][j] = sum over query blocks (in order) of imp_part[b][qb][j].
-__global__ void k_imp_reduce(const float* __restrict__ part, float* __restrict__ imp, int T,
-                             int nqb, int B) {
-  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= static_cast<size_t>(B) * T) return;
-  const size_t b = i / T, j = i % T;
-  const float* p = part + b * nqb * T + j;
-  float s = 0.f;
-  for (int qb = 0; qb < nqb; ++qb) s += p[static_cast<size_t>(qb) * T];
-  imp[i] = s;
+// imp[b][j] = sum over query blocks (in order) of imp_part[b][qb][j], and the
+// first pass of the top-t selection (select.hip): the histogram of the
+// ranking keys' top 11 bits, per workgroup of kImpKeys keys in LDS, added
+// into the head's histogram in sel (cleared by k_lse_merge).  The workgroups
+// also clear the later passes' histograms.  A non-finite importance sets
+// status bit 4.  grid (ceil(T / kImpKeys), B), block 256; key j = workgroup
+// start + 256 i + thread (coalesced), four query blocks' loads in flight.
+constexpr int kImpKeys = 1024;
+__global__ __launch_bounds__(256) void k_imp_reduce(const float* __restrict__ part,
+                                                    float* __restrict__ imp,
+                                                    unsigned* __restrict__ sel,
+                                                    const uint8_t* __restrict__ mask,
+                                                    int32_t* __restrict__ status, int T, int nqb,
+                                                    size_t sstride) {
+  constexpr int PER = kImpKeys / 256;
+  __shared__ unsigned hist[kSelH1];
+  __shared__ int s_bad;
+  const int b = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
+  const float* p = part + static_cast<size_t>(b) * nqb * T;
+  float s[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) s[i] = 0.f;
+  int qb = 0;
+  for (; qb + 4 <= nqb; qb += 4) {
+    float v[4][PER];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int j = g * kImpKeys + i * 256 + tid;
+        v[u][i] = j < T ? p[static_cast<size_t>(qb + u) * T + j] : 0.f;
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) s[i] += v[u][i];
+  }
+  for (; qb < nqb; ++qb)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int j = g * kImpKeys + i * 256 + tid;
+      if (j < T) s[i] += p[static_cast<size_t>(qb) * T + j];
+    }
+  for (int i = tid; i < kSelH1; i += 256) hist[i] = 0;
+  if (tid == 0) s_bad = 0;
+  unsigned* st = sel + b * sstride;
+  {
+    constexpr int later = kSelH2 + kSelH3;
+    const int per = (later + gridDim.x - 1) / gridDim.x;
+    for (int i = g * per + tid; i < min(later, (g + 1) * per); i += 256) st[kSelH1 + i] = 0;
+  }
+  __syncthreads();
+  const uint8_t* mb = mask ? mask + static_cast<size_t>(b) * T : nullptr;
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int j = g * kImpKeys + i * 256 + tid;
+    if (j < T) {
+      imp[static_cast<size_t>(b) * T + j] = s[i];
+      bad |= __float_as_uint(s[i]) >= 0x7f800000u;  // inf / nan (non-negative values)
+      atomicAdd(&hist[sel_key_of(s[i], mb, j) >> 21], 1u);
+    }
+  }
+  if (bad) s_bad = 1;
+  __syncthreads();
+  for (int i = tid; i < kSelH1; i += 256)
+    if (hist[i]) atomicAdd(&st[i], hist[i]);
+  if (tid == 0 && s_bad && status) atomicOr(&status[b], 4);
 }
 
 // ---------------------------------------------------------------------------
@@ -1086,9 +1150,9 @@ __global__ void k_imp_reduce(const float* __restrict__ part, float* __restrict__
 // ---------------------------------------------------------------------------
 template <class In, int D>
 hipError_t launch_score(const void* Q, const void* K, const void* V, double2* ml, double* lse,
-                        float* Opart, float* O, float* imp_part, float* imp, int B, int n, int T,
-                        int nsplit1, int kps1, int nsplit2, int kps2, bool rms, int qg,
-                        const uint8_t* mask, hipStream_t st) {
+                        float* Opart, float* O, float* imp_part, float* imp, uint32_t* sel,
+                        int32_t* status, int B, int n, int T, int nsplit1, int kps1, int nsplit2,
+                        int kps2, bool rms, int qg, const uint8_t* mask, hipStream_t st) {
   const int nqb = (n + kBM - 1) / kBM;
   const In* q = static_cast<const In*>(Q);
   const In* k = static_cast<const In*>(K);
@@ -1112,8 +1176,9 @@ hipError_t launch_score(const void* Q, const void* K, const void* V, double2* ml
                          kps1, nqb, nsplit1, B, qg);
   }
   prof_mark(0, true, st);
+  const size_t ss = sel_words(T);
   hipLaunchKernelGGL(k_lse_merge, dim3((4 * B * n + 255) / 256), dim3(256), 0, st, ml, lse, n,
-                     nsplit1, B);
+                     nsplit1, B, sel, ss);
   prof_mark(1, false, st);
 #define KVC_K2(R, M)                                                                          \
   if constexpr (sizeof(In) == 2)                                                              \
@@ -1133,29 +1198,22 @@ hipError_t launch_score(const void* Q, const void* K, const void* V, double2* ml
   prof_mark(1, true, st);
   hipLaunchKernelGGL(k_o_reduce, dim3((n + 31) / 32, D / 32, B), dim3(32, 8), 0, st, Opart, O, n,
                      D, nsplit2);
-  const size_t tot = static_cast<size_t>(B) * T;
   prof_mark(8, false, st);
-  hipLaunchKernelGGL(k_imp_reduce, dim3((tot + 255) / 256), dim3(256), 0, st, imp_part, imp, T,
-                     nqb, B);
+  hipLaunchKernelGGL(k_imp_reduce, dim3((T + kImpKeys - 1) / kImpKeys, B), dim3(256), 0, st,
+                     imp_part, imp, sel, mask, status, T, nqb, ss);
   prof_mark(8, true, st);
   return hipGetLastError();
 }
 
-template hipError_t launch_score<bf16_t, 128>(const void*, const void*, const void*, double2*,
-                                              double*, float*, float*, float*, float*, int, int,
-                                              int, int, int, int, int, bool, int, const uint8_t*,
-                                             hipStream_t);
-template hipError_t launch_score<bf16_t, 64>(const void*, const void*, const void*, double2*,
-                                             double*, float*, float*, float*, float*, int, int,
-                                             int, int, int, int, int, bool, int, const uint8_t*,
-                                             hipStream_t);
-template hipError_t launch_score<float, 128>(const void*, const void*, const void*, double2*,
-                                             double*, float*, float*, float*, float*, int, int,
-                                             int, int, int, int, int, bool, int, const uint8_t*,
-                                             hipStream_t);
-template hipError_t launch_score<float, 64>(const void*, const void*, const void*, double2*,
-                                            double*, float*, float*, float*, float*, int, int,
-                                            int, int, int, int, int, bool, int, const uint8_t*,
-                                             hipStream_t);
+#define KVC_INST_SCORE(In, D)                                                                  \
+  template hipError_t launch_score<In, D>(const void*, const void*, const void*, double2*,     \
+                                          double*, float*, float*, float*, float*, uint32_t*,  \
+                                          int32_t*, int, int, int, int, int, int, int, bool,   \
+                                          int, const uint8_t*, hipStream_t);
+KVC_INST_SCORE(bf16_t, 128)
+KVC_INST_SCORE(bf16_t, 64)
+KVC_INST_SCORE(float, 128)
+KVC_INST_SCORE(float, 64)
+#undef KVC_INST_SCORE
 
 }  // namespace kvc

@@ -8,13 +8,15 @@
 // indices are emitted in ascending order so the compacted cache keeps the
 // positional order of the original (a contiguous re-indexing of the survivors).
 //
-//   k_select   one workgroup per head: MSB-first radix select over the
-//              uint32 bit patterns of the (non-negative) importances finds the
-//              t-th largest value tau exactly; an order-preserving block scan
-//              then keeps every value > tau and the lowest-index values == tau.
+//   k_sel_*    MSB-first radix select over the uint32 bit patterns of the
+//              (non-negative) importances, several workgroups per head, finds
+//              the t-th largest value tau exactly; an order-preserving
+//              compaction then keeps every value > tau and the lowest-index
+//              values == tau.
 //   k_gather   C_k = K[idx] (exact copies, input dtype).
 #include "common.h"
 #include "launch.h"
+#include "sel.h"
 
 namespace kvc {
 
@@ -48,150 +50,189 @@ __device__ int block_exclusive_scan(int v, int* scratch, int* total) {
   return before;
 }
 
-// grid (B), block kSelThreads.  imp [B][T] (non-negative floats), idx [B][t]:
-// the tb = tv[b] (or t) kept indices ascending, then -1 in the remaining slots.
-// Keys marked in mask (if given) are never kept: the ranking key is the bit
-// pattern plus one, and 0 for a marked key, which keeps the order of the
-// others (patterns of finite non-negative floats stay below 0x7f800000).
-// status[b] |= 4 if an importance is not finite (NaN/Inf input upstream).
-// PER > 0: every thread holds its contiguous chunk of ceil(T / kSelThreads)
-// <= PER keys in registers, read once, for all passes and the compaction;
-// PER == 0 streams the keys from memory in every pass (any T).
-template <int PER>
-__global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict__ imp,
-                                                        int32_t* __restrict__ idx,
-                                                        int32_t* __restrict__ status,
-                                                        const int32_t* __restrict__ tv,
-                                                        const uint8_t* __restrict__ mask, int T,
-                                                        int t) {
-  // one 256-bin histogram per wave: no contention between waves on the few
-  // top-byte bins most keys share; the digit is then found by a parallel scan
-  // of the combined bins
-  __shared__ unsigned int hist[kSelThreads / 64][256];
-  __shared__ int scratch[64];
-  __shared__ unsigned int s_prefix, s_mask;
-  __shared__ int s_need, s_bad;
-  const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
-  const unsigned int* u = reinterpret_cast<const unsigned int*>(imp) + static_cast<size_t>(b) * T;
-  const uint8_t* mb = mask ? mask + static_cast<size_t>(b) * T : nullptr;
-  auto key = [&](int j) -> unsigned int {
-    const unsigned int v = u[j];
-    return mb ? (mb[j] ? 0u : v + 1u) : v;
-  };
+// ---------------------------------------------------------------------------
+// Top-t selection, several workgroups per head.  The ranking key of key j is
+// the uint32 bit pattern of its importance (order-preserving for the
+// non-negative floats), plus one, or 0 when the mask excludes it.  The exact
+// t-th largest key tau is found MSB first in three digits (bits 31-21, 20-10,
+// 9-0): each pass histograms, per chunk of kSelChunk keys, the next digit of
+// the keys that match the digits found so far, and adds the chunk's
+// histogram into the head's (integer atomics: the counts do not depend on
+// the order).  Pass 1 runs inside the importance reduction (score.hip); each
+// later kernel reads the digits found so far from the head's histograms.
+// Then every chunk counts its keys above and equal to tau, and a compaction
+// keeps every key above tau and the lowest-index keys equal to it, in
+// ascending order, from the chunks' counts in chunk order.
+// ---------------------------------------------------------------------------
 
-  const int tb = tv ? tv[b] : t;
-  if (tid == 0) {
-    s_prefix = 0;
-    s_mask = 0;
-    s_need = tb;
-    s_bad = 0;
-  }
-  // the thread's contiguous chunk (also the compaction's)
-  const int chunk = (T + kSelThreads - 1) / kSelThreads;
-  const int c0 = min(T, tid * chunk), c1 = min(T, c0 + chunk);
-  constexpr int NR = PER > 0 ? PER : 1;
-  unsigned int kv[NR];
-  if (PER > 0) {
-    bool bad = false;
+// The chunk's 16 keys of this thread: key chunk start + 256 i + thread.
+__device__ __forceinline__ void sel_load_strided(const float* ib, const uint8_t* mb, int T, int g,
+                                                 unsigned (&kv)[kSelPer]) {
+  float v[kSelPer];
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const int j = c0 + i;
-      const unsigned int raw = j < c1 ? u[j] : 0u;
-      bad |= raw >= 0x7f800000u;  // inf / nan (non-negative inputs)
-      kv[i] = j < c1 ? (mb ? (mb[j] ? 0u : raw + 1u) : raw) : 0u;
-    }
-    __syncthreads();
-    if (bad) s_bad = 1;
+  for (int i = 0; i < kSelPer; ++i) {
+    const int j = g * kSelChunk + i * kSelBlock + threadIdx.x;
+    v[i] = j < T ? ib[j] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < kSelPer; ++i) {
+    const int j = g * kSelChunk + i * kSelBlock + threadIdx.x;
+    kv[i] = j < T ? sel_key_of(v[i], mb, j) : 0u;
+  }
+}
+
+// Passes 2 and 3: histogram of digit P of the chunk's keys that match tau's
+// first P-1 digits.  grid (chunks, B), block 256.
+template <int P>
+__global__ __launch_bounds__(kSelBlock) void k_sel_refine(const float* __restrict__ imp,
+                                                          unsigned* __restrict__ sel,
+                                                          const int32_t* __restrict__ tv,
+                                                          const uint8_t* __restrict__ mask,
+                                                          int T, int t, size_t sstride) {
+  constexpr int NB = P == 2 ? kSelH2 : kSelH3;
+  constexpr int SH = P == 2 ? 10 : 0;
+  constexpr unsigned PM = P == 2 ? 0xFFE00000u : 0xFFFFFC00u;
+  __shared__ unsigned hist[NB];
+  __shared__ int sh[16];
+  const int b = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
+  unsigned* st = sel + b * sstride;
+  const float* ib = imp + static_cast<size_t>(b) * T;
+  const uint8_t* mb = mask ? mask + static_cast<size_t>(b) * T : nullptr;
+  unsigned kv[kSelPer];
+  sel_load_strided(ib, mb, T, g, kv);  // in flight while the prefix is found
+  for (int i = tid; i < NB; i += kSelBlock) hist[i] = 0;
+  unsigned pre;
+  int rest;
+  sel_prefix<P>(st, tv ? tv[b] : t, sh, &pre, &rest);
+#pragma unroll
+  for (int i = 0; i < kSelPer; ++i) {
+    const int j = g * kSelChunk + i * kSelBlock + tid;
+    if (j < T && (kv[i] & PM) == pre) atomicAdd(&hist[(kv[i] >> SH) & (NB - 1)], 1u);
   }
   __syncthreads();
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < (kSelThreads / 64) * 256; i += kSelThreads) (&hist[0][0])[i] = 0;
-    __syncthreads();
-    const unsigned int prefix = s_prefix, mask = s_mask;
-    unsigned int* hw = hist[wave];
-    if (PER > 0) {
-#pragma unroll
-      for (int i = 0; i < NR; ++i)
-        if (c0 + i < c1 && (kv[i] & mask) == prefix) atomicAdd(&hw[(kv[i] >> shift) & 255u], 1u);
-    } else {
-      for (int j0 = 0; j0 < T; j0 += kSelThreads) {
-        const int j = j0 + tid;
-        bool in = false;
-        unsigned int dig = 0;
-        if (j < T) {
-          if (shift == 24 && u[j] >= 0x7f800000u) s_bad = 1;  // inf / nan (non-negative inputs)
-          const unsigned int v = key(j);
-          in = (v & mask) == prefix;
-          dig = (v >> shift) & 255u;
-        }
-        if (in) atomicAdd(&hw[dig], 1u);
-      }
-    }
-    __syncthreads();
-    // digit of the need-th largest: scan the bins from the top (bin 255 first)
-    unsigned int h = 0;
-    if (tid < 256)
-      for (int w = 0; w < kSelThreads / 64; ++w) h += hist[w][255 - tid];
-    int tot;
-    const int above = block_exclusive_scan(static_cast<int>(h), scratch, &tot);
-    const int need = s_need;
-    __syncthreads();
-    if (tid < 256 && above < need && above + static_cast<int>(h) >= need) {
-      s_need = need - above;
-      s_prefix = prefix | (static_cast<unsigned int>(255 - tid) << shift);
-      s_mask = mask | (255u << shift);
-    }
-    __syncthreads();
-  }
-  const unsigned int tau = s_prefix;
-  const int need_eq = s_need;  // how many values equal to tau are kept
+  unsigned* gh = st + (P == 2 ? kSelH1 : kSelH1 + kSelH2);
+  for (int i = tid; i < NB; i += kSelBlock)
+    if (hist[i]) atomicAdd(&gh[i], hist[i]);
+}
 
-  // order-preserving compaction over the contiguous chunks
-  int n_gt = 0, n_eq = 0;
-  if (PER > 0) {
+// tau and the number of keys equal to it that are kept (chunk 0 records
+// them), and the chunk's counts above and equal to tau.  grid (chunks, B).
+__global__ __launch_bounds__(kSelBlock) void k_sel_count(const float* __restrict__ imp,
+                                                         unsigned* __restrict__ sel,
+                                                         const int32_t* __restrict__ tv,
+                                                         const uint8_t* __restrict__ mask, int T,
+                                                         int t, size_t sstride) {
+  __shared__ int sh[16];
+  const int b = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
+  unsigned* st = sel + b * sstride;
+  const float* ib = imp + static_cast<size_t>(b) * T;
+  const uint8_t* mb = mask ? mask + static_cast<size_t>(b) * T : nullptr;
+  unsigned kv[kSelPer];
+  sel_load_strided(ib, mb, T, g, kv);
+  unsigned tau;
+  int need_eq;
+  sel_prefix<4>(st, tv ? tv[b] : t, sh, &tau, &need_eq);
+  int gt = 0, eq = 0;
 #pragma unroll
-    for (int i = 0; i < NR; ++i)
-      if (c0 + i < c1) {
-        n_gt += kv[i] > tau;
-        n_eq += kv[i] == tau;
-      }
-  } else {
-    for (int j = c0; j < c1; ++j) {
-      const unsigned int v = key(j);
-      n_gt += v > tau;
-      n_eq += v == tau;
+  for (int i = 0; i < kSelPer; ++i) {
+    const int j = g * kSelChunk + i * kSelBlock + tid;
+    if (j < T) {
+      gt += kv[i] > tau;
+      eq += kv[i] == tau;
     }
   }
-  int tot;
-  const int eq_before = block_exclusive_scan(n_eq, scratch, &tot);
-  const int take_eq = max(0, min(n_eq, need_eq - eq_before));
-  const int pos0 = block_exclusive_scan(n_gt + take_eq, scratch, &tot);
-  int32_t* out = idx + static_cast<size_t>(b) * t;
-  int pos = pos0, eq_taken = 0;
-  if (PER > 0) {
+  int tgt, teq;
+  scan256(gt, sh, &tgt);
+  scan256(eq, sh, &teq);
+  if (tid == 0) {
+    st[kSelCnt + 2 * g] = static_cast<unsigned>(tgt);
+    st[kSelCnt + 2 * g + 1] = static_cast<unsigned>(teq);
+    if (g == 0) {
+      st[kSelTau] = tau;
+      st[kSelTau + 1] = static_cast<unsigned>(need_eq);
+    }
+  }
+}
+
+// Order-preserving compaction: chunk g starts after the keys kept by the
+// chunks before it (all above tau, plus the equal ones while need_eq lasts);
+// inside the chunk each thread takes 16 contiguous keys, in thread order.
+// idx [B][t]: the tb = tv[b] (or t) kept indices ascending, -1 in the
+// remaining slots.  grid (chunks, B).
+__global__ __launch_bounds__(kSelBlock) void k_sel_compact(const float* __restrict__ imp,
+                                                           const unsigned* __restrict__ sel,
+                                                           int32_t* __restrict__ idx,
+                                                           const int32_t* __restrict__ tv,
+                                                           const uint8_t* __restrict__ mask,
+                                                           int T, int t, size_t sstride) {
+  __shared__ int sh[16];
+  __shared__ int s_base[2];
+  const int b = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
+  const unsigned* st = sel + b * sstride;
+  const float* ib = imp + static_cast<size_t>(b) * T;
+  const uint8_t* mb = mask ? mask + static_cast<size_t>(b) * T : nullptr;
+  const int j0 = g * kSelChunk + tid * kSelPer;
+  float v[kSelPer];
+  if (j0 + kSelPer <= T && (T & 3) == 0) {
+    // whole and 16-byte aligned: four 16-byte loads
 #pragma unroll
-    for (int i = 0; i < NR; ++i)
-      if (c0 + i < c1) {
-        bool keep = kv[i] > tau;
-        if (kv[i] == tau && eq_taken < take_eq) {
-          keep = true;
-          ++eq_taken;
-        }
-        if (keep) out[pos++] = c0 + i;
-      }
+    for (int q = 0; q < kSelPer / 4; ++q) {
+      const float4 w4 = *reinterpret_cast<const float4*>(ib + j0 + 4 * q);
+      v[4 * q] = w4.x;
+      v[4 * q + 1] = w4.y;
+      v[4 * q + 2] = w4.z;
+      v[4 * q + 3] = w4.w;
+    }
   } else {
-    for (int j = c0; j < c1; ++j) {
-      const unsigned int v = key(j);
-      bool keep = v > tau;
-      if (v == tau && eq_taken < take_eq) {
+#pragma unroll
+    for (int i = 0; i < kSelPer; ++i) v[i] = j0 + i < T ? ib[j0 + i] : 0.f;
+  }
+  const unsigned tau = st[kSelTau];
+  const int need_eq = static_cast<int>(st[kSelTau + 1]);
+  if (tid == 0) {
+    int kept = 0, eqb = 0;
+    for (int c = 0; c < g; ++c) {
+      const int gt = static_cast<int>(st[kSelCnt + 2 * c]);
+      const int eq = static_cast<int>(st[kSelCnt + 2 * c + 1]);
+      kept += gt + max(0, min(eq, need_eq - eqb));
+      eqb += eq;
+    }
+    s_base[0] = kept;
+    s_base[1] = eqb;
+  }
+  unsigned kv[kSelPer];
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int i = 0; i < kSelPer; ++i) {
+    kv[i] = j0 + i < T ? sel_key_of(v[i], mb, j0 + i) : 0u;
+    if (j0 + i < T) {
+      gt += kv[i] > tau;
+      eq += kv[i] == tau;
+    }
+  }
+  __syncthreads();
+  int tot;
+  const int eq_before = s_base[1] + scan256(eq, sh, &tot);
+  const int take_eq = max(0, min(eq, need_eq - eq_before));
+  int pos = s_base[0] + scan256(gt + take_eq, sh, &tot);
+  int32_t* out = idx + static_cast<size_t>(b) * t;
+  int taken = 0;
+#pragma unroll
+  for (int i = 0; i < kSelPer; ++i) {
+    const int j = j0 + i;
+    if (j < T) {
+      bool keep = kv[i] > tau;
+      if (kv[i] == tau && taken < take_eq) {
         keep = true;
-        ++eq_taken;
+        ++taken;
       }
       if (keep) out[pos++] = j;
     }
   }
-  for (int a = tb + tid; a < t; a += kSelThreads) out[a] = -1;
-  if (tid == 0 && status && s_bad) status[b] |= 4;
+  if (g == 0) {
+    const int tb = tv ? tv[b] : t;
+    for (int a = tb + tid; a < t; a += kSelBlock) out[a] = -1;
+  }
 }
 
 // out_K[b][a][:] = K[b][idx[b][a]][:], zeros where idx is -1 (unused slots
@@ -235,15 +276,15 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t count, hipStream_t st) 
   return hipGetLastError();
 }
 
-hipError_t launch_select(const float* imp, int32_t* idx, int32_t* status, const int32_t* tv,
+hipError_t launch_select(const float* imp, uint32_t* sel, int32_t* idx, const int32_t* tv,
                          const uint8_t* mask, int B, int T, int t, hipStream_t st) {
-  // keys in registers up to 32 per thread (T <= 32768), streamed beyond
-  if (T <= 32 * kSelThreads)
-    hipLaunchKernelGGL(k_select<32>, dim3(B), dim3(kSelThreads), 0, st, imp, idx, status, tv, mask,
-                       T, t);
-  else
-    hipLaunchKernelGGL(k_select<0>, dim3(B), dim3(kSelThreads), 0, st, imp, idx, status, tv, mask,
-                       T, t);
+  const dim3 grid(sel_chunks(T), B);
+  const size_t ss = sel_words(T);
+  hipLaunchKernelGGL(k_sel_refine<2>, grid, dim3(kSelBlock), 0, st, imp, sel, tv, mask, T, t, ss);
+  hipLaunchKernelGGL(k_sel_refine<3>, grid, dim3(kSelBlock), 0, st, imp, sel, tv, mask, T, t, ss);
+  hipLaunchKernelGGL(k_sel_count, grid, dim3(kSelBlock), 0, st, imp, sel, tv, mask, T, t, ss);
+  hipLaunchKernelGGL(k_sel_compact, grid, dim3(kSelBlock), 0, st, imp, sel, idx, tv, mask, T, t,
+                     ss);
   return hipGetLastError();
 }
 

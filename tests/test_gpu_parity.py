@@ -114,16 +114,20 @@ def test_nonfinite_input_is_flagged():
     assert gpu["status"][1] & 4
 
 
-@pytest.mark.parametrize("cfg,heads", [(2, [0, 7]), (3, [0, 5]), (4, [0, 131, 255]), (5, [3])])
-def test_full_configs_sampled_heads(cfg, heads):
-    """The full-size workloads, launched exactly as the benchmark times them;
-    the oracle checks a sample of heads."""
+@pytest.mark.parametrize("cfg,heads", [(2, list(range(8))), (3, list(range(8))),
+                                       (4, [0, 131, 255]), (5, [3])])
+def test_full_configs(cfg, heads):
+    """The full-size workloads, launched exactly as the benchmark times them
+    (the score kernels' full-size split counts): every head of the 8-head
+    layers, a sample of the 256-head stack and of the 128k-token layer, each
+    compared with the oracle in full, lse, O and importance included (lse
+    within 1e-4 absolute, O and importance within 1e-4 relative)."""
     w = synth.CONFIGS[cfg]
     data = synth.batch(w)
     gpu = run_gpu(w, data)
     assert (gpu["status"] == 0).all(), gpu["status"]
     for h in heads:
-        err = compare_head(gpu, h, data, w.t, _tol(w), tight=False)
+        err = compare_head(gpu, h, data, w.t, _tol(w))
         print(f"C{cfg} head {h}:", {k: (float(f"{v:.3g}") if isinstance(v, float) else v)
                                     for k, v in err.items()}, flush=True)
 
@@ -523,3 +527,33 @@ def test_omp_full_size_sampled_steps():
     err = orc.rel_l2(o_gpu, orc.attend(Qh, Kh[idx], Cv, beta))
     print("omp C3 head 1: Ohat vs oracle fits", err, flush=True)
     assert orc.rel_l2(inter["w"][h], wv) <= TOL_BF16 and err <= TOL_BF16
+
+
+@pytest.mark.slow
+def test_omp_full_size_chosen_set():
+    """One head of the 32k/50x workload: the GPU's whole pursuit against the
+    float64 oracle's.  Either the pick orders agree, or at the first step where
+    they part the GPU's pick is a near-tie of the float64 scores given the same
+    earlier picks (the two runs then continue from different residuals, so
+    later picks are not comparable one by one); the chosen sets are reported."""
+    import torch
+    import kv_cache_compaction_head_amd as kvc
+    w = dataclasses.replace(synth.CONFIGS[3], B=1)
+    data = synth.batch(w)
+    Q, K, V = (to_device(data[k]) for k in ("Q", "K", "V"))
+    res = kvc.compact_omp(Q, K, V, w.t)
+    torch.cuda.synchronize()
+    assert (res.status.cpu().numpy() == 0).all()
+    inter = {k: v.cpu().numpy() for k, v in kvc.intermediates(res).items()}
+    order = inter["omp_order"][0].astype(np.int64)
+    Qh, Kh, Vh = (synth.to_f64(data[k][0]) for k in ("Q", "K", "V"))
+    ref = orc.compact_omp(Qh, Kh, Vh, w.t)
+    common = len(set(order.tolist()) & set(ref["order"].tolist()))
+    same = np.array_equal(order, ref["order"])
+    print(f"omp C3 head 0: same order {same}, chosen sets share {common} of {w.t}", flush=True)
+    if not same:
+        k = int(np.flatnonzero(order != ref["order"])[0])
+        P = orc.omp_dictionary(Qh, Kh, ref["lse"])
+        near = _omp_replay(P, order, [k])
+        print(f"first divergence at step {k}: near-tie {k in near}", flush=True)
+        assert k in near, (k, near)

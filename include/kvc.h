@@ -37,13 +37,14 @@
  *     instrumentation and the wait limit below), so calls with distinct
  *     workspaces may be issued from several host threads; two calls that
  *     share a workspace must be ordered on one stream;
- *   - the fits run as cooperative launches (hipLaunchCooperativeKernel) whose
- *     grid is sized to what the whole device holds at once; HIP guarantees
- *     co-residency only within one such launch, so compactions that should
- *     all succeed must not overlap in time on the device (issue them on one
- *     stream, or synchronize between streams).  If they do overlap, a fit
- *     team's wait may run out: every wait is bounded, so the call still ends,
- *     and the affected heads report KVC_STATUS_SYNC_TIMEOUT.
+ *   - the fits run as launches whose grid is sized to what the whole device
+ *     holds at once (their teams of workgroups wait for each other), which
+ *     assumes the device is not busy with other long-running work meanwhile:
+ *     compactions that should all succeed must not overlap in time on the
+ *     device (issue them on one stream, or synchronize between streams).  If
+ *     they do overlap, a fit team's wait may run out: every wait is bounded,
+ *     so the call still ends, and the affected heads report
+ *     KVC_STATUS_SYNC_TIMEOUT.
  */
 #ifndef KVC_H_
 #define KVC_H_

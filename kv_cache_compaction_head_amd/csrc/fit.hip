@@ -440,9 +440,14 @@ __global__ __launch_bounds__(1024) void k_bias_prep(double* __restrict__ S, size
 }
 
 // Teams.  The iterative parts of the fits (the NNLS pivoting rounds and the
-// value system's sweeps) run in cooperative launches:
-// each head gets a team of g co-resident workgroups synchronised by
-// team_sync, a barrier through per-member flags in global memory.
+// value system's sweeps) run in launches whose grid is no larger than what
+// the device holds at once (occupancy times compute units), so on a device
+// not busy with other long-running work every workgroup is resident: each
+// head gets a team of g workgroups synchronised by team_sync, a barrier
+// through per-member flags in global memory.  (Plain launches: a
+// cooperative launch would add nothing these barriers use, and HIP tears its
+// dedicated queue down at process exit, after tools such as a profiler may
+// already have torn down the runtime below it.)
 //
 // Placement and coherence: workgroups are dispatched round-robin over the
 // XCDs, so with nteams a multiple of 8, team = blockIdx mod nteams keeps a
@@ -2135,7 +2140,7 @@ __global__ void k_write_out(const double* __restrict__ Cb, size_t sS, int ld,
 // Host launchers.
 // ---------------------------------------------------------------------------
 
-// Co-resident workgroups of a team kernel on the current device (cached).
+// Workgroups of a team kernel the current device holds at once (cached).
 static int coop_capacity(const void* func) {
   static int cache[2][64] = {};
   const int which = func == reinterpret_cast<const void*>(&k_nnls_sweep) ? 0 : 1;
@@ -2229,7 +2234,7 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
                      ridge);
   hipLaunchKernelGGL(k_bias_prep, dim3((t + 15) / 16, B), dim3(1024), 0, st, fb.S, sS, ld, fb.cvec,
                      fb.lam, fb.tv, t);
-  // pivoting rounds: one cooperative launch, a team per head
+  // pivoting rounds: one launch, a team per head
   prof_mark(5, false, st);
   int cap = coop_capacity(reinterpret_cast<const void*>(&k_nnls_sweep));
   if (cap <= 0) return hipErrorLaunchFailure;
@@ -2247,8 +2252,8 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
                     &fb.Fidx, &fb.inv, &fb.msz,    &status, &fb.bar, &err,    &fb.xcc,
                     &fb.flops, &tvp,   &B,        &t,         &max_iters, &tx, &fb.wait_ticks,
                     &psp,     &n,      &cvp,      &fb.lam,   &ridge};
-    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_nnls_sweep), dim3(grid),
-                                   dim3(kTeamThreads), args, 0, st);
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&k_nnls_sweep), dim3(grid),
+                        dim3(kTeamThreads), args, 0, st);
     if (e != hipSuccess) return e;
   }
   prof_mark(5, true, st);
@@ -2278,8 +2283,8 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
     const int32_t* ms = fb.msz;
     void* args[] = {&fb.S, &sS,     &ld,  &r_al, &fb.U,     &fb.V, &sUV, &fb.stage, &ms,
                     &status, &fb.bar, &err, &fb.xcc, &fb.flops, &B,    &Dv,  &tx, &fb.wait_ticks};
-    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_value_sweep), dim3(grid),
-                                   dim3(kTeamThreads), args, 0, st);
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&k_value_sweep), dim3(grid),
+                        dim3(kTeamThreads), args, 0, st);
     if (e != hipSuccess) return e;
   }
   prof_mark(12, true, st);

@@ -277,6 +277,13 @@ def main():
         Be, Te, te = B * args.chunks, T // args.chunks, w.t // args.chunks
     elif args.variant == "ragged":
         te = max(variant["budgets"])
+    # fitted keys per entry (the order of its bias system): the budget, a
+    # ragged head's own budget, or what the protected keys leave
+    t_fit = np.full(Be, te, dtype=np.float64)
+    if args.variant == "ragged":
+        t_fit = np.array(variant["budgets"], dtype=np.float64)
+    elif args.variant == "protected":
+        t_fit = w.t - np.minimum(prot_host.sum(axis=1), w.t - 1).astype(np.float64)
     nqb = -(-n // 128)
     mm_peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     inter = kvc.intermediates(res)
@@ -293,7 +300,8 @@ def main():
     #                  the compaction: four launches), algorithmically one read of
     #                  imp and the idx write: 4 T B + 4 t B
     #   k_gather_rows  reads and writes the kept K rows: 2 t d es B
-    #   Grams          n t^2 per entry (symmetric half; value Gram: n m^2, m passive)
+    #   Grams          n t^2 per entry, t its fitted keys (symmetric half; value Gram:
+    #                  n m^2, m passive)
     #   k_nnls_sweep   the block sweeps of the pivoting rounds (counted on device)
     #   k_value_sweep  the value system's block sweeps (counted on device)
     work = {"score_lse": ("k_score_lse", 2.0 * n * Te * d * Be, mm_peak, "mfma"),
@@ -301,7 +309,7 @@ def main():
             "imp_reduce": ("k_imp_reduce", 4.0 * Te * (nqb + 1) * Be, PEAK_HBM_GBS, "hbm"),
             "topt": ("k_sel_* (refine x2, count, compact)", 4.0 * (Te + te) * Be, PEAK_HBM_GBS, "hbm"),
             "gather": ("k_gather_rows", 2.0 * te * d * es * Be, PEAK_HBM_GBS, "hbm"),
-            "gram": ("k_atb (mass Gram)", float(n) * te * te * Be, PEAK_F64_TFLOPS, "mfma"),
+            "gram": ("k_atb (mass Gram)", float(n * (t_fit ** 2).sum()), PEAK_F64_TFLOPS, "mfma"),
             "value_gram": ("k_atb (value Gram)", float(n * (m_pass.astype(float) ** 2).sum()),
                            PEAK_F64_TFLOPS, "mfma"),
             "nnls": ("k_nnls_sweep", float(fit_flops[0]), PEAK_F64_TFLOPS, "mfma"),

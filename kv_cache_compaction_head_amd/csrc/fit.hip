@@ -445,9 +445,9 @@ __global__ __launch_bounds__(1024) void k_bias_prep(double* __restrict__ S, size
 // not busy with other long-running work every workgroup is resident: each
 // head gets a team of g workgroups synchronised by team_sync, a barrier
 // through per-member flags in global memory.  (Plain launches: a
-// cooperative launch would add nothing these barriers use, and HIP tears its
-// dedicated queue down at process exit, after tools such as a profiler may
-// already have torn down the runtime below it.)
+// cooperative launch would add nothing these barriers use, and under a
+// profiler a process that had made one crashed in the HIP runtime's exit
+// handler.)
 //
 // Placement and coherence: workgroups are dispatched round-robin over the
 // XCDs, so with nteams a multiple of 8, team = blockIdx mod nteams keeps a

@@ -748,7 +748,8 @@ __device__ __forceinline__ gdouble* uniform(gdouble* p) {
 }
 __device__ __forceinline__ SweepMat uniform_mat(const SweepMat& m) {
   return SweepMat{uniform(m.S),     uniform(m.U),    uniform(m.V),     uniform(m.stage),
-                  uniform(m.ld),    uniform(m.r_al), uniform(m.n_rhs), uniform(m.n_var)};
+                  uniform(m.ld),    uniform(m.r_al), uniform(m.n_rhs), uniform(m.n_var),
+                  uniform(const_cast<gdouble*>(m.dg0))};
 }
 
 __device__ __forceinline__ size_t s_idx(const SweepMat& M, int i, int j) {

@@ -859,216 +859,1332 @@ __device__ __forceinline__ double recip(double d) {
 // wave: lane c holds column c of the block, a[r] = A[o + r][o + c] (the
 // four rows of lanes compute the same thing; the first one stores).  The
 // pivot row is then lane-local (A[M][c] = a[M]); the pivot column A[r][M]
-// comes from lane M through a DPP row broadcast fused into the update FMA,
-// v_fmac_f64 with row_newbcast on its first source, so a pivot costs one
-// FMA per row and no separate data movement.
+// comes from lane M through a DPP row broadcast fused into the update FMA
+// (v_fmac_f64 with row_newbcast on its first source), so a row update costs
+// one FMA and no separate data movement.
 //
-// a[r] += a[r] of lane M * be for the listed rows.  A VALU write of a DPP
-// source register needs two wait states before the DPP read: one s_nop 1
-// ahead of each group.  sweep_next<M> updates row M + 1 (the next pivot's
-// row, on the dependence chain) alone; sweep_rest<M> the rows other than M
-// and M + 1.
-#define KVC_FMAC_DPP(i) "v_fmac_f64_dpp %" #i ", %" #i ", %[be] row_newbcast:%[m] row_mask:0xf bank_mask:0xf\n"
-#define KVC_FMAC_DPP(i) "v_fmac_f64_dpp %" #i ", %" #i ", %[be] row_newbcast:%[m] row_mask:0xf bank_mask:0xf\n"
-template <int M> __device__ __forceinline__ void sweep_next(double (&a)[16], double be);
-template <int M> __device__ __forceinline__ void sweep_rest(double (&a)[16], double be);
-template <> __device__ __forceinline__ void sweep_next<0>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[1]) : [be] "v"(be), [m] "n"(0));
-}
-template <> __device__ __forceinline__ void sweep_rest<0>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
-      : "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
-      : [be] "v"(be), [m] "n"(0));
-}
-template <> __device__ __forceinline__ void sweep_next<1>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[2]) : [be] "v"(be), [m] "n"(1));
-}
-template <> __device__ __forceinline__ void sweep_rest<1>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
-      : "+v"(a[0]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
-      : [be] "v"(be), [m] "n"(1));
-}
-template <> __device__ __forceinline__ void sweep_next<2>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[3]) : [be] "v"(be), [m] "n"(2));
-}
-template <> __device__ __forceinline__ void sweep_rest<2>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
-      : "+v"(a[0]), "+v"(a[1]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
-      : [be] "v"(be), [m] "n"(2));
-}
-template <> __device__ __forceinline__ void sweep_next<3>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[4]) : [be] "v"(be), [m] "n"(3));
-}
-template <> __device__ __forceinline__ void sweep_rest<3>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
-      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
-      : [be] "v"(be), [m] "n"(3));
-}
-template <> __device__ __forceinline__ void sweep_next<4>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[5]) : [be] "v"(be), [m] "n"(4));
-}
-template <> __device__ __forceinline__ void sweep_rest<4>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
-      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
-      : [be] "v"(be), [m] "n"(4));
-}
-template <> __device__ __forceinline__ void sweep_next<5>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[6]) : [be] "v"(be), [m] "n"(5));
-}
-template <> __device__ __forceinline__ void sweep_rest<5>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
-      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
-      : [be] "v"(be), [m] "n"(5));
-}
-template <> __device__ __forceinline__ void sweep_next<6>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[7]) : [be] "v"(be), [m] "n"(6));
-}
-template <> __device__ __forceinline__ void sweep_rest<6>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
-      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
-      : [be] "v"(be), [m] "n"(6));
-}
-template <> __device__ __forceinline__ void sweep_next<7>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[8]) : [be] "v"(be), [m] "n"(7));
-}
-template <> __device__ __forceinline__ void sweep_rest<7>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
-      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
-      : [be] "v"(be), [m] "n"(7));
-}
-template <> __device__ __forceinline__ void sweep_next<8>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[9]) : [be] "v"(be), [m] "n"(8));
-}
-template <> __device__ __forceinline__ void sweep_rest<8>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
-      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
-      : [be] "v"(be), [m] "n"(8));
-}
-template <> __device__ __forceinline__ void sweep_next<9>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[10]) : [be] "v"(be), [m] "n"(9));
-}
-template <> __device__ __forceinline__ void sweep_rest<9>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
-      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
-      : [be] "v"(be), [m] "n"(9));
-}
-template <> __device__ __forceinline__ void sweep_next<10>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[11]) : [be] "v"(be), [m] "n"(10));
-}
-template <> __device__ __forceinline__ void sweep_rest<10>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
-      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
-      : [be] "v"(be), [m] "n"(10));
-}
-template <> __device__ __forceinline__ void sweep_next<11>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[12]) : [be] "v"(be), [m] "n"(11));
-}
-template <> __device__ __forceinline__ void sweep_rest<11>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
-      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
-      : [be] "v"(be), [m] "n"(11));
-}
-template <> __device__ __forceinline__ void sweep_next<12>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[13]) : [be] "v"(be), [m] "n"(12));
-}
-template <> __device__ __forceinline__ void sweep_rest<12>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
-      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[14]), "+v"(a[15])
-      : [be] "v"(be), [m] "n"(12));
-}
-template <> __device__ __forceinline__ void sweep_next<13>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[14]) : [be] "v"(be), [m] "n"(13));
-}
-template <> __device__ __forceinline__ void sweep_rest<13>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
-      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[15])
-      : [be] "v"(be), [m] "n"(13));
-}
-template <> __device__ __forceinline__ void sweep_next<14>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) : "+v"(a[15]) : [be] "v"(be), [m] "n"(14));
-}
-template <> __device__ __forceinline__ void sweep_rest<14>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13)
-      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13])
-      : [be] "v"(be), [m] "n"(14));
-}
-template <> __device__ __forceinline__ void sweep_rest<15>(double (&a)[16], double be) {
-  asm("s_nop 1\n" KVC_FMAC_DPP(0) KVC_FMAC_DPP(1) KVC_FMAC_DPP(2) KVC_FMAC_DPP(3) KVC_FMAC_DPP(4) KVC_FMAC_DPP(5) KVC_FMAC_DPP(6) KVC_FMAC_DPP(7) KVC_FMAC_DPP(8) KVC_FMAC_DPP(9) KVC_FMAC_DPP(10) KVC_FMAC_DPP(11) KVC_FMAC_DPP(12) KVC_FMAC_DPP(13) KVC_FMAC_DPP(14)
-      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]), "+v"(a[14])
-      : [be] "v"(be), [m] "n"(15));
-}
-#undef KVC_FMAC_DPP
-
-// The pivot test, as one product: pivot d passes when d * f > 1.  A variable
-// swept in (sign +1) needs d > kPivotRel * dg, dg its diagonal before any
-// sweep: d / dg is the squared sine of the angle between its column and the
-// span of the variables already swept, so a smaller ratio means the column
-// is numerically in that span (f = 1 / (kPivotRel dg); with no dg, f = inf
-// and only d > 0 is asked).  A variable swept out (sign -1) needs d < 0
-// (f = -1e300); an identity row past the block passes (d = 1, f = 2).
-constexpr double kPivotRel = 1e-12;
-__device__ __forceinline__ double pivot_test(bool in, double sgn, double dg) {
-  if (!in) return 2.0;
-  return sgn > 0.0 ? 1.0 / (kPivotRel * dg) : -1e300;
-}
-
-// Pivot M: d = A[M][M] (lane M), rd = 1/d.  The other columns lose
-// A[r][M] A[M][c]/d (be = -A[M][c]/d); the pivot row becomes A[M][c]/d; the
-// pivot column would scale by 1/d: instead of rewriting its rows, the pivot
-// lane records 1/d as its column scale sc (be = 0 leaves its rows as they
-// are).  A swept column's stored values are its true values over sc, and the
-// updates of later pivots need no correction (the scale of the pivot column
-// is still 1 when it is swept, and a lane's own scale cancels out of its
-// update); only the L^-1 record reads true values.  lcol[M] records row M of
-// the block's L^-1 at column c (-A[M][c] at the swept columns c < M, 1 at
-// c = M, 0 after).
+// Pivot M, with d = A[M][M] and s, thr its sign and threshold:
+//   ok  = d s > thr (a failed pivot is replaced by s, so 1/s = s)
+//   r   = 1/d (hardware estimate + two Newton-Raphson steps)
+//   be  = -A[M][c] r off the pivot lane, 0 on it
+//   a[i] += A[i][M] be for every row i != M;
+// the pivot row becomes A[M][c] r (tm), -1 on the pivot lane.  Instead of
+// rewriting the pivot column by 1/d, the pivot lane records r as its column
+// scale sc (be = 0 leaves its rows as they are): a swept column's stored
+// values are its true values over sc, and the updates of later pivots need
+// no correction (the scale of the pivot column is still 1 when it is swept,
+// and a lane's own scale cancels out of its update); only the L^-1 record
+// reads true values.  lcol[M] records row M of the block's L^-1 at column c
+// (-A[M][c] at the swept columns c < M, 1 at c = M, 0 after).
+//
+// The chain from one pivot to the next is d -> ok -> r -> be -> the update
+// of row M + 1 (the next pivot's row).  Each pivot's block therefore updates
+// rows M + 1 and M + 2 at once and leaves its other 13 rows to the next
+// block, whose instructions interleave them with its own dependent chain
+// (the waves issue in order, so independent work has to sit between the
+// dependent steps to hide their latency).  Hand-scheduled asm, with the
+// wait states the hardware asks for: two between a VALU write of a register
+// and its read through DPP (the s_nop 1 that opens each block covers
+// whatever the compiler placed between blocks; inside a block the deferred
+// row of M + 3 comes first, ahead of the next block's update of that row),
+// one between the reciprocal estimate and its first use.  ok is the same in
+// every lane (d, s and thr are), so the substitution of s for d is a move
+// under an exec mask built from it; `bad` collects the lanes of failed
+// pivots.
+struct DiagTmp {
+  double x, y, r, tm, be, bp, sg, thr;
+  unsigned long long sv, bad;
+};
+// sgl, thrl: lane c's own pivot's sign and threshold (broadcast from lane M
+// inside block M); nn: 0 on the pivot lane, -1 elsewhere
 template <int M>
-__device__ __forceinline__ void diag_pivot(double (&a)[16], double (&lcol)[16],
-                                           const double (&sgv)[16], int c, double& sc,
-                                           bool& bad) {
-  const double d = rdlane(a[M], M);
-  const double sg = sgv[M];
-  // a failed pivot is replaced by its sign (1/s = s); the test runs beside
-  // the reciprocal instead of ahead of it
-  const bool ok = d * sg > 1.0;
-  bad |= !ok;
-  const double rd = ok ? recip(d) : (sg > 0.0 ? 1.0 : -1.0);
-  const double rowm = a[M];
-  lcol[M] = c < M ? -(rowm * sc) : (c == M ? 1.0 : 0.0);
+__device__ __forceinline__ void diag_blk(double (&a)[16], DiagTmp& z, double sgl, double thrl,
+                                         double nn);
+template <> __device__ __forceinline__ void diag_blk<0>(double (&a)[16], DiagTmp& z, double sgl,
+                                                      double thrl, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a0] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[sg], %[sgl] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[thr], %[thrl] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a0], %[nn]\n"
+      "v_mul_f64 %[x], %[y], %[sg]\n"
+      "v_cmp_lt_f64_e32 vcc, %[thr], %[x]\n"
+      "v_mov_b64_e32 %[x], %[sg]\n"
+      "s_and_saveexec_b64 %[sv], vcc\n"
+      "v_mov_b64_e32 %[x], %[y]\n"
+      "s_mov_b64 exec, %[sv]\n"
+      "s_andn2_b64 %[sv], %[sv], vcc\n"
+      "s_or_b64 %[bad], %[bad], %[sv]\n"
+      "v_rcp_f64_e32 %[r], %[x]\n"
+      "s_nop 0\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_mul_f64 %[tm], %[a0], %[r]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[be] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[be] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [tm] "=&v"(z.tm), [be] "=&v"(z.be),
+        [sg] "=&v"(z.sg), [thr] "=&v"(z.thr), [sv] "=&s"(z.sv), [bad] "+s"(z.bad)
+      : [bp] "v"(z.bp), [sgl] "v"(sgl), [thrl] "v"(thrl), [nn] "v"(nn)
+      : "vcc");
+}
+template <> __device__ __forceinline__ void diag_blk<1>(double (&a)[16], DiagTmp& z, double sgl,
+                                                      double thrl, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a1] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[sg], %[sgl] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[thr], %[thrl] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a1], %[nn]\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[x], %[y], %[sg]\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_cmp_lt_f64_e32 vcc, %[thr], %[x]\n"
+      "v_mov_b64_e32 %[x], %[sg]\n"
+      "s_and_saveexec_b64 %[sv], vcc\n"
+      "v_mov_b64_e32 %[x], %[y]\n"
+      "s_mov_b64 exec, %[sv]\n"
+      "s_andn2_b64 %[sv], %[sv], vcc\n"
+      "s_or_b64 %[bad], %[bad], %[sv]\n"
+      "v_rcp_f64_e32 %[r], %[x]\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[tm], %[a1], %[r]\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[be] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[be] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [tm] "=&v"(z.tm), [be] "=&v"(z.be),
+        [sg] "=&v"(z.sg), [thr] "=&v"(z.thr), [sv] "=&s"(z.sv), [bad] "+s"(z.bad)
+      : [bp] "v"(z.bp), [sgl] "v"(sgl), [thrl] "v"(thrl), [nn] "v"(nn)
+      : "vcc");
+}
+template <> __device__ __forceinline__ void diag_blk<2>(double (&a)[16], DiagTmp& z, double sgl,
+                                                      double thrl, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a2] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[sg], %[sgl] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[thr], %[thrl] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a2], %[nn]\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[x], %[y], %[sg]\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_cmp_lt_f64_e32 vcc, %[thr], %[x]\n"
+      "v_mov_b64_e32 %[x], %[sg]\n"
+      "s_and_saveexec_b64 %[sv], vcc\n"
+      "v_mov_b64_e32 %[x], %[y]\n"
+      "s_mov_b64 exec, %[sv]\n"
+      "s_andn2_b64 %[sv], %[sv], vcc\n"
+      "s_or_b64 %[bad], %[bad], %[sv]\n"
+      "v_rcp_f64_e32 %[r], %[x]\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[tm], %[a2], %[r]\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[be] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[be] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [tm] "=&v"(z.tm), [be] "=&v"(z.be),
+        [sg] "=&v"(z.sg), [thr] "=&v"(z.thr), [sv] "=&s"(z.sv), [bad] "+s"(z.bad)
+      : [bp] "v"(z.bp), [sgl] "v"(sgl), [thrl] "v"(thrl), [nn] "v"(nn)
+      : "vcc");
+}
+template <> __device__ __forceinline__ void diag_blk<3>(double (&a)[16], DiagTmp& z, double sgl,
+                                                      double thrl, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a3] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[sg], %[sgl] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[thr], %[thrl] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a3], %[nn]\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[x], %[y], %[sg]\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_cmp_lt_f64_e32 vcc, %[thr], %[x]\n"
+      "v_mov_b64_e32 %[x], %[sg]\n"
+      "s_and_saveexec_b64 %[sv], vcc\n"
+      "v_mov_b64_e32 %[x], %[y]\n"
+      "s_mov_b64 exec, %[sv]\n"
+      "s_andn2_b64 %[sv], %[sv], vcc\n"
+      "s_or_b64 %[bad], %[bad], %[sv]\n"
+      "v_rcp_f64_e32 %[r], %[x]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[tm], %[a3], %[r]\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[be] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[be] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [tm] "=&v"(z.tm), [be] "=&v"(z.be),
+        [sg] "=&v"(z.sg), [thr] "=&v"(z.thr), [sv] "=&s"(z.sv), [bad] "+s"(z.bad)
+      : [bp] "v"(z.bp), [sgl] "v"(sgl), [thrl] "v"(thrl), [nn] "v"(nn)
+      : "vcc");
+}
+template <> __device__ __forceinline__ void diag_blk<4>(double (&a)[16], DiagTmp& z, double sgl,
+                                                      double thrl, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a4] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[sg], %[sgl] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[thr], %[thrl] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a4], %[nn]\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[x], %[y], %[sg]\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_cmp_lt_f64_e32 vcc, %[thr], %[x]\n"
+      "v_mov_b64_e32 %[x], %[sg]\n"
+      "s_and_saveexec_b64 %[sv], vcc\n"
+      "v_mov_b64_e32 %[x], %[y]\n"
+      "s_mov_b64 exec, %[sv]\n"
+      "s_andn2_b64 %[sv], %[sv], vcc\n"
+      "s_or_b64 %[bad], %[bad], %[sv]\n"
+      "v_rcp_f64_e32 %[r], %[x]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[tm], %[a4], %[r]\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[be] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[be] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [tm] "=&v"(z.tm), [be] "=&v"(z.be),
+        [sg] "=&v"(z.sg), [thr] "=&v"(z.thr), [sv] "=&s"(z.sv), [bad] "+s"(z.bad)
+      : [bp] "v"(z.bp), [sgl] "v"(sgl), [thrl] "v"(thrl), [nn] "v"(nn)
+      : "vcc");
+}
+template <> __device__ __forceinline__ void diag_blk<5>(double (&a)[16], DiagTmp& z, double sgl,
+                                                      double thrl, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a5] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[sg], %[sgl] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[thr], %[thrl] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a5], %[nn]\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[x], %[y], %[sg]\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_cmp_lt_f64_e32 vcc, %[thr], %[x]\n"
+      "v_mov_b64_e32 %[x], %[sg]\n"
+      "s_and_saveexec_b64 %[sv], vcc\n"
+      "v_mov_b64_e32 %[x], %[y]\n"
+      "s_mov_b64 exec, %[sv]\n"
+      "s_andn2_b64 %[sv], %[sv], vcc\n"
+      "s_or_b64 %[bad], %[bad], %[sv]\n"
+      "v_rcp_f64_e32 %[r], %[x]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[tm], %[a5], %[r]\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[be] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[be] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [tm] "=&v"(z.tm), [be] "=&v"(z.be),
+        [sg] "=&v"(z.sg), [thr] "=&v"(z.thr), [sv] "=&s"(z.sv), [bad] "+s"(z.bad)
+      : [bp] "v"(z.bp), [sgl] "v"(sgl), [thrl] "v"(thrl), [nn] "v"(nn)
+      : "vcc");
+}
+template <> __device__ __forceinline__ void diag_blk<6>(double (&a)[16], DiagTmp& z, double sgl,
+                                                      double thrl, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a6] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[sg], %[sgl] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[thr], %[thrl] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a6], %[nn]\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[x], %[y], %[sg]\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_cmp_lt_f64_e32 vcc, %[thr], %[x]\n"
+      "v_mov_b64_e32 %[x], %[sg]\n"
+      "s_and_saveexec_b64 %[sv], vcc\n"
+      "v_mov_b64_e32 %[x], %[y]\n"
+      "s_mov_b64 exec, %[sv]\n"
+      "s_andn2_b64 %[sv], %[sv], vcc\n"
+      "s_or_b64 %[bad], %[bad], %[sv]\n"
+      "v_rcp_f64_e32 %[r], %[x]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[tm], %[a6], %[r]\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[be] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[be] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [tm] "=&v"(z.tm), [be] "=&v"(z.be),
+        [sg] "=&v"(z.sg), [thr] "=&v"(z.thr), [sv] "=&s"(z.sv), [bad] "+s"(z.bad)
+      : [bp] "v"(z.bp), [sgl] "v"(sgl), [thrl] "v"(thrl), [nn] "v"(nn)
+      : "vcc");
+}
+template <> __device__ __forceinline__ void diag_blk<7>(double (&a)[16], DiagTmp& z, double sgl,
+                                                      double thrl, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a7] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[sg], %[sgl] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[thr], %[thrl] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a7], %[nn]\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[x], %[y], %[sg]\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_cmp_lt_f64_e32 vcc, %[thr], %[x]\n"
+      "v_mov_b64_e32 %[x], %[sg]\n"
+      "s_and_saveexec_b64 %[sv], vcc\n"
+      "v_mov_b64_e32 %[x], %[y]\n"
+      "s_mov_b64 exec, %[sv]\n"
+      "s_andn2_b64 %[sv], %[sv], vcc\n"
+      "s_or_b64 %[bad], %[bad], %[sv]\n"
+      "v_rcp_f64_e32 %[r], %[x]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[tm], %[a7], %[r]\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[be] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[be] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [tm] "=&v"(z.tm), [be] "=&v"(z.be),
+        [sg] "=&v"(z.sg), [thr] "=&v"(z.thr), [sv] "=&s"(z.sv), [bad] "+s"(z.bad)
+      : [bp] "v"(z.bp), [sgl] "v"(sgl), [thrl] "v"(thrl), [nn] "v"(nn)
+      : "vcc");
+}
+template <> __device__ __forceinline__ void diag_blk<8>(double (&a)[16], DiagTmp& z, double sgl,
+                                                      double thrl, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a8] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[sg], %[sgl] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[thr], %[thrl] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a8], %[nn]\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[x], %[y], %[sg]\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_cmp_lt_f64_e32 vcc, %[thr], %[x]\n"
+      "v_mov_b64_e32 %[x], %[sg]\n"
+      "s_and_saveexec_b64 %[sv], vcc\n"
+      "v_mov_b64_e32 %[x], %[y]\n"
+      "s_mov_b64 exec, %[sv]\n"
+      "s_andn2_b64 %[sv], %[sv], vcc\n"
+      "s_or_b64 %[bad], %[bad], %[sv]\n"
+      "v_rcp_f64_e32 %[r], %[x]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[tm], %[a8], %[r]\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[be] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[be] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [tm] "=&v"(z.tm), [be] "=&v"(z.be),
+        [sg] "=&v"(z.sg), [thr] "=&v"(z.thr), [sv] "=&s"(z.sv), [bad] "+s"(z.bad)
+      : [bp] "v"(z.bp), [sgl] "v"(sgl), [thrl] "v"(thrl), [nn] "v"(nn)
+      : "vcc");
+}
+template <> __device__ __forceinline__ void diag_blk<9>(double (&a)[16], DiagTmp& z, double sgl,
+                                                      double thrl, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a9] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[sg], %[sgl] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[thr], %[thrl] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a9], %[nn]\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[x], %[y], %[sg]\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_cmp_lt_f64_e32 vcc, %[thr], %[x]\n"
+      "v_mov_b64_e32 %[x], %[sg]\n"
+      "s_and_saveexec_b64 %[sv], vcc\n"
+      "v_mov_b64_e32 %[x], %[y]\n"
+      "s_mov_b64 exec, %[sv]\n"
+      "s_andn2_b64 %[sv], %[sv], vcc\n"
+      "s_or_b64 %[bad], %[bad], %[sv]\n"
+      "v_rcp_f64_e32 %[r], %[x]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[tm], %[a9], %[r]\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[be] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[be] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [tm] "=&v"(z.tm), [be] "=&v"(z.be),
+        [sg] "=&v"(z.sg), [thr] "=&v"(z.thr), [sv] "=&s"(z.sv), [bad] "+s"(z.bad)
+      : [bp] "v"(z.bp), [sgl] "v"(sgl), [thrl] "v"(thrl), [nn] "v"(nn)
+      : "vcc");
+}
+template <> __device__ __forceinline__ void diag_blk<10>(double (&a)[16], DiagTmp& z, double sgl,
+                                                      double thrl, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a10] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[sg], %[sgl] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[thr], %[thrl] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a10], %[nn]\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[x], %[y], %[sg]\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_cmp_lt_f64_e32 vcc, %[thr], %[x]\n"
+      "v_mov_b64_e32 %[x], %[sg]\n"
+      "s_and_saveexec_b64 %[sv], vcc\n"
+      "v_mov_b64_e32 %[x], %[y]\n"
+      "s_mov_b64 exec, %[sv]\n"
+      "s_andn2_b64 %[sv], %[sv], vcc\n"
+      "s_or_b64 %[bad], %[bad], %[sv]\n"
+      "v_rcp_f64_e32 %[r], %[x]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[tm], %[a10], %[r]\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[be] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[be] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [tm] "=&v"(z.tm), [be] "=&v"(z.be),
+        [sg] "=&v"(z.sg), [thr] "=&v"(z.thr), [sv] "=&s"(z.sv), [bad] "+s"(z.bad)
+      : [bp] "v"(z.bp), [sgl] "v"(sgl), [thrl] "v"(thrl), [nn] "v"(nn)
+      : "vcc");
+}
+template <> __device__ __forceinline__ void diag_blk<11>(double (&a)[16], DiagTmp& z, double sgl,
+                                                      double thrl, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a11] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[sg], %[sgl] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[thr], %[thrl] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a11], %[nn]\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[x], %[y], %[sg]\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_cmp_lt_f64_e32 vcc, %[thr], %[x]\n"
+      "v_mov_b64_e32 %[x], %[sg]\n"
+      "s_and_saveexec_b64 %[sv], vcc\n"
+      "v_mov_b64_e32 %[x], %[y]\n"
+      "s_mov_b64 exec, %[sv]\n"
+      "s_andn2_b64 %[sv], %[sv], vcc\n"
+      "s_or_b64 %[bad], %[bad], %[sv]\n"
+      "v_rcp_f64_e32 %[r], %[x]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[tm], %[a11], %[r]\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[be] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[be] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [tm] "=&v"(z.tm), [be] "=&v"(z.be),
+        [sg] "=&v"(z.sg), [thr] "=&v"(z.thr), [sv] "=&s"(z.sv), [bad] "+s"(z.bad)
+      : [bp] "v"(z.bp), [sgl] "v"(sgl), [thrl] "v"(thrl), [nn] "v"(nn)
+      : "vcc");
+}
+template <> __device__ __forceinline__ void diag_blk<12>(double (&a)[16], DiagTmp& z, double sgl,
+                                                      double thrl, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a12] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[sg], %[sgl] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[thr], %[thrl] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a12], %[nn]\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[x], %[y], %[sg]\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_cmp_lt_f64_e32 vcc, %[thr], %[x]\n"
+      "v_mov_b64_e32 %[x], %[sg]\n"
+      "s_and_saveexec_b64 %[sv], vcc\n"
+      "v_mov_b64_e32 %[x], %[y]\n"
+      "s_mov_b64 exec, %[sv]\n"
+      "s_andn2_b64 %[sv], %[sv], vcc\n"
+      "s_or_b64 %[bad], %[bad], %[sv]\n"
+      "v_rcp_f64_e32 %[r], %[x]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[tm], %[a12], %[r]\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[be] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[be] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [tm] "=&v"(z.tm), [be] "=&v"(z.be),
+        [sg] "=&v"(z.sg), [thr] "=&v"(z.thr), [sv] "=&s"(z.sv), [bad] "+s"(z.bad)
+      : [bp] "v"(z.bp), [sgl] "v"(sgl), [thrl] "v"(thrl), [nn] "v"(nn)
+      : "vcc");
+}
+template <> __device__ __forceinline__ void diag_blk<13>(double (&a)[16], DiagTmp& z, double sgl,
+                                                      double thrl, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a13] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[sg], %[sgl] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[thr], %[thrl] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a13], %[nn]\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[x], %[y], %[sg]\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_cmp_lt_f64_e32 vcc, %[thr], %[x]\n"
+      "v_mov_b64_e32 %[x], %[sg]\n"
+      "s_and_saveexec_b64 %[sv], vcc\n"
+      "v_mov_b64_e32 %[x], %[y]\n"
+      "s_mov_b64 exec, %[sv]\n"
+      "s_andn2_b64 %[sv], %[sv], vcc\n"
+      "s_or_b64 %[bad], %[bad], %[sv]\n"
+      "v_rcp_f64_e32 %[r], %[x]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[tm], %[a13], %[r]\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[be] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[be] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [tm] "=&v"(z.tm), [be] "=&v"(z.be),
+        [sg] "=&v"(z.sg), [thr] "=&v"(z.thr), [sv] "=&s"(z.sv), [bad] "+s"(z.bad)
+      : [bp] "v"(z.bp), [sgl] "v"(sgl), [thrl] "v"(thrl), [nn] "v"(nn)
+      : "vcc");
+}
+template <> __device__ __forceinline__ void diag_blk<14>(double (&a)[16], DiagTmp& z, double sgl,
+                                                      double thrl, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a14] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[sg], %[sgl] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[thr], %[thrl] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a14], %[nn]\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[x], %[y], %[sg]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_cmp_lt_f64_e32 vcc, %[thr], %[x]\n"
+      "v_mov_b64_e32 %[x], %[sg]\n"
+      "s_and_saveexec_b64 %[sv], vcc\n"
+      "v_mov_b64_e32 %[x], %[y]\n"
+      "s_mov_b64 exec, %[sv]\n"
+      "s_andn2_b64 %[sv], %[sv], vcc\n"
+      "s_or_b64 %[bad], %[bad], %[sv]\n"
+      "v_rcp_f64_e32 %[r], %[x]\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[tm], %[a14], %[r]\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[be] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [tm] "=&v"(z.tm), [be] "=&v"(z.be),
+        [sg] "=&v"(z.sg), [thr] "=&v"(z.thr), [sv] "=&s"(z.sv), [bad] "+s"(z.bad)
+      : [bp] "v"(z.bp), [sgl] "v"(sgl), [thrl] "v"(thrl), [nn] "v"(nn)
+      : "vcc");
+}
+template <> __device__ __forceinline__ void diag_blk<15>(double (&a)[16], DiagTmp& z, double sgl,
+                                                      double thrl, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a15] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[sg], %[sgl] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b64_dpp %[thr], %[thrl] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a15], %[nn]\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[x], %[y], %[sg]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_cmp_lt_f64_e32 vcc, %[thr], %[x]\n"
+      "v_mov_b64_e32 %[x], %[sg]\n"
+      "s_and_saveexec_b64 %[sv], vcc\n"
+      "v_mov_b64_e32 %[x], %[y]\n"
+      "s_mov_b64 exec, %[sv]\n"
+      "s_andn2_b64 %[sv], %[sv], vcc\n"
+      "s_or_b64 %[bad], %[bad], %[sv]\n"
+      "v_rcp_f64_e32 %[r], %[x]\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[y], -%[x], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[y], %[r]\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[tm], %[a15], %[r]\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [tm] "=&v"(z.tm), [be] "=&v"(z.be),
+        [sg] "=&v"(z.sg), [thr] "=&v"(z.thr), [sv] "=&s"(z.sv), [bad] "+s"(z.bad)
+      : [bp] "v"(z.bp), [sgl] "v"(sgl), [thrl] "v"(thrl), [nn] "v"(nn)
+      : "vcc");
+}
+template <> __device__ __forceinline__ void diag_blk<16>(double (&a)[16], DiagTmp& z, double, double,
+                                                       double) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15])
+      : [bp] "v"(z.bp));
+}
+
+
+// The same sweep without the pivot test on the chain (the common case):
+// d goes straight to the reciprocal, and the test runs once at the end on
+// each pivot's recorded reciprocal (diag_sweep).  A failed pivot leaves
+// non-finite or meaningless values here, and the block is swept again by
+// diag_blk, which substitutes s for d.
+template <int M>
+__device__ __forceinline__ void diag_fast(double (&a)[16], DiagTmp& z, double nn);
+template <> __device__ __forceinline__ void diag_fast<0>(double (&a)[16], DiagTmp& z, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a0] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a0], %[nn]\n"
+      "v_rcp_f64_e32 %[r], %[y]\n"
+      "s_nop 0\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[be] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[be] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [be] "=&v"(z.be)
+      : [bp] "v"(z.bp), [nn] "v"(nn));
+}
+template <> __device__ __forceinline__ void diag_fast<1>(double (&a)[16], DiagTmp& z, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a1] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a1], %[nn]\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_rcp_f64_e32 %[r], %[y]\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[be] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[be] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [be] "=&v"(z.be)
+      : [bp] "v"(z.bp), [nn] "v"(nn));
+}
+template <> __device__ __forceinline__ void diag_fast<2>(double (&a)[16], DiagTmp& z, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a2] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a2], %[nn]\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_rcp_f64_e32 %[r], %[y]\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[be] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[be] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [be] "=&v"(z.be)
+      : [bp] "v"(z.bp), [nn] "v"(nn));
+}
+template <> __device__ __forceinline__ void diag_fast<3>(double (&a)[16], DiagTmp& z, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a3] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a3], %[nn]\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_rcp_f64_e32 %[r], %[y]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[be] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[be] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [be] "=&v"(z.be)
+      : [bp] "v"(z.bp), [nn] "v"(nn));
+}
+template <> __device__ __forceinline__ void diag_fast<4>(double (&a)[16], DiagTmp& z, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a4] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a4], %[nn]\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_rcp_f64_e32 %[r], %[y]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[be] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[be] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [be] "=&v"(z.be)
+      : [bp] "v"(z.bp), [nn] "v"(nn));
+}
+template <> __device__ __forceinline__ void diag_fast<5>(double (&a)[16], DiagTmp& z, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a5] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a5], %[nn]\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_rcp_f64_e32 %[r], %[y]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[be] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[be] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [be] "=&v"(z.be)
+      : [bp] "v"(z.bp), [nn] "v"(nn));
+}
+template <> __device__ __forceinline__ void diag_fast<6>(double (&a)[16], DiagTmp& z, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a6] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a6], %[nn]\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_rcp_f64_e32 %[r], %[y]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[be] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[be] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [be] "=&v"(z.be)
+      : [bp] "v"(z.bp), [nn] "v"(nn));
+}
+template <> __device__ __forceinline__ void diag_fast<7>(double (&a)[16], DiagTmp& z, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a7] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a7], %[nn]\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_rcp_f64_e32 %[r], %[y]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[be] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[be] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [be] "=&v"(z.be)
+      : [bp] "v"(z.bp), [nn] "v"(nn));
+}
+template <> __device__ __forceinline__ void diag_fast<8>(double (&a)[16], DiagTmp& z, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a8] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a8], %[nn]\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_rcp_f64_e32 %[r], %[y]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[be] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[be] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [be] "=&v"(z.be)
+      : [bp] "v"(z.bp), [nn] "v"(nn));
+}
+template <> __device__ __forceinline__ void diag_fast<9>(double (&a)[16], DiagTmp& z, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a9] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a9], %[nn]\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_rcp_f64_e32 %[r], %[y]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[be] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[be] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [be] "=&v"(z.be)
+      : [bp] "v"(z.bp), [nn] "v"(nn));
+}
+template <> __device__ __forceinline__ void diag_fast<10>(double (&a)[16], DiagTmp& z, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a10] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a10], %[nn]\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_rcp_f64_e32 %[r], %[y]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[be] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[be] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [be] "=&v"(z.be)
+      : [bp] "v"(z.bp), [nn] "v"(nn));
+}
+template <> __device__ __forceinline__ void diag_fast<11>(double (&a)[16], DiagTmp& z, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a11] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a11], %[nn]\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_rcp_f64_e32 %[r], %[y]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[be] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[be] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [be] "=&v"(z.be)
+      : [bp] "v"(z.bp), [nn] "v"(nn));
+}
+template <> __device__ __forceinline__ void diag_fast<12>(double (&a)[16], DiagTmp& z, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a12] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a12], %[nn]\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_rcp_f64_e32 %[r], %[y]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[be] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[be] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [be] "=&v"(z.be)
+      : [bp] "v"(z.bp), [nn] "v"(nn));
+}
+template <> __device__ __forceinline__ void diag_fast<13>(double (&a)[16], DiagTmp& z, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a13] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a13], %[nn]\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_rcp_f64_e32 %[r], %[y]\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[be] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[be] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [be] "=&v"(z.be)
+      : [bp] "v"(z.bp), [nn] "v"(nn));
+}
+template <> __device__ __forceinline__ void diag_fast<14>(double (&a)[16], DiagTmp& z, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a14] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a14], %[nn]\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_rcp_f64_e32 %[r], %[y]\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a15], %[a15], %[be] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [be] "=&v"(z.be)
+      : [bp] "v"(z.bp), [nn] "v"(nn));
+}
+template <> __device__ __forceinline__ void diag_fast<15>(double (&a)[16], DiagTmp& z, double nn) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mov_b64_dpp %[y], %[a15] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[a15], %[nn]\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_rcp_f64_e32 %[r], %[y]\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[x], -%[y], %[r], 1.0\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fma_f64 %[r], %[r], %[x], %[r]\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f64 %[be], %[be], %[r]\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15]),
+        [x] "=&v"(z.x), [y] "=&v"(z.y), [r] "=&v"(z.r), [be] "=&v"(z.be)
+      : [bp] "v"(z.bp), [nn] "v"(nn));
+}
+template <> __device__ __forceinline__ void diag_fast<16>(double (&a)[16], DiagTmp& z, double) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_fmac_f64_dpp %[a0], %[a0], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a1], %[a1], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a2], %[a2], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a3], %[a3], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a4], %[a4], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a5], %[a5], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a6], %[a6], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a7], %[a7], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a8], %[a8], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a9], %[a9], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a10], %[a10], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a11], %[a11], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a12], %[a12], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a13], %[a13], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %[a14], %[a14], %[bp] row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+      : [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7]), [a8] "+v"(a[8]), [a9] "+v"(a[9]), [a10] "+v"(a[10]), [a11] "+v"(a[11]), [a12] "+v"(a[12]), [a13] "+v"(a[13]), [a14] "+v"(a[14]), [a15] "+v"(a[15])
+      : [bp] "v"(z.bp));
+}
+
+// Threshold of a pivot's test d s > thr: a variable swept in (s = +1) needs
+// d > kPivotRel * dg, dg its diagonal before any sweep (d / dg is the squared
+// sine of the angle between its column and the span of the variables already
+// swept: a smaller ratio means the column is numerically in that span; with
+// no dg only d > 0 is asked); a variable swept out (s = -1) needs d < 0; an
+// identity row past the block passes (d = 1, s = 1, thr = 0).
+constexpr double kPivotRel = 1e-12;
+
+template <int M>
+__device__ __forceinline__ void diag_pivot(double (&a)[16], double (&lcol)[16], DiagTmp& z,
+                                           double sgl, double thrl, int c, double& sc) {
   const bool piv = c == M;
-  const double tm = rowm * rd;
-  const double be = piv ? 0.0 : -tm;
-  if constexpr (M < 15) sweep_next<M>(a, be);
-  sweep_rest<M>(a, be);
-  a[M] = piv ? -1.0 : tm;
-  if (piv) sc = rd;
+  const double rowm = a[M];
+  diag_blk<M>(a, z, sgl, thrl, piv ? 0.0 : -1.0);
+  lcol[M] = c < M ? -(rowm * sc) : (piv ? 1.0 : 0.0);
+  a[M] = piv ? -1.0 : z.tm;
+  if (piv) sc = z.r;
+  z.bp = z.be;
 }
 template <int... Ms>
 __device__ __forceinline__ void diag_pivots(std::integer_sequence<int, Ms...>, double (&a)[16],
-                                            double (&lcol)[16], const double (&sgv)[16], int c,
-                                            double& sc, bool& bad) {
-  (diag_pivot<Ms>(a, lcol, sgv, c, sc, bad), ...);
+                                            double (&lcol)[16], DiagTmp& z, double sgl,
+                                            double thrl, int c, double& sc) {
+  (diag_pivot<Ms>(a, lcol, z, sgl, thrl, c, sc), ...);
+}
+template <int M>
+__device__ __forceinline__ void diag_pivot_fast(double (&a)[16], double (&lcol)[16], DiagTmp& z,
+                                                int c, double& sc) {
+  const bool piv = c == M;
+  const double rowm = a[M];
+  diag_fast<M>(a, z, piv ? 0.0 : -1.0);
+  lcol[M] = c < M ? -(rowm * sc) : (piv ? 1.0 : 0.0);
+  a[M] = piv ? -1.0 : -z.be;  // off the pivot lane be = -A[M][c] r
+  if (piv) sc = z.r;
+  z.bp = z.be;
+}
+template <int... Ms>
+__device__ __forceinline__ void diag_pivots_fast(std::integer_sequence<int, Ms...>,
+                                                 double (&a)[16], double (&lcol)[16], DiagTmp& z,
+                                                 int c, double& sc) {
+  (diag_pivot_fast<Ms>(a, lcol, z, c, sc), ...);
 }
 // Diagonal block at o: its L^-1 into the diagonal block of sm.li (upper part
-// zero), 1/D into sm.rD[o..o+15].  Run by one wave.
+// zero), 1/D into sm.rD[o..o+15].  Run by one wave.  The fast sweep first;
+// its pivots are then tested on their reciprocals r (d s > thr is r s > 0
+// and r s thr < 1; a NaN or infinite r fails), and only if one fails is the
+// block swept again with the test and substitution on the chain.
 __device__ __forceinline__ bool diag_sweep(int o, int k) {
   SweepSmem& sm = g_sw;
   const int c = threadIdx.x & 15;
-  double a[16], lcol[16], sgv[16];
+  double a[16], lcol[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    a[r] = sm.pp[o + r][o + c];
-    sgv[r] = pivot_test(o + r < k, sm.sgn[o + r], sm.dg[o + r]);
-  }
+  for (int r = 0; r < 16; ++r) a[r] = sm.pp[o + r][o + c];
+  const bool in = o + c < k;
+  const double sgl = in ? sm.sgn[o + c] : 1.0;
+  const double thrl = in && sgl > 0.0 ? kPivotRel * sm.dg[o + c] : 0.0;
   double sc = 1.0;  // after the sweep: 1/D of pivot c
-  bool bad = false;
-  diag_pivots(std::make_integer_sequence<int, 16>{}, a, lcol, sgv, c, sc, bad);
+  DiagTmp z{};
+  diag_pivots_fast(std::make_integer_sequence<int, 16>{}, a, lcol, z, c, sc);
+  diag_fast<16>(a, z, 0.0);
+  const double rs = sc * sgl;
+  const bool ok = rs > 0.0 && rs * thrl < 1.0;
+  if (__builtin_amdgcn_ballot_w64(!ok) != 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) a[r] = sm.pp[o + r][o + c];
+    sc = 1.0;
+    z = DiagTmp{};
+    diag_pivots(std::make_integer_sequence<int, 16>{}, a, lcol, z, sgl, thrl, c, sc);
+    diag_blk<16>(a, z, 0.0, 0.0, 0.0);
+  }
   if ((threadIdx.x & 63) < 16) {
     sm.rD[o + c] = sc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sm.li[o + r][o + c] = lcol[r];
   }
-  return bad;
+  return z.bad != 0;
 }
 
 // Blocked LDL^T helpers, one wave each, fp64 MFMA 16x16x4 (lane l supplies

@@ -2611,19 +2611,9 @@ struct TileWalk {
 // members that build bands and tiles form B from them.
 // Returns whether a pivot of this step had the wrong sign (a lookahead
 // member flags its own into *status).
-__device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& team_ref, int k_arg,
-                                        int skip_arg, int kn_arg, bool pre_arg) {
+__device__ __forceinline__ bool sweep_step(const SweepMat& M, Team& tm, int k, int skip_below,
+                                           int kn, bool pre) {
   SweepSmem& sm = g_sw;
-  // every argument is the same in all lanes; a called function receives them
-  // in vector registers, so say so, or every branch and address derived from
-  // them is compiled as divergent (exec-masked)
-  const SweepMat M = uniform_mat(M_arg);
-  const int k = uniform(k_arg), skip_below = uniform(skip_arg), kn = uniform(kn_arg);
-  const bool pre = uniform(static_cast<int>(pre_arg)) != 0;
-  // the team in registers for the step: the caller's copy lives in scratch,
-  // and every scratch access is a vector memory operation whose wait also
-  // waits for all older loads and stores (the ticket atomic, a tile's stores)
-  Team tm = uniform_team(team_ref);
   const int trank = tm.rank, tsize = tm.size;
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const bool la = kn > 0 && tsize > 1;
@@ -2861,6 +2851,56 @@ __device__ __noinline__ bool sweep_step(const SweepMat M_arg, Team& team_ref, in
   if (me_la && !tm.fast) team_arrive(tm);
   team_wait(tm);
   if (la) tm.pubs += 1;
+  return bad;
+}
+
+// One step as a call (the NNLS rounds): the team and the matrix are copied
+// into registers for the step (the caller's copy lives in scratch, and every
+// scratch access is a vector memory operation whose wait also waits for all
+// older loads and stores).
+__device__ __noinline__ bool sweep_step_call(const SweepMat M_arg, Team& team_ref, int k_arg,
+                                             int skip_arg, int kn_arg, bool pre_arg) {
+  // every argument is the same in all lanes; a called function receives them
+  // in vector registers, so say so, or every branch and address derived from
+  // them is compiled as divergent (exec-masked)
+  const SweepMat M = uniform_mat(M_arg);
+  Team tm = uniform_team(team_ref);
+  const bool bad = sweep_step(M, tm, uniform(k_arg), uniform(skip_arg), uniform(kn_arg),
+                              uniform(static_cast<int>(pre_arg)) != 0);
+  team_ref.gen = tm.gen;
+  team_ref.tbase = tm.tbase;
+  team_ref.pubs = tm.pubs;
+  return bad;
+}
+
+// The value system's n variables (rows r_al .. r_al + n - 1), swept in 64 at
+// a time, no tile above the swept bands updated, as one call: the per-step
+// call costs more here than the register pressure of the loop around the
+// inlined step.
+__device__ __noinline__ bool sweep_run(const SweepMat M_arg, Team& team_ref, int n_arg) {
+  SweepSmem& sm = g_sw;
+  const SweepMat M = uniform_mat(M_arg);
+  const int n = uniform(n_arg);
+  Team tm = uniform_team(team_ref);
+  const int tid = threadIdx.x;
+  bool bad = false;
+  for (int s0 = 0; s0 < n; s0 += kSB) {
+    const int k = min(kSB, n - s0);
+    const int kn = min(kSB, n - s0 - k);
+    if (tid < k) {
+      sm.piv[tid] = M.r_al + s0 + tid;
+      sm.sgn[tid] = 1.0;
+      sm.pos[M.r_al + s0 + tid] = static_cast<int16_t>(tid);
+    }
+    if (tid < kn) {
+      sm.piv2[tid] = M.r_al + s0 + k + tid;
+      sm.sgn2[tid] = 1.0;
+    }
+    __syncthreads();
+    bad |= sweep_step(M, tm, k, s0 / kSB, kn, s0 > 0 && tm.size > 1);
+    if (tid < k) sm.pos[M.r_al + s0 + tid] = -1;
+    __syncthreads();
+  }
   team_ref.gen = tm.gen;
   team_ref.tbase = tm.tbase;
   team_ref.pubs = tm.pubs;
@@ -3041,7 +3081,7 @@ __global__ __launch_bounds__(256) void k_nnls_sweep(
             sm.sgn2[tid] = sm.inF[j] ? -1.0 : 1.0;
           }
           __syncthreads();
-          bad |= sweep_step(M, tm, k, 0, kn, s0 > 0 && tm.size > 1);
+          bad |= sweep_step_call(M, tm, k, 0, kn, s0 > 0 && tm.size > 1);
           if (tid < k) {
             const int j = sm.list[s0 + tid];
             sm.inF[j] ^= 1;
@@ -3126,24 +3166,7 @@ __global__ __launch_bounds__(256) void k_value_sweep(
     const int m = msz[b];
     const SweepMat M{gptr(S + b * sS), gptr(Ub + b * sUV), gptr(Vb + b * sUV),
                      gptr(stage + static_cast<size_t>(b) * kStage), ld, r_al, D, m, nullptr};
-    bool bad = false;
-    for (int s0 = 0; s0 < m; s0 += kSB) {
-      const int k = min(kSB, m - s0);
-      const int kn = min(kSB, m - s0 - k);
-      if (tid < k) {
-        sm.piv[tid] = r_al + s0 + tid;
-        sm.sgn[tid] = 1.0;
-        sm.pos[r_al + s0 + tid] = static_cast<int16_t>(tid);
-      }
-      if (tid < kn) {
-        sm.piv2[tid] = r_al + s0 + k + tid;
-        sm.sgn2[tid] = 1.0;
-      }
-      __syncthreads();
-      bad |= sweep_step(M, tm, k, s0 / kSB, kn, s0 > 0 && tm.size > 1);
-      if (tid < k) sm.pos[r_al + s0 + tid] = -1;
-      __syncthreads();
-    }
+    const bool bad = sweep_run(M, tm, m);
     if (tm.rank == 0 && tid == 0) {
       double fl = 0.0;
       for (int s0 = 0; s0 < m; s0 += kSB) fl += sweep_flops(min(kSB, m - s0), m + D);

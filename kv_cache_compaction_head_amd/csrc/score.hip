@@ -106,12 +106,26 @@ __device__ __forceinline__ void lds_copy16(const void* src, void* dst) {
 }
 
 // XOR swizzle of the 16-byte chunks of a key row in an unpadded LDS tile
-// with CPR chunks per row: the 16 rows an MFMA operand read takes at once
-// land in 16 distinct 16-byte bank groups of a 256-byte bank row.
+// with CPR chunks per row.  Two reads have to be conflict-free:
+//  - an MFMA operand read (16 bytes a lane): lane l takes row l mod 32, one
+//    chunk, so 16 consecutive rows must land in 16 distinct 16-byte bank
+//    groups;
+//  - the value tile's transpose read (8 bytes a lane): 32 lanes take 4
+//    consecutive rows (4-aligned) x 4 consecutive chunks (4-aligned), which
+//    must also land in 16 distinct groups.
+// At 16 chunks a row (d = 128) the swizzle is linear over GF(2) in the row's
+// low four bits, bit b contributing 4, 10, 1, 2 for b = 0..3: rows 0..15 map
+// to a permutation of 0..15, and the four rows of a 4-aligned quad map to
+// four different 4-aligned chunk groups, which serves both reads.  (The plain
+// r mod 16 served the first and put the second four rows to a group.)
 template <int CPR>
 __host__ __device__ constexpr int k_swz(int r) {
   static_assert(CPR == 8 || CPR == 16, "16-byte chunks per row");
-  return (r / (16 / CPR)) & (CPR - 1);
+  if constexpr (CPR == 16) {
+    return ((r & 1) ? 4 : 0) ^ ((r & 2) ? 10 : 0) ^ ((r & 4) ? 1 : 0) ^ ((r & 8) ? 2 : 0);
+  } else {
+    return (r / 2) & 7;
+  }
 }
 
 // Bit r set when accumulator row r of this lane holds a live key: tile key

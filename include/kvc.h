@@ -104,8 +104,15 @@ typedef struct {
   int32_t max_nnls_iters; /* cap on NNLS pivoting rounds, default 32              */
   int32_t out_v_dtype;    /* kvc_dtype_t of out_V, default KVC_F32; KVC_BF16
                              stores the float32 result rounded to nearest-even   */
-  int32_t refine_steps;   /* refinement steps of the value fit, default 0; must
-                             be 0 in this version                                 */
+  int32_t refine_steps;   /* refinement steps of the value fit, 0..4, default 0.
+                             Each step is one corrected semi-normal-equation
+                             step: E = O - X_F C, C += (G + lam_v I)^-1
+                             (X_F^T E - lam_v (C - V_S)), with the inverse the
+                             value sweep leaves when refinement is on.  It
+                             takes the residual against O itself, so it
+                             recovers accuracy the normal equations lose when
+                             X_F is ill-conditioned.  Needs workspace for E
+                             (B n d doubles) and two B t d double buffers      */
   int32_t reserved;       /* must be 0                                            */
 } kvc_params_t;
 
@@ -286,6 +293,11 @@ typedef struct {
   size_t omp_order; /* [B, t] int32: after kvc_compact_omp, the keys in the
                        order the pursuit chose them (workspace of
                        kvc_workspace_bytes_omp) */
+  size_t value_C;   /* f64: the value fit's solution before its float32 (or
+                       bf16) output, head b's passive variable a (the a-th
+                       kept slot with w > 0) at row a of a [value_ld]-strided
+                       matrix starting value_C + 8 b value_ld^2, columns 0..d-1 */
+  size_t value_ld;  /* that row stride, in doubles */
 } kvc_ws_layout_t;
 int kvc_workspace_layout(const kvc_params_t* p, kvc_ws_layout_t* out);
 

@@ -85,7 +85,8 @@ def _workspace(p, device, workspace, need=None):
 
 
 def compact(Q, K, V, t: int, *, agg: str = "rms", ridge_rel: float = 1e-6,
-            max_nnls_iters: int = 32, out_v_dtype=None, workspace=None, stream=None) -> Compacted:
+            max_nnls_iters: int = 32, refine_steps: int = 0, out_v_dtype=None, workspace=None,
+            stream=None) -> Compacted:
     """Compact each head's cache to t kept keys with fitted bias and values."""
     import torch
     Q, K, V, _ = _prep(Q, K, V)
@@ -93,7 +94,7 @@ def compact(Q, K, V, t: int, *, agg: str = "rms", ridge_rel: float = 1e-6,
     T = K.shape[1]
     dt = "bf16" if Q.dtype == torch.bfloat16 else "f32"
     vs, vt = _vdt(out_v_dtype)
-    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters, vs)
+    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters, vs, refine_steps)
     dev = Q.device
     ws = _workspace(p, dev, workspace)
     keys = torch.empty((B, t, d), dtype=Q.dtype, device=dev)
@@ -109,7 +110,8 @@ def compact(Q, K, V, t: int, *, agg: str = "rms", ridge_rel: float = 1e-6,
 
 
 def compact_noalloc(Q, K, V, t: int, *, agg: str = "rms", ridge_rel: float = 1e-6,
-                    max_nnls_iters: int = 32, out_v_dtype=None, stream=None) -> Compacted:
+                    max_nnls_iters: int = 32, refine_steps: int = 0, out_v_dtype=None,
+                    stream=None) -> Compacted:
     """compact() through kvc_compact_noalloc: the library takes its workspace
     from its own per-device scratch array (at most _lib.NOALLOC_SCRATCH_BYTES)
     instead of a caller buffer.  Only the outputs are allocated here."""
@@ -119,7 +121,7 @@ def compact_noalloc(Q, K, V, t: int, *, agg: str = "rms", ridge_rel: float = 1e-
     T = K.shape[1]
     dt = "bf16" if Q.dtype == torch.bfloat16 else "f32"
     vs, vt = _vdt(out_v_dtype)
-    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters, vs)
+    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters, vs, refine_steps)
     dev = Q.device
     keys = torch.empty((B, t, d), dtype=Q.dtype, device=dev)
     bias = torch.empty((B, t), dtype=torch.float32, device=dev)
@@ -134,7 +136,7 @@ def compact_noalloc(Q, K, V, t: int, *, agg: str = "rms", ridge_rel: float = 1e-
 
 
 def compact_omp(Q, K, V, t: int, *, ridge_rel: float = 1e-6, max_nnls_iters: int = 32,
-                out_v_dtype=None, workspace=None, stream=None) -> Compacted:
+                refine_steps: int = 0, out_v_dtype=None, workspace=None, stream=None) -> Compacted:
     """Compact each head to t keys chosen by orthogonal matching pursuit on
     the attention mass (t greedy steps), then the same bias and value fits as
     compact()."""
@@ -144,7 +146,7 @@ def compact_omp(Q, K, V, t: int, *, ridge_rel: float = 1e-6, max_nnls_iters: int
     T = K.shape[1]
     dt = "bf16" if Q.dtype == torch.bfloat16 else "f32"
     vs, vt = _vdt(out_v_dtype)
-    p = make_params(B, T, n, d, t, dt, "rms", ridge_rel, max_nnls_iters, vs)
+    p = make_params(B, T, n, d, t, dt, "rms", ridge_rel, max_nnls_iters, vs, refine_steps)
     dev = Q.device
     need = workspace_bytes_omp(p)
     if need == 0:
@@ -164,7 +166,9 @@ def compact_omp(Q, K, V, t: int, *, ridge_rel: float = 1e-6, max_nnls_iters: int
 
 
 def compact_ragged(Q, K, V, t_heads, *, agg: str = "rms", ridge_rel: float = 1e-6,
-                   max_nnls_iters: int = 32, out_v_dtype=None, workspace=None, stream=None) -> Compacted:
+                   max_nnls_iters: int = 32, refine_steps: int = 0,
+                   out_v_dtype=None, workspace=None,
+            stream=None) -> Compacted:
     """Compact head b to t_heads[b] keys (a per-head budget).  Outputs are
     padded to max(t_heads): head b's slots from t_heads[b] on hold idx -1,
     zero keys and values and bias -inf, which attention ignores."""
@@ -179,7 +183,7 @@ def compact_ragged(Q, K, V, t_heads, *, agg: str = "rms", ridge_rel: float = 1e-
     tv = tv.to(Q.device).contiguous()
     dt = "bf16" if Q.dtype == torch.bfloat16 else "f32"
     vs, vt = _vdt(out_v_dtype)
-    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters, vs)
+    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters, vs, refine_steps)
     dev = Q.device
     ws = _workspace(p, dev, workspace)
     keys = torch.empty((B, t, d), dtype=Q.dtype, device=dev)
@@ -196,7 +200,9 @@ def compact_ragged(Q, K, V, t_heads, *, agg: str = "rms", ridge_rel: float = 1e-
 
 
 def compact_protected(Q, K, V, t: int, protect, *, agg: str = "rms", ridge_rel: float = 1e-6,
-                      max_nnls_iters: int = 32, out_v_dtype=None, workspace=None, stream=None) -> Compacted:
+                      max_nnls_iters: int = 32, refine_steps: int = 0,
+                      out_v_dtype=None, workspace=None,
+            stream=None) -> Compacted:
     """Keep the marked keys of protect [B, T] (bool/uint8) exactly with bias 0
     (at most t - 1 per head, the first by position) and compact the others
     into the remaining slots.  Head b's slots [0, t - p_b) hold the fitted
@@ -210,7 +216,7 @@ def compact_protected(Q, K, V, t: int, protect, *, agg: str = "rms", ridge_rel: 
     m = protect.to(device=Q.device, dtype=torch.uint8).contiguous()
     dt = "bf16" if Q.dtype == torch.bfloat16 else "f32"
     vs, vt = _vdt(out_v_dtype)
-    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters, vs)
+    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters, vs, refine_steps)
     dev = Q.device
     ws = _workspace(p, dev, workspace)
     keys = torch.empty((B, t, d), dtype=Q.dtype, device=dev)
@@ -227,8 +233,8 @@ def compact_protected(Q, K, V, t: int, protect, *, agg: str = "rms", ridge_rel: 
 
 
 def compact_chunked(Q, K, V, t: int, n_chunks: int, *, agg: str = "rms",
-                    ridge_rel: float = 1e-6, max_nnls_iters: int = 32, out_v_dtype=None, workspace=None,
-                    stream=None) -> Compacted:
+                    ridge_rel: float = 1e-6, max_nnls_iters: int = 32, refine_steps: int = 0,
+                    out_v_dtype=None, workspace=None, stream=None) -> Compacted:
     """Cut each head's cache into n_chunks contiguous chunks, compact every chunk
     to t entries on its own, concatenate.  keys/bias/values/idx are
     [B, n_chunks * t, ...] (idx in whole-cache positions); status is
@@ -239,7 +245,7 @@ def compact_chunked(Q, K, V, t: int, n_chunks: int, *, agg: str = "rms",
     T = K.shape[1]
     dt = "bf16" if Q.dtype == torch.bfloat16 else "f32"
     vs, vt = _vdt(out_v_dtype)
-    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters, vs)
+    p = make_params(B, T, n, d, t, dt, agg, ridge_rel, max_nnls_iters, vs, refine_steps)
     dev = Q.device
     need = workspace_bytes_chunked(p, n_chunks)
     if need == 0:
@@ -259,12 +265,12 @@ def compact_chunked(Q, K, V, t: int, n_chunks: int, *, agg: str = "rms",
     _lib.check(rc)
     # intermediates() of this result index (head, chunk) entries b * n_chunks + c
     pc = make_params(B * n_chunks, T // n_chunks, n, d, t, dt, agg, ridge_rel, max_nnls_iters,
-                     vs)
+                     vs, refine_steps)
     return Compacted(keys, bias, values, idx, status, ws, pc)
 
 
 def fit(Q, K, V, idx, *, ridge_rel: float = 1e-6, max_nnls_iters: int = 32,
-        out_v_dtype=None, workspace=None, stream=None) -> Compacted:
+        refine_steps: int = 0, out_v_dtype=None, workspace=None, stream=None) -> Compacted:
     """Bias and value fit for a given kept set idx [B, t] (int32, ascending)."""
     import torch
     Q, K, V, _ = _prep(Q, K, V)
@@ -275,7 +281,7 @@ def fit(Q, K, V, idx, *, ridge_rel: float = 1e-6, max_nnls_iters: int = 32,
     T, t = K.shape[1], idx.shape[1]
     dt = "bf16" if Q.dtype == torch.bfloat16 else "f32"
     vs, vt = _vdt(out_v_dtype)
-    p = make_params(B, T, n, d, t, dt, "rms", ridge_rel, max_nnls_iters, vs)
+    p = make_params(B, T, n, d, t, dt, "rms", ridge_rel, max_nnls_iters, vs, refine_steps)
     dev = Q.device
     ws = _workspace(p, dev, workspace)
     bias = torch.empty((B, t), dtype=torch.float32, device=dev)
@@ -336,7 +342,9 @@ def attend(Q, K1, V1, bias1=None, K2=None, V2=None, *, workspace=None, stream=No
 def intermediates(res: Compacted) -> dict:
     """Views into the workspace: lse [B,n] (float64), O [B,n,d], imp [B,T] (sum of p^2 or
     p per key), w [B,t] (float64 NNLS multipliers), fit_flops [B,2] (fp64
-    operations of the NNLS rounds and the value solve).  Synchronise first."""
+    operations of the NNLS rounds and the value solve), value_C [B,t,d] (the
+    value fit's float64 solution; row a is the a-th kept slot with w > 0, rows
+    past the passive count unused).  Synchronise first."""
     import torch
     p = res.params
     L = workspace_layout(p)
@@ -352,4 +360,9 @@ def intermediates(res: Compacted) -> dict:
             "imp": view(L.imp, B * T, torch.float32, (B, T)),
             "w": view(L.w, B * t, torch.float64, (B, t)),
             "fit_flops": view(L.fit_flops, B * 2, torch.float64, (B, 2)),
+            # the value fit's float64 solution, row a = the a-th kept slot with w > 0
+            "value_C": torch.as_strided(
+                view(L.value_C, (B - 1) * L.value_ld ** 2 + t * L.value_ld, torch.float64,
+                     ((B - 1) * L.value_ld ** 2 + t * L.value_ld,)),
+                (B, t, d), (L.value_ld ** 2, L.value_ld, 1)),
             **({"omp_order": view(L.omp_order, B * t, torch.int32, (B, t))} if res.omp else {})}

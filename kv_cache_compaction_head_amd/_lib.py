@@ -51,7 +51,8 @@ class AttendParams(ctypes.Structure):
 class WsLayout(ctypes.Structure):
     _fields_ = [("lse", ctypes.c_size_t), ("O", ctypes.c_size_t), ("imp", ctypes.c_size_t),
                 ("w", ctypes.c_size_t), ("fit_flops", ctypes.c_size_t),
-                ("omp_order", ctypes.c_size_t)]
+                ("omp_order", ctypes.c_size_t), ("value_C", ctypes.c_size_t),
+                ("value_ld", ctypes.c_size_t)]
 
 
 _lib = None
@@ -115,7 +116,7 @@ def load() -> ctypes.CDLL:
 
 
 def make_params(B, T, n, d, t, dtype, agg="rms", ridge_rel=1e-6, max_nnls_iters=32,
-                out_v_dtype="f32") -> Params:
+                out_v_dtype="f32", refine_steps=0) -> Params:
     p = Params()
     load().kvc_params_default(ctypes.byref(p))
     p.B, p.T, p.n, p.d, p.t = int(B), int(T), int(n), int(d), int(t)
@@ -124,6 +125,7 @@ def make_params(B, T, n, d, t, dtype, agg="rms", ridge_rel=1e-6, max_nnls_iters=
     p.ridge_rel = float(ridge_rel)
     p.max_nnls_iters = int(max_nnls_iters)
     p.out_v_dtype = {"bf16": KVC_BF16, "f32": KVC_F32}[out_v_dtype]
+    p.refine_steps = int(refine_steps)
     return p
 
 

@@ -2874,13 +2874,16 @@ __device__ __noinline__ bool sweep_step_call(const SweepMat M_arg, Team& team_re
 }
 
 // The value system's n variables (rows r_al .. r_al + n - 1), swept in 64 at
-// a time, no tile above the swept bands updated, as one call: the per-step
-// call costs more here than the register pressure of the loop around the
-// inlined step.
-__device__ __noinline__ bool sweep_run(const SweepMat M_arg, Team& team_ref, int n_arg) {
+// a time, as one call: the per-step call costs more here than the register
+// pressure of the loop around the inlined step.  Unless `full`, no tile above
+// the swept bands is updated (the solution needs none of them); with it the
+// variable block ends as -(G + lam I)^-1, which the refinement steps apply.
+__device__ __noinline__ bool sweep_run(const SweepMat M_arg, Team& team_ref, int n_arg,
+                                       int full_arg) {
   SweepSmem& sm = g_sw;
   const SweepMat M = uniform_mat(M_arg);
   const int n = uniform(n_arg);
+  const bool full = uniform(full_arg) != 0;
   Team tm = uniform_team(team_ref);
   const int tid = threadIdx.x;
   bool bad = false;
@@ -2897,7 +2900,7 @@ __device__ __noinline__ bool sweep_run(const SweepMat M_arg, Team& team_ref, int
       sm.sgn2[tid] = 1.0;
     }
     __syncthreads();
-    bad |= sweep_step(M, tm, k, s0 / kSB, kn, s0 > 0 && tm.size > 1);
+    bad |= sweep_step(M, tm, k, full ? 0 : s0 / kSB, kn, s0 > 0 && tm.size > 1);
     if (tid < k) sm.pos[M.r_al + s0 + tid] = -1;
     __syncthreads();
   }
@@ -3155,7 +3158,8 @@ __global__ __launch_bounds__(256) void k_value_sweep(
     double* __restrict__ S, size_t sS, int ld, int r_al, double* __restrict__ Ub,
     double* __restrict__ Vb, size_t sUV, double* __restrict__ stage, const int32_t* __restrict__ msz,
     int32_t* __restrict__ status, unsigned* __restrict__ bar, int* __restrict__ err,
-    int* __restrict__ xcc, double* __restrict__ flops, int B, int D, int tx, uint64_t spin) {
+    int* __restrict__ xcc, double* __restrict__ flops, int B, int D, int tx, uint64_t spin,
+    int full) {
   SweepSmem& sm = g_sw;
   Team tm;
   int team, nteams;
@@ -3166,7 +3170,7 @@ __global__ __launch_bounds__(256) void k_value_sweep(
     const int m = msz[b];
     const SweepMat M{gptr(S + b * sS), gptr(Ub + b * sUV), gptr(Vb + b * sUV),
                      gptr(stage + static_cast<size_t>(b) * kStage), ld, r_al, D, m, nullptr};
-    const bool bad = sweep_run(M, tm, m);
+    const bool bad = sweep_run(M, tm, m, full);
     if (tm.rank == 0 && tid == 0) {
       double fl = 0.0;
       for (int s0 = 0; s0 < m; s0 += kSB) fl += sweep_flops(min(kSB, m - s0), m + D);
@@ -3274,6 +3278,130 @@ __global__ void k_write_out(const double* __restrict__ Cb, size_t sS, int ld,
     out_bias[static_cast<size_t>(b) * t + a] =
         j >= 0 ? static_cast<float>(log(fmax(wv[static_cast<size_t>(b) * t + a], 1e-30)))
                : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// Refinement of the value fit (corrected semi-normal equations).  With C the
+// solution of the swept normal equations, one step is
+//   E = O - X_F C,   Y = X_F^T E - lam_v (C - V_F),   C <- C + (G + lam_v I)^-1 Y,
+// the gradient of the regularised least squares at C mapped through the
+// inverse the full sweep left in the variable block: a residual taken
+// against O itself, so rounding in the normal equations (whose condition is
+// that of X_F squared) is corrected instead of repeated.  Y's first term is a
+// k_atb product; the other two products are small fp64 tiles, 64 x 64 outputs
+// per workgroup, 4 x 4 per thread, the contraction staged 16 at a time.
+// ---------------------------------------------------------------------------
+constexpr int kRK = 16;  // contraction values staged per chunk
+
+// E[b][i][c] = O[b][i][c] - sum_{a < m} X[i][a] C[a][c]; X in PS (row stride
+// t, passive columns first), C the value system's solution rows (stride ld).
+// grid (ceil(n/64), D/64, B), block 256.
+template <int D>
+__global__ __launch_bounds__(256) void k_csne_resid(const double* __restrict__ PS,
+                                                    const double* __restrict__ Cb, size_t sS,
+                                                    int ld, const float* __restrict__ O,
+                                                    const int32_t* __restrict__ msz,
+                                                    double* __restrict__ E, int n, int t) {
+  __shared__ double sA[kTile][kRK + 1], sB[kRK][kTile];
+  const int b = blockIdx.z, m = msz[b], i0 = blockIdx.x * kTile, c0 = blockIdx.y * kTile;
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const double* X = PS + static_cast<size_t>(b) * n * t;
+  const double* C = Cb + b * sS;
+  double acc[4][4] = {};
+  for (int a0 = 0; a0 < m; a0 += kRK) {
+    for (int e = tid; e < kTile * kRK; e += 256) {
+      const int r = e / kRK, k = e % kRK, i = i0 + r, a = a0 + k;
+      sA[r][k] = (i < n && a < m) ? X[static_cast<size_t>(i) * t + a] : 0.0;
+    }
+    for (int e = tid; e < kRK * kTile; e += 256) {
+      const int k = e / kTile, c = e % kTile, a = a0 + k;
+      sB[k][c] = a < m ? C[static_cast<size_t>(a) * ld + c0 + c] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kRK; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] = fma(sA[4 * ty + r][k], sB[k][4 * tx + c], acc[r][c]);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = i0 + 4 * ty + r;
+    if (i >= n) continue;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const size_t o = (static_cast<size_t>(b) * n + i) * D + c0 + 4 * tx + c;
+      E[o] = static_cast<double>(O[o]) - acc[r][c];
+    }
+  }
+}
+
+// Cn[b][a][c] = C[a][c] + sum_{a' < m} Ginv[a][a'] Y[a'][c] for a < m, with
+// Ginv = -(the swept variable block, lower triangle read symmetrically) and
+// Y = XtE - lam_v (C - V_F).  grid (ceil(t/64), D/64, B), block 256.
+template <class In, int D>
+__global__ __launch_bounds__(256) void k_csne_update(
+    const double* __restrict__ Cb, const double* __restrict__ Gb, size_t sS, int ld,
+    const double* __restrict__ XtE, const In* __restrict__ V, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ Fidx, const int32_t* __restrict__ msz,
+    const double* __restrict__ lam, double* __restrict__ Cn, int T, int t) {
+  __shared__ double sA[kTile][kRK + 1], sB[kRK][kTile];
+  const int b = blockIdx.z, m = msz[b], a0t = blockIdx.x * kTile, c0 = blockIdx.y * kTile;
+  if (a0t >= m) return;
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const double* C = Cb + b * sS;
+  const double* G = Gb + b * sS;
+  const double lv = lam[2 * b + 1];
+  double acc[4][4] = {};
+  for (int q0 = 0; q0 < m; q0 += kRK) {
+    for (int e = tid; e < kTile * kRK; e += 256) {
+      const int r = e / kRK, k = e % kRK, a = a0t + r, q = q0 + k;
+      const int hi = a > q ? a : q, lo = a > q ? q : a;
+      sA[r][k] = (a < m && q < m) ? -G[static_cast<size_t>(hi) * ld + lo] : 0.0;
+    }
+    for (int e = tid; e < kRK * kTile; e += 256) {
+      const int k = e / kTile, c = e % kTile, q = q0 + k;
+      double y = 0.0;
+      if (q < m) {
+        const int j = idx[static_cast<size_t>(b) * t + Fidx[static_cast<size_t>(b) * t + q]];
+        const double vs = to_f64<In>(V[(static_cast<size_t>(b) * T + j) * D + c0 + c]);
+        y = XtE[(static_cast<size_t>(b) * t + q) * D + c0 + c] -
+            lv * (C[static_cast<size_t>(q) * ld + c0 + c] - vs);
+      }
+      sB[k][c] = y;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kRK; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] = fma(sA[4 * ty + r][k], sB[k][4 * tx + c], acc[r][c]);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int a = a0t + 4 * ty + r;
+    if (a >= m) continue;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int cc = c0 + 4 * tx + c;
+      Cn[(static_cast<size_t>(b) * t + a) * D + cc] = C[static_cast<size_t>(a) * ld + cc] + acc[r][c];
+    }
+  }
+}
+
+// C[a][c] = Cn[b][a][c] for a < m.  grid (ceil(t*D/256), B).
+__global__ void k_csne_copy(double* __restrict__ Cb, size_t sS, int ld,
+                            const double* __restrict__ Cn, const int32_t* __restrict__ msz, int t,
+                            int D) {
+  const int b = blockIdx.y, m = msz[b];
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  const int a = e / D, c = e % D;
+  if (a >= m) return;
+  Cb[b * sS + static_cast<size_t>(a) * ld + c] = Cn[(static_cast<size_t>(b) * t + a) * D + c];
 }
 
 // ---------------------------------------------------------------------------
@@ -3419,15 +3547,27 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
   if (e != hipSuccess) return e;
   prof_mark(12, false, st);
   {
-    int r_al = rv, Dv = D;
+    int r_al = rv, Dv = D, full = fb.refine > 0 ? 1 : 0;
     const int32_t* ms = fb.msz;
-    void* args[] = {&fb.S, &sS,     &ld,  &r_al, &fb.U,     &fb.V, &sUV, &fb.stage, &ms,
-                    &status, &fb.bar, &err, &fb.xcc, &fb.flops, &B,    &Dv,  &tx, &fb.wait_ticks};
+    void* args[] = {&fb.S,   &sS,     &ld,  &r_al,   &fb.U,     &fb.V, &sUV, &fb.stage,
+                    &ms,     &status, &fb.bar, &err, &fb.xcc, &fb.flops, &B,  &Dv,
+                    &tx,     &fb.wait_ticks, &full};
     e = hipLaunchKernel(reinterpret_cast<const void*>(&k_value_sweep), dim3(grid),
                         dim3(kTeamThreads), args, 0, st);
     if (e != hipSuccess) return e;
   }
   prof_mark(12, true, st);
+  for (int step = 0; step < fb.refine; ++step) {
+    hipLaunchKernelGGL((k_csne_resid<D>), dim3((n + kTile - 1) / kTile, D / kTile, B), dim3(256),
+                       0, st, fb.PS, R0, sS, ld, O, fb.msz, fb.E, n, t);
+    launch_atb<double, false>(fb.PS, sPS, t, nullptr, 0, fb.E, static_cast<size_t>(n) * D, D,
+                              fb.Rp, static_cast<size_t>(t) * D, D, n, fb.msz, t, D, fb.part,
+                              fb.part_cap, B, st);
+    hipLaunchKernelGGL((k_csne_update<In, D>), dim3(tt, D / kTile, B), dim3(256), 0, st, R0, G0,
+                       sS, ld, fb.Rp, V, idx, fb.Fidx, fb.msz, fb.lam, fb.Cn, T, t);
+    hipLaunchKernelGGL(k_csne_copy, dim3((t * D + 255) / 256, B), dim3(256), 0, st, R0, sS, ld,
+                       fb.Cn, fb.msz, t, D);
+  }
   if (v_bf16)
     hipLaunchKernelGGL((k_write_out<In, bf16_t>), dim3((t * D + 255) / 256, B), dim3(256), 0, st,
                        R0, sS, ld, V, idx, fb.inv, fb.wv, static_cast<bf16_t*>(out_V), out_bias, T,

@@ -53,6 +53,7 @@ namespace {
 constexpr int64_t kMaxT = 1 << 30;
 constexpr int64_t kMaxT_keep = 4096;  // the fit kernels stage t values in LDS
 constexpr int64_t kMaxB = 65535;
+constexpr int kMaxRefine = 4;  // value-fit refinement steps
 constexpr int kBM = 128;  // reference queries per score workgroup
 
 struct Plan {
@@ -86,7 +87,7 @@ Plan make_plan(const kvc_params_t* p) {
 
 struct Layout {
   size_t ml, lse, Opart, O, imp_part, imp, sel, idx, status, tv, emask, plist, PS, S, U, V, stage, cvec, wv, lam,
-      colpart, Fidx, inv, msz, bar, xcc, flops, part, total;
+      colpart, Fidx, inv, msz, bar, xcc, flops, part, E, Rp, Cn, total;
   size_t part_cap;
   // greedy selection only (zero otherwise)
   size_t P32, o_nrm, o_r, o_chosen, o_part, o_order, o_a, o_Q, o_h, o_q, o_part2;
@@ -142,6 +143,12 @@ Layout make_layout(const kvc_params_t* p, bool omp = false) {
     L.part_cap = cap < lim ? cap : lim;
     L.part = take(L.part_cap * 8);
   }
+  // value-fit refinement: the residual, X_F^T of it and the refined solution
+  if (p->refine_steps > 0) {
+    L.E = take(B * n * d * 8);
+    L.Rp = take(B * t * d * 8);
+    L.Cn = take(B * t * d * 8);
+  }
   if (omp) {
     L.P32 = take(B * n * T * 4);
     L.o_nrm = take(B * T * 8);
@@ -171,7 +178,7 @@ bool params_ok(const kvc_params_t* p) {
   if (!(p->ridge_rel >= 0.0) || !std::isfinite(p->ridge_rel)) return false;
   if (p->max_nnls_iters < 1 || p->max_nnls_iters > 1000) return false;
   if (p->out_v_dtype != KVC_F32 && p->out_v_dtype != KVC_BF16) return false;
-  if (p->refine_steps != 0) return false;
+  if (p->refine_steps < 0 || p->refine_steps > kMaxRefine) return false;
   if (p->reserved != 0) return false;
   return true;
 }
@@ -203,6 +210,13 @@ kvc::FitBufs fit_bufs(void* ws, const Layout& L) {
   fb.inv = at<int32_t>(ws, L.inv);
   fb.msz = at<int32_t>(ws, L.msz);
   fb.tv = nullptr;
+  fb.refine = 0;
+  fb.E = fb.Rp = fb.Cn = nullptr;
+  if (L.E) {
+    fb.E = at<double>(ws, L.E);
+    fb.Rp = at<double>(ws, L.Rp);
+    fb.Cn = at<double>(ws, L.Cn);
+  }
   return fb;
 }
 
@@ -229,6 +243,7 @@ hipError_t run_fit(const kvc_params_t* p, const void* Q, const void* K, const vo
   kvc::FitBufs fb = fit_bufs(ws, L);
   fb.tv = tv;
   fb.wait_ticks = g_wait_ticks;
+  fb.refine = p->refine_steps;
   return kvc::launch_fit<In, D>(Q, K, V, at<double>(ws, L.lse), at<float>(ws, L.O), idx,
                                 fb, out_bias, out_V, p->out_v_dtype == KVC_BF16, status,
                                 static_cast<int>(p->B), static_cast<int>(p->n),
@@ -400,6 +415,12 @@ int kvc_workspace_layout(const kvc_params_t* p, kvc_ws_layout_t* out) {
   out->w = L.wv;
   out->fit_flops = L.flops;
   out->omp_order = make_layout(p, true).o_order;
+  {
+    const size_t ld = static_cast<size_t>(kvc::sweep_ld(static_cast<int>(p->t), static_cast<int>(p->d)));
+    const size_t rv = (static_cast<size_t>(p->d) + 63) / 64 * 64;  // right-hand-side rows
+    out->value_C = L.S + rv * ld * 8;
+    out->value_ld = ld;
+  }
   return KVC_OK;
 }
 

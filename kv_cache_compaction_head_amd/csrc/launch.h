@@ -71,6 +71,10 @@ struct FitBufs {
   double* part;     // split-K partial tiles of the fit GEMMs
   size_t part_cap;  // its capacity in doubles
   uint64_t wait_ticks;  // bound on each team wait (100 MHz constant clock)
+  int refine;           // refinement steps of the value fit (0: none)
+  double* E;            // [B][n][d] residual O - X_F C (refinement only)
+  double* Rp;           // [B][t][d] X_F^T E (refinement only)
+  double* Cn;           // [B][t][d] the refined solution (refinement only)
 };
 // Order of a head's sweep matrix: right-hand-side rows (d rounded up to 64)
 // plus the variables (t rounded up to 64).

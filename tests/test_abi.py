@@ -45,7 +45,7 @@ def test_params_struct_layout_and_defaults():
                                          ("ridge_rel", -1e-9), ("ridge_rel", float("nan")),
                                          ("ridge_rel", float("inf")), ("max_nnls_iters", 0),
                                          ("out_v_dtype", 2), ("refine_steps", -1),
-                                         ("reserved", 1)])
+                                         ("refine_steps", 5), ("reserved", 1)])
 def test_invalid_params_have_no_workspace(field, value):
     p = kvc.make_params(2, 1024, 64, 128, 16, "bf16")
     assert kvc.workspace_bytes(p) > 0
@@ -62,6 +62,17 @@ def test_workspace_grows_with_problem_and_layout_is_aligned():
     L = kvc.workspace_layout(big)
     for off in (L.lse, L.O, L.imp, L.w):
         assert off % 256 == 0 and off < kvc.workspace_bytes(big)
+
+
+def test_value_refinement_adds_its_buffers_to_the_workspace():
+    """refine_steps > 0 needs the residual (B n d doubles) and two B t d
+    double buffers on top of the plain workspace."""
+    B, T, n, d, t = 8, 32768, 2048, 128, 655
+    plain = kvc.workspace_bytes(kvc.make_params(B, T, n, d, t, "bf16"))
+    for steps in (1, 4):
+        ref = kvc.workspace_bytes(kvc.make_params(B, T, n, d, t, "bf16", refine_steps=steps))
+        assert ref - plain >= 8 * (B * n * d + 2 * B * t * d)
+        assert ref - plain < 8 * (B * n * d + 2 * B * t * d) + 3 * 256
 
 
 def _fake(addr):

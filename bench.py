@@ -30,10 +30,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3      # MI355X fp32 MFMA (and packed-fp32 vector)
 PEAK_F32_VALU_TFLOPS = 78.6  # fp32 vector FMA without packed ops: 256 CU x 64 lanes x 2 x 2.4 GHz
-PEAK_F64_TFLOPS = 78.6       # MI355X fp64 (vector and matrix), published
-# what one fp64 MFMA pipe sustains here: v_mfma_f64_16x16x4f64 issues every
-# ~141 cycles per wave at 2.39 GHz (1024 FMAs), 256 CU x 4 SIMD -> 35.5 TFLOP/s
-MEASURED_F64_MFMA_TFLOPS = 35.5
+PEAK_F64_TFLOPS = 78.6       # MI355X fp64 (vector and matrix)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_nnls_sweep_T32k_50x_hbm_traffic.md")
 FIT_SRC = os.path.join(ROOT, "kv_cache_compaction_head_amd", "csrc", "fit.hip")
@@ -331,9 +328,6 @@ def main():
         k = {"kernel": kname, "bound": bound, "ms": round(prof[stage], 4),
              "achieved": round(ach, 3), "peak": peak, "unit": "GB/s" if hbm else "TFLOP/s",
              "frac": round(ach / peak, 5), "work": amount}
-        if peak == PEAK_F64_TFLOPS:
-            k["measured_mfma_peak"] = MEASURED_F64_MFMA_TFLOPS
-            k["frac_of_measured"] = round(ach / MEASURED_F64_MFMA_TFLOPS, 5)
         if kname in ("k_nnls_sweep", "k_value_sweep"):
             k["limited_by"] = "latency of the chain of dependent block steps"
         kernels.append(k)

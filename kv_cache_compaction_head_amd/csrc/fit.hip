@@ -22,6 +22,7 @@
 // Keys whose multiplier is pinned at zero carry a factor 1e-30 in X; their
 // coupling to the rest is ~1e-30 relative, so the value system is solved on
 // the passive set only and those keys keep C_v = V (the ridge prior).
+#include <type_traits>
 #include <utility>
 
 #include "common.h"
@@ -213,34 +214,37 @@ __device__ __forceinline__ void atb_decode(bool sym, int tile, int tb, int& ty, 
   }
 }
 
-// One 64 x 64 tile (a0, c0) over rows [k0, k1) into acc.
+// One 64 x 64 tile (a0, c0) over rows [k0, k1) into acc.  live: whether this
+// wave's 32 x 32 quadrant holds entries that are needed (a wave whose
+// quadrant is past the sizes or strictly above the diagonal still stages its
+// share of the chunks, but issues no MFMAs).
 template <class TB, bool SYM>
 __device__ __forceinline__ void atb_tile(const double* __restrict__ Ab, int lda,
                                          const int32_t* __restrict__ ca,
                                          const TB* __restrict__ Bb, int ldb, int mA, int mB,
                                          int a0, int c0, int k0, int k1, double* sAt, double* sBt,
-                                         f64x4 (&acc)[2][2]) {
+                                         f64x4 (&acc)[2][2], bool live = true) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  constexpr int NE = kKC * kTile / 256;
-  int colA_r[NE], colB_r[NE];
-#pragma unroll
-  for (int q = 0; q < NE; ++q) {
-    const int r = (threadIdx.x + q * 256) % kTile;
-    const int a = a0 + r, c = c0 + r;
-    colA_r[q] = a < mA ? (ca ? ca[a] : a) : -1;
-    colB_r[q] = c < mB ? (SYM ? (ca ? ca[c] : c) : c) : -1;
-  }
+  // each thread stages one column of A and of B, rows r0, r0 + 4, ... of a
+  // chunk; r0 is its wave's index, so each load is a uniform row address plus
+  // a per-lane column offset
+  constexpr int NE = kKC * kTile / 256, RS = 256 / kTile;
+  const int r0 = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kTile);
+  const int cl = static_cast<int>(threadIdx.x) % kTile;
+  const int colA = a0 + cl < mA ? (ca ? ca[a0 + cl] : a0 + cl) : -1;
+  const int colB = c0 + cl < mB ? (SYM ? (ca ? ca[c0 + cl] : c0 + cl) : c0 + cl) : -1;
   double va[NE], vb[NE];
   auto fetch = [&](int kbase) {
 #pragma unroll
     for (int q = 0; q < NE; ++q) {
-      const int e = threadIdx.x + q * 256, i = kbase + e / kTile;
-      va[q] = (i < k1 && colA_r[q] >= 0) ? Ab[static_cast<size_t>(i) * lda + colA_r[q]] : 0.0;
+      const int i = kbase + r0 + q * RS;
+      const double* rowA = Ab + static_cast<size_t>(i) * lda;
+      va[q] = (i < k1 && colA >= 0) ? rowA[colA] : 0.0;
       if (SYM)
-        vb[q] = (i < k1 && colB_r[q] >= 0) ? Ab[static_cast<size_t>(i) * lda + colB_r[q]] : 0.0;
+        vb[q] = (i < k1 && colB >= 0) ? rowA[colB] : 0.0;
       else
-        vb[q] = (i < k1 && colB_r[q] >= 0)
-                    ? static_cast<double>(Bb[static_cast<size_t>(i) * ldb + colB_r[q]])
+        vb[q] = (i < k1 && colB >= 0)
+                    ? static_cast<double>(Bb[static_cast<size_t>(i) * ldb + colB])
                     : 0.0;
     }
   };
@@ -249,18 +253,24 @@ __device__ __forceinline__ void atb_tile(const double* __restrict__ Ab, int lda,
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) acc[ra][rb] = f64x4{0.0, 0.0, 0.0, 0.0};
   if (k0 < k1) fetch(k0);
-  for (int k = k0; k < k1; k += kKC) {
-    __syncthreads();
+  // (the loop is written out twice, with and without the MFMAs, so that the
+  // accumulators carry no merge across a branch inside it)
+  auto chunks = [&](auto mfma) {
+    for (int k = k0; k < k1; k += kKC) {
+      __syncthreads();
 #pragma unroll
-    for (int q = 0; q < NE; ++q) {
-      const int e = threadIdx.x + q * 256;
-      sAt[e] = va[q];
-      sBt[e] = vb[q];
+      for (int q = 0; q < NE; ++q) {
+        const int e = threadIdx.x + q * 256;
+        sAt[e] = va[q];
+        sBt[e] = vb[q];
+      }
+      __syncthreads();
+      if (k + kKC < k1) fetch(k + kKC);
+      if constexpr (decltype(mfma)::value) tile_mma(sAt, sBt, acc, wave, lane);
     }
-    __syncthreads();
-    if (k + kKC < k1) fetch(k + kKC);
-    tile_mma(sAt, sBt, acc, wave, lane);
-  }
+  };
+  if (live) chunks(std::true_type{});
+  else chunks(std::false_type{});
 }
 
 template <class TB, bool SYM>
@@ -278,7 +288,8 @@ __global__ __launch_bounds__(256) void k_atb(const double* __restrict__ A, size_
   const AtbShape sh = atb_shape(mA, mB, SYM, G, cap_tiles, nrows, gridDim.x / G);
   if (g >= sh.nt * sh.ks && sh.ks > 1) return;
   const int tb = (mB + kTile - 1) / kTile;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63;
   const double* Ab = A + b * sA;
   const TB* Bb = Bm + b * sB;
   const int32_t* ca = colA ? colA + b * sColA : nullptr;
@@ -295,7 +306,14 @@ __global__ __launch_bounds__(256) void k_atb(const double* __restrict__ A, size_
     int ty, tx;
     atb_decode(SYM, tile, tb, ty, tx);
     const int a0 = ty * kTile, c0 = tx * kTile;
-    atb_tile<TB, SYM>(Ab, lda, ca, Bb, ldb, mA, mB, a0, c0, k0, k1, sAt, sBt, acc);
+    // this wave's quadrant: wanted unless past the sizes or (symmetric)
+    // strictly above the diagonal; off-diagonal quadrants of a symmetric
+    // product are mirrored
+    const int qa = a0 + (wave >> 1) * 32, qc = c0 + (wave & 1) * 32;
+    const bool live = qa < mA && qc < mB && !(SYM && qa < qc);
+    const bool mirror = SYM && qa != qc;
+    atb_tile<TB, SYM>(Ab, lda, ca, Bb, ldb, mA, mB, a0, c0, k0, k1, sAt, sBt, acc, live);
+    if (!live) return;
     double* P = part + (static_cast<size_t>(b) * cap_tiles + split * sh.nt + tile) * (kTile * kTile);
 #pragma unroll
     for (int ra = 0; ra < 2; ++ra)
@@ -309,14 +327,15 @@ __global__ __launch_bounds__(256) void k_atb(const double* __restrict__ A, size_
             P[rr * kTile + cc] = acc[ra][rb][i];
           } else if (r < mA && c < mB) {
             Cb[static_cast<size_t>(r) * ldc + c] = acc[ra][rb][i];
-            if (SYM && tx != ty) Cb[static_cast<size_t>(c) * ldc + r] = acc[ra][rb][i];
+            if (mirror) Cb[static_cast<size_t>(c) * ldc + r] = acc[ra][rb][i];
           }
         }
   }
 }
 
 // Sum a head's row slices of each tile in order and store (mirrored for
-// symmetric products); nothing to do for heads computed whole.  grid
+// symmetric products, whose entries above the diagonal of a diagonal tile are
+// taken from below it); nothing to do for heads computed whole.  grid
 // (tiles that may split * 16, B), block 256: one element per thread.
 template <bool SYM>
 __global__ __launch_bounds__(256) void k_atb_reduce(const double* __restrict__ part,
@@ -336,11 +355,12 @@ __global__ __launch_bounds__(256) void k_atb_reduce(const double* __restrict__ p
   const double* P = part + (static_cast<size_t>(b) * cap_tiles + tile) * (kTile * kTile);
   const int e = (blockIdx.x & 15) * 256 + threadIdx.x;
   const int r = a0 + e / kTile, c = c0 + e % kTile;
+  if (SYM && r < c) return;
   double v = 0.0;
   for (int sp = 0; sp < sh.ks; ++sp) v += P[static_cast<size_t>(sp) * sh.nt * kTile * kTile + e];
   if (r < mA && c < mB) {
     Cb[static_cast<size_t>(r) * ldc + c] = v;
-    if (SYM && tx != ty) Cb[static_cast<size_t>(c) * ldc + r] = v;
+    if (SYM && r != c) Cb[static_cast<size_t>(c) * ldc + r] = v;
   }
 }
 

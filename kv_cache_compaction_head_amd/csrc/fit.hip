@@ -2596,10 +2596,13 @@ __device__ __forceinline__ void wave_tile(const SweepMat& M, int I, int J, int r
 }
 
 // Active tiles of a step in row-major order: variable band Iv (0..nvb-1) has
-// nrb right-hand-side tiles, then, unless Iv < skip, variable tiles 0..Iv.
+// nrb right-hand-side tiles, then, unless Iv < skip, variable tiles c0..Iv;
+// bands below c0 have none (c0 > 0: forward elimination, see sweep_step).
 struct TileWalk {
-  int Iv, j, nrb, skip, vb0;
-  __device__ int count(int iv) const { return nrb + (iv >= skip ? iv + 1 : 0); }
+  int Iv, j, nrb, skip, vb0, c0;
+  __device__ int count(int iv) const {
+    return iv < c0 ? 0 : nrb + (iv >= skip ? iv + 1 - c0 : 0);
+  }
   __device__ void seek(int a) {
     Iv = 0;
     while (a >= count(Iv)) {
@@ -2615,12 +2618,17 @@ struct TileWalk {
     }
   }
   __device__ int I() const { return vb0 + Iv; }
-  __device__ int J() const { return j < nrb ? j : vb0 + j - nrb; }
+  __device__ int J() const { return j < nrb ? j : vb0 + c0 + j - nrb; }
 };
 
 // One sweep step over the k pivots in sm.piv / sm.sgn / sm.pos, by the team.
 // Tiles whose row band is a variable band below skip_below (and whose column
 // is a variable band) are left alone: the value fit never reads them again.
+// c0 > 0 (the value fit's forward elimination, pivots in band c0 = skip_below
+// swept in order): no band below c0 is touched at all, and variable tiles
+// start at column band c0.  Bands already swept then keep the values of
+// their own step: right-hand sides (A_PP^-1 b_P) and, below them, pivot
+// columns (A_iP A_PP^-1); sweep_backsub turns those into the solution.
 //
 // Lookahead: when the next step's kn pivots are already known (sm.piv2,
 // sm.sgn2) and the team has more than one member, its last member does no
@@ -2632,7 +2640,7 @@ struct TileWalk {
 // Returns whether a pivot of this step had the wrong sign (a lookahead
 // member flags its own into *status).
 __device__ __forceinline__ bool sweep_step(const SweepMat& M, Team& tm, int k, int skip_below,
-                                           int kn, bool pre) {
+                                           int kn, bool pre, int c0) {
   SweepSmem& sm = g_sw;
   const int trank = tm.rank, tsize = tm.size;
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
@@ -2669,9 +2677,10 @@ __device__ __forceinline__ bool sweep_step(const SweepMat& M, Team& tm, int k, i
   // built: the lookahead member needs L^-1 and D alone
   if (!me_la) small_b(k);
   if (!me_la) {
-    for (int bi = trank; bi < 2 * (nrb + nvb); bi += vmembers) {
+    // (the bands of the right-hand sides and of variable bands c0 on)
+    for (int bi = trank; bi < 2 * (nrb + nvb - c0); bi += vmembers) {
       const int b = bi >> 1;
-      v_band(M, b < nrb ? b : vb0 + b - nrb, bi & 1, k);
+      v_band(M, b < nrb ? b : vb0 + c0 + b - nrb, bi & 1, k);
     }
   } else {
     // the next pivot block after this step's update, A' = A[P', P'] -
@@ -2761,7 +2770,7 @@ __device__ __forceinline__ bool sweep_step(const SweepMat& M, Team& tm, int k, i
         }
   }
   int total = 0;
-  for (int iv = 0; iv < nvb; ++iv) total += nrb + (iv >= skip_below ? iv + 1 : 0);
+  for (int iv = c0; iv < nvb; ++iv) total += nrb + (iv >= skip_below ? iv + 1 - c0 : 0);
   const int workers = la ? tsize - 1 : tsize;
   const int nw = workers * (kTeamThreads / 64);
   const int parts = 2 * total <= nw ? 4 : (total < nw ? 2 : 1);
@@ -2818,7 +2827,7 @@ __device__ __forceinline__ bool sweep_step(const SweepMat& M, Team& tm, int k, i
           wave_tile<4, 1>(M, vb0 + a, 0, 0, 0, nch);
         } else {
           const int av = a - rtasks, part = av % parts;
-          TileWalk w{0, 0, narrow ? 0 : nrb, skip_below, vb0};
+          TileWalk w{0, 0, narrow ? 0 : nrb, skip_below, vb0, c0};
           w.seek(av / parts);
           if (parts == 1) wave_tile<4, 4>(M, w.I(), w.J(), 0, 0, nch);
           else if (parts == 2) wave_tile<2, 4>(M, w.I(), w.J(), 2 * part, 0, nch);
@@ -2886,18 +2895,98 @@ __device__ __noinline__ bool sweep_step_call(const SweepMat M_arg, Team& team_re
   const SweepMat M = uniform_mat(M_arg);
   Team tm = uniform_team(team_ref);
   const bool bad = sweep_step(M, tm, uniform(k_arg), uniform(skip_arg), uniform(kn_arg),
-                              uniform(static_cast<int>(pre_arg)) != 0);
+                              uniform(static_cast<int>(pre_arg)) != 0, 0);
   team_ref.gen = tm.gen;
   team_ref.tbase = tm.tbase;
   team_ref.pubs = tm.pubs;
   return bad;
 }
 
+// Back substitution after the forward elimination (sweep_step with c0 > 0)
+// of the value system's n variables: band k's right-hand sides hold
+// Y_k = A_kk^-1 b_k and band j > k's pivot columns of band k hold
+// L_jk = A_jk A_kk^-1 (the blocks as they stood at step k), so the solution
+// is X_k = Y_k - sum_{j > k} L_jk^T X_j.  Taken band by band from the last:
+// once X_j is final, every (band k < j, right-hand-side tile) of it is a
+// workgroup task (the team's workgroups take them in turn), with a team
+// barrier between bands.
+__device__ __forceinline__ void wg_backsub(const SweepMat& M, int J, int K, int r) {
+  SweepSmem& sm = g_sw;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+  const int g16 = lane >> 4, l16 = lane & 15, wr = wave >> 1, wc = wave & 1;
+  // L_JK (rows b of band J, columns a of band K) into pp, X_J's tile r into
+  // li; rows past the variables and columns past the right-hand sides are 0
+  __syncthreads();  // the previous task's reads of pp and li are done
+#pragma unroll 4
+  for (int e = tid; e < kSB * kSB; e += kTeamThreads) {
+    const int b = e >> 6, x = e & 63;
+    const int row = J * kSB + b, col = r * kSB + x;
+    const bool ok = s_active(M, row);
+    const gdouble* p = M.S + static_cast<size_t>(ok ? row : 0) * M.ld;
+    const double l = p[ok ? K * kSB + x : 0], xv = p[ok && col < M.n_rhs ? col : 0];
+    sm.pp[b][x] = ok ? l : 0.0;
+    sm.li[b][x] = ok && col < M.n_rhs ? xv : 0.0;
+  }
+  __syncthreads();
+  // each wave a 32 x 32 quadrant of the 64 x 64 update L_JK^T X_J
+  f64x4 acc[2][2] = {};
+#pragma unroll
+  for (int c = 0; c < kSB / 4; ++c) {
+    const int b = 4 * c + g16;
+    double av[2], bv[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      av[x] = sm.pp[b][wr * 32 + x * 16 + l16];
+      bv[x] = sm.li[b][wc * 32 + x * 16 + l16];
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+        acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[x], bv[y], acc[x][y], 0, 0, 0);
+  }
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = K * kSB + wr * 32 + x * 16 + g16 + 4 * i;
+        const int col = r * kSB + wc * 32 + y * 16 + l16;
+        if (s_active(M, row) && col < M.n_rhs)
+          M.S[static_cast<size_t>(row) * M.ld + col] -= acc[x][y][i];
+      }
+}
+
+// Whether the value system of n variables and d right-hand sides is solved
+// by forward elimination and back substitution rather than the whole sweep.
+// The elimination skips the swept bands' tiles, but the back substitution
+// adds a team barrier per band: it pays when a team of one workgroup does
+// all tiles itself, or when the first step's tiles fill the team's waves
+// (4 a member) at least twice over.
+__device__ __forceinline__ bool value_elim(int n, int d, int tsize, bool full) {
+  const int nvb = (n + kSB - 1) / kSB, nrb = (d + kSB - 1) / kSB;
+  if (full || nvb < 2) return false;
+  return tsize == 1 || nvb * nrb + nvb * (nvb + 1) / 2 > 8 * tsize;
+}
+
+__device__ __forceinline__ void sweep_backsub(const SweepMat& M, Team& tm, int n) {
+  const int nvb = (n + kSB - 1) / kSB, nrb = (M.n_rhs + kSB - 1) / kSB;
+  const int vb0 = M.r_al / kSB;
+  for (int j = nvb - 1; j >= 1; --j) {
+    for (int a = tm.rank; a < j * nrb; a += tm.size) wg_backsub(M, vb0 + j, vb0 + a / nrb, a % nrb);
+    team_sync(tm);
+  }
+}
+
 // The value system's n variables (rows r_al .. r_al + n - 1), swept in 64 at
 // a time, as one call: the per-step call costs more here than the register
-// pressure of the loop around the inlined step.  Unless `full`, no tile above
-// the swept bands is updated (the solution needs none of them); with it the
-// variable block ends as -(G + lam I)^-1, which the refinement steps apply.
+// pressure of the loop around the inlined step.  Unless `full`, no tile of a
+// swept band is updated again: either its variable tiles alone are left (the
+// solution needs none of them), or (value_elim) the bands are eliminated
+// forward and the solution taken by back substitution, about half the tile
+// work of the sweep.  With `full` the whole sweep runs and the variable
+// block ends as -(G + lam I)^-1, which the refinement steps apply.
 __device__ __noinline__ bool sweep_run(const SweepMat M_arg, Team& team_ref, int n_arg,
                                        int full_arg) {
   SweepSmem& sm = g_sw;
@@ -2906,6 +2995,7 @@ __device__ __noinline__ bool sweep_run(const SweepMat M_arg, Team& team_ref, int
   const bool full = uniform(full_arg) != 0;
   Team tm = uniform_team(team_ref);
   const int tid = threadIdx.x;
+  const bool elim = value_elim(n, M.n_rhs, tm.size, full);
   bool bad = false;
   for (int s0 = 0; s0 < n; s0 += kSB) {
     const int k = min(kSB, n - s0);
@@ -2920,10 +3010,12 @@ __device__ __noinline__ bool sweep_run(const SweepMat M_arg, Team& team_ref, int
       sm.sgn2[tid] = 1.0;
     }
     __syncthreads();
-    bad |= sweep_step(M, tm, k, full ? 0 : s0 / kSB, kn, s0 > 0 && tm.size > 1);
+    bad |= sweep_step(M, tm, k, full ? 0 : s0 / kSB, kn, s0 > 0 && tm.size > 1,
+                      elim ? s0 / kSB : 0);
     if (tid < k) sm.pos[M.r_al + s0 + tid] = -1;
     __syncthreads();
   }
+  if (elim) sweep_backsub(M, tm, n);
   team_ref.gen = tm.gen;
   team_ref.tbase = tm.tbase;
   team_ref.pubs = tm.pubs;
@@ -3192,8 +3284,15 @@ __global__ __launch_bounds__(256) void k_value_sweep(
                      gptr(stage + static_cast<size_t>(b) * kStage), ld, r_al, D, m, nullptr};
     const bool bad = sweep_run(M, tm, m, full);
     if (tm.rank == 0 && tid == 0) {
+      // a sweep (what it counts is the whole sweep's work either way); or
+      // the elimination over the part not yet swept and the back
+      // substitution (each band's rows against all bands above it)
+      const bool elim = value_elim(m, D, tm.size, full != 0);
       double fl = 0.0;
-      for (int s0 = 0; s0 < m; s0 += kSB) fl += sweep_flops(min(kSB, m - s0), m + D);
+      for (int s0 = 0; s0 < m; s0 += kSB) {
+        const int k = min(kSB, m - s0);
+        fl += elim ? sweep_flops(k, m - s0 + D) + 2.0 * s0 * k * D : sweep_flops(k, m + D);
+      }
       flops[2 * b + 1] = fl;
     }
     // every member reports the failed pivots it saw (the lookahead member,

@@ -132,6 +132,24 @@ def test_full_configs(cfg, heads):
                                     for k, v in err.items()}, flush=True)
 
 
+@pytest.mark.parametrize("seed,T,n,d,t,keys", [(60, 2048, 512, 128, 600, "clusters"),
+                                                (61, 2048, 512, 64, 333, "student_t3")])
+def test_value_elimination_on_one_workgroup_teams(seed, T, n, d, t, keys):
+    """256 heads give each head a team of one workgroup, whose value system is
+    solved by forward elimination and back substitution (the sweep's swept
+    bands left alone): the fitted values of sampled heads against the
+    oracle's least squares, with ragged last bands (m not a multiple of 64)
+    and one or two right-hand-side bands."""
+    w = synth.custom(seed, 256, T, n, d, t, "bf16", keys)
+    data = synth.batch(w)
+    gpu = run_gpu(w, data)
+    assert (gpu["status"] == 0).all(), gpu["status"]
+    for h in (0, 77, 255):
+        err = compare_head(gpu, h, data, w.t, _tol(w))
+        print(f"elim head {h}:", {k: (float(f"{v:.3g}") if isinstance(v, float) else v)
+                                  for k, v in err.items()}, flush=True)
+
+
 def _chunk_view(w, data, gpu_res, C):
     """Recast a chunked result as B*C independent heads (entry h*C + c is chunk c
     of head h, with chunk-local indices) so each entry compares against the

@@ -628,10 +628,12 @@ __device__ __forceinline__ float half_wave_rowsum(const Vec& v, int lane) {
   float w[8], x[4], y[2];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float a = SQ ? v[i] * v[i] : v[i], c = SQ ? v[8 + i] * v[8 + i] : v[8 + i];
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(c),
-                                                    false, false);
-    w[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    // the swap moves the values themselves; squaring after it takes one
+    // multiply and one FMA per pair instead of two multiplies and an add
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]),
+                                                    __float_as_uint(v[8 + i]), false, false);
+    const float r0 = __uint_as_float(r[0]), r1 = __uint_as_float(r[1]);
+    w[i] = SQ ? fmaf(r0, r0, r1 * r1) : r0 + r1;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -875,6 +877,29 @@ __global__ __launch_bounds__(256) void k_expweight(const In* __restrict__ Q,
 //     permutation and V no transposed copy.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// p = hi + lo for eight values: hi = bf16(p), lo = bf16(p - hi), both rounded
+// to nearest even, two values per conversion; hi's float value is its bf16
+// bits shifted (low half) or masked (high half) into place.
+__device__ __forceinline__ void split_hi_lo(const f32x16& p, int base, bf16x8& hi, bf16x8& lo) {
+  bf16x2 h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p0 = p[base + 2 * i], p1 = p[base + 2 * i + 1];
+    h[i] = __builtin_convertvector((f32x2{p0, p1}), bf16x2);
+    const uint32_t u = __builtin_bit_cast(uint32_t, h[i]);
+    const float h0 = __uint_as_float(u << 16), h1 = __uint_as_float(u & 0xffff0000u);
+    l[i] = __builtin_convertvector((f32x2{p0 - h0, p1 - h1}), bf16x2);
+  }
+  const bf16x4 h01 = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3);
+  const bf16x4 h23 = __builtin_shufflevector(h[2], h[3], 0, 1, 2, 3);
+  const bf16x4 l01 = __builtin_shufflevector(l[0], l[1], 0, 1, 2, 3);
+  const bf16x4 l23 = __builtin_shufflevector(l[2], l[3], 0, 1, 2, 3);
+  hi = __builtin_shufflevector(h01, h23, 0, 1, 2, 3, 4, 5, 6, 7);
+  lo = __builtin_shufflevector(l01, l23, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 __device__ __forceinline__ bf16x4 lds_read_tr16(const bf16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
@@ -912,6 +937,13 @@ __global__ __launch_bounds__(256) void k_expweight_bf16(
   const double l2 = q < n ? lse[static_cast<size_t>(b) * n + q] * 1.4426950408889634 : 0.0;
   const float ml2 = q < n ? static_cast<float>(l2) : INFINITY;
   const float ml2lo = q < n ? static_cast<float>(l2 - static_cast<double>(ml2)) : 0.f;
+  // The low part enters as the score accumulators' initial value (divided by
+  // log2e), so each p costs one FMA and one exp2: the accumulator holds
+  // s - ml2lo/log2e, rounded once like s alone.
+  const float c0 = -ml2lo * (1.0f / KVC_LOG2E);
+  f32x16 cinit;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) cinit[r] = c0;
 
   // this thread's chunks of a tile (K and V alike): chunk c is slot
   // threadIdx.x + 256 c, i.e. row r = slot / CPR holding source chunk
@@ -986,7 +1018,7 @@ __global__ __launch_bounds__(256) void k_expweight_bf16(
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks)
         ka[ks] = *reinterpret_cast<const bf16x8*>(sk + roff[ks] + st * 32 * D);
-      f32x16 acc{};
+      f32x16 acc = cinit;
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks)
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], bq[ks], acc, 0, 0, 0);
@@ -994,13 +1026,12 @@ __global__ __launch_bounds__(256) void k_expweight_bf16(
       __builtin_amdgcn_sched_group_barrier(0x008, NK, 0);
       if (whole) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          acc[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2) - ml2lo);
+        for (int r = 0; r < 16; ++r) acc[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2));
       } else {
         const unsigned live = live_rows(st, valid, mb, lane);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2) - ml2lo);
+          const float e = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2));
           acc[r] = ((live >> r) & 1u) ? e : 0.f;
         }
       }
@@ -1013,13 +1044,7 @@ __global__ __launch_bounds__(256) void k_expweight_bf16(
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         bf16x8 hi, lo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = acc[h * 8 + e];
-          const __bf16 ph = static_cast<__bf16>(p);
-          hi[e] = ph;
-          lo[e] = static_cast<__bf16>(p - static_cast<float>(ph));
-        }
+        split_hi_lo(acc, h * 8, hi, lo);
         const int kk = 2 * st + h;  // 16-key step of the tile
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) {

@@ -1011,20 +1011,24 @@ __global__ __launch_bounds__(256) void k_expweight_bf16(
     const bf16_t* sv = sV + cur * TILE;
     const uint64_t mb = MASK ? sMb[cur] : 0;
     const bool whole = mb == 0 && valid >= BN;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      __builtin_amdgcn_sched_barrier(0);
+    // Two halves of 32 keys, software-pipelined inside the tile: the scores
+    // of half 1 go to the matrix pipe while half 0's weights are formed, and
+    // half 0's P.V products while half 1's weights are formed.
+    auto scores = [&](int st, f32x16& acc) {
       bf16x8 ka[NK];
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks)
         ka[ks] = *reinterpret_cast<const bf16x8*>(sk + roff[ks] + st * 32 * D);
-      f32x16 acc = cinit;
+      acc = cinit;
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks)
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], bq[ks], acc, 0, 0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, NK, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, NK, 0);
-      if (whole) {
+    };
+    // p = exp(s - lse) of half st (excluded keys and keys past the split
+    // end: 0), its bf16 hi/lo split, then its importance partial (the
+    // butterfly overwrites acc)
+    auto weights = [&](auto whole_c, int st, f32x16& acc, bf16x8 (&hi)[2], bf16x8 (&lo)[2]) {
+      if constexpr (decltype(whole_c)::value) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], KVC_LOG2E, -ml2));
       } else {
@@ -1035,27 +1039,57 @@ __global__ __launch_bounds__(256) void k_expweight_bf16(
           acc[r] = ((live >> r) & 1u) ? e : 0.f;
         }
       }
-      {
-        const float tot = half_wave_rowsum<RMS>(acc, lane);
-        const int r = ((lane >> 4) & 1) * 8 + ((lane >> 3) & 1) * 4 + ((lane >> 2) & 1) * 2 +
-                      ((lane >> 1) & 1);
-        if ((lane & 1) == 0) sImp[cur][wave][st * 32 + mfma32_row(r, lane)] = tot;
-      }
+      split_hi_lo(acc, 0, hi[0], lo[0]);
+      split_hi_lo(acc, 8, hi[1], lo[1]);
+      const float tot = half_wave_rowsum<RMS>(acc, lane);
+      const int r = ((lane >> 4) & 1) * 8 + ((lane >> 3) & 1) * 4 + ((lane >> 2) & 1) * 2 +
+                    ((lane >> 1) & 1);
+      if ((lane & 1) == 0) sImp[cur][wave][st * 32 + mfma32_row(r, lane)] = tot;
+    };
+    auto pv = [&](int st, const bf16x8 (&hi)[2], const bf16x8 (&lo)[2]) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        bf16x8 hi, lo;
-        split_hi_lo(acc, h * 8, hi, lo);
         const int kk = 2 * st + h;  // 16-key step of the tile
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) {
           const bf16x4 v0 = lds_read_tr16(sv + voff[dt][0] + kk * 16 * D);
           const bf16x4 v1 = lds_read_tr16(sv + voff[dt][1] + kk * 16 * D);
           const bf16x8 a = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-          accO[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, hi, accO[dt], 0, 0, 0);
-          accO[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, lo, accO[dt], 0, 0, 0);
+          accO[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, hi[h], accO[dt], 0, 0, 0);
+          accO[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, lo[h], accO[dt], 0, 0, 0);
         }
       }
-    }
+    };
+    auto halves = [&](auto whole_c) {
+      f32x16 a0, a1;
+      bf16x8 h0[2], l0[2], h1[2], l1[2];
+      __builtin_amdgcn_sched_barrier(0);
+      scores(0, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      scores(1, a1);
+      weights(whole_c, 0, a0, h0, l0);
+      // the K reads of half 1, then each of its MFMAs followed by weight work
+      __builtin_amdgcn_sched_group_barrier(0x100, NK, 1);
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, 14, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      pv(0, h0, l0);
+      weights(whole_c, 1, a1, h1, l1);
+      // half 0's P.V (two value reads, two MFMAs) interleaved with weight work
+#pragma unroll
+      for (int i = 0; i < 2 * ND; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 2);
+        __builtin_amdgcn_sched_group_barrier(0x002, 14, 2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      pv(1, h1, l1);
+    };
+    if (whole) halves(std::true_type{});
+    else halves(std::false_type{});
     // publish the next tile's mask bits; its copies must have landed
     if (MASK && wave == 0 && it + 1 < ntile) {
       const uint64_t pm = __ballot(mb_next != 0);

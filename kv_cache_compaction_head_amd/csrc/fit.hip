@@ -364,23 +364,6 @@ __global__ __launch_bounds__(256) void k_atb_reduce(const double* __restrict__ p
   }
 }
 
-// c = P_S^T 1 from the partial column sums k_ps writes per 64-query tile:
-// four threads per column each add a quarter of the tiles in order, then the
-// quarters are added in order.  grid (ceil(t/64), B), block 256.
-__global__ __launch_bounds__(256) void k_colsum_final(const double* __restrict__ part,
-                                                      double* __restrict__ out, int nslab, int t) {
-  __shared__ double sh[4][64];
-  const int b = blockIdx.y, col = threadIdx.x & 63, qt = threadIdx.x >> 6;
-  const int a = blockIdx.x * 64 + col;
-  const int per = (nslab + 3) / 4, k0 = qt * per, k1 = min(nslab, k0 + per);
-  double s = 0.0;
-  if (a < t)
-    for (int k = k0; k < k1; ++k) s += part[(static_cast<size_t>(b) * nslab + k) * t + a];
-  sh[qt][col] = s;
-  __syncthreads();
-  if (qt == 0 && a < t) out[static_cast<size_t>(b) * t + a] = ((sh[0][col] + sh[1][col]) + sh[2][col]) + sh[3][col];
-}
-
 // Block-wide sum (blockDim 256..1024), deterministic tree order.
 __device__ double block_sum(double v, double* sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -424,15 +407,21 @@ __device__ int block_count(int v, int* sh) {
 // Bias system of head b in its sweep matrix (right-hand side in row 0,
 // variables from row 64; see the sweep engine below): the Gram M = P_S^T P_S
 // is already in the variable block.  k_bias_lam: lam_w = ridge * tr(M) / t,
-// and the scale tr(M) / t beside it for a raised ridge (grid (B), block 1024).  k_bias_prep then adds lam_w to the diagonal,
-// stores c = P_S^T 1 + lam_w in column 0 of the variable rows and clears
+// and the scale tr(M) / t beside it for a raised ridge, and c = P_S^T 1 from
+// the partial column sums k_ps writes per 64-query tile (four threads per
+// column each add a quarter of the tiles in order, then the quarters are
+// added in order); grid (B), block 1024.  k_bias_prep then adds lam_w to the
+// diagonal, stores c + lam_w in column 0 of the variable rows and clears
 // columns 1..63 (unused right-hand-side slots), one wave per row (grid
-// (ceil(t/16), B), block 1024).
+// (ceil(t/16), B), block 1024); its threads also clear the team barrier words
+// of the pivoting launch that follows.
 __global__ __launch_bounds__(1024) void k_bias_lam(const double* __restrict__ S, size_t sS, int ld,
                                                    double* __restrict__ lam,
                                                    const int32_t* __restrict__ tv, int t_str,
-                                                   double ridge) {
+                                                   double ridge, const double* __restrict__ part,
+                                                   double* __restrict__ colsum, int nslab) {
   __shared__ double sh[16];
+  __shared__ double q4[4][256];
   const int b = blockIdx.x;
   const int t = tv ? tv[b] : t_str;
   const double* Sb = S + b * sS;
@@ -444,11 +433,34 @@ __global__ __launch_bounds__(1024) void k_bias_lam(const double* __restrict__ S,
     lam[2 * b] = ridge * tr / t;
     lam[2 * b + 1] = tr / t;
   }
+  const int qt = threadIdx.x >> 8, col = threadIdx.x & 255;
+  const int per = (nslab + 3) / 4, k0 = qt * per, k1 = min(nslab, k0 + per);
+  for (int a0 = 0; a0 < t_str; a0 += 256) {
+    const int a = a0 + col;
+    double s = 0.0;
+    if (a < t_str)
+      for (int k = k0; k < k1; ++k) s += part[(static_cast<size_t>(b) * nslab + k) * t_str + a];
+    q4[qt][col] = s;
+    __syncthreads();
+    if (qt == 0 && a < t_str)
+      colsum[static_cast<size_t>(b) * t_str + a] = ((q4[0][col] + q4[1][col]) + q4[2][col]) + q4[3][col];
+    __syncthreads();
+  }
+}
+// Every thread of the grid clears its share of the nbar team barrier words.
+__device__ __forceinline__ void clear_bar(unsigned* __restrict__ bar, int nbar) {
+  const size_t nt = static_cast<size_t>(gridDim.x) * gridDim.y * blockDim.x;
+  for (size_t i = (static_cast<size_t>(blockIdx.y) * gridDim.x + blockIdx.x) * blockDim.x +
+                  threadIdx.x;
+       i < static_cast<size_t>(nbar); i += nt)
+    bar[i] = 0u;
 }
 __global__ __launch_bounds__(1024) void k_bias_prep(double* __restrict__ S, size_t sS, int ld,
                                                     const double* __restrict__ colsum,
                                                     const double* __restrict__ lam,
-                                                    const int32_t* __restrict__ tv, int t_str) {
+                                                    const int32_t* __restrict__ tv, int t_str,
+                                                    unsigned* __restrict__ bar, int nbar) {
+  clear_bar(bar, nbar);
   const int b = blockIdx.y;
   const int t = tv ? tv[b] : t_str;
   const double lw = lam[2 * b];
@@ -3358,12 +3370,15 @@ __global__ void k_ridge_v(double* __restrict__ Gb, size_t sS, int ld,
   if (threadIdx.x == 0) lam[2 * b + 1] = lv;
 }
 
-// R[a][c] += lam_v * V[idx[F[a]]][c]  (R at Rb, stride ld).  grid (ceil(t*D/256), B).
+// R[a][c] += lam_v * V[idx[F[a]]][c]  (R at Rb, stride ld); the grid's
+// threads also clear the team barrier words of the value sweep that follows.
+// grid (ceil(t*D/256), B).
 template <class In>
 __global__ void k_rhs_ridge(double* __restrict__ Rb, size_t sS, int ld, const In* __restrict__ V,
                             const int32_t* __restrict__ idx, const int32_t* __restrict__ Fidx,
                             const int32_t* __restrict__ msz, const double* __restrict__ lam,
-                            int T, int t, int D) {
+                            int T, int t, int D, unsigned* __restrict__ bar, int nbar) {
+  clear_bar(bar, nbar);
   const int b = blockIdx.y, m = msz[b];
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   const int a = e / D, c = e % D;
@@ -3615,12 +3630,10 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
                            fb.S + static_cast<size_t>(kSB) * ld + kSB, sS, ld, n, fb.tv, t, t,
                            fb.part, fb.part_cap, B, st);
   prof_mark(4, true, st);
-  hipLaunchKernelGGL(k_colsum_final, dim3((t + 63) / 64, B), dim3(256), 0, st, fb.colpart,
-                     fb.cvec, tn, t);
   hipLaunchKernelGGL(k_bias_lam, dim3(B), dim3(1024), 0, st, fb.S, sS, ld, fb.lam, fb.tv, t,
-                     ridge);
+                     ridge, fb.colpart, fb.cvec, tn);
   hipLaunchKernelGGL(k_bias_prep, dim3((t + 15) / 16, B), dim3(1024), 0, st, fb.S, sS, ld, fb.cvec,
-                     fb.lam, fb.tv, t);
+                     fb.lam, fb.tv, t, fb.bar, kBarWords);
   // pivoting rounds: one launch, a team per head
   prof_mark(5, false, st);
   int cap = coop_capacity(reinterpret_cast<const void*>(&k_nnls_sweep));
@@ -3628,8 +3641,7 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
   int tx;
   const int nvb = (t + kSB - 1) / kSB;
   int grid = team_shape(B, nvb + nvb * (nvb + 1) / 2, cap, tx);
-  hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(fb.bar), 0, kBarWords, st);
-  if (e != hipSuccess) return e;
+  hipError_t e;
   int* err = reinterpret_cast<int*>(fb.bar + kBarWords - 1);
   const int32_t* tvp = fb.tv;
   {
@@ -3657,13 +3669,11 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
   launch_atb<float, false>(fb.PS, sPS, t, nullptr, 0, O, static_cast<size_t>(n) * D, D, R0, sS, ld,
                            n, fb.msz, t, D, fb.part, fb.part_cap, B, st);
   hipLaunchKernelGGL((k_rhs_ridge<In>), dim3((t * D + 255) / 256, B), dim3(256), 0, st, R0, sS,
-                     ld, V, idx, fb.Fidx, fb.msz, fb.lam, T, t, D);
+                     ld, V, idx, fb.Fidx, fb.msz, fb.lam, T, t, D, fb.bar, kBarWords);
   cap = coop_capacity(reinterpret_cast<const void*>(&k_value_sweep));
   if (cap <= 0) return hipErrorLaunchFailure;
   constexpr int nrb = rv / kSB;
   grid = team_shape(B, nvb * nrb + nvb * (nvb + 1) / 2, cap, tx);
-  e = launch_fill_i32(reinterpret_cast<int32_t*>(fb.bar), 0, kBarWords, st);
-  if (e != hipSuccess) return e;
   prof_mark(12, false, st);
   {
     int r_al = rv, Dv = D, full = fb.refine > 0 ? 1 : 0;

@@ -172,8 +172,9 @@ __global__ __launch_bounds__(256) void k_ps(const In* __restrict__ Q, const In* 
 
 // ---------------------------------------------------------------------------
 // C[b][a][c] = sum_i A[b][i][ca(a)] * Bm[b][i][c]  for a < mA_b, c < mB_b.
-// ca: optional per-head column map of A.  SYM: B = A, lower tiles only,
-// mirrored.  Each head has G workgroups.  Its split into row slices follows
+// ca: optional per-head column map of A.  SYM: B = A, lower tiles only, and
+// only the lower triangle is stored (every reader of the swept systems reads
+// the lower triangle).  Each head has G workgroups.  Its split into row slices follows
 // its own sizes (atb_shape), which only the device knows for the value fit's
 // passive set: with ks > 1 workgroup g sums slice g / nt of tile g % nt into
 // part[b][slice][tile][64*64] and k_atb_reduce adds the slices in order;
@@ -307,11 +308,9 @@ __global__ __launch_bounds__(256) void k_atb(const double* __restrict__ A, size_
     atb_decode(SYM, tile, tb, ty, tx);
     const int a0 = ty * kTile, c0 = tx * kTile;
     // this wave's quadrant: wanted unless past the sizes or (symmetric)
-    // strictly above the diagonal; off-diagonal quadrants of a symmetric
-    // product are mirrored
+    // strictly above the diagonal
     const int qa = a0 + (wave >> 1) * 32, qc = c0 + (wave & 1) * 32;
     const bool live = qa < mA && qc < mB && !(SYM && qa < qc);
-    const bool mirror = SYM && qa != qc;
     atb_tile<TB, SYM>(Ab, lda, ca, Bb, ldb, mA, mB, a0, c0, k0, k1, sAt, sBt, acc, live);
     if (!live) return;
     double* P = part + (static_cast<size_t>(b) * cap_tiles + split * sh.nt + tile) * (kTile * kTile);
@@ -325,18 +324,16 @@ __global__ __launch_bounds__(256) void k_atb(const double* __restrict__ A, size_
           const int r = a0 + rr, c = c0 + cc;
           if (!whole) {
             P[rr * kTile + cc] = acc[ra][rb][i];
-          } else if (r < mA && c < mB) {
+          } else if (r < mA && c < mB && !(SYM && r < c)) {
             Cb[static_cast<size_t>(r) * ldc + c] = acc[ra][rb][i];
-            if (mirror) Cb[static_cast<size_t>(c) * ldc + r] = acc[ra][rb][i];
           }
         }
   }
 }
 
-// Sum a head's row slices of each tile in order and store (mirrored for
-// symmetric products, whose entries above the diagonal of a diagonal tile are
-// taken from below it); nothing to do for heads computed whole.  grid
-// (tiles that may split * 16, B), block 256: one element per thread.
+// Sum a head's row slices of each tile in order and store (the lower
+// triangle of a symmetric product); nothing to do for heads computed whole.
+// grid (tiles that may split * 16, B), block 256: one element per thread.
 template <bool SYM>
 __global__ __launch_bounds__(256) void k_atb_reduce(const double* __restrict__ part,
                                                     double* __restrict__ C, size_t sC, int ldc,
@@ -358,10 +355,7 @@ __global__ __launch_bounds__(256) void k_atb_reduce(const double* __restrict__ p
   if (SYM && r < c) return;
   double v = 0.0;
   for (int sp = 0; sp < sh.ks; ++sp) v += P[static_cast<size_t>(sp) * sh.nt * kTile * kTile + e];
-  if (r < mA && c < mB) {
-    Cb[static_cast<size_t>(r) * ldc + c] = v;
-    if (SYM && r != c) Cb[static_cast<size_t>(c) * ldc + r] = v;
-  }
+  if (r < mA && c < mB) Cb[static_cast<size_t>(r) * ldc + c] = v;
 }
 
 // Block-wide sum (blockDim 256..1024), deterministic tree order.
@@ -407,21 +401,19 @@ __device__ int block_count(int v, int* sh) {
 // Bias system of head b in its sweep matrix (right-hand side in row 0,
 // variables from row 64; see the sweep engine below): the Gram M = P_S^T P_S
 // is already in the variable block.  k_bias_lam: lam_w = ridge * tr(M) / t,
-// and the scale tr(M) / t beside it for a raised ridge, and c = P_S^T 1 from
-// the partial column sums k_ps writes per 64-query tile (four threads per
-// column each add a quarter of the tiles in order, then the quarters are
-// added in order); grid (B), block 1024.  k_bias_prep then adds lam_w to the
-// diagonal, stores c + lam_w in column 0 of the variable rows and clears
-// columns 1..63 (unused right-hand-side slots), one wave per row (grid
+// and the scale tr(M) / t beside it for a raised ridge (grid (B), block
+// 1024).  k_bias_prep, one wave per row a: c_a = (P_S^T 1)_a from the
+// partial column sums k_ps writes per 64-query tile (lanes 0..3 each add a
+// quarter of the tiles in order, then the quarters are added in order; c is
+// kept for a raised ridge), lam_w added to the diagonal, c_a + lam_w stored in
+// column 0 and columns 1..63 (unused right-hand-side slots) cleared (grid
 // (ceil(t/16), B), block 1024); its threads also clear the team barrier words
 // of the pivoting launch that follows.
 __global__ __launch_bounds__(1024) void k_bias_lam(const double* __restrict__ S, size_t sS, int ld,
                                                    double* __restrict__ lam,
                                                    const int32_t* __restrict__ tv, int t_str,
-                                                   double ridge, const double* __restrict__ part,
-                                                   double* __restrict__ colsum, int nslab) {
+                                                   double ridge) {
   __shared__ double sh[16];
-  __shared__ double q4[4][256];
   const int b = blockIdx.x;
   const int t = tv ? tv[b] : t_str;
   const double* Sb = S + b * sS;
@@ -433,19 +425,6 @@ __global__ __launch_bounds__(1024) void k_bias_lam(const double* __restrict__ S,
     lam[2 * b] = ridge * tr / t;
     lam[2 * b + 1] = tr / t;
   }
-  const int qt = threadIdx.x >> 8, col = threadIdx.x & 255;
-  const int per = (nslab + 3) / 4, k0 = qt * per, k1 = min(nslab, k0 + per);
-  for (int a0 = 0; a0 < t_str; a0 += 256) {
-    const int a = a0 + col;
-    double s = 0.0;
-    if (a < t_str)
-      for (int k = k0; k < k1; ++k) s += part[(static_cast<size_t>(b) * nslab + k) * t_str + a];
-    q4[qt][col] = s;
-    __syncthreads();
-    if (qt == 0 && a < t_str)
-      colsum[static_cast<size_t>(b) * t_str + a] = ((q4[0][col] + q4[1][col]) + q4[2][col]) + q4[3][col];
-    __syncthreads();
-  }
 }
 // Every thread of the grid clears its share of the nbar team barrier words.
 __device__ __forceinline__ void clear_bar(unsigned* __restrict__ bar, int nbar) {
@@ -456,7 +435,8 @@ __device__ __forceinline__ void clear_bar(unsigned* __restrict__ bar, int nbar) 
     bar[i] = 0u;
 }
 __global__ __launch_bounds__(1024) void k_bias_prep(double* __restrict__ S, size_t sS, int ld,
-                                                    const double* __restrict__ colsum,
+                                                    const double* __restrict__ part, int nslab,
+                                                    double* __restrict__ colsum,
                                                     const double* __restrict__ lam,
                                                     const int32_t* __restrict__ tv, int t_str,
                                                     unsigned* __restrict__ bar, int nbar) {
@@ -466,8 +446,15 @@ __global__ __launch_bounds__(1024) void k_bias_prep(double* __restrict__ S, size
   const double lw = lam[2 * b];
   const int lane = threadIdx.x & 63, a = blockIdx.x * 16 + (threadIdx.x >> 6);
   if (a >= t) return;
+  const int per = (nslab + 3) / 4, k0 = min(nslab, lane * per), k1 = min(nslab, k0 + per);
+  double qs = 0.0;
+  if (lane < 4)
+    for (int k = k0; k < k1; ++k) qs += part[(static_cast<size_t>(b) * nslab + k) * t_str + a];
+  const double q1 = __shfl(qs, 1), q2 = __shfl(qs, 2), q3 = __shfl(qs, 3);
+  const double c = ((qs + q1) + q2) + q3;  // lane 0's value is the one used
+  if (lane == 0) colsum[static_cast<size_t>(b) * t_str + a] = c;
   double* row = S + b * sS + static_cast<size_t>(kSB + a) * ld;
-  row[lane] = lane == 0 ? colsum[static_cast<size_t>(b) * t_str + a] + lw : 0.0;
+  row[lane] = lane == 0 ? c + lw : 0.0;
   if (lane == 0) row[kSB + a] += lw;
 }
 
@@ -3318,36 +3305,31 @@ __global__ __launch_bounds__(256) void k_value_sweep(
 // r_i = sum_a P_S[i][a] w'_a, X = P_S diag(w') / r, w' = max(w, 1e-30); the
 // passive columns X_F are written compacted to the front of each row (column
 // inv[a] for passive a; the row stride stays t), so the value system's
-// products read them contiguously.  The whole row is read before any of it
-// is written (block_sum's barrier), which makes the in-place rewrite safe.
-// grid (n, B), block 256.
+// products read them contiguously.  One wave per row: it sums the row (lane
+// partials, then a butterfly), then reads it again and writes the passive
+// entries.  The rewrite is in place and safe: passive a goes to slot
+// inv[a] <= a, and the wave reads positions [a0, a0 + 64) of a pass before it
+// writes any slot of that pass (all below a0 + 64), so no position is read
+// after it has been written.  grid (ceil(n/4), B), block 256.
 __global__ __launch_bounds__(256) void k_value_prep(double* __restrict__ PS,
                                                     const double* __restrict__ wv,
                                                     const int32_t* __restrict__ inv, int n,
                                                     int t) {
-  constexpr int NV = kMaxTeamT / 256;
-  __shared__ double sh[16];
-  const int b = blockIdx.y, i = blockIdx.x;
+  const int b = blockIdx.y, i = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (i >= n) return;
   double* row = PS + (static_cast<size_t>(b) * n + i) * t;
   const double* w = wv + static_cast<size_t>(b) * t;
   const int32_t* ib = inv + static_cast<size_t>(b) * t;
-  double v[NV];
   double s = 0.0;
+  for (int a = lane; a < t; a += 64) s += row[a] * fmax(w[a], 1e-30);
 #pragma unroll
-  for (int q = 0; q < NV; ++q) {
-    const int a = threadIdx.x + q * 256;
-    v[q] = a < t ? row[a] * fmax(w[a], 1e-30) : 0.0;
-    s += v[q];
-  }
-  s = block_sum(s, sh);
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
   const double rs = 1.0 / s;
-#pragma unroll
-  for (int q = 0; q < NV; ++q) {
-    const int a = threadIdx.x + q * 256;
-    if (a < t) {
-      const int slot = ib[a];
-      if (slot >= 0) row[slot] = v[q] * rs;
-    }
+  for (int a0 = 0; a0 < t; a0 += 64) {
+    const int a = a0 + lane;
+    const double v = a < t ? row[a] * fmax(w[a], 1e-30) : 0.0;
+    const int slot = a < t ? ib[a] : -1;
+    if (slot >= 0) row[slot] = v * rs;
   }
 }
 
@@ -3631,9 +3613,9 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
                            fb.part, fb.part_cap, B, st);
   prof_mark(4, true, st);
   hipLaunchKernelGGL(k_bias_lam, dim3(B), dim3(1024), 0, st, fb.S, sS, ld, fb.lam, fb.tv, t,
-                     ridge, fb.colpart, fb.cvec, tn);
-  hipLaunchKernelGGL(k_bias_prep, dim3((t + 15) / 16, B), dim3(1024), 0, st, fb.S, sS, ld, fb.cvec,
-                     fb.lam, fb.tv, t, fb.bar, kBarWords);
+                     ridge);
+  hipLaunchKernelGGL(k_bias_prep, dim3((t + 15) / 16, B), dim3(1024), 0, st, fb.S, sS, ld,
+                     fb.colpart, tn, fb.cvec, fb.lam, fb.tv, t, fb.bar, kBarWords);
   // pivoting rounds: one launch, a team per head
   prof_mark(5, false, st);
   int cap = coop_capacity(reinterpret_cast<const void*>(&k_nnls_sweep));
@@ -3658,7 +3640,8 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
   prof_mark(5, true, st);
   // value fit on the passive set: G = X_F^T X_F + lam_v I, R = X_F^T O + lam_v V_F
   prof_mark(6, false, st);
-  hipLaunchKernelGGL(k_value_prep, dim3(n, B), dim3(256), 0, st, fb.PS, fb.wv, fb.inv, n, t);
+  hipLaunchKernelGGL(k_value_prep, dim3((n + 3) / 4, B), dim3(256), 0, st, fb.PS, fb.wv, fb.inv, n,
+                     t);
   double* G0 = fb.S + static_cast<size_t>(rv) * ld + rv;
   double* R0 = fb.S + static_cast<size_t>(rv) * ld;
   prof_mark(11, false, st);

@@ -300,8 +300,9 @@ def main():
     #                  the compaction: four launches), algorithmically one read of
     #                  imp and the idx write: 4 T B + 4 t B
     #   k_gather_rows  reads and writes the kept K rows: 2 t d es B
-    #   Grams          n t^2 per entry, t its fitted keys (symmetric half; value Gram:
-    #                  n m^2, m passive)
+    #   Grams          n t^2 per entry, t its fitted keys (symmetric half); the value
+    #                  system's Gram and right-hand side in one launch: n (m^2 + m d),
+    #                  m passive
     #   k_nnls_sweep   the block sweeps of the pivoting rounds (counted on device)
     #   k_value_sweep  the value system's block sweeps (counted on device)
     work = {"score_lse": ("k_score_lse", 2.0 * n * Te * d * Be, mm_peak, "mfma"),
@@ -310,7 +311,8 @@ def main():
             "topt": ("k_sel_* (refine x2, count, compact)", 4.0 * (Te + te) * Be, PEAK_HBM_GBS, "hbm"),
             "gather": ("k_gather_rows", 2.0 * te * d * es * Be, PEAK_HBM_GBS, "hbm"),
             "gram": ("k_atb (mass Gram)", float(n * (t_fit ** 2).sum()), PEAK_F64_TFLOPS, "mfma"),
-            "value_gram": ("k_atb (value Gram)", float(n * (m_pass.astype(float) ** 2).sum()),
+            "value_gram": ("k_atb2 (value Gram + X_F^T O)",
+                           float(n * (m_pass.astype(float) ** 2 + m_pass.astype(float) * d).sum()),
                            PEAK_F64_TFLOPS, "mfma"),
             "nnls": ("k_nnls_sweep", float(fit_flops[0]), PEAK_F64_TFLOPS, "mfma"),
             "value_sweep": ("k_value_sweep", float(fit_flops[1]), PEAK_F64_TFLOPS, "mfma")}

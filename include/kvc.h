@@ -319,7 +319,8 @@ int kvc_workspace_layout(const kvc_params_t* p, kvc_ws_layout_t* out);
 #define KVC_STAGE_IMP_REDUCE  8  /* importance partials summed per key            */
 #define KVC_STAGE_TOPT        9  /* the top-t select kernel alone                 */
 #define KVC_STAGE_GATHER     10  /* kept-key row gather alone                     */
-#define KVC_STAGE_VALUE_GRAM 11  /* value Gram X_F^T X_F alone (fp64 MFMA)        */
+#define KVC_STAGE_VALUE_GRAM 11  /* value Gram and right-hand side X_F^T [X_F O]
+                                      in one launch (fp64 MFMA)                  */
 #define KVC_STAGE_VALUE_SWEEP 12 /* value system solve alone                      */
 #define KVC_NUM_STAGES       13
 int kvc_profile_enable(uint32_t stage_mask);

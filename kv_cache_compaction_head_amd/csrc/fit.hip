@@ -274,88 +274,127 @@ __device__ __forceinline__ void atb_tile(const double* __restrict__ Ab, int lda,
   else chunks(std::false_type{});
 }
 
+// One product of a launch: C = A^T B over heads (see k_atb).
+template <class TB>
+struct AtbArgs {
+  const double* A;
+  size_t sA;
+  int lda;
+  const int32_t* colA;
+  size_t sColA;
+  const TB* Bm;
+  size_t sB;
+  int ldb;
+  double* C;
+  size_t sC;
+  int ldc, nrows;
+  const int32_t* msz;
+  int mA_const, mB_const;
+  double* part;
+  int G, cap_tiles;
+};
+
+// Workgroup bid (< B G) of product p.
 template <class TB, bool SYM>
-__global__ __launch_bounds__(256) void k_atb(const double* __restrict__ A, size_t sA, int lda,
-                                             const int32_t* __restrict__ colA, size_t sColA,
-                                             const TB* __restrict__ Bm, size_t sB, int ldb,
-                                             double* __restrict__ C, size_t sC, int ldc,
-                                             int nrows, const int32_t* __restrict__ msz,
-                                             int mA_const, int mB_const,
-                                             double* __restrict__ part, int G, int cap_tiles) {
-  __shared__ double sAt[kKC * kTile], sBt[kKC * kTile];
-  const int b = blockIdx.x / G, g = blockIdx.x % G;
-  const int mA = msz ? msz[b] : mA_const;
-  const int mB = SYM ? mA : mB_const;
-  const AtbShape sh = atb_shape(mA, mB, SYM, G, cap_tiles, nrows, gridDim.x / G);
+__device__ __forceinline__ void atb_block(const AtbArgs<TB>& p, int B, int bid, double* sAt,
+                                          double* sBt) {
+  const int G = p.G, b = bid / G, g = bid % G;
+  const int mA = p.msz ? p.msz[b] : p.mA_const;
+  const int mB = SYM ? mA : p.mB_const;
+  const AtbShape sh = atb_shape(mA, mB, SYM, G, p.cap_tiles, p.nrows, B);
   if (g >= sh.nt * sh.ks && sh.ks > 1) return;
   const int tb = (mB + kTile - 1) / kTile;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
-  const double* Ab = A + b * sA;
-  const TB* Bb = Bm + b * sB;
-  const int32_t* ca = colA ? colA + b * sColA : nullptr;
+  const double* Ab = p.A + b * p.sA;
+  const TB* Bb = p.Bm + b * p.sB;
+  const int32_t* ca = p.colA ? p.colA + b * p.sColA : nullptr;
   // ks = 1: tile g over all rows, into C; else tile g % nt over row slice
   // g / nt, into the partials (G is at least the tile count of every head)
   const bool whole = sh.ks == 1;
   const int split = whole ? 0 : g / sh.nt, tile = whole ? g : g % sh.nt;
   if (tile >= sh.nt) return;
   const int k0 = whole ? 0 : split * sh.per * kKC;
-  const int k1 = whole ? nrows : min(nrows, (split + 1) * sh.per * kKC);
-  double* Cb = C + b * sC;
+  const int k1 = whole ? p.nrows : min(p.nrows, (split + 1) * sh.per * kKC);
+  double* Cb = p.C + b * p.sC;
   f64x4 acc[2][2];
-  {
-    int ty, tx;
-    atb_decode(SYM, tile, tb, ty, tx);
-    const int a0 = ty * kTile, c0 = tx * kTile;
-    // this wave's quadrant: wanted unless past the sizes or (symmetric)
-    // strictly above the diagonal
-    const int qa = a0 + (wave >> 1) * 32, qc = c0 + (wave & 1) * 32;
-    const bool live = qa < mA && qc < mB && !(SYM && qa < qc);
-    atb_tile<TB, SYM>(Ab, lda, ca, Bb, ldb, mA, mB, a0, c0, k0, k1, sAt, sBt, acc, live);
-    if (!live) return;
-    double* P = part + (static_cast<size_t>(b) * cap_tiles + split * sh.nt + tile) * (kTile * kTile);
+  int ty, tx;
+  atb_decode(SYM, tile, tb, ty, tx);
+  const int a0 = ty * kTile, c0 = tx * kTile;
+  // this wave's quadrant: wanted unless past the sizes or (symmetric)
+  // strictly above the diagonal
+  const int qa = a0 + (wave >> 1) * 32, qc = c0 + (wave & 1) * 32;
+  const bool live = qa < mA && qc < mB && !(SYM && qa < qc);
+  atb_tile<TB, SYM>(Ab, p.lda, ca, Bb, p.ldb, mA, mB, a0, c0, k0, k1, sAt, sBt, acc, live);
+  if (!live) return;
+  double* P =
+      p.part + (static_cast<size_t>(b) * p.cap_tiles + split * sh.nt + tile) * (kTile * kTile);
 #pragma unroll
-    for (int ra = 0; ra < 2; ++ra)
+  for (int ra = 0; ra < 2; ++ra)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = tile_row(wave, lane, ra, i), cc = tile_col(wave, lane, rb);
-          const int r = a0 + rr, c = c0 + cc;
-          if (!whole) {
-            P[rr * kTile + cc] = acc[ra][rb][i];
-          } else if (r < mA && c < mB && !(SYM && r < c)) {
-            Cb[static_cast<size_t>(r) * ldc + c] = acc[ra][rb][i];
-          }
+      for (int i = 0; i < 4; ++i) {
+        const int rr = tile_row(wave, lane, ra, i), cc = tile_col(wave, lane, rb);
+        const int r = a0 + rr, c = c0 + cc;
+        if (!whole) {
+          P[rr * kTile + cc] = acc[ra][rb][i];
+        } else if (r < mA && c < mB && !(SYM && r < c)) {
+          Cb[static_cast<size_t>(r) * p.ldc + c] = acc[ra][rb][i];
         }
-  }
+      }
+}
+
+template <class TB, bool SYM>
+__global__ __launch_bounds__(256) void k_atb(AtbArgs<TB> p, int B) {
+  __shared__ double sAt[kKC * kTile], sBt[kKC * kTile];
+  atb_block<TB, SYM>(p, B, blockIdx.x, sAt, sBt);
+}
+
+// Two independent products in one launch (the value system's Gram and its
+// right-hand side): the first B G1 workgroups take the first, the rest the
+// second, so neither launch's tail waits on its own.
+template <class TB1, bool S1, class TB2, bool S2>
+__global__ __launch_bounds__(256) void k_atb2(AtbArgs<TB1> p1, AtbArgs<TB2> p2, int B) {
+  __shared__ double sAt[kKC * kTile], sBt[kKC * kTile];
+  const int n1 = B * p1.G;
+  if (static_cast<int>(blockIdx.x) < n1) atb_block<TB1, S1>(p1, B, blockIdx.x, sAt, sBt);
+  else atb_block<TB2, S2>(p2, B, blockIdx.x - n1, sAt, sBt);
 }
 
 // Sum a head's row slices of each tile in order and store (the lower
 // triangle of a symmetric product); nothing to do for heads computed whole.
 // grid (tiles that may split * 16, B), block 256: one element per thread.
-template <bool SYM>
-__global__ __launch_bounds__(256) void k_atb_reduce(const double* __restrict__ part,
-                                                    double* __restrict__ C, size_t sC, int ldc,
-                                                    const int32_t* __restrict__ msz, int mA_const,
-                                                    int mB_const, int nrows, int G,
-                                                    int cap_tiles) {
-  const int b = blockIdx.y, tile = blockIdx.x >> 4;
-  const int mA = msz ? msz[b] : mA_const;
-  const int mB = SYM ? mA : mB_const;
-  const AtbShape sh = atb_shape(mA, mB, SYM, G, cap_tiles, nrows, gridDim.y);
+template <class TB, bool SYM>
+__device__ __forceinline__ void atb_reduce_block(const AtbArgs<TB>& p, int B, int b, int bx) {
+  const int tile = bx >> 4;
+  const int mA = p.msz ? p.msz[b] : p.mA_const;
+  const int mB = SYM ? mA : p.mB_const;
+  const AtbShape sh = atb_shape(mA, mB, SYM, p.G, p.cap_tiles, p.nrows, B);
   if (sh.ks == 1 || tile >= sh.nt) return;
   int ty, tx;
   atb_decode(SYM, tile, (mB + kTile - 1) / kTile, ty, tx);
   const int a0 = ty * kTile, c0 = tx * kTile;
-  double* Cb = C + b * sC;
-  const double* P = part + (static_cast<size_t>(b) * cap_tiles + tile) * (kTile * kTile);
-  const int e = (blockIdx.x & 15) * 256 + threadIdx.x;
+  double* Cb = p.C + b * p.sC;
+  const double* P = p.part + (static_cast<size_t>(b) * p.cap_tiles + tile) * (kTile * kTile);
+  const int e = (bx & 15) * 256 + threadIdx.x;
   const int r = a0 + e / kTile, c = c0 + e % kTile;
   if (SYM && r < c) return;
   double v = 0.0;
   for (int sp = 0; sp < sh.ks; ++sp) v += P[static_cast<size_t>(sp) * sh.nt * kTile * kTile + e];
-  if (r < mA && c < mB) Cb[static_cast<size_t>(r) * ldc + c] = v;
+  if (r < mA && c < mB) Cb[static_cast<size_t>(r) * p.ldc + c] = v;
+}
+
+template <class TB, bool SYM>
+__global__ __launch_bounds__(256) void k_atb_reduce(AtbArgs<TB> p) {
+  atb_reduce_block<TB, SYM>(p, gridDim.y, blockIdx.y, blockIdx.x);
+}
+
+// The reductions of k_atb2's two products: x blocks [0, r1) the first.
+template <class TB1, bool S1, class TB2, bool S2>
+__global__ __launch_bounds__(256) void k_atb_reduce2(AtbArgs<TB1> p1, AtbArgs<TB2> p2, int r1) {
+  if (static_cast<int>(blockIdx.x) < r1) atb_reduce_block<TB1, S1>(p1, gridDim.y, blockIdx.y, blockIdx.x);
+  else atb_reduce_block<TB2, S2>(p2, gridDim.y, blockIdx.y, blockIdx.x - r1);
 }
 
 // Block-wide sum (blockDim 256..1024), deterministic tree order.
@@ -3554,17 +3593,16 @@ static int team_shape(int B, int tiles, int cap, int& tx) {
   return g * nteams;
 }
 
-// A^T B over heads: G workgroups a head (~2048 in all, at least one a tile
-// of the largest product); each head's split-K follows its own sizes.
+// A^T B over heads: G workgroups a head (~`target` in all, at least one a
+// tile of the largest product); each head's split-K follows its own sizes.
 template <class TB, bool SYM>
-static void launch_atb(const double* A, size_t sA, int lda, const int32_t* colA, size_t sColA,
-                       const TB* Bm, size_t sB, int ldb, double* C, size_t sC, int ldc, int nrows,
-                       const int32_t* msz, int mA, int mB, double* part, size_t part_cap, int B,
-                       hipStream_t st) {
+static AtbArgs<TB> atb_args(const double* A, size_t sA, int lda, const int32_t* colA,
+                            size_t sColA, const TB* Bm, size_t sB, int ldb, double* C, size_t sC,
+                            int ldc, int nrows, const int32_t* msz, int mA, int mB, double* part,
+                            size_t part_cap, int B, int target) {
   const int ta = (mA + kTile - 1) / kTile, tb = (mB + kTile - 1) / kTile;
   const int ntiles = SYM ? ta * (ta + 1) / 2 : ta * tb;
-  if (ntiles == 0 || B == 0) return;
-  int G = (kAtbGrid + B - 1) / B;
+  int G = (target + B - 1) / B;
   if (G > 16 * ntiles) G = 16 * ntiles;
   if (G < ntiles) G = ntiles;
   // odd, so that consecutive heads start on different XCDs (workgroups go
@@ -3572,17 +3610,50 @@ static void launch_atb(const double* A, size_t sA, int lda, const int32_t* colA,
   G |= 1;
   const size_t ct = part_cap / (static_cast<size_t>(B) * kTile * kTile);
   const int cap_tiles = ct > (1u << 20) ? (1 << 20) : static_cast<int>(ct);
-  hipLaunchKernelGGL((k_atb<TB, SYM>), dim3(B * G), dim3(256), 0, st, A, sA, lda, colA, sColA, Bm,
-                     sB, ldb, C, sC, ldc, nrows, msz, mA, mB, part, G, cap_tiles);
-  // sizes known here (no per-head column count): skip the reduction when no
+  return AtbArgs<TB>{A,  sA,  lda,   colA,  sColA, Bm, sB, ldb, C,        sC,
+                     ldc, nrows, msz, mA, mB,   part, G,  cap_tiles};
+}
+
+// x blocks of the product's split-K reduction (0: no head splits).
+template <class TB, bool SYM>
+static int atb_reduce_x(const AtbArgs<TB>& p, int B) {
+  const int ta = (p.mA_const + kTile - 1) / kTile, tb = (p.mB_const + kTile - 1) / kTile;
+  const int ntiles = SYM ? ta * (ta + 1) / 2 : ta * tb;
+  if (ntiles == 0 || B == 0) return 0;
+  // sizes known here (no per-head column count): nothing to reduce when no
   // head splits
-  if (!msz && atb_shape(mA, mB, SYM, G, cap_tiles, nrows, B).ks == 1) return;
+  if (!p.msz && atb_shape(p.mA_const, p.mB_const, SYM, p.G, p.cap_tiles, p.nrows, B).ks == 1)
+    return 0;
   // a head splits only with fewer than kAtbGrid / (2 B) tiles
   int rt = kAtbGrid / (2 * B);
   if (rt > ntiles) rt = ntiles;
-  if (rt < 1) return;
-  hipLaunchKernelGGL((k_atb_reduce<SYM>), dim3(rt * 16, B), dim3(256), 0, st, part, C, sC, ldc,
-                     msz, mA, mB, nrows, G, cap_tiles);
+  return rt < 1 ? 0 : rt * 16;
+}
+
+template <class TB, bool SYM>
+static void launch_atb(const double* A, size_t sA, int lda, const int32_t* colA, size_t sColA,
+                       const TB* Bm, size_t sB, int ldb, double* C, size_t sC, int ldc, int nrows,
+                       const int32_t* msz, int mA, int mB, double* part, size_t part_cap, int B,
+                       hipStream_t st) {
+  const int ta = (mA + kTile - 1) / kTile, tb = (mB + kTile - 1) / kTile;
+  if ((SYM ? ta * (ta + 1) / 2 : ta * tb) == 0 || B == 0) return;
+  const AtbArgs<TB> p = atb_args<TB, SYM>(A, sA, lda, colA, sColA, Bm, sB, ldb, C, sC, ldc, nrows,
+                                          msz, mA, mB, part, part_cap, B, kAtbGrid);
+  hipLaunchKernelGGL((k_atb<TB, SYM>), dim3(B * p.G), dim3(256), 0, st, p, B);
+  const int rx = atb_reduce_x<TB, SYM>(p, B);
+  if (rx > 0) hipLaunchKernelGGL((k_atb_reduce<TB, SYM>), dim3(rx, B), dim3(256), 0, st, p);
+}
+
+// Two products in one launch (and one reduction launch), each aiming at half
+// the usual grid and taking half of the partials buffer.
+template <class TB1, bool S1, class TB2, bool S2>
+static void launch_atb2(const AtbArgs<TB1>& p1, const AtbArgs<TB2>& p2, int B, hipStream_t st) {
+  hipLaunchKernelGGL((k_atb2<TB1, S1, TB2, S2>), dim3(B * (p1.G + p2.G)), dim3(256), 0, st, p1,
+                     p2, B);
+  const int r1 = atb_reduce_x<TB1, S1>(p1, B), r2 = atb_reduce_x<TB2, S2>(p2, B);
+  if (r1 + r2 > 0)
+    hipLaunchKernelGGL((k_atb_reduce2<TB1, S1, TB2, S2>), dim3(r1 + r2, B), dim3(256), 0, st, p1,
+                       p2, r1);
 }
 
 int sweep_ld(int t, int D) {
@@ -3645,12 +3716,19 @@ hipError_t launch_fit(const void* Qv, const void* Kv, const void* Vv, const doub
   double* G0 = fb.S + static_cast<size_t>(rv) * ld + rv;
   double* R0 = fb.S + static_cast<size_t>(rv) * ld;
   prof_mark(11, false, st);
-  launch_atb<double, true>(fb.PS, sPS, t, nullptr, 0, fb.PS, sPS, t, G0, sS, ld, n, fb.msz, t, t,
-                           fb.part, fb.part_cap, B, st);
+  {
+    // G = X_F^T X_F and X_F^T O side by side
+    const size_t half = fb.part_cap / 2;
+    const AtbArgs<double> pg = atb_args<double, true>(fb.PS, sPS, t, nullptr, 0, fb.PS, sPS, t, G0,
+                                                      sS, ld, n, fb.msz, t, t, fb.part, half, B,
+                                                      kAtbGrid / 2);
+    const AtbArgs<float> pr = atb_args<float, false>(
+        fb.PS, sPS, t, nullptr, 0, O, static_cast<size_t>(n) * D, D, R0, sS, ld, n, fb.msz, t, D,
+        fb.part + half, half, B, kAtbGrid / 2);
+    launch_atb2<double, true, float, false>(pg, pr, B, st);
+  }
   prof_mark(11, true, st);
   hipLaunchKernelGGL(k_ridge_v, dim3(B), dim3(256), 0, st, G0, sS, ld, fb.msz, fb.lam, fb.tv, t);
-  launch_atb<float, false>(fb.PS, sPS, t, nullptr, 0, O, static_cast<size_t>(n) * D, D, R0, sS, ld,
-                           n, fb.msz, t, D, fb.part, fb.part_cap, B, st);
   hipLaunchKernelGGL((k_rhs_ridge<In>), dim3((t * D + 255) / 256, B), dim3(256), 0, st, R0, sS,
                      ld, V, idx, fb.Fidx, fb.msz, fb.lam, T, t, D, fb.bar, kBarWords);
   cap = coop_capacity(reinterpret_cast<const void*>(&k_value_sweep));

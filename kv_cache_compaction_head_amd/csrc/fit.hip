@@ -767,6 +767,9 @@ struct __align__(16) SweepSmem {
   int piv[kSB];                    // matrix row of pivot q
   double sgn2[kSB];                // the next step's pivots (lookahead)
   int piv2[kSB];
+  double u0[kSB];                  // one right-hand side: A[0, P] before the step
+  double w0d[kSB];                 // ... its W row times 1/D
+  double v0[kSB];                  // ... and its V row
   int16_t list[kMaxTeamT];         // NNLS: variables exchanged this round
   int16_t pos[kMaxRows];           // matrix row -> pivot slot, -1 if not a pivot
   uint8_t inF[kMaxTeamT];   // NNLS: passive set
@@ -2675,6 +2678,50 @@ struct TileWalk {
 // two pivot sets are disjoint), factors it and publishes L^-1 and 1/D in
 // M.stage, which the next step loads instead of factoring (pre = true); the
 // members that build bands and tiles form B from them.
+// One right-hand side (the bias system): its column is updated outside the
+// tile tasks.  Every member forms the right-hand-side row's W and V from
+// U_0 = A[0, P] (gathered before the step's first barrier, so before any
+// member writes column 0) and the step's factors, then updates column 0 of
+// the rows of its own half bands (the ones whose W rows it staged): a pivot
+// row takes s_q V_0q, any other row A_r0 - W_r D^-1 W_0^T, eight lanes a row,
+// each over eight pivots, added by a fixed butterfly.
+__device__ __forceinline__ void rhs_col0(const SweepMat& M, int k, int first, int nhalf,
+                                         int stride) {
+  SweepSmem& sm = g_sw;
+  const int tid = threadIdx.x;
+  __syncthreads();
+  if (tid < kSB) {
+    double w = 0.0, v = 0.0;
+    for (int q = 0; q < k; ++q) {
+      const double u = sm.u0[q];
+      w = fma(u, sm.li[tid][q], w);
+      v = fma(u, sm.pp[q][tid], v);
+    }
+    sm.w0d[tid] = tid < k ? w * sm.rD[tid] : 0.0;
+    sm.v0[tid] = v;
+  }
+  __syncthreads();
+  const int part = tid & 7;
+  for (int bi = first; bi < nhalf; bi += stride) {
+    const int r = M.r_al + 32 * bi + (tid >> 3);
+    const bool act = r < M.r_al + M.n_var;
+    const int q = act ? sm.pos[r] : -1;
+    double d = 0.0;
+    if (act && q < 0) {
+      const gdouble* wr = M.U + static_cast<size_t>(r) * kSB + 8 * part;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) d = fma(wr[i], sm.w0d[8 * part + i], d);
+    }
+    d += __shfl_xor(d, 1);
+    d += __shfl_xor(d, 2);
+    d += __shfl_xor(d, 4);
+    if (act && part == 0) {
+      gdouble* a0 = M.S + static_cast<size_t>(r) * M.ld;
+      *a0 = q >= 0 ? sm.sgn[q] * sm.v0[q] : *a0 - d;
+    }
+  }
+}
+
 // Returns whether a pivot of this step had the wrong sign (a lookahead
 // member flags its own into *status).
 __device__ __forceinline__ bool sweep_step(const SweepMat& M, Team& tm, int k, int skip_below,
@@ -2711,15 +2758,32 @@ __device__ __forceinline__ bool sweep_step(const SweepMat& M, Team& tm, int k, i
   const int nrb = (M.n_rhs + kSB - 1) / kSB, nvb = (M.n_var + kSB - 1) / kSB;
   const int vb0 = M.r_al / kSB;
   const int vmembers = la ? tsize - 1 : tsize;
+  // One right-hand side (the bias system): its column can be updated by
+  // rhs_col0 instead of by tile tasks, and then each diagonal tile taken as
+  // one task.  Used when that lets every tile task of the step go to a wave
+  // of its own and the usual split (right-hand-side tasks, half tiles) does
+  // not: the step then waits for one task per wave instead of two.
+  bool fused = false;
+  if (M.r_al == kSB && M.n_rhs == 1 && c0 == 0 && skip_below == 0 && tsize > 1) {
+    const int tv = nvb * (nvb + 1) / 2, nwv = vmembers * (kTeamThreads / 64);
+    const int tu = tv + nvb, pu = 2 * tu <= nwv ? 4 : (tu < nwv ? 2 : 1);
+    const bool half = 2 * tv > nwv && tv < nwv;
+    fused = half && 2 * tv - nvb <= nwv && nvb + tv * pu > nwv;
+  }
+  double u0r = 0.0;  // A[0, P] for rhs_col0, gathered before any column-0 write
+  if (fused && !me_la && tid < k) u0r = M.S[static_cast<size_t>(sm.piv[tid]) * M.ld];
   // B (for V = U B and the pivot block) only where the bands and tiles are
   // built: the lookahead member needs L^-1 and D alone
   if (!me_la) small_b(k);
   if (!me_la) {
-    // (the bands of the right-hand sides and of variable bands c0 on)
-    for (int bi = trank; bi < 2 * (nrb + nvb - c0); bi += vmembers) {
+    // (the bands of the right-hand sides and of variable bands c0 on; with
+    // one right-hand side, the variable bands alone)
+    const int rb0 = fused ? 0 : nrb;
+    for (int bi = trank; bi < 2 * (rb0 + nvb - c0); bi += vmembers) {
       const int b = bi >> 1;
-      v_band(M, b < nrb ? b : vb0 + c0 + b - nrb, bi & 1, k);
+      v_band(M, b < rb0 ? b : vb0 + c0 + b - rb0, bi & 1, k);
     }
+    if (fused && tid < kSB) sm.u0[tid] = u0r;
   } else {
     // the next pivot block after this step's update, A' = A[P', P'] -
     // W' D^-1 W'^T with W' = A[P', P] L^-T, taken from S before any member
@@ -2808,16 +2872,24 @@ __device__ __forceinline__ bool sweep_step(const SweepMat& M, Team& tm, int k, i
         }
   }
   int total = 0;
-  for (int iv = c0; iv < nvb; ++iv) total += nrb + (iv >= skip_below ? iv + 1 - c0 : 0);
+  for (int iv = c0; iv < nvb; ++iv)
+    total += (fused ? 0 : nrb) + (iv >= skip_below ? iv + 1 - c0 : 0);
   const int workers = la ? tsize - 1 : tsize;
   const int nw = workers * (kTeamThreads / 64);
   const int parts = 2 * total <= nw ? 4 : (total < nw ? 2 : 1);
-  // With at most 16 right-hand sides (the bias system has one), a
+  // With at most 16 right-hand sides (and not one alone, see rhs_col0), a
   // right-hand-side tile is one task over its first 16 columns (the others
   // are inactive: zero and never updated), ahead of the variable tiles.
-  const bool narrow = nrb == 1 && M.n_rhs <= 16;
+  const bool narrow = !fused && nrb == 1 && M.n_rhs <= 16;
   const int rtasks = narrow ? nvb : 0;
-  const int tasks = narrow ? rtasks + (total - nvb) * parts : total * parts;
+  // With one right-hand side and half tiles, a diagonal tile is one task (its
+  // lower ten 16 x 16 blocks; as two halves it was three and seven blocks,
+  // each half paying a task's loads and stores): band iv has tasks
+  // iv^2 .. iv^2 + 2 iv, the last its diagonal tile.
+  const bool dsingle = fused && parts == 2;
+  const int tasks = narrow    ? rtasks + (total - nvb) * parts
+                    : dsingle ? 2 * total - nvb
+                              : total * parts;
   const int nch = (k + 7) / 8;  // contraction chunks of 8 that hold pivots
   if (me_la) {
     // the lookahead member arrived at the first barrier after its gathers;
@@ -2863,9 +2935,16 @@ __device__ __forceinline__ bool sweep_step(const SweepMat& M, Team& tm, int k, i
         const int a = static_cast<int>(tk - base);
         if (a < rtasks) {
           wave_tile<4, 1>(M, vb0 + a, 0, 0, 0, nch);
+        } else if (dsingle) {
+          int iv = static_cast<int>(sqrtf(static_cast<float>(a)));
+          while (iv * iv > a) --iv;
+          while ((iv + 1) * (iv + 1) <= a) ++iv;
+          const int r = a - iv * iv;
+          if (r == 2 * iv) wave_tile<4, 4>(M, vb0 + iv, vb0 + iv, 0, 0, nch);
+          else wave_tile<2, 4>(M, vb0 + iv, vb0 + (r >> 1), 2 * (r & 1), 0, nch);
         } else {
           const int av = a - rtasks, part = av % parts;
-          TileWalk w{0, 0, narrow ? 0 : nrb, skip_below, vb0, c0};
+          TileWalk w{0, 0, (narrow || fused) ? 0 : nrb, skip_below, vb0, c0};
           w.seek(av / parts);
           if (parts == 1) wave_tile<4, 4>(M, w.I(), w.J(), 0, 0, nch);
           else if (parts == 2) wave_tile<2, 4>(M, w.I(), w.J(), 2 * part, 0, nch);
@@ -2874,6 +2953,7 @@ __device__ __forceinline__ bool sweep_step(const SweepMat& M, Team& tm, int k, i
       }
       tk = ticket_value(pend);
     }
+    if (fused) rhs_col0(M, k, trank, 2 * nvb, vmembers);
   }
   tm.tbase += tasks + nw;
   // A tile worker arrives at the closing barrier as soon as its tiles are

@@ -150,6 +150,23 @@ def test_value_elimination_on_one_workgroup_teams(seed, T, n, d, t, keys):
                                   for k, v in err.items()}, flush=True)
 
 
+@pytest.mark.parametrize("seed,T,n,t,keys", [(62, 4096, 1024, 680, "clusters"),
+                                              (63, 3000, 900, 650, "sinks")])
+def test_bias_sweep_rhs_column_outside_the_tiles(seed, T, n, t, keys):
+    """Eleven variable bands (t in 641..704) on teams of 32 workgroups (two
+    heads): the bias sweep updates its one right-hand-side column after the
+    tile tasks and takes each diagonal tile as one task, so every task has a
+    wave of its own.  Every head against the oracle."""
+    w = synth.custom(seed, 2, T, n, 128, t, "bf16", keys)
+    data = synth.batch(w)
+    gpu = run_gpu(w, data)
+    assert (gpu["status"] == 0).all(), gpu["status"]
+    for h in range(w.B):
+        err = compare_head(gpu, h, data, w.t, _tol(w))
+        print(f"rhs-column head {h}:", {k: (float(f"{v:.3g}") if isinstance(v, float) else v)
+                                        for k, v in err.items()}, flush=True)
+
+
 def _chunk_view(w, data, gpu_res, C):
     """Recast a chunked result as B*C independent heads (entry h*C + c is chunk c
     of head h, with chunk-local indices) so each entry compares against the
@@ -242,7 +259,10 @@ def test_chunked_long_context_sampled():
 @pytest.mark.parametrize("w,budgets", [
     (synth.custom(15, 4, 2000, 160, 128, 0, "bf16", "clusters"), [40, 131, 1, 64]),
     (synth.custom(16, 3, 900, 96, 64, 0, "f32", "normal"), [200, 65, 128]),
-], ids=["bf16", "f32_d64"])
+    # one head with eleven variable bands (its right-hand-side column updated
+    # outside the tile tasks), one with ten (the usual split)
+    (synth.custom(17, 2, 3000, 1024, 128, 0, "bf16", "clusters"), [690, 600]),
+], ids=["bf16", "f32_d64", "bf16_11_10_bands"])
 def test_ragged_budgets_match_oracle_per_head(w, budgets):
     """kvc_compact_ragged: head b against the oracle's compaction at its own
     budget; the padded slots are inert (index -1, zero rows, bias -inf)."""

@@ -13,10 +13,13 @@
 // syncs with the host):
 //   k_ps           P_S = exp(Q C_k^T - lse) on fp64 MFMA (16x16x4), with the
 //                  partial column sums of each 64-query tile
-//   k_atb          C = A^T B tiles on fp64 MFMA (Grams, X^T O), split-K
+//   k_atb          C = A^T B tiles on fp64 MFMA (the mass Gram, lower
+//                  triangle), split-K with a fixed-order reduction
 //   k_bias_lam, k_bias_prep   lam_w; H = M + lam_w I, c = P_S^T 1 + lam_w
 //   k_nnls_sweep   block principal pivoting on the swept bias system
-//   k_value_prep, k_ridge_v, k_rhs_ridge   the value system
+//   k_value_prep   X_F compacted at the front of each P_S row
+//   k_atb2         the value Gram X_F^T X_F and X_F^T O in one launch
+//   k_ridge_v, k_rhs_ridge   the value system's ridge
 //   k_value_sweep  its solve by the same block sweeps
 //   k_write_out    C_v and beta to the outputs.
 // Keys whose multiplier is pinned at zero carry a factor 1e-30 in X; their
